@@ -1,0 +1,246 @@
+"""The CSA2 decode step, written out in float64 (TEST INFRASTRUCTURE ONLY).
+
+What the step computes, stage by stage (citations use the page keys of the
+package docstring; the pages give no formulas, so where they are silent the
+reading taken is stated at the function and listed in the design doc):
+
+1. a0  ``quantize_fp4``  - the FP4 main-KV write: E2M1 values, one E4M3
+       scale per 16 channels, no global scale, applied to post-RoPE values
+       [P1 效率组件四件 #4; P4 CSA2 paragraph].
+2. a1  ``index_full``    - Full mode: the layer's own indexer scores every
+       compressed entry [P1 架构三件套 / CSA2; P3 mode paragraph; P4 CSA2 paragraph].
+3. a2  ``index_pool``    - Reindex mode: the layer's own indexer query
+       re-scores only the candidate pool of at most 2048 blocks x 8 positions
+       chosen by an earlier Full layer [P1 Hierarchical Sparse Indexer; P4].
+4. a3  ``topk``          - Top-512 selection [P1 CSA2], ties resolved so
+       that the lower entry position wins.
+5. a4/a5 ``sparse_attn`` - gather of the selected FP4 entries, exact
+       dequantisation, and softmax attention of every query head over them
+       (MLA-style: one latent shared by all heads; the key is [latent ; RoPE
+       part], the value is the latent).  Reuse mode is this stage alone with
+       the index list handed in [P1 CSA2; P3; P4].
+"""
+
+import numpy as np
+
+from .codec import (
+    bf16_bits_to_f64,
+    e2m1_decode,
+    e2m1_encode_magnitude,
+    e4m3_decode,
+    e4m3_scale_code_for_amax,
+)
+
+GROUP = 16  # channels per E4M3 scale [P1 效率组件四件 #4]
+
+
+# ------------------------------------------------------------ a0 quantize
+
+
+def quantize_fp4(x_bits):
+    """Quantise bf16 rows to the FP4 cache format.
+
+    x_bits: uint16 [R, d_c] bf16 patterns (post-RoPE latent rows), d_c % 16 == 0.
+    Returns (codes uint8 [R, d_c/2], scales uint8 [R, d_c/16]).
+
+    Per row and per group of 16 consecutive channels:
+      amax  = max |x| over the group
+      S     = E4M3 code nearest to amax / 6 (ties even, saturate at 448)
+      sigma = value(S)
+      code  = sign bit of x (bit 3) | E2M1 magnitude code nearest to |x|/sigma
+              (ties even, saturating at 6; sigma == 0 gives magnitude 0)
+    Byte j of a row holds channel 2j in its low nibble and 2j+1 in its high
+    nibble.
+    """
+    x_bits = np.asarray(x_bits)
+    R, d_c = x_bits.shape
+    assert d_c % GROUP == 0
+    x = bf16_bits_to_f64(x_bits)                       # exact
+    xg = x.reshape(R, d_c // GROUP, GROUP)
+    amax = np.abs(xg).max(axis=-1)                     # [R, G]
+    S = e4m3_scale_code_for_amax(amax)                 # [R, G] uint8
+    sigma = e4m3_decode(S)                             # [R, G]
+    mag = e2m1_encode_magnitude(np.abs(xg), sigma[..., None])   # [R, G, 16]
+    sign = np.signbit(xg).astype(np.uint8)
+    nib = (sign << 3) | mag                            # [R, G, 16]
+    nib = nib.reshape(R, d_c)
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return codes, S.astype(np.uint8)
+
+
+def dequantize_fp4(codes, scales):
+    """Exact dequantisation: value(code) * value(scale of its group), float64."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    lead = codes.shape[:-1]
+    d_c = codes.shape[-1] * 2
+    nib = np.empty(lead + (d_c,), dtype=np.uint8)
+    nib[..., 0::2] = codes & 0x0F
+    nib[..., 1::2] = codes >> 4
+    v = e2m1_decode(nib)
+    sig = np.repeat(e4m3_decode(scales), GROUP, axis=-1)
+    return v * sig
+
+
+# ------------------------------------------------------------ a1 / a2 indexer
+
+
+def index_scores(q_idx, w, keys):
+    """Indexer score of every key row for one query.
+
+    q_idx [H_I, D_I], w [H_I] (None -> all ones), keys [N, D_I], all float64.
+    score[n] = sum_h w[h] * max(0, q_idx[h] . keys[n])
+
+    Reading (the pages give no formula): several indexer heads, each gated by
+    a ReLU, summed with per-head weights; one key per compressed entry shared
+    by all indexer heads.
+    """
+    H_I = q_idx.shape[0]
+    if w is None:
+        w = np.ones(H_I)
+    dots = keys @ q_idx.T                               # [N, H_I]
+    return (np.maximum(dots, 0.0) * w[None, :]).sum(axis=1)
+
+
+def index_full(q_bits, w, k_bits, n_valid):
+    """Full mode: score every entry n < n_valid[b]; others get -inf.
+
+    q_bits uint16 [B, H_I, D_I]; w float [B, H_I] or None; k_bits uint16
+    [B, N, D_I]; n_valid int [B] or None (= N).  Returns float64 [B, N].
+    """
+    q = bf16_bits_to_f64(q_bits)
+    k = bf16_bits_to_f64(k_bits)
+    B, N, _ = k.shape
+    out = np.full((B, N), -np.inf)
+    for b in range(B):
+        nv = N if n_valid is None else int(min(max(int(n_valid[b]), 0), N))
+        wb = None if w is None else np.asarray(w[b], dtype=np.float64)
+        out[b, :nv] = index_scores(q[b], wb, k[b, :nv])
+    return out
+
+
+def index_pool(q_bits, w, k_bits, n_valid, pool_blocks, n_blocks, block):
+    """Reindex mode: score only the positions of the candidate pool.
+
+    Pool slot (i, j), i < n_blocks[b], j < block, is entry position
+    p = block * pool_blocks[b, i] + j.  It is scored when 0 <= p < n_valid[b]
+    (and the block id is non-negative); every other slot gets score -inf and
+    position -1.  Returns (scores float64 [B, P_max*block],
+    positions int32 [B, P_max*block]).
+    """
+    q = bf16_bits_to_f64(q_bits)
+    k = bf16_bits_to_f64(k_bits)
+    B, N, _ = k.shape
+    P_max = pool_blocks.shape[1]
+    scores = np.full((B, P_max * block), -np.inf)
+    pos = np.full((B, P_max * block), -1, dtype=np.int32)
+    for b in range(B):
+        nv = N if n_valid is None else int(min(max(int(n_valid[b]), 0), N))
+        nb = int(min(max(int(n_blocks[b]), 0), P_max))
+        blk = np.asarray(pool_blocks[b, :nb], dtype=np.int64)
+        p = (block * blk[:, None] + np.arange(block)[None, :]).reshape(-1)
+        ok = (np.repeat(blk, block) >= 0) & (p >= 0) & (p < nv)
+        slots = np.nonzero(ok)[0]
+        wb = None if w is None else np.asarray(w[b], dtype=np.float64)
+        scores[b, slots] = index_scores(q[b], wb, k[b, p[slots]])
+        pos[b, slots] = p[slots]
+    return scores, pos
+
+
+# ------------------------------------------------------------ a3 Top-K
+
+
+def topk(scores, ids, n_valid, K):
+    """Top-K by (score descending, id ascending) over the valid candidates.
+
+    scores float [B, M]; ids int [B, M] or None (None -> the column index);
+    n_valid int [B] or None (= M).  Candidate (b, c) is valid when
+    c < n_valid[b] and its id is not -1.  The first min(K, #valid) candidates
+    of that order are returned in that order; the rest is padded with id -1
+    and score -inf.  NaN scores rank below every other score (numpy sorts
+    NaN last).  Returns (idx int32 [B, K], score float64 [B, K]).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    B, M = scores.shape
+    out_i = np.full((B, K), -1, dtype=np.int32)
+    out_s = np.full((B, K), -np.inf)
+    for b in range(B):
+        nv = M if n_valid is None else int(min(max(int(n_valid[b]), 0), M))
+        cid = np.arange(M, dtype=np.int64) if ids is None else np.asarray(ids[b], dtype=np.int64)
+        valid = (np.arange(M) < nv) & (cid != -1)
+        s = scores[b, valid]
+        i = cid[valid]
+        order = np.lexsort((i, -s))                   # primary: -score, then id
+        take = order[:K]
+        out_i[b, :take.size] = i[take]
+        out_s[b, :take.size] = s[take]
+    return out_i, out_s
+
+
+# ------------------------------------------------------------ a4/a5 attention
+
+
+def sparse_attn(q_bits, codes, scales, rope_bits, idx, sm_scale):
+    """Softmax attention of every head over the selected FP4 entries.
+
+    q_bits uint16 [B, H, d_c + d_r]; codes uint8 [B, N, d_c/2]; scales uint8
+    [B, N, d_c/16]; rope_bits uint16 [B, N, d_r] (d_r may be 0); idx int
+    [B, K] (entries outside [0, N), e.g. -1, are skipped; repeated entries
+    count with multiplicity).
+
+    For each b, h over the selected entries j:
+      key_j   = [dequant(codes_j, scales_j) ; rope_j]
+      value_j = dequant(codes_j, scales_j)
+      s_j = sm_scale * q_h . key_j ;  p_j = exp(s_j - max s) ;  L = sum p
+      out = sum_j p_j value_j / L ;   lse = max s + ln L
+    No selected entry -> out = 0, lse = -inf.
+    Returns (out float64 [B, H, d_c], lse float64 [B, H]).
+    """
+    q = bf16_bits_to_f64(q_bits)
+    B, H, D = q.shape
+    N = codes.shape[1]
+    d_c = codes.shape[2] * 2
+    out = np.zeros((B, H, d_c))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        sel = np.asarray(idx[b], dtype=np.int64)
+        sel = sel[(sel >= 0) & (sel < N)]
+        if sel.size == 0:
+            continue
+        lat = dequantize_fp4(codes[b, sel], scales[b, sel])          # [k, d_c]
+        if D > d_c:
+            key = np.concatenate([lat, bf16_bits_to_f64(rope_bits[b, sel])], axis=1)
+        else:
+            key = lat
+        s = sm_scale * (q[b] @ key.T)                                 # [H, k]
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        L = p.sum(axis=1, keepdims=True)
+        out[b] = (p @ lat) / L
+        lse[b] = m[:, 0] + np.log(L[:, 0])
+    return out, lse
+
+
+# ------------------------------------------------------------ the three modes
+
+
+def decode_full(q_idx_bits, w, k_idx_bits, n_valid, q_bits, codes, scales, rope_bits, K, sm_scale):
+    """Full mode: index every entry -> Top-K -> sparse attention [P1 CSA2; P4]."""
+    sc = index_full(q_idx_bits, w, k_idx_bits, n_valid)
+    idx, top = topk(sc, None, n_valid, K)
+    out, lse = sparse_attn(q_bits, codes, scales, rope_bits, idx, sm_scale)
+    return idx, top, out, lse
+
+
+def decode_reindex(q_idx_bits, w, k_idx_bits, n_valid, pool_blocks, n_blocks, block,
+                   q_bits, codes, scales, rope_bits, K, sm_scale):
+    """Reindex mode: re-score the pool -> Top-K by global position -> attention."""
+    sc, pos = index_pool(q_idx_bits, w, k_idx_bits, n_valid, pool_blocks, n_blocks, block)
+    idx, top = topk(sc, pos, None, K)
+    out, lse = sparse_attn(q_bits, codes, scales, rope_bits, idx, sm_scale)
+    return idx, top, out, lse
+
+
+def decode_reuse(idx, q_bits, codes, scales, rope_bits, sm_scale):
+    """Reuse mode: the index list is handed in; attention only."""
+    return sparse_attn(q_bits, codes, scales, rope_bits, idx, sm_scale)

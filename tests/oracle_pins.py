@@ -1,0 +1,408 @@
+"""Pins that tie the CPU oracle to things other than itself.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees
+with an independent source: a fixture derived by hand from the format
+definitions (``tests/golden``), a library routine that reduces to the same
+operation in a special case (torch's float8_e4m3fn cast, numpy's
+round-half-even, int64 matmul, stable sorts, torch.topk, float64 SDPA), brute
+force on tiny inputs, or closed-form invariants.  ``test_oracle_*.py`` run
+them against the oracle; ``test_oracle_mutations.py`` plants plausible
+mistakes in the oracle and checks that at least one pin catches each.
+"""
+
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import codec, method
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _records(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.lstrip().startswith("#")]
+
+
+def _all_bf16_finite_nonneg():
+    b = np.arange(0x0000, 0x7F80, dtype=np.uint32).astype(np.uint16)  # +0 .. max finite
+    return b, codec.bf16_bits_to_f64(b)
+
+
+# ------------------------------------------------------------------ codecs
+
+
+def check_e2m1_value_set():
+    for code, val in _records("e2m1_values.txt"):
+        c = int(code, 16)
+        got = float(oracle.e2m1_decode(np.array([c]))[0])
+        want = float(val)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got, want)
+    mags = sorted(set(np.abs(oracle.e2m1_decode(np.arange(16))).tolist()))
+    assert mags == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def check_e4m3_decode():
+    for code, val in _records("e4m3_values.txt"):
+        got = float(oracle.e4m3_decode(np.array([int(code, 16)]))[0])
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (code, got)
+    v = oracle.e4m3_decode(np.arange(127))
+    assert np.all(np.diff(v) > 0)                 # 127 finite non-negative codes, increasing
+    assert v[0] == 0.0 and v[-1] == 448.0
+
+
+def check_e4m3_encode_vs_torch():
+    """RNE to E4M3 equals torch's float8_e4m3fn cast for values <= 448."""
+    rng = np.random.default_rng(7)
+    vals = oracle.e4m3_decode(np.arange(127))
+    mids = (vals[:-1] + vals[1:]) / 2
+    t = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, 1000),
+                        rng.uniform(0, 448, 20000), rng.uniform(0, 0.02, 20000)])
+    t = t.astype(np.float32).astype(np.float64)   # fp32-exact so the cast rounds once
+    ref = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(t)
+    bad = np.nonzero(ref != got)[0]
+    assert bad.size == 0, (t[bad[:5]], ref[bad[:5]], got[bad[:5]])
+
+
+def check_scale_code_vs_torch():
+    """Scale code for every positive finite bf16 amax below saturation equals
+    torch's float8_e4m3fn cast of amax / 6."""
+    _, a = _all_bf16_finite_nonneg()
+    a = a[a < 6 * 448]
+    ref = torch.from_numpy(a / 6.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_scale_code_for_amax(a)
+    bad = np.nonzero(ref != got)[0]
+    assert bad.size == 0, (a[bad[:5]], ref[bad[:5]], got[bad[:5]])
+    # saturation: amax/6 above 448 maps to 0x7E (the cast would give NaN there)
+    _, big = _all_bf16_finite_nonneg()
+    big = big[big >= 6 * 448]
+    assert np.all(oracle.e4m3_scale_code_for_amax(big) == 0x7E)
+
+
+def _e2m1_value_by_numpy_round(y):
+    """RNE of y >= 0 onto {0,.5,1,1.5,2,3,4,6} via np.round (half-to-even) with
+    the quantum of each binade, saturating at 6."""
+    q = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    return np.minimum(np.round(y / q) * q, 6.0)
+
+
+def check_e2m1_encode_vs_numpy_round():
+    grid = oracle.e2m1_decode(np.arange(8))
+    _, x = _all_bf16_finite_nonneg()
+    for sigma in [1.0, 1.25, 0.75, 2.0 ** -9, 3 * 2.0 ** -9, 448.0, 1.875, 0.015625, 96.0]:
+        xs = x[x < 16 * sigma]
+        code = oracle.e2m1_encode_magnitude(xs, sigma)
+        want = _e2m1_value_by_numpy_round(xs / sigma)
+        assert np.array_equal(grid[code], want), sigma
+    assert np.all(oracle.e2m1_encode_magnitude(x[:100], 0.0) == 0)
+
+
+def check_bf16_decode():
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127,
+             0x3E9A: 0.30078125, 0x8000: -0.0, 0x0080: 2.0 ** -126}
+    for bits, val in cases.items():
+        got = float(codec.bf16_bits_to_f64(np.array([bits], dtype=np.uint16))[0])
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), hex(bits)
+
+
+# ------------------------------------------------------------------ quantize
+
+
+def check_quantize_golden():
+    recs = _records("quantize_groups.txt")
+    assert len(recs) % 3 == 0 and len(recs) >= 30
+    rows, scales, nibs = [], [], []
+    for i in range(0, len(recs), 3):
+        assert recs[i][0] == "in" and recs[i + 1][0] == "scale" and recs[i + 2][0] == "codes"
+        rows.append([float(v) for v in recs[i][1:]])
+        scales.append(int(recs[i + 1][1], 16))
+        nibs.append([int(c, 16) for c in recs[i + 2][1:]])
+    # one row per group, and the same groups concatenated into one long row
+    x = codec.f64_to_bf16_bits_exact(np.array(rows))
+    want_n = np.array(nibs, dtype=np.uint8)
+    want_c = want_n[:, 0::2] | (want_n[:, 1::2] << 4)
+    c, s = oracle.quantize_fp4(x)
+    assert np.array_equal(s[:, 0], np.array(scales, dtype=np.uint8)), (s[:, 0], scales)
+    assert np.array_equal(c, want_c), (c, want_c)
+    c2, s2 = oracle.quantize_fp4(x.reshape(1, -1))
+    assert np.array_equal(c2.reshape(c.shape), c) and np.array_equal(s2.reshape(-1), s[:, 0])
+
+
+def check_quantize_roundtrip_fixed_point():
+    """Values already on an FP4 grid whose group holds a +-6*sigma element
+    quantise back to the same codes and scale."""
+    rng = np.random.default_rng(3)
+    R, G = 64, 32
+    S = rng.integers(0x08, 0x70, size=(R, G)).astype(np.uint8)       # normal scales
+    nib = rng.integers(0, 16, size=(R, G, 16)).astype(np.uint8)
+    nib[:, :, 5] = np.where(rng.random((R, G)) < 0.5, 0x7, 0xF)      # force a +-6
+    codes = (nib.reshape(R, -1)[:, 0::2] | (nib.reshape(R, -1)[:, 1::2] << 4)).astype(np.uint8)
+    x = oracle.dequantize_fp4(codes, S)
+    bits = codec.f64_to_bf16_bits_exact(x)
+    c2, s2 = oracle.quantize_fp4(bits)
+    assert np.array_equal(s2, S)
+    # -0 codes dequantise to -0.0 and keep their sign bit
+    assert np.array_equal(c2, codes)
+
+
+def check_quantize_error_bound():
+    """Every non-saturated element lands within half a grid step of x, and
+    the chosen scale is the nearest E4M3 value to amax/6."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((256, 512)) * np.exp(rng.uniform(-6, 6, size=(256, 1)))
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xb = codec.bf16_bits_to_f64(bits)
+    c, s = oracle.quantize_fp4(bits)
+    deq = oracle.dequantize_fp4(c, s)
+    sig = np.repeat(oracle.e4m3_decode(s), 16, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.abs(xb) / sig
+    gap = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0)) * sig
+    ok = y <= 6
+    assert np.all(np.abs(xb - deq)[ok] <= gap[ok] / 2 + 0.0)
+    assert np.all(np.sign(deq) * np.sign(xb) >= 0)
+    amax = np.abs(xb).reshape(256, 32, 16).max(-1)
+    vals = oracle.e4m3_decode(np.arange(127))
+    err = np.abs(oracle.e4m3_decode(s) - amax / 6)
+    best = np.abs(vals[None, None, :] - (amax / 6)[..., None]).min(-1)
+    assert np.allclose(err, best, rtol=0, atol=1e-12 * np.maximum(amax, 1e-30))
+
+
+def check_nibble_order():
+    x = np.zeros((1, 16))
+    x[0, 0] = 6.0   # channel 0 -> low nibble of byte 0
+    x[0, 3] = -1.0  # channel 3 -> high nibble of byte 1
+    c, s = oracle.quantize_fp4(codec.f64_to_bf16_bits_exact(x))
+    assert c[0, 0] == 0x07 and c[0, 1] == 0xA0 and s[0, 0] == 0x38
+
+
+# ------------------------------------------------------------------ indexer
+
+
+def check_index_bruteforce():
+    rng = np.random.default_rng(5)
+    H_I, D_I, N = 3, 8, 20
+    q = rng.integers(-8, 9, size=(H_I, D_I)).astype(np.float64)
+    k = rng.integers(-8, 9, size=(N, D_I)).astype(np.float64)
+    w = np.array([0.5, -1.25, 2.0])
+    got = oracle.index_scores(q, w, k)
+    for n in range(N):
+        acc = 0.0
+        for h in range(H_I):
+            d = sum(q[h, i] * k[n, i] for i in range(D_I))
+            acc += w[h] * (d if d > 0 else 0.0)
+        assert got[n] == acc, n
+
+
+def check_index_full_vs_int64_matmul():
+    rng = np.random.default_rng(6)
+    B, H_I, D_I, N = 2, 8, 128, 300
+    qi = rng.integers(-8, 9, size=(B, H_I, D_I))
+    ki = rng.integers(-8, 9, size=(B, N, D_I))
+    qb = codec.f64_to_bf16_bits_exact(qi.astype(np.float64))
+    kb = codec.f64_to_bf16_bits_exact(ki.astype(np.float64))
+    nv = np.array([N, 123])
+    got = oracle.index_full(qb, None, kb, nv)
+    for b in range(B):
+        dots = np.matmul(ki[b], qi[b].T)                     # int64, exact
+        want = np.maximum(dots, 0).sum(axis=1).astype(np.float64)
+        assert np.array_equal(got[b, :nv[b]], want[:nv[b]])
+        assert np.all(np.isneginf(got[b, nv[b]:]))
+
+
+def check_index_pool_bruteforce():
+    rng = np.random.default_rng(8)
+    B, H_I, D_I, N, P_max, blk = 2, 4, 32, 96, 8, 8
+    qi = rng.integers(-8, 9, size=(B, H_I, D_I)).astype(np.float64)
+    ki = rng.integers(-8, 9, size=(B, N, D_I)).astype(np.float64)
+    qb, kb = codec.f64_to_bf16_bits_exact(qi), codec.f64_to_bf16_bits_exact(ki)
+    pool = np.array([[0, 3, 11, 5, -1, 7, 2, 9], [1, 2, 3, 4, 5, 6, 7, 8]], dtype=np.int32)
+    nblk = np.array([7, 5], dtype=np.int32)
+    nv = np.array([N, 50])
+    sc, pos = oracle.index_pool(qb, None, kb, nv, pool, nblk, blk)
+    for b in range(B):
+        for i in range(P_max):
+            for j in range(blk):
+                slot = i * blk + j
+                p = blk * int(pool[b, i]) + j
+                if i < nblk[b] and pool[b, i] >= 0 and 0 <= p < nv[b]:
+                    want = sum(max(0.0, float(qi[b, h] @ ki[b, p])) for h in range(H_I))
+                    assert pos[b, slot] == p and sc[b, slot] == want
+                else:
+                    assert pos[b, slot] == -1 and np.isneginf(sc[b, slot])
+
+
+# ------------------------------------------------------------------ Top-K
+
+
+def _topk_brute(scores, ids, valid, K):
+    cand = [(i, float(scores[i]), int(ids[i])) for i in range(len(scores)) if valid[i]]
+
+    def key(t):
+        s = t[1]
+        return (1 if math.isnan(s) else 0, 0.0 if math.isnan(s) else -s, t[2])
+    cand.sort(key=key)
+    cand = cand[:K]
+    return [c[2] for c in cand] + [-1] * (K - len(cand)), [c[1] for c in cand] + [-math.inf] * (K - len(cand))
+
+
+def check_topk_bruteforce():
+    rng = np.random.default_rng(9)
+    for trial in range(300):
+        M = int(rng.integers(1, 64))
+        K = int(rng.integers(1, 70))
+        s = rng.integers(-3, 4, size=M).astype(np.float64)     # heavy ties
+        if trial % 5 == 0:
+            s[rng.random(M) < 0.2] = np.nan
+        if trial % 7 == 0:
+            s[rng.random(M) < 0.3] = -np.inf
+        use_ids = trial % 2 == 1
+        ids = rng.permutation(1000)[:M].astype(np.int32) if use_ids else np.arange(M, dtype=np.int32)
+        if use_ids:
+            ids[rng.random(M) < 0.15] = -1
+        nv = int(rng.integers(0, M + 1))
+        gi, gs = oracle.topk(s[None], ids[None] if use_ids else None, np.array([nv]), K)
+        valid = (np.arange(M) < nv) & (ids != -1)
+        wi, ws = _topk_brute(s, ids, valid, K)
+        assert gi[0].tolist() == wi, (trial, gi[0], wi)
+        assert np.array_equal(gs[0], np.array(ws), equal_nan=True), trial
+
+
+def check_topk_vs_torch_topk_distinct():
+    rng = np.random.default_rng(10)
+    s = rng.permutation(20000).astype(np.float64)[None, :16384] * 0.5
+    gi, gs = oracle.topk(s, None, None, 512)
+    tv, ti = torch.topk(torch.from_numpy(s[0]), 512, sorted=True)
+    assert np.array_equal(gi[0], ti.numpy().astype(np.int32))
+    assert np.array_equal(gs[0], tv.numpy())
+
+
+def check_topk_ties_vs_stable_sort():
+    rng = np.random.default_rng(12)
+    s = rng.integers(0, 50, size=(3, 4096)).astype(np.float64)
+    gi, _ = oracle.topk(s, None, None, 512)
+    for b in range(3):
+        order = np.argsort(-s[b], kind="stable")[:512]
+        assert np.array_equal(gi[b], order.astype(np.int32))
+
+
+def check_topk_invariants():
+    rng = np.random.default_rng(13)
+    s = rng.integers(0, 200, size=(4, 2000)).astype(np.float64)
+    ids = np.stack([rng.permutation(10 ** 6)[:2000] for _ in range(4)]).astype(np.int32)
+    gi, gs = oracle.topk(s, ids, None, 300)
+    for b in range(4):
+        sel = set(gi[b].tolist())
+        assert len(sel) == 300
+        pos = {int(v): i for i, v in enumerate(ids[b])}
+        chosen = np.array([pos[int(v)] for v in gi[b]])
+        rest = np.setdiff1d(np.arange(2000), chosen)
+        assert s[b, chosen].min() >= s[b, rest].max()
+        thr = s[b, chosen].min()
+        tied_rest = ids[b, rest][s[b, rest] == thr]
+        tied_in = ids[b, chosen][s[b, chosen] == thr]
+        assert tied_rest.size == 0 or tied_in.max() < tied_rest.min()
+        for a in range(299):
+            assert gs[b, a] > gs[b, a + 1] or (gs[b, a] == gs[b, a + 1] and gi[b, a] < gi[b, a + 1])
+    gi, _ = oracle.topk(s[:1, :100], None, None, 100)
+    assert sorted(gi[0].tolist()) == list(range(100))
+
+
+# ------------------------------------------------------------------ attention
+
+
+def _attn_inputs(B=2, H=8, N=40, d_c=64, d_r=32, seed=14):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, d_c + d_r))
+    qb = torch.from_numpy(q).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    codes = rng.integers(0, 256, size=(B, N, d_c // 2)).astype(np.uint8)
+    scales = rng.integers(0x28, 0x40, size=(B, N, d_c // 16)).astype(np.uint8)
+    rope = rng.standard_normal((B, N, d_r))
+    rb = torch.from_numpy(rope).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return qb, codes, scales, rb
+
+
+def check_attn_dense_vs_sdpa():
+    """Top-K covering every entry reproduces dense attention (float64 SDPA)."""
+    qb, codes, scales, rb = _attn_inputs()
+    B, H, D = qb.shape
+    N, d_c = codes.shape[1], codes.shape[2] * 2
+    sm = 1.0 / math.sqrt(D)
+    idx = np.tile(np.arange(N), (B, 1))
+    out, lse = oracle.sparse_attn(qb, codes, scales, rb, idx, sm)
+    q = torch.from_numpy(codec.bf16_bits_to_f64(qb))
+    lat = torch.from_numpy(oracle.dequantize_fp4(codes, scales))
+    key = torch.cat([lat, torch.from_numpy(codec.bf16_bits_to_f64(rb))], dim=-1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, key, lat, scale=sm)
+    assert np.allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+    s = sm * torch.einsum("bhd,bnd->bhn", q, key)
+    assert np.allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def check_attn_special_cases():
+    qb, codes, scales, rb = _attn_inputs(seed=15)
+    B, H, D = qb.shape
+    N = codes.shape[1]
+    sm = 0.125
+    lat = oracle.dequantize_fp4(codes, scales)
+    # K = 1: the output is that entry's value row, exactly
+    idx = np.array([[7], [31]])
+    out, lse = oracle.sparse_attn(qb, codes, scales, rb, idx, sm)
+    for b in range(B):
+        assert np.array_equal(out[b], np.tile(lat[b, idx[b, 0]], (H, 1)))
+    # q = 0: uniform weights -> mean of the selected values, lse = ln k
+    zq = np.zeros_like(qb)
+    idx = np.array([[1, 4, 9, 16, 25], [0, 2, 3, 5, 8]])
+    out, lse = oracle.sparse_attn(zq, codes, scales, rb, idx, sm)
+    for b in range(B):
+        assert np.allclose(out[b], lat[b, idx[b]].mean(0)[None, :], rtol=1e-14, atol=1e-14)
+    assert np.allclose(lse, math.log(5))
+    # permutation of the index list changes nothing; masked ids are skipped
+    rng = np.random.default_rng(1)
+    idx = np.stack([rng.permutation(N)[:16] for _ in range(B)])
+    o1, l1 = oracle.sparse_attn(qb, codes, scales, rb, idx, sm)
+    o2, l2 = oracle.sparse_attn(qb, codes, scales, rb, idx[:, ::-1].copy(), sm)
+    assert np.allclose(o1, o2, rtol=1e-13, atol=1e-13) and np.allclose(l1, l2, rtol=1e-13)
+    idxm = np.concatenate([idx, np.full((B, 3), -1), np.full((B, 2), N + 5)], axis=1)
+    o3, l3 = oracle.sparse_attn(qb, codes, scales, rb, idxm, sm)
+    assert np.allclose(o1, o3, rtol=1e-13, atol=1e-13) and np.allclose(l1, l3, rtol=1e-13)
+    # nothing valid -> zeros and -inf
+    o4, l4 = oracle.sparse_attn(qb, codes, scales, rb, np.full((B, 4), -1), sm)
+    assert np.all(o4 == 0) and np.all(np.isneginf(l4))
+    # a repeated entry counts twice: same as giving it weight 2 (lse + ln of the multiplicity mix)
+    o5, _ = oracle.sparse_attn(qb, codes, scales, rb, np.array([[3, 3], [6, 6]]), sm)
+    for b, j in enumerate([3, 6]):
+        assert np.array_equal(o5[b], np.tile(lat[b, j], (H, 1)))
+
+
+def check_decode_modes_compose():
+    """Full and Reindex decode are exactly index -> topk -> attention."""
+    rng = np.random.default_rng(16)
+    B, N, H_I, D_I = 1, 64, 2, 32
+    qi = codec.f64_to_bf16_bits_exact(rng.integers(-8, 9, size=(B, H_I, D_I)).astype(float))
+    ki = codec.f64_to_bf16_bits_exact(rng.integers(-8, 9, size=(B, N, D_I)).astype(float))
+    qb, codes, scales, rb = _attn_inputs(B=1, N=N, seed=17)
+    idx, top, out, lse = oracle.decode_full(qi, None, ki, None, qb, codes, scales, rb, 8, 0.1)
+    want_i, _ = oracle.topk(oracle.index_full(qi, None, ki, None), None, None, 8)
+    assert np.array_equal(idx, want_i)
+    pool = np.array([[1, 3, 5, 7]], dtype=np.int32)
+    idx2, _, _, _ = oracle.decode_reindex(qi, None, ki, None, pool, np.array([4]), 8,
+                                          qb, codes, scales, rb, 8, 0.1)
+    assert set(idx2[0].tolist()) <= set(sum(([8 * b + j for j in range(8)] for b in [1, 3, 5, 7]), []))
+
+
+ALL_PINS = [
+    check_e2m1_value_set, check_e4m3_decode, check_e4m3_encode_vs_torch, check_scale_code_vs_torch,
+    check_e2m1_encode_vs_numpy_round, check_bf16_decode, check_quantize_golden,
+    check_quantize_roundtrip_fixed_point, check_quantize_error_bound, check_nibble_order,
+    check_index_bruteforce, check_index_full_vs_int64_matmul, check_index_pool_bruteforce,
+    check_topk_bruteforce, check_topk_vs_torch_topk_distinct, check_topk_ties_vs_stable_sort,
+    check_topk_invariants, check_attn_dense_vs_sdpa, check_attn_special_cases, check_decode_modes_compose,
+]

@@ -1,0 +1,113 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them.  Each mutation replaces one oracle function for the
+duration of the test only."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle_pins as P  # noqa: E402
+import oracle  # noqa: E402
+from oracle import codec, method  # noqa: E402
+
+_orig_quantize = method.quantize_fp4
+_orig_enc = codec.e2m1_encode_magnitude
+_orig_scale = codec.e4m3_scale_code_for_amax
+_orig_topk = method.topk
+_orig_attn = method.sparse_attn
+_orig_pool = method.index_pool
+_orig_scores = method.index_scores
+
+
+def _swap_nibbles(x_bits):
+    c, s = _orig_quantize(x_bits)
+    return ((c >> 4) | (c << 4)).astype(np.uint8), s
+
+
+def _ties_away(y_abs, sigma):
+    code = _orig_enc(y_abs, sigma)
+    grid = codec.e2m1_decode(np.arange(8))
+    y = np.asarray(y_abs, dtype=np.float64)
+    sg = np.broadcast_to(np.asarray(sigma, dtype=np.float64), y.shape)
+    up = np.minimum(code + 1, 7)
+    tie = (sg * (grid[code] + grid[up]) / 2 == y) & (code < 7)
+    return np.where(tie, up, code).astype(np.uint8)
+
+
+def _scale_div4(amax):
+    return _orig_scale(np.asarray(amax) * 1.5)
+
+
+def _fnuz_decode(codes):
+    return codec_e4m3_orig(codes) / 2.0
+
+
+codec_e4m3_orig = codec.e4m3_decode
+
+
+def _no_relu(q_idx, w, keys):
+    H_I = q_idx.shape[0]
+    w = np.ones(H_I) if w is None else w
+    return ((keys @ q_idx.T) * w[None, :]).sum(axis=1)
+
+
+def _topk_id_desc(scores, ids, n_valid, K):
+    scores = np.asarray(scores, dtype=np.float64)
+    B, M = scores.shape
+    out_i = np.full((B, K), -1, dtype=np.int32)
+    out_s = np.full((B, K), -np.inf)
+    for b in range(B):
+        nv = M if n_valid is None else int(min(max(int(n_valid[b]), 0), M))
+        cid = np.arange(M) if ids is None else np.asarray(ids[b], dtype=np.int64)
+        valid = (np.arange(M) < nv) & (cid != -1)
+        s, i = scores[b, valid], cid[valid]
+        order = np.lexsort((-i, -s))[:K]
+        out_i[b, :order.size] = i[order]
+        out_s[b, :order.size] = s[order]
+    return out_i, out_s
+
+
+def _attn_no_rope(q_bits, codes, scales, rope_bits, idx, sm_scale):
+    return _orig_attn(q_bits, codes, scales, np.zeros_like(rope_bits), idx, sm_scale)
+
+
+def _attn_lse_log2(*a):
+    out, lse = _orig_attn(*a)
+    return out, lse / np.log(2.0)
+
+
+def _pool_transposed(q_bits, w, k_bits, n_valid, pool_blocks, n_blocks, block):
+    # plant: position = block id + block * j instead of block * id + j
+    pb = np.asarray(pool_blocks)
+    sc, pos = _orig_pool(q_bits, w, k_bits, n_valid, pb, n_blocks, block)
+    return sc, np.where(pos >= 0, pos // block + (pos % block) * block, pos).astype(np.int32)
+
+
+MUTATIONS = {
+    "nibble_order_swapped": [(method, "quantize_fp4", _swap_nibbles), (oracle, "quantize_fp4", _swap_nibbles)],
+    "e2m1_ties_away": [(method, "e2m1_encode_magnitude", _ties_away), (oracle, "e2m1_encode_magnitude", _ties_away)],
+    "scale_wrong_divisor": [(method, "e4m3_scale_code_for_amax", _scale_div4),
+                            (oracle, "e4m3_scale_code_for_amax", _scale_div4)],
+    "e4m3_fnuz_bias": [(method, "e4m3_decode", _fnuz_decode), (oracle, "e4m3_decode", _fnuz_decode)],
+    "indexer_without_relu": [(method, "index_scores", _no_relu), (oracle, "index_scores", _no_relu)],
+    "topk_tie_id_descending": [(method, "topk", _topk_id_desc), (oracle, "topk", _topk_id_desc)],
+    "attention_drops_rope": [(method, "sparse_attn", _attn_no_rope), (oracle, "sparse_attn", _attn_no_rope)],
+    "attention_lse_base2": [(method, "sparse_attn", _attn_lse_log2), (oracle, "sparse_attn", _attn_lse_log2)],
+    "pool_position_transposed": [(method, "index_pool", _pool_transposed), (oracle, "index_pool", _pool_transposed)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    for mod, attr, fn in MUTATIONS[name]:
+        monkeypatch.setattr(mod, attr, fn)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
