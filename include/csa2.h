@@ -1,0 +1,200 @@
+/*
+ * csa2.h - C ABI of libcsa2.so, the MI355X (gfx950) CSA2 FP4 sparse-attention
+ * decode step.
+ *
+ * The method: DeepSeek-V4.1-Flash's Compressed Sparse Attention 2 (CSA2).
+ * Each decode query runs, per layer, one of three statically assigned modes:
+ *   Full    - the layer's indexer scores every compressed KV entry, Top-K
+ *             picks the entries, sparse attention runs over them;
+ *   Reindex - the layer reuses an earlier layer's KV cache but re-scores with
+ *             its own indexer query, only inside the candidate pool (at most
+ *             2048 blocks x 8 positions) an earlier Full layer chose;
+ *   Reuse   - the layer reuses KV and the Top-K list; attention only.
+ * The main KV cache is FP4: E2M1 values with one E4M3 scale per 16 channels,
+ * no second-level global scale, quantised after RoPE.
+ *
+ * Page keys used in the citations below:
+ *  [P1] "DeepSeek-V4.1-Flash：把 KV Cache 压缩到极限的百万上下文 MoE（技术报告全系统解读）"
+ *       (ai-engineering-6yk.pages.dev, ch01/059)
+ *  [P3] "552B参数干掉1.6T：DeepSeek V4.1 Flash技术深度解析" (55zb.com)
+ *  [P4] "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression" (agihunt.info)
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; tensors are
+ *    dense row-major with the shapes given; every tensor pointer must be
+ *    16-byte aligned.  bf16 values are passed as raw uint16_t bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on that stream and returns; nothing synchronises.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    non-zero csa2_status is returned and nothing is enqueued.  Values that
+ *    live in device memory (n_valid, indices, pool ids) cannot be checked on
+ *    the host: out-of-range values there have the defined behaviour stated
+ *    per function (masking / clamping), never an out-of-bounds access.
+ *  - The library allocates no device memory and keeps no mutable global
+ *    state; calls on different streams may run concurrently.  Where a kernel
+ *    needs scratch space the caller passes a workspace whose size comes from
+ *    the matching *_workspace_bytes() query.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* csa2_stream_t; /* a hipStream_t */
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,        /* a required pointer is NULL */
+  CSA2_ERR_SHAPE = 2,       /* a size is negative or inconsistent */
+  CSA2_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  CSA2_ERR_RANGE = 4,       /* append past capacity, K out of [1, 2048], ... */
+  CSA2_ERR_UNSUPPORTED = 5, /* dimensions without a compiled kernel */
+  CSA2_ERR_HIP = 6,         /* the HIP runtime refused a launch */
+  CSA2_ERR_WORKSPACE = 7    /* workspace NULL or smaller than required */
+} csa2_status;
+
+/* Static text for a status code (never NULL). */
+const char* csa2_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int csa2_version(void);
+
+/*
+ * a0. FP4 quantise + append (the main-KV write).
+ * Defined by [P1] section 效率组件四件, item 4 (E2M1 values, one E4M3 scale per
+ * 16 channels, no global scale, quantised after RoPE) and [P4] CSA2 paragraph.
+ *
+ * x        bf16 [n_rows, d_c]   post-RoPE latent rows (RoPE is applied by the
+ *                               caller; this call does not rotate)
+ * rope_src bf16 [n_rows, d_r]   RoPE part, copied unchanged (NULL iff d_r == 0)
+ * codes    u8  [capacity, d_c/2]  cache: byte j of a row = channel 2j (low
+ *                                 nibble) | channel 2j+1 (high nibble)
+ * scales   u8  [capacity, d_c/16] cache: E4M3 scale of channels [16g, 16g+16)
+ * rope_dst bf16 [capacity, d_r]   cache RoPE part (NULL iff d_r == 0)
+ * Rows [dst_row0, dst_row0 + n_rows) of the three caches are written.
+ *
+ * Per group of 16 channels: scale = the E4M3 value nearest to max|x| / 6
+ * (ties to the even code, saturating at 448 = 0x7E); each element's code is
+ * the input's sign bit plus the E2M1 magnitude nearest to |x| / scale (ties
+ * to the even code, saturating at 6); a zero scale gives magnitude 0.
+ * Bit-exact with the oracle for all finite inputs; codes for non-finite
+ * inputs are unspecified (but written, in bounds).
+ * Requires d_c % 32 == 0, 32 <= d_c <= 4096, d_r % 8 == 0, d_r <= 1024,
+ * n_rows >= 0, 0 <= dst_row0, dst_row0 + n_rows <= capacity.
+ */
+int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c,
+                      const uint16_t* rope_src, int32_t d_r,
+                      uint8_t* codes, uint8_t* scales, uint16_t* rope_dst,
+                      int64_t dst_row0, int64_t capacity, csa2_stream_t stream);
+
+/*
+ * a1. Indexer scores, Full mode: every entry of the cache is scored.
+ * Defined by [P1] 架构三件套, CSA2 (Full mode runs the whole pipeline) and
+ * [P4] CSA2 paragraph (Full produces its own KV and Top-K).  The pages give
+ * no formula; the reading implemented is
+ *   score[b, n] = sum_h w[b, h] * max(0, q_idx[b, h, :] . k_idx[b, n, :])
+ * (ReLU-gated indexer heads, one key per entry shared by all heads), summed
+ * over h in increasing order in fp32 after an exact-order-free fp32 dot
+ * (bf16 products accumulated in fp32 by the matrix cores).
+ *
+ * q_idx   bf16 [B, H_I, D_I]
+ * w       f32  [B, H_I]  per-head weights, or NULL for all ones
+ * k_idx   bf16 [B, N_cap, D_I]  indexer key cache
+ * n_valid i32  [B]  valid entries per sequence, or NULL for N_cap; values are
+ *                   clamped to [0, N_cap] on the device
+ * scores  f32  [B, N_cap]  out; entries n >= n_valid[b] get -inf (not read)
+ * Integer-valued inputs with |sums| < 2^24 give exact scores.
+ * Requires 1 <= H_I <= 16, D_I in {32, 64, 128, 256}, B >= 0, N_cap >= 0.
+ */
+int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                    const int32_t* n_valid, int32_t B, int32_t H_I, int32_t D_I,
+                    int64_t N_cap, float* scores, csa2_stream_t stream);
+
+/*
+ * a2. Indexer scores, Reindex mode: only the candidate pool is scored.
+ * Defined by [P1] section Hierarchical Sparse Indexer (an earlier Full layer
+ * builds a block-level candidate pool of at most 2048 blocks x 8 positions;
+ * later Reindex layers score only inside it, so the cost stops growing with
+ * the context) and [P4] CSA2 paragraph.
+ *
+ * pool_blocks i32 [B, P_max]  block ids; block id p covers entries
+ *                             [block*p, block*p + block)
+ * n_blocks    i32 [B]         used pool slots per sequence (clamped to [0, P_max])
+ * scores      f32 [B, P_max*block]  out: slot i*block + j scores entry
+ *                                   block*pool_blocks[b,i] + j
+ * positions   i32 [B, P_max*block]  out: that entry's global position
+ * A slot is empty (score -inf, position -1, key not read) when i >=
+ * n_blocks[b], the block id is negative, or the position is >= n_valid[b].
+ * Other arguments as csa2_index_full.  Requires 1 <= block <= 64,
+ * 1 <= P_max, P_max * block <= 2^24.
+ */
+int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                    const int32_t* n_valid, const int32_t* pool_blocks,
+                    const int32_t* n_blocks, int32_t B, int32_t H_I, int32_t D_I,
+                    int64_t N_cap, int32_t P_max, int32_t block, float* scores,
+                    int32_t* positions, csa2_stream_t stream);
+
+/*
+ * a3. Top-K selection with the lower id winning ties.
+ * Top-512 per [P1] 架构三件套, CSA2; the tie rule (lower index wins) is a
+ * fixed parameter of this build; ids are global entry positions.
+ *
+ * scores    f32 [B, M]
+ * ids       i32 [B, M]  candidate ids, or NULL for the column index; id -1
+ *                       marks an empty candidate (never chosen)
+ * n_valid   i32 [B]     only columns c < n_valid[b] are candidates (NULL = M;
+ *                       clamped to [0, M] on the device)
+ * out_idx   i32 [B, K]  out: ids of the min(K, #candidates) best candidates
+ *                       in order (score descending, id ascending), then -1
+ * out_score f32 [B, K]  out (nullable): their scores, then -inf
+ * -0.0 ranks equal to +0.0 and is reported as +0.0; NaN ranks below every
+ * other score and is reported as a quiet NaN.  Ids must be >= 0 (other than
+ * -1); equal (score, id) pairs are interchangeable.  Bit-exact.
+ * Requires 1 <= K <= 2048, 1 <= M < 2^31, B >= 0, and a workspace of at
+ * least csa2_topk_workspace_bytes(B, M, K) bytes (may be 0 / NULL then).
+ */
+size_t csa2_topk_workspace_bytes(int32_t B, int64_t M, int32_t K);
+int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
+              int32_t B, int64_t M, int32_t K, int32_t* out_idx, float* out_score,
+              void* workspace, size_t workspace_bytes, csa2_stream_t stream);
+
+/*
+ * a4 + a5. Gather, FP4 dequantisation and softmax attention over the
+ * selected entries (also the whole of Reuse mode, where idx is handed in).
+ * Defined by [P1] 架构三件套, CSA2 (Reuse reuses KV and the index and runs
+ * sparse attention directly), [P3] (modes paragraph) and [P4] CSA2 paragraph;
+ * the entry layout is MLA-style: key_j = [dequant(latent_j) ; rope_j],
+ * value_j = dequant(latent_j), shared by all H query heads.
+ *
+ * q      bf16 [B, H, d_c + d_r]
+ * codes  u8   [B, N_cap, d_c/2]   scales u8 [B, N_cap, d_c/16]
+ * rope   bf16 [B, N_cap, d_r]     (NULL iff d_r == 0)
+ * idx    i32  [B, K]  selected entries; ids < 0 or >= N_cap are skipped,
+ *                     repeated ids count with multiplicity
+ * out    f32  [B, H, d_c]  softmax(sm_scale * q . key) . value
+ * lse    f32  [B, H]  (nullable) natural-log sum-exp of the scaled scores
+ * A row with no usable entry gets out = 0, lse = -inf.
+ * Dequantised values are exact (E2M1 x E4M3 has at most 6 significant bits);
+ * products are formed by the matrix cores with fp32 accumulation and the
+ * softmax runs in fp32: the error against an exact evaluation is < 2e-3 of
+ * max|out| per (b, h) row for unit-scale inputs.
+ * Requires d_c in {128, 512}, d_r in {0, 64}, 1 <= H <= 128, K >= 1, B >= 0,
+ * and a workspace of csa2_sparse_attn_workspace_bytes(B, H, d_c, K) bytes.
+ */
+size_t csa2_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t K);
+int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                         const uint16_t* rope, const int32_t* idx, int32_t K, int32_t B,
+                         int32_t H, int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale,
+                         float* out, float* lse, void* workspace, size_t workspace_bytes,
+                         csa2_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,202 @@
+"""Thin ctypes binding of libcsa2.so (declared in include/csa2.h).
+
+Argument marshalling only: torch tensors become device pointers, the stream is
+torch's current HIP stream, and a non-zero status raises ``Csa2Error``.  Every
+step of the decode path runs in the library's HIP kernels; there is no
+fallback of any kind.  When the library is missing the first call raises.
+
+Functions carry the C names.  Output tensors (and workspaces) may be passed in
+(the call then allocates nothing) or are allocated here with torch.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "csa2.h")
+
+_lib = None
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+        self.status = status
+
+
+def load():
+    """Load libcsa2.so (once).  Raises OSError when it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise OSError(f"{LIB_PATH} is not built: run python -m sparse_attention_decode_csa2_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "csa2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "csa2_version": (ctypes.c_int, []),
+        "csa2_quantize_fp4": (ctypes.c_int, [P, I64, I32, P, I32, P, P, P, I64, I64, P]),
+        "csa2_index_full": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I64, P, P]),
+        "csa2_index_pool": (ctypes.c_int, [P, P, P, P, P, P, I32, I32, I32, I64, I32, I32, P, P, P]),
+        "csa2_topk_workspace_bytes": (SZ, [I32, I64, I32]),
+        "csa2_topk": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P, SZ, P]),
+        "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "csa2_sparse_attn_fp4": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I32, I64, F, P, P,
+                                                P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def declared_functions():
+    """Names of the functions include/csa2.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int|size_t)\s+(csa2_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status):
+    return load().csa2_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, st):
+    if st != 0:
+        raise Csa2Error(fn, st)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor")
+
+
+# ------------------------------------------------------------------ a0
+
+
+def csa2_quantize_fp4(x, codes, scales, dst_row0=0, rope_src=None, rope_dst=None):
+    """Quantise bf16 rows x [R, d_c] into rows [dst_row0, dst_row0+R) of the
+    FP4 cache (codes u8 [cap, d_c/2], scales u8 [cap, d_c/16]); copies the
+    RoPE part rope_src [R, d_r] into rope_dst [cap, d_r] when given."""
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    R, d_c = x.shape
+    d_r = 0 if rope_src is None else rope_src.shape[1]
+    st = lib.csa2_quantize_fp4(_ptr(x), R, d_c, _ptr(rope_src), d_r, _ptr(codes), _ptr(scales),
+                               _ptr(rope_dst), int(dst_row0), codes.shape[0], _stream())
+    _check("csa2_quantize_fp4", st)
+    return codes, scales
+
+
+# ------------------------------------------------------------------ a1 / a2
+
+
+def csa2_index_full(q_idx, k_idx, scores=None, w=None, n_valid=None):
+    """Full-mode indexer scores [B, N_cap] (f32)."""
+    lib = load()
+    B, H_I, D_I = q_idx.shape
+    N_cap = k_idx.shape[1]
+    if scores is None:
+        scores = torch.empty(B, N_cap, dtype=torch.float32, device=k_idx.device)
+    st = lib.csa2_index_full(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(n_valid), B, H_I, D_I, N_cap,
+                             _ptr(scores), _stream())
+    _check("csa2_index_full", st)
+    return scores
+
+
+def csa2_index_pool(q_idx, k_idx, pool_blocks, n_blocks, block=8, scores=None, positions=None, w=None,
+                    n_valid=None):
+    """Reindex-mode pool scores and global positions, both [B, P_max*block]."""
+    lib = load()
+    B, H_I, D_I = q_idx.shape
+    N_cap = k_idx.shape[1]
+    P_max = pool_blocks.shape[1]
+    M = P_max * block
+    if scores is None:
+        scores = torch.empty(B, M, dtype=torch.float32, device=k_idx.device)
+    if positions is None:
+        positions = torch.empty(B, M, dtype=torch.int32, device=k_idx.device)
+    st = lib.csa2_index_pool(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(n_valid), _ptr(pool_blocks),
+                             _ptr(n_blocks), B, H_I, D_I, N_cap, P_max, block, _ptr(scores),
+                             _ptr(positions), _stream())
+    _check("csa2_index_pool", st)
+    return scores, positions
+
+
+# ------------------------------------------------------------------ a3
+
+
+def csa2_topk_workspace_bytes(B, M, K):
+    return int(load().csa2_topk_workspace_bytes(B, M, K))
+
+
+def csa2_topk(scores, K, ids=None, n_valid=None, out_idx=None, out_score=None, workspace=None,
+              want_score=True):
+    """Top-K (score desc, id asc): returns (idx i32 [B, K], score f32 [B, K] or None)."""
+    lib = load()
+    B, M = scores.shape
+    dev = scores.device
+    if out_idx is None:
+        out_idx = torch.empty(B, K, dtype=torch.int32, device=dev)
+    if out_score is None and want_score:
+        out_score = torch.empty(B, K, dtype=torch.float32, device=dev)
+    need = csa2_topk_workspace_bytes(B, M, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.csa2_topk(_ptr(scores), _ptr(ids), _ptr(n_valid), B, M, K, _ptr(out_idx), _ptr(out_score),
+                       _ptr(workspace), ws_bytes, _stream())
+    _check("csa2_topk", st)
+    return out_idx, out_score
+
+
+# ------------------------------------------------------------------ a4 / a5
+
+
+def csa2_sparse_attn_workspace_bytes(B, H, d_c, K):
+    return int(load().csa2_sparse_attn_workspace_bytes(B, H, d_c, K))
+
+
+def csa2_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, lse=None, workspace=None,
+                         want_lse=True):
+    """Sparse attention over the selected FP4 entries: returns (out f32 [B, H, d_c], lse f32 [B, H])."""
+    lib = load()
+    B, H, D = q.shape
+    N_cap = codes.shape[1]
+    d_c = codes.shape[2] * 2
+    d_r = D - d_c
+    K = idx.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, H, d_c, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    need = csa2_sparse_attn_workspace_bytes(B, H, d_c, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.csa2_sparse_attn_fp4(_ptr(q), _ptr(codes), _ptr(scales), _ptr(rope if d_r > 0 else None),
+                                  _ptr(idx), K, B, H, d_c, d_r, N_cap, float(sm_scale), _ptr(out), _ptr(lse),
+                                  _ptr(workspace), ws_bytes, _stream())
+    _check("csa2_sparse_attn_fp4", st)
+    return out, lse

@@ -1,0 +1,140 @@
+// extern "C" boundary of libcsa2: host-side validation, then the launches.
+// Nothing here allocates device memory or synchronises.
+#include "../../include/csa2.h"
+#include "csa2_internal.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool opt_aligned16(const void* p) { return p == nullptr || aligned16(p); }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+inline hipStream_t as_stream(csa2_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_NULL: return "a required pointer is NULL";
+    case CSA2_ERR_SHAPE: return "a size is negative or inconsistent";
+    case CSA2_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case CSA2_ERR_RANGE: return "a value is out of its allowed range";
+    case CSA2_ERR_UNSUPPORTED: return "dimensions without a compiled kernel";
+    case CSA2_ERR_HIP: return "the HIP runtime refused a launch";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int csa2_version(void) { return 100; }
+
+int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
+                      int32_t d_r, uint8_t* codes, uint8_t* scales, uint16_t* rope_dst,
+                      int64_t dst_row0, int64_t capacity, csa2_stream_t stream) {
+  if (n_rows < 0 || capacity < 0 || d_c < 32 || d_c > 4096 || d_c % 32 != 0 || d_r < 0 ||
+      d_r > 1024 || d_r % 8 != 0)
+    return CSA2_ERR_SHAPE;
+  if (dst_row0 < 0 || dst_row0 > capacity || n_rows > capacity - dst_row0) return CSA2_ERR_RANGE;
+  if (n_rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales || (d_r > 0 && (!rope_src || !rope_dst))) return CSA2_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !opt_aligned16(rope_src) ||
+      !opt_aligned16(rope_dst))
+    return CSA2_ERR_ALIGN;
+  return hip_status(csa2::launch_quantize_fp4(x, n_rows, d_c, d_r > 0 ? rope_src : nullptr, d_r,
+                                              codes, scales, d_r > 0 ? rope_dst : nullptr, dst_row0,
+                                              as_stream(stream)));
+}
+
+static int check_index_common(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                              const int32_t* n_valid, int32_t B, int32_t H_I, int32_t D_I,
+                              int64_t N_cap, const float* scores) {
+  if (B < 0 || N_cap < 0) return CSA2_ERR_SHAPE;
+  if (H_I < 1 || H_I > 16 || (D_I != 32 && D_I != 64 && D_I != 128 && D_I != 256))
+    return CSA2_ERR_UNSUPPORTED;
+  if (!q_idx || !k_idx || !scores) return CSA2_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(scores) || !opt_aligned16(w) ||
+      !opt_aligned16(n_valid))
+    return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
+
+int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                    const int32_t* n_valid, int32_t B, int32_t H_I, int32_t D_I, int64_t N_cap,
+                    float* scores, csa2_stream_t stream) {
+  if (B == 0 || N_cap == 0) {
+    if (B < 0 || N_cap < 0) return CSA2_ERR_SHAPE;
+    return CSA2_OK;
+  }
+  const int st = check_index_common(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, scores);
+  if (st != CSA2_OK) return st;
+  return hip_status(csa2::launch_index(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, nullptr,
+                                       nullptr, 0, 1, scores, nullptr, as_stream(stream)));
+}
+
+int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                    const int32_t* n_valid, const int32_t* pool_blocks, const int32_t* n_blocks,
+                    int32_t B, int32_t H_I, int32_t D_I, int64_t N_cap, int32_t P_max, int32_t block,
+                    float* scores, int32_t* positions, csa2_stream_t stream) {
+  if (B < 0 || N_cap < 0 || P_max < 1) return CSA2_ERR_SHAPE;
+  if (block < 1 || block > 64 || (int64_t)P_max * block > (1 << 24)) return CSA2_ERR_RANGE;
+  if (B == 0) return CSA2_OK;
+  const int st = check_index_common(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, scores);
+  if (st != CSA2_OK) return st;
+  if (!pool_blocks || !n_blocks || !positions) return CSA2_ERR_NULL;
+  if (!aligned16(pool_blocks) || !aligned16(n_blocks) || !aligned16(positions)) return CSA2_ERR_ALIGN;
+  return hip_status(csa2::launch_index(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, pool_blocks,
+                                       n_blocks, P_max, block, scores, positions,
+                                       as_stream(stream)));
+}
+
+size_t csa2_topk_workspace_bytes(int32_t B, int64_t M, int32_t K) {
+  if (B <= 0 || M < 1 || K < 1 || K > 2048) return 0;
+  return csa2::topk_workspace_bytes(B, M, K);
+}
+
+int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, int32_t B, int64_t M,
+              int32_t K, int32_t* out_idx, float* out_score, void* workspace,
+              size_t workspace_bytes, csa2_stream_t stream) {
+  if (B < 0 || M < 1 || M > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
+  if (K < 1 || K > 2048) return CSA2_ERR_RANGE;
+  if (B == 0) return CSA2_OK;
+  if (!scores || !out_idx) return CSA2_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(out_idx) || !opt_aligned16(ids) || !opt_aligned16(n_valid) ||
+      !opt_aligned16(out_score))
+    return CSA2_ERR_ALIGN;
+  const size_t need = csa2::topk_workspace_bytes(B, M, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;
+  return hip_status(csa2::launch_topk(scores, ids, n_valid, B, M, K, out_idx, out_score, workspace,
+                                      as_stream(stream)));
+}
+
+size_t csa2_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t K) {
+  if (B <= 0 || H < 1 || H > 128 || K < 1 || d_c < 1) return 0;
+  return csa2::attn_workspace_bytes(B, H, d_c, K);
+}
+
+int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                         const uint16_t* rope, const int32_t* idx, int32_t K, int32_t B, int32_t H,
+                         int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale, float* out,
+                         float* lse, void* workspace, size_t workspace_bytes,
+                         csa2_stream_t stream) {
+  if (B < 0 || K < 1 || N_cap < 0) return CSA2_ERR_SHAPE;
+  if (!((d_c == 128 || d_c == 512) && (d_r == 0 || d_r == 64)) || H < 1 || H > 128)
+    return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!q || !codes || !scales || !idx || !out || (d_r > 0 && !rope)) return CSA2_ERR_NULL;
+  if (!aligned16(q) || !aligned16(codes) || !aligned16(scales) || !aligned16(idx) ||
+      !aligned16(out) || !opt_aligned16(rope) || !opt_aligned16(lse))
+    return CSA2_ERR_ALIGN;
+  const size_t need = csa2::attn_workspace_bytes(B, H, d_c, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;
+  return hip_status(csa2::launch_sparse_attn(q, codes, scales, d_r > 0 ? rope : nullptr, idx, K, B,
+                                             H, d_c, d_r, N_cap, sm_scale, out, lse, workspace,
+                                             as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Internal launch entry points of libcsa2 (host side).  Each returns the HIP
+// error of its launches; arguments are validated by csa2_api.hip beforehand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+hipError_t launch_quantize_fp4(const uint16_t* x, int64_t n_rows, int d_c, const uint16_t* rope_src,
+                               int d_r, uint8_t* codes, uint8_t* scales, uint16_t* rope_dst,
+                               int64_t dst_row0, hipStream_t stream);
+
+hipError_t launch_index(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* n_valid,
+                        int B, int H_I, int D_I, int64_t N_cap, const int32_t* pool,
+                        const int32_t* n_blocks, int P_max, int block, float* scores,
+                        int32_t* positions, hipStream_t stream);
+
+size_t topk_workspace_bytes(int B, int64_t M, int K);
+hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, int B,
+                       int64_t M, int K, int32_t* out_idx, float* out_score, void* workspace,
+                       hipStream_t stream);
+
+size_t attn_workspace_bytes(int B, int H, int d_c, int K);
+hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                              const uint16_t* rope, const int32_t* idx, int K, int B, int H, int d_c,
+                              int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,
+                              void* workspace, hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,156 @@
+// a1 / a2: indexer scoring (Full mode over every entry, Reindex mode over the
+// candidate pool).
+//
+// score[b, n] = sum_h w[b, h] * max(0, q_idx[b, h, :] . k_idx[b, n, :])
+// ([P1] 架构三件套 - CSA2 and Hierarchical Sparse Indexer; [P4] CSA2 paragraph;
+// the ReLU-gated multi-head form is the reading documented in the header).
+//
+// The multi-head q . K contraction runs on the matrix cores: one
+// v_mfma_f32_16x16x32_bf16 per 32 key dimensions computes a 16 (heads, padded
+// with zero rows) x 16 (keys) tile.  Each lane streams 16*KS contiguous bytes of
+// one key (lane = key (l % 16), quarter (l / 16) of the key's dimensions), so a
+// wave reads 16 whole keys (16 x 2*D_I bytes, contiguous in Full mode, two
+// 8-entry runs per tile in pool mode) with 16-byte loads.  The k-dimension of
+// the MFMA is permuted identically for q and the keys, which leaves the dot
+// products unchanged.  The epilogue applies ReLU and the head weights and
+// reduces the four head quarters across lane groups.
+//
+// HBM-bound: 2*D_I bytes of key per scored entry against 4*H_I*D_I flops
+// (8 flop/byte at H_I = 8): the matrix cores only have to keep up with HBM.
+#include "csa2_device.h"
+#include "csa2_internal.h"
+
+namespace csa2 {
+
+template <int KS, int TPW, bool POOL>
+__global__ __launch_bounds__(256) void index_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
+    const int32_t* __restrict__ n_valid, int H_I, int64_t N_cap, const int32_t* __restrict__ pool,
+    const int32_t* __restrict__ n_blocks, int P_max, int block, int64_t M, int64_t wg_per_row,
+    float* __restrict__ scores, int32_t* __restrict__ positions) {
+  constexpr int D_I = 32 * KS;
+  constexpr int LANE_DIMS = 8 * KS;  // contiguous key dims owned by one lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t b = blockIdx.x / wg_per_row;
+  const int64_t wg = blockIdx.x - b * wg_per_row;
+
+  // A operand: indexer query head n (rows >= H_I are zero), dims of quarter g
+  bf16x8 A[KS];
+  {
+    const uint16_t* qrow = q + (b * H_I + n) * D_I + g * LANE_DIMS;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (n < H_I) v = *reinterpret_cast<const u32x4*>(qrow + 8 * s);
+      A[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // weights of the four heads whose dot products this lane receives
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    wv[i] = h < H_I ? (w ? w[b * H_I + h] : 1.0f) : 0.0f;
+  }
+  int64_t nv = N_cap;
+  if (n_valid) nv = min<int64_t>(max<int64_t>(n_valid[b], 0), N_cap);
+  int nb = 0;
+  if (POOL) nb = min(max(n_blocks[b], 0), P_max);
+
+  const int64_t tile0 = (wg * 4 + wave) * TPW;
+  u32x4 Bv[TPW][KS];
+  int64_t pos[TPW];
+  bool ok[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int64_t col = (tile0 + t) * 16 + n;
+    int64_t p = col;
+    bool valid;
+    if (POOL) {
+      const int64_t i = col / block;
+      const int j = (int)(col - i * block);
+      const int64_t blk = (col < M && i < nb) ? (int64_t)pool[b * P_max + i] : -1;
+      p = blk * block + j;
+      valid = blk >= 0 && p < nv;
+    } else {
+      valid = col < nv;
+    }
+    pos[t] = p;
+    ok[t] = valid;
+    const uint16_t* krow = k + (b * N_cap + (valid ? p : 0)) * D_I + g * LANE_DIMS;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (valid) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + 8 * s));
+      Bv[t][s] = v;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mfma16x16x32_bf16(A[s], __builtin_bit_cast(bf16x8, Bv[t][s]), acc);
+    // acc[i] = dot(head 4g + i, key n of this tile)
+    float part = wv[0] * fmaxf(acc[0], 0.f);
+    part += wv[1] * fmaxf(acc[1], 0.f);
+    part += wv[2] * fmaxf(acc[2], 0.f);
+    part += wv[3] * fmaxf(acc[3], 0.f);
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    const int64_t col = (tile0 + t) * 16 + n;
+    if (g == 0 && col < M) {
+      scores[b * M + col] = ok[t] ? part : -INFINITY;
+      if (POOL) positions[b * M + col] = ok[t] ? (int32_t)pos[t] : -1;
+    }
+  }
+}
+
+template <int KS, bool POOL>
+static hipError_t launch_index_ks(const uint16_t* q, const float* w, const uint16_t* k,
+                                  const int32_t* n_valid, int B, int H_I, int64_t N_cap,
+                                  const int32_t* pool, const int32_t* n_blocks, int P_max, int block,
+                                  int64_t M, float* scores, int32_t* positions, hipStream_t stream) {
+  const int64_t tiles_per_row = (M + 15) / 16;
+  const int64_t total_tiles = tiles_per_row * B;
+  // enough workgroups to fill 256 CUs several times over; more tiles per wave
+  // (loads issued back to back) once the grid is large
+  int tpw = 1;
+  if (total_tiles >= 4 * 4 * 4096) tpw = 4;
+  else if (total_tiles >= 2 * 4 * 2048) tpw = 2;
+  const int64_t wg_per_row = (tiles_per_row + 4 * tpw - 1) / (4 * tpw);
+  const dim3 grid((unsigned)(wg_per_row * B)), blk(256);
+#define CSA2_IDX_LAUNCH(T)                                                                          \
+  hipLaunchKernelGGL((index_kernel<KS, T, POOL>), grid, blk, 0, stream, q, w, k, n_valid, H_I, N_cap, \
+                     pool, n_blocks, P_max, block, M, wg_per_row, scores, positions)
+  if (tpw == 4) CSA2_IDX_LAUNCH(4);
+  else if (tpw == 2) CSA2_IDX_LAUNCH(2);
+  else CSA2_IDX_LAUNCH(1);
+#undef CSA2_IDX_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_index(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* n_valid,
+                        int B, int H_I, int D_I, int64_t N_cap, const int32_t* pool,
+                        const int32_t* n_blocks, int P_max, int block, float* scores,
+                        int32_t* positions, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const bool is_pool = pool != nullptr;
+  const int64_t M = is_pool ? (int64_t)P_max * block : N_cap;
+  if (M == 0) return hipSuccess;
+#define CSA2_IDX_KS(KS)                                                                              \
+  return is_pool ? launch_index_ks<KS, true>(q, w, k, n_valid, B, H_I, N_cap, pool, n_blocks, P_max, \
+                                             block, M, scores, positions, stream)                    \
+                 : launch_index_ks<KS, false>(q, w, k, n_valid, B, H_I, N_cap, pool, n_blocks, P_max, \
+                                              block, M, scores, positions, stream)
+  switch (D_I) {
+    case 32: CSA2_IDX_KS(1);
+    case 64: CSA2_IDX_KS(2);
+    case 128: CSA2_IDX_KS(4);
+    case 256: CSA2_IDX_KS(8);
+    default: return hipErrorInvalidValue;
+  }
+#undef CSA2_IDX_KS
+}
+
+}  // namespace csa2

@@ -1,0 +1,107 @@
+"""The C-ABI library loads and exports every declared symbol; host-side
+argument validation returns its status before anything reaches the GPU
+(these calls never launch, so they run without one)."""
+
+import ctypes
+import os
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+from sparse_attention_decode_csa2_amd import csa2  # noqa: E402
+
+OK, NULL, SHAPE, ALIGN, RANGE, UNSUP, HIP, WS = range(8)
+A = ctypes.c_void_p(0x1000)      # 16-byte aligned fake device address (never dereferenced)
+U = ctypes.c_void_p(0x1004)      # misaligned
+N = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return csa2.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = csa2.declared_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert csa2.status_string(s)
+    assert csa2.status_string(99) == "unknown status"
+    assert lib.csa2_version() >= 100
+
+
+def test_quantize_validation(lib):
+    f = lib.csa2_quantize_fp4
+    assert f(A, -1, 512, N, 0, A, A, N, 0, 10, N) == SHAPE
+    assert f(A, 4, 500, N, 0, A, A, N, 0, 10, N) == SHAPE
+    assert f(A, 4, 512, N, 12, A, A, N, 0, 10, N) == SHAPE
+    assert f(A, 4, 512, N, 0, A, A, N, 8, 10, N) == RANGE
+    assert f(A, 4, 512, N, 0, A, A, N, -1, 10, N) == RANGE
+    assert f(A, 0, 512, N, 0, A, A, N, 10, 10, N) == OK      # empty append at the end: no-op
+    assert f(N, 4, 512, N, 0, A, A, N, 0, 10, N) == NULL
+    assert f(A, 4, 512, N, 64, A, A, N, 0, 10, N) == NULL
+    assert f(U, 4, 512, N, 0, A, A, N, 0, 10, N) == ALIGN
+
+
+def test_index_validation(lib):
+    f = lib.csa2_index_full
+    assert f(A, N, A, N, 0, 8, 128, 100, A, N) == OK          # B == 0: nothing to do
+    assert f(A, N, A, N, 1, 8, 128, 0, A, N) == OK            # empty cache
+    assert f(A, N, A, N, -1, 8, 128, 100, A, N) == SHAPE
+    assert f(A, N, A, N, 1, 17, 128, 100, A, N) == UNSUP
+    assert f(A, N, A, N, 1, 8, 96, 100, A, N) == UNSUP
+    assert f(N, N, A, N, 1, 8, 128, 100, A, N) == NULL
+    assert f(A, U, A, N, 1, 8, 128, 100, A, N) == ALIGN
+    g = lib.csa2_index_pool
+    assert g(A, N, A, N, A, A, 1, 8, 128, 100, 0, 8, A, A, N) == SHAPE
+    assert g(A, N, A, N, A, A, 1, 8, 128, 100, 2048, 0, A, A, N) == RANGE
+    assert g(A, N, A, N, A, A, 1, 8, 128, 100, 2048, 65, A, A, N) == RANGE
+    assert g(A, N, A, N, N, A, 1, 8, 128, 100, 2048, 8, A, A, N) == NULL
+    assert g(A, N, A, N, A, A, 1, 8, 128, 100, 2048, 8, A, N, N) == NULL
+
+
+def test_topk_validation(lib):
+    f = lib.csa2_topk
+    assert f(A, N, N, 1, 100, 0, A, N, N, 0, N) == RANGE
+    assert f(A, N, N, 1, 100, 2049, A, N, N, 0, N) == RANGE
+    assert f(A, N, N, 1, 0, 8, A, N, N, 0, N) == SHAPE
+    assert f(A, N, N, -1, 100, 8, A, N, N, 0, N) == SHAPE
+    assert f(A, N, N, 0, 100, 8, A, N, N, 0, N) == OK
+    assert f(N, N, N, 1, 100, 8, A, N, N, 0, N) == NULL
+    assert f(A, U, N, 1, 100, 8, A, N, N, 0, N) == ALIGN
+    need = lib.csa2_topk_workspace_bytes(2, 40000, 512)
+    assert need == 2 * 3 * 512 * 8
+    assert lib.csa2_topk_workspace_bytes(2, 16384, 512) == 0
+    assert f(A, N, N, 2, 40000, 512, A, N, N, 0, N) == WS
+    assert f(A, N, N, 2, 40000, 512, A, N, A, need - 1, N) == WS
+
+
+def test_attn_validation(lib):
+    f = lib.csa2_sparse_attn_fp4
+    args = dict(q=A, codes=A, scales=A, rope=A, idx=A, K=512, B=1, H=64, d_c=512, d_r=64, N=100,
+                sm=0.04, out=A, lse=N, ws=A, wsb=1 << 30, st=N)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["q"], a["codes"], a["scales"], a["rope"], a["idx"], a["K"], a["B"], a["H"], a["d_c"],
+                 a["d_r"], a["N"], ctypes.c_float(a["sm"]), a["out"], a["lse"], a["ws"], a["wsb"], a["st"])
+    assert call(B=0) == OK
+    assert call(K=0) == SHAPE
+    assert call(d_c=256) == UNSUP
+    assert call(d_r=32) == UNSUP
+    assert call(H=129) == UNSUP
+    assert call(q=N) == NULL
+    assert call(rope=N) == NULL
+    assert call(out=U) == ALIGN
+    need = lib.csa2_sparse_attn_workspace_bytes(1, 64, 512, 512)
+    assert need > 0
+    assert call(ws=N) == WS
+    assert call(wsb=need - 4) == WS
+    assert lib.csa2_sparse_attn_workspace_bytes(128, 64, 512, 512) == 0

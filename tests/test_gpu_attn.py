@@ -1,0 +1,107 @@
+"""a4 + a5 csa2_sparse_attn_fp4 on the GPU against the oracle (normwise 2e-3
+per (b, h) row, lse to 1e-3), over raw random caches and edge-case index lists."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, W, attn_close, csa2, note, np_bits, oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _raw_cache(wl, B, N):
+    codes = torch.empty(B, N, wl.d_c // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(B, N, wl.d_c // 16, dtype=torch.uint8, device=DEV)
+    for b in range(B):
+        c, s = W.random_codes(wl, b, N, DEV)
+        codes[b], scales[b] = c, s
+    rope = torch.stack([W.rope_rows(wl, b, N, DEV) for b in range(B)]) if wl.d_r else \
+        torch.zeros(B, N, 0, dtype=torch.bfloat16, device=DEV)
+    return codes, scales, rope
+
+
+def _check(wl, B, N, idx, q=None, tol=2e-3):
+    codes, scales, rope = _raw_cache(wl, B, N)
+    if q is None:
+        q = W.attn_query(wl.scaled(B=B), DEV)
+    idx_t = torch.from_numpy(np.asarray(idx, dtype=np.int32)).to(DEV)
+    out, lse = csa2.csa2_sparse_attn_fp4(q, codes, scales, rope, idx_t, wl.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attn(np_bits(q), codes.cpu().numpy(), scales.cpu().numpy(), np_bits(rope),
+                                np.asarray(idx), wl.sm_scale)
+    return attn_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol)
+
+
+def _rand_idx(rng, B, K, N):
+    return np.stack([np.sort(rng.permutation(N)[:K]) for _ in range(B)])
+
+
+@pytest.mark.parametrize("wi,B,N", [(0, 1, 1024), (1, 1, 16384), (1, 3, 4096), (3, 40, 2048), (3, 130, 1024)])
+def test_attention_workload_shapes(wi, B, N):
+    wl = W.WORKLOADS[wi]
+    note(f"attn: {wl.name} B={B} N={N} K={wl.K} H={wl.H} d_c={wl.d_c} d_r={wl.d_r}")
+    rng = np.random.default_rng(B + N)
+    _check(wl, B, N, _rand_idx(rng, B, wl.K, N))
+
+
+@pytest.mark.parametrize("K", [1, 5, 63, 64, 65, 200, 1000])
+def test_attention_ragged_k(K):
+    wl = W.WORKLOADS[1]
+    note(f"attn: ragged K={K}")
+    rng = np.random.default_rng(K)
+    _check(wl, 2, 2048, _rand_idx(rng, 2, K, 2048))
+
+
+def test_attention_masked_duplicate_and_empty_rows():
+    wl = W.WORKLOADS[1]
+    note("attn: masked ids, duplicates, empty rows")
+    rng = np.random.default_rng(5)
+    N = 1024
+    idx = _rand_idx(rng, 4, 512, N)
+    idx[0, ::7] = -1
+    idx[1, ::5] = N + 3            # past the cache: skipped
+    idx[2, 100:300] = idx[2, 0]    # repeated entry
+    idx[3, :] = -1                 # nothing valid
+    _check(wl, 4, N, idx)
+
+
+@pytest.mark.parametrize("H", [1, 8, 17, 64, 128])
+def test_attention_head_counts(H):
+    wl = W.WORKLOADS[1].scaled(H=H)
+    note(f"attn: H={H}")
+    rng = np.random.default_rng(H)
+    _check(wl, 2, 1024, _rand_idx(rng, 2, 512, 1024))
+
+
+@pytest.mark.parametrize("dc,dr", [(512, 0), (128, 64)])
+def test_attention_other_dims(dc, dr):
+    wl = W.WORKLOADS[1].scaled(d_c=dc, d_r=dr)
+    note(f"attn: d_c={dc} d_r={dr}")
+    rng = np.random.default_rng(dc + dr)
+    _check(wl, 2, 1024, _rand_idx(rng, 2, 512, 1024))
+
+
+def test_attention_query_magnitudes():
+    wl = W.WORKLOADS[1].scaled(H=16)
+    note("attn: zero / huge / tiny query heads")
+    rng = np.random.default_rng(9)
+    q = W.attn_query(wl.scaled(B=1), DEV).float()
+    q[0, 0] = 0
+    q[0, 1] *= 3000.0
+    q[0, 2] *= 1e-30
+    q[0, 3, :512] = 0            # only the RoPE part
+    q[0, 4, 512:] = 0            # only the latent part
+    _check(wl, 1, 2048, _rand_idx(rng, 1, 512, 2048), q=q.to(torch.bfloat16))
+
+
+def test_attention_on_quantized_cache_is_dense_attention_when_k_is_n():
+    wl = W.WORKLOADS[0]
+    note("attn: tiny cache built by csa2_quantize_fp4, Top-K = every entry")
+    from gpu_util import Cache, oracle_attention_rows
+    cache = Cache(wl)
+    q = W.attn_query(wl, DEV)
+    idx = torch.arange(wl.N, dtype=torch.int32, device=DEV)[None]
+    out, lse = csa2.csa2_sparse_attn_fp4(q, cache.codes, cache.scales, cache.rope, idx, wl.sm_scale)
+    ro, rl = oracle_attention_rows(cache, 0, np_bits(q)[0], idx.cpu().numpy()[0], wl.sm_scale)
+    attn_close(out.cpu().numpy()[0], lse.cpu().numpy()[0], ro, rl)
