@@ -117,3 +117,45 @@ def test_prefill_write_then_full_decode_1m():
         return full if rows is None else full[np.asarray(rows)]
     cache.latents_host, cache.rope_host = lat0, rope0
     _check_full(wl, cache, _keys(wl, wl.B), W.index_query(wl, DEV), W.attn_query(wl, DEV), (0, 7))
+
+
+def test_full_step_in_a_hip_graph_matches_eager():
+    """The Full-mode step captured into a HIP graph and replayed several times,
+    with eager work in between, reproduces the eager result bit for bit."""
+    wl = W.WORKLOADS[1]
+    note("decode full: HIP graph capture + 3 replays vs eager")
+    cache = Cache(wl)
+    k = _keys(wl, 1)
+    qi = W.index_query(wl, DEV)
+    q = W.attn_query(wl, DEV)
+    sc = torch.empty(1, wl.N, dtype=torch.float32, device=DEV)
+    idx = torch.empty(1, wl.K, dtype=torch.int32, device=DEV)
+    top = torch.empty(1, wl.K, dtype=torch.float32, device=DEV)
+    out = torch.empty(1, wl.H, wl.d_c, dtype=torch.float32, device=DEV)
+    lse = torch.empty(1, wl.H, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(csa2.csa2_sparse_attn_workspace_bytes(1, wl.H, wl.d_c, wl.K), 16),
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        csa2.csa2_index_full(qi, k, scores=sc)
+        csa2.csa2_topk(sc, wl.K, out_idx=idx, out_score=top)
+        csa2.csa2_sparse_attn_fp4(q, cache.codes, cache.scales, cache.rope, idx, wl.sm_scale, out=out,
+                                  lse=lse, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (sc, idx, top, out, lse)]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(3):
+        for t in (sc, idx, top, out, lse):
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((sc, idx, top, out, lse), ref):
+            assert torch.equal(a, b), rep
+        # eager work between replays
+        csa2.csa2_index_full(qi, k)
+        torch.cuda.synchronize()
