@@ -66,73 +66,152 @@ def committed_traffic(kernel_file, workload):
     return rec.get("bytes_per_launch")
 
 
-class FullStep:
-    """Full-mode decode over R rotating input sets (B sequences each)."""
+def _entry_bytes(wl):
+    """Algorithmic bytes of one cache entry (codes + scales + RoPE part)."""
+    return wl.d_c // 2 + wl.d_c // 16 + 2 * wl.d_r
 
-    def __init__(self, wl, R, dev):
+
+class Step:
+    """One decode step of a workload over R rotating input sets.
+
+    Full (tiny-full, full-64k): index -> topk -> attn, each set its own caches.
+    Reindex (reindex-1m): pool -> topk -> attn over one cache; sets = pools + queries.
+    Reuse (reuse-128k): attn over one cache; sets = index lists + queries.
+    Prefill + Full (prefill-full-1m): quantize (append 8192 rows) -> index -> topk -> attn.
+    """
+
+    def __init__(self, wl, dev, rotation_bytes=ROTATION_BYTES):
         import torch
         from sparse_attention_decode_csa2_amd import csa2
         from sparse_attention_decode_csa2_amd import workloads as W
-        self.wl, self.R, self.csa2 = wl, R, csa2
+        self.wl, self.csa2, self.W, self.dev = wl, csa2, W, dev
         B, N = wl.B, wl.N
-        self.sets = []
-        for r in range(R):
-            ws = wl.scaled(seed=wl.seed * 1000 + r)
-            keys = torch.stack([W.index_keys(ws, b, dev) for b in range(B)])
-            codes = torch.empty(B, N, wl.d_c // 2, dtype=torch.uint8, device=dev)
-            scales = torch.empty(B, N, wl.d_c // 16, dtype=torch.uint8, device=dev)
-            rope = torch.empty(B, N, wl.d_r, dtype=torch.bfloat16, device=dev)
-            for b in range(B):
-                lat = W.latent_rows(ws, b, N, dev)
-                rp = W.rope_rows(ws, b, N, dev) if wl.d_r else None
-                csa2.csa2_quantize_fp4(lat, codes[b], scales[b], 0, rp, rope[b] if wl.d_r else None)
-            self.sets.append(dict(ws=ws, keys=keys, codes=codes, scales=scales, rope=rope,
-                                  qi=W.index_query(ws, dev), q=W.attn_query(ws, dev)))
-        self.scores = torch.empty(B, N, dtype=torch.float32, device=dev)
+        self.mode = wl.mode
+        if self.mode == "full":
+            per_set = B * N * (wl.D_I * 2 + _entry_bytes(wl))
+            self.R = max(2, math.ceil(rotation_bytes / per_set))
+            self.sets = [self._full_set(wl.scaled(seed=wl.seed * 1000 + r)) for r in range(self.R)]
+        else:
+            self.cache = self._cache(wl)
+            if self.mode in ("reindex", "prefill_full"):
+                self.keys = torch.stack([W.index_keys(wl, b, dev) for b in range(B)])
+            touched = {"reindex": B * (wl.n_blocks * wl.block * wl.D_I * 2 + wl.K * _entry_bytes(wl)),
+                       "reuse": B * wl.K * _entry_bytes(wl),
+                       "prefill_full": B * N * wl.D_I * 2}[self.mode]
+            self.R = max(2, math.ceil(rotation_bytes / touched))
+            self.sets = []
+            for r in range(self.R):
+                ws = wl.scaled(seed=wl.seed * 1000 + r)
+                st = {"q": W.attn_query(ws, dev)}
+                if self.mode == "reindex":
+                    st["pool"], st["nb"] = W.pool_blocks(ws, dev)
+                if self.mode in ("reindex", "prefill_full"):
+                    st["qi"] = W.index_query(ws, dev)
+                if self.mode == "reuse":
+                    st["idx"] = W.reuse_index(ws, dev)
+                self.sets.append(st)
+            if self.mode == "prefill_full":
+                self.chunk = W.prefill_chunk(wl, dev)
+                self.chunk_rope = W.prefill_rope(wl, dev)
+        M = {"full": N, "prefill_full": N, "reindex": wl.P_max * wl.block, "reuse": 0}[self.mode]
+        self.M = M
+        self.scores = torch.empty(B, max(M, 1), dtype=torch.float32, device=dev)
+        self.positions = torch.empty(B, max(M, 1), dtype=torch.int32, device=dev)
         self.idx = torch.empty(B, wl.K, dtype=torch.int32, device=dev)
         self.top = torch.empty(B, wl.K, dtype=torch.float32, device=dev)
         self.out = torch.empty(B, wl.H, wl.d_c, dtype=torch.float32, device=dev)
         self.lse = torch.empty(B, wl.H, dtype=torch.float32, device=dev)
-        tk = csa2.csa2_topk_workspace_bytes(B, N, wl.K)
+        tk = csa2.csa2_topk_workspace_bytes(B, M, wl.K) if M else 0
         at = csa2.csa2_sparse_attn_workspace_bytes(B, wl.H, wl.d_c, wl.K)
         self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
         self.ws_attn = torch.empty(max(at, 16), dtype=torch.uint8, device=dev) if at else None
+        self.stages = {"full": ["index", "topk", "attn"], "reindex": ["pool", "topk", "attn"],
+                       "reuse": ["attn"], "prefill_full": ["quantize", "index", "topk", "attn"]}[self.mode]
+        if self.mode == "reuse":
+            self.idx = None
 
-    def bytes_per_set(self):
-        s = self.sets[0]
-        return sum(t.numel() * t.element_size() for t in (s["keys"], s["codes"], s["scales"], s["rope"]))
+    def _cache(self, ws):
+        import torch
+        W, csa2, dev = self.W, self.csa2, self.dev
+        B, N = ws.B, ws.N
+        codes, scales, rope = csa2.alloc_cache(B, N, ws.d_c, ws.d_r, dev)
+        for b in range(B):
+            lat = W.latent_rows(ws, b, N, dev)
+            rp = W.rope_rows(ws, b, N, dev) if ws.d_r else None
+            csa2.csa2_quantize_fp4(lat, codes[b], scales[b], 0, rp, rope[b] if ws.d_r else None)
+            del lat, rp
+        return {"codes": codes, "scales": scales, "rope": rope}
 
-    # the three stages; `ev` optionally records events around each
+    def _full_set(self, ws):
+        import torch
+        W, dev = self.W, self.dev
+        st = self._cache(ws)
+        st["keys"] = torch.stack([W.index_keys(ws, b, dev) for b in range(ws.B)])
+        st["qi"] = W.index_query(ws, dev)
+        st["q"] = W.attn_query(ws, dev)
+        return st
+
+    def _kv(self, r):
+        return self.sets[r] if self.mode == "full" else self.cache
+
+    def _keys(self, r):
+        return self.sets[r]["keys"] if self.mode == "full" else self.keys
+
+    # ---- stages
+    def quantize(self, r):
+        c, wl = self.cache, self.wl
+        self.csa2.csa2_quantize_fp4(self.chunk, c["codes"][0], c["scales"][0], wl.prefill_row0,
+                                    self.chunk_rope, c["rope"][0])
+
     def index(self, r):
-        s = self.sets[r]
-        self.csa2.csa2_index_full(s["qi"], s["keys"], scores=self.scores)
+        self.csa2.csa2_index_full(self.sets[r]["qi"], self._keys(r), scores=self.scores)
+
+    def pool(self, r):
+        st = self.sets[r]
+        self.csa2.csa2_index_pool(st["qi"], self.keys, st["pool"], st["nb"], block=self.wl.block,
+                                  scores=self.scores, positions=self.positions)
 
     def topk(self, r):
-        self.csa2.csa2_topk(self.scores, self.wl.K, out_idx=self.idx, out_score=self.top,
+        ids = self.positions if self.mode == "reindex" else None
+        self.csa2.csa2_topk(self.scores, self.wl.K, ids=ids, out_idx=self.idx, out_score=self.top,
                             workspace=self.ws_topk)
 
     def attn(self, r):
-        s = self.sets[r]
-        self.csa2.csa2_sparse_attn_fp4(s["q"], s["codes"], s["scales"], s["rope"], self.idx,
+        kv, st = self._kv(r), self.sets[r]
+        idx = st["idx"] if self.mode == "reuse" else self.idx
+        self.csa2.csa2_sparse_attn_fp4(st["q"], kv["codes"], kv["scales"], kv["rope"], idx,
                                        self.wl.sm_scale, out=self.out, lse=self.lse,
                                        workspace=self.ws_attn)
 
     def step(self, r):
-        self.index(r)
-        self.topk(r)
-        self.attn(r)
+        for s in self.stages:
+            getattr(self, s)(r)
 
     def alg_bytes(self):
-        """Algorithmic bytes: inputs read once, outputs written once."""
+        """Algorithmic bytes per launch of each stage and per step: inputs read
+        once, outputs written once."""
         wl = self.wl
-        B, N, K = wl.B, wl.N, wl.K
-        entry = wl.d_c // 2 + wl.d_c // 16 + 2 * wl.d_r
-        index = B * (N * wl.D_I * 2 + wl.H_I * wl.D_I * 2 + N * 4)
-        topk = B * (N * 4 + K * 8)
-        attn = B * (K * 4 + K * entry + wl.H * wl.D * 2 + wl.H * wl.d_c * 4 + wl.H * 4)
-        step = B * (N * wl.D_I * 2 + wl.H_I * wl.D_I * 2 + K * entry + wl.H * wl.D * 2
-                    + wl.H * wl.d_c * 4 + wl.H * 4 + K * 4)
-        return {"index": index, "topk": topk, "attn": attn, "step": step}
+        B, N, K, H = wl.B, wl.N, wl.K, wl.H
+        ent = _entry_bytes(wl)
+        qi = wl.H_I * wl.D_I * 2
+        attn = B * (K * 4 + K * ent + H * wl.D * 2 + H * wl.d_c * 4 + H * 4)
+        d = {"attn": attn}
+        step = attn
+        if self.mode in ("full", "prefill_full"):
+            d["index"] = B * (N * wl.D_I * 2 + qi + N * 4)
+            d["topk"] = B * (N * 4 + K * 8)
+            step += B * (N * wl.D_I * 2 + qi)
+        if self.mode == "reindex":
+            Mp = wl.P_max * wl.block
+            d["pool"] = B * (wl.n_blocks * wl.block * wl.D_I * 2 + qi + wl.P_max * 4 + Mp * 8)
+            d["topk"] = B * (Mp * 8 + K * 8)
+            step += B * (wl.n_blocks * wl.block * wl.D_I * 2 + qi + wl.n_blocks * 4)
+        if self.mode == "prefill_full":
+            R = wl.prefill_rows
+            d["quantize"] = R * (wl.d_c * 2 + wl.d_r * 2) + R * (wl.d_c // 2 + wl.d_c // 16 + wl.d_r * 2)
+            step += d["quantize"]
+        d["step"] = step
+        return d
 
 
 def cpu_baseline(wl, budget_s):
@@ -178,16 +257,10 @@ def main():
         sys.exit(1)
     wl = W.BY_NAME[args.workload]
     dev = "cuda"
-    if wl.mode != "full":
-        raise SystemExit(f"--workload {args.workload}: only Full-mode workloads are wired into bench.py")
-    # size the rotation so one pass over the sets touches >= 1 GiB
-    probe = FullStep(wl, 1, dev)
-    R = max(2, math.ceil(ROTATION_BYTES / probe.bytes_per_set()))
-    del probe
-    step = FullStep(wl, R, dev)
+    step = Step(wl, dev)
+    R = step.R
     torch.cuda.synchronize()
-    print(f"[bench] {wl.name}: {R} input sets x {step.bytes_per_set() / 2**20:.1f} MiB", file=sys.stderr,
-          flush=True)
+    print(f"[bench] {wl.name}: mode {wl.mode}, {R} rotating input sets", file=sys.stderr, flush=True)
 
     # The host cannot enqueue a ~10 us step through Python faster than the GPU
     # runs it, so steps are captured into HIP graphs and replayed: one graph of
@@ -209,7 +282,7 @@ def main():
     torch.cuda.synchronize()
     g_warm = capture(step.step, max(args.warmup, 1))
     g_timed = capture(step.step, args.steps)
-    stages = ["index", "topk", "attn"]
+    stages = step.stages
     g_stage = {s: capture(getattr(step, s), args.steps) for s in stages}
 
     def timed(g):
@@ -233,7 +306,8 @@ def main():
     stage_us = {s: 1000.0 * timed(g_stage[s]) / args.steps for s in stages}
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
-    kernel_file = {"index": "index.hip", "topk": "topk.hip", "attn": "attn.hip"}[dom]
+    kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
+                   "quantize": "quantize.hip"}[dom]
     achieved = alg[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = committed_traffic(kernel_file, wl.name)
 
@@ -263,11 +337,12 @@ def main():
         "step_hbm_gbs": alg["step"] / (ms_per_step * 1e-3) / 1e9,
         "step_alg_bytes": alg["step"],
         "stage_us": {s: round(v, 3) for s, v in stage_us.items()},
+        "stage_gbs": {s: round(alg[s] / (stage_us[s] * 1e-6) / 1e9, 1) for s in stages},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": alg[dom]},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.mode == "full":
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

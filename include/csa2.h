@@ -21,8 +21,9 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; tensors are
- *    dense row-major with the shapes given; every tensor pointer must be
- *    16-byte aligned.  bf16 values are passed as raw uint16_t bit patterns.
+ *    dense row-major with the shapes given (the FP4 cache alone takes row
+ *    strides); every tensor pointer must be 16-byte aligned unless stated.
+ *    bf16 values are passed as raw uint16_t bit patterns.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *    enqueues work on that stream and returns; nothing synchronises.
  *  - Arguments are validated on the host before anything is launched; a
@@ -51,7 +52,7 @@ typedef enum {
   CSA2_OK = 0,
   CSA2_ERR_NULL = 1,        /* a required pointer is NULL */
   CSA2_ERR_SHAPE = 2,       /* a size is negative or inconsistent */
-  CSA2_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  CSA2_ERR_ALIGN = 3,       /* a pointer or stride breaks its alignment rule */
   CSA2_ERR_RANGE = 4,       /* append past capacity, K out of [1, 2048], ... */
   CSA2_ERR_UNSUPPORTED = 5, /* dimensions without a compiled kernel */
   CSA2_ERR_HIP = 6,         /* the HIP runtime refused a launch */
@@ -72,11 +73,17 @@ int csa2_version(void);
  * x        bf16 [n_rows, d_c]   post-RoPE latent rows (RoPE is applied by the
  *                               caller; this call does not rotate)
  * rope_src bf16 [n_rows, d_r]   RoPE part, copied unchanged (NULL iff d_r == 0)
- * codes    u8  [capacity, d_c/2]  cache: byte j of a row = channel 2j (low
- *                                 nibble) | channel 2j+1 (high nibble)
- * scales   u8  [capacity, d_c/16] cache: E4M3 scale of channels [16g, 16g+16)
- * rope_dst bf16 [capacity, d_r]   cache RoPE part (NULL iff d_r == 0)
- * Rows [dst_row0, dst_row0 + n_rows) of the three caches are written.
+ * codes    u8   cache rows of d_c/2 bytes: byte j = channel 2j (low nibble) |
+ *                 channel 2j+1 (high nibble); row r at codes + r * codes_stride
+ * scales   u8   cache rows of d_c/16 E4M3 bytes (byte g scales channels
+ *                 [16g, 16g+16)); row r at scales + r * scales_stride
+ * rope_dst bf16 cache rows of d_r values; row r at rope_dst + r * rope_stride
+ *                 bytes (NULL iff d_r == 0)
+ * Strides are in bytes; 0 means dense rows.  The three regions may be three
+ * arrays or share one buffer of fixed-size entry records (the layout the
+ * attention gather reads fastest: one contiguous record per entry, e.g.
+ * 512 bytes = codes at 0, scales at d_c/2, RoPE at d_c/2 + d_c/16).
+ * Rows [dst_row0, dst_row0 + n_rows) are written.
  *
  * Per group of 16 channels: scale = the E4M3 value nearest to max|x| / 6
  * (ties to the even code, saturating at 448 = 0x7E); each element's code is
@@ -85,11 +92,14 @@ int csa2_version(void);
  * Bit-exact with the oracle for all finite inputs; codes for non-finite
  * inputs are unspecified (but written, in bounds).
  * Requires d_c % 32 == 0, 32 <= d_c <= 4096, d_r % 8 == 0, d_r <= 1024,
- * n_rows >= 0, 0 <= dst_row0, dst_row0 + n_rows <= capacity.
+ * n_rows >= 0, 0 <= dst_row0, dst_row0 + n_rows <= capacity, x / codes /
+ * rope pointers and codes / rope strides multiples of 16, scales pointer and
+ * stride even, each stride at least its row width.
  */
 int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c,
                       const uint16_t* rope_src, int32_t d_r,
-                      uint8_t* codes, uint8_t* scales, uint16_t* rope_dst,
+                      uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                      uint16_t* rope_dst, int64_t rope_stride,
                       int64_t dst_row0, int64_t capacity, csa2_stream_t stream);
 
 /*
@@ -98,9 +108,10 @@ int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c,
  * [P4] CSA2 paragraph (Full produces its own KV and Top-K).  The pages give
  * no formula; the reading implemented is
  *   score[b, n] = sum_h w[b, h] * max(0, q_idx[b, h, :] . k_idx[b, n, :])
- * (ReLU-gated indexer heads, one key per entry shared by all heads), summed
- * over h in increasing order in fp32 after an exact-order-free fp32 dot
- * (bf16 products accumulated in fp32 by the matrix cores).
+ * (ReLU-gated indexer heads, one key per entry shared by all heads): bf16
+ * products accumulated in fp32 by the matrix cores, then the weighted head
+ * terms summed in fp32 (heads 4j..4j+3 in order, then the four partial sums
+ * pairwise).
  *
  * q_idx   bf16 [B, H_I, D_I]
  * w       f32  [B, H_I]  per-head weights, or NULL for all ones
@@ -172,8 +183,9 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
  * value_j = dequant(latent_j), shared by all H query heads.
  *
  * q      bf16 [B, H, d_c + d_r]
- * codes  u8   [B, N_cap, d_c/2]   scales u8 [B, N_cap, d_c/16]
- * rope   bf16 [B, N_cap, d_r]     (NULL iff d_r == 0)
+ * codes / scales / rope   the cache of csa2_quantize_fp4 (same row strides, 0 =
+ *        dense), B sequences of N_cap rows each: entry n of sequence b is row
+ *        b * N_cap + n; rope is NULL iff d_r == 0
  * idx    i32  [B, K]  selected entries; ids < 0 or >= N_cap are skipped,
  *                     repeated ids count with multiplicity
  * out    f32  [B, H, d_c]  softmax(sm_scale * q . key) . value
@@ -184,11 +196,13 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
  * softmax runs in fp32: the error against an exact evaluation is < 2e-3 of
  * max|out| per (b, h) row for unit-scale inputs.
  * Requires d_c in {128, 512}, d_r in {0, 64}, 1 <= H <= 128, K >= 1, B >= 0,
- * and a workspace of csa2_sparse_attn_workspace_bytes(B, H, d_c, K) bytes.
+ * the alignment rules of csa2_quantize_fp4 for the cache, and a workspace of
+ * csa2_sparse_attn_workspace_bytes(B, H, d_c, K) bytes.
  */
 size_t csa2_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t K);
-int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                         const uint16_t* rope, const int32_t* idx, int32_t K, int32_t B,
+int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
+                         const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
+                         int64_t rope_stride, const int32_t* idx, int32_t K, int32_t B,
                          int32_t H, int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale,
                          float* out, float* lse, void* workspace, size_t workspace_bytes,
                          csa2_stream_t stream);

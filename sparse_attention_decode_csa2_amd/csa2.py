@@ -41,14 +41,14 @@ def load():
     sig = {
         "csa2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "csa2_version": (ctypes.c_int, []),
-        "csa2_quantize_fp4": (ctypes.c_int, [P, I64, I32, P, I32, P, P, P, I64, I64, P]),
+        "csa2_quantize_fp4": (ctypes.c_int, [P, I64, I32, P, I32, P, I64, P, I64, P, I64, I64, I64, P]),
         "csa2_index_full": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I64, P, P]),
         "csa2_index_pool": (ctypes.c_int, [P, P, P, P, P, P, I32, I32, I32, I64, I32, I32, P, P, P]),
         "csa2_topk_workspace_bytes": (SZ, [I32, I64, I32]),
         "csa2_topk": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
-        "csa2_sparse_attn_fp4": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I32, I64, F, P, P,
-                                                P, SZ, P]),
+        "csa2_sparse_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I64,
+                                                F, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -87,21 +87,63 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor")
 
 
+# ------------------------------------------------------------------ the FP4 cache
+
+
+def _row_stride(t, elem_bytes, name):
+    """Byte distance between consecutive rows of a (possibly strided) cache view;
+    rows of all sequences must be evenly spaced."""
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the channel dimension must be contiguous")
+    rs = t.stride(-2)
+    if t.dim() == 3 and t.shape[0] > 1 and t.stride(0) != t.shape[1] * rs:
+        raise ValueError(f"{name}: sequences must be evenly spaced rows")
+    return rs * elem_bytes
+
+
+def alloc_cache(B, N, d_c, d_r, device="cuda", layout="record"):
+    """Allocates an FP4 cache for B sequences of N entries; returns (codes,
+    scales, rope) views [B, N, *] (rope is [B, N, 0] when d_r == 0).
+
+    layout "record": one buffer of fixed-size entry records, codes | RoPE |
+    scales, record size the next power of two >= d_c/2 + 2*d_r + d_c/16 (512
+    bytes for d_c = 512, d_r = 64): the attention gather then reads one
+    contiguous record per entry.  layout "separate": three dense arrays.
+    """
+    cb, rb, sb = d_c // 2, 2 * d_r, d_c // 16
+    if layout == "separate":
+        codes = torch.empty(B, N, cb, dtype=torch.uint8, device=device)
+        scales = torch.empty(B, N, sb, dtype=torch.uint8, device=device)
+        rope = torch.empty(B, N, d_r, dtype=torch.bfloat16, device=device)
+        return codes, scales, rope
+    rec = 1
+    while rec < cb + rb + sb:
+        rec *= 2
+    buf = torch.empty(B, N, rec, dtype=torch.uint8, device=device)
+    codes = buf[:, :, :cb]
+    rope = buf[:, :, cb:cb + rb].view(torch.bfloat16)
+    scales = buf[:, :, cb + rb:cb + rb + sb]
+    return codes, scales, rope
+
+
 # ------------------------------------------------------------------ a0
 
 
 def csa2_quantize_fp4(x, codes, scales, dst_row0=0, rope_src=None, rope_dst=None):
-    """Quantise bf16 rows x [R, d_c] into rows [dst_row0, dst_row0+R) of the
-    FP4 cache (codes u8 [cap, d_c/2], scales u8 [cap, d_c/16]); copies the
-    RoPE part rope_src [R, d_r] into rope_dst [cap, d_r] when given."""
+    """Quantise bf16 rows x [R, d_c] into rows [dst_row0, dst_row0+R) of one
+    sequence's FP4 cache (codes u8 [cap, d_c/2], scales u8 [cap, d_c/16] and
+    rope_dst bf16 [cap, d_r], possibly strided views of one record buffer);
+    copies the RoPE part rope_src [R, d_r] when given."""
     lib = load()
     _need(x, torch.bfloat16, "x")
-    _need(codes, torch.uint8, "codes")
-    _need(scales, torch.uint8, "scales")
     R, d_c = x.shape
     d_r = 0 if rope_src is None else rope_src.shape[1]
-    st = lib.csa2_quantize_fp4(_ptr(x), R, d_c, _ptr(rope_src), d_r, _ptr(codes), _ptr(scales),
-                               _ptr(rope_dst), int(dst_row0), codes.shape[0], _stream())
+    cs = _row_stride(codes, 1, "codes")
+    ss = _row_stride(scales, 1, "scales")
+    rs = _row_stride(rope_dst, 2, "rope_dst") if d_r else 0
+    st = lib.csa2_quantize_fp4(_ptr(x), R, d_c, _ptr(rope_src), d_r, _ptr(codes), cs, _ptr(scales), ss,
+                               _ptr(rope_dst if d_r else None), rs, int(dst_row0), codes.shape[-2],
+                               _stream())
     _check("csa2_quantize_fp4", st)
     return codes, scales
 
@@ -177,7 +219,9 @@ def csa2_sparse_attn_workspace_bytes(B, H, d_c, K):
 
 def csa2_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, lse=None, workspace=None,
                          want_lse=True):
-    """Sparse attention over the selected FP4 entries: returns (out f32 [B, H, d_c], lse f32 [B, H])."""
+    """Sparse attention over the selected FP4 entries of the cache (codes,
+    scales, rope: [B, N_cap, *] views as from alloc_cache): returns
+    (out f32 [B, H, d_c], lse f32 [B, H])."""
     lib = load()
     B, H, D = q.shape
     N_cap = codes.shape[1]
@@ -195,8 +239,11 @@ def csa2_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, l
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.csa2_sparse_attn_fp4(_ptr(q), _ptr(codes), _ptr(scales), _ptr(rope if d_r > 0 else None),
-                                  _ptr(idx), K, B, H, d_c, d_r, N_cap, float(sm_scale), _ptr(out), _ptr(lse),
-                                  _ptr(workspace), ws_bytes, _stream())
+    cs = _row_stride(codes, 1, "codes")
+    ss = _row_stride(scales, 1, "scales")
+    rs = _row_stride(rope, 2, "rope") if d_r > 0 else 0
+    st = lib.csa2_sparse_attn_fp4(_ptr(q), _ptr(codes), cs, _ptr(scales), ss,
+                                  _ptr(rope if d_r > 0 else None), rs, _ptr(idx), K, B, H, d_c, d_r, N_cap,
+                                  float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream())
     _check("csa2_sparse_attn_fp4", st)
     return out, lse

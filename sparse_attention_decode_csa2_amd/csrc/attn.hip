@@ -26,20 +26,43 @@
 namespace csa2 {
 
 constexpr int AT_TILE = 64;
+constexpr int AT_IDS = 512;  // entry ids one workgroup handles (8 tiles)
+constexpr int AT_IDS_PAD = AT_IDS + 2 * AT_TILE;  // + two tiles of -1 for the look-ahead loads
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-// E2M1 nibble -> fp32 value (sign included), exact.
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t k = c & 7u;
-  float v = k >= 2 ? __uint_as_float((k << 22) + 0x3F000000u) : 0.5f * (float)k;
-  return __uint_as_float(__float_as_uint(v) | ((c & 8u) << 28));
+// Value of lane (lane ^ 16) / (lane ^ 32) through the permlane swaps.
+__device__ __forceinline__ uint32_t xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float xor16f(float v) { return __uint_as_float(xor16(__float_as_uint(v))); }
+__device__ __forceinline__ float xor32f(float v) { return __uint_as_float(xor32(__float_as_uint(v))); }
+
+// Transposing LDS read (ds_read_b64_tr_b16): see the PV step below.
+__device__ __forceinline__ f16x4 tr16_read(const _Float16* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(f16x4, v);
 }
 
 template <int DC, int DR>
-__global__ __launch_bounds__(256) void sparse_attn_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const uint16_t* __restrict__ rope,
+struct GatherRegs {
+  static constexpr int NCW = DC / 2 / 4 / 16;       // 16-byte code words per quarter entry
+  static constexpr int RW = DR > 0 ? DR / 4 / 8 : 1;  // 16-byte RoPE words per quarter entry
+  u32x4 cw[NCW];
+  uint16_t sb[NCW];  // the two scale bytes of each code word
+  u32x4 rw[RW];
+  bool valid;
+};
+
+template <int DC, int DR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
+    const uint16_t* __restrict__ q, const CacheRef cache,
     const int32_t* __restrict__ idx, int K, int H, int64_t N_cap, float sm_scale_log2e, int n_hg,
     int n_split, int per_split, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
@@ -47,15 +70,16 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   constexpr int KSR = DR / 32;           // RoPE k-steps
   constexpr int LDK = DC + 8;            // fp16 pitch of the latent tile
   constexpr int LDR = DR + 8;            // bf16 pitch of the RoPE tile
-  constexpr int CB = DC / 2;             // code bytes per entry
-  constexpr int GPE = DC / 16;           // scale bytes per entry
-  constexpr int QCH = DC / 4;            // latent channels per gather thread / per PV wave
+  constexpr int QCH = DC / 4;            // latent channels per PV wave
   constexpr int NDB = QCH / 16;          // PV d-blocks per wave
+  using GR = GatherRegs<DC, DR>;
+  constexpr int NCW = GR::NCW;
   __shared__ __attribute__((aligned(16))) _Float16 sK[AT_TILE][LDK];
   __shared__ __attribute__((aligned(16))) __bf16 sR[AT_TILE][DR > 0 ? LDR : 8];
   __shared__ __attribute__((aligned(16))) _Float16 sP[16][AT_TILE + 8];
   __shared__ float sMax[4][16], sSum[4][16], sAlpha[16], sFinM[16], sFinL[16];
   __shared__ int sValid[AT_TILE];
+  __shared__ int32_t sIdx[AT_IDS_PAD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -65,122 +89,122 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   const int hg = bid % n_hg;
   const int64_t b = bid / n_hg;
   const int h0 = hg * 16;
+  const int e_begin = split * per_split;
+  const int e_end = min(K, e_begin + per_split);
+  const int32_t* idx_row = idx + b * K;
+  const int er = tid >> 2, part = tid & 3;  // gather: entry row of the tile, quarter
+  // an empty slice or cache: no loads at all, the epilogue writes the empty result
+  const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
 
-  // ---- query heads h0 + n as MFMA B operands (k-step t, k-group g -> dims 32t + 8g .. +7)
+  // The vector-memory counter retires loads in order and the compiler can
+  // only wait for "all but the last n", so every load below is issued
+  // unconditionally, in the order its data is needed: entry ids, query heads,
+  // then the look-ahead tiles.
+  // ---- the slice's entry ids (at most AT_IDS, then -1 padding) go to LDS once
+  static_assert(AT_IDS % 256 == 0 && AT_IDS_PAD - AT_IDS <= 256, "id staging layout");
+  int32_t ids[AT_IDS / 256];
+#pragma unroll
+  for (int k = 0; k < AT_IDS / 256; ++k) {
+    const int e = e_begin + tid + 256 * k;
+    ids[k] = idx_row[min(e, max(e_end - 1, 0))];
+  }
+  // ---- query heads h0 + n as MFMA B operands (k-step t, k-group g -> dims
+  // 32t + 8g .. +7)
   f16x8 Bq[KSL];
   bf16x8 Br[KSR > 0 ? KSR : 1];
   float fscale;  // multiplies the MFMA result into base-2 softmax logits for head h0 + n
+  const bool hv = h0 + n < H;
+  u32x4 qraw[KSL + KSR];
   {
-    const int h = h0 + n;
-    const bool hv = h < H;
-    const uint16_t* qrow = q + (b * H + (hv ? h : 0)) * (DC + DR);
-    u32x4 raw[KSL + KSR];
-    uint32_t mx = 0;
+    const uint16_t* qrow = q + (b * H + (hv ? h0 + n : 0)) * (DC + DR);
 #pragma unroll
     for (int t = 0; t < KSL + KSR; ++t) {
       const int off = t < KSL ? 32 * t + 8 * g : DC + 32 * (t - KSL) + 8 * g;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hv) v = *reinterpret_cast<const u32x4*>(qrow + off);
-      raw[t] = v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mx = max(mx, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
-    }
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
-    // 2^sh brings the largest |q| of the head into [2^14, 2^15): fp16 keeps all
-    // of a bf16 value's bits there; bf16 subnormals are treated as exponent -126
-    int e = (int)((mx >> 7) & 0xFF) - 127;
-    if (e < -126) e = -126;
-    int sh = mx == 0 ? 0 : min(120, max(-120, 14 - e));
-    const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
-    fscale = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
-#pragma unroll
-    for (int t = 0; t < KSL; ++t) {
-      f16x8 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = (_Float16)(bf16_bits_to_f32(raw[t][j] & 0xFFFFu) * up);
-        v[2 * j + 1] = (_Float16)(bf16_bits_to_f32(raw[t][j] >> 16) * up);
-      }
-      Bq[t] = v;
-    }
-#pragma unroll
-    for (int t = 0; t < KSR; ++t) {
-      bf16x8 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = (__bf16)(bf16_bits_to_f32(raw[KSL + t][j] & 0xFFFFu) * up);
-        v[2 * j + 1] = (__bf16)(bf16_bits_to_f32(raw[KSL + t][j] >> 16) * up);
-      }
-      Br[t] = v;
+      qraw[t] = *reinterpret_cast<const u32x4*>(qrow + off);
     }
   }
+#pragma unroll
+  for (int k = 0; k < AT_IDS / 256; ++k) {
+    const int j = tid + 256 * k;
+    sIdx[j] = e_begin + j < e_end ? ids[k] : -1;
+  }
+  if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
+  __syncthreads();
+
+  // ---- gather: thread (er, part) fetches, for code word i, bytes
+  // [16 part + 64 i, +16) of entry er (channels 32 part + 128 i .. +31), so the
+  // four threads of an entry read whole 64-byte segments; plus the two scale
+  // bytes of those channels and a quarter of the RoPE part.  Loads are
+  // unconditional (a skipped entry reads row 0 of its sequence) so they issue
+  // back to back; the scale of a skipped entry is zeroed when it is used.
+  auto gather = [&](GR& gr, int tile) {
+    // pinned in program order: a load hoisted above the previous tile's work
+    // lands in registers that are still in flight and forces a full wait
+    __builtin_amdgcn_sched_barrier(0);
+    const int32_t id = sIdx[tile * AT_TILE + er];
+    gr.valid = id >= 0 && (int64_t)id < N_cap;
+    const int64_t row = b * N_cap + (gr.valid ? id : 0);
+    const uint8_t* cp = cache.codes + row * cache.codes_stride + 16 * part;
+    const uint8_t* sp = cache.scales + row * cache.scales_stride + 2 * part;
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) {
+      gr.cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp + 64 * i));
+      gr.sb[i] = *reinterpret_cast<const uint16_t*>(sp + 8 * i);
+    }
+    if constexpr (DR > 0) {
+      const uint8_t* rp = reinterpret_cast<const uint8_t*>(cache.rope) + row * cache.rope_stride + part * (DR / 2);
+#pragma unroll
+      for (int i = 0; i < GR::RW; ++i) gr.rw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + 16 * i));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   float m_run = -INFINITY, l_run = 0.f;  // per head h0 + n (redundant in every wave)
   f32x4 acc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int e_begin = split * per_split;
-  const int e_end = min(K, e_begin + per_split);
-  const int32_t* idx_row = idx + b * K;
-  const int er = tid >> 2, part = tid & 3;  // gather: entry row, quarter
-
-  for (int tb = e_begin; tb < e_end; tb += AT_TILE) {
-    // ---- 1. gather + dequantise one quarter of entry `er`
-    {
-      const int e = tb + er;
-      const int32_t id = e < e_end ? idx_row[e] : -1;
-      const bool valid = id >= 0 && (int64_t)id < N_cap;
-      const int64_t row = b * N_cap + (valid ? id : 0);
-      u32x4 cw[CB / 4 / 16 > 0 ? CB / 4 / 16 : 1];
-      constexpr int NCW = CB / 4 / 16;  // 16-byte code words per quarter
-      const uint8_t* cp = codes + row * CB + part * (CB / 4);
+  auto process = [&](GR& gr) {
+    // The scale bytes are first used here and nowhere earlier: a use hoisted
+    // into the previous tile's work would wait for loads still in flight.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < NCW; ++i) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (valid) v = *reinterpret_cast<const u32x4*>(cp + 16 * i);
-        cw[i] = v;
-      }
-      uint8_t sb[GPE / 4];
+    for (int i = 0; i < NCW; ++i) asm volatile("" : "+v"(gr.sb[i]));
+    // ---- 1. dequantise the gathered quarter into the LDS tile.  The FP4 pairs
+    // go through the hardware converter with a unit scale; the E4M3 block scale
+    // (exact in fp16) is applied with a packed fp16 multiply, and every product
+    // (<= 6 significant bits, within [2^-10, 2688]) is exact in fp16.
 #pragma unroll
-      for (int i = 0; i < GPE / 4; ++i) sb[i] = valid ? scales[row * GPE + part * (GPE / 4) + i] : 0;
-      // channels part*QCH + 32i + 2j + {0,1} come from byte j of word i
+    for (int i = 0; i < NCW; ++i) {
 #pragma unroll
-      for (int i = 0; i < NCW; ++i) {
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t sbv = gr.valid ? (uint32_t)gr.sb[i] : 0u;  // a skipped entry contributes zeros
+        const _Float16 sg = (_Float16)e4m3_decode((sbv >> (8 * half)) & 0xFFu);
+        const f16x2 s2v = {sg, sg};
+        f16x8 outv[2];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {       // 16 channels = one scale group
-          const float sg = e4m3_decode(sb[2 * i + half]);
-          f16x8 lo, hi;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t word = cw[i][2 * half + (j >> 2)];
-            const uint32_t byte = (word >> (8 * (j & 3))) & 0xFFu;
-            const _Float16 v0 = (_Float16)(e2m1_value(byte & 15u) * sg);
-            const _Float16 v1 = (_Float16)(e2m1_value(byte >> 4) * sg);
-            if (j < 4) { lo[2 * j] = v0; lo[2 * j + 1] = v1; }
-            else { hi[2 * (j - 4)] = v0; hi[2 * (j - 4) + 1] = v1; }
-          }
-          _Float16* dst = &sK[er][part * QCH + 32 * i + 16 * half];
-          *reinterpret_cast<f16x8*>(dst) = lo;
-          *reinterpret_cast<f16x8*>(dst + 8) = hi;
+        for (int dw = 0; dw < 2; ++dw) {
+          const uint32_t word = gr.cw[i][2 * half + dw];
+          const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * s2v;
+          const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * s2v;
+          const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * s2v;
+          const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * s2v;
+          outv[dw] = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
         }
+        _Float16* dst = &sK[er][32 * part + 128 * i + 16 * half];
+        *reinterpret_cast<f16x8*>(dst) = outv[0];
+        *reinterpret_cast<f16x8*>(dst + 8) = outv[1];
       }
-      if (DR > 0) {
-        constexpr int RW = DR / 4 / 8;  // 16-byte RoPE words per quarter
-        const uint16_t* rp = rope + row * DR + part * (DR / 4);
-#pragma unroll
-        for (int i = 0; i < RW; ++i) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (valid) v = *reinterpret_cast<const u32x4*>(rp + 8 * i);
-          *reinterpret_cast<u32x4*>(&sR[er][part * (DR / 4) + 8 * i]) = v;
-        }
-      }
-      if (part == 0) sValid[er] = valid;
     }
+    if constexpr (DR > 0) {
+#pragma unroll
+      for (int i = 0; i < GR::RW; ++i) *reinterpret_cast<u32x4*>(&sR[er][part * (DR / 4) + 8 * i]) = gr.rw[i];
+    }
+    if (part == 0) sValid[er] = gr.valid;
     __syncthreads();
 
-    // ---- 2. S^T for entries 16*wave + (0..15): lane (entry n, k-group g) supplies A
+    // ---- 2. S^T for entries 16*wave + (0..15): lane (entry n, k-group g)
+    // supplies A from the tile
     float s2[4];
     {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -201,8 +225,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     }
     // ---- 3. online softmax for head n (lanes n, n+16, n+32, n+48 hold its 16 entries)
     float mt = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = fmaxf(mt, xor16f(mt));
+    mt = fmaxf(mt, xor32f(mt));
     if (g == 0) sMax[wave][n] = mt;
     __syncthreads();
     const float m_tile = fmaxf(fmaxf(sMax[0][n], sMax[1][n]), fmaxf(sMax[2][n], sMax[3][n]));
@@ -214,20 +238,23 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
       p[i] = s2[i] == -INFINITY ? 0.f : exp2f(s2[i] - m_new);
       ps += p[i];
     }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    ps += xor16f(ps);
+    ps += xor32f(ps);
     if (g == 0) sSum[wave][n] = ps;
     if (wave == 0 && g == 0) sAlpha[n] = alpha;
     {
       _Float16* prow = &sP[n][16 * wave + 4 * g];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) prow[i] = (_Float16)p[i];
+      *reinterpret_cast<f16x4*>(prow) = f16x4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
     }
     __syncthreads();
     l_run = l_run * alpha + (sSum[0][n] + sSum[1][n] + sSum[2][n] + sSum[3][n]);
     m_run = m_new;
 
-    // ---- 4. O[heads][channels of this wave] = alpha * O + P . V
+    // ---- 4. O[heads][channels of this wave] = alpha * O + P . V.  The V
+    // operand (8 consecutive entries of one channel per lane) comes from the
+    // row-major LDS tile through two transposing reads: in each 16-lane group
+    // lane 4r + c points at 4 channels of entry row r, and lane i receives
+    // channel i of the four rows.
     {
       float al[4];
 #pragma unroll
@@ -236,20 +263,79 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
       for (int d = 0; d < NDB; ++d)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[d][i] *= al[i];
+      const int tr_r = n >> 2, tr_c = n & 3;
 #pragma unroll
       for (int u = 0; u < AT_TILE / 32; ++u) {
         const f16x8 a = *reinterpret_cast<const f16x8*>(&sP[n][32 * u + 8 * g]);
 #pragma unroll
         for (int d = 0; d < NDB; ++d) {
-          const int col = wave * QCH + 16 * d + n;
-          f16x8 bv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) bv[i] = sK[32 * u + 8 * g + i][col];
+          const int col = wave * QCH + 16 * d + 4 * tr_c;
+          const f16x4 v0 = tr16_read(&sK[32 * u + 8 * g + tr_r][col]);
+          const f16x4 v1 = tr16_read(&sK[32 * u + 8 * g + 4 + tr_r][col]);
+          const f16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
           acc[d] = mfma16x16x32_f16(a, bv, acc[d]);
         }
       }
     }
     __syncthreads();
+  };
+
+  if (n_tiles > 0) {
+    GR ga, gb;
+    gather(ga, 0);
+    {
+      uint32_t mx = 0;
+#pragma unroll
+      for (int t = 0; t < KSL + KSR; ++t) {
+        if (!hv) qraw[t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = max(mx, max(qraw[t][j] & 0x7FFFu, (qraw[t][j] >> 16) & 0x7FFFu));
+      }
+      mx = max(mx, xor16(mx));
+      mx = max(mx, xor32(mx));
+      // 2^sh brings the largest |q| of the head into [2^14, 2^15): fp16 keeps all
+      // of a bf16 value's bits there; bf16 subnormals are treated as exponent -126
+      int e = (int)((mx >> 7) & 0xFF) - 127;
+      if (e < -126) e = -126;
+      const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - e));
+      const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
+      fscale = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
+#pragma unroll
+      for (int t = 0; t < KSL; ++t) {
+        f16x8 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = (_Float16)(bf16_bits_to_f32(qraw[t][j] & 0xFFFFu) * up);
+          o[2 * j + 1] = (_Float16)(bf16_bits_to_f32(qraw[t][j] >> 16) * up);
+        }
+        Bq[t] = o;
+      }
+#pragma unroll
+      for (int t = 0; t < KSR; ++t) {
+        bf16x8 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = (__bf16)(bf16_bits_to_f32(qraw[KSL + t][j] & 0xFFFFu) * up);
+          o[2 * j + 1] = (__bf16)(bf16_bits_to_f32(qraw[KSL + t][j] >> 16) * up);
+        }
+        Br[t] = o;
+      }
+    }
+    // the second tile's loads go out once the query registers are converted
+    gather(gb, 1);
+
+    // two register sets in flight: while tile t is processed, tiles t+1 and t+2
+    // load.  Past the last tile the padding ids (-1) load row 0 again, which
+    // keeps every load unconditional; the loop has a single exit so that every
+    // path into a process step has the same loads in flight.
+    int t = 0;
+    for (; t + 2 <= n_tiles; t += 2) {
+      process(ga);
+      gather(ga, t + 2);
+      process(gb);
+      gather(gb, t + 3);
+    }
+    if (t < n_tiles) process(ga);
   }
 
   // ---- epilogue: lane (channel n of each d-block, k-group g) holds heads h0 + 4g + i
@@ -283,30 +369,32 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   }
 }
 
-// Merge the per-slice partial results of one (b, h) row by log-sum-exp.
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_o,
+// Merge the per-slice partial results of one (b, h) row by log-sum-exp; each
+// of the 128 threads owns 4 consecutive channels.
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ ws_o,
                                                            const float* __restrict__ ws_ml,
-                                                           int n_split, int DC, int64_t rows,
+                                                           int n_split, int DC,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
   const int64_t row = blockIdx.x;
-  if (row >= rows) return;
   const float* ml = ws_ml + row * n_split * 2;
   float m = -INFINITY;
   for (int s = 0; s < n_split; ++s) m = fmaxf(m, ml[2 * s]);
   float L = 0.f;
   for (int s = 0; s < n_split; ++s) {
     const float ms = ml[2 * s];
-    L += ms == -INFINITY ? 0.f : ml[2 * s + 1] * exp2f(ms - m);
+    L += ms == -INFINITY ? 0.f : exp2f(ms - m) * ml[2 * s + 1];
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  for (int c = threadIdx.x; c < DC; c += blockDim.x) {
-    float o = 0.f;
+  for (int c = threadIdx.x * 4; c < DC; c += 512) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n_split; ++s) {
       const float ms = ml[2 * s];
-      if (ms != -INFINITY) o += ws_o[(row * n_split + s) * DC + c] * exp2f(ms - m);
+      const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - m);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ws_o + (row * n_split + s) * DC + c);
+      o += v * wgt;
     }
-    out[row * DC + c] = o * inv;
+    *reinterpret_cast<f32x4*>(out + row * DC + c) = o * inv;
   }
   if (lse && threadIdx.x == 0) lse[row] = L > 0.f ? (m + __log2f(L)) * LN2 : -INFINITY;
 }
@@ -317,6 +405,7 @@ static void attn_plan(int B, int H, int K, int* n_split, int* per_split) {
   const int tiles = (K + AT_TILE - 1) / AT_TILE;
   const int base = B * n_hg;
   int s = base >= 512 ? 1 : (512 + base - 1) / max(base, 1);
+  s = max(s, (tiles + AT_IDS / AT_TILE - 1) / (AT_IDS / AT_TILE));  // <= 8 tiles per split
   s = max(1, min(s, tiles));
   const int tps = (tiles + s - 1) / s;
   s = (tiles + tps - 1) / tps;
@@ -331,9 +420,8 @@ size_t attn_workspace_bytes(int B, int H, int d_c, int K) {
   return (size_t)B * H * s * ((size_t)d_c + 2) * sizeof(float);
 }
 
-hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                              const uint16_t* rope, const int32_t* idx, int K, int B, int H, int d_c,
-                              int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,
+hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
+                              int d_c, int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,
                               void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   int s, ps;
@@ -344,8 +432,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
   const dim3 grid((unsigned)(B * n_hg * s)), blk(256);
   const float sl = sm_scale * LOG2E;
 #define CSA2_ATTN(DCV, DRV)                                                                     \
-  hipLaunchKernelGGL((sparse_attn_kernel<DCV, DRV>), grid, blk, 0, stream, q, codes, scales, rope, \
-                     idx, K, H, N_cap, sl, n_hg, s, ps, out, lse, ws_o, ws_ml)
+  hipLaunchKernelGGL((sparse_attn_kernel<DCV, DRV>), grid, blk, 0, stream, q, cache, idx, K, H, N_cap, \
+                     sl, n_hg, s, ps, out, lse, ws_o, ws_ml)
   if (d_c == 512 && d_r == 64) CSA2_ATTN(512, 64);
   else if (d_c == 512 && d_r == 0) CSA2_ATTN(512, 0);
   else if (d_c == 128 && d_r == 0) CSA2_ATTN(128, 0);
@@ -354,9 +442,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
 #undef CSA2_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
-  const int64_t rows = (int64_t)B * H;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, stream, ws_o, ws_ml, s,
-                     d_c, rows, out, lse);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)B * H)), dim3(128), 0, stream, ws_o,
+                     ws_ml, s, d_c, out, lse);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ const char* csa2_status_string(int status) {
     case CSA2_OK: return "ok";
     case CSA2_ERR_NULL: return "a required pointer is NULL";
     case CSA2_ERR_SHAPE: return "a size is negative or inconsistent";
-    case CSA2_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case CSA2_ERR_ALIGN: return "a pointer or stride breaks its alignment rule";
     case CSA2_ERR_RANGE: return "a value is out of its allowed range";
     case CSA2_ERR_UNSUPPORTED: return "dimensions without a compiled kernel";
     case CSA2_ERR_HIP: return "the HIP runtime refused a launch";
@@ -30,21 +30,36 @@ const char* csa2_status_string(int status) {
 
 int csa2_version(void) { return 100; }
 
+// Resolves 0 strides to dense rows and checks the cache layout rules.
+static int check_cache(int32_t d_c, int32_t d_r, const void* codes, int64_t& codes_stride,
+                       const void* scales, int64_t& scales_stride, const void* rope, int64_t& rope_stride) {
+  if (codes_stride == 0) codes_stride = d_c / 2;
+  if (scales_stride == 0) scales_stride = d_c / 16;
+  if (rope_stride == 0) rope_stride = 2 * (int64_t)d_r;
+  if (codes_stride < d_c / 2 || scales_stride < d_c / 16 || (d_r > 0 && rope_stride < 2 * (int64_t)d_r))
+    return CSA2_ERR_SHAPE;
+  if (!aligned16(codes) || codes_stride % 16 != 0) return CSA2_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(scales) & 1u) != 0 || scales_stride % 2 != 0) return CSA2_ERR_ALIGN;
+  if (d_r > 0 && (!aligned16(rope) || rope_stride % 16 != 0)) return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
+
 int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
-                      int32_t d_r, uint8_t* codes, uint8_t* scales, uint16_t* rope_dst,
+                      int32_t d_r, uint8_t* codes, int64_t codes_stride, uint8_t* scales,
+                      int64_t scales_stride, uint16_t* rope_dst, int64_t rope_stride,
                       int64_t dst_row0, int64_t capacity, csa2_stream_t stream) {
   if (n_rows < 0 || capacity < 0 || d_c < 32 || d_c > 4096 || d_c % 32 != 0 || d_r < 0 ||
-      d_r > 1024 || d_r % 8 != 0)
+      d_r > 1024 || d_r % 8 != 0 || codes_stride < 0 || scales_stride < 0 || rope_stride < 0)
     return CSA2_ERR_SHAPE;
   if (dst_row0 < 0 || dst_row0 > capacity || n_rows > capacity - dst_row0) return CSA2_ERR_RANGE;
   if (n_rows == 0) return CSA2_OK;
   if (!x || !codes || !scales || (d_r > 0 && (!rope_src || !rope_dst))) return CSA2_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !opt_aligned16(rope_src) ||
-      !opt_aligned16(rope_dst))
-    return CSA2_ERR_ALIGN;
-  return hip_status(csa2::launch_quantize_fp4(x, n_rows, d_c, d_r > 0 ? rope_src : nullptr, d_r,
-                                              codes, scales, d_r > 0 ? rope_dst : nullptr, dst_row0,
-                                              as_stream(stream)));
+  if (!aligned16(x) || !opt_aligned16(rope_src)) return CSA2_ERR_ALIGN;
+  const int st = check_cache(d_c, d_r, codes, codes_stride, scales, scales_stride, rope_dst, rope_stride);
+  if (st != CSA2_OK) return st;
+  const csa2::CacheRef c{codes, codes_stride, scales, scales_stride, d_r > 0 ? rope_dst : nullptr, rope_stride};
+  return hip_status(csa2::launch_quantize_fp4(x, n_rows, d_c, d_r > 0 ? rope_src : nullptr, d_r, c,
+                                              dst_row0, as_stream(stream)));
 }
 
 static int check_index_common(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
@@ -116,25 +131,27 @@ size_t csa2_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32
   return csa2::attn_workspace_bytes(B, H, d_c, K);
 }
 
-int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                         const uint16_t* rope, const int32_t* idx, int32_t K, int32_t B, int32_t H,
+int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
+                         const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
+                         int64_t rope_stride, const int32_t* idx, int32_t K, int32_t B, int32_t H,
                          int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale, float* out,
-                         float* lse, void* workspace, size_t workspace_bytes,
-                         csa2_stream_t stream) {
-  if (B < 0 || K < 1 || N_cap < 0) return CSA2_ERR_SHAPE;
+                         float* lse, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+  if (B < 0 || K < 1 || N_cap < 0 || codes_stride < 0 || scales_stride < 0 || rope_stride < 0)
+    return CSA2_ERR_SHAPE;
   if (!((d_c == 128 || d_c == 512) && (d_r == 0 || d_r == 64)) || H < 1 || H > 128)
     return CSA2_ERR_UNSUPPORTED;
   if (B == 0) return CSA2_OK;
   if (!q || !codes || !scales || !idx || !out || (d_r > 0 && !rope)) return CSA2_ERR_NULL;
-  if (!aligned16(q) || !aligned16(codes) || !aligned16(scales) || !aligned16(idx) ||
-      !aligned16(out) || !opt_aligned16(rope) || !opt_aligned16(lse))
-    return CSA2_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(idx) || !aligned16(out) || !opt_aligned16(lse)) return CSA2_ERR_ALIGN;
+  const int st = check_cache(d_c, d_r, codes, codes_stride, scales, scales_stride, rope, rope_stride);
+  if (st != CSA2_OK) return st;
   const size_t need = csa2::attn_workspace_bytes(B, H, d_c, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;
-  return hip_status(csa2::launch_sparse_attn(q, codes, scales, d_r > 0 ? rope : nullptr, idx, K, B,
-                                             H, d_c, d_r, N_cap, sm_scale, out, lse, workspace,
-                                             as_stream(stream)));
+  const csa2::CacheRef c{const_cast<uint8_t*>(codes), codes_stride, const_cast<uint8_t*>(scales),
+                         scales_stride, d_r > 0 ? const_cast<uint16_t*>(rope) : nullptr, rope_stride};
+  return hip_status(csa2::launch_sparse_attn(q, c, idx, K, B, H, d_c, d_r, N_cap, sm_scale, out, lse,
+                                             workspace, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -8,9 +8,18 @@
 
 namespace csa2 {
 
+// Row strides are in bytes and already resolved (non-zero).
+struct CacheRef {
+  uint8_t* codes;
+  int64_t codes_stride;
+  uint8_t* scales;
+  int64_t scales_stride;
+  uint16_t* rope;
+  int64_t rope_stride;
+};
+
 hipError_t launch_quantize_fp4(const uint16_t* x, int64_t n_rows, int d_c, const uint16_t* rope_src,
-                               int d_r, uint8_t* codes, uint8_t* scales, uint16_t* rope_dst,
-                               int64_t dst_row0, hipStream_t stream);
+                               int d_r, CacheRef cache, int64_t dst_row0, hipStream_t stream);
 
 hipError_t launch_index(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* n_valid,
                         int B, int H_I, int D_I, int64_t N_cap, const int32_t* pool,
@@ -23,9 +32,8 @@ hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n
                        hipStream_t stream);
 
 size_t attn_workspace_bytes(int B, int H, int d_c, int K);
-hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                              const uint16_t* rope, const int32_t* idx, int K, int B, int H, int d_c,
-                              int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,
+hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
+                              int d_c, int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,
                               void* workspace, hipStream_t stream);
 
 }  // namespace csa2

@@ -14,8 +14,7 @@ namespace csa2 {
 
 __global__ __launch_bounds__(256) void quantize_fp4_kernel(
     const uint16_t* __restrict__ x, int64_t n_rows, int d_c, const uint16_t* __restrict__ rope_src,
-    int d_r, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    uint16_t* __restrict__ rope_dst, int64_t dst_row0, int64_t n_groups, int64_t n_rope_chunks) {
+    int d_r, CacheRef cache, int64_t dst_row0, int64_t n_groups, int64_t n_rope_chunks) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid < n_groups) {
     const int gpr = d_c >> 4;                       // groups per row
@@ -45,8 +44,8 @@ __global__ __launch_bounds__(256) void quantize_fp4_kernel(
       packed |= (uint64_t)code << (4 * i);
     }
     const int64_t row = dst_row0 + r;
-    *reinterpret_cast<uint64_t*>(codes + row * (d_c >> 1) + g * 8) = packed;
-    scales[row * gpr + g] = (uint8_t)S;
+    *reinterpret_cast<uint64_t*>(cache.codes + row * cache.codes_stride + g * 8) = packed;
+    cache.scales[row * cache.scales_stride + g] = (uint8_t)S;
   } else if (gid < n_groups + n_rope_chunks) {
     // RoPE part: copied unchanged, 8 bf16 (16 bytes) per thread
     const int64_t c = gid - n_groups;
@@ -54,20 +53,20 @@ __global__ __launch_bounds__(256) void quantize_fp4_kernel(
     const int64_t r = c / cpr;
     const int j = (int)(c - r * cpr);
     const u32x4 v = *reinterpret_cast<const u32x4*>(rope_src + r * d_r + j * 8);
-    *reinterpret_cast<u32x4*>(rope_dst + (dst_row0 + r) * d_r + j * 8) = v;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(cache.rope) + (dst_row0 + r) * cache.rope_stride + j * 16;
+    *reinterpret_cast<u32x4*>(dst) = v;
   }
 }
 
 hipError_t launch_quantize_fp4(const uint16_t* x, int64_t n_rows, int d_c, const uint16_t* rope_src,
-                               int d_r, uint8_t* codes, uint8_t* scales, uint16_t* rope_dst,
-                               int64_t dst_row0, hipStream_t stream) {
+                               int d_r, CacheRef cache, int64_t dst_row0, hipStream_t stream) {
   const int64_t n_groups = n_rows * (d_c / 16);
   const int64_t n_rope = d_r > 0 ? n_rows * (d_r / 8) : 0;
   const int64_t total = n_groups + n_rope;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(quantize_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n_rows,
-                     d_c, rope_src, d_r, codes, scales, rope_dst, dst_row0, n_groups, n_rope);
+                     d_c, rope_src, d_r, cache, dst_row0, n_groups, n_rope);
   return hipGetLastError();
 }
 

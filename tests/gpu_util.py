@@ -33,13 +33,11 @@ class Cache:
     from seeded bf16 latent rows; latents of any sequence can be regenerated
     (same generator, same device) for the oracle."""
 
-    def __init__(self, wl, B=None, device=DEV):
+    def __init__(self, wl, B=None, device=DEV, layout="record"):
         self.wl = wl
         self.B = wl.B if B is None else B
         N, d_c, d_r = wl.N, wl.d_c, wl.d_r
-        self.codes = torch.empty(self.B, N, d_c // 2, dtype=torch.uint8, device=device)
-        self.scales = torch.empty(self.B, N, d_c // 16, dtype=torch.uint8, device=device)
-        self.rope = torch.empty(self.B, N, max(d_r, 0), dtype=torch.bfloat16, device=device)
+        self.codes, self.scales, self.rope = csa2.alloc_cache(self.B, N, d_c, d_r, device, layout)
         for b in range(self.B):
             lat = W.latent_rows(wl, b, N, device)
             rp = W.rope_rows(wl, b, N, device) if d_r > 0 else None

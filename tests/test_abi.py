@@ -38,15 +38,24 @@ def test_status_strings(lib):
 
 def test_quantize_validation(lib):
     f = lib.csa2_quantize_fp4
-    assert f(A, -1, 512, N, 0, A, A, N, 0, 10, N) == SHAPE
-    assert f(A, 4, 500, N, 0, A, A, N, 0, 10, N) == SHAPE
-    assert f(A, 4, 512, N, 12, A, A, N, 0, 10, N) == SHAPE
-    assert f(A, 4, 512, N, 0, A, A, N, 8, 10, N) == RANGE
-    assert f(A, 4, 512, N, 0, A, A, N, -1, 10, N) == RANGE
-    assert f(A, 0, 512, N, 0, A, A, N, 10, 10, N) == OK      # empty append at the end: no-op
-    assert f(N, 4, 512, N, 0, A, A, N, 0, 10, N) == NULL
-    assert f(A, 4, 512, N, 64, A, A, N, 0, 10, N) == NULL
-    assert f(U, 4, 512, N, 0, A, A, N, 0, 10, N) == ALIGN
+
+    def call(x=A, n=4, d_c=512, rs=N, d_r=0, codes=A, cst=0, scales=A, sst=0, rd=N, rst=0, r0=0, cap=10):
+        return f(x, n, d_c, rs, d_r, codes, cst, scales, sst, rd, rst, r0, cap, N)
+    assert call(n=-1) == SHAPE
+    assert call(d_c=500) == SHAPE
+    assert call(d_r=12) == SHAPE
+    assert call(cst=-16) == SHAPE
+    assert call(r0=8) == RANGE
+    assert call(r0=-1) == RANGE
+    assert call(n=0, r0=10) == OK                    # empty append at the end: no-op
+    assert call(x=N) == NULL
+    assert call(d_r=64) == NULL                      # RoPE part without its buffers
+    assert call(x=U) == ALIGN
+    assert call(cst=520) == ALIGN                    # codes stride not a multiple of 16
+    assert call(scales=ctypes.c_void_p(0x1005)) == ALIGN
+    assert call(sst=33) == ALIGN                     # odd scales stride
+    assert call(cst=128) == SHAPE                    # stride narrower than a row
+    assert call(d_r=64, rs=A, rd=ctypes.c_void_p(0x1008), rst=512) == ALIGN
 
 
 def test_index_validation(lib):
@@ -84,22 +93,26 @@ def test_topk_validation(lib):
 
 def test_attn_validation(lib):
     f = lib.csa2_sparse_attn_fp4
-    args = dict(q=A, codes=A, scales=A, rope=A, idx=A, K=512, B=1, H=64, d_c=512, d_r=64, N=100,
-                sm=0.04, out=A, lse=N, ws=A, wsb=1 << 30, st=N)
+    args = dict(q=A, codes=A, cst=512, scales=A, sst=512, rope=A, rst=512, idx=A, K=512, B=1, H=64, d_c=512,
+                d_r=64, N=100, sm=0.04, out=A, lse=N, ws=A, wsb=1 << 30, st=N)
 
     def call(**kw):
         a = dict(args)
         a.update(kw)
-        return f(a["q"], a["codes"], a["scales"], a["rope"], a["idx"], a["K"], a["B"], a["H"], a["d_c"],
-                 a["d_r"], a["N"], ctypes.c_float(a["sm"]), a["out"], a["lse"], a["ws"], a["wsb"], a["st"])
+        return f(a["q"], a["codes"], a["cst"], a["scales"], a["sst"], a["rope"], a["rst"], a["idx"], a["K"],
+                 a["B"], a["H"], a["d_c"], a["d_r"], a["N"], ctypes.c_float(a["sm"]), a["out"], a["lse"],
+                 a["ws"], a["wsb"], a["st"])
     assert call(B=0) == OK
     assert call(K=0) == SHAPE
+    assert call(cst=-1) == SHAPE
     assert call(d_c=256) == UNSUP
     assert call(d_r=32) == UNSUP
     assert call(H=129) == UNSUP
     assert call(q=N) == NULL
     assert call(rope=N) == NULL
     assert call(out=U) == ALIGN
+    assert call(rst=520) == ALIGN
+    assert call(cst=128) == SHAPE
     need = lib.csa2_sparse_attn_workspace_bytes(1, 64, 512, 512)
     assert need > 0
     assert call(ws=N) == WS

@@ -10,26 +10,26 @@ from gpu_util import DEV, W, attn_close, csa2, note, np_bits, oracle
 pytestmark = pytest.mark.gpu
 
 
-def _raw_cache(wl, B, N):
-    codes = torch.empty(B, N, wl.d_c // 2, dtype=torch.uint8, device=DEV)
-    scales = torch.empty(B, N, wl.d_c // 16, dtype=torch.uint8, device=DEV)
+def _raw_cache(wl, B, N, layout="record"):
+    codes, scales, rope = csa2.alloc_cache(B, N, wl.d_c, wl.d_r, DEV, layout)
     for b in range(B):
         c, s = W.random_codes(wl, b, N, DEV)
-        codes[b], scales[b] = c, s
-    rope = torch.stack([W.rope_rows(wl, b, N, DEV) for b in range(B)]) if wl.d_r else \
-        torch.zeros(B, N, 0, dtype=torch.bfloat16, device=DEV)
+        codes[b].copy_(c)
+        scales[b].copy_(s)
+        if wl.d_r:
+            rope[b].copy_(W.rope_rows(wl, b, N, DEV))
     return codes, scales, rope
 
 
-def _check(wl, B, N, idx, q=None, tol=2e-3):
-    codes, scales, rope = _raw_cache(wl, B, N)
+def _check(wl, B, N, idx, q=None, tol=2e-3, layout="record"):
+    codes, scales, rope = _raw_cache(wl, B, N, layout)
     if q is None:
         q = W.attn_query(wl.scaled(B=B), DEV)
     idx_t = torch.from_numpy(np.asarray(idx, dtype=np.int32)).to(DEV)
     out, lse = csa2.csa2_sparse_attn_fp4(q, codes, scales, rope, idx_t, wl.sm_scale)
     torch.cuda.synchronize()
-    ro, rl = oracle.sparse_attn(np_bits(q), codes.cpu().numpy(), scales.cpu().numpy(), np_bits(rope),
-                                np.asarray(idx), wl.sm_scale)
+    ro, rl = oracle.sparse_attn(np_bits(q), codes.cpu().numpy(), scales.cpu().numpy(),
+                                np_bits(rope.contiguous()), np.asarray(idx), wl.sm_scale)
     return attn_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol)
 
 
@@ -80,6 +80,14 @@ def test_attention_other_dims(dc, dr):
     note(f"attn: d_c={dc} d_r={dr}")
     rng = np.random.default_rng(dc + dr)
     _check(wl, 2, 1024, _rand_idx(rng, 2, 512, 1024))
+
+
+@pytest.mark.parametrize("wi", [0, 1])
+def test_attention_separate_array_layout(wi):
+    wl = W.WORKLOADS[wi]
+    note(f"attn: {wl.name} with codes / scales / RoPE in three dense arrays")
+    rng = np.random.default_rng(77)
+    _check(wl, 3, 2048, _rand_idx(rng, 3, wl.K, 2048), layout="separate")
 
 
 def test_attention_query_magnitudes():

@@ -9,13 +9,16 @@ from gpu_util import DEV, W, csa2, note, np_bits, oracle
 pytestmark = pytest.mark.gpu
 
 
-def _run(x, d_r=0, cap=None, row0=0, rope=None):
+def _run(x, d_r=0, cap=None, row0=0, rope=None, layout="record"):
     R, d_c = x.shape
     cap = R + row0 if cap is None else cap
-    codes = torch.full((cap, d_c // 2), 0xAB, dtype=torch.uint8, device=DEV)
-    scales = torch.full((cap, d_c // 16), 0xCD, dtype=torch.uint8, device=DEV)
-    rope_dst = torch.zeros(cap, d_r, dtype=torch.bfloat16, device=DEV) if d_r else None
-    csa2.csa2_quantize_fp4(x, codes, scales, row0, rope, rope_dst)
+    codes, scales, rope_dst = csa2.alloc_cache(1, cap, d_c, d_r, DEV, layout)
+    codes, scales, rope_dst = codes[0], scales[0], rope_dst[0]
+    codes.fill_(0xAB)
+    scales.fill_(0xCD)
+    if d_r:
+        rope_dst.zero_()
+    csa2.csa2_quantize_fp4(x, codes, scales, row0, rope, rope_dst if d_r else None)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), scales.cpu().numpy(), (rope_dst.cpu() if d_r else None)
 
@@ -76,15 +79,16 @@ def test_golden_groups_on_gpu():
     assert np.array_equal(scales, ws) and np.array_equal(codes, wc)
 
 
+@pytest.mark.parametrize("layout", ["record", "separate"])
 @pytest.mark.parametrize("d_c,d_r,R,row0,cap", [(512, 64, 8192, 262144 - 8192, 262144), (512, 64, 1, 5, 9),
                                                 (512, 0, 777, 100, 1000), (128, 0, 1024, 0, 1024),
-                                                (32, 8, 33, 1, 40), (2048, 16, 65, 0, 65)])
-def test_append_rows_and_leave_the_rest(d_c, d_r, R, row0, cap):
-    note(f"quantize: append d_c={d_c} d_r={d_r} R={R} row0={row0} cap={cap}")
+                                                (32, 8, 33, 1, 40), (2048, 16, 65, 0, 65), (128, 64, 50, 3, 60)])
+def test_append_rows_and_leave_the_rest(d_c, d_r, R, row0, cap, layout):
+    note(f"quantize: append d_c={d_c} d_r={d_r} R={R} row0={row0} cap={cap} layout={layout}")
     wl = W.WORKLOADS[4].scaled(prefill_rows=R, d_c=d_c, d_r=d_r)
     x = W.prefill_chunk(wl, DEV)
     rope = W.prefill_rope(wl, DEV) if d_r else None
-    codes, scales, rope_dst = _run(x, d_r=d_r, cap=cap, row0=row0, rope=rope)
+    codes, scales, rope_dst = _run(x, d_r=d_r, cap=cap, row0=row0, rope=rope, layout=layout)
     wc, ws = oracle.quantize_fp4(np_bits(x))
     assert np.array_equal(codes[row0:row0 + R], wc)
     assert np.array_equal(scales[row0:row0 + R], ws)
