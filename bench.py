@@ -16,7 +16,6 @@ the committed rocprofv3 FETCH_SIZE / WRITE_SIZE measurement of that kernel
 """
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -41,29 +40,23 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run one 256 MiB device copy (FETCH/WRITE calibration under rocprofv3)")
+                    help="also run one elementwise copy of 256 MiB (float32 negation: 256 MiB read, "
+                         "256 MiB written) as the FETCH/WRITE calibration under rocprofv3")
     return ap.parse_args()
 
 
-def kernel_source_hash(name):
-    p = os.path.join(ROOT, "sparse_attention_decode_csa2_amd", "csrc", name)
-    h = hashlib.sha256()
-    for f in (p, os.path.join(os.path.dirname(p), "csa2_device.h")):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def committed_traffic(kernel_file, workload):
-    """Per-launch HBM bytes measured with rocprofv3 counters, if still valid."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """Per-launch HBM bytes of the dominant kernel measured with rocprofv3
+    counters (profiles/traffic_<workload>.txt), or None when absent or taken
+    on a different version of the kernel's source."""
+    from sparse_attention_decode_csa2_amd.rocprof_summary import kernel_source_hash, read_traffic
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(p):
         return None
-    with open(p) as f:
-        rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash(kernel_file):
+    rec = read_traffic(p)
+    if rec.get("source_file") != kernel_file or rec.get("source_hash") != kernel_source_hash(kernel_file):
         return None
-    return rec.get("bytes_per_launch")
+    return float(rec["bytes_per_launch"])
 
 
 def _entry_bytes(wl):
@@ -312,10 +305,12 @@ def main():
     traffic = committed_traffic(kernel_file, wl.name)
 
     if args.calib_copy:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
         torch.cuda.synchronize()
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
 
     qps = wl.B / (ms_per_step * 1e-3)
     line = {

@@ -1,0 +1,161 @@
+"""Condense rocprofv3 CSV output into the short text summaries kept under
+profiles/.
+
+    python -m sparse_attention_decode_csa2_amd.rocprof_summary stats DIR --command "..."
+        Kernel table (calls, average / min / max duration, share of GPU time)
+        from the *_kernel_stats.csv of a `rocprofv3 --kernel-trace --stats` run.
+
+    python -m sparse_attention_decode_csa2_amd.rocprof_summary traffic \
+        --fetch DIR1 --write DIR2 --kernel REGEX --calib REGEX --calib-bytes N \
+        --workload NAME --source attn.hip --command "..."
+        HBM bytes per launch of the kernels matching REGEX, from two `--pmc`
+        runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is
+        scaled by the factor that makes it read N bytes for a calibration
+        kernel of known size (a plain device copy: N bytes read, N written).
+        The output is what bench.py reads as roofline.traffic, tagged with a
+        hash of the kernel's source so that a stale measurement is ignored.
+"""
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def kernel_source_hash(name):
+    """Hash of one kernel source file plus the shared device header."""
+    h = hashlib.sha256()
+    for f in (os.path.join(CSRC, name), os.path.join(CSRC, "csa2_device.h")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _find(d, suffix):
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits
+
+
+def _short(name, width=96):
+    """Kernel name without its trailing parameter list, cut to `width`."""
+    name = name.strip()
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                name = name[:i].rstrip()
+                break
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def stats(args):
+    rows = []
+    for f in _find(args.dir, "kernel_stats.csv"):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# rocprofv3 kernel statistics", f"# command: {args.command}", "#",
+           f"{'kernel':<98} {'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share%':>7}"]
+    for r in rows:
+        out.append(f"{_short(r['Name']):<98} {int(r['Calls']):>7} {float(r['AverageNs']) / 1e3:>9.3f} "
+                   f"{float(r['MinNs']) / 1e3:>9.3f} {float(r['MaxNs']) / 1e3:>9.3f} "
+                   f"{float(r['Percentage']):>7.2f}")
+    print("\n".join(out))
+
+
+def _counter_means(d, counter):
+    """Average counter value per dispatch, keyed by kernel name."""
+    acc = {}
+    for f in _find(d, "counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
+                acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    per = {}
+    for (name, _), v in acc.items():
+        per.setdefault(name, []).append(v)
+    return per
+
+
+def _pick(per, regex, what):
+    hits = {k: v for k, v in per.items() if re.search(regex, k)}
+    if not hits:
+        raise SystemExit(f"no {what} kernel matches {regex!r}")
+    vals = [x for v in hits.values() for x in v]
+    return sum(vals) / len(vals), len(vals), sorted(hits)
+
+
+def traffic(args):
+    f_per = _counter_means(args.fetch, "FETCH_SIZE")
+    w_per = _counter_means(args.write, "WRITE_SIZE")
+    cf, _, cnames = _pick(f_per, args.calib, "calibration")
+    cw, _, _ = _pick(w_per, args.calib, "calibration")
+    f_scale = args.calib_bytes / (cf * 1024.0)
+    w_scale = args.calib_bytes / (cw * 1024.0)
+    kf, nf, knames = _pick(f_per, args.kernel, "measured")
+    kw, nw, _ = _pick(w_per, args.kernel, "measured")
+    fetch = kf * 1024.0 * f_scale
+    write = kw * 1024.0 * w_scale
+    print("\n".join([
+        f"# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
+        f"# each scaled so that the calibration copy reads and writes exactly {args.calib_bytes} bytes",
+        f"# command: {args.command}",
+        f"workload: {args.workload}",
+        f"kernel: {' | '.join(_short(k, 200) for k in knames)}",
+        f"calibration_kernel: {' | '.join(_short(k, 200) for k in cnames)}",
+        f"source_file: {args.source}",
+        f"source_hash: {kernel_source_hash(args.source)}",
+        f"dispatches: {nf} fetch, {nw} write",
+        f"fetch_kib_raw: {kf:.1f}",
+        f"write_kib_raw: {kw:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"fetch_bytes_per_launch: {fetch:.0f}",
+        f"write_bytes_per_launch: {write:.0f}",
+        f"bytes_per_launch: {fetch + write:.0f}",
+    ]))
+
+
+def read_traffic(path):
+    """Parse a traffic summary written by `traffic` into a dict of strings."""
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    return rec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--calib", required=True)
+    t.add_argument("--calib-bytes", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--command", required=True)
+    args = ap.parse_args(argv)
+    {"stats": stats, "traffic": traffic}[args.cmd](args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
