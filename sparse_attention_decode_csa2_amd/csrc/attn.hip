@@ -19,7 +19,15 @@
 //  4. P (fp16) . V with v_mfma_f32_16x16x32_f16, wave w owning a quarter of
 //     the latent channels; V comes from the same LDS tile.
 // With several slices per query the unnormalised partial results (O, max,
-// sum) go to the workspace and a combine kernel merges them by log-sum-exp.
+// sum) go to the workspace and a second kernel merges them by log-sum-exp
+// (merging inside the last workgroup to finish would need device-scope
+// fences, which write back and invalidate the whole XCD L2 under the other
+// workgroups' gathers).
+//
+// Workgroups are numbered so that all of one query's workgroups land on the
+// same XCD (consecutive workgroup ids go round-robin over the eight XCDs): the
+// head groups of a query gather the same entries, and only the first of them
+// misses in that XCD's L2.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -63,7 +71,7 @@ struct GatherRegs {
 template <int DC, int DR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
-    const int32_t* __restrict__ idx, int K, int H, int64_t N_cap, float sm_scale_log2e, int n_hg,
+    const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, float sm_scale_log2e, int n_hg,
     int n_split, int per_split, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int KSL = DC / 32;           // latent k-steps
@@ -83,11 +91,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  int bid = blockIdx.x;
-  const int split = bid % n_split;
-  bid /= n_split;
-  const int hg = bid % n_hg;
-  const int64_t b = bid / n_hg;
+  // workgroup x runs on XCD x % 8; that XCD's slots x / 8 enumerate
+  // (query b / 8, slice, head group) for the queries b = xcd (mod 8)
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int per_q = n_split * n_hg;
+  const int64_t b = (int64_t)(slot / per_q) * 8 + xcd;
+  if (b >= B) return;  // padding of the grid to whole groups of eight queries
+  const int split = (slot % per_q) / n_hg;
+  const int hg = slot % n_hg;
   const int h0 = hg * 16;
   const int e_begin = split * per_split;
   const int e_end = min(K, e_begin + per_split);
@@ -357,13 +369,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int d = 0; d < NDB; ++d) orow[16 * d + n] = acc[d][i] * inv;
       if (lse && wave == 0 && n == 0) lse[b * H + h] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
     } else {
-      const int64_t slot = (b * H + h) * n_split + split;
-      float* orow = ws_o + slot * DC + wave * QCH;
+      const int64_t slot_o = (b * H + h) * n_split + split;
+      float* orow = ws_o + slot_o * DC + wave * QCH;
 #pragma unroll
       for (int d = 0; d < NDB; ++d) orow[16 * d + n] = acc[d][i];
       if (wave == 0 && n == 0) {
-        ws_ml[2 * slot] = m;
-        ws_ml[2 * slot + 1] = l;
+        ws_ml[2 * slot_o] = m;
+        ws_ml[2 * slot_o + 1] = l;
       }
     }
   }
@@ -413,6 +425,7 @@ static void attn_plan(int B, int H, int K, int* n_split, int* per_split) {
   *per_split = tps * AT_TILE;
 }
 
+// Workspace: partial outputs f32 [B, H, s, d_c], then (max, sum) f32 [B, H, s, 2].
 size_t attn_workspace_bytes(int B, int H, int d_c, int K) {
   int s, ps;
   attn_plan(B, H, K, &s, &ps);
@@ -429,11 +442,12 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
   const int n_hg = (H + 15) / 16;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = s > 1 ? ws_o + (size_t)B * H * s * d_c : nullptr;
-  const dim3 grid((unsigned)(B * n_hg * s)), blk(256);
+  const int64_t groups = ((int64_t)B + 7) / 8;  // of eight queries, one per XCD
+  const dim3 grid((unsigned)(groups * 8 * n_hg * s)), blk(256);
   const float sl = sm_scale * LOG2E;
 #define CSA2_ATTN(DCV, DRV)                                                                     \
-  hipLaunchKernelGGL((sparse_attn_kernel<DCV, DRV>), grid, blk, 0, stream, q, cache, idx, K, H, N_cap, \
-                     sl, n_hg, s, ps, out, lse, ws_o, ws_ml)
+  hipLaunchKernelGGL((sparse_attn_kernel<DCV, DRV>), grid, blk, 0, stream, q, cache, idx, K, B, H, \
+                     N_cap, sl, n_hg, s, ps, out, lse, ws_o, ws_ml)
   if (d_c == 512 && d_r == 64) CSA2_ATTN(512, 64);
   else if (d_c == 512 && d_r == 0) CSA2_ATTN(512, 0);
   else if (d_c == 128 && d_r == 0) CSA2_ATTN(128, 0);
