@@ -5,10 +5,16 @@
 //
 // One workgroup (4 waves) owns one query, 16 heads and a slice of the index
 // list, walked in tiles of 64 entries:
-//  1. gather: each thread fetches a quarter of one entry (codes, scales, RoPE
-//     part) with 16-byte loads and dequantises it into an LDS tile (latent as
-//     fp16, RoPE as bf16).  E2M1 x E4M3 products have <= 6 significant bits
-//     and lie in [2^-10, 2688], so the fp16 latent is exact.
+//  1. gather: wave w fetches entries [16w, 16w + 16) of the tile.  Each load
+//     instruction covers whole cache lines: for the codes, 16 lanes read the
+//     256 bytes of one entry (four entries per instruction), each lane also
+//     reading the two E4M3 scale bytes of its 32 channels; for the RoPE part,
+//     8 lanes read the 128 bytes of one entry.  The lanes dequantise into an
+//     LDS tile (latent as fp16, RoPE as bf16).  E2M1 x E4M3 products have
+//     <= 6 significant bits and lie in [2^-10, 2688], so the fp16 latent is
+//     exact.  The latent tile is stored with its 16-byte pieces permuted
+//     within each 32-channel chunk, so that the dequant stores, the score
+//     reads and the transposing value reads are all free of bank conflicts.
 //  2. scores: wave w forms S^T for entries [16w, 16w + 16) of the tile with
 //     v_mfma_f32_16x16x32 (A = the entry rows from LDS, B = the 16 query
 //     heads held in registers), fp16 for the latent part, bf16 for RoPE.
@@ -58,14 +64,37 @@ __device__ __forceinline__ f16x4 tr16_read(const _Float16* p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
+// Position (in halves) of channel chunk c (32 channels), piece p (8 channels)
+// of tile row r in the latent tile: pieces are permuted within a chunk by
+// ((c >> 1) & 3) ^ ((r >> 2) & 1).  With a row pitch of 8 (mod 32) dwords this
+// makes the dequant stores (8 lanes = 8 chunks of one row), the score reads
+// (8 lanes = 8 rows, one piece) and the transposing reads (4 rows x 4 lanes
+// inside one piece pair) each touch 32 distinct banks.
+__device__ __forceinline__ int tile_col(int r, int c, int p) {
+  return 32 * c + 8 * (p ^ ((c >> 1) & 3) ^ ((r >> 2) & 1));
+}
+
+// Latent chunk m of the 128 (32 with 128 channels) that PV wave w owns:
+// chunks 8 (w >> 1) + (w & 1) + 2m, so that (chunk >> 1) & 3 = m does not
+// depend on w and every transposing read address is a per-lane base plus an
+// immediate offset.
+template <int DC>
+__device__ __forceinline__ int pv_chunk(int w, int m) {
+  if constexpr (DC >= 512) return 8 * (w >> 1) + (w & 1) + 2 * m;
+  else return w;
+}
+
 template <int DC, int DR>
 struct GatherRegs {
-  static constexpr int NCW = DC / 2 / 4 / 16;       // 16-byte code words per quarter entry
-  static constexpr int RW = DR > 0 ? DR / 4 / 8 : 1;  // 16-byte RoPE words per quarter entry
-  u32x4 cw[NCW];
-  uint16_t sb[NCW];  // the two scale bytes of each code word
-  u32x4 rw[RW];
-  bool valid;
+  static constexpr int CPE = DC / 32;               // 32-channel chunks (16 code bytes) per entry
+  static constexpr int EPI = 64 / CPE;              // entries per code load instruction
+  static constexpr int NCI = 16 / EPI;              // code load instructions per wave and tile
+  static constexpr int RPE = DR > 0 ? DR / 8 : 1;   // 8-channel RoPE pieces per entry
+  static constexpr int NRI = DR > 0 ? 16 * RPE / 64 : 0;  // RoPE load instructions per wave and tile
+  u32x4 cw[NCI];
+  uint16_t sb[NCI];  // the two scale bytes of each lane's chunk
+  u32x4 rw[NRI > 0 ? NRI : 1];
+  uint32_t vmask;    // bit k: the entry of code instruction k is selected and in range
 };
 
 template <int DC, int DR>
@@ -76,12 +105,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int KSL = DC / 32;           // latent k-steps
   constexpr int KSR = DR / 32;           // RoPE k-steps
-  constexpr int LDK = DC + 8;            // fp16 pitch of the latent tile
-  constexpr int LDR = DR + 8;            // bf16 pitch of the RoPE tile
+  constexpr int LDK = DC + 16;           // fp16 pitch of the latent tile (8 mod 32 dwords)
+  constexpr int LDR = DR;                // bf16 pitch of the RoPE tile (pieces XOR-permuted by row)
+  constexpr int RPM = DR / 8 - 1;        // piece-index mask of a RoPE row
   constexpr int QCH = DC / 4;            // latent channels per PV wave
   constexpr int NDB = QCH / 16;          // PV d-blocks per wave
   using GR = GatherRegs<DC, DR>;
-  constexpr int NCW = GR::NCW;
+  constexpr int CPE = GR::CPE, EPI = GR::EPI, NCI = GR::NCI, RPE = GR::RPE, NRI = GR::NRI;
+  static_assert(64 % CPE == 0 && 16 % EPI == 0 && (DR == 0 || (64 % RPE == 0 && NRI >= 1)), "gather layout");
   __shared__ __attribute__((aligned(16))) _Float16 sK[AT_TILE][LDK];
   __shared__ __attribute__((aligned(16))) __bf16 sR[AT_TILE][DR > 0 ? LDR : 8];
   __shared__ __attribute__((aligned(16))) _Float16 sP[16][AT_TILE + 8];
@@ -104,7 +135,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int e_begin = split * per_split;
   const int e_end = min(K, e_begin + per_split);
   const int32_t* idx_row = idx + b * K;
-  const int er = tid >> 2, part = tid & 3;  // gather: entry row of the tile, quarter
+  const int cl_e = lane / CPE, cl_c = lane % CPE;  // code lanes: entry within the instruction, chunk
+  const int rl_e = lane / RPE, rl_p = lane % RPE;  // RoPE lanes: entry within the instruction, piece
   // an empty slice or cache: no loads at all, the epilogue writes the empty result
   const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
 
@@ -143,30 +175,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
   __syncthreads();
 
-  // ---- gather: thread (er, part) fetches, for code word i, bytes
-  // [16 part + 64 i, +16) of entry er (channels 32 part + 128 i .. +31), so the
-  // four threads of an entry read whole 64-byte segments; plus the two scale
-  // bytes of those channels and a quarter of the RoPE part.  Loads are
-  // unconditional (a skipped entry reads row 0 of its sequence) so they issue
-  // back to back; the scale of a skipped entry is zeroed when it is used.
+  // ---- gather (see the header): unconditional loads (a skipped entry reads
+  // row 0 of its sequence and has its scales zeroed when it is used), so they
+  // issue back to back.
+  // Rows of one sequence span less than 4 GiB in each array (checked by the
+  // host), so a row's offset from its sequence base is 32-bit arithmetic.
+  const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride + 16 * cl_c;
+  const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride + 2 * cl_c;
+  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride + 16 * rl_p;
+  const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
+  const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
   auto gather = [&](GR& gr, int tile) {
     // pinned in program order: a load hoisted above the previous tile's work
     // lands in registers that are still in flight and forces a full wait
     __builtin_amdgcn_sched_barrier(0);
-    const int32_t id = sIdx[tile * AT_TILE + er];
-    gr.valid = id >= 0 && (int64_t)id < N_cap;
-    const int64_t row = b * N_cap + (gr.valid ? id : 0);
-    const uint8_t* cp = cache.codes + row * cache.codes_stride + 16 * part;
-    const uint8_t* sp = cache.scales + row * cache.scales_stride + 2 * part;
+    gr.vmask = 0;
 #pragma unroll
-    for (int i = 0; i < NCW; ++i) {
-      gr.cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp + 64 * i));
-      gr.sb[i] = *reinterpret_cast<const uint16_t*>(sp + 8 * i);
+    for (int k = 0; k < NCI; ++k) {
+      const uint32_t id = (uint32_t)sIdx[tile * AT_TILE + 16 * wave + EPI * k + cl_e];
+      const bool ok = id < ncap32;  // also rejects negative ids
+      gr.vmask |= (uint32_t)ok << k;
+      const uint32_t r = ok ? id : 0u;
+      gr.cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seq_codes + r * cs32));
+      gr.sb[k] = *reinterpret_cast<const uint16_t*>(seq_scales + r * ss32);
     }
     if constexpr (DR > 0) {
-      const uint8_t* rp = reinterpret_cast<const uint8_t*>(cache.rope) + row * cache.rope_stride + part * (DR / 2);
 #pragma unroll
-      for (int i = 0; i < GR::RW; ++i) gr.rw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + 16 * i));
+      for (int k = 0; k < NRI; ++k) {
+        const uint32_t id = (uint32_t)sIdx[tile * AT_TILE + 16 * wave + (64 / RPE) * k + rl_e];
+        const uint32_t r = id < ncap32 ? id : 0u;
+        gr.rw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seq_rope + r * rs32));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -181,38 +220,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     // into the previous tile's work would wait for loads still in flight.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < NCW; ++i) asm volatile("" : "+v"(gr.sb[i]));
-    // ---- 1. dequantise the gathered quarter into the LDS tile.  The FP4 pairs
-    // go through the hardware converter with a unit scale; the E4M3 block scale
-    // (exact in fp16) is applied with a packed fp16 multiply, and every product
-    // (<= 6 significant bits, within [2^-10, 2688]) is exact in fp16.
+    for (int i = 0; i < NCI; ++i) asm volatile("" : "+v"(gr.sb[i]));
+    // ---- 1. dequantise into the LDS tile.  The two E4M3 scales of a lane's
+    // chunk go through the hardware fp8 converter (exact in fp16), the FP4
+    // pairs through the fp4 converter with a unit scale; the block scale is
+    // applied with a packed fp16 multiply, exact as every product has <= 6
+    // significant bits within [2^-10, 2688].
 #pragma unroll
-    for (int i = 0; i < NCW; ++i) {
+    for (int k = 0; k < NCI; ++k) {
+      const int e = 16 * wave + EPI * k + cl_e;
+      const bool ok = (gr.vmask >> k) & 1u;
+      const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ok ? (uint32_t)gr.sb[k] : 0u, 1.0f, false);
+      const f16x2 s_lo = {sc[0], sc[0]}, s_hi = {sc[1], sc[1]};  // channels 0-15 / 16-31 of the chunk
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const uint32_t sbv = gr.valid ? (uint32_t)gr.sb[i] : 0u;  // a skipped entry contributes zeros
-        const _Float16 sg = (_Float16)e4m3_decode((sbv >> (8 * half)) & 0xFFu);
-        const f16x2 s2v = {sg, sg};
-        f16x8 outv[2];
-#pragma unroll
-        for (int dw = 0; dw < 2; ++dw) {
-          const uint32_t word = gr.cw[i][2 * half + dw];
-          const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * s2v;
-          const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * s2v;
-          const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * s2v;
-          const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * s2v;
-          outv[dw] = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        }
-        _Float16* dst = &sK[er][32 * part + 128 * i + 16 * half];
-        *reinterpret_cast<f16x8*>(dst) = outv[0];
-        *reinterpret_cast<f16x8*>(dst + 8) = outv[1];
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t word = gr.cw[k][p];
+        const f16x2 sv = p < 2 ? s_lo : s_hi;
+        const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sv;
+        const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sv;
+        const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sv;
+        const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sv;
+        *reinterpret_cast<f16x8*>(&sK[e][tile_col(e, cl_c, p)]) =
+            f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       }
+      if (cl_c == 0) sValid[e] = ok;
     }
     if constexpr (DR > 0) {
 #pragma unroll
-      for (int i = 0; i < GR::RW; ++i) *reinterpret_cast<u32x4*>(&sR[er][part * (DR / 4) + 8 * i]) = gr.rw[i];
+      for (int k = 0; k < NRI; ++k)
+      {
+        // piece p of row r lives at piece p ^ (r & RPM): the 8 rows a score
+        // read touches then fall on distinct banks
+        const int r = 16 * wave + (64 / RPE) * k + rl_e;
+        *reinterpret_cast<u32x4*>(&sR[r][8 * (rl_p ^ (r & RPM))]) = gr.rw[k];
+      }
     }
-    if (part == 0) sValid[er] = gr.valid;
     __syncthreads();
 
     // ---- 2. S^T for entries 16*wave + (0..15): lane (entry n, k-group g)
@@ -223,12 +265,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       const int r = 16 * wave + n;
 #pragma unroll
       for (int t = 0; t < KSL; ++t) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(&sK[r][32 * t + 8 * g]);
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&sK[r][tile_col(r, t, g)]);
         c = mfma16x16x32_f16(a, Bq[t], c);
       }
 #pragma unroll
       for (int t = 0; t < KSR; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sR[r][32 * t + 8 * g]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sR[r][8 * ((4 * t + g) ^ (r & RPM))]);
         c = mfma16x16x32_bf16(a, Br[t], c);
       }
       // c[i] = S^T[entry 16*wave + 4g + i][head n]
@@ -281,9 +323,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         const f16x8 a = *reinterpret_cast<const f16x8*>(&sP[n][32 * u + 8 * g]);
 #pragma unroll
         for (int d = 0; d < NDB; ++d) {
-          const int col = wave * QCH + 16 * d + 4 * tr_c;
-          const f16x4 v0 = tr16_read(&sK[32 * u + 8 * g + tr_r][col]);
-          const f16x4 v1 = tr16_read(&sK[32 * u + 8 * g + 4 + tr_r][col]);
+          // 4 channels inside one 8-channel piece of d-block d (16 channels)
+          const int ch = 32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + 4 * tr_c;
+          const int r0 = 32 * u + 8 * g + tr_r, r1 = r0 + 4;
+          const f16x4 v0 = tr16_read(&sK[r0][tile_col(r0, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+          const f16x4 v1 = tr16_read(&sK[r1][tile_col(r1, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
           const f16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
           acc[d] = mfma16x16x32_f16(a, bv, acc[d]);
         }
@@ -364,15 +408,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const float m = sFinM[hl], l = sFinL[hl];
     if (n_split == 1) {
       const float inv = l > 0.f ? 1.0f / l : 0.f;
-      float* orow = out + (b * H + h) * DC + wave * QCH;
+      float* orow = out + (b * H + h) * DC;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) orow[16 * d + n] = acc[d][i] * inv;
+      for (int d = 0; d < NDB; ++d) orow[32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + n] = acc[d][i] * inv;
       if (lse && wave == 0 && n == 0) lse[b * H + h] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
     } else {
       const int64_t slot_o = (b * H + h) * n_split + split;
-      float* orow = ws_o + slot_o * DC + wave * QCH;
+      float* orow = ws_o + slot_o * DC;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) orow[16 * d + n] = acc[d][i];
+      for (int d = 0; d < NDB; ++d) orow[32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + n] = acc[d][i];
       if (wave == 0 && n == 0) {
         ws_ml[2 * slot_o] = m;
         ws_ml[2 * slot_o + 1] = l;

@@ -113,3 +113,28 @@ def test_attention_on_quantized_cache_is_dense_attention_when_k_is_n():
     out, lse = csa2.csa2_sparse_attn_fp4(q, cache.codes, cache.scales, cache.rope, idx, wl.sm_scale)
     ro, rl = oracle_attention_rows(cache, 0, np_bits(q)[0], idx.cpu().numpy()[0], wl.sm_scale)
     attn_close(out.cpu().numpy()[0], lse.cpu().numpy()[0], ro, rl)
+
+
+def test_attention_every_e4m3_scale_byte():
+    wl = W.WORKLOADS[1].scaled(H=16)
+    note("attn: every non-NaN E4M3 scale byte (subnormal, negative, 448)")
+    B, N = 2, 1024
+    codes, scales, rope = csa2.alloc_cache(B, N, wl.d_c, wl.d_r, DEV)
+    for b in range(B):
+        c, _ = W.random_codes(wl, b, N, DEV)
+        codes[b].copy_(c)
+        rope[b].copy_(W.rope_rows(wl, b, N, DEV))
+    # scale bytes cycle through 0x00..0xFE, skipping the two NaN codes
+    allb = torch.tensor([v for v in range(256) if v not in (0x7F, 0xFF)], dtype=torch.uint8)
+    reps = (B * N * (wl.d_c // 16) + allb.numel() - 1) // allb.numel()
+    sc = allb.repeat(reps)[: B * N * (wl.d_c // 16)].view(B, N, wl.d_c // 16)
+    scales.copy_(sc.to(DEV))
+    q = W.attn_query(wl.scaled(B=B), DEV)
+    rng = np.random.default_rng(21)
+    idx = _rand_idx(rng, B, 512, N)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    out, lse = csa2.csa2_sparse_attn_fp4(q, codes, scales, rope, idx_t, wl.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attn(np_bits(q), codes.cpu().numpy(), scales.cpu().numpy(),
+                                np_bits(rope.contiguous()), idx, wl.sm_scale)
+    attn_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
