@@ -7,12 +7,12 @@
 //
 // The multi-head q . K contraction runs on the matrix cores: one
 // v_mfma_f32_16x16x32_bf16 per 32 key dimensions computes a 16 (heads, padded
-// with zero rows) x 16 (keys) tile.  Each lane streams 16*KS contiguous bytes of
-// one key (lane = key (l % 16), quarter (l / 16) of the key's dimensions), so a
-// wave reads 16 whole keys (16 x 2*D_I bytes, contiguous in Full mode, two
-// 8-entry runs per tile in pool mode) with 16-byte loads.  The k-dimension of
-// the MFMA is permuted identically for q and the keys, which leaves the dot
-// products unchanged.  The epilogue applies ReLU and the head weights and
+// with zero rows) x 16 (keys) tile.  For k-step s, lane (key l % 16, group
+// l / 16) supplies dimensions 32s + 8 (l / 16) .. +7 of its key, so the four
+// lanes of a key read 64 contiguous bytes per load instruction and a wave's
+// KS instructions read 16 whole keys (contiguous in Full mode, two 8-entry
+// runs per tile in pool mode).  The query is laid out the same way, which is
+// the MFMA's own k order.  The epilogue applies ReLU and the head weights and
 // reduces the four head quarters across lane groups.
 //
 // HBM-bound: 2*D_I bytes of key per scored entry against 4*H_I*D_I flops
@@ -29,7 +29,6 @@ __global__ __launch_bounds__(256) void index_kernel(
     const int32_t* __restrict__ n_blocks, int P_max, int block, int64_t M, int64_t wg_per_row,
     float* __restrict__ scores, int32_t* __restrict__ positions) {
   constexpr int D_I = 32 * KS;
-  constexpr int LANE_DIMS = 8 * KS;  // contiguous key dims owned by one lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t b = blockIdx.x / wg_per_row;
@@ -38,11 +37,11 @@ __global__ __launch_bounds__(256) void index_kernel(
   // A operand: indexer query head n (rows >= H_I are zero), dims of quarter g
   bf16x8 A[KS];
   {
-    const uint16_t* qrow = q + (b * H_I + n) * D_I + g * LANE_DIMS;
+    const uint16_t* qrow = q + (b * H_I + n) * D_I + 8 * g;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (n < H_I) v = *reinterpret_cast<const u32x4*>(qrow + 8 * s);
+      if (n < H_I) v = *reinterpret_cast<const u32x4*>(qrow + 32 * s);
       A[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -78,11 +77,11 @@ __global__ __launch_bounds__(256) void index_kernel(
     }
     pos[t] = p;
     ok[t] = valid;
-    const uint16_t* krow = k + (b * N_cap + (valid ? p : 0)) * D_I + g * LANE_DIMS;
+    const uint16_t* krow = k + (b * N_cap + (valid ? p : 0)) * D_I + 8 * g;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + 8 * s));
+      if (valid) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + 32 * s));
       Bv[t][s] = v;
     }
   }
