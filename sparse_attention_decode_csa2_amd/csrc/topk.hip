@@ -3,25 +3,29 @@
 // Every candidate becomes one 64-bit key: high word = order-preserving image of
 // its fp32 score (-0 folded onto +0, NaN lowest), low word = ~id, so that
 // "larger key" is exactly "higher score, then lower id" and an empty candidate
-// is key 0.  One workgroup of 1024 threads owns up to 16384 keys (16 per
-// thread, in registers):
+// is key 0.  One workgroup of 1024 threads owns up to 16384 candidates, thread
+// t the 16 consecutive columns [16t, 16t + 16) of its chunk, held in registers
+// as 32-bit score keys (thread order is column order):
 //
-//  1. skip the bits shared by every valid key (block max / min of the high
-//     words), then histogram the next 13 bits into 8192 LDS bins and find,
-//     with a block scan, the bin holding the K-th largest key.  Keys above that
-//     bin are certainly selected ("definite", fewer than K of them); the keys
-//     in it are the "boundary" set.  Should the boundary set exceed 2048 keys
-//     the next 13 bits of that bin are histogrammed, and so on.
-//  2. compact both sets into LDS with one atomic per wave (ballot counts).
-//  3. sort each set descending with a bitonic network held in registers
-//     (exchanges through DPP / permlane swaps below stride 64, through LDS
-//     above); the output is the sorted definite set followed by the largest
-//     K - |definite| boundary keys, i.e. (score desc, id asc).
+//  1. a block reduction gives the number of valid candidates and the highest
+//     and lowest score keys; the bits they share are skipped;
+//  2. one radix pass over the chunk (11 bits, 2048 LDS bins, one suffix scan)
+//     finds the bin holding the K-th largest score key;
+//  3. the keys above that bin go straight to the output buffer and the keys
+//     of the bin (at most 2048, else the passes continue over the chunk) to a
+//     candidate buffer, both in column order;
+//  4. the rest of the selection runs on the candidates, 2 per thread: radix
+//     passes until the wanted part of a bin is the whole bin or one exact
+//     score, then a tie on one score is cut by id (in column order by one
+//     block scan when the ids are the columns, else by radix select on ~id);
+//  5. a bitonic network (DPP / permlane exchanges below stride 64, LDS for
+//     strides 64 and 128, in-register above) sorts the K keys descending.
 //
 // Rows longer than 16384 are cut into 16384-key chunks; each chunk keeps its
-// own top K keys (the union of chunk winners contains the row's winners, the
-// key order being total) and the winners are reduced again until one chunk
-// remains.  Bit-exact by construction: only integer compares and counts.
+// own top K keys, unsorted (the union of chunk winners contains the row's
+// winners, the key order being total) and the winners are reduced again
+// until one chunk remains.  Bit-exact by construction: only integer compares
+// and counts.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -30,22 +34,27 @@ namespace csa2 {
 constexpr int TK_T = 1024;
 constexpr int TK_E = 16;
 constexpr int TK_CHUNK = TK_T * TK_E;
-constexpr int TK_BITS = 13;
+constexpr int TK_BITS = 11;
 constexpr int TK_BINS = 1 << TK_BITS;
-constexpr int TK_CAP = 2048;  // largest set sorted directly (>= K)
+constexpr int TK_KMAX = 2048;            // largest K, largest candidate set
+constexpr int TK_CE = TK_KMAX / TK_T;    // candidates per thread
 constexpr int TK_WAVES = TK_T / WAVE;
+static_assert(TK_WAVES <= 16, "block ops combine the wave partials in one 16-lane row");
 
 struct TkSmem {
-  uint32_t hist[TK_BINS];    // histogram; later parks the sorted definite set
-  uint64_t buf[2][TK_CAP];   // [0]: definite set, [1]: boundary set
-  uint64_t xbuf[TK_CAP];     // second buffer of the sort's LDS exchanges
+  uint32_t hist[TK_BINS + WAVE];  // radix histogram + one dummy bin per lane
+  uint64_t buf[TK_KMAX];          // the selected keys
+  uint64_t xbuf[TK_KMAX];         // candidates; second buffer of the sort's LDS exchanges
   uint32_t wtmp[3][TK_WAVES];
-  uint32_t info[8];
+  uint32_t info[4];
 };
+
+typedef uint64_t lanemask;  // one bit per element a thread holds
 
 // ---------------------------------------------------------------- wave ops
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
@@ -79,35 +88,6 @@ __device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
   return ((uint64_t)xor_lane<M>((uint32_t)(v >> 32)) << 32) | xor_lane<M>((uint32_t)v);
 }
 
-// Wave-wide sum / max / min; every lane gets the result.
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-  v += xor_lane<1>(v);
-  v += xor_lane<2>(v);
-  v += xor_lane<4>(v);
-  v += xor_lane<8>(v);
-  v += xor_lane<16>(v);
-  v += xor_lane<32>(v);
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-  v = max(v, xor_lane<1>(v));
-  v = max(v, xor_lane<2>(v));
-  v = max(v, xor_lane<4>(v));
-  v = max(v, xor_lane<8>(v));
-  v = max(v, xor_lane<16>(v));
-  v = max(v, xor_lane<32>(v));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-  v = min(v, xor_lane<1>(v));
-  v = min(v, xor_lane<2>(v));
-  v = min(v, xor_lane<4>(v));
-  v = min(v, xor_lane<8>(v));
-  v = min(v, xor_lane<16>(v));
-  v = min(v, xor_lane<32>(v));
-  return v;
-}
-
 // Inclusive prefix sum across the wave: row shifts, then row broadcasts.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr 1
@@ -119,74 +99,71 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// Inclusive prefix over each 16-lane row (lanes shifted in from outside the
+// row read `ident`): lane 15 of a row holds the row's whole reduction.
+template <typename Op>
+__device__ __forceinline__ uint32_t row_incl(uint32_t v, uint32_t ident, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x111, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x112, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x114, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x118, 0xF, 0xF, false));
+  return v;
+}
+
+// Reduction over the wave, returned to every lane (formed in lane 63 by the
+// row prefixes and two row broadcasts).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, uint32_t ident, Op op) {
+  v = row_incl(v, ident, op);
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x142, 0xA, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+
 // ---------------------------------------------------------------- block ops
+//
+// The wave partials go through LDS once; every wave combines them in the
+// lanes of one row with DPP and broadcasts the result with readlane.
 
 // Block-wide (sum of a, max of b, min of c); every thread gets the results.
 __device__ __forceinline__ void block_sum_max_min(uint32_t& a, uint32_t& b, uint32_t& c, TkSmem& sm) {
-  const int wave = threadIdx.x >> 6;
-  a = wave_sum(a);
-  b = wave_max(b);
-  c = wave_min(c);
+  const int wave = wave_id();
+  a = wave_reduce(a, 0u, OpAdd());
+  b = wave_reduce(b, 0u, OpMax());
+  c = wave_reduce(c, 0xFFFFFFFFu, OpMin());
   if (lane_id() == 0) {
     sm.wtmp[0][wave] = a;
     sm.wtmp[1][wave] = b;
     sm.wtmp[2][wave] = c;
   }
   __syncthreads();
-  a = 0;
-  b = 0;
-  c = 0xFFFFFFFFu;
-#pragma unroll
-  for (int i = 0; i < TK_WAVES; ++i) {
-    a += sm.wtmp[0][i];
-    b = max(b, sm.wtmp[1][i]);
-    c = min(c, sm.wtmp[2][i]);
-  }
+  const int l = lane_id() & 15;
+  const bool in = l < TK_WAVES;
+  a = row_incl(in ? sm.wtmp[0][in ? l : 0] : 0u, 0u, OpAdd());
+  b = row_incl(in ? sm.wtmp[1][in ? l : 0] : 0u, 0u, OpMax());
+  c = row_incl(in ? sm.wtmp[2][in ? l : 0] : 0xFFFFFFFFu, 0xFFFFFFFFu, OpMin());
+  a = (uint32_t)__builtin_amdgcn_readlane((int)a, TK_WAVES - 1);
+  b = (uint32_t)__builtin_amdgcn_readlane((int)b, TK_WAVES - 1);
+  c = (uint32_t)__builtin_amdgcn_readlane((int)c, TK_WAVES - 1);
   __syncthreads();
 }
 
 // Exclusive prefix sum over the block in thread order; *total gets the sum.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, TkSmem& sm) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const uint32_t incl = wave_incl_scan(v);
   if (lane_id() == 63) sm.wtmp[0][wave] = incl;
   __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < TK_WAVES; ++i) {
-    const uint32_t s = sm.wtmp[0][i];
-    before += i < wave ? s : 0u;
-    all += s;
-  }
+  const int l = lane_id() & 15;
+  const uint32_t x = row_incl(l < TK_WAVES ? sm.wtmp[0][l < TK_WAVES ? l : 0] : 0u, 0u, OpAdd());
+  const uint32_t before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)x, wave - 1) : 0u;
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)x, TK_WAVES - 1);
   __syncthreads();
-  *total = all;
   return before + incl - v;
-}
-
-// Appends the keys for which pick(e) holds to an LDS list; one atomic per wave.
-template <typename Pred>
-__device__ __forceinline__ void wave_compact(const uint64_t (&key)[TK_E], Pred pick, uint32_t* counter,
-                                             uint64_t* list, uint32_t cap) {
-  uint64_t m[TK_E];
-  uint32_t tot = 0;
-#pragma unroll
-  for (int e = 0; e < TK_E; ++e) {
-    m[e] = __ballot(pick(e));
-    tot += (uint32_t)__popcll(m[e]);
-  }
-  uint32_t base = 0;
-  if (tot != 0) {
-    if (lane_id() == 0) base = atomicAdd(counter, tot);
-    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-  }
-#pragma unroll
-  for (int e = 0; e < TK_E; ++e) {
-    const uint32_t below =
-        __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], 0u));
-    const uint32_t slot = base + below;
-    if (((m[e] >> lane_id()) & 1ull) && slot < cap) list[slot] = key[e];
-    base += (uint32_t)__popcll(m[e]);
-  }
 }
 
 // ---------------------------------------------------------------- sort
@@ -201,13 +178,28 @@ __device__ __forceinline__ uint64_t cmpx(uint64_t v, uint64_t p, int i) {
   return (gt == (lower == desc)) ? v : p;
 }
 
+template <int N>
+constexpr int sort_slots() { return N > TK_T ? N / TK_T : 1; }
+
+// Element i of the N being sorted lives in thread i % TK_T, slot i / TK_T.
 template <int SIZE, int STRIDE, int N>
-__device__ __forceinline__ void sort_stage(uint64_t (&v)[2], TkSmem& sm, int& pb) {
-  constexpr int SLOTS = N > TK_T ? 2 : 1;
+__device__ __forceinline__ void sort_stage(uint64_t (&v)[sort_slots<N>()], TkSmem& sm, int& pb) {
+  constexpr int SLOTS = sort_slots<N>();
   const int tid = threadIdx.x;
   const bool active = tid < N;
-  if constexpr (STRIDE >= WAVE && STRIDE < TK_T) {
-    uint64_t* x = pb ? sm.xbuf : sm.buf[0];
+  if constexpr (STRIDE >= TK_T) {
+    // partner in another slot of the same thread
+    constexpr int SS = STRIDE / TK_T;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      if ((s & SS) == 0) {
+        const uint64_t a = v[s], b = v[s | SS];
+        v[s] = cmpx<SIZE, STRIDE>(a, b, tid + TK_T * s);
+        v[s | SS] = cmpx<SIZE, STRIDE>(b, a, tid + TK_T * (s | SS));
+      }
+    }
+  } else if constexpr (STRIDE >= WAVE) {
+    uint64_t* x = pb ? sm.xbuf : sm.buf;
     if (active) {
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) x[tid + TK_T * s] = v[s];
@@ -221,12 +213,6 @@ __device__ __forceinline__ void sort_stage(uint64_t (&v)[2], TkSmem& sm, int& pb
       }
     }
     pb ^= 1;
-  } else if constexpr (STRIDE == TK_T) {
-    if (active) {
-      const uint64_t a = v[0], b = v[1];
-      v[0] = cmpx<SIZE, STRIDE>(a, b, tid);
-      v[1] = cmpx<SIZE, STRIDE>(b, a, tid + TK_T);
-    }
   } else {
     if (active) {
 #pragma unroll
@@ -237,37 +223,35 @@ __device__ __forceinline__ void sort_stage(uint64_t (&v)[2], TkSmem& sm, int& pb
 }
 
 template <int SIZE, int STRIDE, int N>
-__device__ __forceinline__ void sort_merge(uint64_t (&v)[2], TkSmem& sm, int& pb) {
+__device__ __forceinline__ void sort_merge(uint64_t (&v)[sort_slots<N>()], TkSmem& sm, int& pb) {
   sort_stage<SIZE, STRIDE, N>(v, sm, pb);
   if constexpr (STRIDE > 1) sort_merge<SIZE, STRIDE / 2, N>(v, sm, pb);
 }
 
 template <int SIZE, int N>
-__device__ __forceinline__ void sort_sizes(uint64_t (&v)[2], TkSmem& sm, int& pb) {
+__device__ __forceinline__ void sort_sizes(uint64_t (&v)[sort_slots<N>()], TkSmem& sm, int& pb) {
   sort_merge<SIZE, SIZE / 2, N>(v, sm, pb);
   if constexpr (SIZE < N) sort_sizes<SIZE * 2, N>(v, sm, pb);
 }
 
-// Sorts sm.buf[0][0 .. N) descending (N a power of two in [64, 2048]; entries
-// past the live ones must be 0).  Element i lives in thread i % 1024, slot
-// i / 1024; the LDS exchange stages alternate between sm.buf[0] and sm.xbuf.
+// Sorts sm.buf[0 .. N) descending (N a power of two in [64, 2048]; entries
+// past the live ones must be 0); the LDS exchange stages alternate between
+// sm.buf and sm.xbuf.
 template <int N>
 __device__ void sort_desc(TkSmem& sm) {
-  constexpr int SLOTS = N > TK_T ? 2 : 1;
+  constexpr int SLOTS = sort_slots<N>();
   const int tid = threadIdx.x;
-  uint64_t v[2] = {0ull, 0ull};
+  uint64_t v[SLOTS];
   __syncthreads();
-  if (tid < N) {
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) v[s] = sm.buf[0][tid + TK_T * s];
-  }
+  for (int s = 0; s < SLOTS; ++s) v[s] = tid < N ? sm.buf[tid + TK_T * s] : 0ull;
   __syncthreads();
   int pb = 0;
   sort_sizes<2, N>(v, sm, pb);
   __syncthreads();
   if (tid < N) {
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) sm.buf[0][tid + TK_T * s] = v[s];
+    for (int s = 0; s < SLOTS; ++s) sm.buf[tid + TK_T * s] = v[s];
   }
   __syncthreads();
 }
@@ -284,128 +268,261 @@ __device__ void sort_desc_n(int n, TkSmem& sm) {
 }
 
 // ---------------------------------------------------------------- select
+//
+// The helpers below work on E values per thread (E = 16 for a whole chunk,
+// E = 2 for the compacted candidates), thread t holding positions
+// E*t .. E*t + E - 1, so thread order is position order.
 
-struct TkResult {
-  uint32_t n_def;  // sorted definite keys at sm.buf[0][0 .. n_def)
-  uint32_t n_bnd;  // sorted boundary keys at sm.buf[1][0 .. n_bnd)
-  uint32_t count;  // min(K, #valid keys)
+// One radix pass over the values v[e] with act bit e set and (v & pmask) ==
+// prefix: histogram of bits [lo, lo + width) and a suffix scan.  Returns, in
+// *d / *n_above / *n_eq, the bin holding the r-th largest such value (r >= 1),
+// the number of values in higher bins and the number in that bin.
+template <int E>
+__device__ __forceinline__ void radix_pass(const uint32_t (&v)[E], lanemask act, uint32_t prefix,
+                                           uint32_t pmask, int lo, int width, uint32_t r, TkSmem& sm,
+                                           uint32_t* d, uint32_t* n_above, uint32_t* n_eq) {
+  const int tid = threadIdx.x;
+  const int nbins = 1 << width;
+  for (int i = tid; i < nbins; i += TK_T) sm.hist[i] = 0;
+  __syncthreads();
+  // inactive values count into the lane's own dummy bin: no branches and no
+  // collisions between lanes on a shared dummy
+  const uint32_t dummy = TK_BINS + (uint32_t)lane_id();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool in = ((act >> e) & 1u) && (v[e] & pmask) == prefix;
+    atomicAdd(&sm.hist[in ? (v[e] >> lo) & (uint32_t)(nbins - 1) : dummy], 1u);
+  }
+  __syncthreads();
+  // thread t owns bins [t*bpt, t*bpt + bpt); ranks count from the top bin
+  const int bpt = nbins >= TK_T ? nbins / TK_T : 1;
+  const int b0 = tid * bpt;
+  uint32_t mine = 0;
+  if (b0 < nbins)
+    for (int i = 0; i < bpt; ++i) mine += sm.hist[b0 + i];
+  uint32_t total;
+  const uint32_t excl = block_excl_scan(mine, &total, sm);
+  uint32_t above = total - excl - mine;
+  if (b0 < nbins) {
+    for (int i = bpt - 1; i >= 0; --i) {
+      const uint32_t h = sm.hist[b0 + i];
+      if (above < r && above + h >= r) {
+        sm.info[0] = (uint32_t)(b0 + i);
+        sm.info[1] = above;
+        sm.info[2] = h;
+      }
+      above += h;
+    }
+  }
+  __syncthreads();
+  *d = sm.info[0];
+  *n_above = sm.info[1];
+  *n_eq = sm.info[2];
+  __syncthreads();
+}
+
+// The region of values holding the r-th largest active value: (v & pmask) ==
+// prefix, with r of its n_eq values wanted.  `whole`: all of them (r ==
+// n_eq); `single`: the region is one exact value.  Neither: more bits remain.
+struct TkRegion {
+  uint32_t prefix, pmask, r, n_eq;
+  bool whole, single;
+  __device__ uint32_t top() const { return prefix | ~pmask; }  // largest value of the region
 };
 
-// Top K of the non-zero keys held by the block (TK_E per thread).
-__device__ TkResult block_topk(uint64_t (&key)[TK_E], int K, TkSmem& sm) {
-  const int tid = threadIdx.x;
-  uint32_t n_all = 0, hmax = 0, hmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int e = 0; e < TK_E; ++e) {
-    if (key[e] != 0) {
-      const uint32_t hi = (uint32_t)(key[e] >> 32);
-      ++n_all;
-      hmax = max(hmax, hi);
-      hmin = min(hmin, hi);
-    }
+// Radix select of the r-th largest of the active values (r <= their count),
+// starting below the bits they all share; at most max_passes passes.
+template <int E>
+__device__ TkRegion radix_select(const uint32_t (&v)[E], lanemask act, uint32_t r, uint32_t vmax,
+                                 uint32_t vmin, uint32_t count, int max_passes, TkSmem& sm) {
+  TkRegion g;
+  const uint32_t diff = vmax ^ vmin;
+  if (diff == 0) {  // every active value is the same
+    g.prefix = vmax;
+    g.pmask = 0xFFFFFFFFu;
+    g.r = r;
+    g.n_eq = count;
+    g.whole = r == count;
+    g.single = true;
+    return g;
   }
-  if (tid == 0) {
-    sm.info[4] = 0;
-    sm.info[5] = 0;
+  int top = 31 - __clz(diff);
+  g.pmask = top == 31 ? 0u : ~((2u << top) - 1u);
+  g.prefix = vmax & g.pmask;
+  g.r = r;
+  for (int pass = 0;; ++pass) {
+    const int width = min(TK_BITS, top + 1);
+    const int lo = top - width + 1;
+    uint32_t d, n_above, n_eq;
+    radix_pass<E>(v, act, g.prefix, g.pmask, lo, width, g.r, sm, &d, &n_above, &n_eq);
+    g.prefix |= d << lo;
+    g.pmask |= (uint32_t)((1u << width) - 1u) << lo;
+    g.r -= n_above;
+    g.n_eq = n_eq;
+    g.whole = n_eq == g.r;
+    g.single = lo == 0;
+    if (g.whole || g.single || pass + 1 >= max_passes) return g;
+    top = lo - 1;
   }
-  block_sum_max_min(n_all, hmax, hmin, sm);
+}
 
-  // definite: key > t_def; boundary: t_lo <= key <= t_def
-  uint64_t t_def = ~0ull, t_lo = 1ull;
-  bool dup = false;
-  if (n_all > (uint32_t)K) {
-    int top;
-    uint64_t prefix, pmask;
-    const uint32_t diff = hmax ^ hmin;
-    if (diff) {
-      top = 32 + 31 - __clz(diff);
-      pmask = ~((2ull << top) - 1ull);
-    } else {
-      top = 31;
-      pmask = 0xFFFFFFFF00000000ull;
+// Block-wide count, max and min of the active values.
+template <int E>
+__device__ __forceinline__ void active_stats(const uint32_t (&v)[E], lanemask act, TkSmem& sm,
+                                             uint32_t* count, uint32_t* vmax, uint32_t* vmin) {
+  uint32_t n = (uint32_t)__popcll(act), hi = 0, lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool a = (act >> e) & 1u;
+    hi = max(hi, a ? v[e] : 0u);
+    lo = min(lo, a ? v[e] : 0xFFFFFFFFu);
+  }
+  block_sum_max_min(n, hi, lo, sm);
+  *count = n;
+  *vmax = hi;
+  *vmin = lo;
+}
+
+template <int E>
+__device__ __forceinline__ void region_masks(const uint32_t (&v)[E], lanemask act, const TkRegion& g,
+                                             lanemask* above, lanemask* in) {
+  lanemask a = 0, i = 0;
+  const uint32_t top = g.top();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool on = (act >> e) & 1u;
+    a |= (lanemask)(on && v[e] > top) << e;
+    i |= (lanemask)(on && (v[e] & g.pmask) == g.prefix) << e;
+  }
+  *above = a;
+  *in = i;
+}
+
+// The first r of the `take` elements in position order (one block scan).
+template <int E>
+__device__ __forceinline__ lanemask first_in_order(lanemask take, uint32_t r, TkSmem& sm) {
+  uint32_t total;
+  lanemask sel = 0;
+  uint32_t k = block_excl_scan((uint32_t)__popcll(take), &total, sm);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if ((take >> e) & 1u) {
+      if (k < r) sel |= (lanemask)1 << e;
+      ++k;
     }
-    prefix = ((uint64_t)hmax << 32) & pmask;
-    uint32_t r = (uint32_t)K;  // rank of the K-th key inside the current region
-    for (;;) {
-      const int width = min(TK_BITS, top + 1);
-      const int lo = top - width + 1;
-      const int nbins = 1 << width;
-      for (int i = tid; i < nbins; i += TK_T) sm.hist[i] = 0;
-      __syncthreads();
+  }
+  return sel;
+}
+
+// Given a region that is one exact score with r of its copies wanted (`in`):
+// the r lowest ids, identical (score, id) pairs taken in position order.
+// `nid_in_order`: nid = ~id falls with the position (ids are the columns).
+template <int E>
+__device__ lanemask cut_tie(const uint32_t (&nid)[E], lanemask in, uint32_t r, bool nid_in_order,
+                            TkSmem& sm) {
+  lanemask sel = 0, take = in;
+  if (!nid_in_order) {
+    uint32_t cnt, vmax, vmin;
+    active_stats<E>(nid, in, sm, &cnt, &vmax, &vmin);
+    const TkRegion h = radix_select<E>(nid, in, r, vmax, vmin, cnt, 99, sm);
+    lanemask h_above, h_in;
+    region_masks<E>(nid, in, h, &h_above, &h_in);
+    sel = h_above;
+    if (h.whole) return sel | h_in;
+    take = h_in;  // repeated (score, id) pairs
+    r = h.r;
+  }
+  return sel | first_in_order<E>(take, r, sm);
+}
+
+// Mask of the r active elements with the largest (hi, nid) pairs.
+template <int E>
+__device__ lanemask select_top(const uint32_t (&hi)[E], const uint32_t (&nid)[E], lanemask act, uint32_t r,
+                               bool nid_in_order, TkSmem& sm) {
+  uint32_t cnt, vmax, vmin;
+  active_stats<E>(hi, act, sm, &cnt, &vmax, &vmin);
+  const TkRegion g = radix_select<E>(hi, act, r, vmax, vmin, cnt, 99, sm);
+  lanemask sel, in;
+  region_masks<E>(hi, act, g, &sel, &in);
+  if (g.whole) return sel | in;
+  return sel | cut_tie<E>(nid, in, g.r, nid_in_order, sm);
+}
+
+// Writes the selected elements' keys to dst[base + ...] in position order;
+// returns how many there are.
+template <int E>
+__device__ __forceinline__ uint32_t compact(const uint32_t (&hi)[E], const uint32_t (&nid)[E], lanemask sel,
+                                            uint64_t* dst, uint32_t base, TkSmem& sm) {
+  uint32_t total;
+  uint32_t pos = base + block_excl_scan((uint32_t)__popcll(sel), &total, sm);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if ((sel >> e) & 1u) {
+      if (pos < (uint32_t)TK_KMAX) dst[pos] = ((uint64_t)hi[e] << 32) | (uint64_t)nid[e];
+      ++pos;
+    }
+  }
+  return total;
+}
+
+// Top K of the candidates (sk[e] score keys, 0 = empty; nid[e] = ~id) held by
+// the block, thread t owning positions 16t .. 16t + 15 in column order.
+// Writes the selected keys to sm.buf[0 .. count), count = min(K, #valid).
+__device__ uint32_t block_select(const uint32_t (&sk)[TK_E], const uint32_t (&nid)[TK_E],
+                                 bool ids_are_columns, int K, TkSmem& sm) {
+  lanemask valid = 0;
+#pragma unroll
+  for (int e = 0; e < TK_E; ++e) valid |= (lanemask)(sk[e] != 0) << e;
+  uint32_t n_all, smax, smin;
+  active_stats<TK_E>(sk, valid, sm, &n_all, &smax, &smin);
+  uint32_t count;
+  if (n_all <= (uint32_t)K) {
+    count = compact<TK_E>(sk, nid, valid, sm.buf, 0, sm);
+  } else {
+    // one radix pass over the whole chunk
+    const TkRegion g = radix_select<TK_E>(sk, valid, (uint32_t)K, smax, smin, n_all, 1, sm);
+    lanemask above, in;
+    region_masks<TK_E>(sk, valid, g, &above, &in);
+    if (g.whole || g.single || g.n_eq > (uint32_t)TK_KMAX) {
+      lanemask sel = above;
+      if (g.whole) sel |= in;
+      else if (g.single) sel |= cut_tie<TK_E>(nid, in, g.r, ids_are_columns, sm);
+      else sel |= select_top<TK_E>(sk, nid, in, g.r, ids_are_columns, sm);  // a huge bin
+      count = compact<TK_E>(sk, nid, sel, sm.buf, 0, sm);
+    } else {
+      // the keys above the boundary bin go straight to the output buffer, the
+      // n_eq <= 2048 keys of the bin to the candidate buffer (both in column
+      // order, one scan of packed counts); the rest of the selection runs on
+      // the candidates, TK_CE per thread
+      uint32_t total;
+      const uint32_t x =
+          block_excl_scan(((uint32_t)__popcll(above) << 16) | (uint32_t)__popcll(in), &total, sm);
+      uint32_t pa = x >> 16, pi = x & 0xFFFFu;
 #pragma unroll
       for (int e = 0; e < TK_E; ++e) {
-        if (key[e] != 0 && (key[e] & pmask) == prefix)
-          atomicAdd(&sm.hist[(uint32_t)(key[e] >> lo) & (uint32_t)(nbins - 1)], 1u);
+        const uint64_t key = ((uint64_t)sk[e] << 32) | (uint64_t)nid[e];
+        if ((above >> e) & 1u) sm.buf[pa++] = key;
+        if ((in >> e) & 1u) sm.xbuf[pi++] = key;
       }
+      const uint32_t n_above = (uint32_t)K - g.r;
       __syncthreads();
-      // thread t owns bins [t*bpt, t*bpt + bpt); ranks count from the top bin
-      const int bpt = nbins >= TK_T ? nbins / TK_T : 1;
-      const int b0 = tid * bpt;
-      uint32_t mine = 0;
-      if (b0 < nbins)
-        for (int i = 0; i < bpt; ++i) mine += sm.hist[b0 + i];
-      uint32_t total;
-      const uint32_t excl = block_excl_scan(mine, &total, sm);
-      uint32_t above = total - excl - mine;
-      if (b0 < nbins) {
-        for (int d = b0 + bpt - 1; d >= b0; --d) {
-          const uint32_t h = sm.hist[d];
-          if (above < r && above + h >= r) {
-            sm.info[0] = (uint32_t)d;
-            sm.info[1] = above;
-            sm.info[2] = h;
-          }
-          above += h;
-        }
+      uint32_t chi[TK_CE], cnid[TK_CE];
+      lanemask cact = 0;
+#pragma unroll
+      for (int e = 0; e < TK_CE; ++e) {
+        const uint32_t j = (uint32_t)(TK_CE * threadIdx.x + e);
+        const uint64_t key = j < g.n_eq ? sm.xbuf[j] : 0ull;
+        chi[e] = (uint32_t)(key >> 32);
+        cnid[e] = (uint32_t)key;
+        cact |= (lanemask)(j < g.n_eq) << e;
       }
-      __syncthreads();
-      const uint32_t d = sm.info[0], n_above = sm.info[1], n_eq = sm.info[2];
-      __syncthreads();
-      prefix |= (uint64_t)d << lo;
-      pmask |= (uint64_t)(nbins - 1) << lo;
-      r -= n_above;
-      t_lo = prefix;
-      t_def = prefix | ((1ull << lo) - 1ull);
-      if (n_eq <= (uint32_t)TK_CAP) break;
-      if (lo == 0) {  // one exact key repeated more than TK_CAP times
-        dup = true;
-        break;
-      }
-      top = lo - 1;
+      const lanemask csel = select_top<TK_CE>(chi, cnid, cact, g.r, ids_are_columns, sm);
+      (void)compact<TK_CE>(chi, cnid, csel, sm.buf, n_above, sm);
+      count = (uint32_t)K;
     }
   }
-  // compact: definite -> buf[0], boundary -> buf[1]
-  wave_compact(key, [&](int e) { return key[e] > t_def; }, &sm.info[4], sm.buf[0], TK_CAP);
-  wave_compact(key, [&](int e) { return key[e] != 0 && key[e] >= t_lo && key[e] <= t_def; }, &sm.info[5],
-               sm.buf[1], TK_CAP);
   __syncthreads();
-  TkResult res;
-  res.n_def = sm.info[4];
-  res.n_bnd = min(sm.info[5], (uint32_t)TK_CAP);
-  res.count = min(n_all, (uint32_t)K);
-  __syncthreads();
-  // sort the definite set in place
-  if (res.n_def > 0) {
-    int n = 64;
-    while (n < (int)res.n_def) n <<= 1;
-    for (int j = (int)res.n_def + tid; j < n; j += TK_T) sm.buf[0][j] = 0ull;
-    sort_desc_n(n, sm);
-  }
-  // sort the boundary set (identical keys when dup): park the definite keys in
-  // the histogram area (<= 2047 keys fit in its 32 KiB), sort through buf[0]
-  if (!dup && res.n_bnd > 1 && res.n_def < (uint32_t)K) {
-    uint64_t* park = reinterpret_cast<uint64_t*>(sm.hist);
-    for (int j = tid; j < (int)res.n_def; j += TK_T) park[j] = sm.buf[0][j];
-    int nb = 64;
-    while (nb < (int)res.n_bnd) nb <<= 1;
-    __syncthreads();
-    for (int j = tid; j < nb; j += TK_T) sm.buf[0][j] = j < (int)res.n_bnd ? sm.buf[1][j] : 0ull;
-    sort_desc_n(nb, sm);
-    for (int j = tid; j < (int)res.n_bnd; j += TK_T) sm.buf[1][j] = sm.buf[0][j];
-    for (int j = tid; j < (int)res.n_def; j += TK_T) sm.buf[0][j] = park[j];
-    __syncthreads();
-  }
-  return res;
+  return min(count, (uint32_t)TK_KMAX);
 }
 
 template <bool FROM_SCORES, bool FINAL>
@@ -422,40 +539,71 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   const int c = (int)(blockIdx.x - b * chunks);
   const int64_t base = (int64_t)c * TK_CHUNK;
   int64_t limit = min<int64_t>(M, base + TK_CHUNK);
-  uint64_t key[TK_E];
+  const int64_t col0 = base + (int64_t)TK_E * tid;  // this thread's first column
+  uint32_t sk[TK_E], nid[TK_E];
+  bool ids_are_columns;
   if (FROM_SCORES) {
     if (n_valid) limit = min<int64_t>(limit, max<int64_t>(n_valid[b], 0));
+    ids_are_columns = ids == nullptr;
+    const float* srow = scores + b * M;
+    const int32_t* irow = ids ? ids + b * M : nullptr;
+    if (col0 + TK_E <= limit && (M & 3) == 0) {
+      // a whole run of columns: 16-byte loads (rows stay 16-byte aligned)
 #pragma unroll
-    for (int e = 0; e < TK_E; ++e) {
-      const int64_t col = base + (int64_t)e * TK_T + tid;
-      uint64_t k = 0;
-      if (col < limit) {
-        const float s = scores[b * M + col];
-        const int32_t id = ids ? ids[b * M + col] : (int32_t)col;
-        if (id != -1) k = ((uint64_t)score_key(s) << 32) | (uint64_t)(~(uint32_t)id);
+      for (int q4 = 0; q4 < TK_E / 4; ++q4) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(srow + col0 + 4 * q4);
+        u32x4 i4;
+        if (irow) i4 = *reinterpret_cast<const u32x4*>(irow + col0 + 4 * q4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * q4 + j;
+          const uint32_t i = irow ? i4[j] : (uint32_t)(col0 + e);
+          nid[e] = ~i;
+          sk[e] = i != 0xFFFFFFFFu ? score_key(v4[j]) : 0u;
+        }
       }
-      key[e] = k;
+    } else {
+#pragma unroll
+      for (int e = 0; e < TK_E; ++e) {
+        const int64_t col = col0 + e;
+        uint32_t k = 0, i = 0;
+        if (col < limit) {
+          i = irow ? (uint32_t)irow[col] : (uint32_t)col;
+          if (i != 0xFFFFFFFFu) k = score_key(srow[col]);
+        }
+        sk[e] = k;
+        nid[e] = ~i;
+      }
     }
   } else {
+    ids_are_columns = false;
+    const uint64_t* krow = keys_in + b * M;
 #pragma unroll
     for (int e = 0; e < TK_E; ++e) {
-      const int64_t col = base + (int64_t)e * TK_T + tid;
-      key[e] = col < limit ? keys_in[b * M + col] : 0ull;
+      const int64_t col = col0 + e;
+      const uint64_t k = col < limit ? krow[col] : 0ull;
+      sk[e] = (uint32_t)(k >> 32);
+      nid[e] = (uint32_t)k;
     }
   }
-  const TkResult res = block_topk(key, K, sm);
-  // output position j: definite keys first, then the boundary keys
-  for (int j = tid; j < K; j += TK_T) {
-    uint64_t k = 0;
-    if (j < (int)res.count)
-      k = j < (int)res.n_def ? sm.buf[0][j] : sm.buf[1][min(j - (int)res.n_def, TK_CAP - 1)];
-    if (FINAL) {
-      const bool ok = j < (int)res.count;
+  const uint32_t count = block_select(sk, nid, ids_are_columns, K, sm);
+  if (FINAL) {
+    // sort the selected keys descending: (score desc, id asc)
+    if (count > 1) {
+      int n = 64;
+      while (n < (int)count) n <<= 1;
+      for (int j = (int)count + tid; j < n; j += TK_T) sm.buf[j] = 0ull;
+      sort_desc_n(n, sm);
+    }
+    for (int j = tid; j < K; j += TK_T) {
+      const bool ok = j < (int)count;
+      const uint64_t k = ok ? sm.buf[j] : 0ull;
       out_idx[b * K + j] = ok ? (int32_t)(~(uint32_t)k) : -1;
       if (out_score) out_score[b * K + j] = ok ? key_score((uint32_t)(k >> 32)) : -INFINITY;
-    } else {
-      keys_out[(b * chunks + c) * (int64_t)K + j] = k;
     }
+  } else {
+    for (int j = tid; j < K; j += TK_T)
+      keys_out[(b * chunks + c) * (int64_t)K + j] = j < (int)count ? sm.buf[j] : 0ull;
   }
 }
 

@@ -86,3 +86,12 @@ def test_topk_indexer_workload_rows():
     rng = np.random.default_rng(42)
     s = _scores(rng, 8, 262144, "int_scores")
     _check(s, 512)
+
+
+@pytest.mark.parametrize("M,K", [(1000, 64), (16384, 512), (40000, 512)])
+def test_topk_repeated_score_id_pairs(M, K):
+    note(f"topk: repeated (score, id) pairs M={M} K={K}")
+    rng = np.random.default_rng(M + 5)
+    s = rng.integers(0, 6, size=(2, M)).astype(np.float32)
+    ids = rng.integers(0, 50, size=(2, M)).astype(np.int32)   # every id repeated many times
+    _check(s, K, ids=ids)
