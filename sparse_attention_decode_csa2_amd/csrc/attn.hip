@@ -426,32 +426,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 }
 
 // Merge the per-slice partial results of one (b, h) row by log-sum-exp; each
-// of the 128 threads owns 4 consecutive channels.
+// of the 128 threads owns 4 consecutive channels (d_c <= 512).  The slices are
+// taken 8 at a time with every load of a round issued together (one memory
+// round trip per 8 slices), merged online.  Block x runs on XCD x % 8 like the
+// attention workgroups of its query, whose partials sit in that XCD's L2.
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ ws_o,
                                                            const float* __restrict__ ws_ml,
-                                                           int n_split, int DC,
+                                                           int B, int H, int n_split, int DC,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
-  const int64_t row = blockIdx.x;
+  constexpr int R = 8;
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int64_t b = (int64_t)(slot / H) * 8 + xcd;
+  if (b >= B) return;
+  const int64_t row = b * H + slot % H;
   const float* ml = ws_ml + row * n_split * 2;
-  float m = -INFINITY;
-  for (int s = 0; s < n_split; ++s) m = fmaxf(m, ml[2 * s]);
-  float L = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float ms = ml[2 * s];
-    L += ms == -INFINITY ? 0.f : exp2f(ms - m) * ml[2 * s + 1];
+  const int c = 4 * threadIdx.x;
+  const bool has = c < DC;
+  const float* po = ws_o + row * n_split * DC + (has ? c : 0);
+  float m = -INFINITY, L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_split; s0 += R) {
+    float mm[R], ll[R];
+    f32x4 v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const bool ok = s0 + j < n_split;
+      mm[j] = ok ? ml[2 * (s0 + j)] : -INFINITY;
+      ll[j] = ok ? ml[2 * (s0 + j) + 1] : 0.f;
+      v[j] = ok && has ? *reinterpret_cast<const f32x4*>(po + (int64_t)(s0 + j) * DC) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mn = m;
+#pragma unroll
+    for (int j = 0; j < R; ++j) mn = fmaxf(mn, mm[j]);
+    const float a = mn == -INFINITY ? 1.f : exp2f(m - mn);
+    L *= a;
+    o *= a;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float w = mm[j] == -INFINITY ? 0.f : exp2f(mm[j] - mn);
+      L += w * ll[j];
+      o += v[j] * w;
+    }
+    m = mn;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  for (int c = threadIdx.x * 4; c < DC; c += 512) {
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_split; ++s) {
-      const float ms = ml[2 * s];
-      const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - m);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(ws_o + (row * n_split + s) * DC + c);
-      o += v * wgt;
-    }
-    *reinterpret_cast<f32x4*>(out + row * DC + c) = o * inv;
-  }
+  if (has) *reinterpret_cast<f32x4*>(out + row * DC + c) = o * inv;
   if (lse && threadIdx.x == 0) lse[row] = L > 0.f ? (m + __log2f(L)) * LN2 : -INFINITY;
 }
 
@@ -500,8 +521,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
 #undef CSA2_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)B * H)), dim3(128), 0, stream, ws_o,
-                     ws_ml, s, d_c, out, lse);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(groups * 8 * H)), dim3(128), 0, stream, ws_o,
+                     ws_ml, B, H, s, d_c, out, lse);
   return hipGetLastError();
 }
 
