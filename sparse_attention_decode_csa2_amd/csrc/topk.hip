@@ -45,7 +45,7 @@ struct TkSmem {
   uint32_t hist[TK_BINS + WAVE];  // radix histogram + one dummy bin per lane
   uint64_t buf[TK_KMAX];          // the selected keys
   uint64_t xbuf[TK_KMAX];         // candidates; second buffer of the sort's LDS exchanges
-  uint32_t wtmp[3][TK_WAVES];
+  uint32_t wtmp[2][3][TK_WAVES];  // wave partials of block ops, two alternating sets
   uint32_t info[4];
 };
 
@@ -127,42 +127,48 @@ struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { re
 // ---------------------------------------------------------------- block ops
 //
 // The wave partials go through LDS once; every wave combines them in the
-// lanes of one row with DPP and broadcasts the result with readlane.
+// lanes of one row with DPP and broadcasts the result with readlane.  Block
+// ops alternate between two sets of partials (`par`, identical in every
+// thread), so each needs a single barrier: a set is rewritten two ops later,
+// after a barrier every thread has passed only once done reading it.
 
 // Block-wide (sum of a, max of b, min of c); every thread gets the results.
-__device__ __forceinline__ void block_sum_max_min(uint32_t& a, uint32_t& b, uint32_t& c, TkSmem& sm) {
+__device__ __forceinline__ void block_sum_max_min(uint32_t& a, uint32_t& b, uint32_t& c, TkSmem& sm,
+                                                  int& par) {
   const int wave = wave_id();
   a = wave_reduce(a, 0u, OpAdd());
   b = wave_reduce(b, 0u, OpMax());
   c = wave_reduce(c, 0xFFFFFFFFu, OpMin());
+  uint32_t(&w)[3][TK_WAVES] = sm.wtmp[par];
   if (lane_id() == 0) {
-    sm.wtmp[0][wave] = a;
-    sm.wtmp[1][wave] = b;
-    sm.wtmp[2][wave] = c;
+    w[0][wave] = a;
+    w[1][wave] = b;
+    w[2][wave] = c;
   }
   __syncthreads();
   const int l = lane_id() & 15;
   const bool in = l < TK_WAVES;
-  a = row_incl(in ? sm.wtmp[0][in ? l : 0] : 0u, 0u, OpAdd());
-  b = row_incl(in ? sm.wtmp[1][in ? l : 0] : 0u, 0u, OpMax());
-  c = row_incl(in ? sm.wtmp[2][in ? l : 0] : 0xFFFFFFFFu, 0xFFFFFFFFu, OpMin());
+  a = row_incl(in ? w[0][in ? l : 0] : 0u, 0u, OpAdd());
+  b = row_incl(in ? w[1][in ? l : 0] : 0u, 0u, OpMax());
+  c = row_incl(in ? w[2][in ? l : 0] : 0xFFFFFFFFu, 0xFFFFFFFFu, OpMin());
   a = (uint32_t)__builtin_amdgcn_readlane((int)a, TK_WAVES - 1);
   b = (uint32_t)__builtin_amdgcn_readlane((int)b, TK_WAVES - 1);
   c = (uint32_t)__builtin_amdgcn_readlane((int)c, TK_WAVES - 1);
-  __syncthreads();
+  par ^= 1;
 }
 
 // Exclusive prefix sum over the block in thread order; *total gets the sum.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, TkSmem& sm) {
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, TkSmem& sm, int& par) {
   const int wave = wave_id();
   const uint32_t incl = wave_incl_scan(v);
-  if (lane_id() == 63) sm.wtmp[0][wave] = incl;
+  uint32_t(&w)[3][TK_WAVES] = sm.wtmp[par];
+  if (lane_id() == 63) w[0][wave] = incl;
   __syncthreads();
   const int l = lane_id() & 15;
-  const uint32_t x = row_incl(l < TK_WAVES ? sm.wtmp[0][l < TK_WAVES ? l : 0] : 0u, 0u, OpAdd());
+  const uint32_t x = row_incl(l < TK_WAVES ? w[0][l < TK_WAVES ? l : 0] : 0u, 0u, OpAdd());
   const uint32_t before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)x, wave - 1) : 0u;
   *total = (uint32_t)__builtin_amdgcn_readlane((int)x, TK_WAVES - 1);
-  __syncthreads();
+  par ^= 1;
   return before + incl - v;
 }
 
@@ -276,15 +282,15 @@ __device__ void sort_desc_n(int n, TkSmem& sm) {
 // One radix pass over the values v[e] with act bit e set and (v & pmask) ==
 // prefix: histogram of bits [lo, lo + width) and a suffix scan.  Returns, in
 // *d / *n_above / *n_eq, the bin holding the r-th largest such value (r >= 1),
-// the number of values in higher bins and the number in that bin.
+// the number of values in higher bins and the number in that bin.  The
+// histogram is all zero on entry and is left so: each thread reads only the
+// bins it owns and clears them after use.
 template <int E>
 __device__ __forceinline__ void radix_pass(const uint32_t (&v)[E], lanemask act, uint32_t prefix,
                                            uint32_t pmask, int lo, int width, uint32_t r, TkSmem& sm,
-                                           uint32_t* d, uint32_t* n_above, uint32_t* n_eq) {
+                                           int& par, uint32_t* d, uint32_t* n_above, uint32_t* n_eq) {
   const int tid = threadIdx.x;
   const int nbins = 1 << width;
-  for (int i = tid; i < nbins; i += TK_T) sm.hist[i] = 0;
-  __syncthreads();
   // inactive values count into the lane's own dummy bin: no branches and no
   // collisions between lanes on a shared dummy
   const uint32_t dummy = TK_BINS + (uint32_t)lane_id();
@@ -297,28 +303,32 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&v)[E], lanemask act,
   // thread t owns bins [t*bpt, t*bpt + bpt); ranks count from the top bin
   const int bpt = nbins >= TK_T ? nbins / TK_T : 1;
   const int b0 = tid * bpt;
+  uint32_t h[TK_BINS / TK_T > 0 ? TK_BINS / TK_T : 1];
   uint32_t mine = 0;
-  if (b0 < nbins)
-    for (int i = 0; i < bpt; ++i) mine += sm.hist[b0 + i];
+#pragma unroll
+  for (int i = 0; i < (TK_BINS / TK_T > 0 ? TK_BINS / TK_T : 1); ++i) {
+    h[i] = (i < bpt && b0 < nbins) ? sm.hist[b0 + i] : 0u;
+    mine += h[i];
+  }
   uint32_t total;
-  const uint32_t excl = block_excl_scan(mine, &total, sm);
+  const uint32_t excl = block_excl_scan(mine, &total, sm, par);
   uint32_t above = total - excl - mine;
-  if (b0 < nbins) {
-    for (int i = bpt - 1; i >= 0; --i) {
-      const uint32_t h = sm.hist[b0 + i];
-      if (above < r && above + h >= r) {
+#pragma unroll
+  for (int i = (TK_BINS / TK_T > 0 ? TK_BINS / TK_T : 1) - 1; i >= 0; --i) {
+    if (i < bpt && b0 < nbins) {
+      if (above < r && above + h[i] >= r) {
         sm.info[0] = (uint32_t)(b0 + i);
         sm.info[1] = above;
-        sm.info[2] = h;
+        sm.info[2] = h[i];
       }
-      above += h;
+      above += h[i];
+      sm.hist[b0 + i] = 0;
     }
   }
   __syncthreads();
   *d = sm.info[0];
   *n_above = sm.info[1];
   *n_eq = sm.info[2];
-  __syncthreads();
 }
 
 // The region of values holding the r-th largest active value: (v & pmask) ==
@@ -334,7 +344,7 @@ struct TkRegion {
 // starting below the bits they all share; at most max_passes passes.
 template <int E>
 __device__ TkRegion radix_select(const uint32_t (&v)[E], lanemask act, uint32_t r, uint32_t vmax,
-                                 uint32_t vmin, uint32_t count, int max_passes, TkSmem& sm) {
+                                 uint32_t vmin, uint32_t count, int max_passes, TkSmem& sm, int& par) {
   TkRegion g;
   const uint32_t diff = vmax ^ vmin;
   if (diff == 0) {  // every active value is the same
@@ -354,7 +364,7 @@ __device__ TkRegion radix_select(const uint32_t (&v)[E], lanemask act, uint32_t 
     const int width = min(TK_BITS, top + 1);
     const int lo = top - width + 1;
     uint32_t d, n_above, n_eq;
-    radix_pass<E>(v, act, g.prefix, g.pmask, lo, width, g.r, sm, &d, &n_above, &n_eq);
+    radix_pass<E>(v, act, g.prefix, g.pmask, lo, width, g.r, sm, par, &d, &n_above, &n_eq);
     g.prefix |= d << lo;
     g.pmask |= (uint32_t)((1u << width) - 1u) << lo;
     g.r -= n_above;
@@ -368,7 +378,7 @@ __device__ TkRegion radix_select(const uint32_t (&v)[E], lanemask act, uint32_t 
 
 // Block-wide count, max and min of the active values.
 template <int E>
-__device__ __forceinline__ void active_stats(const uint32_t (&v)[E], lanemask act, TkSmem& sm,
+__device__ __forceinline__ void active_stats(const uint32_t (&v)[E], lanemask act, TkSmem& sm, int& par,
                                              uint32_t* count, uint32_t* vmax, uint32_t* vmin) {
   uint32_t n = (uint32_t)__popcll(act), hi = 0, lo = 0xFFFFFFFFu;
 #pragma unroll
@@ -377,7 +387,7 @@ __device__ __forceinline__ void active_stats(const uint32_t (&v)[E], lanemask ac
     hi = max(hi, a ? v[e] : 0u);
     lo = min(lo, a ? v[e] : 0xFFFFFFFFu);
   }
-  block_sum_max_min(n, hi, lo, sm);
+  block_sum_max_min(n, hi, lo, sm, par);
   *count = n;
   *vmax = hi;
   *vmin = lo;
@@ -400,10 +410,10 @@ __device__ __forceinline__ void region_masks(const uint32_t (&v)[E], lanemask ac
 
 // The first r of the `take` elements in position order (one block scan).
 template <int E>
-__device__ __forceinline__ lanemask first_in_order(lanemask take, uint32_t r, TkSmem& sm) {
+__device__ __forceinline__ lanemask first_in_order(lanemask take, uint32_t r, TkSmem& sm, int& par) {
   uint32_t total;
   lanemask sel = 0;
-  uint32_t k = block_excl_scan((uint32_t)__popcll(take), &total, sm);
+  uint32_t k = block_excl_scan((uint32_t)__popcll(take), &total, sm, par);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if ((take >> e) & 1u) {
@@ -419,12 +429,12 @@ __device__ __forceinline__ lanemask first_in_order(lanemask take, uint32_t r, Tk
 // `nid_in_order`: nid = ~id falls with the position (ids are the columns).
 template <int E>
 __device__ lanemask cut_tie(const uint32_t (&nid)[E], lanemask in, uint32_t r, bool nid_in_order,
-                            TkSmem& sm) {
+                            TkSmem& sm, int& par) {
   lanemask sel = 0, take = in;
   if (!nid_in_order) {
     uint32_t cnt, vmax, vmin;
-    active_stats<E>(nid, in, sm, &cnt, &vmax, &vmin);
-    const TkRegion h = radix_select<E>(nid, in, r, vmax, vmin, cnt, 99, sm);
+    active_stats<E>(nid, in, sm, par, &cnt, &vmax, &vmin);
+    const TkRegion h = radix_select<E>(nid, in, r, vmax, vmin, cnt, 99, sm, par);
     lanemask h_above, h_in;
     region_masks<E>(nid, in, h, &h_above, &h_in);
     sel = h_above;
@@ -432,29 +442,29 @@ __device__ lanemask cut_tie(const uint32_t (&nid)[E], lanemask in, uint32_t r, b
     take = h_in;  // repeated (score, id) pairs
     r = h.r;
   }
-  return sel | first_in_order<E>(take, r, sm);
+  return sel | first_in_order<E>(take, r, sm, par);
 }
 
 // Mask of the r active elements with the largest (hi, nid) pairs.
 template <int E>
 __device__ lanemask select_top(const uint32_t (&hi)[E], const uint32_t (&nid)[E], lanemask act, uint32_t r,
-                               bool nid_in_order, TkSmem& sm) {
+                               bool nid_in_order, TkSmem& sm, int& par) {
   uint32_t cnt, vmax, vmin;
-  active_stats<E>(hi, act, sm, &cnt, &vmax, &vmin);
-  const TkRegion g = radix_select<E>(hi, act, r, vmax, vmin, cnt, 99, sm);
+  active_stats<E>(hi, act, sm, par, &cnt, &vmax, &vmin);
+  const TkRegion g = radix_select<E>(hi, act, r, vmax, vmin, cnt, 99, sm, par);
   lanemask sel, in;
   region_masks<E>(hi, act, g, &sel, &in);
   if (g.whole) return sel | in;
-  return sel | cut_tie<E>(nid, in, g.r, nid_in_order, sm);
+  return sel | cut_tie<E>(nid, in, g.r, nid_in_order, sm, par);
 }
 
 // Writes the selected elements' keys to dst[base + ...] in position order;
 // returns how many there are.
 template <int E>
 __device__ __forceinline__ uint32_t compact(const uint32_t (&hi)[E], const uint32_t (&nid)[E], lanemask sel,
-                                            uint64_t* dst, uint32_t base, TkSmem& sm) {
+                                            uint64_t* dst, uint32_t base, TkSmem& sm, int& par) {
   uint32_t total;
-  uint32_t pos = base + block_excl_scan((uint32_t)__popcll(sel), &total, sm);
+  uint32_t pos = base + block_excl_scan((uint32_t)__popcll(sel), &total, sm, par);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if ((sel >> e) & 1u) {
@@ -470,25 +480,26 @@ __device__ __forceinline__ uint32_t compact(const uint32_t (&hi)[E], const uint3
 // Writes the selected keys to sm.buf[0 .. count), count = min(K, #valid).
 __device__ uint32_t block_select(const uint32_t (&sk)[TK_E], const uint32_t (&nid)[TK_E],
                                  bool ids_are_columns, int K, TkSmem& sm) {
+  int par = 0;
   lanemask valid = 0;
 #pragma unroll
   for (int e = 0; e < TK_E; ++e) valid |= (lanemask)(sk[e] != 0) << e;
   uint32_t n_all, smax, smin;
-  active_stats<TK_E>(sk, valid, sm, &n_all, &smax, &smin);
+  active_stats<TK_E>(sk, valid, sm, par, &n_all, &smax, &smin);
   uint32_t count;
   if (n_all <= (uint32_t)K) {
-    count = compact<TK_E>(sk, nid, valid, sm.buf, 0, sm);
+    count = compact<TK_E>(sk, nid, valid, sm.buf, 0, sm, par);
   } else {
     // one radix pass over the whole chunk
-    const TkRegion g = radix_select<TK_E>(sk, valid, (uint32_t)K, smax, smin, n_all, 1, sm);
+    const TkRegion g = radix_select<TK_E>(sk, valid, (uint32_t)K, smax, smin, n_all, 1, sm, par);
     lanemask above, in;
     region_masks<TK_E>(sk, valid, g, &above, &in);
     if (g.whole || g.single || g.n_eq > (uint32_t)TK_KMAX) {
       lanemask sel = above;
       if (g.whole) sel |= in;
-      else if (g.single) sel |= cut_tie<TK_E>(nid, in, g.r, ids_are_columns, sm);
-      else sel |= select_top<TK_E>(sk, nid, in, g.r, ids_are_columns, sm);  // a huge bin
-      count = compact<TK_E>(sk, nid, sel, sm.buf, 0, sm);
+      else if (g.single) sel |= cut_tie<TK_E>(nid, in, g.r, ids_are_columns, sm, par);
+      else sel |= select_top<TK_E>(sk, nid, in, g.r, ids_are_columns, sm, par);  // a huge bin
+      count = compact<TK_E>(sk, nid, sel, sm.buf, 0, sm, par);
     } else {
       // the keys above the boundary bin go straight to the output buffer, the
       // n_eq <= 2048 keys of the bin to the candidate buffer (both in column
@@ -496,7 +507,7 @@ __device__ uint32_t block_select(const uint32_t (&sk)[TK_E], const uint32_t (&ni
       // the candidates, TK_CE per thread
       uint32_t total;
       const uint32_t x =
-          block_excl_scan(((uint32_t)__popcll(above) << 16) | (uint32_t)__popcll(in), &total, sm);
+          block_excl_scan(((uint32_t)__popcll(above) << 16) | (uint32_t)__popcll(in), &total, sm, par);
       uint32_t pa = x >> 16, pi = x & 0xFFFFu;
 #pragma unroll
       for (int e = 0; e < TK_E; ++e) {
@@ -516,8 +527,8 @@ __device__ uint32_t block_select(const uint32_t (&sk)[TK_E], const uint32_t (&ni
         cnid[e] = (uint32_t)key;
         cact |= (lanemask)(j < g.n_eq) << e;
       }
-      const lanemask csel = select_top<TK_CE>(chi, cnid, cact, g.r, ids_are_columns, sm);
-      (void)compact<TK_CE>(chi, cnid, csel, sm.buf, n_above, sm);
+      const lanemask csel = select_top<TK_CE>(chi, cnid, cact, g.r, ids_are_columns, sm, par);
+      (void)compact<TK_CE>(chi, cnid, csel, sm.buf, n_above, sm, par);
       count = (uint32_t)K;
     }
   }
@@ -535,6 +546,7 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
                                                     float* __restrict__ out_score) {
   __shared__ TkSmem sm;
   const int tid = threadIdx.x;
+  for (int i = tid; i < TK_BINS; i += TK_T) sm.hist[i] = 0;  // radix passes keep it zero
   const int64_t b = blockIdx.x / chunks;
   const int c = (int)(blockIdx.x - b * chunks);
   const int64_t base = (int64_t)c * TK_CHUNK;
