@@ -96,12 +96,14 @@ class Step:
             for r in range(self.R):
                 ws = wl.scaled(seed=wl.seed * 1000 + r)
                 st = {"q": W.attn_query(ws, dev)}
+                # index lists and pools are drawn on the host (no device
+                # random-permutation kernels in the profiled process)
                 if self.mode == "reindex":
-                    st["pool"], st["nb"] = W.pool_blocks(ws, dev)
+                    st["pool"], st["nb"] = (t.to(dev) for t in W.pool_blocks(ws, "cpu"))
                 if self.mode in ("reindex", "prefill_full"):
                     st["qi"] = W.index_query(ws, dev)
                 if self.mode == "reuse":
-                    st["idx"] = W.reuse_index(ws, dev)
+                    st["idx"] = W.reuse_index(ws, "cpu").to(dev)
                 self.sets.append(st)
             if self.mode == "prefill_full":
                 self.chunk = W.prefill_chunk(wl, dev)
