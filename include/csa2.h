@@ -196,7 +196,9 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
  * softmax runs in fp32: the error against an exact evaluation is < 2e-3 of
  * max|out| per (b, h) row for unit-scale inputs.
  * Requires d_c in {128, 512}, d_r in {0, 64}, 1 <= H <= 128, K >= 1, B >= 0,
- * the alignment rules of csa2_quantize_fp4 for the cache, and a workspace of
+ * the alignment rules of csa2_quantize_fp4 for the cache, N_cap * stride <=
+ * 4 GiB for each of codes, scales and rope (one sequence's rows; else
+ * CSA2_ERR_RANGE), and a workspace of
  * csa2_sparse_attn_workspace_bytes(B, H, d_c, K) bytes.
  */
 size_t csa2_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t K);

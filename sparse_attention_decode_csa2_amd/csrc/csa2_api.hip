@@ -145,6 +145,11 @@ int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_
   if (!aligned16(q) || !aligned16(idx) || !aligned16(out) || !opt_aligned16(lse)) return CSA2_ERR_ALIGN;
   const int st = check_cache(d_c, d_r, codes, codes_stride, scales, scales_stride, rope, rope_stride);
   if (st != CSA2_OK) return st;
+  // the kernel addresses a row inside its sequence with 32-bit offsets
+  const int64_t lim = (int64_t)1 << 32;
+  if (N_cap > 0 && (N_cap > lim / codes_stride || N_cap > lim / scales_stride ||
+                    (d_r > 0 && N_cap > lim / rope_stride)))
+    return CSA2_ERR_RANGE;
   const size_t need = csa2::attn_workspace_bytes(B, H, d_c, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;

@@ -118,3 +118,8 @@ def test_attn_validation(lib):
     assert call(ws=N) == WS
     assert call(wsb=need - 4) == WS
     assert lib.csa2_sparse_attn_workspace_bytes(128, 64, 512, 512) == 0
+    # one sequence's rows must span at most 4 GiB per array (32-bit row offsets)
+    RANGE = 4
+    assert call(N=(1 << 32) // 512 + 1) == RANGE
+    assert call(N=(1 << 32) // 1024 + 1, cst=1024) == RANGE
+    assert call(N=(1 << 32) // 512, K=512, B=0) == OK
