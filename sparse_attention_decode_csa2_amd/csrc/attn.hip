@@ -5,22 +5,23 @@
 //
 // One workgroup (4 waves) owns one query, 16 heads and a slice of the index
 // list, walked in tiles of 64 entries:
-//  1. gather: wave w fetches entries [16w, 16w + 16) of the tile.  Each load
-//     instruction covers whole cache lines: for the codes, 16 lanes read the
-//     256 bytes of one entry (four entries per instruction), each lane also
-//     reading the two E4M3 scale bytes of its 32 channels; for the RoPE part,
-//     8 lanes read the 128 bytes of one entry.  The lanes dequantise into an
-//     LDS tile (latent as fp16, RoPE as bf16).  E2M1 x E4M3 products have
-//     <= 6 significant bits and lie in [2^-10, 2688], so the fp16 latent is
-//     exact.  The latent tile is stored with its 16-byte pieces permuted
-//     within each 32-channel chunk, so that the dequant stores, the score
-//     reads and the transposing value reads are all free of bank conflicts.
-//  2. scores: wave w forms S^T for entries [16w, 16w + 16) of the tile with
-//     v_mfma_f32_16x16x32 (A = the entry rows from LDS, B = the 16 query
-//     heads held in registers), fp16 for the latent part, bf16 for RoPE.
+//  1. gather: wave w fetches entries [16w, 16w + 16) of the tile, lane
+//     (n, g) = (l % 16, l / 16) a quarter of entry 16w + n: the 64 code
+//     bytes [64i + 16g, +16) for i < 4 (channels 128i + 32g .. +31, so the
+//     four lanes of an entry read 64 contiguous bytes per load), their two
+//     E4M3 scale bytes, and 16 channels of the RoPE part.
+//  2. the lane dequantises its quarter (exact: E2M1 x E4M3 products have
+//     <= 6 significant bits within [2^-10, 2688]) straight into the MFMA A
+//     operand of the scores: S^T for the wave's 16 entries and the 16 query
+//     heads comes from v_mfma_f32_16x16x32 (fp16 latent, bf16 RoPE) with the
+//     heads as the B operand held in registers, whose k order is permuted to
+//     match (k-step 4i + j, lane group g <-> channels 128i + 32g + 8j .. +7).
 //     The query latent is multiplied by a power of two per head so that it
 //     converts to fp16 without rounding; the factor is undone in the softmax
-//     scale.
+//     scale.  The same fp16 values go to an LDS tile, the value operand of
+//     P . V; its 16-byte pieces are permuted within each 32-channel chunk so
+//     that these stores and the transposing reads below are free of bank
+//     conflicts.
 //  3. online softmax in fp32 (base 2), row max / sum exchanged through LDS.
 //  4. P (fp16) . V with v_mfma_f32_16x16x32_f16, wave w owning a quarter of
 //     the latent channels; V comes from the same LDS tile.
@@ -86,15 +87,12 @@ __device__ __forceinline__ int pv_chunk(int w, int m) {
 
 template <int DC, int DR>
 struct GatherRegs {
-  static constexpr int CPE = DC / 32;               // 32-channel chunks (16 code bytes) per entry
-  static constexpr int EPI = 64 / CPE;              // entries per code load instruction
-  static constexpr int NCI = 16 / EPI;              // code load instructions per wave and tile
-  static constexpr int RPE = DR > 0 ? DR / 8 : 1;   // 8-channel RoPE pieces per entry
-  static constexpr int NRI = DR > 0 ? 16 * RPE / 64 : 0;  // RoPE load instructions per wave and tile
-  u32x4 cw[NCI];
-  uint16_t sb[NCI];  // the two scale bytes of each lane's chunk
-  u32x4 rw[NRI > 0 ? NRI : 1];
-  uint32_t vmask;    // bit k: the entry of code instruction k is selected and in range
+  static constexpr int NCW = DC / 128;               // 16-byte code words per lane (a quarter entry)
+  static constexpr int RW = DR > 0 ? DR / 32 : 1;    // 16-byte RoPE words per lane
+  u32x4 cw[NCW];
+  uint16_t sb[NCW];  // the two scale bytes of each code word
+  u32x4 rw[RW];
+  bool valid;        // the lane's entry is selected and inside the cache
 };
 
 template <int DC, int DR>
@@ -106,18 +104,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   constexpr int KSL = DC / 32;           // latent k-steps
   constexpr int KSR = DR / 32;           // RoPE k-steps
   constexpr int LDK = DC + 16;           // fp16 pitch of the latent tile (8 mod 32 dwords)
-  constexpr int LDR = DR;                // bf16 pitch of the RoPE tile (pieces XOR-permuted by row)
-  constexpr int RPM = DR / 8 - 1;        // piece-index mask of a RoPE row
   constexpr int QCH = DC / 4;            // latent channels per PV wave
   constexpr int NDB = QCH / 16;          // PV d-blocks per wave
   using GR = GatherRegs<DC, DR>;
-  constexpr int CPE = GR::CPE, EPI = GR::EPI, NCI = GR::NCI, RPE = GR::RPE, NRI = GR::NRI;
-  static_assert(64 % CPE == 0 && 16 % EPI == 0 && (DR == 0 || (64 % RPE == 0 && NRI >= 1)), "gather layout");
+  constexpr int NCW = GR::NCW, RW = GR::RW;
+  static_assert(4 * NCW == KSL && (DR == 0 || RW == KSR), "gather layout = MFMA k-steps");
   __shared__ __attribute__((aligned(16))) _Float16 sK[AT_TILE][LDK];
-  __shared__ __attribute__((aligned(16))) __bf16 sR[AT_TILE][DR > 0 ? LDR : 8];
   __shared__ __attribute__((aligned(16))) _Float16 sP[16][AT_TILE + 8];
   __shared__ float sMax[4][16], sSum[4][16], sAlpha[16], sFinM[16], sFinL[16];
-  __shared__ int sValid[AT_TILE];
   __shared__ int32_t sIdx[AT_IDS_PAD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -135,8 +129,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int e_begin = split * per_split;
   const int e_end = min(K, e_begin + per_split);
   const int32_t* idx_row = idx + b * K;
-  const int cl_e = lane / CPE, cl_c = lane % CPE;  // code lanes: entry within the instruction, chunk
-  const int rl_e = lane / RPE, rl_p = lane % RPE;  // RoPE lanes: entry within the instruction, piece
   // an empty slice or cache: no loads at all, the epilogue writes the empty result
   const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
 
@@ -152,8 +144,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int e = e_begin + tid + 256 * k;
     ids[k] = idx_row[min(e, max(e_end - 1, 0))];
   }
-  // ---- query heads h0 + n as MFMA B operands (k-step t, k-group g -> dims
-  // 32t + 8g .. +7)
+  // ---- query heads h0 + n as MFMA B operands: latent k-step t = 4i + j,
+  // k-group g -> dims 128i + 32g + 8j .. +7 (the gather's order); RoPE k-step
+  // t -> dims d_c + 16g + 8t .. +7
   f16x8 Bq[KSL];
   bf16x8 Br[KSR > 0 ? KSR : 1];
   float fscale;  // multiplies the MFMA result into base-2 softmax logits for head h0 + n
@@ -163,7 +156,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const uint16_t* qrow = q + (b * H + (hv ? h0 + n : 0)) * (DC + DR);
 #pragma unroll
     for (int t = 0; t < KSL + KSR; ++t) {
-      const int off = t < KSL ? 32 * t + 8 * g : DC + 32 * (t - KSL) + 8 * g;
+      const int off = t < KSL ? 128 * (t >> 2) + 32 * g + 8 * (t & 3) : DC + 16 * g + 8 * (t - KSL);
       qraw[t] = *reinterpret_cast<const u32x4*>(qrow + off);
     }
   }
@@ -180,32 +173,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // issue back to back.
   // Rows of one sequence span less than 4 GiB in each array (checked by the
   // host), so a row's offset from its sequence base is 32-bit arithmetic.
-  const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride + 16 * cl_c;
-  const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride + 2 * cl_c;
-  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride + 16 * rl_p;
+  const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride + 16 * g;
+  const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride + 2 * g;
+  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride + 32 * g;
   const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
   const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
   auto gather = [&](GR& gr, int tile) {
     // pinned in program order: a load hoisted above the previous tile's work
     // lands in registers that are still in flight and forces a full wait
     __builtin_amdgcn_sched_barrier(0);
-    gr.vmask = 0;
+    const uint32_t id = (uint32_t)sIdx[tile * AT_TILE + 16 * wave + n];
+    gr.valid = id < ncap32;  // also rejects negative ids
+    const uint32_t r = gr.valid ? id : 0u;
 #pragma unroll
-    for (int k = 0; k < NCI; ++k) {
-      const uint32_t id = (uint32_t)sIdx[tile * AT_TILE + 16 * wave + EPI * k + cl_e];
-      const bool ok = id < ncap32;  // also rejects negative ids
-      gr.vmask |= (uint32_t)ok << k;
-      const uint32_t r = ok ? id : 0u;
-      gr.cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seq_codes + r * cs32));
-      gr.sb[k] = *reinterpret_cast<const uint16_t*>(seq_scales + r * ss32);
+    for (int i = 0; i < NCW; ++i) {
+      gr.cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seq_codes + r * cs32 + 64 * i));
+      gr.sb[i] = *reinterpret_cast<const uint16_t*>(seq_scales + r * ss32 + 8 * i);
     }
     if constexpr (DR > 0) {
 #pragma unroll
-      for (int k = 0; k < NRI; ++k) {
-        const uint32_t id = (uint32_t)sIdx[tile * AT_TILE + 16 * wave + (64 / RPE) * k + rl_e];
-        const uint32_t r = id < ncap32 ? id : 0u;
-        gr.rw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seq_rope + r * rs32));
-      }
+      for (int t = 0; t < RW; ++t)
+        gr.rw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seq_rope + r * rs32 + 16 * t));
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -220,63 +208,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     // into the previous tile's work would wait for loads still in flight.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < NCI; ++i) asm volatile("" : "+v"(gr.sb[i]));
-    // ---- 1. dequantise into the LDS tile.  The two E4M3 scales of a lane's
-    // chunk go through the hardware fp8 converter (exact in fp16), the FP4
-    // pairs through the fp4 converter with a unit scale; the block scale is
-    // applied with a packed fp16 multiply, exact as every product has <= 6
-    // significant bits within [2^-10, 2688].
+    for (int i = 0; i < NCW; ++i) asm volatile("" : "+v"(gr.sb[i]));
+    // ---- 1 + 2. dequantise the lane's quarter entry: the two E4M3 scales of
+    // a code word through the hardware fp8 converter (exact in fp16), the FP4
+    // pairs through the fp4 converter with a unit scale, the block scale with
+    // a packed fp16 multiply.  Each 8-channel piece is the A operand of one
+    // score k-step and is also stored to the value tile.
+    const int e = 16 * wave + n;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < NCI; ++k) {
-      const int e = 16 * wave + EPI * k + cl_e;
-      const bool ok = (gr.vmask >> k) & 1u;
-      const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ok ? (uint32_t)gr.sb[k] : 0u, 1.0f, false);
-      const f16x2 s_lo = {sc[0], sc[0]}, s_hi = {sc[1], sc[1]};  // channels 0-15 / 16-31 of the chunk
+    for (int i = 0; i < NCW; ++i) {
+      const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gr.valid ? (uint32_t)gr.sb[i] : 0u, 1.0f, false);
+      const f16x2 s_lo = {sc[0], sc[0]}, s_hi = {sc[1], sc[1]};  // channels 0-15 / 16-31 of the word
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t word = gr.cw[k][p];
-        const f16x2 sv = p < 2 ? s_lo : s_hi;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t word = gr.cw[i][j];
+        const f16x2 sv = j < 2 ? s_lo : s_hi;
         const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sv;
         const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sv;
         const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sv;
         const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sv;
-        *reinterpret_cast<f16x8*>(&sK[e][tile_col(e, cl_c, p)]) =
-            f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        const f16x8 a = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        *reinterpret_cast<f16x8*>(&sK[e][tile_col(e, 4 * i + g, j)]) = a;
+        c = mfma16x16x32_f16(a, Bq[4 * i + j], c);
       }
-      if (cl_c == 0) sValid[e] = ok;
     }
-    if constexpr (DR > 0) {
 #pragma unroll
-      for (int k = 0; k < NRI; ++k)
-      {
-        // piece p of row r lives at piece p ^ (r & RPM): the 8 rows a score
-        // read touches then fall on distinct banks
-        const int r = 16 * wave + (64 / RPE) * k + rl_e;
-        *reinterpret_cast<u32x4*>(&sR[r][8 * (rl_p ^ (r & RPM))]) = gr.rw[k];
-      }
-    }
-    __syncthreads();
-
-    // ---- 2. S^T for entries 16*wave + (0..15): lane (entry n, k-group g)
-    // supplies A from the tile
+    for (int t = 0; t < KSR; ++t) c = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, gr.rw[t]), Br[t], c);
+    // c[i] = S^T[entry 16*wave + 4g + i][head n]; entry validity from lanes 0..15
+    const uint64_t vb = __ballot(g == 0 && gr.valid);
     float s2[4];
-    {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-      const int r = 16 * wave + n;
 #pragma unroll
-      for (int t = 0; t < KSL; ++t) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(&sK[r][tile_col(r, t, g)]);
-        c = mfma16x16x32_f16(a, Bq[t], c);
-      }
-#pragma unroll
-      for (int t = 0; t < KSR; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sR[r][8 * ((4 * t + g) ^ (r & RPM))]);
-        c = mfma16x16x32_bf16(a, Br[t], c);
-      }
-      // c[i] = S^T[entry 16*wave + 4g + i][head n]
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s2[i] = sValid[16 * wave + 4 * g + i] ? c[i] * fscale : -INFINITY;
-    }
+    for (int i = 0; i < 4; ++i) s2[i] = ((vb >> (4 * g + i)) & 1u) ? c[i] * fscale : -INFINITY;
     // ---- 3. online softmax for head n (lanes n, n+16, n+32, n+48 hold its 16 entries)
     float mt = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
     mt = fmaxf(mt, xor16f(mt));
