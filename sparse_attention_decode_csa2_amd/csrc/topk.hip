@@ -43,6 +43,9 @@ static_assert(TK_WAVES <= 16, "block ops combine the wave partials in one 16-lan
 
 struct TkSmem {
   uint32_t hist[TK_BINS + WAVE];  // radix histogram + one dummy bin per lane
+  uint32_t lcnt[TK_BINS + WAVE];  // score-bucket histogram + one dummy bin per lane
+  uint32_t lcur[TK_BINS];         // score-bucket output cursors
+  uint16_t lbk[TK_KMAX];          // bucket of each key in buf
   uint64_t buf[TK_KMAX];          // the selected keys
   uint64_t xbuf[TK_KMAX];         // candidates; second buffer of the sort's LDS exchanges
   uint32_t wtmp[2][3][TK_WAVES];  // wave partials of block ops, two alternating sets
@@ -475,11 +478,133 @@ __device__ __forceinline__ uint32_t compact(const uint32_t (&hi)[E], const uint3
   return total;
 }
 
+// Where a workgroup's selected keys go: the final (idx, score) row, sorted, or
+// a row of chunk-winner keys in any order.
+struct TkDst {
+  int32_t* idx;
+  float* score;
+  uint64_t* keys;
+};
+
+constexpr uint32_t TK_WRITTEN = 0xFFFFFFFFu;  // block_select wrote the output row itself
+constexpr uint32_t TK_SEG_MAX = 32;           // longest score bucket ranked by a plain scan
+constexpr uint32_t TK_WAVE_SORT = WAVE;       // boundary buckets this small are sorted by one wave
+
+__device__ __forceinline__ void put_final(const TkDst& dst, uint32_t j, uint64_t key) {
+  dst.idx[j] = (int32_t)(~(uint32_t)key);
+  if (dst.score) dst.score[j] = key_score((uint32_t)(key >> 32));
+}
+
+// Selection by linear score buckets, for a chunk whose scores are finite and
+// not all equal.  Bucket (s - lo) * 2048 / (hi - lo), clamped, is a monotone
+// function of the score, so the buckets above the one holding the K-th
+// largest key are wholly selected and the rest of the selection happens in
+// that one bucket.  Unlike the radix digits of a float key, the buckets
+// spread scores evenly over their range, so a bucket holds a few keys and:
+//  - the histogram's suffix sums place every key of a selected bucket in
+//    the output order, bucket by bucket; within a bucket one short scan of
+//    its keys ranks it;
+//  - the boundary bucket, when it holds at most 64 keys, is sorted by one
+//    wave and its first r keys complete the output.
+// Returns TK_WRITTEN when the output row is written, else the number of keys
+// left in sm.buf for the caller to sort (final) or write (chunk winners).
+template <bool FINAL>
+__device__ uint32_t bucket_select(const uint32_t (&sk)[TK_E], const uint32_t (&nid)[TK_E], lanemask valid,
+                                  float lo, float span, int K, const TkDst& dst, TkSmem& sm, int& par) {
+  const int tid = threadIdx.x;
+  const float scale = (float)TK_BINS / span;
+  // buckets of elements 2i and 2i + 1 (dummy bins for empty ones) in the
+  // halves of bp[i]
+  uint32_t bp[TK_E / 2];
+#pragma unroll
+  for (int e = 0; e < TK_E; ++e) {
+    const float t = (key_score(sk[e]) - lo) * scale;
+    const uint32_t bk = ((valid >> e) & 1u) ? min((uint32_t)t, (uint32_t)(TK_BINS - 1))
+                                            : (uint32_t)(TK_BINS + lane_id());
+    atomicAdd(&sm.lcnt[bk], 1u);
+    if (e & 1) bp[e >> 1] |= bk << 16;
+    else bp[e >> 1] = bk;
+  }
+  __syncthreads();
+  // thread t owns buckets 2t and 2t + 1; keys in higher buckets come first
+  static_assert(TK_BINS == 2 * TK_T, "two buckets per thread");
+  const uint32_t h0 = sm.lcnt[2 * tid], h1 = sm.lcnt[2 * tid + 1];
+  uint32_t total;
+  const uint32_t excl = block_excl_scan(h0 + h1, &total, sm, par);
+  const uint32_t above1 = total - excl - h0 - h1, above0 = above1 + h1;
+  sm.lcur[2 * tid + 1] = above1;
+  sm.lcur[2 * tid] = above0;
+  if (above1 < (uint32_t)K && above0 >= (uint32_t)K) {
+    sm.info[0] = 2 * tid + 1;
+    sm.info[1] = above1;
+    sm.info[2] = h1;
+  } else if (above0 < (uint32_t)K && above0 + h0 >= (uint32_t)K) {
+    sm.info[0] = 2 * tid;
+    sm.info[1] = above0;
+    sm.info[2] = h0;
+  }
+  __syncthreads();
+  const uint32_t d = sm.info[0], n_above = sm.info[1], n_eq = sm.info[2];
+  const uint32_t r = (uint32_t)K - n_above;  // wanted from bucket d, 1 <= r <= n_eq
+  // a selected bucket too long for the plain in-bucket ranking
+  if ((2 * tid > d && h0 > TK_SEG_MAX) || (2 * tid + 1 > d && h1 > TK_SEG_MAX)) sm.info[3] = 1;
+  // keys of the selected buckets to sm.buf bucket by bucket, keys of bucket
+  // d to sm.xbuf (when they fit)
+  const bool d_fits = n_eq <= (uint32_t)TK_KMAX;
+#pragma unroll
+  for (int e = 0; e < TK_E; ++e) {
+    const uint32_t bk = (bp[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    const uint64_t key = ((uint64_t)sk[e] << 32) | (uint64_t)nid[e];
+    if (bk < (uint32_t)TK_BINS && bk > d) {
+      const uint32_t pos = atomicAdd(&sm.lcur[bk], 1u);
+      sm.buf[pos] = key;
+      sm.lbk[pos] = (uint16_t)bk;
+      if (!FINAL) dst.keys[pos] = key;
+    } else if (bk == d && d_fits) {
+      sm.xbuf[atomicAdd(&sm.lcur[d], 1u) - n_above] = key;
+    }
+  }
+  __syncthreads();
+  const bool long_seg = sm.info[3] != 0;
+  if (n_eq <= TK_WAVE_SORT) {
+    // one wave sorts bucket d and completes the output with its first r keys
+    if (wave_id() == 0) {
+      uint64_t v[1] = {(uint32_t)tid < n_eq ? sm.xbuf[tid] : 0ull};
+      int pb = 0;
+      sort_sizes<2, WAVE>(v, sm, pb);
+      if ((uint32_t)tid < r) {
+        if (!FINAL) dst.keys[n_above + tid] = v[0];
+        else if (long_seg) sm.buf[n_above + tid] = v[0];
+        else put_final(dst, n_above + tid, v[0]);
+      }
+    }
+    if (!FINAL) return TK_WRITTEN;
+    if (long_seg) return (uint32_t)K;  // the caller sorts sm.buf (its barrier orders the writes)
+    // every key of sm.buf: its bucket's place in the output plus its rank
+    // among the keys of the bucket (equal keys by their place in sm.buf)
+    for (uint32_t pos = (uint32_t)tid; pos < n_above; pos += TK_T) {
+      const uint64_t key = sm.buf[pos];
+      const uint32_t bk = sm.lbk[pos];
+      const uint32_t end = sm.lcur[bk], beg = end - sm.lcnt[bk];
+      uint32_t rank = 0;
+      for (uint32_t j = beg; j < end; ++j) {
+        const uint64_t o = sm.buf[j];
+        rank += (o > key || (o == key && j < pos)) ? 1u : 0u;
+      }
+      put_final(dst, beg + rank, key);
+    }
+    return TK_WRITTEN;
+  }
+  return TK_KMAX + 1;  // bucket d is large: the caller selects in it
+}
+
 // Top K of the candidates (sk[e] score keys, 0 = empty; nid[e] = ~id) held by
 // the block, thread t owning positions 16t .. 16t + 15 in column order.
-// Writes the selected keys to sm.buf[0 .. count), count = min(K, #valid).
+// Writes the selected keys to sm.buf[0 .. count), count = min(K, #valid), or
+// the output row itself (returns TK_WRITTEN).
+template <bool FINAL>
 __device__ uint32_t block_select(const uint32_t (&sk)[TK_E], const uint32_t (&nid)[TK_E],
-                                 bool ids_are_columns, int K, TkSmem& sm) {
+                                 bool ids_are_columns, int K, const TkDst& dst, TkSmem& sm) {
   int par = 0;
   lanemask valid = 0;
 #pragma unroll
@@ -487,6 +612,36 @@ __device__ uint32_t block_select(const uint32_t (&sk)[TK_E], const uint32_t (&ni
   uint32_t n_all, smax, smin;
   active_stats<TK_E>(sk, valid, sm, par, &n_all, &smax, &smin);
   uint32_t count;
+  const float hi = key_score(smax), lo = key_score(smin);
+  const float span = hi - lo;  // NaN or infinite for keys outside the finite scores
+  const bool linear = n_all > (uint32_t)K && span >= 1e-30f && span <= 3.4e38f;
+  if (linear) {
+    const uint32_t res = bucket_select<FINAL>(sk, nid, valid, lo, span, K, dst, sm, par);
+    if (res <= (uint32_t)TK_KMAX || res == TK_WRITTEN) return res;
+    // bucket d holds more than 64 keys: select in it below
+    const uint32_t d = sm.info[0], n_above = sm.info[1], n_eq = sm.info[2];
+    const uint32_t r = (uint32_t)K - n_above;
+    if (n_eq <= (uint32_t)TK_KMAX) {
+      // its keys are in sm.xbuf[0 .. n_eq) in no particular order
+      uint32_t chi[TK_CE], cnid[TK_CE];
+      lanemask cact = 0;
+#pragma unroll
+      for (int e = 0; e < TK_CE; ++e) {
+        const uint32_t j = (uint32_t)(TK_CE * threadIdx.x + e);
+        const uint64_t key = j < n_eq ? sm.xbuf[j] : 0ull;
+        chi[e] = (uint32_t)(key >> 32);
+        cnid[e] = (uint32_t)key;
+        cact |= (lanemask)(j < n_eq) << e;
+      }
+      const lanemask csel = select_top<TK_CE>(chi, cnid, cact, r, false, sm, par);
+      (void)compact<TK_CE>(chi, cnid, csel, sm.buf, n_above, sm, par);
+      __syncthreads();
+      return (uint32_t)K;
+    }
+    // more than 2048 keys in one bucket: the radix path below, from the start
+    (void)d;
+    __syncthreads();
+  }
   if (n_all <= (uint32_t)K) {
     count = compact<TK_E>(sk, nid, valid, sm.buf, 0, sm, par);
   } else {
@@ -546,7 +701,11 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
                                                     float* __restrict__ out_score) {
   __shared__ TkSmem sm;
   const int tid = threadIdx.x;
-  for (int i = tid; i < TK_BINS; i += TK_T) sm.hist[i] = 0;  // radix passes keep it zero
+  for (int i = tid; i < TK_BINS; i += TK_T) {
+    sm.hist[i] = 0;  // radix passes keep it zero
+    sm.lcnt[i] = 0;
+  }
+  if (tid == 0) sm.info[3] = 0;
   const int64_t b = blockIdx.x / chunks;
   const int c = (int)(blockIdx.x - b * chunks);
   const int64_t base = (int64_t)c * TK_CHUNK;
@@ -598,7 +757,12 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
       nid[e] = (uint32_t)k;
     }
   }
-  const uint32_t count = block_select(sk, nid, ids_are_columns, K, sm);
+  TkDst dst;
+  dst.idx = FINAL ? out_idx + b * K : nullptr;
+  dst.score = FINAL && out_score ? out_score + b * K : nullptr;
+  dst.keys = FINAL ? nullptr : keys_out + (b * chunks + c) * (int64_t)K;
+  const uint32_t count = block_select<FINAL>(sk, nid, ids_are_columns, K, dst, sm);
+  if (count == TK_WRITTEN) return;
   if (FINAL) {
     // sort the selected keys descending: (score desc, id asc)
     if (count > 1) {

@@ -18,6 +18,18 @@ def _scores(rng, B, M, kind):
         s = np.maximum(rng.normal(900, 500, size=(B, M)), 0).round().astype(np.float32)
     elif kind == "continuous":
         s = rng.standard_normal((B, M)).astype(np.float32)
+    elif kind == "cluster":          # runs of equal scores above and at the K-th largest
+        s = np.maximum(rng.normal(900, 500, size=(B, M)), 0).round().astype(np.float32)
+        r = rng.random((B, M))
+        s[r < 0.01] = 5000.0
+        s[(r >= 0.01) & (r < 0.015)] = 2500.0
+    elif kind == "outlier":          # one far-off score squeezes the rest into a bucket or two
+        s = np.maximum(rng.normal(900, 500, size=(B, M)), 0).round().astype(np.float32)
+        s[:, rng.integers(0, M, size=B)] = -1e30
+    elif kind == "narrow":           # a tiny spread, then subnormals
+        s = (1.0 + rng.random((B, M)) * 1e-6).astype(np.float32)
+        if M > 1:
+            s[:, ::2] = (rng.random((B, (M + 1) // 2)) * 1e-39).astype(np.float32)
     else:                            # specials sprinkled over tied integers
         s = rng.integers(-3, 4, size=(B, M)).astype(np.float32)
         r = rng.random((B, M))
@@ -47,7 +59,8 @@ CASES = [(1, 1, 1), (2, 7, 4), (3, 1000, 64), (1, 16384, 512), (2, 16385, 512), 
 
 
 @pytest.mark.parametrize("B,M,K", CASES)
-@pytest.mark.parametrize("kind", ["ties", "int_scores", "continuous", "specials"])
+@pytest.mark.parametrize("kind", ["ties", "int_scores", "continuous", "specials", "cluster", "outlier",
+                                  "narrow"])
 def test_topk_column_ids(B, M, K, kind):
     note(f"topk: B={B} M={M} K={K} {kind}")
     rng = np.random.default_rng(B * 7 + M + K)
