@@ -126,6 +126,18 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t v, uint32_t ident, Op o
 struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
 struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
 struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+// fp32 max / min on the bit patterns; a NaN operand is ignored, so NaN is the identity
+struct OpFMax {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }
+};
+struct OpFMin {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  }
+};
+constexpr uint32_t F_NAN = 0x7FC00000u;
 
 // ---------------------------------------------------------------- block ops
 //
@@ -135,13 +147,15 @@ struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { re
 // thread), so each needs a single barrier: a set is rewritten two ops later,
 // after a barrier every thread has passed only once done reading it.
 
-// Block-wide (sum of a, max of b, min of c); every thread gets the results.
-__device__ __forceinline__ void block_sum_max_min(uint32_t& a, uint32_t& b, uint32_t& c, TkSmem& sm,
-                                                  int& par) {
+// Block-wide reductions of a, b and c under the operations OA, OB, OC (with
+// identities ia, ib, ic); every thread gets the results.
+template <typename OA, typename OB, typename OC>
+__device__ __forceinline__ void block_reduce3(uint32_t& a, uint32_t& b, uint32_t& c, uint32_t ia, uint32_t ib,
+                                              uint32_t ic, TkSmem& sm, int& par) {
   const int wave = wave_id();
-  a = wave_reduce(a, 0u, OpAdd());
-  b = wave_reduce(b, 0u, OpMax());
-  c = wave_reduce(c, 0xFFFFFFFFu, OpMin());
+  a = wave_reduce(a, ia, OA());
+  b = wave_reduce(b, ib, OB());
+  c = wave_reduce(c, ic, OC());
   uint32_t(&w)[3][TK_WAVES] = sm.wtmp[par];
   if (lane_id() == 0) {
     w[0][wave] = a;
@@ -151,13 +165,19 @@ __device__ __forceinline__ void block_sum_max_min(uint32_t& a, uint32_t& b, uint
   __syncthreads();
   const int l = lane_id() & 15;
   const bool in = l < TK_WAVES;
-  a = row_incl(in ? w[0][in ? l : 0] : 0u, 0u, OpAdd());
-  b = row_incl(in ? w[1][in ? l : 0] : 0u, 0u, OpMax());
-  c = row_incl(in ? w[2][in ? l : 0] : 0xFFFFFFFFu, 0xFFFFFFFFu, OpMin());
+  a = row_incl(in ? w[0][in ? l : 0] : ia, ia, OA());
+  b = row_incl(in ? w[1][in ? l : 0] : ib, ib, OB());
+  c = row_incl(in ? w[2][in ? l : 0] : ic, ic, OC());
   a = (uint32_t)__builtin_amdgcn_readlane((int)a, TK_WAVES - 1);
   b = (uint32_t)__builtin_amdgcn_readlane((int)b, TK_WAVES - 1);
   c = (uint32_t)__builtin_amdgcn_readlane((int)c, TK_WAVES - 1);
   par ^= 1;
+}
+
+// Block-wide (sum of a, max of b, min of c).
+__device__ __forceinline__ void block_sum_max_min(uint32_t& a, uint32_t& b, uint32_t& c, TkSmem& sm,
+                                                  int& par) {
+  block_reduce3<OpAdd, OpMax, OpMin>(a, b, c, 0u, 0u, 0xFFFFFFFFu, sm, par);
 }
 
 // Exclusive prefix sum over the block in thread order; *total gets the sum.
@@ -488,28 +508,31 @@ struct TkDst {
 
 constexpr uint32_t TK_WRITTEN = 0xFFFFFFFFu;  // block_select wrote the output row itself
 constexpr uint32_t TK_SEG_MAX = 32;           // longest score bucket ranked by a plain scan
-constexpr uint32_t TK_WAVE_SORT = WAVE;       // boundary buckets this small are sorted by one wave
+constexpr uint32_t TK_WAVE_SORT = WAVE;       // boundary buckets this small are ordered by one wave,
+constexpr uint32_t TK_RANK_SORT = 24;         // by counting ranks up to this size, else a sort
 
 __device__ __forceinline__ void put_final(const TkDst& dst, uint32_t j, uint64_t key) {
   dst.idx[j] = (int32_t)(~(uint32_t)key);
   if (dst.score) dst.score[j] = key_score((uint32_t)(key >> 32));
 }
 
-// Selection by linear score buckets, for a chunk whose scores are finite and
-// not all equal.  Bucket (s - lo) * 2048 / (hi - lo), clamped, is a monotone
-// function of the score, so the buckets above the one holding the K-th
-// largest key are wholly selected and the rest of the selection happens in
-// that one bucket.  Unlike the radix digits of a float key, the buckets
-// spread scores evenly over their range, so a bucket holds a few keys and:
+// Selection by linear score buckets, for a chunk whose scores (of the valid
+// elements: v[e] for valid bit e, NaN elsewhere) have a finite, nonzero range
+// [lo, lo + span].  Bucket max((s - lo) * 2048 / span, 0), clamped, is a
+// monotone function of the score (a NaN score, ranked lowest, lands in bucket
+// 0), so the buckets above the one holding the K-th largest key are wholly
+// selected and the rest of the selection happens in that one bucket.  Unlike
+// the radix digits of a float key, the buckets spread scores evenly over
+// their range, so a bucket holds a few keys and:
 //  - the histogram's suffix sums place every key of a selected bucket in
 //    the output order, bucket by bucket; within a bucket one short scan of
 //    its keys ranks it;
-//  - the boundary bucket, when it holds at most 64 keys, is sorted by one
+//  - the boundary bucket, when it holds at most 64 keys, is ordered by one
 //    wave and its first r keys complete the output.
 // Returns TK_WRITTEN when the output row is written, else the number of keys
 // left in sm.buf for the caller to sort (final) or write (chunk winners).
 template <bool FINAL>
-__device__ uint32_t bucket_select(const uint32_t (&sk)[TK_E], const uint32_t (&nid)[TK_E], lanemask valid,
+__device__ uint32_t bucket_select(const float (&v)[TK_E], const uint32_t (&idv)[TK_E], lanemask valid,
                                   float lo, float span, int K, const TkDst& dst, TkSmem& sm, int& par) {
   const int tid = threadIdx.x;
   const float scale = (float)TK_BINS / span;
@@ -518,7 +541,7 @@ __device__ uint32_t bucket_select(const uint32_t (&sk)[TK_E], const uint32_t (&n
   uint32_t bp[TK_E / 2];
 #pragma unroll
   for (int e = 0; e < TK_E; ++e) {
-    const float t = (key_score(sk[e]) - lo) * scale;
+    const float t = fmaxf((v[e] - lo) * scale, 0.f);  // NaN -> 0
     const uint32_t bk = ((valid >> e) & 1u) ? min((uint32_t)t, (uint32_t)(TK_BINS - 1))
                                             : (uint32_t)(TK_BINS + lane_id());
     atomicAdd(&sm.lcnt[bk], 1u);
@@ -549,47 +572,66 @@ __device__ uint32_t bucket_select(const uint32_t (&sk)[TK_E], const uint32_t (&n
   // a selected bucket too long for the plain in-bucket ranking
   if ((2 * tid > d && h0 > TK_SEG_MAX) || (2 * tid + 1 > d && h1 > TK_SEG_MAX)) sm.info[3] = 1;
   // keys of the selected buckets to sm.buf bucket by bucket, keys of bucket
-  // d to sm.xbuf (when they fit)
-  const bool d_fits = n_eq <= (uint32_t)TK_KMAX;
+  // d to sm.xbuf (when they fit): all cursor updates first, then the stores
+  const uint32_t dd = n_eq <= (uint32_t)TK_KMAX ? d : 0xFFFFu;  // no bucket matches 0xFFFF
+  uint32_t pos[TK_E];
 #pragma unroll
   for (int e = 0; e < TK_E; ++e) {
     const uint32_t bk = (bp[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-    const uint64_t key = ((uint64_t)sk[e] << 32) | (uint64_t)nid[e];
-    if (bk < (uint32_t)TK_BINS && bk > d) {
-      const uint32_t pos = atomicAdd(&sm.lcur[bk], 1u);
-      sm.buf[pos] = key;
-      sm.lbk[pos] = (uint16_t)bk;
-      if (!FINAL) dst.keys[pos] = key;
-    } else if (bk == d && d_fits) {
-      sm.xbuf[atomicAdd(&sm.lcur[d], 1u) - n_above] = key;
+    pos[e] = (bk < (uint32_t)TK_BINS && bk > d) || bk == dd ? atomicAdd(&sm.lcur[bk], 1u) : 0xFFFFFFFFu;
+  }
+#pragma unroll
+  for (int e = 0; e < TK_E; ++e) {
+    if (pos[e] != 0xFFFFFFFFu) {
+      const uint32_t bk = (bp[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint64_t key = ((uint64_t)score_key(v[e]) << 32) | (uint64_t)(~idv[e]);
+      if (bk != d) {
+        sm.buf[pos[e]] = key;
+        sm.lbk[pos[e]] = (uint16_t)bk;
+        if (!FINAL) dst.keys[pos[e]] = key;
+      } else {
+        sm.xbuf[pos[e] - n_above] = key;
+      }
     }
   }
   __syncthreads();
   const bool long_seg = sm.info[3] != 0;
   if (n_eq <= TK_WAVE_SORT) {
-    // one wave sorts bucket d and completes the output with its first r keys
+    // one wave orders bucket d and completes the output with its first r keys
     if (wave_id() == 0) {
-      uint64_t v[1] = {(uint32_t)tid < n_eq ? sm.xbuf[tid] : 0ull};
-      int pb = 0;
-      sort_sizes<2, WAVE>(v, sm, pb);
-      if ((uint32_t)tid < r) {
-        if (!FINAL) dst.keys[n_above + tid] = v[0];
-        else if (long_seg) sm.buf[n_above + tid] = v[0];
-        else put_final(dst, n_above + tid, v[0]);
+      uint64_t kv[1] = {(uint32_t)tid < n_eq ? sm.xbuf[tid] : 0ull};
+      uint32_t slot = (uint32_t)tid;
+      if (n_eq <= TK_RANK_SORT) {
+        // rank among the n_eq keys, equal keys by lane
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < n_eq; ++j) {
+          const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kv[0] >> 32), (int)j) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kv[0], (int)j);
+          rank += (o > kv[0] || (o == kv[0] && j < (uint32_t)tid)) ? 1u : 0u;
+        }
+        slot = (uint32_t)tid < n_eq ? rank : 0xFFFFFFFFu;
+      } else {
+        int pb = 0;
+        sort_sizes<2, WAVE>(kv, sm, pb);
+      }
+      if (slot < r) {
+        if (!FINAL) dst.keys[n_above + slot] = kv[0];
+        else if (long_seg) sm.buf[n_above + slot] = kv[0];
+        else put_final(dst, n_above + slot, kv[0]);
       }
     }
     if (!FINAL) return TK_WRITTEN;
     if (long_seg) return (uint32_t)K;  // the caller sorts sm.buf (its barrier orders the writes)
     // every key of sm.buf: its bucket's place in the output plus its rank
     // among the keys of the bucket (equal keys by their place in sm.buf)
-    for (uint32_t pos = (uint32_t)tid; pos < n_above; pos += TK_T) {
-      const uint64_t key = sm.buf[pos];
-      const uint32_t bk = sm.lbk[pos];
+    for (uint32_t p = (uint32_t)tid; p < n_above; p += TK_T) {
+      const uint64_t key = sm.buf[p];
+      const uint32_t bk = sm.lbk[p];
       const uint32_t end = sm.lcur[bk], beg = end - sm.lcnt[bk];
       uint32_t rank = 0;
       for (uint32_t j = beg; j < end; ++j) {
         const uint64_t o = sm.buf[j];
-        rank += (o > key || (o == key && j < pos)) ? 1u : 0u;
+        rank += (o > key || (o == key && j < p)) ? 1u : 0u;
       }
       put_final(dst, beg + rank, key);
     }
@@ -598,25 +640,34 @@ __device__ uint32_t bucket_select(const uint32_t (&sk)[TK_E], const uint32_t (&n
   return TK_KMAX + 1;  // bucket d is large: the caller selects in it
 }
 
-// Top K of the candidates (sk[e] score keys, 0 = empty; nid[e] = ~id) held by
-// the block, thread t owning positions 16t .. 16t + 15 in column order.
-// Writes the selected keys to sm.buf[0 .. count), count = min(K, #valid), or
-// the output row itself (returns TK_WRITTEN).
+// Top K of the candidates held by the block, thread t owning positions
+// 16t .. 16t + 15 in column order: element e has score v[e] and id idv[e]
+// when valid bit e is set (v[e] is NaN otherwise).  Writes the selected keys
+// to sm.buf[0 .. count), count = min(K, #valid), or the output row itself
+// (returns TK_WRITTEN).
 template <bool FINAL>
-__device__ uint32_t block_select(const uint32_t (&sk)[TK_E], const uint32_t (&nid)[TK_E],
+__device__ uint32_t block_select(const float (&v)[TK_E], const uint32_t (&idv)[TK_E], lanemask valid,
                                  bool ids_are_columns, int K, const TkDst& dst, TkSmem& sm) {
   int par = 0;
-  lanemask valid = 0;
+  // count, highest and lowest score of the valid elements (NaN scores and
+  // the NaN placeholders of empty elements are skipped by max / min)
+  uint32_t n_all = (uint32_t)__popcll(valid), fhi = F_NAN, flo = F_NAN;
+  {
+    float h = __uint_as_float(F_NAN), l = __uint_as_float(F_NAN);
 #pragma unroll
-  for (int e = 0; e < TK_E; ++e) valid |= (lanemask)(sk[e] != 0) << e;
-  uint32_t n_all, smax, smin;
-  active_stats<TK_E>(sk, valid, sm, par, &n_all, &smax, &smin);
-  uint32_t count;
-  const float hi = key_score(smax), lo = key_score(smin);
-  const float span = hi - lo;  // NaN or infinite for keys outside the finite scores
+    for (int e = 0; e < TK_E; ++e) {
+      h = fmaxf(h, v[e]);
+      l = fminf(l, v[e]);
+    }
+    fhi = __float_as_uint(h);
+    flo = __float_as_uint(l);
+  }
+  block_reduce3<OpAdd, OpFMax, OpFMin>(n_all, fhi, flo, 0u, F_NAN, F_NAN, sm, par);
+  const float hi = __uint_as_float(fhi), lo = __uint_as_float(flo);
+  const float span = hi - lo;  // NaN or infinite unless both ends are finite
   const bool linear = n_all > (uint32_t)K && span >= 1e-30f && span <= 3.4e38f;
   if (linear) {
-    const uint32_t res = bucket_select<FINAL>(sk, nid, valid, lo, span, K, dst, sm, par);
+    const uint32_t res = bucket_select<FINAL>(v, idv, valid, lo, span, K, dst, sm, par);
     if (res <= (uint32_t)TK_KMAX || res == TK_WRITTEN) return res;
     // bucket d holds more than 64 keys: select in it below
     const uint32_t d = sm.info[0], n_above = sm.info[1], n_eq = sm.info[2];
@@ -642,10 +693,20 @@ __device__ uint32_t block_select(const uint32_t (&sk)[TK_E], const uint32_t (&ni
     (void)d;
     __syncthreads();
   }
+  // ---- radix selection on the 32-bit score keys (0 = empty)
+  uint32_t sk[TK_E], nid[TK_E];
+#pragma unroll
+  for (int e = 0; e < TK_E; ++e) {
+    sk[e] = ((valid >> e) & 1u) ? score_key(v[e]) : 0u;
+    nid[e] = ~idv[e];
+  }
+  uint32_t count;
   if (n_all <= (uint32_t)K) {
     count = compact<TK_E>(sk, nid, valid, sm.buf, 0, sm, par);
   } else {
     // one radix pass over the whole chunk
+    uint32_t n_chk, smax, smin;
+    active_stats<TK_E>(sk, valid, sm, par, &n_chk, &smax, &smin);
     const TkRegion g = radix_select<TK_E>(sk, valid, (uint32_t)K, smax, smin, n_all, 1, sm, par);
     lanemask above, in;
     region_masks<TK_E>(sk, valid, g, &above, &in);
@@ -711,7 +772,11 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   const int64_t base = (int64_t)c * TK_CHUNK;
   int64_t limit = min<int64_t>(M, base + TK_CHUNK);
   const int64_t col0 = base + (int64_t)TK_E * tid;  // this thread's first column
-  uint32_t sk[TK_E], nid[TK_E];
+  // element e: score v[e] (NaN when empty), id idv[e], valid bit e
+  float v[TK_E];
+  uint32_t idv[TK_E];
+  lanemask valid = 0;
+  const float qnan = __uint_as_float(F_NAN);
   bool ids_are_columns;
   if (FROM_SCORES) {
     if (n_valid) limit = min<int64_t>(limit, max<int64_t>(n_valid[b], 0));
@@ -728,22 +793,32 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * q4 + j;
-          const uint32_t i = irow ? i4[j] : (uint32_t)(col0 + e);
-          nid[e] = ~i;
-          sk[e] = i != 0xFFFFFFFFu ? score_key(v4[j]) : 0u;
+          if (irow) {
+            const bool ok = i4[j] != 0xFFFFFFFFu;
+            idv[e] = i4[j];
+            v[e] = ok ? v4[j] : qnan;
+            valid |= (lanemask)ok << e;
+          } else {
+            idv[e] = (uint32_t)(col0 + e);
+            v[e] = v4[j];
+          }
         }
       }
+      if (!irow) valid = (lanemask(1) << TK_E) - 1u;
     } else {
 #pragma unroll
       for (int e = 0; e < TK_E; ++e) {
         const int64_t col = col0 + e;
-        uint32_t k = 0, i = 0;
+        uint32_t i = 0xFFFFFFFFu;
+        float x = qnan;
         if (col < limit) {
           i = irow ? (uint32_t)irow[col] : (uint32_t)col;
-          if (i != 0xFFFFFFFFu) k = score_key(srow[col]);
+          if (i != 0xFFFFFFFFu) x = srow[col];
         }
-        sk[e] = k;
-        nid[e] = ~i;
+        const bool ok = i != 0xFFFFFFFFu;
+        idv[e] = i;
+        v[e] = ok ? x : qnan;
+        valid |= (lanemask)ok << e;
       }
     }
   } else {
@@ -753,15 +828,17 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
     for (int e = 0; e < TK_E; ++e) {
       const int64_t col = col0 + e;
       const uint64_t k = col < limit ? krow[col] : 0ull;
-      sk[e] = (uint32_t)(k >> 32);
-      nid[e] = (uint32_t)k;
+      const uint32_t hk = (uint32_t)(k >> 32);
+      idv[e] = ~(uint32_t)k;
+      v[e] = hk != 0 ? key_score(hk) : qnan;
+      valid |= (lanemask)(hk != 0) << e;
     }
   }
   TkDst dst;
   dst.idx = FINAL ? out_idx + b * K : nullptr;
   dst.score = FINAL && out_score ? out_score + b * K : nullptr;
   dst.keys = FINAL ? nullptr : keys_out + (b * chunks + c) * (int64_t)K;
-  const uint32_t count = block_select<FINAL>(sk, nid, ids_are_columns, K, dst, sm);
+  const uint32_t count = block_select<FINAL>(v, idv, valid, ids_are_columns, K, dst, sm);
   if (count == TK_WRITTEN) return;
   if (FINAL) {
     // sort the selected keys descending: (score desc, id asc)
