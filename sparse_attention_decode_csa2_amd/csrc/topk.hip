@@ -46,10 +46,11 @@ struct TkSmem {
   uint32_t lcnt[TK_BINS + WAVE];  // score-bucket histogram + one dummy bin per lane
   uint32_t lcur[TK_BINS];         // score-bucket output cursors
   uint16_t lbk[TK_KMAX];          // bucket of each key in buf
+  uint64_t stage[2 * TK_KMAX];    // (score bits, id) of the entries placed by score buckets
   uint64_t buf[TK_KMAX];          // the selected keys
   uint64_t xbuf[TK_KMAX];         // candidates; second buffer of the sort's LDS exchanges
   uint32_t wtmp[2][3][TK_WAVES];  // wave partials of block ops, two alternating sets
-  uint32_t info[4];
+  uint32_t info[5];
 };
 
 typedef uint64_t lanemask;  // one bit per element a thread holds
@@ -531,22 +532,31 @@ __device__ __forceinline__ void put_final(const TkDst& dst, uint32_t j, uint64_t
 //    wave and its first r keys complete the output.
 // Returns TK_WRITTEN when the output row is written, else the number of keys
 // left in sm.buf for the caller to sort (final) or write (chunk winners).
+// Score bucket: monotone in s, NaN -> 0.  The one definition used for every
+// evaluation, so that an entry always lands in the same bucket.
+__device__ __forceinline__ uint32_t score_bucket(float s, float lo, float scale) {
+  const float t = fmaxf((s - lo) * scale, 0.f);
+  return min((uint32_t)t, (uint32_t)(TK_BINS - 1));
+}
+
 template <bool FINAL>
 __device__ uint32_t bucket_select(const float (&v)[TK_E], const uint32_t (&idv)[TK_E], lanemask valid,
                                   float lo, float span, int K, const TkDst& dst, TkSmem& sm, int& par) {
   const int tid = threadIdx.x;
   const float scale = (float)TK_BINS / span;
-  // buckets of elements 2i and 2i + 1 (dummy bins for empty ones) in the
-  // halves of bp[i]
-  uint32_t bp[TK_E / 2];
+  // empty elements count into the lane's own dummy bin (no collisions);
+  // threads with none skip the test, threads with no valid element skip all
+  uint32_t bk[TK_E];
 #pragma unroll
-  for (int e = 0; e < TK_E; ++e) {
-    const float t = fmaxf((v[e] - lo) * scale, 0.f);  // NaN -> 0
-    const uint32_t bk = ((valid >> e) & 1u) ? min((uint32_t)t, (uint32_t)(TK_BINS - 1))
-                                            : (uint32_t)(TK_BINS + lane_id());
-    atomicAdd(&sm.lcnt[bk], 1u);
-    if (e & 1) bp[e >> 1] |= bk << 16;
-    else bp[e >> 1] = bk;
+  for (int e = 0; e < TK_E; ++e) bk[e] = score_bucket(v[e], lo, scale);
+  constexpr lanemask all = (lanemask(1) << TK_E) - 1u;
+  if (valid == all) {
+#pragma unroll
+    for (int e = 0; e < TK_E; ++e) atomicAdd(&sm.lcnt[bk[e]], 1u);
+  } else if (valid) {
+#pragma unroll
+    for (int e = 0; e < TK_E; ++e)
+      atomicAdd(&sm.lcnt[((valid >> e) & 1u) ? bk[e] : (uint32_t)(TK_BINS + lane_id())], 1u);
   }
   __syncthreads();
   // thread t owns buckets 2t and 2t + 1; keys in higher buckets come first
@@ -571,27 +581,51 @@ __device__ uint32_t bucket_select(const float (&v)[TK_E], const uint32_t (&idv)[
   const uint32_t r = (uint32_t)K - n_above;  // wanted from bucket d, 1 <= r <= n_eq
   // a selected bucket too long for the plain in-bucket ranking
   if ((2 * tid > d && h0 > TK_SEG_MAX) || (2 * tid + 1 > d && h1 > TK_SEG_MAX)) sm.info[3] = 1;
-  // keys of the selected buckets to sm.buf bucket by bucket, keys of bucket
-  // d to sm.xbuf (when they fit): all cursor updates first, then the stores
-  const uint32_t dd = n_eq <= (uint32_t)TK_KMAX ? d : 0xFFFFu;  // no bucket matches 0xFFFF
-  uint32_t pos[TK_E];
+  // ---- the entries of buckets above d, and of bucket d when it fits, are
+  // compacted wave by wave into sm.stage as (score bits, id)
+  const bool d_fits = n_eq <= (uint32_t)TK_KMAX;
+  const uint32_t dd = d_fits ? d : 0xFFFFu;  // no bucket matches 0xFFFF
+  auto stage = [&](auto check_valid) {
+    // in bucket 0 (d == 0) only the valid elements count
+    auto st = [&](int e) {
+      if constexpr (decltype(check_valid)::value) return bk[e] > 0u || (d_fits && ((valid >> e) & 1u));
+      else return bk[e] > d || bk[e] == dd;
+    };
+    uint32_t wn = 0;
 #pragma unroll
-  for (int e = 0; e < TK_E; ++e) {
-    const uint32_t bk = (bp[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-    pos[e] = (bk < (uint32_t)TK_BINS && bk > d) || bk == dd ? atomicAdd(&sm.lcur[bk], 1u) : 0xFFFFFFFFu;
-  }
+    for (int e = 0; e < TK_E; ++e) wn += (uint32_t)__popcll(__ballot(st(e)));
+    uint32_t wbase = 0;
+    if (lane_id() == 0 && wn) wbase = atomicAdd(&sm.info[4], wn);
+    wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
 #pragma unroll
-  for (int e = 0; e < TK_E; ++e) {
-    if (pos[e] != 0xFFFFFFFFu) {
-      const uint32_t bk = (bp[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const uint64_t key = ((uint64_t)score_key(v[e]) << 32) | (uint64_t)(~idv[e]);
-      if (bk != d) {
-        sm.buf[pos[e]] = key;
-        sm.lbk[pos[e]] = (uint16_t)bk;
-        if (!FINAL) dst.keys[pos[e]] = key;
-      } else {
-        sm.xbuf[pos[e] - n_above] = key;
+    for (int e = 0; e < TK_E; ++e) {
+      const uint64_t m = __ballot(st(e));
+      if (m) {
+        const uint32_t below =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (st(e)) sm.stage[wbase + below] = ((uint64_t)__float_as_uint(v[e]) << 32) | (uint64_t)idv[e];
+        wbase += (uint32_t)__popcll(m);
       }
+    }
+  };
+  if (d != 0) stage(std::false_type());
+  else stage(std::true_type());
+  __syncthreads();
+  // ---- staged entries to sm.buf bucket by bucket (buckets above d) or to
+  // sm.xbuf (bucket d), as 64-bit keys
+  const uint32_t n_stage = n_above + (d_fits ? n_eq : 0u);
+  for (uint32_t i = (uint32_t)tid; i < n_stage; i += TK_T) {
+    const uint64_t sv = sm.stage[i];
+    const float s = __uint_as_float((uint32_t)(sv >> 32));
+    const uint32_t bk = score_bucket(s, lo, scale);
+    const uint64_t key = ((uint64_t)score_key(s) << 32) | (uint64_t)(~(uint32_t)sv);
+    const uint32_t p = atomicAdd(&sm.lcur[bk], 1u);
+    if (bk != d) {
+      sm.buf[p] = key;
+      sm.lbk[p] = (uint16_t)bk;
+      if (!FINAL) dst.keys[p] = key;
+    } else {
+      sm.xbuf[p - n_above] = key;
     }
   }
   __syncthreads();
@@ -766,7 +800,10 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
     sm.hist[i] = 0;  // radix passes keep it zero
     sm.lcnt[i] = 0;
   }
-  if (tid == 0) sm.info[3] = 0;
+  if (tid == 0) {
+    sm.info[3] = 0;
+    sm.info[4] = 0;
+  }
   const int64_t b = blockIdx.x / chunks;
   const int c = (int)(blockIdx.x - b * chunks);
   const int64_t base = (int64_t)c * TK_CHUNK;
@@ -824,12 +861,23 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   } else {
     ids_are_columns = false;
     const uint64_t* krow = keys_in + b * M;
+    uint64_t k[TK_E];
+    if (col0 + TK_E <= limit && (M & 1) == 0) {
+      // a whole run: 16-byte loads (rows stay 16-byte aligned)
+#pragma unroll
+      for (int q = 0; q < TK_E / 2; ++q) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(krow + col0 + 2 * q);
+        k[2 * q] = ((uint64_t)w[1] << 32) | w[0];
+        k[2 * q + 1] = ((uint64_t)w[3] << 32) | w[2];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < TK_E; ++e) k[e] = col0 + e < limit ? krow[col0 + e] : 0ull;
+    }
 #pragma unroll
     for (int e = 0; e < TK_E; ++e) {
-      const int64_t col = col0 + e;
-      const uint64_t k = col < limit ? krow[col] : 0ull;
-      const uint32_t hk = (uint32_t)(k >> 32);
-      idv[e] = ~(uint32_t)k;
+      const uint32_t hk = (uint32_t)(k[e] >> 32);
+      idv[e] = ~(uint32_t)k[e];
       v[e] = hk != 0 ? key_score(hk) : qnan;
       valid |= (lanemask)(hk != 0) << e;
     }
