@@ -9,7 +9,10 @@ profiles/.
         --fetch DIR1 --write DIR2 --kernel REGEX --calib REGEX --calib-bytes N \
         --workload NAME --source attn.hip --command "..."
         HBM bytes per launch of the kernels matching REGEX, from two `--pmc`
-        runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is
+        runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  With --kernel
+        given more than once, the figure is the sum over the kernels of their
+        averages per dispatch: the bytes of one call that launches each of
+        them once (the attention kernel and its split combine).  Each counter is
         scaled by the factor that makes it read N bytes for a calibration
         kernel of known size (a plain device copy: N bytes read, N written).
         The output is what bench.py reads as roofline.traffic, tagged with a
@@ -102,8 +105,16 @@ def traffic(args):
     cw, _, _ = _pick(w_per, args.calib, "calibration")
     f_scale = args.calib_bytes / (cf * 1024.0)
     w_scale = args.calib_bytes / (cw * 1024.0)
-    kf, nf, knames = _pick(f_per, args.kernel, "measured")
-    kw, nw, _ = _pick(w_per, args.kernel, "measured")
+    kf = kw = 0.0
+    nf, nw, knames = [], [], []
+    for rx in args.kernel:
+        f, n1, names = _pick(f_per, rx, "measured")
+        w, n2, _ = _pick(w_per, rx, "measured")
+        kf += f
+        kw += w
+        nf.append(str(n1))
+        nw.append(str(n2))
+        knames += names
     fetch = kf * 1024.0 * f_scale
     write = kw * 1024.0 * w_scale
     print("\n".join([
@@ -115,7 +126,7 @@ def traffic(args):
         f"calibration_kernel: {' | '.join(_short(k, 200) for k in cnames)}",
         f"source_file: {args.source}",
         f"source_hash: {kernel_source_hash(args.source)}",
-        f"dispatches: {nf} fetch, {nw} write",
+        f"dispatches: {'+'.join(nf)} fetch, {'+'.join(nw)} write",
         f"fetch_kib_raw: {kf:.1f}",
         f"write_kib_raw: {kw:.1f}",
         f"fetch_scale: {f_scale:.4f}",
@@ -147,7 +158,7 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, action="append")
     t.add_argument("--calib", required=True)
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--workload", required=True)
