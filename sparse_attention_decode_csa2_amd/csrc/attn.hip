@@ -173,6 +173,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // issue back to back.
   // Rows of one sequence span less than 4 GiB in each array (checked by the
   // host), so a row's offset from its sequence base is 32-bit arithmetic.
+  // Plain (cached) loads: the other head blocks of the query gather the same
+  // rows through the same XCD's L2, and a streaming hint would evict them.
   const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride + 16 * g;
   const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride + 2 * g;
   const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride + 32 * g;
@@ -187,13 +189,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const uint32_t r = gr.valid ? id : 0u;
 #pragma unroll
     for (int i = 0; i < NCW; ++i) {
-      gr.cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seq_codes + r * cs32 + 64 * i));
+      gr.cw[i] = *reinterpret_cast<const u32x4*>(seq_codes + r * cs32 + 64 * i);
       gr.sb[i] = *reinterpret_cast<const uint16_t*>(seq_scales + r * ss32 + 8 * i);
     }
     if constexpr (DR > 0) {
 #pragma unroll
       for (int t = 0; t < RW; ++t)
-        gr.rw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seq_rope + r * rs32 + 16 * t));
+        gr.rw[t] = *reinterpret_cast<const u32x4*>(seq_rope + r * rs32 + 16 * t);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
