@@ -446,7 +446,9 @@ static void attn_plan(int B, int H, int K, int* n_split, int* per_split) {
   const int n_hg = (H + 15) / 16;
   const int tiles = (K + AT_TILE - 1) / AT_TILE;
   const int base = B * n_hg;
-  int s = base >= 512 ? 1 : (512 + base - 1) / max(base, 1);
+  // about one workgroup per CU: measured, splitting further (two per CU)
+  // costs more in partials and contention than it gains in parallelism
+  int s = base >= 256 ? 1 : (256 + base - 1) / max(base, 1);
   s = max(s, (tiles + AT_IDS / AT_TILE - 1) / (AT_IDS / AT_TILE));  // <= 8 tiles per split
   s = max(1, min(s, tiles));
   const int tps = (tiles + s - 1) / s;
