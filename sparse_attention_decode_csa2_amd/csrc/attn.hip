@@ -390,6 +390,315 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 }
 
+// Two head groups (32 heads) per workgroup of eight waves; wave w serves head
+// group w / 4 and plays the role of wave w % 4 above for it.  The two waves of
+// a role gather the same 16 entries: each fetches and dequantises half of the
+// code words (words 2k, 2k + 1 of its quarter entry for head group k), scores
+// them from its registers, stores them to the value tile and, after a
+// barrier, scores the other half from the tile.  So one gather and one
+// dequantisation serve 32 heads, and the L1 of the CU sees each code byte
+// once.  The value tile is double-buffered (tile t in buffer t % 2), which
+// leaves two barriers per tile: tile t + 1 overwrites the buffer of tile t - 1
+// only after every wave has passed tile t's first barrier, i.e. finished the
+// value products of tile t - 1.  The softmax of each wave runs against its
+// own maximum; one exchange of (max, sum) per tile rescales the running state
+// and each wave's P as it enters the value products.
+template <int DC, int DR>
+struct PairGatherRegs {
+  static constexpr int NHW = DC / 256;               // 16-byte code words per lane: half of a quarter entry
+  static constexpr int RW = DR > 0 ? DR / 32 : 1;    // 16-byte RoPE words per lane
+  u32x4 cw[NHW];
+  uint16_t sb[NHW];  // the two scale bytes of each code word
+  u32x4 rw[RW];
+  bool valid;        // the lane's entry is selected and inside the cache
+};
+
+template <int DC, int DR>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_pair_kernel(
+    const uint16_t* __restrict__ q, const CacheRef cache,
+    const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, float sm_scale_log2e, int n_hp,
+    int n_split, int per_split, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  constexpr int KSL = DC / 32;           // latent k-steps
+  constexpr int KSR = DR / 32;           // RoPE k-steps
+  constexpr int LDK = DC + 16;           // fp16 pitch of the latent tile (8 mod 32 dwords)
+  constexpr int QCH = DC / 4;            // latent channels per PV wave
+  constexpr int NDB = QCH / 16;          // PV d-blocks per wave
+  using GR = PairGatherRegs<DC, DR>;
+  constexpr int NHW = GR::NHW, RW = GR::RW;
+  static_assert(8 * NHW == KSL && (DR == 0 || RW == KSR), "gather layout = MFMA k-steps");
+  __shared__ __attribute__((aligned(16))) _Float16 sK[2][AT_TILE][LDK];
+  __shared__ __attribute__((aligned(16))) _Float16 sP[2][16][AT_TILE + 8];
+  __shared__ __attribute__((aligned(16))) float sML[2][16][4][2];  // head group, head, role: (max, sum)
+  __shared__ float sFinM[2][16], sFinL[2][16];
+  __shared__ int32_t sIdx[AT_IDS_PAD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int hgl = wave >> 2, rl = wave & 3;  // head group within the pair, role
+  // workgroup x runs on XCD x % 8; that XCD's slots x / 8 enumerate
+  // (query b / 8, slice, head pair) for the queries b = xcd (mod 8)
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int per_q = n_split * n_hp;
+  const int64_t b = (int64_t)(slot / per_q) * 8 + xcd;
+  if (b >= B) return;  // padding of the grid to whole groups of eight queries
+  const int split = (slot % per_q) / n_hp;
+  const int h0 = (slot % n_hp) * 32 + 16 * hgl;  // this wave's heads: h0 + 0 .. 15
+  const int e_begin = split * per_split;
+  const int e_end = min(K, e_begin + per_split);
+  const int32_t* idx_row = idx + b * K;
+  const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
+  // own code words 2*hgl + k, the partner's 2*(1 - hgl) + k
+  const int own_w = 2 * hgl, oth_w = 2 - 2 * hgl;
+
+  // ---- entry ids to LDS (one per thread), loads in the order their data is needed
+  static_assert(AT_IDS == 512 && AT_IDS_PAD - AT_IDS <= 512, "id staging layout");
+  const int32_t id_t = idx_row[min(e_begin + tid, max(e_end - 1, 0))];
+  // ---- query heads h0 + n as MFMA B operands, ordered as this wave uses
+  // them: local k-step 4k + j for own word k, 8 + 4k + j for the partner's
+  f16x8 Bq[KSL];
+  bf16x8 Br[KSR > 0 ? KSR : 1];
+  float fscale;
+  const bool hv = h0 + n < H;
+  u32x4 qraw[KSL + KSR];
+  {
+    const uint16_t* qrow = q + (b * H + (hv ? h0 + n : 0)) * (DC + DR);
+#pragma unroll
+    for (int t = 0; t < KSL + KSR; ++t) {
+      int off;
+      if (t < KSL) {
+        const int word = (t < KSL / 2 ? own_w : oth_w) + ((t % (KSL / 2)) >> 2);
+        off = 128 * word + 32 * g + 8 * (t & 3);
+      } else {
+        off = DC + 16 * g + 8 * (t - KSL);
+      }
+      qraw[t] = *reinterpret_cast<const u32x4*>(qrow + off);
+    }
+  }
+  sIdx[tid] = e_begin + tid < e_end ? id_t : -1;
+  if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
+  __syncthreads();
+
+  const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride + 16 * g;
+  const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride + 2 * g;
+  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride + 32 * g;
+  const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
+  const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
+  const int cw_off = 64 * own_w, sb_off = 8 * own_w;
+  auto gather = [&](GR& gr, int tile) {
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t id = (uint32_t)sIdx[tile * AT_TILE + 16 * rl + n];
+    gr.valid = id < ncap32;
+    const uint32_t r = gr.valid ? id : 0u;
+#pragma unroll
+    for (int k = 0; k < NHW; ++k) {
+      gr.cw[k] = *reinterpret_cast<const u32x4*>(seq_codes + r * cs32 + cw_off + 64 * k);
+      gr.sb[k] = *reinterpret_cast<const uint16_t*>(seq_scales + r * ss32 + sb_off + 8 * k);
+    }
+    if constexpr (DR > 0) {
+#pragma unroll
+      for (int t = 0; t < RW; ++t)
+        gr.rw[t] = *reinterpret_cast<const u32x4*>(seq_rope + r * rs32 + 16 * t);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;  // per head h0 + n
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](GR& gr, int buf) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NHW; ++k) asm volatile("" : "+v"(gr.sb[k]));
+    _Float16 (*tk)[LDK] = sK[buf];
+    const int e = 16 * rl + n;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    // ---- own half: dequantise, score from registers, store to the tile
+#pragma unroll
+    for (int k = 0; k < NHW; ++k) {
+      const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gr.valid ? (uint32_t)gr.sb[k] : 0u, 1.0f, false);
+      const f16x2 s_lo = {sc[0], sc[0]}, s_hi = {sc[1], sc[1]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t word = gr.cw[k][j];
+        const f16x2 sv = j < 2 ? s_lo : s_hi;
+        const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sv;
+        const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sv;
+        const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sv;
+        const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sv;
+        const f16x8 a = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        *reinterpret_cast<f16x8*>(&tk[e][tile_col(e, 4 * (own_w + k) + g, j)]) = a;
+        c = mfma16x16x32_f16(a, Bq[4 * k + j], c);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < KSR; ++t) c = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, gr.rw[t]), Br[t], c);
+    const uint64_t vb = __ballot(g == 0 && gr.valid);
+    __syncthreads();  // both halves of the tile are in the buffer
+    // ---- the partner's half from the tile
+#pragma unroll
+    for (int k = 0; k < NHW; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&tk[e][tile_col(e, 4 * (oth_w + k) + g, j)]);
+        c = mfma16x16x32_f16(a, Bq[KSL / 2 + 4 * k + j], c);
+      }
+    // c[i] = S^T[entry 16*rl + 4g + i][head h0 + n]
+    float s2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s2[i] = ((vb >> (4 * g + i)) & 1u) ? c[i] * fscale : -INFINITY;
+    // ---- softmax of head h0 + n against this wave's maximum
+    float mt = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+    mt = fmaxf(mt, xor16f(mt));
+    mt = fmaxf(mt, xor32f(mt));
+    const float mt_ref = mt == -INFINITY ? 0.f : mt;  // masked scores give exp2(-inf) = 0
+    float p[4], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(s2[i] - mt_ref);
+      ps += p[i];
+    }
+    ps += xor16f(ps);
+    ps += xor32f(ps);
+    if (g == 0) {
+      sML[hgl][n][rl][0] = mt;
+      sML[hgl][n][rl][1] = ps;
+    }
+    *reinterpret_cast<f16x4*>(&sP[hgl][n][16 * rl + 4 * g]) =
+        f16x4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    __syncthreads();
+    float fw[4];  // exp2(maximum of role w - new maximum) for head h0 + n
+    float alpha;
+    {
+      const f32x4 ml01 = *reinterpret_cast<const f32x4*>(&sML[hgl][n][0][0]);
+      const f32x4 ml23 = *reinterpret_cast<const f32x4*>(&sML[hgl][n][2][0]);
+      const float mw[4] = {ml01[0], ml01[2], ml23[0], ml23[2]};
+      const float sw[4] = {ml01[1], ml01[3], ml23[1], ml23[3]};
+      const float m_new = fmaxf(m_run, fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3])));
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // all masked so far: O = l = 0
+      alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      float l_tile = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        fw[w] = __builtin_amdgcn_exp2f(mw[w] - m_ref);
+        l_tile += fw[w] * sw[w];
+      }
+      l_run = l_run * alpha + l_tile;
+      m_run = m_new;
+    }
+    // ---- O[heads][channels of this role] = alpha * O + P . V
+    {
+      float al[4];  // the rows of acc are heads h0 + 4g + i: their alpha from lanes 4g + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        al[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * g + i), __float_as_int(alpha)));
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[d][i] *= al[i];
+      const int tr_r = n >> 2, tr_c = n & 3;
+#pragma unroll
+      for (int u = 0; u < AT_TILE / 32; ++u) {
+        // entries 32u + 8g .. + 7 were exponentiated by role 2u + g / 2
+        const _Float16 fu = (_Float16)((g >> 1) ? fw[2 * u + 1] : fw[2 * u]);
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&sP[hgl][n][32 * u + 8 * g]) * fu;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const int ch = 32 * pv_chunk<DC>(rl, d >> 1) + 16 * (d & 1) + 4 * tr_c;
+          const int r0 = 32 * u + 8 * g + tr_r, r1 = r0 + 4;
+          const f16x4 v0 = tr16_read(&tk[r0][tile_col(r0, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+          const f16x4 v1 = tr16_read(&tk[r1][tile_col(r1, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+          const f16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[d] = mfma16x16x32_f16(a, bv, acc[d]);
+        }
+      }
+    }
+  };
+
+  if (n_tiles > 0) {
+    GR ga, gb;
+    gather(ga, 0);
+    {
+      uint32_t mx = 0;
+#pragma unroll
+      for (int t = 0; t < KSL + KSR; ++t) {
+        if (!hv) qraw[t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = max(mx, max(qraw[t][j] & 0x7FFFu, (qraw[t][j] >> 16) & 0x7FFFu));
+      }
+      mx = max(mx, xor16(mx));
+      mx = max(mx, xor32(mx));
+      int e = (int)((mx >> 7) & 0xFF) - 127;
+      if (e < -126) e = -126;
+      const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - e));
+      const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
+      fscale = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
+#pragma unroll
+      for (int t = 0; t < KSL; ++t) {
+        f16x8 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = (_Float16)(bf16_bits_to_f32(qraw[t][j] & 0xFFFFu) * up);
+          o[2 * j + 1] = (_Float16)(bf16_bits_to_f32(qraw[t][j] >> 16) * up);
+        }
+        Bq[t] = o;
+      }
+#pragma unroll
+      for (int t = 0; t < KSR; ++t) {
+        bf16x8 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = (__bf16)(bf16_bits_to_f32(qraw[KSL + t][j] & 0xFFFFu) * up);
+          o[2 * j + 1] = (__bf16)(bf16_bits_to_f32(qraw[KSL + t][j] >> 16) * up);
+        }
+        Br[t] = o;
+      }
+    }
+    gather(gb, 1);
+    int t = 0;
+    for (; t + 2 <= n_tiles; t += 2) {
+      process(ga, 0);
+      gather(ga, t + 2);
+      process(gb, 1);
+      gather(gb, t + 3);
+    }
+    if (t < n_tiles) process(ga, 0);
+  }
+
+  // ---- epilogue: lane (channel n of each d-block, k-group g) holds heads h0 + 4g + i
+  if (rl == 0 && g == 0) {
+    sFinM[hgl][n] = m_run;
+    sFinL[hgl][n] = l_run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * g + i;
+    const int h = h0 + hl;
+    if (h >= H) continue;
+    const float m = sFinM[hgl][hl], l = sFinL[hgl][hl];
+    if (n_split == 1) {
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      float* orow = out + (b * H + h) * DC;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) orow[32 * pv_chunk<DC>(rl, d >> 1) + 16 * (d & 1) + n] = acc[d][i] * inv;
+      if (lse && rl == 0 && n == 0) lse[b * H + h] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
+    } else {
+      const int64_t slot_o = (b * H + h) * n_split + split;
+      float* orow = ws_o + slot_o * DC;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) orow[32 * pv_chunk<DC>(rl, d >> 1) + 16 * (d & 1) + n] = acc[d][i];
+      if (rl == 0 && n == 0) {
+        ws_ml[2 * slot_o] = m;
+        ws_ml[2 * slot_o + 1] = l;
+      }
+    }
+  }
+}
+
 // Merge the per-slice partial results of one (b, h) row by log-sum-exp; each
 // of the 128 threads owns 4 consecutive channels (d_c <= 512).  The slices are
 // taken 8 at a time with every load of a round issued together (one memory
@@ -441,9 +750,19 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
   if (lse && threadIdx.x == 0) lse[row] = L > 0.f ? (m + __log2f(L)) * LN2 : -INFINITY;
 }
 
+// Heads per workgroup: 32 (two head groups, eight waves) for the 512-channel
+// latent when the batch alone gives a workgroup per CU that way, else 16.
+// Measured: the pair kernel is faster unsplit (batch 128: 31.8 vs 34.7 us)
+// but slower wherever slices are needed (batch 1: 14.5 vs 11.3 us), where
+// the per-workgroup latency path rather than the CU's throughput sets the time.
+static int attn_heads_per_wg(int B, int H, int d_c) {
+  return (d_c == 512 && H > 16 && (int64_t)B * ((H + 31) / 32) >= 256) ? 32 : 16;
+}
+
 // Slices per query: enough workgroups for 256 CUs, whole 64-entry tiles.
-static void attn_plan(int B, int H, int K, int* n_split, int* per_split) {
-  const int n_hg = (H + 15) / 16;
+static void attn_plan(int B, int H, int K, int d_c, int* n_split, int* per_split) {
+  const int hpw = attn_heads_per_wg(B, H, d_c);
+  const int n_hg = (H + hpw - 1) / hpw;
   const int tiles = (K + AT_TILE - 1) / AT_TILE;
   const int base = B * n_hg;
   // about one workgroup per CU: measured, splitting further (two per CU)
@@ -460,7 +779,7 @@ static void attn_plan(int B, int H, int K, int* n_split, int* per_split) {
 // Workspace: partial outputs f32 [B, H, s, d_c], then (max, sum) f32 [B, H, s, 2].
 size_t attn_workspace_bytes(int B, int H, int d_c, int K) {
   int s, ps;
-  attn_plan(B, H, K, &s, &ps);
+  attn_plan(B, H, K, d_c, &s, &ps);
   if (s <= 1) return 0;
   return (size_t)B * H * s * ((size_t)d_c + 2) * sizeof(float);
 }
@@ -470,20 +789,25 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
                               void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   int s, ps;
-  attn_plan(B, H, K, &s, &ps);
-  const int n_hg = (H + 15) / 16;
+  attn_plan(B, H, K, d_c, &s, &ps);
+  const int hpw = attn_heads_per_wg(B, H, d_c);
+  const int n_hg = (H + hpw - 1) / hpw;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = s > 1 ? ws_o + (size_t)B * H * s * d_c : nullptr;
   const int64_t groups = ((int64_t)B + 7) / 8;  // of eight queries, one per XCD
-  const dim3 grid((unsigned)(groups * 8 * n_hg * s)), blk(256);
+  const dim3 grid((unsigned)(groups * 8 * n_hg * s));
   const float sl = sm_scale * LOG2E;
-#define CSA2_ATTN(DCV, DRV)                                                                     \
-  hipLaunchKernelGGL((sparse_attn_kernel<DCV, DRV>), grid, blk, 0, stream, q, cache, idx, K, B, H, \
-                     N_cap, sl, n_hg, s, ps, out, lse, ws_o, ws_ml)
-  if (d_c == 512 && d_r == 64) CSA2_ATTN(512, 64);
-  else if (d_c == 512 && d_r == 0) CSA2_ATTN(512, 0);
-  else if (d_c == 128 && d_r == 0) CSA2_ATTN(128, 0);
-  else if (d_c == 128 && d_r == 64) CSA2_ATTN(128, 64);
+#define CSA2_ATTN(KERNEL, THREADS, DCV, DRV)                                                          \
+  hipLaunchKernelGGL((KERNEL<DCV, DRV>), grid, dim3(THREADS), 0, stream, q, cache, idx, K, B, H, N_cap, sl, \
+                     n_hg, s, ps, out, lse, ws_o, ws_ml)
+  if (hpw == 32) {
+    if (d_r == 64) CSA2_ATTN(sparse_attn_pair_kernel, 512, 512, 64);
+    else if (d_r == 0) CSA2_ATTN(sparse_attn_pair_kernel, 512, 512, 0);
+    else return hipErrorInvalidValue;
+  } else if (d_c == 512 && d_r == 64) CSA2_ATTN(sparse_attn_kernel, 256, 512, 64);
+  else if (d_c == 512 && d_r == 0) CSA2_ATTN(sparse_attn_kernel, 256, 512, 0);
+  else if (d_c == 128 && d_r == 0) CSA2_ATTN(sparse_attn_kernel, 256, 128, 0);
+  else if (d_c == 128 && d_r == 64) CSA2_ATTN(sparse_attn_kernel, 256, 128, 64);
   else return hipErrorInvalidValue;
 #undef CSA2_ATTN
   hipError_t e = hipGetLastError();

@@ -138,3 +138,21 @@ def test_attention_every_e4m3_scale_byte():
     ro, rl = oracle.sparse_attn(np_bits(q), codes.cpu().numpy(), scales.cpu().numpy(),
                                 np_bits(rope.contiguous()), idx, wl.sm_scale)
     attn_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("H,dr,K", [(64, 64, 512), (64, 64, 200), (48, 64, 130), (64, 0, 512)])
+def test_attention_paired_head_groups(H, dr, K):
+    """Batches large enough for 32 heads per workgroup (one gather and one
+    dequantisation shared by two head groups): masked, out-of-range and
+    repeated ids, an empty row, ragged K and a partial head pair."""
+    B = 260 if H == 48 else 130
+    wl = W.WORKLOADS[3].scaled(H=H, d_r=dr)
+    note(f"attn: paired B={B} H={H} d_r={dr} K={K}")
+    rng = np.random.default_rng(H + dr + K)
+    N = 1024
+    idx = _rand_idx(rng, B, K, N)
+    idx[0, ::7] = -1
+    idx[1, ::5] = N + 3
+    idx[2, K // 4:K // 2] = idx[2, 0]
+    idx[3, :] = -1
+    _check(wl, B, N, idx)
