@@ -455,6 +455,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   // ---- entry ids to LDS (one per thread), loads in the order their data is needed
   static_assert(AT_IDS == 512 && AT_IDS_PAD - AT_IDS <= 512, "id staging layout");
   const int32_t id_t = idx_row[min(e_begin + tid, max(e_end - 1, 0))];
+  // ---- the 32 query rows, each fetched once (the four waves of a head group
+  // all need all of its 16 rows): 16-byte pieces to LDS, in the second value
+  // buffer, which is free until the second tile
+  constexpr int QP = (DC + DR) / 8;          // 16-byte pieces per query row
+  constexpr int QPITCH = DC + DR + 8;        // bf16 pitch of a staged row (rows 4 banks apart)
+  constexpr int QN = (32 * QP + 511) / 512;  // pieces per thread
+  static_assert(32 * QPITCH * 2 <= (int)sizeof(sK[1]), "query staging fits the second buffer");
+  uint16_t* qs = reinterpret_cast<uint16_t*>(&sK[1][0][0]);
+  const int hq0 = (slot % n_hp) * 32;
+  u32x4 qv[QN];
+#pragma unroll
+  for (int k = 0; k < QN; ++k) {
+    const int pc = tid + 512 * k, row = pc / QP, col = pc - row * QP;
+    const bool ok = pc < 32 * QP && hq0 + row < H;
+    qv[k] = ok ? *reinterpret_cast<const u32x4*>(q + (b * H + hq0 + row) * (DC + DR) + 8 * col)
+               : u32x4{0u, 0u, 0u, 0u};
+  }
+  sIdx[tid] = e_begin + tid < e_end ? id_t : -1;
+  if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
+#pragma unroll
+  for (int k = 0; k < QN; ++k) {
+    const int pc = tid + 512 * k, row = pc / QP, col = pc - row * QP;
+    if (pc < 32 * QP) *reinterpret_cast<u32x4*>(qs + row * QPITCH + 8 * col) = qv[k];
+  }
+  __syncthreads();
   // ---- query heads h0 + n as MFMA B operands, ordered as this wave uses
   // them: local k-step 4k + j for own word k, 8 + 4k + j for the partner's
   f16x8 Bq[KSL];
@@ -463,7 +488,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const bool hv = h0 + n < H;
   u32x4 qraw[KSL + KSR];
   {
-    const uint16_t* qrow = q + (b * H + (hv ? h0 + n : 0)) * (DC + DR);
+    const uint16_t* qrow = qs + (16 * hgl + n) * QPITCH;
 #pragma unroll
     for (int t = 0; t < KSL + KSR; ++t) {
       int off;
@@ -476,9 +501,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       qraw[t] = *reinterpret_cast<const u32x4*>(qrow + off);
     }
   }
-  sIdx[tid] = e_begin + tid < e_end ? id_t : -1;
-  if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
-  __syncthreads();
 
   const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride + 16 * g;
   const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride + 2 * g;
