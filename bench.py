@@ -13,6 +13,9 @@ stream the kernels run on), against the 8 TB/s HBM peak.  `traffic` comes from
 the committed rocprofv3 FETCH_SIZE / WRITE_SIZE measurement of that kernel
 (profiles/), and is null when the kernel source changed since it was taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`single_step_us_cold` is one step run on its own after a 512 MiB write has
+evicted the caches (median of five): the latency of an isolated decode step,
+beside `value`, the steady-state rate of back-to-back steps.
 """
 
 import argparse
@@ -299,6 +302,17 @@ def main():
     for s in stages:
         g_stage[s].replay()          # untimed pass over the same launches
     stage_us = {s: 1000.0 * timed(g_stage[s]) / args.steps for s in stages}
+    # one step on its own with cold caches (what an isolated decode step
+    # waits for, beside the steady-state rate above): a 512 MiB write evicts
+    # the L2s and the Infinity Cache before each run; median of five
+    g_one = capture(step.step, 1)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(5):
+        flush.fill_(1)
+        cold.append(1000.0 * timed(g_one))
+    del flush
+    single_step_us = sorted(cold)[len(cold) // 2]
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
     kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
@@ -332,6 +346,7 @@ def main():
                    "context_tokens": wl.N * 4, "latent": wl.d_c, "rope": wl.d_r, "heads": wl.H,
                    "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "rotation_sets": R},
         "step_hbm_gbs": alg["step"] / (ms_per_step * 1e-3) / 1e9,
+        "single_step_us_cold": round(single_step_us, 2),
         "step_alg_bytes": alg["step"],
         "stage_us": {s: round(v, 3) for s, v in stage_us.items()},
         "stage_gbs": {s: round(alg[s] / (stage_us[s] * 1e-6) / 1e9, 1) for s in stages},

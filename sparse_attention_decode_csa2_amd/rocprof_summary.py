@@ -17,6 +17,15 @@ profiles/.
         kernel of known size (a plain device copy: N bytes read, N written).
         The output is what bench.py reads as roofline.traffic, tagged with a
         hash of the kernel's source so that a stale measurement is ignored.
+
+    python -m sparse_attention_decode_csa2_amd.rocprof_summary counters DIR \
+        --kernel REGEX --workload NAME --command "..."
+        Average per dispatch of every counter of a `--pmc` run for the kernels
+        matching REGEX (instances summed), and the matrix-core utilisation
+        SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs) when both
+        are present (ROCm's MfmaUtil): the rows hold GRBM_GUI_ACTIVE, the busy
+        cycles of the kernel, summed over MI355X's 8 XCDs, and the MFMA busy
+        cycles summed over its 256 x 4 SIMDs.
 """
 
 import argparse
@@ -75,7 +84,7 @@ def stats(args):
 
 
 def _counter_means(d, counter):
-    """Average counter value per dispatch, keyed by kernel name."""
+    """Average counter value per dispatch (instances summed), keyed by kernel name."""
     acc = {}
     for f in _find(d, "counter_collection.csv"):
         with open(f) as fh:
@@ -137,6 +146,31 @@ def traffic(args):
     ]))
 
 
+def counters(args):
+    names = set()
+    for f in _find(args.dir, "counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                names.add(r["Counter_Name"])
+    vals = {}
+    knames = []
+    for c in sorted(names):
+        v, nd, kn = _pick(_counter_means(args.dir, c), args.kernel, "measured")
+        vals[c] = (v, nd)
+        knames = kn
+    out = ["# rocprofv3 counters, average per dispatch",
+           f"# command: {args.command}",
+           f"workload: {args.workload}",
+           f"kernel: {' | '.join(_short(k, 200) for k in knames)}"]
+    for c, (v, nd) in vals.items():
+        out.append(f"{c}: {v:.1f}  ({nd} dispatches)")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals:
+        busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"][0]
+        simd_cycles = vals["GRBM_GUI_ACTIVE"][0] / 8.0 * 1024.0
+        out.append(f"mfma_util: {busy / simd_cycles:.4f}  (matrix-core busy cycles over the kernel's SIMD cycles)")
+    print("\n".join(out))
+
+
 def read_traffic(path):
     """Parse a traffic summary written by `traffic` into a dict of strings."""
     rec = {}
@@ -164,8 +198,13 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--source", required=True)
     t.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", required=True)
     args = ap.parse_args(argv)
-    {"stats": stats, "traffic": traffic}[args.cmd](args)
+    {"stats": stats, "traffic": traffic, "counters": counters}[args.cmd](args)
 
 
 if __name__ == "__main__":
