@@ -31,10 +31,11 @@
 // fences, which write back and invalidate the whole XCD L2 under the other
 // workgroups' gathers).
 //
-// Workgroups are numbered so that all of one query's workgroups land on the
-// same XCD (consecutive workgroup ids go round-robin over the eight XCDs): the
-// head groups of a query gather the same entries, and only the first of them
-// misses in that XCD's L2.
+// Workgroups are numbered so that all head groups of one (query, slice) land
+// on the same XCD (consecutive workgroup ids go round-robin over the eight
+// XCDs): they gather the same entries, and only the first of them misses in
+// that XCD's L2; the slices of a query, which share nothing, go to different
+// XCDs.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -99,7 +100,7 @@ template <int DC, int DR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
     const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, float sm_scale_log2e, int n_hg,
-    int n_split, int per_split, float* __restrict__ out, float* __restrict__ lse,
+    int n_split, int per_split, int spread, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int KSL = DC / 32;           // latent k-steps
   constexpr int KSR = DR / 32;           // RoPE k-steps
@@ -116,14 +117,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  // workgroup x runs on XCD x % 8; that XCD's slots x / 8 enumerate
-  // (query b / 8, slice, head group) for the queries b = xcd (mod 8)
+  // workgroup x runs on XCD x % 8, and the head groups of one (query, slice)
+  // unit, which gather the same entries, always share that XCD's L2.  With
+  // eight queries or more, all of a query's units go to XCD b % 8 (so the
+  // combine of its slices finds their partials in that L2); a smaller batch
+  // spreads its units, which share nothing, over the XCDs (`spread`).
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
-  const int per_q = n_split * n_hg;
-  const int64_t b = (int64_t)(slot / per_q) * 8 + xcd;
-  if (b >= B) return;  // padding of the grid to whole groups of eight queries
-  const int split = (slot % per_q) / n_hg;
+  int64_t b;
+  int split;
+  if (spread) {
+    const int64_t unit = (int64_t)(slot / n_hg) * 8 + xcd;
+    if (unit >= (int64_t)B * n_split) return;  // padding of the grid to whole groups of eight units
+    b = unit / n_split;
+    split = (int)(unit - b * n_split);
+  } else {
+    const int per_q = n_split * n_hg;
+    b = (int64_t)(slot / per_q) * 8 + xcd;
+    if (b >= B) return;  // padding of the grid to whole groups of eight queries
+    split = (slot % per_q) / n_hg;
+  }
   const int hg = slot % n_hg;
   const int h0 = hg * 16;
   const int e_begin = split * per_split;
@@ -417,7 +430,7 @@ template <int DC, int DR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_pair_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
     const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, float sm_scale_log2e, int n_hp,
-    int n_split, int per_split, float* __restrict__ out, float* __restrict__ lse,
+    int n_split, int per_split, int spread, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int KSL = DC / 32;           // latent k-steps
   constexpr int KSR = DR / 32;           // RoPE k-steps
@@ -436,14 +449,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int hgl = wave >> 2, rl = wave & 3;  // head group within the pair, role
-  // workgroup x runs on XCD x % 8; that XCD's slots x / 8 enumerate
-  // (query b / 8, slice, head pair) for the queries b = xcd (mod 8)
+  // XCD placement as in the 16-head kernel (head pairs for head groups)
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
-  const int per_q = n_split * n_hp;
-  const int64_t b = (int64_t)(slot / per_q) * 8 + xcd;
-  if (b >= B) return;  // padding of the grid to whole groups of eight queries
-  const int split = (slot % per_q) / n_hp;
+  int64_t b;
+  int split;
+  if (spread) {
+    const int64_t unit = (int64_t)(slot / n_hp) * 8 + xcd;
+    if (unit >= (int64_t)B * n_split) return;
+    b = unit / n_split;
+    split = (int)(unit - b * n_split);
+  } else {
+    const int per_q = n_split * n_hp;
+    b = (int64_t)(slot / per_q) * 8 + xcd;
+    if (b >= B) return;
+    split = (slot % per_q) / n_hp;
+  }
   const int h0 = (slot % n_hp) * 32 + 16 * hgl;  // this wave's heads: h0 + 0 .. 15
   const int e_begin = split * per_split;
   const int e_end = min(K, e_begin + per_split);
@@ -724,19 +745,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // Merge the per-slice partial results of one (b, h) row by log-sum-exp; each
 // of the 128 threads owns 4 consecutive channels (d_c <= 512).  The slices are
 // taken 8 at a time with every load of a round issued together (one memory
-// round trip per 8 slices), merged online.  Block x runs on XCD x % 8 like the
+// round trip per 8 slices), merged online.  Unless the attention spread its
+// slices (`spread`: block x merges row x), block x runs on XCD x % 8 like the
 // attention workgroups of its query, whose partials sit in that XCD's L2.
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ ws_o,
                                                            const float* __restrict__ ws_ml,
-                                                           int B, int H, int n_split, int DC,
+                                                           int B, int H, int n_split, int DC, int spread,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
   constexpr int R = 8;
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int64_t b = (int64_t)(slot / H) * 8 + xcd;
-  if (b >= B) return;
-  const int64_t row = b * H + slot % H;
+  int64_t row;
+  if (spread) {
+    row = blockIdx.x;
+  } else {
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int64_t b = (int64_t)(slot / H) * 8 + xcd;
+    if (b >= B) return;
+    row = b * H + slot % H;
+  }
   const float* ml = ws_ml + row * n_split * 2;
   const int c = 4 * threadIdx.x;
   const bool has = c < DC;
@@ -816,12 +843,14 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
   const int n_hg = (H + hpw - 1) / hpw;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = s > 1 ? ws_o + (size_t)B * H * s * d_c : nullptr;
-  const int64_t groups = ((int64_t)B + 7) / 8;  // of eight queries, one per XCD
-  const dim3 grid((unsigned)(groups * 8 * n_hg * s));
+  // slices of a small batch spread over the XCDs; else one query per XCD
+  const int spread = B < 8 ? 1 : 0;
+  const int64_t groups = spread ? ((int64_t)B * s + 7) / 8 : ((int64_t)B + 7) / 8 * s;
+  const dim3 grid((unsigned)(groups * 8 * n_hg));
   const float sl = sm_scale * LOG2E;
 #define CSA2_ATTN(KERNEL, THREADS, DCV, DRV)                                                          \
   hipLaunchKernelGGL((KERNEL<DCV, DRV>), grid, dim3(THREADS), 0, stream, q, cache, idx, K, B, H, N_cap, sl, \
-                     n_hg, s, ps, out, lse, ws_o, ws_ml)
+                     n_hg, s, ps, spread, out, lse, ws_o, ws_ml)
   if (hpw == 32) {
     if (d_r == 64) CSA2_ATTN(sparse_attn_pair_kernel, 512, 512, 64);
     else if (d_r == 0) CSA2_ATTN(sparse_attn_pair_kernel, 512, 512, 0);
@@ -834,8 +863,9 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
 #undef CSA2_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(groups * 8 * H)), dim3(128), 0, stream, ws_o,
-                     ws_ml, B, H, s, d_c, out, lse);
+  const int64_t cblocks = spread ? (int64_t)B * H : ((int64_t)B + 7) / 8 * 8 * H;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)cblocks), dim3(128), 0, stream, ws_o, ws_ml, B, H,
+                     s, d_c, spread, out, lse);
   return hipGetLastError();
 }
 
