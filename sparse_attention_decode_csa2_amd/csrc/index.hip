@@ -8,12 +8,13 @@
 // The multi-head q . K contraction runs on the matrix cores: one
 // v_mfma_f32_16x16x32_bf16 per 32 key dimensions computes a 16 (heads, padded
 // with zero rows) x 16 (keys) tile.  For k-step s, lane (key l % 16, group
-// l / 16) supplies dimensions 32s + 8 (l / 16) .. +7 of its key, so the four
-// lanes of a key read 64 contiguous bytes per load instruction and a wave's
-// KS instructions read 16 whole keys (contiguous in Full mode, two 8-entry
-// runs per tile in pool mode).  The query is laid out the same way, which is
-// the MFMA's own k order.  The epilogue applies ReLU and the head weights and
-// reduces the four head quarters across lane groups.
+// l / 16) supplies dimensions 32s + 8 (l / 16) .. +7 of its key; a wave's KS
+// steps cover 16 whole keys (contiguous in Full mode, two 8-entry runs per
+// tile in pool mode).  Full mode loads the 16 keys contiguously and reorders
+// them through LDS (see below); pool mode loads each lane's operand directly.
+// The query is laid out the same way, which is the MFMA's own k order.  The
+// epilogue applies ReLU and the head weights and reduces the four head
+// quarters across lane groups.
 //
 // HBM-bound: 2*D_I bytes of key per scored entry against 4*H_I*D_I flops
 // (8 flop/byte at H_I = 8): the matrix cores only have to keep up with HBM.
@@ -57,13 +58,9 @@ __global__ __launch_bounds__(256) void index_kernel(
   int nb = 0;
   if (POOL) nb = min(max(n_blocks[b], 0), P_max);
 
-  const int64_t tile0 = (wg * 4 + wave) * TPW;
-  u32x4 Bv[TPW][KS];
-  int64_t pos[TPW];
-  bool ok[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int64_t col = (tile0 + t) * 16 + n;
+  // Key column col of the row -> cache position and validity (pool mode:
+  // position 8 * pool[col / 8] + col % 8).
+  auto locate = [&](int64_t col, int64_t* p_out) {
     int64_t p = col;
     bool valid;
     if (POOL) {
@@ -75,21 +72,66 @@ __global__ __launch_bounds__(256) void index_kernel(
     } else {
       valid = col < nv;
     }
-    pos[t] = p;
-    ok[t] = valid;
-    const uint16_t* krow = k + (b * N_cap + (valid ? p : 0)) * D_I + 8 * g;
+    *p_out = p;
+    return valid;
+  };
+  // Full mode reads keys contiguously: load s of a tile brings 16-byte word
+  // 64 s + lane of the tile's 16 consecutive keys (key (64 s + lane) / KW,
+  // word (64 s + lane) % KW of it), so a wave-wide load covers whole cache
+  // lines, and a wave-private LDS buffer turns the tile into the MFMA layout,
+  // where lane (n, g) needs word 4 s + g of key n (rows padded by one word:
+  // the stores and the operand reads hit distinct banks).  Measured: 6.25
+  // against 5.46 TB/s for loads straight into the MFMA layout, whose wave
+  // loads touch twice the cache lines, half of each.  Pool mode keeps the
+  // direct layout: one block lookup per key and tile (instead of one per
+  // load) matters more there (33.5 against 38.3 us at 32 x 16384 keys).
+  constexpr int KW = D_I / 8;                 // 16-byte words per key
+  static_assert(16 * KW == 64 * KS, "a tile is KS wave-wide loads");
+  __shared__ u32x4 kbuf[POOL ? 1 : 4][POOL ? 1 : 16 * (KW + 1)];
+  u32x4* kb = kbuf[POOL ? 0 : wave];
+  const int64_t tile0 = (wg * 4 + wave) * TPW;
+  u32x4 Bv[TPW][KS];
+  int64_t pos[TPW];
+  bool ok[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    ok[t] = locate((tile0 + t) * 16 + n, &pos[t]);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
+      const uint16_t* kp;
+      bool valid;
+      if (POOL) {
+        valid = ok[t];
+        kp = k + (b * N_cap + (valid ? pos[t] : 0)) * D_I + 8 * g + 32 * s;
+      } else {
+        const int w = 64 * s + lane;
+        int64_t p;
+        valid = locate((tile0 + t) * 16 + w / KW, &p);
+        kp = k + (b * N_cap + (valid ? p : 0)) * D_I + 8 * (w % KW);
+      }
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + 32 * s));
+      if (valid) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
       Bv[t][s] = v;
     }
   }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
+    u32x4 Bt[KS];
+    if (POOL) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) Bt[s] = Bv[t][s];
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int w = 64 * s + lane;
+        kb[(w / KW) * (KW + 1) + w % KW] = Bv[t][s];
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) Bt[s] = kb[n * (KW + 1) + 4 * s + g];
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mfma16x16x32_bf16(A[s], __builtin_bit_cast(bf16x8, Bv[t][s]), acc);
+    for (int s = 0; s < KS; ++s) acc = mfma16x16x32_bf16(A[s], __builtin_bit_cast(bf16x8, Bt[s]), acc);
     // acc[i] = dot(head 4g + i, key n of this tile)
     float part = wv[0] * fmaxf(acc[0], 0.f);
     part += wv[1] * fmaxf(acc[1], 0.f);
