@@ -75,21 +75,27 @@ __global__ __launch_bounds__(256) void index_kernel(
     *p_out = p;
     return valid;
   };
-  // Full mode reads keys contiguously: load s of a tile brings 16-byte word
-  // 64 s + lane of the tile's 16 consecutive keys (key (64 s + lane) / KW,
-  // word (64 s + lane) % KW of it), so a wave-wide load covers whole cache
-  // lines, and a wave-private LDS buffer turns the tile into the MFMA layout,
-  // where lane (n, g) needs word 4 s + g of key n (rows padded by one word:
-  // the stores and the operand reads hit distinct banks).  Measured: 6.25
-  // against 5.46 TB/s for loads straight into the MFMA layout, whose wave
-  // loads touch twice the cache lines, half of each.  Pool mode keeps the
-  // direct layout: one block lookup per key and tile (instead of one per
-  // load) matters more there (33.5 against 38.3 us at 32 x 16384 keys).
+  // Keys are read contiguously: load s of a tile brings 16-byte word
+  // 64 s + lane of the tile's 16 keys (key (64 s + lane) / KW, word
+  // (64 s + lane) % KW of it), so a wave-wide load covers whole cache lines,
+  // and a wave-private LDS buffer turns the tile into the MFMA layout, where
+  // lane (n, g) needs word 4 s + g of key n (rows padded by one word: the
+  // stores and the operand reads hit distinct banks).  Measured: 6.25 against
+  // 5.46 TB/s for loads straight into the MFMA layout, whose wave-wide loads
+  // touch twice the cache lines, half of each.  In pool mode a load's keys
+  // must then sit in one block (block a multiple of the keys per load), so
+  // that one wave-uniform block lookup serves the load; other block sizes
+  // load each lane's operand directly, one lookup per key.
   constexpr int KW = D_I / 8;                 // 16-byte words per key
   static_assert(16 * KW == 64 * KS, "a tile is KS wave-wide loads");
-  __shared__ u32x4 kbuf[POOL ? 1 : 4][POOL ? 1 : 16 * (KW + 1)];
-  u32x4* kb = kbuf[POOL ? 0 : wave];
-  const int64_t tile0 = (wg * 4 + wave) * TPW;
+  constexpr int KPL = 64 / KW;                // keys per wave-wide load
+  // contiguous loads in pool mode when every load's keys sit in one block
+  // (8-position blocks and 128-dimension keys: 4 keys per load): then a
+  // load needs one block id, the same for the whole wave
+  const bool contig = !POOL || block % KPL == 0;
+  __shared__ u32x4 kbuf[4][16 * (KW + 1)];
+  u32x4* kb = kbuf[wave];
+  const int64_t tile0 = (int64_t)(wg * 4 + __builtin_amdgcn_readfirstlane(wave)) * TPW;
   u32x4 Bv[TPW][KS];
   int64_t pos[TPW];
   bool ok[TPW];
@@ -100,11 +106,19 @@ __global__ __launch_bounds__(256) void index_kernel(
     for (int s = 0; s < KS; ++s) {
       const uint16_t* kp;
       bool valid;
-      if (POOL) {
+      const int w = 64 * s + lane;
+      if (POOL && !contig) {
         valid = ok[t];
         kp = k + (b * N_cap + (valid ? pos[t] : 0)) * D_I + 8 * g + 32 * s;
+      } else if (POOL) {
+        // block of keys 16 t' + KPL s .. (wave-uniform), then the lane's key in it
+        const int64_t c0 = (tile0 + t) * 16 + KPL * s;
+        const int64_t i = c0 / block;
+        const int64_t blk = (c0 < M && i < nb) ? (int64_t)pool[b * P_max + i] : -1;
+        const int64_t p = blk * block + (c0 - i * block) + lane / KW;
+        valid = blk >= 0 && p < nv;
+        kp = k + (b * N_cap + (valid ? p : 0)) * D_I + 8 * (w % KW);
       } else {
-        const int w = 64 * s + lane;
         int64_t p;
         valid = locate((tile0 + t) * 16 + w / KW, &p);
         kp = k + (b * N_cap + (valid ? p : 0)) * D_I + 8 * (w % KW);
@@ -117,7 +131,7 @@ __global__ __launch_bounds__(256) void index_kernel(
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     u32x4 Bt[KS];
-    if (POOL) {
+    if (POOL && !contig) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) Bt[s] = Bv[t][s];
     } else {

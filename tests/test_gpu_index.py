@@ -80,12 +80,16 @@ def test_pool_mode_workload_exact():
     assert np.array_equal(sc.cpu().numpy().astype(np.float64), rs)
 
 
-def test_pool_mode_edges():
-    note("index_pool: empty slots, negative ids, ids past n_valid, odd block sizes")
-    wl = W.WORKLOADS[1].scaled(B=3, N=300, H_I=4, D_I=64)
+@pytest.mark.parametrize("D_I,blocks", [(64, (8, 1, 3)), (128, (4, 8, 12)), (32, (16, 5))])
+def test_pool_mode_edges(D_I, blocks):
+    """Blocks holding whole wave-wide loads (contiguous loads, one lookup per
+    load; 12 does not divide a 16-key tile) and blocks that do not (a lookup
+    per key), with empty slots, negative ids and ids past n_valid."""
+    note(f"index_pool: D_I={D_I} blocks={blocks}: empty slots, negative ids, ids past n_valid")
+    wl = W.WORKLOADS[1].scaled(B=3, N=300, H_I=4, D_I=D_I)
     k = _keys(wl, 3)
     q = W.index_query(wl, DEV)
-    for block in (8, 1, 3):
+    for block in blocks:
         P_max = 40
         nbk = 300 // block
         rng = np.random.default_rng(block)
