@@ -115,10 +115,13 @@ def test_attention_on_quantized_cache_is_dense_attention_when_k_is_n():
     attn_close(out.cpu().numpy()[0], lse.cpu().numpy()[0], ro, rl)
 
 
-def test_attention_every_e4m3_scale_byte():
-    wl = W.WORKLOADS[1].scaled(H=16)
-    note("attn: every non-NaN E4M3 scale byte (subnormal, negative, 448)")
-    B, N = 2, 1024
+@pytest.mark.parametrize("H,B", [(16, 2), (64, 130)])
+def test_attention_every_e4m3_scale_byte(H, B):
+    """Both kernels (16 heads per workgroup; 32 heads per workgroup at a
+    batch that fills the GPU unsplit) over every non-NaN scale byte."""
+    wl = W.WORKLOADS[1].scaled(H=H)
+    note(f"attn: every non-NaN E4M3 scale byte (subnormal, negative, 448), H={H} B={B}")
+    N = 1024
     codes, scales, rope = csa2.alloc_cache(B, N, wl.d_c, wl.d_r, DEV)
     for b in range(B):
         c, _ = W.random_codes(wl, b, N, DEV)
