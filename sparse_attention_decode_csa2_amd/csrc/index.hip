@@ -168,18 +168,17 @@ static hipError_t launch_index_ks(const uint16_t* q, const float* w, const uint1
                                   int64_t M, float* scores, int32_t* positions, hipStream_t stream) {
   const int64_t tiles_per_row = (M + 15) / 16;
   const int64_t total_tiles = tiles_per_row * B;
-  // enough workgroups to fill 256 CUs several times over; more tiles per wave
-  // (loads issued back to back) once the grid is large
-  int tpw = 1;
-  if (total_tiles >= 4 * 4 * 4096) tpw = 4;
-  else if (total_tiles >= 2 * 4 * 2048) tpw = 2;
+  // Tiles per wave, measured: Full mode is fastest with one (its contiguous
+  // loads keep enough in flight; prefill-full-1m 80.6 us against 86.7 with
+  // four); pool mode, whose loads wait for block lookups, with two once the
+  // grid fills the GPU (reindex-1m 28.7 us against 30.4 with four).
+  const int tpw = (POOL && total_tiles >= 2 * 4 * 2048) ? 2 : 1;
   const int64_t wg_per_row = (tiles_per_row + 4 * tpw - 1) / (4 * tpw);
   const dim3 grid((unsigned)(wg_per_row * B)), blk(256);
 #define CSA2_IDX_LAUNCH(T)                                                                          \
   hipLaunchKernelGGL((index_kernel<KS, T, POOL>), grid, blk, 0, stream, q, w, k, n_valid, H_I, N_cap, \
                      pool, n_blocks, P_max, block, M, wg_per_row, scores, positions)
-  if (tpw == 4) CSA2_IDX_LAUNCH(4);
-  else if (tpw == 2) CSA2_IDX_LAUNCH(2);
+  if (tpw == 2) CSA2_IDX_LAUNCH(2);
   else CSA2_IDX_LAUNCH(1);
 #undef CSA2_IDX_LAUNCH
   return hipGetLastError();
