@@ -742,6 +742,352 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 }
 
+// 32 heads per workgroup with the waves split by role, for batches that fill
+// the GPU unsplit.  Waves 0-3 ("score waves") each gather, dequantise and
+// score 16 entries of a 64-entry tile against all 32 heads (the dequantised
+// words are the A operand of two 16x16x32 products, one per head group, so
+// each entry is converted once for 32 heads), store the fp16 values to the
+// value tile and write their softmax numerators P against their own maximum,
+// with that (max, sum) per head.  Waves 4-7 ("value waves") each own 128
+// latent channels of all 32 heads and run P . V on the previous tile with
+// 32x32x16 products (each value element read from LDS once per workgroup):
+// they merge the four (max, sum) pairs of a head, rescale the running output
+// and scale each score wave's P by exp2(its max - new max) as it enters the
+// product.  Tile t is scored while tile t - 1 is multiplied, from two value
+// buffers, so one barrier per tile separates the roles and the two kinds of
+// work of a SIMD (one wave of each role) overlap.
+template <int DR>
+__global__ __launch_bounds__(512) void sparse_attn_role_kernel(
+    const uint16_t* __restrict__ q, const CacheRef cache,
+    const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, float sm_scale_log2e, int n_hp,
+    int n_split, int per_split, int spread, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  constexpr int DC = 512;
+  constexpr int KSL = DC / 32;           // latent k-steps of the scores
+  constexpr int KSR = DR / 32;           // RoPE k-steps
+  constexpr int LDK = DC + 16;           // fp16 pitch of the value tile
+  constexpr int PP = AT_TILE + 8;        // fp16 pitch of the P rows
+  using GR = GatherRegs<DC, DR>;
+  constexpr int NCW = GR::NCW, RW = GR::RW;
+  static_assert(4 * NCW == KSL && (DR == 0 || RW == KSR), "gather layout = MFMA k-steps");
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2][AT_TILE][LDK];
+  __shared__ __attribute__((aligned(16))) _Float16 sP[2][32][PP];
+  __shared__ __attribute__((aligned(16))) float sML[2][32][4][2];  // buffer, head, score wave: (max, sum)
+  __shared__ __attribute__((aligned(16))) float sHd[4][2][32];     // value wave: per-head broadcast
+  __shared__ int32_t sIdx[AT_IDS_PAD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  int64_t b;
+  int split;
+  if (spread) {
+    const int64_t unit = (int64_t)(slot / n_hp) * 8 + xcd;
+    if (unit >= (int64_t)B * n_split) return;
+    b = unit / n_split;
+    split = (int)(unit - b * n_split);
+  } else {
+    const int per_q = n_split * n_hp;
+    b = (int64_t)(slot / per_q) * 8 + xcd;
+    if (b >= B) return;
+    split = (slot % per_q) / n_hp;
+  }
+  const int hq0 = (slot % n_hp) * 32;  // heads hq0 .. hq0 + 31
+  const int e_begin = split * per_split;
+  const int e_end = min(K, e_begin + per_split);
+  const int32_t* idx_row = idx + b * K;
+  const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
+
+  // ---- entry ids (one per thread) and the 32 query rows to LDS; the rows go
+  // to the second value buffer, which is first written by tile 1
+  static_assert(AT_IDS == 512 && AT_IDS_PAD - AT_IDS <= 512, "id staging layout");
+  const int32_t id_t = idx_row[min(e_begin + tid, max(e_end - 1, 0))];
+  constexpr int QP = (DC + DR) / 8;
+  constexpr int QPITCH = DC + DR + 8;
+  constexpr int QN = (32 * QP + 511) / 512;
+  static_assert(32 * QPITCH * 2 <= (int)sizeof(sV[1]), "query staging fits the second buffer");
+  uint16_t* qs = reinterpret_cast<uint16_t*>(&sV[1][0][0]);
+  {
+    u32x4 qv[QN];
+#pragma unroll
+    for (int k = 0; k < QN; ++k) {
+      const int pc = tid + 512 * k, row = pc / QP, col = pc - row * QP;
+      const bool ok = pc < 32 * QP && hq0 + row < H;
+      qv[k] = ok ? *reinterpret_cast<const u32x4*>(q + (b * H + hq0 + row) * (DC + DR) + 8 * col)
+                 : u32x4{0u, 0u, 0u, 0u};
+    }
+    sIdx[tid] = e_begin + tid < e_end ? id_t : -1;
+    if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
+#pragma unroll
+    for (int k = 0; k < QN; ++k) {
+      const int pc = tid + 512 * k, row = pc / QP, col = pc - row * QP;
+      if (pc < 32 * QP) *reinterpret_cast<u32x4*>(qs + row * QPITCH + 8 * col) = qv[k];
+    }
+  }
+  __syncthreads();
+  // iterations: in iteration i the score waves handle tile i (buffer i % 2)
+  // and the value waves tile i - 1; an even count, one barrier each
+  const int n_iter = n_tiles > 0 ? (n_tiles + 2) & ~1 : 0;
+
+  if (wave < 4) {
+    // ================= score waves: entries 16 * wave + n of each tile
+    const int w = wave;
+    f16x8 Bq[2][KSL];
+    bf16x8 Br[2][KSR > 0 ? KSR : 1];
+    float fscale[2];
+    // wave-uniform sequence bases, per-lane 32-bit offsets
+    const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride;
+    const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride;
+    const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride;
+    const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
+    const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
+    auto gather = [&](GR& gr, int tile) {
+      __builtin_amdgcn_sched_barrier(0);
+      tile = min(tile, AT_IDS_PAD / AT_TILE - 1);  // past the last tile: the -1 padding
+      const uint32_t id = (uint32_t)sIdx[tile * AT_TILE + 16 * w + n];
+      gr.valid = id < ncap32;
+      const uint32_t r = gr.valid ? id : 0u;
+      const uint32_t oc = r * cs32 + 16 * g, os = r * ss32 + 2 * g, orp = r * rs32 + 32 * g;
+#pragma unroll
+      for (int i = 0; i < NCW; ++i) {
+        gr.cw[i] = *reinterpret_cast<const u32x4*>(seq_codes + (oc + 64 * i));
+        gr.sb[i] = *reinterpret_cast<const uint16_t*>(seq_scales + (os + 8 * i));
+      }
+      if constexpr (DR > 0) {
+#pragma unroll
+        for (int t = 0; t < RW; ++t)
+          gr.rw[t] = *reinterpret_cast<const u32x4*>(seq_rope + (orp + 16 * t));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto process = [&](GR& gr, int buf) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NCW; ++i) asm volatile("" : "+v"(gr.sb[i]));
+      _Float16 (*tk)[LDK] = sV[buf];
+      const int e = 16 * w + n;
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NCW; ++i) {
+        const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gr.valid ? (uint32_t)gr.sb[i] : 0u, 1.0f, false);
+        const f16x2 s_lo = {sc[0], sc[0]}, s_hi = {sc[1], sc[1]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t word = gr.cw[i][j];
+          const f16x2 sv = j < 2 ? s_lo : s_hi;
+          const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sv;
+          const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sv;
+          const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sv;
+          const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sv;
+          const f16x8 a = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          *reinterpret_cast<f16x8*>(&tk[e][tile_col(e, 4 * i + g, j)]) = a;
+          c0 = mfma16x16x32_f16(a, Bq[0][4 * i + j], c0);
+          c1 = mfma16x16x32_f16(a, Bq[1][4 * i + j], c1);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < KSR; ++t) {
+        const bf16x8 rv = __builtin_bit_cast(bf16x8, gr.rw[t]);
+        c0 = mfma16x16x32_bf16(rv, Br[0][t], c0);
+        c1 = mfma16x16x32_bf16(rv, Br[1][t], c1);
+      }
+      // c_k[i] = S^T[entry 16 w + 4 g + i][head hq0 + 16 k + n]
+      const uint64_t vb = __ballot(g == 0 && gr.valid);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const f32x4 c = k ? c1 : c0;
+        float s2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s2[i] = ((vb >> (4 * g + i)) & 1u) ? c[i] * fscale[k] : -INFINITY;
+        float mt = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+        mt = fmaxf(mt, xor16f(mt));
+        mt = fmaxf(mt, xor32f(mt));
+        const float mt_ref = mt == -INFINITY ? 0.f : mt;  // masked scores give exp2(-inf) = 0
+        float p[4], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(s2[i] - mt_ref);
+          ps += p[i];
+        }
+        ps += xor16f(ps);
+        ps += xor32f(ps);
+        if (g == 0) *reinterpret_cast<float2*>(&sML[buf][16 * k + n][w][0]) = float2{mt, ps};
+        *reinterpret_cast<f16x4*>(&sP[buf][16 * k + n][16 * w + 4 * g]) =
+            f16x4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      }
+    };
+
+    if (n_iter > 0) {
+      GR ga, gb;
+      gather(ga, 0);
+      // query heads hq0 + 16 k + n as B operands (k-step order of the gather)
+      {
+        u32x4 qraw[2][KSL + KSR];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint16_t* qrow = qs + (16 * k + n) * QPITCH;
+#pragma unroll
+          for (int t = 0; t < KSL + KSR; ++t) {
+            const int off = t < KSL ? 128 * (t >> 2) + 32 * g + 8 * (t & 3) : DC + 16 * g + 8 * (t - KSL);
+            qraw[k][t] = *reinterpret_cast<const u32x4*>(qrow + off);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          uint32_t mx = 0;
+#pragma unroll
+          for (int t = 0; t < KSL + KSR; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              mx = max(mx, max(qraw[k][t][j] & 0x7FFFu, (qraw[k][t][j] >> 16) & 0x7FFFu));
+          mx = max(mx, xor16(mx));
+          mx = max(mx, xor32(mx));
+          // 2^sh brings the largest |q| of the head into [2^14, 2^15), where fp16
+          // keeps every bit of a bf16 value; bf16 subnormals count as exponent -126
+          int ex = (int)((mx >> 7) & 0xFF) - 127;
+          if (ex < -126) ex = -126;
+          const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - ex));
+          const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
+          fscale[k] = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
+#pragma unroll
+          for (int t = 0; t < KSL; ++t) {
+            f16x8 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              o[2 * j] = (_Float16)(bf16_bits_to_f32(qraw[k][t][j] & 0xFFFFu) * up);
+              o[2 * j + 1] = (_Float16)(bf16_bits_to_f32(qraw[k][t][j] >> 16) * up);
+            }
+            Bq[k][t] = o;
+          }
+#pragma unroll
+          for (int t = 0; t < KSR; ++t) {
+            bf16x8 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              o[2 * j] = (__bf16)(bf16_bits_to_f32(qraw[k][KSL + t][j] & 0xFFFFu) * up);
+              o[2 * j + 1] = (__bf16)(bf16_bits_to_f32(qraw[k][KSL + t][j] >> 16) * up);
+            }
+            Br[k][t] = o;
+          }
+        }
+      }
+      gather(gb, 1);
+      // every gather is unconditional (past the last tile they load row 0
+      // again), so each process step waits for exactly the loads it needs
+      for (int i = 0; i < n_iter; i += 2) {
+        if (i < n_tiles) process(ga, 0);
+        gather(ga, i + 2);
+        __syncthreads();
+        if (i + 1 < n_tiles) process(gb, 1);
+        gather(gb, i + 3);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+
+  // ================= value waves: channels 128 r .. + 127 of all 32 heads
+  const int r = wave - 4;
+  const int hl = lane & 31, kh = lane >> 5;  // A-operand row (head) and k-half of this lane
+  float m_run = -INFINITY, l_run = 0.f;      // head hq0 + hl
+  f32x16 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[k][i] = 0.f;
+  // transposing reads: lane group G = lane / 16 supplies channels 16 (G % 2) +
+  // 0..15 of entries 8 (G / 2) + 0..7 of a 16-entry k-step; lane 4 tr_r + tr_c
+  // points at 4 channels of one entry row
+  const int G = lane >> 4, tr_r = (lane & 15) >> 2, tr_c = lane & 3;
+
+  auto pv = [&](int buf) {
+    _Float16 (*tk)[LDK] = sV[buf];
+    const f32x4 ml01 = *reinterpret_cast<const f32x4*>(&sML[buf][hl][0][0]);
+    const f32x4 ml23 = *reinterpret_cast<const f32x4*>(&sML[buf][hl][2][0]);
+    const float mw[4] = {ml01[0], ml01[2], ml23[0], ml23[2]};
+    const float sw[4] = {ml01[1], ml01[3], ml23[1], ml23[3]};
+    const float m_new = fmaxf(m_run, fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3])));
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // nothing valid yet: O = l = 0
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    float fw[4], l_tile = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      fw[u] = __builtin_amdgcn_exp2f(mw[u] - m_ref);
+      l_tile += fw[u] * sw[u];
+    }
+    l_run = l_run * alpha + l_tile;
+    m_run = m_new;
+    // alpha of the heads whose output rows this lane holds: 8 q + 4 kh + 0..3
+    if (kh == 0) sHd[r][0][hl] = alpha;
+    f32x4 al[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) al[qq] = *reinterpret_cast<const f32x4*>(&sHd[r][0][8 * qq + 4 * kh]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[k][i] *= al[i >> 2][i & 3];
+#pragma unroll
+    for (int u = 0; u < AT_TILE / 16; ++u) {
+      // k-step u = the 16 entries of score wave u, rescaled to the common maximum
+      const f16x8 a = *reinterpret_cast<const f16x8*>(&sP[buf][hl][16 * u + 8 * kh]) * (_Float16)fw[u];
+      const int r0 = 16 * u + 8 * (G >> 1) + tr_r, r1 = r0 + 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ch = 32 * (4 * r + k) + 16 * (G & 1) + 4 * tr_c;
+        const f16x4 v0 = tr16_read(&tk[r0][tile_col(r0, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+        const f16x4 v1 = tr16_read(&tk[r1][tile_col(r1, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+        const f16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[k] = mfma32x32x16_f16(a, bv, acc[k]);
+      }
+    }
+  };
+
+  for (int i = 0; i < n_iter; i += 2) {
+    if (i >= 1 && i - 1 < n_tiles) pv(1);
+    __syncthreads();
+    if (i < n_tiles) pv(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue: element i of acc[k] is head 8 (i / 4) + 4 kh + i % 4,
+  // channel 32 (4 r + k) + hl
+  if (kh == 0) {
+    sHd[r][0][hl] = m_run;
+    sHd[r][1][hl] = l_run;
+  }
+  f32x4 lv[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) lv[qq] = *reinterpret_cast<const f32x4*>(&sHd[r][1][8 * qq + 4 * kh]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int hh = 8 * (i >> 2) + 4 * kh + (i & 3);
+    const int h = hq0 + hh;
+    if (h >= H) continue;
+    const float l = lv[i >> 2][i & 3];
+    if (n_split == 1) {
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      float* orow = out + (b * H + h) * DC + 128 * r + hl;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) orow[32 * k] = acc[k][i] * inv;
+    } else {
+      float* orow = ws_o + ((b * H + h) * n_split + split) * DC + 128 * r + hl;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) orow[32 * k] = acc[k][i];
+    }
+  }
+  if (r == 0 && kh == 0 && hq0 + hl < H) {
+    const int64_t row = b * H + hq0 + hl;
+    if (n_split == 1) {
+      if (lse) lse[row] = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+    } else {
+      ws_ml[2 * (row * n_split + split)] = m_run;
+      ws_ml[2 * (row * n_split + split) + 1] = l_run;
+    }
+  }
+}
+
 // Merge the per-slice partial results of one (b, h) row by log-sum-exp; each
 // of the 128 threads owns 4 consecutive channels (d_c <= 512).  The slices are
 // taken 8 at a time with every load of a round issued together (one memory
@@ -852,8 +1198,12 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
   hipLaunchKernelGGL((KERNEL<DCV, DRV>), grid, dim3(THREADS), 0, stream, q, cache, idx, K, B, H, N_cap, sl, \
                      n_hg, s, ps, spread, out, lse, ws_o, ws_ml)
   if (hpw == 32) {
-    if (d_r == 64) CSA2_ATTN(sparse_attn_pair_kernel, 512, 512, 64);
-    else if (d_r == 0) CSA2_ATTN(sparse_attn_pair_kernel, 512, 512, 0);
+    if (d_r == 64)
+      hipLaunchKernelGGL((sparse_attn_role_kernel<64>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,
+                         sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml);
+    else if (d_r == 0)
+      hipLaunchKernelGGL((sparse_attn_role_kernel<0>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,
+                         sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml);
     else return hipErrorInvalidValue;
   } else if (d_c == 512 && d_r == 64) CSA2_ATTN(sparse_attn_kernel, 256, 512, 64);
   else if (d_c == 512 && d_r == 0) CSA2_ATTN(sparse_attn_kernel, 256, 512, 0);

@@ -143,11 +143,12 @@ def test_attention_every_e4m3_scale_byte(H, B):
     attn_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
 
 
-@pytest.mark.parametrize("H,dr,K", [(64, 64, 512), (64, 64, 200), (48, 64, 130), (64, 0, 512)])
+@pytest.mark.parametrize("H,dr,K", [(64, 64, 512), (64, 64, 200), (48, 64, 130), (64, 0, 512), (64, 64, 1000)])
 def test_attention_paired_head_groups(H, dr, K):
-    """Batches large enough for 32 heads per workgroup (one gather and one
-    dequantisation shared by two head groups): masked, out-of-range and
-    repeated ids, an empty row, ragged K and a partial head pair."""
+    """Batches large enough for 32 heads per workgroup (score waves that
+    dequantise each entry once for 32 heads, value waves on the previous
+    tile): masked, out-of-range and repeated ids, an empty row, ragged K, a
+    partial head pair, and K = 1000 (two slices merged by the combine)."""
     B = 260 if H == 48 else 130
     wl = W.WORKLOADS[3].scaled(H=H, d_r=dr)
     note(f"attn: paired B={B} H={H} d_r={dr} K={K}")
