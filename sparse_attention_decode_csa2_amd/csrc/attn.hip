@@ -370,6 +370,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       gather(gb, t + 3);
     }
     if (t < n_tiles) process(ga);
+    // the look-ahead loads past the last tile are never used: wait for them
+    // before the wave can end
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // ---- epilogue: lane (channel n of each d-block, k-group g) holds heads h0 + 4g + i
@@ -403,345 +406,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 }
 
-// Two head groups (32 heads) per workgroup of eight waves; wave w serves head
-// group w / 4 and plays the role of wave w % 4 above for it.  The two waves of
-// a role gather the same 16 entries: each fetches and dequantises half of the
-// code words (words 2k, 2k + 1 of its quarter entry for head group k), scores
-// them from its registers, stores them to the value tile and, after a
-// barrier, scores the other half from the tile.  So one gather and one
-// dequantisation serve 32 heads, and the L1 of the CU sees each code byte
-// once.  The value tile is double-buffered (tile t in buffer t % 2), which
-// leaves two barriers per tile: tile t + 1 overwrites the buffer of tile t - 1
-// only after every wave has passed tile t's first barrier, i.e. finished the
-// value products of tile t - 1.  The softmax of each wave runs against its
-// own maximum; one exchange of (max, sum) per tile rescales the running state
-// and each wave's P as it enters the value products.
-template <int DC, int DR>
-struct PairGatherRegs {
-  static constexpr int NHW = DC / 256;               // 16-byte code words per lane: half of a quarter entry
-  static constexpr int RW = DR > 0 ? DR / 32 : 1;    // 16-byte RoPE words per lane
-  u32x4 cw[NHW];
-  uint16_t sb[NHW];  // the two scale bytes of each code word
-  u32x4 rw[RW];
-  bool valid;        // the lane's entry is selected and inside the cache
-};
-
-template <int DC, int DR>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_pair_kernel(
-    const uint16_t* __restrict__ q, const CacheRef cache,
-    const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, float sm_scale_log2e, int n_hp,
-    int n_split, int per_split, int spread, float* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  constexpr int KSL = DC / 32;           // latent k-steps
-  constexpr int KSR = DR / 32;           // RoPE k-steps
-  constexpr int LDK = DC + 16;           // fp16 pitch of the latent tile (8 mod 32 dwords)
-  constexpr int QCH = DC / 4;            // latent channels per PV wave
-  constexpr int NDB = QCH / 16;          // PV d-blocks per wave
-  using GR = PairGatherRegs<DC, DR>;
-  constexpr int NHW = GR::NHW, RW = GR::RW;
-  static_assert(8 * NHW == KSL && (DR == 0 || RW == KSR), "gather layout = MFMA k-steps");
-  __shared__ __attribute__((aligned(16))) _Float16 sK[2][AT_TILE][LDK];
-  __shared__ __attribute__((aligned(16))) _Float16 sP[2][16][AT_TILE + 8];
-  __shared__ __attribute__((aligned(16))) float sML[2][16][4][2];  // head group, head, role: (max, sum)
-  __shared__ float sFinM[2][16], sFinL[2][16];
-  __shared__ int32_t sIdx[AT_IDS_PAD];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int hgl = wave >> 2, rl = wave & 3;  // head group within the pair, role
-  // XCD placement as in the 16-head kernel (head pairs for head groups)
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  int64_t b;
-  int split;
-  if (spread) {
-    const int64_t unit = (int64_t)(slot / n_hp) * 8 + xcd;
-    if (unit >= (int64_t)B * n_split) return;
-    b = unit / n_split;
-    split = (int)(unit - b * n_split);
-  } else {
-    const int per_q = n_split * n_hp;
-    b = (int64_t)(slot / per_q) * 8 + xcd;
-    if (b >= B) return;
-    split = (slot % per_q) / n_hp;
-  }
-  const int h0 = (slot % n_hp) * 32 + 16 * hgl;  // this wave's heads: h0 + 0 .. 15
-  const int e_begin = split * per_split;
-  const int e_end = min(K, e_begin + per_split);
-  const int32_t* idx_row = idx + b * K;
-  const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
-  // own code words 2*hgl + k, the partner's 2*(1 - hgl) + k
-  const int own_w = 2 * hgl, oth_w = 2 - 2 * hgl;
-
-  // ---- entry ids to LDS (one per thread), loads in the order their data is needed
-  static_assert(AT_IDS == 512 && AT_IDS_PAD - AT_IDS <= 512, "id staging layout");
-  const int32_t id_t = idx_row[min(e_begin + tid, max(e_end - 1, 0))];
-  // ---- the 32 query rows, each fetched once (the four waves of a head group
-  // all need all of its 16 rows): 16-byte pieces to LDS, in the second value
-  // buffer, which is free until the second tile
-  constexpr int QP = (DC + DR) / 8;          // 16-byte pieces per query row
-  constexpr int QPITCH = DC + DR + 8;        // bf16 pitch of a staged row (rows 4 banks apart)
-  constexpr int QN = (32 * QP + 511) / 512;  // pieces per thread
-  static_assert(32 * QPITCH * 2 <= (int)sizeof(sK[1]), "query staging fits the second buffer");
-  uint16_t* qs = reinterpret_cast<uint16_t*>(&sK[1][0][0]);
-  const int hq0 = (slot % n_hp) * 32;
-  u32x4 qv[QN];
-#pragma unroll
-  for (int k = 0; k < QN; ++k) {
-    const int pc = tid + 512 * k, row = pc / QP, col = pc - row * QP;
-    const bool ok = pc < 32 * QP && hq0 + row < H;
-    qv[k] = ok ? *reinterpret_cast<const u32x4*>(q + (b * H + hq0 + row) * (DC + DR) + 8 * col)
-               : u32x4{0u, 0u, 0u, 0u};
-  }
-  sIdx[tid] = e_begin + tid < e_end ? id_t : -1;
-  if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
-#pragma unroll
-  for (int k = 0; k < QN; ++k) {
-    const int pc = tid + 512 * k, row = pc / QP, col = pc - row * QP;
-    if (pc < 32 * QP) *reinterpret_cast<u32x4*>(qs + row * QPITCH + 8 * col) = qv[k];
-  }
-  __syncthreads();
-  // ---- query heads h0 + n as MFMA B operands, ordered as this wave uses
-  // them: local k-step 4k + j for own word k, 8 + 4k + j for the partner's
-  f16x8 Bq[KSL];
-  bf16x8 Br[KSR > 0 ? KSR : 1];
-  float fscale;
-  const bool hv = h0 + n < H;
-  u32x4 qraw[KSL + KSR];
-  {
-    const uint16_t* qrow = qs + (16 * hgl + n) * QPITCH;
-#pragma unroll
-    for (int t = 0; t < KSL + KSR; ++t) {
-      int off;
-      if (t < KSL) {
-        const int word = (t < KSL / 2 ? own_w : oth_w) + ((t % (KSL / 2)) >> 2);
-        off = 128 * word + 32 * g + 8 * (t & 3);
-      } else {
-        off = DC + 16 * g + 8 * (t - KSL);
-      }
-      qraw[t] = *reinterpret_cast<const u32x4*>(qrow + off);
-    }
-  }
-
-  const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride + 16 * g;
-  const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride + 2 * g;
-  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride + 32 * g;
-  const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
-  const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
-  const int cw_off = 64 * own_w, sb_off = 8 * own_w;
-  auto gather = [&](GR& gr, int tile) {
-    __builtin_amdgcn_sched_barrier(0);
-    const uint32_t id = (uint32_t)sIdx[tile * AT_TILE + 16 * rl + n];
-    gr.valid = id < ncap32;
-    const uint32_t r = gr.valid ? id : 0u;
-#pragma unroll
-    for (int k = 0; k < NHW; ++k) {
-      gr.cw[k] = *reinterpret_cast<const u32x4*>(seq_codes + r * cs32 + cw_off + 64 * k);
-      gr.sb[k] = *reinterpret_cast<const uint16_t*>(seq_scales + r * ss32 + sb_off + 8 * k);
-    }
-    if constexpr (DR > 0) {
-#pragma unroll
-      for (int t = 0; t < RW; ++t)
-        gr.rw[t] = *reinterpret_cast<const u32x4*>(seq_rope + r * rs32 + 16 * t);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  float m_run = -INFINITY, l_run = 0.f;  // per head h0 + n
-  f32x4 acc[NDB];
-#pragma unroll
-  for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto process = [&](GR& gr, int buf) {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < NHW; ++k) asm volatile("" : "+v"(gr.sb[k]));
-    _Float16 (*tk)[LDK] = sK[buf];
-    const int e = 16 * rl + n;
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-    // ---- own half: dequantise, score from registers, store to the tile
-#pragma unroll
-    for (int k = 0; k < NHW; ++k) {
-      const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gr.valid ? (uint32_t)gr.sb[k] : 0u, 1.0f, false);
-      const f16x2 s_lo = {sc[0], sc[0]}, s_hi = {sc[1], sc[1]};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t word = gr.cw[k][j];
-        const f16x2 sv = j < 2 ? s_lo : s_hi;
-        const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sv;
-        const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sv;
-        const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sv;
-        const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sv;
-        const f16x8 a = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        *reinterpret_cast<f16x8*>(&tk[e][tile_col(e, 4 * (own_w + k) + g, j)]) = a;
-        c = mfma16x16x32_f16(a, Bq[4 * k + j], c);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < KSR; ++t) c = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, gr.rw[t]), Br[t], c);
-    const uint64_t vb = __ballot(g == 0 && gr.valid);
-    __syncthreads();  // both halves of the tile are in the buffer
-    // ---- the partner's half from the tile
-#pragma unroll
-    for (int k = 0; k < NHW; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(&tk[e][tile_col(e, 4 * (oth_w + k) + g, j)]);
-        c = mfma16x16x32_f16(a, Bq[KSL / 2 + 4 * k + j], c);
-      }
-    // c[i] = S^T[entry 16*rl + 4g + i][head h0 + n]
-    float s2[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s2[i] = ((vb >> (4 * g + i)) & 1u) ? c[i] * fscale : -INFINITY;
-    // ---- softmax of head h0 + n against this wave's maximum
-    float mt = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-    mt = fmaxf(mt, xor16f(mt));
-    mt = fmaxf(mt, xor32f(mt));
-    const float mt_ref = mt == -INFINITY ? 0.f : mt;  // masked scores give exp2(-inf) = 0
-    float p[4], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(s2[i] - mt_ref);
-      ps += p[i];
-    }
-    ps += xor16f(ps);
-    ps += xor32f(ps);
-    if (g == 0) {
-      sML[hgl][n][rl][0] = mt;
-      sML[hgl][n][rl][1] = ps;
-    }
-    *reinterpret_cast<f16x4*>(&sP[hgl][n][16 * rl + 4 * g]) =
-        f16x4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-    __syncthreads();
-    float fw[4];  // exp2(maximum of role w - new maximum) for head h0 + n
-    float alpha;
-    {
-      const f32x4 ml01 = *reinterpret_cast<const f32x4*>(&sML[hgl][n][0][0]);
-      const f32x4 ml23 = *reinterpret_cast<const f32x4*>(&sML[hgl][n][2][0]);
-      const float mw[4] = {ml01[0], ml01[2], ml23[0], ml23[2]};
-      const float sw[4] = {ml01[1], ml01[3], ml23[1], ml23[3]};
-      const float m_new = fmaxf(m_run, fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3])));
-      const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // all masked so far: O = l = 0
-      alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-      float l_tile = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        fw[w] = __builtin_amdgcn_exp2f(mw[w] - m_ref);
-        l_tile += fw[w] * sw[w];
-      }
-      l_run = l_run * alpha + l_tile;
-      m_run = m_new;
-    }
-    // ---- O[heads][channels of this role] = alpha * O + P . V
-    {
-      float al[4];  // the rows of acc are heads h0 + 4g + i: their alpha from lanes 4g + i
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        al[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * g + i), __float_as_int(alpha)));
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[d][i] *= al[i];
-      const int tr_r = n >> 2, tr_c = n & 3;
-#pragma unroll
-      for (int u = 0; u < AT_TILE / 32; ++u) {
-        // entries 32u + 8g .. + 7 were exponentiated by role 2u + g / 2
-        const _Float16 fu = (_Float16)((g >> 1) ? fw[2 * u + 1] : fw[2 * u]);
-        const f16x8 a = *reinterpret_cast<const f16x8*>(&sP[hgl][n][32 * u + 8 * g]) * fu;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          const int ch = 32 * pv_chunk<DC>(rl, d >> 1) + 16 * (d & 1) + 4 * tr_c;
-          const int r0 = 32 * u + 8 * g + tr_r, r1 = r0 + 4;
-          const f16x4 v0 = tr16_read(&tk[r0][tile_col(r0, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
-          const f16x4 v1 = tr16_read(&tk[r1][tile_col(r1, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
-          const f16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[d] = mfma16x16x32_f16(a, bv, acc[d]);
-        }
-      }
-    }
-  };
-
-  if (n_tiles > 0) {
-    GR ga, gb;
-    gather(ga, 0);
-    {
-      uint32_t mx = 0;
-#pragma unroll
-      for (int t = 0; t < KSL + KSR; ++t) {
-        if (!hv) qraw[t] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = max(mx, max(qraw[t][j] & 0x7FFFu, (qraw[t][j] >> 16) & 0x7FFFu));
-      }
-      mx = max(mx, xor16(mx));
-      mx = max(mx, xor32(mx));
-      int e = (int)((mx >> 7) & 0xFF) - 127;
-      if (e < -126) e = -126;
-      const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - e));
-      const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
-      fscale = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
-#pragma unroll
-      for (int t = 0; t < KSL; ++t) {
-        f16x8 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[2 * j] = (_Float16)(bf16_bits_to_f32(qraw[t][j] & 0xFFFFu) * up);
-          o[2 * j + 1] = (_Float16)(bf16_bits_to_f32(qraw[t][j] >> 16) * up);
-        }
-        Bq[t] = o;
-      }
-#pragma unroll
-      for (int t = 0; t < KSR; ++t) {
-        bf16x8 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[2 * j] = (__bf16)(bf16_bits_to_f32(qraw[KSL + t][j] & 0xFFFFu) * up);
-          o[2 * j + 1] = (__bf16)(bf16_bits_to_f32(qraw[KSL + t][j] >> 16) * up);
-        }
-        Br[t] = o;
-      }
-    }
-    gather(gb, 1);
-    int t = 0;
-    for (; t + 2 <= n_tiles; t += 2) {
-      process(ga, 0);
-      gather(ga, t + 2);
-      process(gb, 1);
-      gather(gb, t + 3);
-    }
-    if (t < n_tiles) process(ga, 0);
-  }
-
-  // ---- epilogue: lane (channel n of each d-block, k-group g) holds heads h0 + 4g + i
-  if (rl == 0 && g == 0) {
-    sFinM[hgl][n] = m_run;
-    sFinL[hgl][n] = l_run;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hl = 4 * g + i;
-    const int h = h0 + hl;
-    if (h >= H) continue;
-    const float m = sFinM[hgl][hl], l = sFinL[hgl][hl];
-    if (n_split == 1) {
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      float* orow = out + (b * H + h) * DC;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) orow[32 * pv_chunk<DC>(rl, d >> 1) + 16 * (d & 1) + n] = acc[d][i] * inv;
-      if (lse && rl == 0 && n == 0) lse[b * H + h] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
-    } else {
-      const int64_t slot_o = (b * H + h) * n_split + split;
-      float* orow = ws_o + slot_o * DC;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) orow[32 * pv_chunk<DC>(rl, d >> 1) + 16 * (d & 1) + n] = acc[d][i];
-      if (rl == 0 && n == 0) {
-        ws_ml[2 * slot_o] = m;
-        ws_ml[2 * slot_o + 1] = l;
-      }
-    }
-  }
-}
-
 // 32 heads per workgroup with the waves split by role, for batches that fill
 // the GPU unsplit.  Waves 0-3 ("score waves") each gather, dequantise and
 // score 16 entries of a 64-entry tile against all 32 heads (the dequantised
@@ -765,6 +429,7 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   constexpr int DC = 512;
   constexpr int KSL = DC / 32;           // latent k-steps of the scores
   constexpr int KSR = DR / 32;           // RoPE k-steps
+  constexpr int KS = KSL + KSR;
   constexpr int LDK = DC + 16;           // fp16 pitch of the value tile
   constexpr int PP = AT_TILE + 8;        // fp16 pitch of the P rows
   using GR = GatherRegs<DC, DR>;
@@ -774,6 +439,7 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   __shared__ __attribute__((aligned(16))) _Float16 sP[2][32][PP];
   __shared__ __attribute__((aligned(16))) float sML[2][32][4][2];  // buffer, head, score wave: (max, sum)
   __shared__ __attribute__((aligned(16))) float sHd[4][2][32];     // value wave: per-head broadcast
+  __shared__ float sFs[32];                                        // per head: MFMA result -> base-2 logit
   __shared__ int32_t sIdx[AT_IDS_PAD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -798,6 +464,12 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   const int e_end = min(K, e_begin + per_split);
   const int32_t* idx_row = idx + b * K;
   const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
+  // wave-uniform sequence bases; rows are addressed by 32-bit offsets from them
+  const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride;
+  const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride;
+  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride;
+  const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
+  const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
 
   // ---- entry ids (one per thread) and the 32 query rows to LDS; the rows go
   // to the second value buffer, which is first written by tile 1
@@ -807,6 +479,7 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   constexpr int QPITCH = DC + DR + 8;
   constexpr int QN = (32 * QP + 511) / 512;
   static_assert(32 * QPITCH * 2 <= (int)sizeof(sV[1]), "query staging fits the second buffer");
+  static_assert(2 * KS * 64 * 16 <= (int)sizeof(sV[1]), "converted query fits the second buffer");
   uint16_t* qs = reinterpret_cast<uint16_t*>(&sV[1][0][0]);
   {
     u32x4 qv[QN];
@@ -829,19 +502,14 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   // iterations: in iteration i the score waves handle tile i (buffer i % 2)
   // and the value waves tile i - 1; an even count, one barrier each
   const int n_iter = n_tiles > 0 ? (n_tiles + 2) & ~1 : 0;
+  // The value waves convert the query (below) into the score waves' B
+  // operands: 16-byte piece (k, t, lane) = head group k, k-step t of lane
+  // (n, g), in the second value buffer after the raw rows have been read.
+  const u32x4* qcv = reinterpret_cast<const u32x4*>(&sV[1][0][0]);
 
   if (wave < 4) {
     // ================= score waves: entries 16 * wave + n of each tile
     const int w = wave;
-    f16x8 Bq[2][KSL];
-    bf16x8 Br[2][KSR > 0 ? KSR : 1];
-    float fscale[2];
-    // wave-uniform sequence bases, per-lane 32-bit offsets
-    const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride;
-    const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride;
-    const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride;
-    const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
-    const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
     auto gather = [&](GR& gr, int tile) {
       __builtin_amdgcn_sched_barrier(0);
       tile = min(tile, AT_IDS_PAD / AT_TILE - 1);  // past the last tile: the -1 padding
@@ -862,6 +530,9 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
       __builtin_amdgcn_sched_barrier(0);
     };
 
+    f16x8 Bq[2][KSL];
+    bf16x8 Br[2][KSR > 0 ? KSR : 1];
+    float fscale[2];
     auto process = [&](GR& gr, int buf) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -919,61 +590,22 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
       }
     };
 
+    GR ga, gb;
     if (n_iter > 0) {
-      GR ga, gb;
       gather(ga, 0);
-      // query heads hq0 + 16 k + n as B operands (k-step order of the gather)
-      {
-        u32x4 qraw[2][KSL + KSR];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const uint16_t* qrow = qs + (16 * k + n) * QPITCH;
-#pragma unroll
-          for (int t = 0; t < KSL + KSR; ++t) {
-            const int off = t < KSL ? 128 * (t >> 2) + 32 * g + 8 * (t & 3) : DC + 16 * g + 8 * (t - KSL);
-            qraw[k][t] = *reinterpret_cast<const u32x4*>(qrow + off);
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          uint32_t mx = 0;
-#pragma unroll
-          for (int t = 0; t < KSL + KSR; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              mx = max(mx, max(qraw[k][t][j] & 0x7FFFu, (qraw[k][t][j] >> 16) & 0x7FFFu));
-          mx = max(mx, xor16(mx));
-          mx = max(mx, xor32(mx));
-          // 2^sh brings the largest |q| of the head into [2^14, 2^15), where fp16
-          // keeps every bit of a bf16 value; bf16 subnormals count as exponent -126
-          int ex = (int)((mx >> 7) & 0xFF) - 127;
-          if (ex < -126) ex = -126;
-          const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - ex));
-          const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
-          fscale[k] = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
-#pragma unroll
-          for (int t = 0; t < KSL; ++t) {
-            f16x8 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              o[2 * j] = (_Float16)(bf16_bits_to_f32(qraw[k][t][j] & 0xFFFFu) * up);
-              o[2 * j + 1] = (_Float16)(bf16_bits_to_f32(qraw[k][t][j] >> 16) * up);
-            }
-            Bq[k][t] = o;
-          }
-#pragma unroll
-          for (int t = 0; t < KSR; ++t) {
-            bf16x8 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              o[2 * j] = (__bf16)(bf16_bits_to_f32(qraw[k][KSL + t][j] & 0xFFFFu) * up);
-              o[2 * j + 1] = (__bf16)(bf16_bits_to_f32(qraw[k][KSL + t][j] >> 16) * up);
-            }
-            Br[k][t] = o;
-          }
-        }
-      }
       gather(gb, 1);
+    }
+    __syncthreads();  // the value waves have read the raw query rows
+    __syncthreads();  // ... and written the converted operands
+    if (n_iter > 0) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+#pragma unroll
+        for (int t = 0; t < KSL; ++t) Bq[k][t] = __builtin_bit_cast(f16x8, qcv[(k * KS + t) * 64 + lane]);
+#pragma unroll
+        for (int t = 0; t < KSR; ++t) Br[k][t] = __builtin_bit_cast(bf16x8, qcv[(k * KS + KSL + t) * 64 + lane]);
+        fscale[k] = sFs[16 * k + n];
+      }
       // every gather is unconditional (past the last tile they load row 0
       // again), so each process step waits for exactly the loads it needs
       for (int i = 0; i < n_iter; i += 2) {
@@ -984,12 +616,70 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
         gather(gb, i + 3);
         __syncthreads();
       }
+      // the two look-ahead gathers past the last tile are never used: the wave
+      // waits for them, so that no load returns into its registers after it
+      // has ended and they have been handed to another wave
+      __builtin_amdgcn_s_waitcnt(0);
     }
     return;
   }
 
   // ================= value waves: channels 128 r .. + 127 of all 32 heads
   const int r = wave - 4;
+  // ---- query conversion: lane (8 heads per wave, 8 lanes per head) handles
+  // pieces p = sub + 8 m of head hh, piece p = (k-step p / 4, k-group p % 4)
+  {
+    constexpr int NPC = KS * 4 / 8;
+    const int hh = 8 * r + (lane >> 3), sub = lane & 7;
+    u32x4 raw[NPC];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int m = 0; m < NPC; ++m) {
+      const int p = sub + 8 * m, t = p >> 2, gg = p & 3;
+      const int off = t < KSL ? 128 * (t >> 2) + 32 * gg + 8 * (t & 3) : DC + 16 * gg + 8 * (t - KSL);
+      raw[m] = *reinterpret_cast<const u32x4*>(qs + hh * QPITCH + off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = max(mx, max(raw[m][j] & 0x7FFFu, (raw[m][j] >> 16) & 0x7FFFu));
+    }
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4));
+    // 2^sh brings the largest |q| of the head into [2^14, 2^15), where fp16
+    // keeps every bit of a bf16 value; bf16 subnormals count as exponent -126
+    int ex = (int)((mx >> 7) & 0xFF) - 127;
+    if (ex < -126) ex = -126;
+    const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - ex));
+    const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
+    __syncthreads();  // every value wave has read its raw rows
+    u32x4* qc = reinterpret_cast<u32x4*>(&sV[1][0][0]);
+    const int k = hh >> 4, nn = hh & 15;
+#pragma unroll
+    for (int m = 0; m < NPC; ++m) {
+      const int p = sub + 8 * m, t = p >> 2, gg = p & 3;
+      u32x4 o;
+      if (t < KSL) {
+        f16x8 h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h[2 * j] = (_Float16)(bf16_bits_to_f32(raw[m][j] & 0xFFFFu) * up);
+          h[2 * j + 1] = (_Float16)(bf16_bits_to_f32(raw[m][j] >> 16) * up);
+        }
+        o = __builtin_bit_cast(u32x4, h);
+      } else {
+        bf16x8 h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h[2 * j] = (__bf16)(bf16_bits_to_f32(raw[m][j] & 0xFFFFu) * up);
+          h[2 * j + 1] = (__bf16)(bf16_bits_to_f32(raw[m][j] >> 16) * up);
+        }
+        o = __builtin_bit_cast(u32x4, h);
+      }
+      qc[(k * KS + t) * 64 + 16 * gg + nn] = o;
+    }
+    if (sub == 0) sFs[hh] = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
+    __syncthreads();  // the converted operands are in place
+  }
+
   const int hl = lane & 31, kh = lane >> 5;  // A-operand row (head) and k-half of this lane
   float m_run = -INFINITY, l_run = 0.f;      // head hq0 + hl
   f32x16 acc[4];
