@@ -44,6 +44,15 @@ namespace csa2 {
 constexpr int AT_TILE = 64;
 constexpr int AT_IDS = 512;  // entry ids one workgroup handles (8 tiles)
 constexpr int AT_IDS_PAD = AT_IDS + 2 * AT_TILE;  // + two tiles of -1 for the look-ahead loads
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D = A(32x16) * B(16x32) + C, fp32 accumulate.  Lane l supplies row (l % 32)
+// of A and column (l % 32) of B, each with the 8 k-elements 8 (l / 32) .. + 7;
+// element i of lane l is D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
