@@ -28,6 +28,8 @@ Parity status per function (the pins live in ``tests/test_oracle_*.py``):
 * quantize_fp4 / dequantize_fp4: pinned (hand-derived fixtures, invariants).
 * index_full / index_pool: pinned (int64 matmul, brute-force loops).
 * topk: pinned (brute-force sort, torch.topk / stable sort special cases).
+* build_pool: pinned (hand-derived fixture, brute-force selection, and Reindex
+  over the built pool reproducing the Full-mode Top-K).
 * sparse_attn: pinned (dense float64 SDPA when Top-K covers every entry,
   closed-form special cases, logsumexp).
 """
@@ -48,6 +50,7 @@ from .method import (  # noqa: F401
     index_full,
     index_pool,
     topk,
+    build_pool,
     sparse_attn,
     decode_full,
     decode_reindex,

@@ -14,6 +14,8 @@ reading taken is stated at the function and listed in the design doc):
        chosen by an earlier Full layer [P1 Hierarchical Sparse Indexer; P4].
 4. a3  ``topk``          - Top-512 selection [P1 CSA2], ties resolved so
        that the lower entry position wins.
+   ``build_pool``    - the block-level candidate pool an earlier Full layer
+       hands to the Reindex layers [P1 Hierarchical Sparse Indexer].
 5. a4/a5 ``sparse_attn`` - gather of the selected FP4 entries, exact
        dequantisation, and softmax attention of every query head over them
        (MLA-style: one latent shared by all heads; the key is [latent ; RoPE
@@ -175,6 +177,39 @@ def topk(scores, ids, n_valid, K):
         out_i[b, :take.size] = i[take]
         out_s[b, :take.size] = s[take]
     return out_i, out_s
+
+
+# ------------------------------------------------------------ pool construction
+
+
+def build_pool(scores, n_valid, block, P_max):
+    """Block-level candidate pool built from a Full layer's indexer scores, for
+    the Reindex layers after it [P1 Hierarchical Sparse Indexer; P4 CSA2
+    paragraph].
+
+    The pages say only that the decoder's first Full layer builds a pool of at
+    most 2048 blocks x 8 positions and that later layers score inside it.
+    Reading taken: block beta covers positions [block*beta, block*beta + block);
+    it is a candidate when its first position is valid (< n_valid[b]); its
+    score is the largest score among its valid positions (NaN ignored unless
+    every one is NaN); the pool is the first min(P_max, #candidates) blocks in
+    the Top-K order applied to blocks (block score descending, block id
+    ascending), padded with -1.
+    scores float [B, M]; n_valid int [B] or None (= M).
+    Returns (pool_blocks int32 [B, P_max], n_blocks int32 [B]).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    B, M = scores.shape
+    n_cand_max = (M + block - 1) // block
+    block_scores = np.full((B, max(n_cand_max, 1)), -np.inf)
+    n_cand = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        nv = M if n_valid is None else int(min(max(int(n_valid[b]), 0), M))
+        n_cand[b] = (nv + block - 1) // block
+        for beta in range(n_cand[b]):
+            block_scores[b, beta] = np.fmax.reduce(scores[b, block * beta:min(block * beta + block, nv)])
+    pool, _ = topk(block_scores, None, n_cand, P_max)
+    return pool, np.minimum(n_cand, P_max).astype(np.int32)
 
 
 # ------------------------------------------------------------ a4/a5 attention

@@ -398,6 +398,89 @@ def check_decode_modes_compose():
     assert set(idx2[0].tolist()) <= set(sum(([8 * b + j for j in range(8)] for b in [1, 3, 5, 7]), []))
 
 
+# ------------------------------------------------------------ pool construction
+
+POOL_SCORES = [1, 5, 2, 2, 3, 3, 3, 3, 5, 9]
+
+
+def check_pool_golden():
+    """Hand-derived pools (tests/golden/pool_blocks.txt)."""
+    sc = np.array([POOL_SCORES], dtype=np.float64)
+    for rec in _records("pool_blocks.txt"):
+        rec = [int(v) for v in rec]
+        nv, P_max, nb = rec[:3]
+        want = np.array(rec[3:3 + P_max], dtype=np.int32)
+        pool, n_blocks = oracle.build_pool(sc, np.array([nv]), 4, P_max)
+        assert np.array_equal(pool[0], want), (nv, P_max, pool[0], want)
+        assert int(n_blocks[0]) == nb
+
+
+def _pool_brute(scores, nv, block, P_max):
+    # block scores by explicit loops, then selection by repeated scans
+    cand = []
+    beta = 0
+    while block * beta < nv:
+        best = None
+        for p in range(block * beta, min(block * beta + block, nv)):
+            v = float(scores[p])
+            if v == v and (best is None or v > best):
+                best = v
+        cand.append((float("nan") if best is None else best, beta))
+        beta += 1
+    out = []
+    left = list(cand)
+    while left and len(out) < P_max:
+        pick = None
+        for c in left:
+            if pick is None:
+                pick = c
+                continue
+            a, b = c[0], pick[0]
+            if (a == a and (b != b or a > b)) or ((a == b or (a != a and b != b)) and c[1] < pick[1]):
+                pick = c
+        out.append(pick[1])
+        left.remove(pick)
+    return out + [-1] * (P_max - len(out)), min(len(cand), P_max)
+
+
+def check_pool_bruteforce():
+    """Random tiny score rows full of ties (and -inf, NaN), ragged n_valid."""
+    rng = np.random.default_rng(31)
+    for it in range(60):
+        B, M = 3, int(rng.integers(1, 41))
+        block = int(rng.integers(1, 6))
+        P_max = int(rng.integers(1, 9))
+        sc = rng.integers(0, 4, size=(B, M)).astype(np.float64)
+        sc[rng.random((B, M)) < 0.1] = -np.inf
+        sc[rng.random((B, M)) < 0.05] = np.nan
+        nv = rng.integers(0, M + 1, size=B)
+        pool, n_blocks = oracle.build_pool(sc, nv, block, P_max)
+        for b in range(B):
+            want, wnb = _pool_brute(sc[b], int(nv[b]), block, P_max)
+            assert pool[b].tolist() == want, (it, b, pool[b].tolist(), want)
+            assert int(n_blocks[b]) == wnb
+
+
+def check_pool_reindex_reproduces_full_topk():
+    """With P_max >= K, re-scoring the pool built from a layer's own Full
+    scores with the same indexer query selects exactly the Full-mode Top-K:
+    every top-K position lies in a block whose score is at least its own."""
+    rng = np.random.default_rng(32)
+    for it in range(12):
+        B, N, H_I, D_I, K, block = 2, 128, 2, 4, 8, 8
+        P_max = int(rng.integers(K, 12))
+        qi = codec.f64_to_bf16_bits_exact(rng.integers(-2, 3, size=(B, H_I, D_I)).astype(float))
+        ki = codec.f64_to_bf16_bits_exact(rng.integers(-2, 3, size=(B, N, D_I)).astype(float))
+        nv = np.array([N, int(rng.integers(1, N))])
+        full = oracle.index_full(qi, None, ki, nv)
+        want_i, want_s = oracle.topk(full, None, nv, K)
+        pool, n_blocks = oracle.build_pool(full, nv, block, P_max)
+        sc, pos = oracle.index_pool(qi, None, ki, nv, pool, n_blocks, block)
+        got_i, got_s = oracle.topk(sc, pos, None, K)
+        assert np.array_equal(got_i, want_i), (it, got_i, want_i)
+        assert np.array_equal(got_s, want_s)
+
+
 ALL_PINS = [
     check_e2m1_value_set, check_e4m3_decode, check_e4m3_encode_vs_torch, check_scale_code_vs_torch,
     check_e2m1_encode_vs_numpy_round, check_bf16_decode, check_quantize_golden,
@@ -405,4 +488,5 @@ ALL_PINS = [
     check_index_bruteforce, check_index_full_vs_int64_matmul, check_index_pool_bruteforce,
     check_topk_bruteforce, check_topk_vs_torch_topk_distinct, check_topk_ties_vs_stable_sort,
     check_topk_invariants, check_attn_dense_vs_sdpa, check_attn_special_cases, check_decode_modes_compose,
+    check_pool_golden, check_pool_bruteforce, check_pool_reindex_reproduces_full_topk,
 ]

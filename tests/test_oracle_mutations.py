@@ -20,6 +20,7 @@ _orig_topk = method.topk
 _orig_attn = method.sparse_attn
 _orig_pool = method.index_pool
 _orig_scores = method.index_scores
+_orig_build_pool = method.build_pool
 
 
 def _swap_nibbles(x_bits):
@@ -86,6 +87,38 @@ def _pool_transposed(q_bits, w, k_bits, n_valid, pool_blocks, n_blocks, block):
     return sc, np.where(pos >= 0, pos // block + (pos % block) * block, pos).astype(np.int32)
 
 
+def _pool_block_sum(scores, n_valid, block, P_max):
+    # plant: a block scored by the sum of its positions instead of the largest
+    sc = np.asarray(scores, dtype=np.float64)
+    B, M = sc.shape
+    nb = (M + block - 1) // block
+    summed = np.full((B, M), -np.inf)
+    for b in range(B):
+        nv = M if n_valid is None else int(min(max(int(n_valid[b]), 0), M))
+        for beta in range((nv + block - 1) // block):
+            summed[b, block * beta] = np.nansum(sc[b, block * beta:min(block * beta + block, nv)])
+    del nb
+    return _orig_build_pool(summed, n_valid, block, P_max)
+
+
+def _pool_high_id_first(scores, n_valid, block, P_max):
+    # plant: among blocks of equal score the higher block id wins
+    sc = np.asarray(scores, dtype=np.float64)
+    B, M = sc.shape
+    nbk = (M + block - 1) // block
+    pool = np.full((B, P_max), -1, dtype=np.int32)
+    n_blocks = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        nv = M if n_valid is None else int(min(max(int(n_valid[b]), 0), M))
+        nc = (nv + block - 1) // block
+        bs = np.array([np.fmax.reduce(sc[b, block * t:min(block * t + block, nv)]) for t in range(nc)])
+        order = np.lexsort((-np.arange(nc), -bs))[:P_max]
+        pool[b, :order.size] = order
+        n_blocks[b] = min(nc, P_max)
+    del nbk
+    return pool, n_blocks
+
+
 MUTATIONS = {
     "nibble_order_swapped": [(method, "quantize_fp4", _swap_nibbles), (oracle, "quantize_fp4", _swap_nibbles)],
     "e2m1_ties_away": [(method, "e2m1_encode_magnitude", _ties_away), (oracle, "e2m1_encode_magnitude", _ties_away)],
@@ -97,6 +130,9 @@ MUTATIONS = {
     "attention_drops_rope": [(method, "sparse_attn", _attn_no_rope), (oracle, "sparse_attn", _attn_no_rope)],
     "attention_lse_base2": [(method, "sparse_attn", _attn_lse_log2), (oracle, "sparse_attn", _attn_lse_log2)],
     "pool_position_transposed": [(method, "index_pool", _pool_transposed), (oracle, "index_pool", _pool_transposed)],
+    "pool_block_sum": [(method, "build_pool", _pool_block_sum), (oracle, "build_pool", _pool_block_sum)],
+    "pool_higher_block_id_wins": [(method, "build_pool", _pool_high_id_first),
+                                  (oracle, "build_pool", _pool_high_id_first)],
 }
 
 
