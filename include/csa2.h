@@ -175,6 +175,35 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
               void* workspace, size_t workspace_bytes, csa2_stream_t stream);
 
 /*
+ * Candidate-pool construction for Reindex mode: the block-level pool that the
+ * decoder's first Full layer keeps (at most 2048 blocks x 8 positions) so that
+ * later layers score only inside it ([P1] 架构三件套, Hierarchical Sparse
+ * Indexer; [P4] CSA2 paragraph).  The pages give no block score; this build
+ * reads it as the largest score of the block's valid positions.
+ *
+ * scores      f32 [B, M]  a Full layer's indexer scores (csa2_index_full)
+ * n_valid     i32 [B]     positions p < n_valid[b] are valid (NULL = M;
+ *                         clamped to [0, M] on the device)
+ * block       positions per block (block b covers [block*b, block*b + block));
+ *             a block is a candidate when its first position is valid
+ * pool_blocks i32 [B, P_max]  out: the first min(P_max, #candidates) block ids
+ *             by (block score descending, block id ascending), then -1; block
+ *             score = max of the valid positions' scores (NaN ignored unless
+ *             all are NaN).  Ready for csa2_index_pool (whose result does not
+ *             depend on the order of the pool).
+ * n_blocks    i32 [B]     out: min(P_max, #candidates)
+ * Bit-exact (comparisons only).  Requires 1 <= block <= 64,
+ * 1 <= P_max <= 2048, 1 <= M < 2^31, B >= 0, 16-byte aligned scores,
+ * pool_blocks, n_blocks (and n_valid when given), and a caller workspace of at
+ * least csa2_build_pool_workspace_bytes(B, M, block, P_max) bytes, 16-byte
+ * aligned (block scores, candidate counts, Top-K chunk winners).
+ */
+size_t csa2_build_pool_workspace_bytes(int32_t B, int64_t M, int32_t block, int32_t P_max);
+int csa2_build_pool(const float* scores, const int32_t* n_valid, int32_t B, int64_t M,
+                    int32_t block, int32_t P_max, int32_t* pool_blocks, int32_t* n_blocks,
+                    void* workspace, size_t workspace_bytes, csa2_stream_t stream);
+
+/*
  * a4 + a5. Gather, FP4 dequantisation and softmax attention over the
  * selected entries (also the whole of Reuse mode, where idx is handed in).
  * Defined by [P1] 架构三件套, CSA2 (Reuse reuses KV and the index and runs

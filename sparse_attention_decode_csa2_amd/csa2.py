@@ -46,6 +46,8 @@ def load():
         "csa2_index_pool": (ctypes.c_int, [P, P, P, P, P, P, I32, I32, I32, I64, I32, I32, P, P, P]),
         "csa2_topk_workspace_bytes": (SZ, [I32, I64, I32]),
         "csa2_topk": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P, SZ, P]),
+        "csa2_build_pool_workspace_bytes": (SZ, [I32, I64, I32, I32]),
+        "csa2_build_pool": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "csa2_sparse_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I64,
                                                 F, P, P, P, SZ, P]),
@@ -211,6 +213,31 @@ def csa2_topk(scores, K, ids=None, n_valid=None, out_idx=None, out_score=None, w
 
 
 # ------------------------------------------------------------------ a4 / a5
+
+
+def csa2_build_pool_workspace_bytes(B, M, block, P_max):
+    return int(load().csa2_build_pool_workspace_bytes(B, M, block, P_max))
+
+
+def csa2_build_pool(scores, P_max, block=8, n_valid=None, pool_blocks=None, n_blocks=None, workspace=None):
+    """Block-level candidate pool from a Full layer's scores f32 [B, M]:
+    returns (pool_blocks i32 [B, P_max], n_blocks i32 [B])."""
+    lib = load()
+    B, M = scores.shape
+    dev = scores.device
+    _need(scores, torch.float32, "scores")
+    if pool_blocks is None:
+        pool_blocks = torch.empty(B, P_max, dtype=torch.int32, device=dev)
+    if n_blocks is None:
+        n_blocks = torch.empty(B, dtype=torch.int32, device=dev)
+    need = csa2_build_pool_workspace_bytes(B, M, block, P_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.csa2_build_pool(_ptr(scores), _ptr(n_valid), B, M, block, P_max, _ptr(pool_blocks),
+                             _ptr(n_blocks), _ptr(workspace), ws_bytes, _stream())
+    _check("csa2_build_pool", st)
+    return pool_blocks, n_blocks
 
 
 def csa2_sparse_attn_workspace_bytes(B, H, d_c, K):

@@ -104,6 +104,26 @@ int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
                                        as_stream(stream)));
 }
 
+size_t csa2_build_pool_workspace_bytes(int32_t B, int64_t M, int32_t block, int32_t P_max) {
+  if (B <= 0 || M < 1 || M > INT32_MAX || block < 1 || block > 64 || P_max < 1 || P_max > 2048) return 0;
+  return csa2::pool_workspace_bytes(B, M, block, P_max);
+}
+
+int csa2_build_pool(const float* scores, const int32_t* n_valid, int32_t B, int64_t M, int32_t block,
+                    int32_t P_max, int32_t* pool_blocks, int32_t* n_blocks, void* workspace,
+                    size_t workspace_bytes, csa2_stream_t stream) {
+  if (B < 0 || M < 1 || M > INT32_MAX) return CSA2_ERR_SHAPE;
+  if (block < 1 || block > 64 || P_max < 1 || P_max > 2048) return CSA2_ERR_RANGE;
+  if (B == 0) return CSA2_OK;
+  if (!scores || !pool_blocks || !n_blocks || !workspace) return CSA2_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(pool_blocks) || !aligned16(n_blocks) || !opt_aligned16(n_valid) ||
+      !aligned16(workspace))
+    return CSA2_ERR_ALIGN;
+  if (workspace_bytes < csa2::pool_workspace_bytes(B, M, block, P_max)) return CSA2_ERR_WORKSPACE;
+  return hip_status(csa2::launch_build_pool(scores, n_valid, B, M, block, P_max, pool_blocks, n_blocks,
+                                            workspace, as_stream(stream)));
+}
+
 size_t csa2_topk_workspace_bytes(int32_t B, int64_t M, int32_t K) {
   if (B <= 0 || M < 1 || K < 1 || K > 2048) return 0;
   return csa2::topk_workspace_bytes(B, M, K);

@@ -31,6 +31,11 @@ hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n
                        int64_t M, int K, int32_t* out_idx, float* out_score, void* workspace,
                        hipStream_t stream);
 
+size_t pool_workspace_bytes(int B, int64_t M, int block, int P_max);
+hipError_t launch_build_pool(const float* scores, const int32_t* n_valid, int B, int64_t M, int block,
+                             int P_max, int32_t* pool_blocks, int32_t* n_blocks, void* workspace,
+                             hipStream_t stream);
+
 size_t attn_workspace_bytes(int B, int H, int d_c, int K);
 hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
                               int d_c, int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,

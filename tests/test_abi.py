@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
 
@@ -89,6 +89,26 @@ def test_topk_validation(lib):
     assert lib.csa2_topk_workspace_bytes(2, 16384, 512) == 0
     assert f(A, N, N, 2, 40000, 512, A, N, N, 0, N) == WS
     assert f(A, N, N, 2, 40000, 512, A, N, A, need - 1, N) == WS
+
+
+def test_build_pool_validation(lib):
+    f = lib.csa2_build_pool
+    need = lib.csa2_build_pool_workspace_bytes(2, 262144, 8, 2048)
+    # block scores (2 x 32768 f32) + counts (16 B) + two-level Top-K winners (2 x 2 x 2048 u64)
+    assert need == 2 * 32768 * 4 + 16 + 2 * 2 * 2048 * 8
+    assert lib.csa2_build_pool_workspace_bytes(2, 262144, 0, 2048) == 0
+    assert f(A, N, 2, 262144, 0, 2048, A, A, A, need, N) == RANGE
+    assert f(A, N, 2, 262144, 65, 2048, A, A, A, need, N) == RANGE
+    assert f(A, N, 2, 262144, 8, 2049, A, A, A, need, N) == RANGE
+    assert f(A, N, 2, 0, 8, 2048, A, A, A, need, N) == SHAPE
+    assert f(A, N, -1, 262144, 8, 2048, A, A, A, need, N) == SHAPE
+    assert f(A, N, 0, 262144, 8, 2048, A, A, A, need, N) == OK
+    assert f(N, N, 2, 262144, 8, 2048, A, A, A, need, N) == NULL
+    assert f(A, N, 2, 262144, 8, 2048, N, A, A, need, N) == NULL
+    assert f(A, N, 2, 262144, 8, 2048, A, A, N, need, N) == NULL
+    assert f(U, N, 2, 262144, 8, 2048, A, A, A, need, N) == ALIGN
+    assert f(A, U, 2, 262144, 8, 2048, A, A, A, need, N) == ALIGN
+    assert f(A, N, 2, 262144, 8, 2048, A, A, A, need - 1, N) == WS
 
 
 def test_attn_validation(lib):
