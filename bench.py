@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="full-64k",
                     help="full-64k (default, the reported line); others for supplementary runs: "
-                         "tiny-full, reindex-1m, reuse-128k, prefill-full-1m")
+                         "tiny-full, reindex-1m, reuse-128k, prefill-full-1m, pool-build-1m")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -74,6 +74,7 @@ class Step:
     Reindex (reindex-1m): pool -> topk -> attn over one cache; sets = pools + queries.
     Reuse (reuse-128k): attn over one cache; sets = index lists + queries.
     Prefill + Full (prefill-full-1m): quantize (append 8192 rows) -> index -> topk -> attn.
+    Pool construction (pool-build-1m): index (Full scores) -> build (the Reindex pool).
     """
 
     def __init__(self, wl, dev, rotation_bytes=ROTATION_BYTES):
@@ -88,12 +89,13 @@ class Step:
             self.R = max(2, math.ceil(rotation_bytes / per_set))
             self.sets = [self._full_set(wl.scaled(seed=wl.seed * 1000 + r)) for r in range(self.R)]
         else:
-            self.cache = self._cache(wl)
-            if self.mode in ("reindex", "prefill_full"):
+            if self.mode != "pool_build":
+                self.cache = self._cache(wl)
+            if self.mode in ("reindex", "prefill_full", "pool_build"):
                 self.keys = torch.stack([W.index_keys(wl, b, dev) for b in range(B)])
             touched = {"reindex": B * (wl.n_blocks * wl.block * wl.D_I * 2 + wl.K * _entry_bytes(wl)),
                        "reuse": B * wl.K * _entry_bytes(wl),
-                       "prefill_full": B * N * wl.D_I * 2}[self.mode]
+                       "prefill_full": B * N * wl.D_I * 2, "pool_build": B * N * wl.D_I * 2}[self.mode]
             self.R = max(2, math.ceil(rotation_bytes / touched))
             self.sets = []
             for r in range(self.R):
@@ -103,7 +105,7 @@ class Step:
                 # random-permutation kernels in the profiled process)
                 if self.mode == "reindex":
                     st["pool"], st["nb"] = (t.to(dev) for t in W.pool_blocks(ws, "cpu"))
-                if self.mode in ("reindex", "prefill_full"):
+                if self.mode in ("reindex", "prefill_full", "pool_build"):
                     st["qi"] = W.index_query(ws, dev)
                 if self.mode == "reuse":
                     st["idx"] = W.reuse_index(ws, "cpu").to(dev)
@@ -111,7 +113,7 @@ class Step:
             if self.mode == "prefill_full":
                 self.chunk = W.prefill_chunk(wl, dev)
                 self.chunk_rope = W.prefill_rope(wl, dev)
-        M = {"full": N, "prefill_full": N, "reindex": wl.P_max * wl.block, "reuse": 0}[self.mode]
+        M = {"full": N, "prefill_full": N, "reindex": wl.P_max * wl.block, "reuse": 0, "pool_build": N}[self.mode]
         self.M = M
         self.scores = torch.empty(B, max(M, 1), dtype=torch.float32, device=dev)
         self.positions = torch.empty(B, max(M, 1), dtype=torch.int32, device=dev)
@@ -124,7 +126,13 @@ class Step:
         self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
         self.ws_attn = torch.empty(max(at, 16), dtype=torch.uint8, device=dev) if at else None
         self.stages = {"full": ["index", "topk", "attn"], "reindex": ["pool", "topk", "attn"],
-                       "reuse": ["attn"], "prefill_full": ["quantize", "index", "topk", "attn"]}[self.mode]
+                       "reuse": ["attn"], "prefill_full": ["quantize", "index", "topk", "attn"],
+                       "pool_build": ["index", "build"]}[self.mode]
+        if self.mode == "pool_build":
+            self.pool_out = torch.empty(B, wl.P_max, dtype=torch.int32, device=dev)
+            self.nb_out = torch.empty(B, dtype=torch.int32, device=dev)
+            pb = csa2.csa2_build_pool_workspace_bytes(B, N, wl.block, wl.P_max)
+            self.ws_build = torch.empty(max(pb, 16), dtype=torch.uint8, device=dev)
         if self.mode == "reuse":
             self.idx = None
 
@@ -169,6 +177,10 @@ class Step:
         self.csa2.csa2_index_pool(st["qi"], self.keys, st["pool"], st["nb"], block=self.wl.block,
                                   scores=self.scores, positions=self.positions)
 
+    def build(self, r):
+        self.csa2.csa2_build_pool(self.scores, self.wl.P_max, block=self.wl.block, pool_blocks=self.pool_out,
+                                  n_blocks=self.nb_out, workspace=self.ws_build)
+
     def topk(self, r):
         ids = self.positions if self.mode == "reindex" else None
         self.csa2.csa2_topk(self.scores, self.wl.K, ids=ids, out_idx=self.idx, out_score=self.top,
@@ -195,6 +207,11 @@ class Step:
         attn = B * (K * 4 + K * ent + H * wl.D * 2 + H * wl.d_c * 4 + H * 4)
         d = {"attn": attn}
         step = attn
+        if self.mode == "pool_build":
+            d["index"] = B * (N * wl.D_I * 2 + qi + N * 4)
+            d["build"] = B * (N * 4 + wl.P_max * 4 + 4)
+            d["step"] = B * (N * wl.D_I * 2 + qi + wl.P_max * 4 + 4)
+            return d
         if self.mode in ("full", "prefill_full"):
             d["index"] = B * (N * wl.D_I * 2 + qi + N * 4)
             d["topk"] = B * (N * 4 + K * 8)
@@ -316,7 +333,7 @@ def main():
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
     kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
-                   "quantize": "quantize.hip"}[dom]
+                   "quantize": "quantize.hip", "build": "pool.hip"}[dom]
     achieved = alg[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = committed_traffic(kernel_file, wl.name)
 

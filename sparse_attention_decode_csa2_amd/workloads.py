@@ -23,6 +23,9 @@ compressed entry per 4 tokens):
 4. prefill-full-1m  an 8192-row post-RoPE chunk (N(0,1), 1% of elements
                   x20) appended to sequence 0 at rows [253952, 262144), then
                   B=8 Full-mode decode over 262144 entries
+5. pool-build-1m  the shapes of reindex-1m, for the layer before it: Full
+                  indexer scores over 262144 entries, then the pool of 2048
+                  blocks x 8 positions built from them (no attention)
 """
 
 from dataclasses import dataclass
@@ -35,7 +38,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    mode: str            # "full" | "reindex" | "reuse" | "prefill_full"
+    mode: str            # "full" | "reindex" | "reuse" | "prefill_full" | "pool_build"
     B: int               # decode queries (sequences) per step
     N: int               # compressed entries per sequence (cache capacity)
     d_c: int             # FP4 latent channels
@@ -73,6 +76,8 @@ WORKLOADS = [
     Workload("reuse-128k", "reuse", B=128, N=32768, d_c=512, d_r=64, H=64, H_I=8, D_I=128, K=512, seed=3),
     Workload("prefill-full-1m", "prefill_full", B=8, N=262144, d_c=512, d_r=64, H=64, H_I=8, D_I=128,
              K=512, seed=4, prefill_rows=8192, prefill_row0=262144 - 8192),
+    Workload("pool-build-1m", "pool_build", B=32, N=262144, d_c=512, d_r=64, H=64, H_I=8, D_I=128, K=512,
+             seed=5),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
