@@ -480,40 +480,35 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
   const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
 
-  // ---- entry ids (one per thread) and the 32 query rows to LDS; the rows go
-  // to the second value buffer, which is first written by tile 1
+  // ---- entry ids to LDS (one per thread).  The value waves, idle until the
+  // first tile has been scored, fetch the 32 query rows meanwhile and convert
+  // them (below) into the score waves' B operands: lane (8 heads per wave, 8
+  // lanes per head) loads pieces p = sub + 8 m of head hh, piece p = (k-step
+  // p / 4, k-group p % 4) in the order the gather lays out the latent.
   static_assert(AT_IDS == 512 && AT_IDS_PAD - AT_IDS <= 512, "id staging layout");
-  const int32_t id_t = idx_row[min(e_begin + tid, max(e_end - 1, 0))];
-  constexpr int QP = (DC + DR) / 8;
-  constexpr int QPITCH = DC + DR + 8;
-  constexpr int QN = (32 * QP + 511) / 512;
-  static_assert(32 * QPITCH * 2 <= (int)sizeof(sV[1]), "query staging fits the second buffer");
   static_assert(2 * KS * 64 * 16 <= (int)sizeof(sV[1]), "converted query fits the second buffer");
-  uint16_t* qs = reinterpret_cast<uint16_t*>(&sV[1][0][0]);
-  {
-    u32x4 qv[QN];
+  const int32_t id_t = idx_row[min(e_begin + tid, max(e_end - 1, 0))];
+  constexpr int NPC = KS * 4 / 8;
+  const int hh = 8 * (wave & 3) + (lane >> 3), sub = lane & 7;
+  u32x4 raw[NPC];
+  if (wave >= 4) {
+    const bool hok = hq0 + hh < H;
+    const uint16_t* qrow = q + (b * H + (hok ? hq0 + hh : 0)) * (DC + DR);
 #pragma unroll
-    for (int k = 0; k < QN; ++k) {
-      const int pc = tid + 512 * k, row = pc / QP, col = pc - row * QP;
-      const bool ok = pc < 32 * QP && hq0 + row < H;
-      qv[k] = ok ? *reinterpret_cast<const u32x4*>(q + (b * H + hq0 + row) * (DC + DR) + 8 * col)
-                 : u32x4{0u, 0u, 0u, 0u};
-    }
-    sIdx[tid] = e_begin + tid < e_end ? id_t : -1;
-    if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
-#pragma unroll
-    for (int k = 0; k < QN; ++k) {
-      const int pc = tid + 512 * k, row = pc / QP, col = pc - row * QP;
-      if (pc < 32 * QP) *reinterpret_cast<u32x4*>(qs + row * QPITCH + 8 * col) = qv[k];
+    for (int m = 0; m < NPC; ++m) {
+      const int p = sub + 8 * m, t = p >> 2, gg = p & 3;
+      const int off = t < KSL ? 128 * (t >> 2) + 32 * gg + 8 * (t & 3) : DC + 16 * gg + 8 * (t - KSL);
+      raw[m] = hok ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  sIdx[tid] = e_begin + tid < e_end ? id_t : -1;
+  if (tid < AT_IDS_PAD - AT_IDS) sIdx[AT_IDS + tid] = -1;
   __syncthreads();
   // iterations: in iteration i the score waves handle tile i (buffer i % 2)
   // and the value waves tile i - 1; an even count, one barrier each
   const int n_iter = n_tiles > 0 ? (n_tiles + 2) & ~1 : 0;
-  // The value waves convert the query (below) into the score waves' B
-  // operands: 16-byte piece (k, t, lane) = head group k, k-step t of lane
-  // (n, g), in the second value buffer after the raw rows have been read.
+  // converted query: 16-byte piece (k, t, lane) = head group k, k-step t of
+  // score-wave lane (n, g), in the second value buffer (first written by tile 1)
   const u32x4* qcv = reinterpret_cast<const u32x4*>(&sV[1][0][0]);
 
   if (wave < 4) {
@@ -604,8 +599,7 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
       gather(ga, 0);
       gather(gb, 1);
     }
-    __syncthreads();  // the value waves have read the raw query rows
-    __syncthreads();  // ... and written the converted operands
+    __syncthreads();  // the value waves have written the converted query
     if (n_iter > 0) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -635,21 +629,13 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
 
   // ================= value waves: channels 128 r .. + 127 of all 32 heads
   const int r = wave - 4;
-  // ---- query conversion: lane (8 heads per wave, 8 lanes per head) handles
-  // pieces p = sub + 8 m of head hh, piece p = (k-step p / 4, k-group p % 4)
+  // ---- query conversion (the rows were fetched before the first barrier)
   {
-    constexpr int NPC = KS * 4 / 8;
-    const int hh = 8 * r + (lane >> 3), sub = lane & 7;
-    u32x4 raw[NPC];
     uint32_t mx = 0;
 #pragma unroll
-    for (int m = 0; m < NPC; ++m) {
-      const int p = sub + 8 * m, t = p >> 2, gg = p & 3;
-      const int off = t < KSL ? 128 * (t >> 2) + 32 * gg + 8 * (t & 3) : DC + 16 * gg + 8 * (t - KSL);
-      raw[m] = *reinterpret_cast<const u32x4*>(qs + hh * QPITCH + off);
+    for (int m = 0; m < NPC; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) mx = max(mx, max(raw[m][j] & 0x7FFFu, (raw[m][j] >> 16) & 0x7FFFu));
-    }
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4));
@@ -659,7 +645,6 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     if (ex < -126) ex = -126;
     const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - ex));
     const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
-    __syncthreads();  // every value wave has read its raw rows
     u32x4* qc = reinterpret_cast<u32x4*>(&sV[1][0][0]);
     const int k = hh >> 4, nn = hh & 15;
 #pragma unroll
