@@ -13,6 +13,8 @@ stream the kernels run on), against the 8 TB/s HBM peak.  `traffic` comes from
 the committed rocprofv3 FETCH_SIZE / WRITE_SIZE measurement of that kernel
 (profiles/), and is null when the kernel source changed since it was taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`torch_topk_us` times torch.topk on the same score rows (K launches in one
+graph), the reference the pages quote for their Top-K kernel's speed-up.
 `single_step_us_cold` is one step run on its own after a 512 MiB write has
 evicted the caches (median of five): the latency of an isolated decode step,
 beside `value`, the steady-state rate of back-to-back steps.
@@ -319,6 +321,14 @@ def main():
     for s in stages:
         g_stage[s].replay()          # untimed pass over the same launches
     stage_us = {s: 1000.0 * timed(g_stage[s]) / args.steps for s in stages}
+    # the same selection by torch.topk (speed reference only: its order among
+    # equal scores is unspecified), K launches on the stage's own score rows
+    torch_topk_us = None
+    if "topk" in stages:
+        g_tt = capture(lambda r: torch.topk(step.scores, wl.K, dim=1), args.steps)
+        g_tt.replay()
+        torch_topk_us = 1000.0 * timed(g_tt) / args.steps
+        del g_tt
     # one step on its own with cold caches (what an isolated decode step
     # waits for, beside the steady-state rate above): a 512 MiB write evicts
     # the L2s and the Infinity Cache before each run; median of five
@@ -367,6 +377,7 @@ def main():
         "step_alg_bytes": alg["step"],
         "stage_us": {s: round(v, 3) for s, v in stage_us.items()},
         "stage_gbs": {s: round(alg[s] / (stage_us[s] * 1e-6) / 1e9, 1) for s in stages},
+        "torch_topk_us": None if torch_topk_us is None else round(torch_topk_us, 3),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": alg[dom]},
