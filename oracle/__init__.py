@@ -28,6 +28,9 @@ Parity status per function (the pins live in ``tests/test_oracle_*.py``):
 * quantize_fp4 / dequantize_fp4: pinned (hand-derived fixtures, invariants).
 * index_full / index_pool: pinned (int64 matmul, brute-force loops).
 * topk: pinned (brute-force sort, torch.topk / stable sort special cases).
+* quantize_fp8 / swa_attn / merge_branches: pinned (hand-derived scales and
+  codes, torch's float8_e4m3fn cast, float64 SDPA over the window and over the
+  union of the selected entries and the window).
 * build_pool: pinned (hand-derived fixture, brute-force selection, and Reindex
   over the built pool reproducing the Full-mode Top-K).
 * sparse_attn: pinned (dense float64 SDPA when Top-K covers every entry,
@@ -52,6 +55,11 @@ from .method import (  # noqa: F401
     topk,
     build_pool,
     sparse_attn,
+    fp8_row_scale_exponent,
+    quantize_fp8,
+    dequantize_fp8,
+    swa_attn,
+    merge_branches,
     decode_full,
     decode_reindex,
     decode_reuse,

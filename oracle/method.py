@@ -27,6 +27,7 @@ import numpy as np
 
 from .codec import (
     bf16_bits_to_f64,
+    e4m3_encode,
     e2m1_decode,
     e2m1_encode_magnitude,
     e4m3_decode,
@@ -253,6 +254,111 @@ def sparse_attn(q_bits, codes, scales, rope_bits, idx, sm_scale):
         L = p.sum(axis=1, keepdims=True)
         out[b] = (p @ lat) / L
         lse[b] = m[:, 0] + np.log(L[:, 0])
+    return out, lse
+
+
+# ------------------------------------------------------------ sliding-window branch (FP8)
+
+E4M3_MAX = 448.0
+
+
+def fp8_row_scale_exponent(amax):
+    """Smallest integer e with amax <= 448 * 2^e (0 when amax = 0), clamped to
+    [-126, 127] so that 2^e is a normal fp32 number."""
+    amax = np.asarray(amax, dtype=np.float64)
+    e = np.zeros(amax.shape, dtype=np.int64)
+    for idx in np.ndindex(amax.shape):
+        a = float(amax[idx])
+        if a == 0.0:
+            continue
+        k = int(np.floor(np.log2(a))) - 9          # start below, then walk up
+        while E4M3_MAX * 2.0 ** k < a:
+            k += 1
+        while E4M3_MAX * 2.0 ** (k - 1) >= a:
+            k -= 1
+        e[idx] = min(max(k, -126), 127)
+    return e
+
+
+def quantize_fp8(x_bits):
+    """FP8 write of the sliding-window KV: the window branch keeps its KV in
+    FP8 [P4 CSA2 paragraph; P1 效率组件四件 #4].
+
+    The pages give no scale granularity.  Reading taken: one power-of-two
+    scale per token (row), sigma = 2^e with e the smallest integer such that
+    max|x| <= 448 * sigma (sigma = 1 for an all-zero row), so x / sigma is
+    exact and no element saturates; each element's code is the E4M3 value
+    nearest to |x| / sigma (ties to the even code), with the sign bit copied
+    from the input (-0 -> 0x80).
+    x_bits uint16 bf16 [R, C].  Returns (codes uint8 [R, C], sigma float64 [R]).
+    """
+    bits = np.asarray(x_bits, dtype=np.uint16)
+    x = bf16_bits_to_f64(bits)
+    e = fp8_row_scale_exponent(np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0]))
+    sigma = 2.0 ** e.astype(np.float64)
+    mag = e4m3_encode(np.abs(x) / sigma[:, None])
+    codes = (mag | (((bits >> 15) & 1).astype(np.uint8) << 7)).astype(np.uint8)
+    return codes, sigma
+
+
+def dequantize_fp8(codes, sigma):
+    """Exact dequantisation of the window rows: value(code) * sigma, float64."""
+    return e4m3_decode(codes) * np.asarray(sigma, dtype=np.float64)[..., None]
+
+
+def swa_attn(q_bits, codes, sigma, rope_bits, n_win, sm_scale):
+    """Softmax attention of every head over the sliding window (the last
+    tokens, uncompressed, one FP8 entry per token) [P4 CSA2 paragraph: SWA
+    branch beside the sparse one; P1 效率组件四件 #4].
+
+    Same MLA form as the main cache: key_j = [dequant(codes_j) ; rope_j],
+    value_j = dequant(codes_j).  Rows j < n_win[b] of the window are used (the
+    window's order does not matter).  q_bits uint16 [B, H, d_c + d_r]; codes
+    uint8 [B, W, d_c]; sigma [B, W]; rope_bits uint16 [B, W, d_r]; n_win int
+    [B] or None (= W).  Returns (out float64 [B, H, d_c], lse float64 [B, H]);
+    an empty window gives out = 0, lse = -inf.
+    """
+    q = bf16_bits_to_f64(q_bits)
+    B, H, D = q.shape
+    W, d_c = codes.shape[1], codes.shape[2]
+    out = np.zeros((B, H, d_c))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        nw = W if n_win is None else int(min(max(int(n_win[b]), 0), W))
+        if nw == 0:
+            continue
+        lat = dequantize_fp8(codes[b, :nw], sigma[b, :nw])
+        key = np.concatenate([lat, bf16_bits_to_f64(rope_bits[b, :nw])], axis=1) if D > d_c else lat
+        s = sm_scale * (q[b] @ key.T)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        L = p.sum(axis=1, keepdims=True)
+        out[b] = (p @ lat) / L
+        lse[b] = m[:, 0] + np.log(L[:, 0])
+    return out, lse
+
+
+def merge_branches(out_a, lse_a, out_b, lse_b):
+    """One softmax over the union of two disjoint key sets, from each set's
+    normalised output and natural-log sum-exp: the sparse branch and the
+    window branch of a layer attend as one [P4 CSA2 paragraph: the sparse
+    branch beside the SWA branch; reading: one softmax over the union, the
+    LSE the sparse attention exports for this].
+
+    out = (e^lse_a out_a + e^lse_b out_b) / (e^lse_a + e^lse_b),
+    lse = log(e^lse_a + e^lse_b); both empty -> out = 0, lse = -inf.
+    """
+    la = np.asarray(lse_a, dtype=np.float64)
+    lb = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(la, lb)
+    safe = np.where(np.isfinite(m), m, 0.0)
+    wa = np.exp(la - safe)
+    wb = np.exp(lb - safe)
+    tot = wa + wb
+    den = np.where(tot > 0, tot, 1.0)
+    out = (wa[..., None] * np.asarray(out_a, dtype=np.float64) +
+           wb[..., None] * np.asarray(out_b, dtype=np.float64)) / den[..., None]
+    lse = np.where(tot > 0, safe + np.log(den), -np.inf)
     return out, lse
 
 

@@ -481,6 +481,118 @@ def check_pool_reindex_reproduces_full_topk():
         assert np.array_equal(got_s, want_s)
 
 
+# ------------------------------------------------------------ sliding-window branch (FP8)
+
+
+def check_fp8_golden():
+    """Hand-derived FP8 rows (tests/golden/fp8_rows.txt)."""
+    for rec in _records("fp8_rows.txt"):
+        e = int(rec[0])
+        vals = [float(v.split(":")[0]) for v in rec[1:]]
+        want = [int(v.split(":")[1], 16) for v in rec[1:]]
+        bits = codec.f64_to_bf16_bits_exact(np.array([vals]))
+        if any(v.split(":")[0].startswith("-0") for v in rec[1:]):
+            for j, v in enumerate(rec[1:]):
+                if v.split(":")[0] == "-0":
+                    bits[0, j] = 0x8000
+        codes, sigma = oracle.quantize_fp8(bits)
+        assert codes[0].tolist() == want, (rec, [hex(c) for c in codes[0]])
+        assert sigma[0] == 2.0 ** e
+
+
+def _fp8_rows(rng, R=64, C=512):
+    x = rng.standard_normal((R, C))
+    x[rng.random((R, C)) < 0.01] *= 20.0
+    x[::7] *= 2.0 ** rng.integers(-40, 40, size=(len(x[::7]), 1))
+    x[3] = 0.0
+    return codec.f64_to_bf16_bits_exact(codec.bf16_bits_to_f64(
+        (np.frombuffer(x.astype(np.float32).tobytes(), dtype=np.uint32) >> 16).astype(np.uint16).reshape(R, C)))
+
+
+def check_fp8_vs_torch_cast():
+    """Codes = torch's float8_e4m3fn cast of x / sigma (RNE); sigma puts the
+    row's largest magnitude in (224, 448] (the top binade of E4M3), and the
+    round trip is within half an E4M3 step."""
+    rng = np.random.default_rng(41)
+    bits = _fp8_rows(rng)
+    x = codec.bf16_bits_to_f64(bits)
+    codes, sigma = oracle.quantize_fp8(bits)
+    amax = np.abs(x).max(axis=1)
+    nz = amax > 0
+    r = amax[nz] / sigma[nz]
+    assert np.all((r > 224.0) & (r <= 448.0)), r.min()
+    assert np.all(sigma[~nz] == 1.0)
+    y = torch.from_numpy(x / sigma[:, None]).to(torch.float8_e4m3fn)
+    tb = y.view(torch.uint8).numpy()
+    assert np.array_equal(codes, tb)
+    back = oracle.dequantize_fp8(codes, sigma)
+    step = sigma[:, None] * 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x) / sigma[:, None], 2.0 ** -6))) - 3)
+    assert np.all(np.abs(back - x) <= step / 2 + 1e-300)
+
+
+def _swa_inputs(B=2, H=8, W=24, d_c=64, d_r=32, seed=42):
+    rng = np.random.default_rng(seed)
+    qb = codec.f64_to_bf16_bits_exact(codec.bf16_bits_to_f64(
+        (np.frombuffer(rng.standard_normal((B, H, d_c + d_r)).astype(np.float32).tobytes(),
+                       dtype=np.uint32) >> 16).astype(np.uint16).reshape(B, H, d_c + d_r)))
+    codes = rng.integers(0, 256, size=(B, W, d_c)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10          # no NaN codes
+    sigma = 2.0 ** rng.integers(-8, -2, size=(B, W)).astype(np.float64)
+    rb = (np.frombuffer(rng.standard_normal((B, W, d_r)).astype(np.float32).tobytes(),
+                        dtype=np.uint32) >> 16).astype(np.uint16).reshape(B, W, d_r)
+    return qb, codes, sigma, rb
+
+
+def check_swa_vs_sdpa():
+    """Window attention = float64 SDPA over the dequantised window rows."""
+    qb, codes, sigma, rb = _swa_inputs()
+    sm = 0.1
+    nw = np.array([24, 17])
+    out, lse = oracle.swa_attn(qb, codes, sigma, rb, nw, sm)
+    q = torch.from_numpy(codec.bf16_bits_to_f64(qb))
+    for b in range(2):
+        lat = torch.from_numpy(codec.e4m3_decode(codes[b, :nw[b]]) * sigma[b, :nw[b], None])
+        key = torch.cat([lat, torch.from_numpy(codec.bf16_bits_to_f64(rb[b, :nw[b]]))], dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[b][None], key[None], lat[None], scale=sm)[0]
+        assert np.allclose(out[b], ref.numpy(), rtol=1e-12, atol=1e-12)
+        s = sm * (q[b] @ key.T)
+        assert np.allclose(lse[b], torch.logsumexp(s, dim=1).numpy(), rtol=1e-12, atol=1e-12)
+    o0, l0 = oracle.swa_attn(qb, codes, sigma, rb, np.array([0, 1]), sm)
+    assert np.all(o0[0] == 0) and np.all(np.isneginf(l0[0]))
+    lat1 = codec.e4m3_decode(codes[1, 0]) * sigma[1, 0]
+    assert np.array_equal(o0[1], np.tile(lat1, (qb.shape[1], 1)))
+
+
+def check_merge_is_one_softmax_over_the_union():
+    """The sparse branch (FP4 entries picked by idx) merged with the window
+    branch (FP8 rows) equals one float64 SDPA over the concatenation of both
+    key sets; an empty side leaves the other unchanged."""
+    qb, codes, scales, rb = _attn_inputs(B=2, H=8, N=40, d_c=64, d_r=32, seed=43)
+    _, c8, s8, r8 = _swa_inputs(B=2, H=8, W=24, d_c=64, d_r=32, seed=44)
+    sm = 0.1
+    idx = np.array([[3, 9, 11, 30, -1], [0, 1, 2, 3, 39]])
+    nw = np.array([24, 5])
+    o1, l1 = oracle.sparse_attn(qb, codes, scales, rb, idx, sm)
+    o2, l2 = oracle.swa_attn(qb, c8, s8, r8, nw, sm)
+    o, l = oracle.merge_branches(o1, l1, o2, l2)
+    q = torch.from_numpy(codec.bf16_bits_to_f64(qb))
+    for b in range(2):
+        sel = idx[b][idx[b] >= 0]
+        lat1 = oracle.dequantize_fp4(codes[b, sel], scales[b, sel])
+        lat2 = codec.e4m3_decode(c8[b, :nw[b]]) * s8[b, :nw[b], None]
+        lat = torch.from_numpy(np.concatenate([lat1, lat2]))
+        rope = np.concatenate([codec.bf16_bits_to_f64(rb[b, sel]), codec.bf16_bits_to_f64(r8[b, :nw[b]])])
+        key = torch.cat([lat, torch.from_numpy(rope)], dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[b][None], key[None], lat[None], scale=sm)[0]
+        assert np.allclose(o[b], ref.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(l[b], torch.logsumexp(sm * (q[b] @ key.T), dim=1).numpy(), rtol=1e-12, atol=1e-12)
+    e_o, e_l = np.zeros_like(o1), np.full_like(l1, -np.inf)
+    oa, la = oracle.merge_branches(o1, l1, e_o, e_l)
+    assert np.array_equal(oa, o1) and np.array_equal(la, l1)
+    oz, lz = oracle.merge_branches(e_o, e_l, e_o, e_l)
+    assert np.all(oz == 0) and np.all(np.isneginf(lz))
+
+
 ALL_PINS = [
     check_e2m1_value_set, check_e4m3_decode, check_e4m3_encode_vs_torch, check_scale_code_vs_torch,
     check_e2m1_encode_vs_numpy_round, check_bf16_decode, check_quantize_golden,
@@ -489,4 +601,5 @@ ALL_PINS = [
     check_topk_bruteforce, check_topk_vs_torch_topk_distinct, check_topk_ties_vs_stable_sort,
     check_topk_invariants, check_attn_dense_vs_sdpa, check_attn_special_cases, check_decode_modes_compose,
     check_pool_golden, check_pool_bruteforce, check_pool_reindex_reproduces_full_topk,
+    check_fp8_golden, check_fp8_vs_torch_cast, check_swa_vs_sdpa, check_merge_is_one_softmax_over_the_union,
 ]

@@ -21,6 +21,9 @@ _orig_attn = method.sparse_attn
 _orig_pool = method.index_pool
 _orig_scores = method.index_scores
 _orig_build_pool = method.build_pool
+_orig_fp8_exp = method.fp8_row_scale_exponent
+_orig_swa = method.swa_attn
+_orig_merge = method.merge_branches
 
 
 def _swap_nibbles(x_bits):
@@ -119,6 +122,21 @@ def _pool_high_id_first(scores, n_valid, block, P_max):
     return pool, n_blocks
 
 
+def _fp8_scale_one_lower(amax):
+    # plant: the row scale one binade too small (the largest elements saturate)
+    e = _orig_fp8_exp(amax)
+    return np.where(np.asarray(amax) > 0, e - 1, e)
+
+
+def _swa_no_rope(q_bits, codes, sigma, rope_bits, n_win, sm_scale):
+    return _orig_swa(q_bits, codes, sigma, np.zeros_like(rope_bits), n_win, sm_scale)
+
+
+def _merge_base2(out_a, lse_a, out_b, lse_b):
+    # plant: branch weights 2^lse instead of e^lse
+    return _orig_merge(out_a, np.asarray(lse_a) * np.log(2.0), out_b, np.asarray(lse_b) * np.log(2.0))
+
+
 MUTATIONS = {
     "nibble_order_swapped": [(method, "quantize_fp4", _swap_nibbles), (oracle, "quantize_fp4", _swap_nibbles)],
     "e2m1_ties_away": [(method, "e2m1_encode_magnitude", _ties_away), (oracle, "e2m1_encode_magnitude", _ties_away)],
@@ -133,6 +151,10 @@ MUTATIONS = {
     "pool_block_sum": [(method, "build_pool", _pool_block_sum), (oracle, "build_pool", _pool_block_sum)],
     "pool_higher_block_id_wins": [(method, "build_pool", _pool_high_id_first),
                                   (oracle, "build_pool", _pool_high_id_first)],
+    "fp8_scale_one_binade_low": [(method, "fp8_row_scale_exponent", _fp8_scale_one_lower),
+                                 (oracle, "fp8_row_scale_exponent", _fp8_scale_one_lower)],
+    "window_drops_rope": [(method, "swa_attn", _swa_no_rope), (oracle, "swa_attn", _swa_no_rope)],
+    "merge_weights_base2": [(method, "merge_branches", _merge_base2), (oracle, "merge_branches", _merge_base2)],
 }
 
 
