@@ -175,6 +175,63 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
               void* workspace, size_t workspace_bytes, csa2_stream_t stream);
 
 /*
+ * Sliding-window branch, write: FP8 rows of the window KV.  The window branch
+ * keeps its KV in FP8 ([P4] CSA2 paragraph; [P1] 效率组件四件, item 4); the
+ * pages give no scale granularity, this build uses one power-of-two scale per
+ * row: sigma = 2^e, e the smallest integer with max|x| <= 448 * 2^e (1 for an
+ * all-zero row, e clamped to [-126, 127]), codes = E4M3 (OCP E4M3FN) nearest
+ * to |x| / sigma, ties to the even code, sign bit copied (-0 -> 0x80).
+ *
+ * x        bf16 [n_rows, d_c] (rows of the latent)
+ * rope_src bf16 [n_rows, d_r] or NULL when d_r == 0 (copied unchanged)
+ * codes    u8  rows of codes_stride bytes (0 = d_c), 8-byte aligned, stride % 8 == 0
+ * sigma    f32 [capacity]  out: the row scales
+ * rope_dst bf16 rows of rope_stride bytes (0 = 2 d_r), 16-byte aligned
+ * Writes rows [dst_row0, dst_row0 + n_rows) of a window of `capacity` rows.
+ * Bit-exact.  Requires d_c % 8 == 0, 8 <= d_c <= 4096, d_r % 8 == 0,
+ * 0 <= d_r <= 512, 16-byte aligned x / rope_src, 4-byte aligned sigma.
+ */
+int csa2_quantize_fp8(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
+                      int32_t d_r, uint8_t* codes, int64_t codes_stride, float* sigma,
+                      uint16_t* rope_dst, int64_t rope_stride, int64_t dst_row0, int64_t capacity,
+                      csa2_stream_t stream);
+
+/*
+ * Sliding-window branch, attention, and its merge with the sparse branch.  A
+ * layer's sparse branch and its SWA branch ([P4] CSA2 paragraph) are read as
+ * one softmax over the union of their keys: the window rows attend like the
+ * selected entries (key = [dequant(latent) ; rope], value = dequant(latent),
+ * dequant = E4M3 value * sigma of the row), and the two results combine as
+ *   out = (e^lse_s out_s + e^lse_w out_w) / (e^lse_s + e^lse_w),
+ *   lse = log(e^lse_s + e^lse_w),
+ * which is why csa2_sparse_attn_fp4 exports its lse.
+ *
+ * q         bf16 [B, H, d_c + d_r]
+ * codes     u8   window rows of csa2_quantize_fp8: row j of sequence b is row
+ *                b * W_cap + j (codes_stride bytes apart, 0 = d_c), sigma f32
+ *                [B, W_cap], rope bf16 rows (rope_stride bytes, 0 = 2 d_r)
+ * n_win     i32  [B]  rows j < n_win[b] form the window (NULL = W_cap;
+ *                clamped to [0, W_cap] on the device); their order is free
+ * merge_out f32 [B, H, d_c], merge_lse f32 [B, H]: the sparse branch's result
+ *                (csa2_sparse_attn_fp4), both NULL for the window branch alone;
+ *                merge_out may be the same buffer as out
+ * out       f32  [B, H, d_c] out;  lse f32 [B, H] out (nullable)
+ * An empty window leaves the sparse result unchanged (or gives out = 0,
+ * lse = -inf alone).  Scores and values use the exact E4M3 values in fp16
+ * with fp32 accumulation; the row scales multiply the fp32 latent scores and
+ * enter P as sigma_j / max sigma (exact for the power-of-two scales
+ * csa2_quantize_fp8 writes): the error is < 2e-3 of max|out| per (b, h) row.
+ * Requires d_c == 512, d_r in {0, 64}, 1 <= H <= 128, 0 <= W_cap <= 256
+ * (CSA2_ERR_RANGE beyond), 16-byte aligned q, out, codes, rope and their
+ * strides, 4-byte aligned sigma, window values of E4M3 codes (no 0x7F/0xFF).
+ */
+int csa2_swa_attn_fp8(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
+                      const float* sigma, const uint16_t* rope, int64_t rope_stride,
+                      const int32_t* n_win, int32_t B, int32_t H, int32_t d_c, int32_t d_r,
+                      int32_t W_cap, float sm_scale, const float* merge_out,
+                      const float* merge_lse, float* out, float* lse, csa2_stream_t stream);
+
+/*
  * Candidate-pool construction for Reindex mode: the block-level pool that the
  * decoder's first Full layer keeps (at most 2048 blocks x 8 positions) so that
  * later layers score only inside it ([P1] 架构三件套, Hierarchical Sparse

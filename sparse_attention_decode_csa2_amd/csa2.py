@@ -46,6 +46,8 @@ def load():
         "csa2_index_pool": (ctypes.c_int, [P, P, P, P, P, P, I32, I32, I32, I64, I32, I32, P, P, P]),
         "csa2_topk_workspace_bytes": (SZ, [I32, I64, I32]),
         "csa2_topk": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P, SZ, P]),
+        "csa2_quantize_fp8": (ctypes.c_int, [P, I64, I32, P, I32, P, I64, P, P, I64, I64, I64, P]),
+        "csa2_swa_attn_fp8": (ctypes.c_int, [P, P, I64, P, P, I64, P, I32, I32, I32, I32, I32, F, P, P, P, P, P]),
         "csa2_build_pool_workspace_bytes": (SZ, [I32, I64, I32, I32]),
         "csa2_build_pool": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
@@ -213,6 +215,55 @@ def csa2_topk(scores, K, ids=None, n_valid=None, out_idx=None, out_score=None, w
 
 
 # ------------------------------------------------------------------ a4 / a5
+
+
+def alloc_window(B, W_cap, d_c, d_r, device="cuda"):
+    """Sliding-window FP8 cache: codes u8 [B, W_cap, d_c], sigma f32 [B, W_cap],
+    rope bf16 [B, W_cap, d_r] (dense rows)."""
+    codes = torch.zeros(B, W_cap, d_c, dtype=torch.uint8, device=device)
+    sigma = torch.ones(B, W_cap, dtype=torch.float32, device=device)
+    rope = torch.zeros(B, W_cap, d_r, dtype=torch.bfloat16, device=device)
+    return codes, sigma, rope
+
+
+def csa2_quantize_fp8(x, codes, sigma, dst_row0=0, rope_src=None, rope_dst=None):
+    """FP8 write of window rows: x bf16 [R, d_c] -> rows [dst_row0, dst_row0 + R)
+    of codes u8 [cap, d_c] / sigma f32 [cap] (and the RoPE part, copied)."""
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    R, d_c = x.shape
+    d_r = 0 if rope_src is None else rope_src.shape[1]
+    cap = codes.shape[0]
+    cs = _row_stride(codes, 1, "codes")
+    rs = _row_stride(rope_dst, 2, "rope_dst") if d_r > 0 else 0
+    st = lib.csa2_quantize_fp8(_ptr(x), R, d_c, _ptr(rope_src), d_r, _ptr(codes), cs, _ptr(sigma),
+                               _ptr(rope_dst if d_r > 0 else None), rs, dst_row0, cap, _stream())
+    _check("csa2_quantize_fp8", st)
+
+
+def csa2_swa_attn_fp8(q, codes, sigma, rope, sm_scale=None, n_win=None, merge_out=None, merge_lse=None,
+                      out=None, lse=None):
+    """Window attention over codes [B, W_cap, d_c] (E4M3) with row scales sigma
+    [B, W_cap], merged with (merge_out, merge_lse) when given: returns
+    (out f32 [B, H, d_c], lse f32 [B, H])."""
+    lib = load()
+    B, H, D = q.shape
+    W_cap, d_c = codes.shape[1], codes.shape[2]
+    d_r = D - d_c
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, H, d_c, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    cs = _row_stride(codes, 1, "codes")
+    rs = _row_stride(rope, 2, "rope") if d_r > 0 else 0
+    st = lib.csa2_swa_attn_fp8(_ptr(q), _ptr(codes), cs, _ptr(sigma), _ptr(rope if d_r > 0 else None), rs,
+                               _ptr(n_win), B, H, d_c, d_r, W_cap, float(sm_scale), _ptr(merge_out),
+                               _ptr(merge_lse), _ptr(out), _ptr(lse), _stream())
+    _check("csa2_swa_attn_fp8", st)
+    return out, lse
 
 
 def csa2_build_pool_workspace_bytes(B, M, block, P_max):

@@ -903,4 +903,266 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
   return hipGetLastError();
 }
 
+// Sliding-window branch: softmax attention of 16 query heads over the window
+// rows of one sequence (the last tokens, one FP8 entry per token: E4M3 latent
+// with a power-of-two scale per row, bf16 RoPE part), optionally merged with
+// the sparse branch's (out, lse) into one softmax over the union of both key
+// sets ([P4] CSA2 paragraph: the SWA branch beside the sparse one, SWA KV in
+// FP8; [P1] section 效率组件四件, item 4).
+//
+// Same wave layout as the 16-head sparse kernel: wave w scores window rows
+// 16w .. 16w + 15 of a 64-row tile, lane (n, g) holding channels 128 g .. + 127
+// of row n as 8 words of 16 E4M3 values; each word is two score k-steps after
+// an exact E4M3 -> fp16 conversion.  The latent products and the RoPE
+// products go to separate accumulators so that the row scale multiplies only
+// the latent part; the value products use the unscaled E4M3 values with P
+// scaled by sigma_j / max sigma (a power of two, <= 1), and max sigma is
+// applied once in the epilogue.  The window is at most 256 rows (4 tiles),
+// loaded tile by tile.
+template <int DR>
+__global__ __launch_bounds__(256) void swa_attn_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, int64_t codes_stride,
+    const float* __restrict__ sigma, const uint16_t* __restrict__ rope, int64_t rope_stride,
+    const int32_t* __restrict__ n_win, int B, int H, int W_cap, float sm_scale_log2e, int n_hg,
+    const float* __restrict__ in_out, const float* __restrict__ in_lse, float* __restrict__ out,
+    float* __restrict__ lse) {
+  constexpr int DC = 512;
+  constexpr int KSL = DC / 32;            // latent k-steps
+  constexpr int KSR = DR / 32;            // RoPE k-steps
+  constexpr int LDK = DC + 16;
+  constexpr int NDB = DC / 4 / 16;        // PV d-blocks per wave (128 channels)
+  __shared__ __attribute__((aligned(16))) _Float16 sK[AT_TILE][LDK];
+  __shared__ __attribute__((aligned(16))) _Float16 sP[16][AT_TILE + 8];
+  __shared__ float sMax[4][16], sSum[4][16], sAlpha[16], sFinM[16], sFinL[16];
+  __shared__ float sSig[256];
+  __shared__ float sRed[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t b = blockIdx.x / n_hg;
+  const int h0 = (int)(blockIdx.x - b * n_hg) * 16;
+  const int nw = n_win ? min(max(n_win[b], 0), W_cap) : W_cap;
+  const int n_tiles = (nw + AT_TILE - 1) / AT_TILE;
+
+  // ---- row scales of the window and their maximum
+  float sg = 0.f;
+  if (tid < nw) sg = sigma[b * W_cap + tid];
+  sSig[tid] = sg;
+  float smax = sg;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) smax = fmaxf(smax, __shfl_xor(smax, o));
+  if (lane == 0) sRed[wave] = smax;
+
+  // ---- query heads h0 + n as B operands: latent k-step t -> channels
+  // 128 g + 8 t .. + 7, RoPE k-step t -> channels d_c + 16 g + 8 t .. + 7
+  const bool hv = h0 + n < H;
+  u32x4 qraw[KSL + KSR];
+  {
+    const uint16_t* qrow = q + (b * H + (hv ? h0 + n : 0)) * (DC + DR);
+#pragma unroll
+    for (int t = 0; t < KSL + KSR; ++t) {
+      const int off = t < KSL ? 128 * g + 8 * t : DC + 16 * g + 8 * (t - KSL);
+      qraw[t] = hv ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  f16x8 Bq[KSL];
+  bf16x8 Br[KSR > 0 ? KSR : 1];
+  float fscale;
+  {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int t = 0; t < KSL + KSR; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = max(mx, max(qraw[t][j] & 0x7FFFu, (qraw[t][j] >> 16) & 0x7FFFu));
+    mx = max(mx, xor16(mx));
+    mx = max(mx, xor32(mx));
+    // 2^sh brings the largest |q| of the head into [2^14, 2^15), where fp16
+    // keeps every bit of a bf16 value
+    int ex = (int)((mx >> 7) & 0xFF) - 127;
+    if (ex < -126) ex = -126;
+    const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - ex));
+    const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
+    fscale = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
+#pragma unroll
+    for (int t = 0; t < KSL; ++t) {
+      f16x8 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = (_Float16)(bf16_bits_to_f32(qraw[t][j] & 0xFFFFu) * up);
+        o[2 * j + 1] = (_Float16)(bf16_bits_to_f32(qraw[t][j] >> 16) * up);
+      }
+      Bq[t] = o;
+    }
+#pragma unroll
+    for (int t = 0; t < KSR; ++t) {
+      bf16x8 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = (__bf16)(bf16_bits_to_f32(qraw[KSL + t][j] & 0xFFFFu) * up);
+        o[2 * j + 1] = (__bf16)(bf16_bits_to_f32(qraw[KSL + t][j] >> 16) * up);
+      }
+      Br[t] = o;
+    }
+  }
+  __syncthreads();  // row scales and their per-wave maxima
+  const float s_max = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
+  const float inv_smax = s_max > 0.f ? 1.0f / s_max : 0.f;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    // ---- gather: row 64 tile + 16 wave + n, channels 128 g .. + 127
+    const int row = tile * AT_TILE + 16 * wave + n;
+    const bool valid = row < nw;
+    const int64_t rr = b * W_cap + (valid ? row : 0);
+    const uint8_t* crow = codes + rr * codes_stride + 128 * g;
+    u32x4 cw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cw[i] = *reinterpret_cast<const u32x4*>(crow + 16 * i);
+    u32x4 rw[KSR > 0 ? KSR : 1];
+    if constexpr (DR > 0) {
+      const uint8_t* rrow = reinterpret_cast<const uint8_t*>(rope) + rr * rope_stride + 32 * g;
+#pragma unroll
+      for (int t = 0; t < KSR; ++t) rw[t] = *reinterpret_cast<const u32x4*>(rrow + 16 * t);
+    }
+    // ---- exact E4M3 -> fp16, latent scores, value tile
+    const int e = 16 * wave + n;
+    f32x4 cl = {0.f, 0.f, 0.f, 0.f}, cr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[i][2 * h], 1.0f, false);
+        const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[i][2 * h], 1.0f, true);
+        const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[i][2 * h + 1], 1.0f, false);
+        const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[i][2 * h + 1], 1.0f, true);
+        f16x8 a = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        if (!valid) a = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        const int t = 2 * i + h;  // channels 128 g + 8 t .. + 7
+        *reinterpret_cast<f16x8*>(&sK[e][tile_col(e, 4 * g + (t >> 2), t & 3)]) = a;
+        cl = mfma16x16x32_f16(a, Bq[t], cl);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < KSR; ++t) cr = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, rw[t]), Br[t], cr);
+    // cl[i], cr[i]: row 16 wave + 4 g + i, head n
+    const uint64_t vb = __ballot(g == 0 && valid);
+    float s2[4], rs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float sgi = sSig[tile * AT_TILE + 16 * wave + 4 * g + i];
+      rs[i] = sgi * inv_smax;
+      s2[i] = ((vb >> (4 * g + i)) & 1u) ? (cl[i] * sgi + cr[i]) * fscale : -INFINITY;
+    }
+    // ---- online softmax (base 2), maxima exchanged through LDS
+    float mt = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+    mt = fmaxf(mt, xor16f(mt));
+    mt = fmaxf(mt, xor32f(mt));
+    if (g == 0) sMax[wave][n] = mt;
+    __syncthreads();
+    const float m_tile = fmaxf(fmaxf(sMax[0][n], sMax[1][n]), fmaxf(sMax[2][n], sMax[3][n]));
+    const float m_new = fmaxf(m_run, m_tile);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    float p[4], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = s2[i] == -INFINITY ? 0.f : exp2f(s2[i] - m_new);
+      ps += p[i];
+    }
+    ps += xor16f(ps);
+    ps += xor32f(ps);
+    if (g == 0) sSum[wave][n] = ps;
+    if (wave == 0 && g == 0) sAlpha[n] = alpha;
+    *reinterpret_cast<f16x4*>(&sP[n][16 * wave + 4 * g]) =
+        f16x4{(_Float16)(p[0] * rs[0]), (_Float16)(p[1] * rs[1]), (_Float16)(p[2] * rs[2]), (_Float16)(p[3] * rs[3])};
+    __syncthreads();
+    l_run = l_run * alpha + (sSum[0][n] + sSum[1][n] + sSum[2][n] + sSum[3][n]);
+    m_run = m_new;
+    // ---- O = alpha O + P' . V (V: the unscaled E4M3 values of the tile)
+    {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = sAlpha[4 * g + i];
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[d][i] *= al[i];
+      const int tr_r = n >> 2, tr_c = n & 3;
+#pragma unroll
+      for (int u = 0; u < AT_TILE / 32; ++u) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&sP[n][32 * u + 8 * g]);
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const int ch = 32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + 4 * tr_c;
+          const int r0 = 32 * u + 8 * g + tr_r, r1 = r0 + 4;
+          const f16x4 v0 = tr16_read(&sK[r0][tile_col(r0, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+          const f16x4 v1 = tr16_read(&sK[r1][tile_col(r1, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+          const f16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[d] = mfma16x16x32_f16(a, bv, acc[d]);
+        }
+      }
+    }
+    __syncthreads();  // the tile buffers are rewritten by the next tile
+  }
+
+  // ---- epilogue: lane (channel n of each d-block, k-group g) holds heads
+  // h0 + 4 g + i; window result o_w = acc * max sigma / l, merged with the
+  // sparse branch when given: weights e^(lse - max lse) of the two branches
+  if (wave == 0 && g == 0) {
+    sFinM[n] = m_run;
+    sFinL[n] = l_run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * g + i;
+    const int h = h0 + hl;
+    if (h >= H) continue;
+    const float m = sFinM[hl], l = sFinL[hl];
+    const float lw = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;  // window lse (natural log)
+    const float ow = l > 0.f ? s_max / l : 0.f;                        // scale of acc -> o_w
+    float wa = 0.f, wb = 1.f, den = 1.f, lo = lw;
+    if (in_lse) {
+      const float ls = in_lse[b * H + h];
+      const float mm = fmaxf(ls, lw);
+      const float ref = mm == -INFINITY ? 0.f : mm;
+      wa = ls == -INFINITY ? 0.f : __expf(ls - ref);
+      wb = lw == -INFINITY ? 0.f : __expf(lw - ref);
+      den = wa + wb;
+      lo = den > 0.f ? ref + __logf(den) : -INFINITY;
+      den = den > 0.f ? den : 1.f;
+    }
+    const int64_t orow = (b * H + h) * DC;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int64_t c = orow + 32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + n;
+      const float v = acc[d][i] * ow;
+      out[c] = in_lse ? (wa * in_out[c] + wb * v) / den : v;
+    }
+    if (lse && wave == 0 && n == 0) lse[b * H + h] = lo;
+  }
+}
+
+hipError_t launch_swa_attn(const uint16_t* q, const uint8_t* codes, int64_t codes_stride, const float* sigma,
+                           const uint16_t* rope, int64_t rope_stride, const int32_t* n_win, int B, int H, int d_r,
+                           int W_cap, float sm_scale, const float* in_out, const float* in_lse, float* out,
+                           float* lse, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const int n_hg = (H + 15) / 16;
+  const dim3 grid((unsigned)((int64_t)B * n_hg));
+  const float sl = sm_scale * LOG2E;
+  if (d_r == 64)
+    hipLaunchKernelGGL(swa_attn_kernel<64>, grid, dim3(256), 0, stream, q, codes, codes_stride, sigma, rope,
+                       rope_stride, n_win, B, H, W_cap, sl, n_hg, in_out, in_lse, out, lse);
+  else if (d_r == 0)
+    hipLaunchKernelGGL(swa_attn_kernel<0>, grid, dim3(256), 0, stream, q, codes, codes_stride, sigma, rope,
+                       rope_stride, n_win, B, H, W_cap, sl, n_hg, in_out, in_lse, out, lse);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace csa2

@@ -62,6 +62,28 @@ int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint
                                               dst_row0, as_stream(stream)));
 }
 
+int csa2_quantize_fp8(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
+                      int32_t d_r, uint8_t* codes, int64_t codes_stride, float* sigma,
+                      uint16_t* rope_dst, int64_t rope_stride, int64_t dst_row0, int64_t capacity,
+                      csa2_stream_t stream) {
+  if (n_rows < 0 || capacity < 0 || d_c < 8 || d_c > 4096 || d_c % 8 != 0 || d_r < 0 || d_r > 512 ||
+      d_r % 8 != 0 || codes_stride < 0 || rope_stride < 0)
+    return CSA2_ERR_SHAPE;
+  if (dst_row0 < 0 || dst_row0 > capacity || n_rows > capacity - dst_row0) return CSA2_ERR_RANGE;
+  if (n_rows == 0) return CSA2_OK;
+  if (!x || !codes || !sigma || (d_r > 0 && (!rope_src || !rope_dst))) return CSA2_ERR_NULL;
+  if (codes_stride == 0) codes_stride = d_c;
+  if (rope_stride == 0) rope_stride = 2 * (int64_t)d_r;
+  if (codes_stride < d_c || (d_r > 0 && rope_stride < 2 * (int64_t)d_r)) return CSA2_ERR_SHAPE;
+  if (!aligned16(x) || !opt_aligned16(rope_src) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
+      codes_stride % 8 != 0 || (reinterpret_cast<uintptr_t>(sigma) & 3u) != 0 ||
+      (d_r > 0 && (!aligned16(rope_dst) || rope_stride % 16 != 0)))
+    return CSA2_ERR_ALIGN;
+  return hip_status(csa2::launch_quantize_fp8(x, n_rows, d_c, d_r > 0 ? rope_src : nullptr, d_r, codes,
+                                              codes_stride, sigma, d_r > 0 ? rope_dst : nullptr, rope_stride,
+                                              dst_row0, as_stream(stream)));
+}
+
 static int check_index_common(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                               const int32_t* n_valid, int32_t B, int32_t H_I, int32_t D_I,
                               int64_t N_cap, const float* scores) {
@@ -102,6 +124,29 @@ int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
   return hip_status(csa2::launch_index(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, pool_blocks,
                                        n_blocks, P_max, block, scores, positions,
                                        as_stream(stream)));
+}
+
+int csa2_swa_attn_fp8(const uint16_t* q, const uint8_t* codes, int64_t codes_stride, const float* sigma,
+                      const uint16_t* rope, int64_t rope_stride, const int32_t* n_win, int32_t B, int32_t H,
+                      int32_t d_c, int32_t d_r, int32_t W_cap, float sm_scale, const float* merge_out,
+                      const float* merge_lse, float* out, float* lse, csa2_stream_t stream) {
+  if (B < 0 || W_cap < 0 || codes_stride < 0 || rope_stride < 0) return CSA2_ERR_SHAPE;
+  if (d_c != 512 || !(d_r == 0 || d_r == 64) || H < 1 || H > 128) return CSA2_ERR_UNSUPPORTED;
+  if (W_cap > 256) return CSA2_ERR_RANGE;
+  if (B == 0) return CSA2_OK;
+  if (!q || !out || (W_cap > 0 && (!codes || !sigma || (d_r > 0 && !rope))) || (!merge_out != !merge_lse))
+    return CSA2_ERR_NULL;
+  if (codes_stride == 0) codes_stride = d_c;
+  if (rope_stride == 0) rope_stride = 2 * (int64_t)d_r;
+  if (codes_stride < d_c || (d_r > 0 && rope_stride < 2 * (int64_t)d_r)) return CSA2_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out) || !opt_aligned16(lse) || !opt_aligned16(merge_out) ||
+      !opt_aligned16(merge_lse) || !opt_aligned16(n_win) || (W_cap > 0 && (!aligned16(codes) ||
+      codes_stride % 16 != 0 || (reinterpret_cast<uintptr_t>(sigma) & 3u) != 0 ||
+      (d_r > 0 && (!aligned16(rope) || rope_stride % 16 != 0)))))
+    return CSA2_ERR_ALIGN;
+  return hip_status(csa2::launch_swa_attn(q, codes, codes_stride, sigma, d_r > 0 ? rope : nullptr, rope_stride,
+                                          n_win, B, H, d_r, W_cap, sm_scale, merge_out, merge_lse, out, lse,
+                                          as_stream(stream)));
 }
 
 size_t csa2_build_pool_workspace_bytes(int32_t B, int64_t M, int32_t block, int32_t P_max) {

@@ -36,6 +36,14 @@ hipError_t launch_build_pool(const float* scores, const int32_t* n_valid, int B,
                              int P_max, int32_t* pool_blocks, int32_t* n_blocks, void* workspace,
                              hipStream_t stream);
 
+hipError_t launch_quantize_fp8(const uint16_t* x, int64_t n_rows, int d_c, const uint16_t* rope_src, int d_r,
+                               uint8_t* codes, int64_t codes_stride, float* sigma, uint16_t* rope_dst,
+                               int64_t rope_stride, int64_t dst_row0, hipStream_t stream);
+hipError_t launch_swa_attn(const uint16_t* q, const uint8_t* codes, int64_t codes_stride, const float* sigma,
+                           const uint16_t* rope, int64_t rope_stride, const int32_t* n_win, int B, int H, int d_r,
+                           int W_cap, float sm_scale, const float* in_out, const float* in_lse, float* out,
+                           float* lse, hipStream_t stream);
+
 size_t attn_workspace_bytes(int B, int H, int d_c, int K);
 hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
                               int d_c, int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
 
@@ -109,6 +109,37 @@ def test_build_pool_validation(lib):
     assert f(U, N, 2, 262144, 8, 2048, A, A, A, need, N) == ALIGN
     assert f(A, U, 2, 262144, 8, 2048, A, A, A, need, N) == ALIGN
     assert f(A, N, 2, 262144, 8, 2048, A, A, A, need - 1, N) == WS
+
+
+def test_window_validation(lib):
+    q8 = lib.csa2_quantize_fp8
+    assert q8(A, -1, 512, N, 0, A, 0, A, N, 0, 0, 10, N) == SHAPE
+    assert q8(A, 4, 500, N, 0, A, 0, A, N, 0, 0, 10, N) == SHAPE
+    assert q8(A, 4, 512, N, 0, A, 0, A, N, 0, 8, 10, N) == RANGE
+    assert q8(A, 0, 512, N, 0, A, 0, A, N, 0, 10, 10, N) == OK
+    assert q8(N, 4, 512, N, 0, A, 0, A, N, 0, 0, 10, N) == NULL
+    assert q8(A, 4, 512, N, 64, A, 0, A, N, 0, 0, 10, N) == NULL
+    assert q8(U, 4, 512, N, 0, A, 0, A, N, 0, 0, 10, N) == ALIGN
+    assert q8(A, 4, 512, N, 0, A, 516, A, N, 0, 0, 10, N) == ALIGN
+    assert q8(A, 4, 512, N, 0, A, 256, A, N, 0, 0, 10, N) == SHAPE
+    sw = lib.csa2_swa_attn_fp8
+    sm = ctypes.c_float(0.04)
+
+    def call(q=A, codes=A, cst=0, sig=A, rope=A, rst=0, nw=N, B=2, H=64, d_c=512, d_r=64, W=128,
+             mo=N, ml=N, out=A, lse=N):
+        return sw(q, codes, cst, sig, rope, rst, nw, B, H, d_c, d_r, W, sm, mo, ml, out, lse, N)
+    assert call(B=-1) == SHAPE
+    assert call(d_c=128) == UNSUP
+    assert call(d_r=32) == UNSUP
+    assert call(H=129) == UNSUP
+    assert call(W=257) == RANGE
+    assert call(B=0) == OK
+    assert call(q=N) == NULL
+    assert call(sig=N) == NULL
+    assert call(mo=A) == NULL                       # one half of the merge input
+    assert call(q=U) == ALIGN
+    assert call(cst=520) == ALIGN
+    assert call(cst=256) == SHAPE
 
 
 def test_attn_validation(lib):
