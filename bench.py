@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="full-64k",
                     help="full-64k (default, the reported line); others for supplementary runs: "
-                         "tiny-full, reindex-1m, reuse-128k, prefill-full-1m, pool-build-1m")
+                         "tiny-full, reindex-1m, reuse-128k, prefill-full-1m, pool-build-1m, reuse-swa-128k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -64,6 +64,11 @@ def committed_traffic(kernel_file, workload):
     return float(rec["bytes_per_launch"])
 
 
+def _window_bytes(wl):
+    """Algorithmic bytes of one FP8 window row (codes + row scale + RoPE part)."""
+    return wl.d_c + 4 + 2 * wl.d_r
+
+
 def _entry_bytes(wl):
     """Algorithmic bytes of one cache entry (codes + scales + RoPE part)."""
     return wl.d_c // 2 + wl.d_c // 16 + 2 * wl.d_r
@@ -77,6 +82,7 @@ class Step:
     Reuse (reuse-128k): attn over one cache; sets = index lists + queries.
     Prefill + Full (prefill-full-1m): quantize (append 8192 rows) -> index -> topk -> attn.
     Pool construction (pool-build-1m): index (Full scores) -> build (the Reindex pool).
+    Reuse + window (reuse-swa-128k): attn -> swa (the FP8 window branch merged in).
     """
 
     def __init__(self, wl, dev, rotation_bytes=ROTATION_BYTES):
@@ -97,6 +103,7 @@ class Step:
                 self.keys = torch.stack([W.index_keys(wl, b, dev) for b in range(B)])
             touched = {"reindex": B * (wl.n_blocks * wl.block * wl.D_I * 2 + wl.K * _entry_bytes(wl)),
                        "reuse": B * wl.K * _entry_bytes(wl),
+                       "reuse_swa": B * (wl.K * _entry_bytes(wl) + wl.window * _window_bytes(wl)),
                        "prefill_full": B * N * wl.D_I * 2, "pool_build": B * N * wl.D_I * 2}[self.mode]
             self.R = max(2, math.ceil(rotation_bytes / touched))
             self.sets = []
@@ -109,13 +116,14 @@ class Step:
                     st["pool"], st["nb"] = (t.to(dev) for t in W.pool_blocks(ws, "cpu"))
                 if self.mode in ("reindex", "prefill_full", "pool_build"):
                     st["qi"] = W.index_query(ws, dev)
-                if self.mode == "reuse":
+                if self.mode in ("reuse", "reuse_swa"):
                     st["idx"] = W.reuse_index(ws, "cpu").to(dev)
                 self.sets.append(st)
             if self.mode == "prefill_full":
                 self.chunk = W.prefill_chunk(wl, dev)
                 self.chunk_rope = W.prefill_rope(wl, dev)
-        M = {"full": N, "prefill_full": N, "reindex": wl.P_max * wl.block, "reuse": 0, "pool_build": N}[self.mode]
+        M = {"full": N, "prefill_full": N, "reindex": wl.P_max * wl.block, "reuse": 0, "pool_build": N,
+             "reuse_swa": 0}[self.mode]
         self.M = M
         self.scores = torch.empty(B, max(M, 1), dtype=torch.float32, device=dev)
         self.positions = torch.empty(B, max(M, 1), dtype=torch.int32, device=dev)
@@ -129,13 +137,22 @@ class Step:
         self.ws_attn = torch.empty(max(at, 16), dtype=torch.uint8, device=dev) if at else None
         self.stages = {"full": ["index", "topk", "attn"], "reindex": ["pool", "topk", "attn"],
                        "reuse": ["attn"], "prefill_full": ["quantize", "index", "topk", "attn"],
-                       "pool_build": ["index", "build"]}[self.mode]
+                       "pool_build": ["index", "build"], "reuse_swa": ["attn", "swa"]}[self.mode]
+        if self.mode == "reuse_swa":
+            Wn = wl.window
+            self.win = csa2.alloc_window(B, Wn, wl.d_c, wl.d_r, dev)
+            for b in range(B):
+                lat = W.latent_rows(wl, b, Wn, dev, name="window")
+                csa2.csa2_quantize_fp8(lat, self.win[0][b], self.win[1][b], 0,
+                                       W.rope_rows(wl.scaled(seed=wl.seed + 7919), b, Wn, dev), self.win[2][b])
+            self.out2 = torch.empty_like(self.out)
+            self.lse2 = torch.empty_like(self.lse)
         if self.mode == "pool_build":
             self.pool_out = torch.empty(B, wl.P_max, dtype=torch.int32, device=dev)
             self.nb_out = torch.empty(B, dtype=torch.int32, device=dev)
             pb = csa2.csa2_build_pool_workspace_bytes(B, N, wl.block, wl.P_max)
             self.ws_build = torch.empty(max(pb, 16), dtype=torch.uint8, device=dev)
-        if self.mode == "reuse":
+        if self.mode in ("reuse", "reuse_swa"):
             self.idx = None
 
     def _cache(self, ws):
@@ -188,9 +205,14 @@ class Step:
         self.csa2.csa2_topk(self.scores, self.wl.K, ids=ids, out_idx=self.idx, out_score=self.top,
                             workspace=self.ws_topk)
 
+    def swa(self, r):
+        c, sg, rp = self.win
+        self.csa2.csa2_swa_attn_fp8(self.sets[r]["q"], c, sg, rp, self.wl.sm_scale, merge_out=self.out,
+                                    merge_lse=self.lse, out=self.out2, lse=self.lse2)
+
     def attn(self, r):
         kv, st = self._kv(r), self.sets[r]
-        idx = st["idx"] if self.mode == "reuse" else self.idx
+        idx = st["idx"] if self.mode in ("reuse", "reuse_swa") else self.idx
         self.csa2.csa2_sparse_attn_fp4(st["q"], kv["codes"], kv["scales"], kv["rope"], idx,
                                        self.wl.sm_scale, out=self.out, lse=self.lse,
                                        workspace=self.ws_attn)
@@ -209,6 +231,11 @@ class Step:
         attn = B * (K * 4 + K * ent + H * wl.D * 2 + H * wl.d_c * 4 + H * 4)
         d = {"attn": attn}
         step = attn
+        if self.mode == "reuse_swa":
+            win = B * wl.window * _window_bytes(wl)
+            d["swa"] = win + B * (H * wl.D * 2 + 2 * (H * wl.d_c * 4 + H * 4))
+            d["step"] = attn + win
+            return d
         if self.mode == "pool_build":
             d["index"] = B * (N * wl.D_I * 2 + qi + N * 4)
             d["build"] = B * (N * 4 + wl.P_max * 4 + 4)
@@ -343,7 +370,7 @@ def main():
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
     kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
-                   "quantize": "quantize.hip", "build": "pool.hip"}[dom]
+                   "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip"}[dom]
     achieved = alg[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = committed_traffic(kernel_file, wl.name)
 

@@ -919,13 +919,17 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
 // scaled by sigma_j / max sigma (a power of two, <= 1), and max sigma is
 // applied once in the epilogue.  The window is at most 256 rows (4 tiles),
 // loaded tile by tile.
+struct SwaRegs {
+  u32x4 cw[8];  // 128 E4M3 latent values of the lane's quarter row
+  u32x4 rw[2];  // 16 RoPE channels (bf16)
+};
+
 template <int DR>
 __global__ __launch_bounds__(256) void swa_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, int64_t codes_stride,
     const float* __restrict__ sigma, const uint16_t* __restrict__ rope, int64_t rope_stride,
     const int32_t* __restrict__ n_win, int B, int H, int W_cap, float sm_scale_log2e, int n_hg,
-    const float* __restrict__ in_out, const float* __restrict__ in_lse, float* __restrict__ out,
-    float* __restrict__ lse) {
+    const float* in_out, const float* __restrict__ in_lse, float* out, float* __restrict__ lse) {
   constexpr int DC = 512;
   constexpr int KSL = DC / 32;            // latent k-steps
   constexpr int KSR = DR / 32;            // RoPE k-steps
@@ -939,8 +943,13 @@ __global__ __launch_bounds__(256) void swa_attn_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int64_t b = blockIdx.x / n_hg;
-  const int h0 = (int)(blockIdx.x - b * n_hg) * 16;
+  // workgroup x runs on XCD x % 8: the head groups of one query, which read
+  // the same window rows, share that XCD's L2
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int64_t b = (int64_t)(slot / n_hg) * 8 + xcd;
+  if (b >= B) return;  // padding of the grid to whole groups of eight queries
+  const int h0 = (slot % n_hg) * 16;
   const int nw = n_win ? min(max(n_win[b], 0), W_cap) : W_cap;
   const int n_tiles = (nw + AT_TILE - 1) / AT_TILE;
 
@@ -952,6 +961,25 @@ __global__ __launch_bounds__(256) void swa_attn_kernel(
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) smax = fmaxf(smax, __shfl_xor(smax, o));
   if (lane == 0) sRed[wave] = smax;
+
+  // ---- window rows: row 64 tile + 16 wave + n, channels 128 g .. + 127 as
+  // 8 words of 16 E4M3 values, and 16 channels of the RoPE part per word
+  auto gather = [&](SwaRegs& gr, int tile) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int row = tile * AT_TILE + 16 * wave + n;
+    const int64_t rr = b * W_cap + (row < nw ? row : 0);
+    const uint8_t* crow = codes + rr * codes_stride + 128 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gr.cw[i] = *reinterpret_cast<const u32x4*>(crow + 16 * i);
+    if constexpr (DR > 0) {
+      const uint8_t* rrow = reinterpret_cast<const uint8_t*>(rope) + rr * rope_stride + 32 * g;
+#pragma unroll
+      for (int t = 0; t < KSR; ++t) gr.rw[t] = *reinterpret_cast<const u32x4*>(rrow + 16 * t);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  SwaRegs ra0;
+  if (n_tiles > 0) gather(ra0, 0);
 
   // ---- query heads h0 + n as B operands: latent k-step t -> channels
   // 128 g + 8 t .. + 7, RoPE k-step t -> channels d_c + 16 g + 8 t .. + 7
@@ -1013,21 +1041,11 @@ __global__ __launch_bounds__(256) void swa_attn_kernel(
 #pragma unroll
   for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    // ---- gather: row 64 tile + 16 wave + n, channels 128 g .. + 127
+  auto process = [&](const SwaRegs& gr, int tile) {
+    const u32x4* cw = gr.cw;
+    const u32x4* rw = gr.rw;
     const int row = tile * AT_TILE + 16 * wave + n;
     const bool valid = row < nw;
-    const int64_t rr = b * W_cap + (valid ? row : 0);
-    const uint8_t* crow = codes + rr * codes_stride + 128 * g;
-    u32x4 cw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cw[i] = *reinterpret_cast<const u32x4*>(crow + 16 * i);
-    u32x4 rw[KSR > 0 ? KSR : 1];
-    if constexpr (DR > 0) {
-      const uint8_t* rrow = reinterpret_cast<const uint8_t*>(rope) + rr * rope_stride + 32 * g;
-#pragma unroll
-      for (int t = 0; t < KSR; ++t) rw[t] = *reinterpret_cast<const u32x4*>(rrow + 16 * t);
-    }
     // ---- exact E4M3 -> fp16, latent scores, value tile
     const int e = 16 * wave + n;
     f32x4 cl = {0.f, 0.f, 0.f, 0.f}, cr = {0.f, 0.f, 0.f, 0.f};
@@ -1106,6 +1124,22 @@ __global__ __launch_bounds__(256) void swa_attn_kernel(
       }
     }
     __syncthreads();  // the tile buffers are rewritten by the next tile
+  };
+  // two register sets: the loads of tile t + 1 are in flight while tile t is
+  // processed (past the last tile they read row 0 again, unconditionally)
+  if (n_tiles > 0) {
+    SwaRegs& ra = ra0;
+    SwaRegs rb;
+    int t = 0;
+    gather(rb, 1);
+    for (; t + 2 <= n_tiles; t += 2) {
+      process(ra, t);
+      gather(ra, t + 2);
+      process(rb, t + 1);
+      gather(rb, t + 3);
+    }
+    if (t < n_tiles) process(ra, t);
+    __builtin_amdgcn_s_waitcnt(0);  // no load may land after the wave ends
   }
 
   // ---- epilogue: lane (channel n of each d-block, k-group g) holds heads
@@ -1136,11 +1170,16 @@ __global__ __launch_bounds__(256) void swa_attn_kernel(
       den = den > 0.f ? den : 1.f;
     }
     const int64_t orow = (b * H + h) * DC;
+    float mi[NDB];  // the sparse branch's values, all read before any write (out may be in_out)
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+      mi[d] = in_lse ? in_out[orow + 32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + n] : 0.f;
+    const float inv_den = 1.0f / den;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
       const int64_t c = orow + 32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + n;
       const float v = acc[d][i] * ow;
-      out[c] = in_lse ? (wa * in_out[c] + wb * v) / den : v;
+      out[c] = in_lse ? (wa * mi[d] + wb * v) * inv_den : v;
     }
     if (lse && wave == 0 && n == 0) lse[b * H + h] = lo;
   }
@@ -1152,7 +1191,7 @@ hipError_t launch_swa_attn(const uint16_t* q, const uint8_t* codes, int64_t code
                            float* lse, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   const int n_hg = (H + 15) / 16;
-  const dim3 grid((unsigned)((int64_t)B * n_hg));
+  const dim3 grid((unsigned)(((int64_t)B + 7) / 8 * 8 * n_hg));
   const float sl = sm_scale * LOG2E;
   if (d_r == 64)
     hipLaunchKernelGGL(swa_attn_kernel<64>, grid, dim3(256), 0, stream, q, codes, codes_stride, sigma, rope,

@@ -26,6 +26,9 @@ compressed entry per 4 tokens):
 5. pool-build-1m  the shapes of reindex-1m, for the layer before it: Full
                   indexer scores over 262144 entries, then the pool of 2048
                   blocks x 8 positions built from them (no attention)
+6. reuse-swa-128k reuse-128k plus the sliding-window branch: 128 FP8 window
+                  rows per sequence (RMS-normalised N(0,1) latents, one
+                  power-of-two scale per row) merged with the sparse result
 """
 
 from dataclasses import dataclass
@@ -38,7 +41,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    mode: str            # "full" | "reindex" | "reuse" | "prefill_full" | "pool_build"
+    mode: str            # "full" | "reindex" | "reuse" | "prefill_full" | "pool_build" | "reuse_swa"
     B: int               # decode queries (sequences) per step
     N: int               # compressed entries per sequence (cache capacity)
     d_c: int             # FP4 latent channels
@@ -53,6 +56,7 @@ class Workload:
     n_blocks: int = 2048  # pool blocks drawn per sequence
     prefill_rows: int = 0
     prefill_row0: int = 0
+    window: int = 0      # sliding-window rows per sequence (FP8)
 
     @property
     def sm_scale(self) -> float:
@@ -78,6 +82,8 @@ WORKLOADS = [
              K=512, seed=4, prefill_rows=8192, prefill_row0=262144 - 8192),
     Workload("pool-build-1m", "pool_build", B=32, N=262144, d_c=512, d_r=64, H=64, H_I=8, D_I=128, K=512,
              seed=5),
+    Workload("reuse-swa-128k", "reuse_swa", B=128, N=32768, d_c=512, d_r=64, H=64, H_I=8, D_I=128, K=512,
+             seed=6, window=128),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
