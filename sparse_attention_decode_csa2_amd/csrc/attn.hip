@@ -983,14 +983,33 @@ __global__ __launch_bounds__(256) void swa_attn_kernel(
 
   // ---- query heads h0 + n as B operands: latent k-step t -> channels
   // 128 g + 8 t .. + 7, RoPE k-step t -> channels d_c + 16 g + 8 t .. + 7
-  const bool hv = h0 + n < H;
   u32x4 qraw[KSL + KSR];
   {
-    const uint16_t* qrow = q + (b * H + (hv ? h0 + n : 0)) * (DC + DR);
+    // the 16 query rows, fetched once per workgroup as contiguous 16-byte
+    // pieces into the value tile (free until the first tile), then read in
+    // the operand layout (rows of heads >= H are zero)
+    constexpr int QP = (DC + DR) / 8, QPITCH = DC + DR + 8, QN = (16 * QP + 255) / 256;
+    static_assert(16 * QPITCH * 2 <= (int)sizeof(sK), "query staging fits the value tile");
+    uint16_t* qs = reinterpret_cast<uint16_t*>(&sK[0][0]);
+    u32x4 qv[QN];
+#pragma unroll
+    for (int k = 0; k < QN; ++k) {
+      const int pc = tid + 256 * k, row = pc / QP, col = pc - row * QP;
+      const bool ok = pc < 16 * QP && h0 + row < H;
+      qv[k] = ok ? *reinterpret_cast<const u32x4*>(q + (b * H + h0 + row) * (DC + DR) + 8 * col)
+                 : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < QN; ++k) {
+      const int pc = tid + 256 * k, row = pc / QP, col = pc - row * QP;
+      if (pc < 16 * QP) *reinterpret_cast<u32x4*>(qs + row * QPITCH + 8 * col) = qv[k];
+    }
+    __syncthreads();
+    const uint16_t* qrow = qs + n * QPITCH;
 #pragma unroll
     for (int t = 0; t < KSL + KSR; ++t) {
       const int off = t < KSL ? 128 * g + 8 * t : DC + 16 * g + 8 * (t - KSL);
-      qraw[t] = hv ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0u, 0u, 0u, 0u};
+      qraw[t] = *reinterpret_cast<const u32x4*>(qrow + off);
     }
   }
   f16x8 Bq[KSL];
