@@ -188,8 +188,10 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
  * sigma    f32 [capacity]  out: the row scales
  * rope_dst bf16 rows of rope_stride bytes (0 = 2 d_r), 16-byte aligned
  * Writes rows [dst_row0, dst_row0 + n_rows) of a window of `capacity` rows.
- * Bit-exact.  Requires d_c % 8 == 0, 8 <= d_c <= 4096, d_r % 8 == 0,
- * 0 <= d_r <= 512, 16-byte aligned x / rope_src, 4-byte aligned sigma.
+ * Bit-exact for finite inputs (an infinite or NaN element gives an
+ * unspecified row, never an out-of-bounds access).  Requires d_c % 8 == 0,
+ * 8 <= d_c <= 4096, d_r % 8 == 0, 0 <= d_r <= 512, 16-byte aligned x /
+ * rope_src, 4-byte aligned sigma.
  */
 int csa2_quantize_fp8(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
                       int32_t d_r, uint8_t* codes, int64_t codes_stride, float* sigma,

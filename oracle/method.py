@@ -266,6 +266,8 @@ def fp8_row_scale_exponent(amax):
     """Smallest integer e with amax <= 448 * 2^e (0 when amax = 0), clamped to
     [-126, 127] so that 2^e is a normal fp32 number."""
     amax = np.asarray(amax, dtype=np.float64)
+    if not np.all(np.isfinite(amax)):
+        raise ValueError("FP8 rows must be finite")
     e = np.zeros(amax.shape, dtype=np.int64)
     for idx in np.ndindex(amax.shape):
         a = float(amax[idx])
