@@ -829,11 +829,11 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
   if (lse && threadIdx.x == 0) lse[row] = L > 0.f ? (m + __log2f(L)) * LN2 : -INFINITY;
 }
 
-// Heads per workgroup: 32 (two head groups, eight waves) for the 512-channel
+// Heads per workgroup: 32 (score waves and value waves) for the 512-channel
 // latent when the batch alone gives a workgroup per CU that way, else 16.
-// Measured: the pair kernel is faster unsplit (batch 128: 31.8 vs 34.7 us)
-// but slower wherever slices are needed (batch 1: 14.5 vs 11.3 us), where
-// the per-workgroup latency path rather than the CU's throughput sets the time.
+// Measured: the 32-head kernel is faster unsplit (batch 128: 25.6 vs 34.7 us)
+// but slower where slices are needed (batch 1: 12.1 vs 10.8 us), where the
+// per-workgroup latency path rather than the CU's throughput sets the time.
 static int attn_heads_per_wg(int B, int H, int d_c) {
   return (d_c == 512 && H > 16 && (int64_t)B * ((H + 31) / 32) >= 256) ? 32 : 16;
 }

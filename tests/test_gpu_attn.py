@@ -144,14 +144,14 @@ def test_attention_every_e4m3_scale_byte(H, B):
 
 
 @pytest.mark.parametrize("H,dr,K", [(64, 64, 512), (64, 64, 200), (48, 64, 130), (64, 0, 512), (64, 64, 1000)])
-def test_attention_paired_head_groups(H, dr, K):
+def test_attention_32_heads_per_workgroup(H, dr, K):
     """Batches large enough for 32 heads per workgroup (score waves that
     dequantise each entry once for 32 heads, value waves on the previous
     tile): masked, out-of-range and repeated ids, an empty row, ragged K, a
-    partial head pair, and K = 1000 (two slices merged by the combine)."""
+    partial second head group, and K = 1000 (two slices merged by the combine)."""
     B = 260 if H == 48 else 130
     wl = W.WORKLOADS[3].scaled(H=H, d_r=dr)
-    note(f"attn: paired B={B} H={H} d_r={dr} K={K}")
+    note(f"attn: 32 heads per workgroup B={B} H={H} d_r={dr} K={K}")
     rng = np.random.default_rng(H + dr + K)
     N = 1024
     idx = _rand_idx(rng, B, K, N)
