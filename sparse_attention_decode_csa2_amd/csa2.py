@@ -100,7 +100,7 @@ def _row_stride(t, elem_bytes, name):
     if t.stride(-1) != 1:
         raise ValueError(f"{name}: the channel dimension must be contiguous")
     rs = t.stride(-2)
-    if t.dim() == 3 and t.shape[0] > 1 and t.stride(0) != t.shape[1] * rs:
+    if t.dim() == 3 and t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) != t.shape[1] * rs:
         raise ValueError(f"{name}: sequences must be evenly spaced rows")
     return rs * elem_bytes
 

@@ -136,3 +136,25 @@ def test_window_merged_with_sparse_branch(H, d_r):
     ro, rl = oracle.merge_branches(ro1, rl1, ro2, rl2)
     attn_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
     assert torch.equal(out[2], o_keep[2]) and torch.equal(lse[2], l_keep[2])
+
+
+def test_window_of_zero_rows_and_full_windows_without_n_win():
+    """W_cap = 0 (no window buffers at all): the merge returns the sparse
+    result bit for bit; n_win omitted: every row of the window is used."""
+    B, H = 3, 64
+    note("swa: W_cap = 0 with merge; n_win omitted")
+    q = W.attn_query(W.WORKLOADS[3].scaled(B=B, H=H), DEV)
+    mo = torch.randn(B, H, 512, device=DEV)
+    ml = torch.randn(B, H, device=DEV)
+    empty = torch.empty(B, 0, 512, dtype=torch.uint8, device=DEV)
+    out, lse = csa2.csa2_swa_attn_fp8(q, empty, torch.empty(B, 0, device=DEV),
+                                      torch.empty(B, 0, 64, dtype=torch.bfloat16, device=DEV), 1 / 24,
+                                      merge_out=mo, merge_lse=ml)
+    torch.cuda.synchronize()
+    assert torch.equal(out, mo) and torch.equal(lse, ml)
+    codes, sigma, rope = _window(B, 96, 64, 81)
+    out2, lse2 = csa2.csa2_swa_attn_fp8(q, codes, sigma, rope, 1 / 24)
+    torch.cuda.synchronize()
+    ro, rl = oracle.swa_attn(np_bits(q), codes.cpu().numpy(), sigma.cpu().numpy().astype(np.float64),
+                             np_bits(rope.contiguous()), None, 1 / 24)
+    attn_close(out2.cpu().numpy(), lse2.cpu().numpy(), ro, rl)
