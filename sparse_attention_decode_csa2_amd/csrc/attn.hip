@@ -420,15 +420,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 // score 16 entries of a 64-entry tile against all 32 heads (the dequantised
 // words are the A operand of two 16x16x32 products, one per head group, so
 // each entry is converted once for 32 heads), store the fp16 values to the
-// value tile and write their softmax numerators P against their own maximum,
-// with that (max, sum) per head.  Waves 4-7 ("value waves") each own 128
-// latent channels of all 32 heads and run P . V on the previous tile with
-// 32x32x16 products (each value element read from LDS once per workgroup):
-// they merge the four (max, sum) pairs of a head, rescale the running output
-// and scale each score wave's P by exp2(its max - new max) as it enters the
-// product.  Tile t is scored while tile t - 1 is multiplied, from two value
-// buffers, so one barrier per tile separates the roles and the two kinds of
-// work of a SIMD (one wave of each role) overlap.
+// value tile and their base-2 logits to the score rows.  Waves 4-7 ("value
+// waves") each own 128 latent channels of all 32 heads and work on the
+// previous tile: each lane takes half of one head's 64 logits, the pair of
+// lanes of a head agrees on the new maximum, and the exponentials become the
+// A operand of the 32x32x16 value products straight from registers (each
+// value element is read from LDS once per workgroup).  Tile t is scored while
+// tile t - 1 is multiplied, from two buffers, so one barrier per tile
+// separates the roles and the two kinds of work of a SIMD (one wave of each
+// role) overlap.
 template <int DR>
 __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
@@ -440,13 +440,12 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   constexpr int KSR = DR / 32;           // RoPE k-steps
   constexpr int KS = KSL + KSR;
   constexpr int LDK = DC + 16;           // fp16 pitch of the value tile
-  constexpr int PP = AT_TILE + 8;        // fp16 pitch of the P rows
+  constexpr int SP = AT_TILE + 4;        // fp32 pitch of the score rows
   using GR = GatherRegs<DC, DR>;
   constexpr int NCW = GR::NCW, RW = GR::RW;
   static_assert(4 * NCW == KSL && (DR == 0 || RW == KSR), "gather layout = MFMA k-steps");
   __shared__ __attribute__((aligned(16))) _Float16 sV[2][AT_TILE][LDK];
-  __shared__ __attribute__((aligned(16))) _Float16 sP[2][32][PP];
-  __shared__ __attribute__((aligned(16))) float sML[2][32][4][2];  // buffer, head, score wave: (max, sum)
+  __shared__ __attribute__((aligned(16))) float sS[2][32][SP];     // buffer, head, entry: base-2 logits
   __shared__ __attribute__((aligned(16))) float sHd[4][2][32];     // value wave: per-head broadcast
   __shared__ float sFs[32];                                        // per head: MFMA result -> base-2 logit
   __shared__ int32_t sIdx[AT_IDS_PAD];
@@ -568,29 +567,16 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
         c0 = mfma16x16x32_bf16(rv, Br[0][t], c0);
         c1 = mfma16x16x32_bf16(rv, Br[1][t], c1);
       }
-      // c_k[i] = S^T[entry 16 w + 4 g + i][head hq0 + 16 k + n]
+      // c_k[i] = S^T[entry 16 w + 4 g + i][head hq0 + 16 k + n]: base-2 logits
+      // (-inf for a masked entry) to the score rows of the value waves
       const uint64_t vb = __ballot(g == 0 && gr.valid);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const f32x4 c = k ? c1 : c0;
-        float s2[4];
+        f32x4 sv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s2[i] = ((vb >> (4 * g + i)) & 1u) ? c[i] * fscale[k] : -INFINITY;
-        float mt = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-        mt = fmaxf(mt, xor16f(mt));
-        mt = fmaxf(mt, xor32f(mt));
-        const float mt_ref = mt == -INFINITY ? 0.f : mt;  // masked scores give exp2(-inf) = 0
-        float p[4], ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(s2[i] - mt_ref);
-          ps += p[i];
-        }
-        ps += xor16f(ps);
-        ps += xor32f(ps);
-        if (g == 0) *reinterpret_cast<float2*>(&sML[buf][16 * k + n][w][0]) = float2{mt, ps};
-        *reinterpret_cast<f16x4*>(&sP[buf][16 * k + n][16 * w + 4 * g]) =
-            f16x4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+        for (int i = 0; i < 4; ++i) sv[i] = ((vb >> (4 * g + i)) & 1u) ? c[i] * fscale[k] : -INFINITY;
+        *reinterpret_cast<f32x4*>(&sS[buf][16 * k + n][16 * w + 4 * g]) = sv;
       }
     };
 
@@ -688,20 +674,34 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
 
   auto pv = [&](int buf) {
     _Float16 (*tk)[LDK] = sV[buf];
-    const f32x4 ml01 = *reinterpret_cast<const f32x4*>(&sML[buf][hl][0][0]);
-    const f32x4 ml23 = *reinterpret_cast<const f32x4*>(&sML[buf][hl][2][0]);
-    const float mw[4] = {ml01[0], ml01[2], ml23[0], ml23[2]};
-    const float sw[4] = {ml01[1], ml01[3], ml23[1], ml23[3]};
-    const float m_new = fmaxf(m_run, fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3])));
-    const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // nothing valid yet: O = l = 0
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    float fw[4], l_tile = 0.f;
+    // ---- softmax of head hl over the tile: this lane holds entries 16 u +
+    // 8 kh + 0..7 (u < 4), its partner lane hl + 32 the other half
+    f32x4 sv[8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      fw[u] = __builtin_amdgcn_exp2f(mw[u] - m_ref);
-      l_tile += fw[u] * sw[u];
+      sv[2 * u] = *reinterpret_cast<const f32x4*>(&sS[buf][hl][16 * u + 8 * kh]);
+      sv[2 * u + 1] = *reinterpret_cast<const f32x4*>(&sS[buf][hl][16 * u + 8 * kh + 4]);
     }
-    l_run = l_run * alpha + l_tile;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mt = fmaxf(mt, fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])));
+    mt = fmaxf(mt, xor32f(mt));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // nothing valid yet: O = l = 0
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    f16x8 a[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(sv[2 * u + (j >> 2)][j & 3] - m_ref);
+        ps += p;
+        a[u][j] = (_Float16)p;
+      }
+    }
+    ps += xor32f(ps);
+    l_run = l_run * alpha + ps;
     m_run = m_new;
     // alpha of the heads whose output rows this lane holds: 8 q + 4 kh + 0..3
     if (kh == 0) sHd[r][0][hl] = alpha;
@@ -714,8 +714,6 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
       for (int i = 0; i < 16; ++i) acc[k][i] *= al[i >> 2][i & 3];
 #pragma unroll
     for (int u = 0; u < AT_TILE / 16; ++u) {
-      // k-step u = the 16 entries of score wave u, rescaled to the common maximum
-      const f16x8 a = *reinterpret_cast<const f16x8*>(&sP[buf][hl][16 * u + 8 * kh]) * (_Float16)fw[u];
       const int r0 = 16 * u + 8 * (G >> 1) + tr_r, r1 = r0 + 4;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -723,7 +721,7 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
         const f16x4 v0 = tr16_read(&tk[r0][tile_col(r0, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
         const f16x4 v1 = tr16_read(&tk[r1][tile_col(r1, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
         const f16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[k] = mfma32x32x16_f16(a, bv, acc[k]);
+        acc[k] = mfma32x32x16_f16(a[u], bv, acc[k]);
       }
     }
   };
