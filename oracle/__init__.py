@@ -35,6 +35,9 @@ Parity status per function (the pins live in ``tests/test_oracle_*.py``):
   over the built pool reproducing the Full-mode Top-K).
 * sparse_attn: pinned (dense float64 SDPA when Top-K covers every entry,
   closed-form special cases, logsumexp).
+* sample: pinned (hand-derived draws, the token frequencies over a grid of
+  uniforms against scipy's softmax, the nucleus' minimality, greedy and
+  single-candidate limits).
 """
 
 from .codec import (  # noqa: F401
@@ -60,6 +63,7 @@ from .method import (  # noqa: F401
     dequantize_fp8,
     swa_attn,
     merge_branches,
+    sample,
     decode_full,
     decode_reindex,
     decode_reuse,

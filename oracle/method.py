@@ -21,6 +21,8 @@ reading taken is stated at the function and listed in the design doc):
        (MLA-style: one latent shared by all heads; the key is [latent ; RoPE
        part], the value is the latent).  Reuse mode is this stage alone with
        the index list handed in [P1 CSA2; P3; P4].
+   ``sample``        - the decode sampler on the same Top-K: temperature,
+       top-p nucleus, inverse-CDF draw [P3 DeepSelect; P1 sampling settings].
 """
 
 import numpy as np
@@ -387,3 +389,75 @@ def decode_reindex(q_idx_bits, w, k_idx_bits, n_valid, pool_blocks, n_blocks, bl
 def decode_reuse(idx, q_bits, codes, scales, rope_bits, sm_scale):
     """Reuse mode: the index list is handed in; attention only."""
     return sparse_attn(q_bits, codes, scales, rope_bits, idx, sm_scale)
+
+
+# ------------------------------------------------------------ the sampler
+
+
+def sample(logits, K, temperature, top_p, u):
+    """One token drawn per row by the decode sampler built on the Top-K
+    selection [P3 DeepSelect paragraph: one Top-K implementation serves the
+    sparse attention and the sampler; P1 interface paragraph: the recommended
+    sampling settings name a temperature and a top_p].
+
+    The pages name the knobs, not their order.  Reading taken:
+    1. the candidates are the row's Top-K (logit descending, token id
+       ascending), as ``topk`` returns them;
+    2. weight w_i = exp((l_i - l_0) / T) for the i-th candidate, l_0 the
+       largest logit (a -inf logit and an empty slot weigh 0); the candidate
+       probabilities are w_i / sum(w), normalised over the K candidates;
+    3. the nucleus is the shortest prefix of that order whose probability
+       reaches top_p; every candidate when top_p >= 1 or when no prefix
+       reaches top_p;
+    4. the draw takes the uniform u in [0, 1) as an input and returns the
+       first position of the nucleus whose running weight exceeds u times the
+       nucleus weight (if rounding leaves none, the last position of nonzero
+       weight).
+    A row whose largest logit is -inf draws its first candidate.
+
+    logits float [B, V]; u float [B].  Returns (token int32 [B], prob float64
+    [B] = w_pos / nucleus weight, n_kept int32 [B], pos int32 [B], idx int32
+    [B, K] the candidates, w float64 [B, K] their weights).
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    B = logits.shape[0]
+    idx, s = topk(logits, None, None, K)
+    u = np.asarray(u, dtype=np.float64).reshape(B)
+    w = np.zeros((B, K))
+    token = np.zeros(B, dtype=np.int32)
+    prob = np.ones(B)
+    n_kept = np.ones(B, dtype=np.int32)
+    pos = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n_cand = int((idx[b] >= 0).sum())
+        token[b] = idx[b, 0]
+        if s[b, 0] == -np.inf:
+            continue
+        for i in range(n_cand):
+            if s[b, i] != -np.inf:
+                w[b, i] = np.exp((s[b, i] - s[b, 0]) / temperature)
+        total = w[b].sum()
+        n = n_cand
+        if top_p < 1.0:
+            mass = 0.0
+            for i in range(n_cand):
+                mass += w[b, i] / total
+                if mass >= top_p:
+                    n = i + 1
+                    break
+        nucleus = w[b, :n].sum()
+        target = u[b] * nucleus
+        run = 0.0
+        p = -1
+        for i in range(n):
+            run += w[b, i]
+            if run > target:
+                p = i
+                break
+        if p < 0:
+            p = max(i for i in range(n) if w[b, i] > 0)
+        n_kept[b] = n
+        pos[b] = p
+        token[b] = idx[b, p]
+        prob[b] = w[b, p] / nucleus
+    return token, prob, n_kept, pos, idx, w

@@ -593,6 +593,83 @@ def check_merge_is_one_softmax_over_the_union():
     assert np.all(oz == 0) and np.all(np.isneginf(lz))
 
 
+# ------------------------------------------------------------------ sampler
+
+
+def _sample_records():
+    out = []
+    for rec in _records("sampler_rows.txt"):
+        a = rec.index("|")
+        b = rec.index("|", a + 1)
+        K, T, top_p, u = int(rec[0]), float(rec[1]), float(rec[2]), float(rec[3])
+        logits = np.array([float(v) for v in rec[a + 1:b]])
+        tok, n, pos, prob = int(rec[b + 1]), int(rec[b + 2]), int(rec[b + 3]), float(rec[b + 4])
+        out.append((K, T, top_p, u, logits, tok, n, pos, prob))
+    return out
+
+
+def check_sample_golden():
+    """Hand-derived draws (tests/golden/sampler_rows.txt)."""
+    for K, T, top_p, u, logits, tok, n, pos, prob in _sample_records():
+        t, p, nk, ps, _, _ = oracle.sample(logits[None], K, T, top_p, [u])
+        assert (int(t[0]), int(nk[0]), int(ps[0])) == (tok, n, pos), (logits, K, T, top_p, u, t, nk, ps)
+        assert abs(float(p[0]) - prob) <= 1e-15, (logits, p, prob)
+
+
+def check_sample_frequencies_vs_softmax():
+    """With every token a candidate and top_p = 1, the draws over a uniform
+    grid of u give each token the share scipy's softmax of logits / T gives
+    it (within one grid step), and the most likely tokens come first in u."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(61)
+    V, T, G = 12, 0.7, 6000
+    logits = rng.standard_normal(V) * 2.0
+    u = (np.arange(G) + 0.5) / G
+    tok, _, _, _, _, _ = oracle.sample(np.tile(logits, (G, 1)), V, T, 1.0, u)
+    want = softmax(logits / T)
+    freq = np.bincount(tok, minlength=V) / G
+    assert np.all(np.abs(freq - want) <= 1.0 / G + 1e-12), (freq, want)
+    assert np.all(np.diff(want[tok]) <= 0)                  # along u: most likely first
+
+
+def check_sample_nucleus_is_minimal():
+    """The nucleus is the shortest most-probable prefix reaching top_p, with
+    the candidate probabilities from scipy's softmax over the K largest
+    logits / T (numpy sort); the reported probability is the drawn token's
+    share of the nucleus."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(62)
+    B, V, K, T = 60, 40, 16, 0.8
+    logits = rng.standard_normal((B, V)) * 1.5
+    top_p = rng.uniform(0.05, 0.99, size=B)
+    u = rng.random(B)
+    for b in range(B):
+        tok, prob, n, pos, _, _ = oracle.sample(logits[b][None], K, T, float(top_p[b]), u[b:b + 1])
+        order = np.argsort(-logits[b], kind="stable")[:K]
+        P = softmax(logits[b, order] / T)
+        n, pos = int(n[0]), int(pos[0])
+        assert P[:n].sum() >= top_p[b] - 1e-12 and P[:n - 1].sum() < top_p[b] + 1e-12, (b, n)
+        assert 0 <= pos < n and int(tok[0]) == int(order[pos])
+        assert abs(float(prob[0]) - P[pos] / P[:n].sum()) <= 1e-12
+        assert P[:pos].sum() / P[:n].sum() <= u[b] + 1e-12 < P[:pos + 1].sum() / P[:n].sum() + 2e-12
+
+
+def check_sample_limits():
+    """K = 1 and a vanishing temperature draw the largest logit (lower id on
+    ties) with probability 1, whatever u is."""
+    rng = np.random.default_rng(63)
+    logits = np.round(rng.standard_normal((20, 30)) * 3)      # integer logits: ties, gaps >= 1
+    for u in (0.0, 0.5, 0.999999):
+        uu = np.full(20, u)
+        want = np.argmax(logits, axis=1)                        # first maximum = lower id
+        t1, p1, n1, _, _, _ = oracle.sample(logits, 1, 1.0, 1.0, uu)
+        assert np.array_equal(t1, want) and np.all(p1 == 1.0) and np.all(n1 == 1)
+        distinct = logits.copy()
+        distinct[np.arange(20), want] += 0.5                    # a unique maximum, gap >= 0.5
+        t0, p0, _, _, _, _ = oracle.sample(distinct, 8, 1e-3, 1.0, uu)
+        assert np.array_equal(t0, want) and np.all(p0 == 1.0)
+
+
 ALL_PINS = [
     check_e2m1_value_set, check_e4m3_decode, check_e4m3_encode_vs_torch, check_scale_code_vs_torch,
     check_e2m1_encode_vs_numpy_round, check_bf16_decode, check_quantize_golden,
@@ -602,4 +679,6 @@ ALL_PINS = [
     check_topk_invariants, check_attn_dense_vs_sdpa, check_attn_special_cases, check_decode_modes_compose,
     check_pool_golden, check_pool_bruteforce, check_pool_reindex_reproduces_full_topk,
     check_fp8_golden, check_fp8_vs_torch_cast, check_swa_vs_sdpa, check_merge_is_one_softmax_over_the_union,
+    check_sample_golden, check_sample_frequencies_vs_softmax, check_sample_nucleus_is_minimal,
+    check_sample_limits,
 ]

@@ -24,6 +24,7 @@ _orig_build_pool = method.build_pool
 _orig_fp8_exp = method.fp8_row_scale_exponent
 _orig_swa = method.swa_attn
 _orig_merge = method.merge_branches
+_orig_sample = method.sample
 
 
 def _swap_nibbles(x_bits):
@@ -137,6 +138,66 @@ def _merge_base2(out_a, lse_a, out_b, lse_b):
     return _orig_merge(out_a, np.asarray(lse_a) * np.log(2.0), out_b, np.asarray(lse_b) * np.log(2.0))
 
 
+def _sample_generic(logits, K, temperature, top_p, u, weight, reach, exceeds, over_vocab=False):
+    """The sampler written with one step replaceable (for the plants below)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    B = logits.shape[0]
+    idx, sc = _orig_topk(logits, None, None, K)
+    u = np.asarray(u, dtype=np.float64).reshape(B)
+    w = np.zeros((B, K))
+    tok = np.zeros(B, dtype=np.int32)
+    prob = np.ones(B)
+    nk = np.ones(B, dtype=np.int32)
+    pos = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        nc = int((idx[b] >= 0).sum())
+        tok[b] = idx[b, 0]
+        if sc[b, 0] == -np.inf:
+            continue
+        w[b, :nc] = [weight(sc[b, i], sc[b, 0], temperature) if sc[b, i] != -np.inf else 0.0 for i in range(nc)]
+        total = np.exp((logits[b] - sc[b, 0]) / temperature).sum() if over_vocab else w[b].sum()
+        n = nc
+        if top_p < 1.0:
+            cum = np.cumsum(w[b, :nc]) / total
+            hit = [i for i in range(nc) if reach(cum[i], top_p)]
+            n = hit[0] + 1 if hit else nc
+        nuc = w[b, :n].sum()
+        run = np.cumsum(w[b, :n])
+        hit = [i for i in range(n) if exceeds(run, i, u[b] * nuc)]
+        p = hit[0] if hit else max(i for i in range(n) if w[b, i] > 0)
+        nk[b], pos[b], tok[b], prob[b] = n, p, idx[b, p], w[b, p] / nuc
+    return tok, prob, nk, pos, idx, w
+
+
+_W = lambda l, l0, T: np.exp((l - l0) / T)          # noqa: E731
+_REACH = lambda c, p: c >= p                         # noqa: E731
+_EXCEEDS = lambda run, i, t: run[i] > t              # noqa: E731
+
+
+def _sample_temperature_multiplies(*a):
+    # plant: logits multiplied by the temperature instead of divided
+    return _sample_generic(*a, lambda l, l0, T: np.exp((l - l0) * T), _REACH, _EXCEEDS)
+
+
+def _sample_nucleus_strict(*a):
+    # plant: the nucleus must exceed top_p instead of reaching it
+    return _sample_generic(*a, _W, lambda c, p: c > p, _EXCEEDS)
+
+
+def _sample_draw_exclusive(*a):
+    # plant: the draw compares the weight before a position, not through it
+    return _sample_generic(*a, _W, _REACH, lambda run, i, t: (run[i - 1] if i else 0.0) > t)
+
+
+def _sample_probs_over_vocab(*a):
+    # plant: top_p measured against the whole vocabulary instead of the K candidates
+    return _sample_generic(*a, _W, _REACH, _EXCEEDS, over_vocab=True)
+
+
+def _sample_unmutated(*a):
+    return _sample_generic(*a, _W, _REACH, _EXCEEDS)
+
+
 MUTATIONS = {
     "nibble_order_swapped": [(method, "quantize_fp4", _swap_nibbles), (oracle, "quantize_fp4", _swap_nibbles)],
     "e2m1_ties_away": [(method, "e2m1_encode_magnitude", _ties_away), (oracle, "e2m1_encode_magnitude", _ties_away)],
@@ -155,6 +216,12 @@ MUTATIONS = {
                                  (oracle, "fp8_row_scale_exponent", _fp8_scale_one_lower)],
     "window_drops_rope": [(method, "swa_attn", _swa_no_rope), (oracle, "swa_attn", _swa_no_rope)],
     "merge_weights_base2": [(method, "merge_branches", _merge_base2), (oracle, "merge_branches", _merge_base2)],
+    "sample_temperature_multiplies": [(method, "sample", _sample_temperature_multiplies),
+                                      (oracle, "sample", _sample_temperature_multiplies)],
+    "sample_nucleus_strict": [(method, "sample", _sample_nucleus_strict), (oracle, "sample", _sample_nucleus_strict)],
+    "sample_draw_exclusive": [(method, "sample", _sample_draw_exclusive), (oracle, "sample", _sample_draw_exclusive)],
+    "sample_probs_over_vocab": [(method, "sample", _sample_probs_over_vocab),
+                                (oracle, "sample", _sample_probs_over_vocab)],
 }
 
 
@@ -169,3 +236,13 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+def test_sampler_plant_harness_is_faithful(monkeypatch):
+    """The replaceable sampler above, unmutated, passes every pin (so each
+    plant is caught for its planted step, not for the harness)."""
+    monkeypatch.setattr(method, "sample", _sample_unmutated)
+    monkeypatch.setattr(oracle, "sample", _sample_unmutated)
+    for pin in P.ALL_PINS:
+        if "sample" in pin.__name__:
+            pin()
