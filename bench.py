@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="full-64k",
                     help="full-64k (default, the reported line); others for supplementary runs: "
-                         "tiny-full, reindex-1m, reuse-128k, prefill-full-1m, pool-build-1m, reuse-swa-128k")
+                         "tiny-full, reindex-1m, reuse-128k, prefill-full-1m, pool-build-1m, reuse-swa-128k, "
+                         "sample-129k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -83,6 +84,7 @@ class Step:
     Prefill + Full (prefill-full-1m): quantize (append 8192 rows) -> index -> topk -> attn.
     Pool construction (pool-build-1m): index (Full scores) -> build (the Reindex pool).
     Reuse + window (reuse-swa-128k): attn -> swa (the FP8 window branch merged in).
+    Sampler (sample-129k): topk (over the vocabulary logits) -> draw; sets = logits + uniforms.
     """
 
     def __init__(self, wl, dev, rotation_bytes=ROTATION_BYTES):
@@ -92,6 +94,9 @@ class Step:
         self.wl, self.csa2, self.W, self.dev = wl, csa2, W, dev
         B, N = wl.B, wl.N
         self.mode = wl.mode
+        if self.mode == "sample":
+            self._init_sample(wl, dev)
+            return
         if self.mode == "full":
             per_set = B * N * (wl.D_I * 2 + _entry_bytes(wl))
             self.R = max(2, math.ceil(rotation_bytes / per_set))
@@ -155,6 +160,40 @@ class Step:
         if self.mode in ("reuse", "reuse_swa"):
             self.idx = None
 
+    def _init_sample(self, wl, dev):
+        import torch
+        csa2, W = self.csa2, self.W
+        B, V, K = wl.B, wl.N, wl.K
+        self.R = max(2, math.ceil(ROTATION_BYTES / (B * V * 4)))
+        self.sets = []
+        for r in range(self.R):
+            ws = wl.scaled(seed=wl.seed * 1000 + r)
+            self.sets.append({"logits": W.vocab_logits(ws, dev), "u": W.sampler_uniforms(ws, dev)})
+        self.M = V
+        self.scores = self.sets[0]["logits"]
+        self.idx = torch.empty(B, K, dtype=torch.int32, device=dev)
+        self.top = torch.empty(B, K, dtype=torch.float32, device=dev)
+        tk = csa2.csa2_topk_workspace_bytes(B, V, K)
+        self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
+        self.token = torch.empty(B, dtype=torch.int32, device=dev)
+        self.prob = torch.empty(B, dtype=torch.float32, device=dev)
+        self.n_kept = torch.empty(B, dtype=torch.int32, device=dev)
+        self.stages = ["topk", "draw"]
+
+    def draw(self, r):
+        wl = self.wl
+        self.csa2.csa2_sample_draw(self.idx, self.top, wl.temperature, wl.top_p, self.sets[r]["u"],
+                                   token=self.token, prob=self.prob, n_kept=self.n_kept)
+
+    def torch_sampler(self, r):
+        """The same draw in eager torch ops (speed reference; top_p = 1 only)."""
+        import torch
+        wl = self.wl
+        vals, ids = torch.topk(self.sets[r]["logits"], wl.K, dim=1)
+        c = torch.cumsum(torch.softmax(vals / wl.temperature, dim=1), dim=1)
+        pos = torch.searchsorted(c, self.sets[r]["u"][:, None] * c[:, -1:], right=True)
+        return ids.gather(1, pos.clamp(max=wl.K - 1))
+
     def _cache(self, ws):
         import torch
         W, csa2, dev = self.W, self.csa2, self.dev
@@ -201,6 +240,10 @@ class Step:
                                   n_blocks=self.nb_out, workspace=self.ws_build)
 
     def topk(self, r):
+        if self.mode == "sample":
+            self.csa2.csa2_topk(self.sets[r]["logits"], self.wl.K, out_idx=self.idx, out_score=self.top,
+                                workspace=self.ws_topk)
+            return
         ids = self.positions if self.mode == "reindex" else None
         self.csa2.csa2_topk(self.scores, self.wl.K, ids=ids, out_idx=self.idx, out_score=self.top,
                             workspace=self.ws_topk)
@@ -226,6 +269,9 @@ class Step:
         once, outputs written once."""
         wl = self.wl
         B, N, K, H = wl.B, wl.N, wl.K, wl.H
+        if self.mode == "sample":
+            # logits read once; uniform in, token + prob + n_kept out; candidates (ids + logits) between stages
+            return {"topk": B * (N * 4 + K * 8), "draw": B * (K * 8 + 4 + 12), "step": B * (N * 4 + 4 + 12)}
         ent = _entry_bytes(wl)
         qi = wl.H_I * wl.D_I * 2
         attn = B * (K * 4 + K * ent + H * wl.D * 2 + H * wl.d_c * 4 + H * 4)
@@ -350,7 +396,12 @@ def main():
     stage_us = {s: 1000.0 * timed(g_stage[s]) / args.steps for s in stages}
     # the same selection by torch.topk (speed reference only: its order among
     # equal scores is unspecified), K launches on the stage's own score rows
-    torch_topk_us = None
+    torch_topk_us = torch_sampler_us = None
+    if wl.mode == "sample" and wl.top_p >= 1.0:
+        g_ts = capture(step.torch_sampler, args.steps)
+        g_ts.replay()
+        torch_sampler_us = 1000.0 * timed(g_ts) / args.steps
+        del g_ts
     if "topk" in stages:
         g_tt = capture(lambda r: torch.topk(step.scores, wl.K, dim=1), args.steps)
         g_tt.replay()
@@ -370,7 +421,7 @@ def main():
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
     kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
-                   "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip"}[dom]
+                   "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip"}[dom]
     achieved = alg[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = committed_traffic(kernel_file, wl.name)
 
@@ -384,9 +435,11 @@ def main():
 
     qps = wl.B / (ms_per_step * 1e-3)
     line = {
-        "metric": "decode queries/s + achieved HBM GB/s (% of peak), CSA2 FP4 sparse attn",
+        "metric": ("decode sampler rows/s + achieved HBM GB/s (% of peak), Top-K + top-p draw"
+                   if wl.mode == "sample" else
+                   "decode queries/s + achieved HBM GB/s (% of peak), CSA2 FP4 sparse attn"),
         "value": qps,
-        "unit": "queries/s",
+        "unit": "rows/s" if wl.mode == "sample" else "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -394,17 +447,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4(e2m1)+e4m3 cache, bf16/fp16 mfma, fp32 softmax",
-        "data": "synthetic (seeded; integer indexer, RMS-normalised N(0,1) latents)",
-        "config": {"workload": wl.name, "mode": wl.mode, "batch": wl.B, "entries": wl.N,
-                   "context_tokens": wl.N * 4, "latent": wl.d_c, "rope": wl.d_r, "heads": wl.H,
-                   "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "rotation_sets": R},
+        "dtype": ("f32 logits, f32 weights" if wl.mode == "sample" else
+                  "fp4(e2m1)+e4m3 cache, bf16/fp16 mfma, fp32 softmax"),
+        "data": ("synthetic (seeded; N(0,1) x 4 logits, uniform draws)" if wl.mode == "sample" else
+                 "synthetic (seeded; integer indexer, RMS-normalised N(0,1) latents)"),
+        "config": ({"workload": wl.name, "mode": wl.mode, "batch": wl.B, "vocab": wl.N, "top_k": wl.K,
+                    "temperature": wl.temperature, "top_p": wl.top_p, "rotation_sets": R}
+                   if wl.mode == "sample" else
+                   {"workload": wl.name, "mode": wl.mode, "batch": wl.B, "entries": wl.N,
+                    "context_tokens": wl.N * 4, "latent": wl.d_c, "rope": wl.d_r, "heads": wl.H,
+                    "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "rotation_sets": R}),
         "step_hbm_gbs": alg["step"] / (ms_per_step * 1e-3) / 1e9,
         "single_step_us_cold": round(single_step_us, 2),
         "step_alg_bytes": alg["step"],
         "stage_us": {s: round(v, 3) for s, v in stage_us.items()},
         "stage_gbs": {s: round(alg[s] / (stage_us[s] * 1e-6) / 1e9, 1) for s in stages},
         "torch_topk_us": None if torch_topk_us is None else round(torch_topk_us, 3),
+        "torch_sampler_us": None if torch_sampler_us is None else round(torch_sampler_us, 3),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": alg[dom]},

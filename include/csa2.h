@@ -175,6 +175,55 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
               void* workspace, size_t workspace_bytes, csa2_stream_t stream);
 
 /*
+ * The decode sampler on the Top-K selection.  One Top-K implementation serves
+ * the sparse attention and the sampler ([P3] DeepSelect paragraph); sampling
+ * is set by a temperature and a top_p ([P1] interface paragraph).  The order
+ * of the steps is this build's reading, the usual one:
+ *   candidates = the row's K largest logits, in csa2_topk order (logit
+ *                descending, token id ascending);
+ *   w_i        = exp((l_i - l_0) / T) for the i-th candidate (0 for -inf);
+ *   nucleus    = the shortest prefix of the candidates whose weight reaches
+ *                top_p * sum(w) (all candidates when top_p >= 1 or when none
+ *                reaches it);
+ *   token      = the candidate at the first nucleus position whose running
+ *                weight exceeds u * (nucleus weight) (the last position of
+ *                nonzero weight if rounding leaves none);
+ *   prob       = w_token / (nucleus weight), n_kept = nucleus size.
+ * A row whose largest logit is -inf, or whose first slot is empty, reports
+ * its first candidate with prob 1, n_kept 1.  The weights and running sums
+ * are float32, so a token or nucleus end decided by a running weight within
+ * float32 rounding of its threshold may differ from an exact evaluation by
+ * one position; the token is always a candidate of the row.  A +inf or NaN
+ * logit gives an unspecified token of the row.
+ *
+ * csa2_sample_draw: the draw alone, on candidates the caller already holds.
+ * cand_idx   i32 [B, K] candidate token ids in csa2_topk order, -1 = empty
+ *                       slot (empty slots only after the others)
+ * cand_score f32 [B, K] their logits (-inf for empty slots)
+ * u          f32 [B]    the uniforms, in [0, 1), drawn by the caller
+ * token      i32 [B]    out: the drawn token id
+ * prob       f32 [B]    out (nullable): its share of the nucleus weight
+ * n_kept     i32 [B]    out (nullable): the nucleus size
+ * Requires 1 <= K <= 2048, 1e-30 <= T <= 1e30, 0 < top_p (NaN rejected),
+ * 16-byte aligned arrays.
+ */
+int csa2_sample_draw(const int32_t* cand_idx, const float* cand_score, int32_t B, int32_t K, float temperature,
+                     float top_p, const float* u, int32_t* token, float* prob, int32_t* n_kept,
+                     csa2_stream_t stream);
+
+/*
+ * csa2_sample: csa2_topk over the logits f32 [B, V] (row c = token id c),
+ * then csa2_sample_draw, in one call.  The workspace (at least
+ * csa2_sample_workspace_bytes(B, V, K) bytes, 16-byte aligned, caller-owned,
+ * contents not preserved) holds the candidates and the Top-K workspace.
+ * Requires 1 <= V < 2^31; the other arguments as csa2_sample_draw.
+ */
+size_t csa2_sample_workspace_bytes(int32_t B, int64_t V, int32_t K);
+int csa2_sample(const float* logits, int32_t B, int64_t V, int32_t K, float temperature, float top_p,
+                const float* u, int32_t* token, float* prob, int32_t* n_kept, void* workspace,
+                size_t workspace_bytes, csa2_stream_t stream);
+
+/*
  * Sliding-window branch, write: FP8 rows of the window KV.  The window branch
  * keeps its KV in FP8 ([P4] CSA2 paragraph; [P1] 效率组件四件, item 4); the
  * pages give no scale granularity, this build uses one power-of-two scale per

@@ -50,6 +50,9 @@ def load():
         "csa2_swa_attn_fp8": (ctypes.c_int, [P, P, I64, P, P, I64, P, I32, I32, I32, I32, I32, F, P, P, P, P, P]),
         "csa2_build_pool_workspace_bytes": (SZ, [I32, I64, I32, I32]),
         "csa2_build_pool": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, P, P, SZ, P]),
+        "csa2_sample_draw": (ctypes.c_int, [P, P, I32, I32, F, F, P, P, P, P, P]),
+        "csa2_sample_workspace_bytes": (SZ, [I32, I64, I32]),
+        "csa2_sample": (ctypes.c_int, [P, I32, I64, I32, F, F, P, P, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "csa2_sparse_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I64,
                                                 F, P, P, P, SZ, P]),
@@ -212,6 +215,44 @@ def csa2_topk(scores, K, ids=None, n_valid=None, out_idx=None, out_score=None, w
                        _ptr(workspace), ws_bytes, _stream())
     _check("csa2_topk", st)
     return out_idx, out_score
+
+
+# ------------------------------------------------------------------ sampler
+
+
+def csa2_sample_draw(cand_idx, cand_score, temperature, top_p, u, token=None, prob=None, n_kept=None):
+    """Draw over Top-K candidates: cand_idx i32 [B, K], cand_score f32 [B, K],
+    u f32 [B] -> (token i32 [B], prob f32 [B], n_kept i32 [B])."""
+    lib = load()
+    B, K = cand_idx.shape
+    dev = cand_idx.device
+    token = torch.empty(B, dtype=torch.int32, device=dev) if token is None else token
+    prob = torch.empty(B, dtype=torch.float32, device=dev) if prob is None else prob
+    n_kept = torch.empty(B, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    st = lib.csa2_sample_draw(_ptr(cand_idx), _ptr(cand_score), B, K, float(temperature), float(top_p), _ptr(u),
+                              _ptr(token), _ptr(prob), _ptr(n_kept), _stream())
+    _check("csa2_sample_draw", st)
+    return token, prob, n_kept
+
+
+def csa2_sample_workspace_bytes(B, V, K):
+    return int(load().csa2_sample_workspace_bytes(B, V, K))
+
+
+def csa2_sample(logits, K, temperature, top_p, u, token=None, prob=None, n_kept=None, workspace=None):
+    """Top-K over logits f32 [B, V], then the draw: (token, prob, n_kept)."""
+    lib = load()
+    B, V = logits.shape
+    dev = logits.device
+    token = torch.empty(B, dtype=torch.int32, device=dev) if token is None else token
+    prob = torch.empty(B, dtype=torch.float32, device=dev) if prob is None else prob
+    n_kept = torch.empty(B, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    if workspace is None:
+        workspace = torch.empty(max(csa2_sample_workspace_bytes(B, V, K), 16), dtype=torch.uint8, device=dev)
+    st = lib.csa2_sample(_ptr(logits), B, V, K, float(temperature), float(top_p), _ptr(u), _ptr(token),
+                         _ptr(prob), _ptr(n_kept), _ptr(workspace), workspace.numel(), _stream())
+    _check("csa2_sample", st)
+    return token, prob, n_kept
 
 
 # ------------------------------------------------------------------ a4 / a5

@@ -191,6 +191,46 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, i
                                       as_stream(stream)));
 }
 
+static bool sampler_params_ok(float temperature, float top_p) {
+  // 1/T must stay a finite float; top_p > 0 (NaN fails both tests)
+  return temperature >= 1e-30f && temperature <= 1e30f && top_p > 0.0f && top_p <= 1e30f;
+}
+
+int csa2_sample_draw(const int32_t* cand_idx, const float* cand_score, int32_t B, int32_t K, float temperature,
+                     float top_p, const float* u, int32_t* token, float* prob, int32_t* n_kept,
+                     csa2_stream_t stream) {
+  if (B < 0) return CSA2_ERR_SHAPE;
+  if (K < 1 || K > 2048 || !sampler_params_ok(temperature, top_p)) return CSA2_ERR_RANGE;
+  if (B == 0) return CSA2_OK;
+  if (!cand_idx || !cand_score || !u || !token) return CSA2_ERR_NULL;
+  if (!aligned16(cand_idx) || !aligned16(cand_score) || !aligned16(u) || !aligned16(token) ||
+      !opt_aligned16(prob) || !opt_aligned16(n_kept))
+    return CSA2_ERR_ALIGN;
+  return hip_status(csa2::launch_sample_draw(cand_idx, cand_score, B, K, temperature, top_p, u, token, prob,
+                                             n_kept, as_stream(stream)));
+}
+
+size_t csa2_sample_workspace_bytes(int32_t B, int64_t V, int32_t K) {
+  if (B <= 0 || V < 1 || V > 0x7FFFFFFFll || K < 1 || K > 2048) return 0;
+  return csa2::sample_workspace_bytes(B, V, K);
+}
+
+int csa2_sample(const float* logits, int32_t B, int64_t V, int32_t K, float temperature, float top_p,
+                const float* u, int32_t* token, float* prob, int32_t* n_kept, void* workspace,
+                size_t workspace_bytes, csa2_stream_t stream) {
+  if (B < 0 || V < 1 || V > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
+  if (K < 1 || K > 2048 || !sampler_params_ok(temperature, top_p)) return CSA2_ERR_RANGE;
+  if (B == 0) return CSA2_OK;
+  if (!logits || !u || !token) return CSA2_ERR_NULL;
+  if (!workspace) return CSA2_ERR_WORKSPACE;
+  if (!aligned16(logits) || !aligned16(u) || !aligned16(token) || !opt_aligned16(prob) ||
+      !opt_aligned16(n_kept) || !aligned16(workspace))
+    return CSA2_ERR_ALIGN;
+  if (workspace_bytes < csa2::sample_workspace_bytes(B, V, K)) return CSA2_ERR_WORKSPACE;
+  return hip_status(csa2::launch_sample(logits, B, V, K, temperature, top_p, u, token, prob, n_kept, workspace,
+                                        as_stream(stream)));
+}
+
 size_t csa2_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t K) {
   if (B <= 0 || H < 1 || H > 128 || K < 1 || d_c < 1) return 0;
   return csa2::attn_workspace_bytes(B, H, d_c, K);

@@ -44,6 +44,14 @@ hipError_t launch_swa_attn(const uint16_t* q, const uint8_t* codes, int64_t code
                            int W_cap, float sm_scale, const float* in_out, const float* in_lse, float* out,
                            float* lse, hipStream_t stream);
 
+size_t sample_workspace_bytes(int B, int64_t V, int K);
+hipError_t launch_sample_draw(const int32_t* cand_idx, const float* cand_score, int B, int K, float temperature,
+                              float top_p, const float* u, int32_t* token, float* prob, int32_t* n_kept,
+                              hipStream_t stream);
+hipError_t launch_sample(const float* logits, int B, int64_t V, int K, float temperature, float top_p,
+                         const float* u, int32_t* token, float* prob, int32_t* n_kept, void* workspace,
+                         hipStream_t stream);
+
 size_t attn_workspace_bytes(int B, int H, int d_c, int K);
 hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
                               int d_c, int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,

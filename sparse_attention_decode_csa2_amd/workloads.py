@@ -29,6 +29,10 @@ compressed entry per 4 tokens):
 6. reuse-swa-128k reuse-128k plus the sliding-window branch: 128 FP8 window
                   rows per sequence (RMS-normalised N(0,1) latents, one
                   power-of-two scale per row) merged with the sparse result
+7. sample-129k    the decode sampler: B=128 rows of f32 logits over a
+                  129280-token vocabulary (N(0,1) x 4), Top-2048, temperature
+                  1 and top_p 1 (the recommended sampling settings), one
+                  uniform per row
 """
 
 from dataclasses import dataclass
@@ -41,7 +45,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    mode: str            # "full" | "reindex" | "reuse" | "prefill_full" | "pool_build" | "reuse_swa"
+    mode: str            # "full" | "reindex" | "reuse" | "prefill_full" | "pool_build" | "reuse_swa" | "sample"
     B: int               # decode queries (sequences) per step
     N: int               # compressed entries per sequence (cache capacity)
     d_c: int             # FP4 latent channels
@@ -57,6 +61,8 @@ class Workload:
     prefill_rows: int = 0
     prefill_row0: int = 0
     window: int = 0      # sliding-window rows per sequence (FP8)
+    temperature: float = 1.0  # sampler: logits are divided by it
+    top_p: float = 1.0   # sampler: nucleus mass
 
     @property
     def sm_scale(self) -> float:
@@ -84,6 +90,7 @@ WORKLOADS = [
              seed=5),
     Workload("reuse-swa-128k", "reuse_swa", B=128, N=32768, d_c=512, d_r=64, H=64, H_I=8, D_I=128, K=512,
              seed=6, window=128),
+    Workload("sample-129k", "sample", B=128, N=129280, d_c=0, d_r=0, H=0, H_I=0, D_I=0, K=2048, seed=7),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -178,3 +185,15 @@ def random_codes(wl: Workload, b: int, n: int, device="cpu", scale_lo=0x20, scal
 def bf16_bits(t: torch.Tensor):
     """Host numpy uint16 view of a bf16 tensor (for the oracle)."""
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def vocab_logits(wl: Workload, device="cpu", name="logits") -> torch.Tensor:
+    """f32 [B, N]: next-token logits, N(0,1) x 4 (a peaked distribution: at
+    temperature 1 the 2048 largest of 129280 hold 95-97 % of the mass)."""
+    g = _gen(wl, name, 0, device)
+    return torch.randn(wl.B, wl.N, generator=g, device=device, dtype=torch.float32) * 4.0
+
+
+def sampler_uniforms(wl: Workload, device="cpu", name="uniforms") -> torch.Tensor:
+    """f32 [B]: the sampler's uniforms in [0, 1)."""
+    return torch.rand(wl.B, generator=_gen(wl, name, 0, device), device=device, dtype=torch.float32)

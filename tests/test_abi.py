@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
 
@@ -174,3 +174,33 @@ def test_attn_validation(lib):
     assert call(N=(1 << 32) // 512 + 1) == RANGE
     assert call(N=(1 << 32) // 1024 + 1, cst=1024) == RANGE
     assert call(N=(1 << 32) // 512, K=512, B=0) == OK
+
+
+def test_sample_validation(lib):
+    d = lib.csa2_sample_draw
+    assert d(A, A, 0, 8, 1.0, 1.0, A, A, N, N, N) == OK            # B == 0: nothing to do
+    assert d(A, A, -1, 8, 1.0, 1.0, A, A, N, N, N) == SHAPE
+    assert d(A, A, 1, 0, 1.0, 1.0, A, A, N, N, N) == RANGE
+    assert d(A, A, 1, 2049, 1.0, 1.0, A, A, N, N, N) == RANGE
+    assert d(A, A, 1, 8, 0.0, 1.0, A, A, N, N, N) == RANGE           # temperature 0
+    assert d(A, A, 1, 8, 1e-31, 1.0, A, A, N, N, N) == RANGE         # 1/T overflows float32
+    assert d(A, A, 1, 8, 1.0, 0.0, A, A, N, N, N) == RANGE           # top_p 0
+    assert d(A, A, 1, 8, 1.0, float("nan"), A, A, N, N, N) == RANGE
+    assert d(A, A, 1, 8, float("nan"), 1.0, A, A, N, N, N) == RANGE
+    assert d(A, A, 1, 8, 1.0, 1.0, N, A, N, N, N) == NULL            # no uniforms
+    assert d(A, A, 1, 8, 1.0, 1.0, A, N, N, N, N) == NULL            # no token output
+    assert d(U, A, 1, 8, 1.0, 1.0, A, A, N, N, N) == ALIGN
+    assert d(A, A, 1, 8, 1.0, 1.0, A, A, U, N, N) == ALIGN
+    s = lib.csa2_sample
+    need = lib.csa2_sample_workspace_bytes(2, 129280, 2048)
+    # candidates (2 x 2048 ids + 2 x 2048 logits) + the Top-K chunk winners (2 rows x 8 chunks x 2048 u64)
+    assert need == 2 * 2 * 2048 * 4 + 2 * 8 * 2048 * 8
+    assert lib.csa2_sample_workspace_bytes(2, 129280, 2049) == 0
+    assert s(A, 0, 129280, 2048, 1.0, 1.0, A, A, N, N, N, 0, N) == OK
+    assert s(A, 2, 0, 2048, 1.0, 1.0, A, A, N, N, A, need, N) == SHAPE
+    assert s(A, 2, 129280, 2049, 1.0, 1.0, A, A, N, N, A, need, N) == RANGE
+    assert s(A, 2, 129280, 2048, -1.0, 1.0, A, A, N, N, A, need, N) == RANGE
+    assert s(N, 2, 129280, 2048, 1.0, 1.0, A, A, N, N, A, need, N) == NULL
+    assert s(A, 2, 129280, 2048, 1.0, 1.0, A, A, N, N, N, need, N) == WS
+    assert s(A, 2, 129280, 2048, 1.0, 1.0, A, A, N, N, A, need - 1, N) == WS
+    assert s(A, 2, 129280, 2048, 1.0, 1.0, A, A, N, N, U, need, N) == ALIGN
