@@ -15,13 +15,16 @@
 // empty, reports its first candidate with probability 1.  Whatever the
 // inputs, the drawn position is a slot of the row (never out of bounds).
 //
-// One 64-lane wave per row: lane t holds the E = ceil(K / 64) consecutive
-// candidates [tE, tE + E) in registers (K <= 2048, so E <= 32); one wave scan
-// of the lane sums gives every lane its running weight; the nucleus end and
-// the drawn position are wave minima of per-lane first hits.  Both decisions
-// read the same running sums, so the drawn position always lies inside the
-// nucleus.  The candidates are a few KB per row: the kernel is latency-bound
-// (one wave per row, no LDS), its cost is the Top-K launch before it.
+// One workgroup of 256 threads (4 waves) per row: the candidates are read
+// coalesced and their weights passed through LDS so that thread t holds the
+// E = ceil(K / 256) consecutive candidates [tE, tE + E) in registers (K <=
+// 2048, so E <= 8); wave scans of the thread sums plus the wave totals give
+// every thread its running weight; the nucleus end and the drawn position are
+// minima of per-thread first hits.  Both decisions read the same running
+// sums, so the drawn position always lies inside the nucleus.  The
+// candidates are a few KB per row: the kernel is latency-bound (a serial
+// chain of loads, scans and reductions per row), and four waves per row keep
+// that chain a quarter as long as one wave would.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -32,7 +35,9 @@
 namespace csa2 {
 namespace {
 
-constexpr int SMP_E = 32;   // candidates per lane at K = 2048
+constexpr int SMP_T = 256;                  // threads per row (4 waves)
+constexpr int SMP_WAVES = SMP_T / 64;
+constexpr int SMP_E = 2048 / SMP_T;         // candidates per thread at K = 2048
 
 __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
 #pragma unroll
@@ -61,22 +66,33 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
-__global__ __launch_bounds__(64) void sample_draw_kernel(const int32_t* __restrict__ cand_idx,
-                                                         const float* __restrict__ cand_score, int K,
-                                                         float log2e_over_t, float top_p,
-                                                         const float* __restrict__ u,
-                                                         int32_t* __restrict__ token, float* __restrict__ prob,
-                                                         int32_t* __restrict__ n_kept) {
+struct SmpSmem {
+  float w[SMP_T * SMP_E + SMP_T * SMP_E / 32];   // weights, one pad word per 32
+  float wsum[SMP_WAVES];
+  int wint[2][SMP_WAVES];
+  float cn, wp;
+};
+
+__device__ __forceinline__ int pad_idx(int i) { return i + (i >> 5); }
+
+__global__ __launch_bounds__(SMP_T) void sample_draw_kernel(const int32_t* __restrict__ cand_idx,
+                                                            const float* __restrict__ cand_score, int K,
+                                                            float log2e_over_t, float top_p,
+                                                            const float* __restrict__ u,
+                                                            int32_t* __restrict__ token, float* __restrict__ prob,
+                                                            int32_t* __restrict__ n_kept) {
+  __shared__ SmpSmem sm;
   const int64_t b = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
   const int32_t* ci = cand_idx + b * K;
   const float* cs = cand_score + b * K;
-  const int E = (K + 63) >> 6;
-  const int i0 = lane * E;
+  const int E = (K + SMP_T - 1) / SMP_T;
+  const int i0 = t * E;
   const float s0 = cs[0];
   const int32_t id0 = ci[0];
   if (!(s0 > -INFINITY) || id0 < 0) {   // every logit -inf, NaN at the top, or no candidate
-    if (lane == 0) {
+    if (t == 0) {
       token[b] = id0;
       if (prob) prob[b] = 1.0f;
       if (n_kept) n_kept[b] = 1;
@@ -84,31 +100,52 @@ __global__ __launch_bounds__(64) void sample_draw_kernel(const int32_t* __restri
     return;
   }
 
-  // weights and running weights (inclusive) of this lane's candidates
-  float w[SMP_E], run[SMP_E];
+  // weights from coalesced loads (element 256 j + t; every load issued before
+  // the first use, the index clamped into the row), handed through LDS to the
+  // thread that scans them (elements [tE, tE + E))
+  int32_t idv[SMP_E];
+  float scv[SMP_E];
+#pragma unroll
+  for (int j = 0; j < SMP_E; ++j) {
+    const int i = min(j * SMP_T + t, K - 1);
+    idv[j] = ci[i];
+    scv[j] = cs[i];
+  }
   int valid = 0;
 #pragma unroll
   for (int j = 0; j < SMP_E; ++j) {
-    const int i = i0 + j;
-    float x = 0.0f;
-    if (j < E && i < K) {
-      const int32_t id = ci[i];
-      const float s = cs[i];
-      valid += id >= 0 ? 1 : 0;
-      x = (id >= 0 && s > -INFINITY) ? exp2f((s - s0) * log2e_over_t) : 0.0f;
+    const int i = j * SMP_T + t;
+    if (i < K) {
+      valid += idv[j] >= 0 ? 1 : 0;
+      sm.w[pad_idx(i)] = (idv[j] >= 0 && scv[j] > -INFINITY) ? exp2f((scv[j] - s0) * log2e_over_t) : 0.0f;
     }
-    w[j] = x;
   }
+  valid = wave_sum_i(valid);
+  if (lane == 0) sm.wint[0][wv] = valid;
+  __syncthreads();
+
+  float w[SMP_E], run[SMP_E];
   float local = 0.0f;
 #pragma unroll
   for (int j = 0; j < SMP_E; ++j) {
+    const int i = i0 + j;
+    w[j] = (j < E && i < K) ? sm.w[pad_idx(i)] : 0.0f;
     local += w[j];
     run[j] = local;
   }
-  const int n_cand = wave_sum_i(valid);                  // candidates are a prefix of the row
+  int n_cand = 0;
+#pragma unroll
+  for (int v = 0; v < SMP_WAVES; ++v) n_cand += sm.wint[0][v];   // candidates are a prefix of the row
   const float incl = wave_inclusive_sum(local, lane);
-  const float before = incl - local;
-  const float total = __shfl(incl, 63, 64);
+  if (lane == 63) sm.wsum[wv] = incl;
+  __syncthreads();
+  float before = incl - local, total = 0.0f;
+#pragma unroll
+  for (int v = 0; v < SMP_WAVES; ++v) {
+    const float x = sm.wsum[v];
+    before += v < wv ? x : 0.0f;
+    total += x;
+  }
 #pragma unroll
   for (int j = 0; j < SMP_E; ++j) run[j] += before;
 
@@ -123,15 +160,22 @@ __global__ __launch_bounds__(64) void sample_draw_kernel(const int32_t* __restri
       hit = min(hit, (j < E && i < n_cand && run[j] >= thr) ? i : INT32_MAX);
     }
     hit = wave_min_i(hit);
+    if (lane == 0) sm.wint[1][wv] = hit;
+    __syncthreads();
+    hit = INT32_MAX;
+#pragma unroll
+    for (int v = 0; v < SMP_WAVES; ++v) hit = min(hit, sm.wint[1][v]);
     n = hit != INT32_MAX ? hit + 1 : n_cand;
   }
 
-  // nucleus weight: the running weight at position n - 1, from its lane
+  // nucleus weight: the running weight at position n - 1, written by the one
+  // thread that holds that position (j < E: slots j >= E belong to no one)
   const int jn = (n - 1) - i0;
-  float cn_lane = 0.0f;
 #pragma unroll
-  for (int j = 0; j < SMP_E; ++j) cn_lane = (j == jn) ? run[j] : cn_lane;
-  const float cn = __shfl(cn_lane, (n - 1) / E, 64);
+  for (int j = 0; j < SMP_E; ++j)
+    if (j < E && j == jn) sm.cn = run[j];
+  __syncthreads();
+  const float cn = sm.cn;
   const float target = u[b] * cn;
 
   // draw: first position < n of nonzero weight whose running weight exceeds the target
@@ -145,16 +189,27 @@ __global__ __launch_bounds__(64) void sample_draw_kernel(const int32_t* __restri
   }
   hit = wave_min_i(hit);
   last = wave_max_i(last);
-  const int pos = hit != INT32_MAX ? hit : (last >= 0 ? last : 0);
-
-  const int jp = pos - i0;
-  float wp = 0.0f;
-#pragma unroll
-  for (int j = 0; j < SMP_E; ++j) wp = (j == jp) ? w[j] : wp;
-  wp = __shfl(wp, pos / E, 64);
   if (lane == 0) {
+    sm.wint[0][wv] = hit;      // the valid counts were read before the last barrier
+    sm.wint[1][wv] = last;
+  }
+  __syncthreads();
+  hit = INT32_MAX;
+  last = -1;
+#pragma unroll
+  for (int v = 0; v < SMP_WAVES; ++v) {
+    hit = min(hit, sm.wint[0][v]);
+    last = max(last, sm.wint[1][v]);
+  }
+  const int pos = hit != INT32_MAX ? hit : (last >= 0 ? last : 0);
+  const int jp = pos - i0;
+#pragma unroll
+  for (int j = 0; j < SMP_E; ++j)
+    if (j < E && j == jp) sm.wp = w[j];
+  __syncthreads();
+  if (t == 0) {
     token[b] = ci[pos];
-    if (prob) prob[b] = wp / cn;
+    if (prob) prob[b] = sm.wp / cn;
     if (n_kept) n_kept[b] = n;
   }
 }
@@ -171,7 +226,7 @@ hipError_t launch_sample_draw(const int32_t* cand_idx, const float* cand_score, 
                               float top_p, const float* u, int32_t* token, float* prob, int32_t* n_kept,
                               hipStream_t stream) {
   const float log2e_over_t = (float)(1.4426950408889634 / (double)temperature);
-  hipLaunchKernelGGL(sample_draw_kernel, dim3(B), dim3(64), 0, stream, cand_idx, cand_score, K, log2e_over_t,
+  hipLaunchKernelGGL(sample_draw_kernel, dim3(B), dim3(SMP_T), 0, stream, cand_idx, cand_score, K, log2e_over_t,
                      top_p, u, token, prob, n_kept);
   return hipGetLastError();
 }
