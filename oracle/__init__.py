@@ -35,6 +35,8 @@ Parity status per function (the pins live in ``tests/test_oracle_*.py``):
   over the built pool reproducing the Full-mode Top-K).
 * sparse_attn: pinned (dense float64 SDPA when Top-K covers every entry,
   closed-form special cases, logsumexp).
+* prefill_sparse_attn: pinned (float64 SDPA with a causal mask over two
+  sequences with different caches, every visible entry selected).
 * sample: pinned (hand-derived draws, the token frequencies over a grid of
   uniforms against scipy's softmax, the nucleus' minimality, greedy and
   single-candidate limits).
@@ -58,6 +60,7 @@ from .method import (  # noqa: F401
     topk,
     build_pool,
     sparse_attn,
+    prefill_sparse_attn,
     fp8_row_scale_exponent,
     quantize_fp8,
     dequantize_fp8,

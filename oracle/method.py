@@ -21,6 +21,8 @@ reading taken is stated at the function and listed in the design doc):
        (MLA-style: one latent shared by all heads; the key is [latent ; RoPE
        part], the value is the latent).  Reuse mode is this stage alone with
        the index list handed in [P1 CSA2; P3; P4].
+   ``prefill_sparse_attn`` - the same attention for a prefill chunk: many
+       queries of one sequence, each with its own list [P1 inference paragraph].
    ``sample``        - the decode sampler on the same Top-K: temperature,
        top-p nucleus, inverse-CDF draw [P3 DeepSelect; P1 sampling settings].
 """
@@ -365,6 +367,29 @@ def merge_branches(out_a, lse_a, out_b, lse_b):
     lse = np.where(tot > 0, safe + np.log(den), -np.inf)
     return out, lse
 
+
+
+def prefill_sparse_attn(q_bits, codes, scales, rope_bits, idx, sm_scale):
+    """Sparse attention of a prefill chunk: T queries of each sequence, every
+    one with its own index list into that sequence's cache [P1 inference
+    paragraph: the Reuse layers also run in prefill; P4 CSA2 paragraph].
+
+    Reading taken: a prefill query attends exactly as a decode query does
+    (``sparse_attn``), over its own sequence's cache through its own list;
+    causality is the lists' business (an entry a query may not see is never
+    in its list), the attention adds no mask of its own.
+    q_bits u16 [S, T, H, D]; codes / scales / rope_bits [S, N, ...] (one cache
+    per sequence); idx int [S, T, K].  Returns (out float64 [S, T, H, d_c],
+    lse float64 [S, T, H]).
+    """
+    S, T = q_bits.shape[:2]
+    outs, lses = [], []
+    for s in range(S):
+        rep = lambda a: np.broadcast_to(a[s], (T,) + a.shape[1:])   # noqa: E731
+        o, l = sparse_attn(q_bits[s], rep(codes), rep(scales), rep(rope_bits), np.asarray(idx[s]), sm_scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
 
 # ------------------------------------------------------------ the three modes
 

@@ -346,6 +346,31 @@ def check_attn_dense_vs_sdpa():
     assert np.allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
 
 
+def check_prefill_vs_causal_sdpa():
+    """A prefill chunk whose query t lists every entry it may see (the first
+    v_t entries of its own sequence, v_t growing with t, padded with -1)
+    equals float64 SDPA with the causal mask, sequence by sequence."""
+    S, T, H, N, d_c, d_r, K = 2, 6, 4, 24, 64, 32, 24
+    qb, codes, scales, rb = _attn_inputs(B=S * T, H=H, N=N, d_c=d_c, d_r=d_r, seed=71)
+    qb = qb.reshape(S, T, H, d_c + d_r)
+    codes, scales, rb = codes[:S], scales[:S], rb[:S]              # one cache per sequence
+    vis = np.array([5, 9, 12, 17, 20, 24])                          # entries query t may see
+    idx = np.full((S, T, K), -1)
+    for t in range(T):
+        idx[:, t, :vis[t]] = np.arange(vis[t])[::-1]                # any order
+    sm = 1.0 / math.sqrt(d_c + d_r)
+    out, lse = oracle.prefill_sparse_attn(qb, codes, scales, rb, idx, sm)
+    for s in range(S):
+        q = torch.from_numpy(codec.bf16_bits_to_f64(qb[s]))          # [T, H, D]
+        lat = torch.from_numpy(oracle.dequantize_fp4(codes[s], scales[s]))
+        key = torch.cat([lat, torch.from_numpy(codec.bf16_bits_to_f64(rb[s]))], dim=-1)
+        mask = torch.from_numpy(np.arange(N)[None, :] < vis[:, None])[:, None, :]   # [T, 1, N]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, key[None], lat[None], attn_mask=mask, scale=sm)
+        assert np.allclose(out[s], ref.numpy(), rtol=1e-12, atol=1e-12), s
+        sc = sm * torch.einsum("thd,nd->thn", q, key).masked_fill(~mask, -math.inf)
+        assert np.allclose(lse[s], torch.logsumexp(sc, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+
+
 def check_attn_special_cases():
     qb, codes, scales, rb = _attn_inputs(seed=15)
     B, H, D = qb.shape
@@ -677,6 +702,7 @@ ALL_PINS = [
     check_index_bruteforce, check_index_full_vs_int64_matmul, check_index_pool_bruteforce,
     check_topk_bruteforce, check_topk_vs_torch_topk_distinct, check_topk_ties_vs_stable_sort,
     check_topk_invariants, check_attn_dense_vs_sdpa, check_attn_special_cases, check_decode_modes_compose,
+    check_prefill_vs_causal_sdpa,
     check_pool_golden, check_pool_bruteforce, check_pool_reindex_reproduces_full_topk,
     check_fp8_golden, check_fp8_vs_torch_cast, check_swa_vs_sdpa, check_merge_is_one_softmax_over_the_union,
     check_sample_golden, check_sample_frequencies_vs_softmax, check_sample_nucleus_is_minimal,

@@ -25,6 +25,7 @@ _orig_fp8_exp = method.fp8_row_scale_exponent
 _orig_swa = method.swa_attn
 _orig_merge = method.merge_branches
 _orig_sample = method.sample
+_orig_prefill = method.prefill_sparse_attn
 
 
 def _swap_nibbles(x_bits):
@@ -198,6 +199,17 @@ def _sample_unmutated(*a):
     return _sample_generic(*a, _W, _REACH, _EXCEEDS)
 
 
+def _prefill_first_cache(q_bits, codes, scales, rope_bits, idx, sm_scale):
+    # plant: every sequence of the chunk reads the first sequence's cache
+    rep = lambda a: np.broadcast_to(a[:1], a.shape)   # noqa: E731
+    return _orig_prefill(q_bits, rep(codes), rep(scales), rep(rope_bits), idx, sm_scale)
+
+
+def _prefill_query_order(q_bits, codes, scales, rope_bits, idx, sm_scale):
+    # plant: the chunk's queries paired with the lists in reverse order
+    return _orig_prefill(q_bits, codes, scales, rope_bits, np.asarray(idx)[:, ::-1], sm_scale)
+
+
 MUTATIONS = {
     "nibble_order_swapped": [(method, "quantize_fp4", _swap_nibbles), (oracle, "quantize_fp4", _swap_nibbles)],
     "e2m1_ties_away": [(method, "e2m1_encode_magnitude", _ties_away), (oracle, "e2m1_encode_magnitude", _ties_away)],
@@ -216,6 +228,10 @@ MUTATIONS = {
                                  (oracle, "fp8_row_scale_exponent", _fp8_scale_one_lower)],
     "window_drops_rope": [(method, "swa_attn", _swa_no_rope), (oracle, "swa_attn", _swa_no_rope)],
     "merge_weights_base2": [(method, "merge_branches", _merge_base2), (oracle, "merge_branches", _merge_base2)],
+    "prefill_first_cache": [(method, "prefill_sparse_attn", _prefill_first_cache),
+                            (oracle, "prefill_sparse_attn", _prefill_first_cache)],
+    "prefill_lists_reversed": [(method, "prefill_sparse_attn", _prefill_query_order),
+                               (oracle, "prefill_sparse_attn", _prefill_query_order)],
     "sample_temperature_multiplies": [(method, "sample", _sample_temperature_multiplies),
                                       (oracle, "sample", _sample_temperature_multiplies)],
     "sample_nucleus_strict": [(method, "sample", _sample_nucleus_strict), (oracle, "sample", _sample_nucleus_strict)],
