@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--workload", default="full-64k",
                     help="full-64k (default, the reported line); others for supplementary runs: "
                          "tiny-full, reindex-1m, reuse-128k, prefill-full-1m, pool-build-1m, reuse-swa-128k, "
-                         "sample-129k")
+                         "sample-129k, prefill-reuse-1m")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -85,6 +85,8 @@ class Step:
     Pool construction (pool-build-1m): index (Full scores) -> build (the Reindex pool).
     Reuse + window (reuse-swa-128k): attn -> swa (the FP8 window branch merged in).
     Sampler (sample-129k): topk (over the vocabulary logits) -> draw; sets = logits + uniforms.
+    Prefill, Reuse layer (prefill-reuse-1m): attn over one cache for the 8192 queries of a chunk,
+    each with its own causal list; sets = queries + lists.
     """
 
     def __init__(self, wl, dev, rotation_bytes=ROTATION_BYTES):
@@ -106,7 +108,8 @@ class Step:
                 self.cache = self._cache(wl)
             if self.mode in ("reindex", "prefill_full", "pool_build"):
                 self.keys = torch.stack([W.index_keys(wl, b, dev) for b in range(B)])
-            touched = {"reindex": B * (wl.n_blocks * wl.block * wl.D_I * 2 + wl.K * _entry_bytes(wl)),
+            touched = {"prefill_reuse": wl.prefill_rows * (wl.K * _entry_bytes(wl) + wl.H * wl.D * 2),
+                       "reindex": B * (wl.n_blocks * wl.block * wl.D_I * 2 + wl.K * _entry_bytes(wl)),
                        "reuse": B * wl.K * _entry_bytes(wl),
                        "reuse_swa": B * (wl.K * _entry_bytes(wl) + wl.window * _window_bytes(wl)),
                        "prefill_full": B * N * wl.D_I * 2, "pool_build": B * N * wl.D_I * 2}[self.mode]
@@ -114,6 +117,11 @@ class Step:
             self.sets = []
             for r in range(self.R):
                 ws = wl.scaled(seed=wl.seed * 1000 + r)
+                if self.mode == "prefill_reuse":
+                    T = wl.prefill_rows
+                    self.sets.append({"q": W.attn_query(ws.scaled(B=T), dev).view(1, T, wl.H, wl.D),
+                                      "idx": W.chunk_index(ws).to(dev)})
+                    continue
                 st = {"q": W.attn_query(ws, dev)}
                 # index lists and pools are drawn on the host (no device
                 # random-permutation kernels in the profiled process)
@@ -128,7 +136,7 @@ class Step:
                 self.chunk = W.prefill_chunk(wl, dev)
                 self.chunk_rope = W.prefill_rope(wl, dev)
         M = {"full": N, "prefill_full": N, "reindex": wl.P_max * wl.block, "reuse": 0, "pool_build": N,
-             "reuse_swa": 0}[self.mode]
+             "reuse_swa": 0, "prefill_reuse": 0}[self.mode]
         self.M = M
         self.scores = torch.empty(B, max(M, 1), dtype=torch.float32, device=dev)
         self.positions = torch.empty(B, max(M, 1), dtype=torch.int32, device=dev)
@@ -137,12 +145,17 @@ class Step:
         self.out = torch.empty(B, wl.H, wl.d_c, dtype=torch.float32, device=dev)
         self.lse = torch.empty(B, wl.H, dtype=torch.float32, device=dev)
         tk = csa2.csa2_topk_workspace_bytes(B, M, wl.K) if M else 0
-        at = csa2.csa2_sparse_attn_workspace_bytes(B, wl.H, wl.d_c, wl.K)
+        nq = wl.prefill_rows if self.mode == "prefill_reuse" else B
+        at = csa2.csa2_sparse_attn_workspace_bytes(nq, wl.H, wl.d_c, wl.K)
         self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
         self.ws_attn = torch.empty(max(at, 16), dtype=torch.uint8, device=dev) if at else None
         self.stages = {"full": ["index", "topk", "attn"], "reindex": ["pool", "topk", "attn"],
                        "reuse": ["attn"], "prefill_full": ["quantize", "index", "topk", "attn"],
-                       "pool_build": ["index", "build"], "reuse_swa": ["attn", "swa"]}[self.mode]
+                       "pool_build": ["index", "build"], "reuse_swa": ["attn", "swa"],
+                       "prefill_reuse": ["attn"]}[self.mode]
+        if self.mode == "prefill_reuse":
+            self.out = torch.empty(1, wl.prefill_rows, wl.H, wl.d_c, dtype=torch.float32, device=dev)
+            self.lse = torch.empty(1, wl.prefill_rows, wl.H, dtype=torch.float32, device=dev)
         if self.mode == "reuse_swa":
             Wn = wl.window
             self.win = csa2.alloc_window(B, Wn, wl.d_c, wl.d_r, dev)
@@ -157,7 +170,7 @@ class Step:
             self.nb_out = torch.empty(B, dtype=torch.int32, device=dev)
             pb = csa2.csa2_build_pool_workspace_bytes(B, N, wl.block, wl.P_max)
             self.ws_build = torch.empty(max(pb, 16), dtype=torch.uint8, device=dev)
-        if self.mode in ("reuse", "reuse_swa"):
+        if self.mode in ("reuse", "reuse_swa", "prefill_reuse"):
             self.idx = None
 
     def _init_sample(self, wl, dev):
@@ -255,6 +268,11 @@ class Step:
 
     def attn(self, r):
         kv, st = self._kv(r), self.sets[r]
+        if self.mode == "prefill_reuse":
+            self.csa2.csa2_prefill_sparse_attn_fp4(st["q"], kv["codes"], kv["scales"], kv["rope"], st["idx"],
+                                                   self.wl.sm_scale, out=self.out, lse=self.lse,
+                                                   workspace=self.ws_attn)
+            return
         idx = st["idx"] if self.mode in ("reuse", "reuse_swa") else self.idx
         self.csa2.csa2_sparse_attn_fp4(st["q"], kv["codes"], kv["scales"], kv["rope"], idx,
                                        self.wl.sm_scale, out=self.out, lse=self.lse,
@@ -274,6 +292,8 @@ class Step:
             return {"topk": B * (N * 4 + K * 8), "draw": B * (K * 8 + 4 + 12), "step": B * (N * 4 + 4 + 12)}
         ent = _entry_bytes(wl)
         qi = wl.H_I * wl.D_I * 2
+        if self.mode == "prefill_reuse":
+            B = wl.prefill_rows            # the chunk's queries
         attn = B * (K * 4 + K * ent + H * wl.D * 2 + H * wl.d_c * 4 + H * 4)
         d = {"attn": attn}
         step = attn
@@ -433,7 +453,20 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    qps = wl.B / (ms_per_step * 1e-3)
+    n_queries = wl.prefill_rows if wl.mode == "prefill_reuse" else wl.B
+    qps = n_queries / (ms_per_step * 1e-3)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "alg_bytes_per_launch": alg[dom]}
+    if wl.mode == "prefill_reuse":
+        # the chunk's queries share one cache (134 MB, held in the Infinity
+        # Cache), so the matrix cores, not HBM, bound the step: scores and
+        # value products, 2 flops per multiply-add, fp16 operands
+        flops = n_queries * wl.H * wl.K * (wl.D + wl.d_c) * 2
+        tf = flops / (stage_us["attn"] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": "attn", "achieved": tf, "peak": 2500.0, "unit": "TFLOP/s",
+                    "frac": tf / 2500.0, "traffic": traffic, "alg_flops_per_launch": flops,
+                    "alg_bytes_per_launch": alg["attn"], "alg_gbs": achieved}
     line = {
         "metric": ("decode sampler rows/s + achieved HBM GB/s (% of peak), Top-K + top-p draw"
                    if wl.mode == "sample" else
@@ -456,7 +489,8 @@ def main():
                    if wl.mode == "sample" else
                    {"workload": wl.name, "mode": wl.mode, "batch": wl.B, "entries": wl.N,
                     "context_tokens": wl.N * 4, "latent": wl.d_c, "rope": wl.d_r, "heads": wl.H,
-                    "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "rotation_sets": R}),
+                    "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "rotation_sets": R,
+                    **({"chunk_queries": wl.prefill_rows} if wl.mode == "prefill_reuse" else {})}),
         "step_hbm_gbs": alg["step"] / (ms_per_step * 1e-3) / 1e9,
         "single_step_us_cold": round(single_step_us, 2),
         "step_alg_bytes": alg["step"],
@@ -464,9 +498,7 @@ def main():
         "stage_gbs": {s: round(alg[s] / (stage_us[s] * 1e-6) / 1e9, 1) for s in stages},
         "torch_topk_us": None if torch_topk_us is None else round(torch_topk_us, 3),
         "torch_sampler_us": None if torch_sampler_us is None else round(torch_sampler_us, 3),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes_per_launch": alg[dom]},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline and wl.mode == "full":
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

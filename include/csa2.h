@@ -346,6 +346,28 @@ int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_
                          float* out, float* lse, void* workspace, size_t workspace_bytes,
                          csa2_stream_t stream);
 
+/*
+ * Prefill sparse attention: a chunk of T queries of each of S sequences,
+ * every query with its own index list into its own sequence's cache.  The
+ * Reuse layers run in prefill too ([P1] inference-kernel paragraph); each
+ * prefill query attends exactly like a decode query of csa2_sparse_attn_fp4
+ * (same formula, same accuracy), and causality is the lists' business: an
+ * entry a query may not see must not be in its list.
+ *
+ * q    bf16 [S, T, H, d_c + d_r]   (query t of sequence s is row s * T + t)
+ * idx  i32  [S, T, K]              entry ids into the sequence's rows, -1 = none
+ * out  f32  [S, T, H, d_c], lse f32 [S, T, H] (nullable)
+ * codes / scales / rope: one cache per sequence, as csa2_sparse_attn_fp4
+ * (sequence s's row r at s * N_cap + r).  The workspace is
+ * csa2_sparse_attn_workspace_bytes(S * T, H, d_c, K) bytes.  Requires
+ * S, T >= 0 and S * T <= 2^24; the rest as csa2_sparse_attn_fp4.
+ */
+int csa2_prefill_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
+                                 const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
+                                 int64_t rope_stride, const int32_t* idx, int32_t K, int32_t S, int32_t T,
+                                 int32_t H, int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, csa2_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

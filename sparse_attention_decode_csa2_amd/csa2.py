@@ -56,6 +56,8 @@ def load():
         "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "csa2_sparse_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I64,
                                                 F, P, P, P, SZ, P]),
+        "csa2_prefill_sparse_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I32,
+                                                        I64, F, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -365,4 +367,37 @@ def csa2_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, l
                                   _ptr(rope if d_r > 0 else None), rs, _ptr(idx), K, B, H, d_c, d_r, N_cap,
                                   float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream())
     _check("csa2_sparse_attn_fp4", st)
+    return out, lse
+
+
+def csa2_prefill_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, lse=None, workspace=None,
+                                 want_lse=True):
+    """Prefill sparse attention: q bf16 [S, T, H, D], idx i32 [S, T, K], one
+    cache per sequence (codes, scales, rope: [S, N_cap, *] views as from
+    alloc_cache): returns (out f32 [S, T, H, d_c], lse f32 [S, T, H])."""
+    lib = load()
+    S, T, H, D = q.shape
+    N_cap = codes.shape[1]
+    d_c = codes.shape[2] * 2
+    d_r = D - d_c
+    K = idx.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if out is None:
+        out = torch.empty(S, T, H, d_c, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(S, T, H, dtype=torch.float32, device=dev)
+    need = csa2_sparse_attn_workspace_bytes(S * T, H, d_c, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cs = _row_stride(codes, 1, "codes")
+    ss = _row_stride(scales, 1, "scales")
+    rs = _row_stride(rope, 2, "rope") if d_r > 0 else 0
+    st = lib.csa2_prefill_sparse_attn_fp4(_ptr(q), _ptr(codes), cs, _ptr(scales), ss,
+                                          _ptr(rope if d_r > 0 else None), rs, _ptr(idx), K, S, T, H, d_c, d_r,
+                                          N_cap, float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                          _stream())
+    _check("csa2_prefill_sparse_attn_fp4", st)
     return out, lse

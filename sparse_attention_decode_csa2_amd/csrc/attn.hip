@@ -108,7 +108,7 @@ struct GatherRegs {
 template <int DC, int DR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
-    const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, float sm_scale_log2e, int n_hg,
+    const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, int qps, float sm_scale_log2e, int n_hg,
     int n_split, int per_split, int spread, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int KSL = DC / 32;           // latent k-steps
@@ -197,9 +197,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // host), so a row's offset from its sequence base is 32-bit arithmetic.
   // Plain (cached) loads: the other head blocks of the query gather the same
   // rows through the same XCD's L2, and a streaming hint would evict them.
-  const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride + 16 * g;
-  const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride + 2 * g;
-  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride + 32 * g;
+  // query b reads the cache of sequence b / qps (qps = 1 in decode; a
+  // prefill chunk has qps queries per sequence)
+  const int64_t sq = b / qps;
+  const uint8_t* seq_codes = cache.codes + sq * N_cap * cache.codes_stride + 16 * g;
+  const uint8_t* seq_scales = cache.scales + sq * N_cap * cache.scales_stride + 2 * g;
+  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + sq * N_cap * cache.rope_stride + 32 * g;
   const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
   const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
   auto gather = [&](GR& gr, int tile) {
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 template <int DR>
 __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
-    const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, float sm_scale_log2e, int n_hp,
+    const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, int qps, float sm_scale_log2e, int n_hp,
     int n_split, int per_split, int spread, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int DC = 512;
@@ -472,10 +475,12 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   const int e_end = min(K, e_begin + per_split);
   const int32_t* idx_row = idx + b * K;
   const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
-  // wave-uniform sequence bases; rows are addressed by 32-bit offsets from them
-  const uint8_t* seq_codes = cache.codes + b * N_cap * cache.codes_stride;
-  const uint8_t* seq_scales = cache.scales + b * N_cap * cache.scales_stride;
-  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + b * N_cap * cache.rope_stride;
+  // wave-uniform sequence bases (query b reads sequence b / qps); rows are
+  // addressed by 32-bit offsets from them
+  const int64_t sq = b / qps;
+  const uint8_t* seq_codes = cache.codes + sq * N_cap * cache.codes_stride;
+  const uint8_t* seq_scales = cache.scales + sq * N_cap * cache.scales_stride;
+  const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + sq * N_cap * cache.rope_stride;
   const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
   const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
 
@@ -862,7 +867,7 @@ size_t attn_workspace_bytes(int B, int H, int d_c, int K) {
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
-                              int d_c, int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,
+                              int d_c, int d_r, int64_t N_cap, int qps, float sm_scale, float* out, float* lse,
                               void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   int s, ps;
@@ -877,14 +882,14 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
   const dim3 grid((unsigned)(groups * 8 * n_hg));
   const float sl = sm_scale * LOG2E;
 #define CSA2_ATTN(KERNEL, THREADS, DCV, DRV)                                                          \
-  hipLaunchKernelGGL((KERNEL<DCV, DRV>), grid, dim3(THREADS), 0, stream, q, cache, idx, K, B, H, N_cap, sl, \
+  hipLaunchKernelGGL((KERNEL<DCV, DRV>), grid, dim3(THREADS), 0, stream, q, cache, idx, K, B, H, N_cap, qps, sl, \
                      n_hg, s, ps, spread, out, lse, ws_o, ws_ml)
   if (hpw == 32) {
     if (d_r == 64)
-      hipLaunchKernelGGL((sparse_attn_role_kernel<64>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,
+      hipLaunchKernelGGL((sparse_attn_role_kernel<64>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, qps,
                          sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml);
     else if (d_r == 0)
-      hipLaunchKernelGGL((sparse_attn_role_kernel<0>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,
+      hipLaunchKernelGGL((sparse_attn_role_kernel<0>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, qps,
                          sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml);
     else return hipErrorInvalidValue;
   } else if (d_c == 512 && d_r == 64) CSA2_ATTN(sparse_attn_kernel, 256, 512, 64);

@@ -236,11 +236,12 @@ size_t csa2_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32
   return csa2::attn_workspace_bytes(B, H, d_c, K);
 }
 
-int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
-                         const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
-                         int64_t rope_stride, const int32_t* idx, int32_t K, int32_t B, int32_t H,
-                         int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale, float* out,
-                         float* lse, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+// B queries; query b reads sequence b / qps (validated by the callers: qps >= 1, B % qps == 0).
+static int sparse_attn_checked(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
+                               const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
+                               int64_t rope_stride, const int32_t* idx, int32_t K, int32_t B, int32_t qps,
+                               int32_t H, int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
   if (B < 0 || K < 1 || N_cap < 0 || codes_stride < 0 || scales_stride < 0 || rope_stride < 0)
     return CSA2_ERR_SHAPE;
   if (!((d_c == 128 || d_c == 512) && (d_r == 0 || d_r == 64)) || H < 1 || H > 128)
@@ -260,8 +261,29 @@ int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_
   if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;
   const csa2::CacheRef c{const_cast<uint8_t*>(codes), codes_stride, const_cast<uint8_t*>(scales),
                          scales_stride, d_r > 0 ? const_cast<uint16_t*>(rope) : nullptr, rope_stride};
-  return hip_status(csa2::launch_sparse_attn(q, c, idx, K, B, H, d_c, d_r, N_cap, sm_scale, out, lse,
+  return hip_status(csa2::launch_sparse_attn(q, c, idx, K, B, H, d_c, d_r, N_cap, qps, sm_scale, out, lse,
                                              workspace, as_stream(stream)));
+}
+
+int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
+                         const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
+                         int64_t rope_stride, const int32_t* idx, int32_t K, int32_t B, int32_t H,
+                         int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale, float* out,
+                         float* lse, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+  return sparse_attn_checked(q, codes, codes_stride, scales, scales_stride, rope, rope_stride, idx, K, B, 1, H,
+                             d_c, d_r, N_cap, sm_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int csa2_prefill_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
+                                 const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
+                                 int64_t rope_stride, const int32_t* idx, int32_t K, int32_t S, int32_t T,
+                                 int32_t H, int32_t d_c, int32_t d_r, int64_t N_cap, float sm_scale, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+  if (S < 0 || T < 0) return CSA2_ERR_SHAPE;
+  if ((int64_t)S * T > (1 << 24)) return CSA2_ERR_RANGE;
+  if (S == 0 || T == 0) return CSA2_OK;
+  return sparse_attn_checked(q, codes, codes_stride, scales, scales_stride, rope, rope_stride, idx, K, S * T, T,
+                             H, d_c, d_r, N_cap, sm_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -53,8 +53,9 @@ hipError_t launch_sample(const float* logits, int B, int64_t V, int K, float tem
                          hipStream_t stream);
 
 size_t attn_workspace_bytes(int B, int H, int d_c, int K);
+// Query b reads the rows of sequence b / qps (qps = 1: one query per sequence).
 hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
-                              int d_c, int d_r, int64_t N_cap, float sm_scale, float* out, float* lse,
+                              int d_c, int d_r, int64_t N_cap, int qps, float sm_scale, float* out, float* lse,
                               void* workspace, hipStream_t stream);
 
 }  // namespace csa2

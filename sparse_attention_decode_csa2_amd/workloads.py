@@ -29,6 +29,10 @@ compressed entry per 4 tokens):
 6. reuse-swa-128k reuse-128k plus the sliding-window branch: 128 FP8 window
                   rows per sequence (RMS-normalised N(0,1) latents, one
                   power-of-two scale per row) merged with the sparse result
+8. prefill-reuse-1m  a Reuse layer in prefill: an 8192-token chunk at the end
+                  of a 1M-token context (262144 entries), every chunk token a
+                  query (64 heads) with its own list of 512 entries, unique
+                  and uniform over the entries it may see (sorted)
 7. sample-129k    the decode sampler: B=128 rows of f32 logits over a
                   129280-token vocabulary (N(0,1) x 4), Top-2048, temperature
                   1 and top_p 1 (the recommended sampling settings), one
@@ -46,6 +50,7 @@ import torch
 class Workload:
     name: str
     mode: str            # "full" | "reindex" | "reuse" | "prefill_full" | "pool_build" | "reuse_swa" | "sample"
+                         # | "prefill_reuse"
     B: int               # decode queries (sequences) per step
     N: int               # compressed entries per sequence (cache capacity)
     d_c: int             # FP4 latent channels
@@ -91,6 +96,8 @@ WORKLOADS = [
     Workload("reuse-swa-128k", "reuse_swa", B=128, N=32768, d_c=512, d_r=64, H=64, H_I=8, D_I=128, K=512,
              seed=6, window=128),
     Workload("sample-129k", "sample", B=128, N=129280, d_c=0, d_r=0, H=0, H_I=0, D_I=0, K=2048, seed=7),
+    Workload("prefill-reuse-1m", "prefill_reuse", B=1, N=262144, d_c=512, d_r=64, H=64, H_I=8, D_I=128, K=512,
+             seed=8, prefill_rows=8192),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -197,3 +204,45 @@ def vocab_logits(wl: Workload, device="cpu", name="logits") -> torch.Tensor:
 def sampler_uniforms(wl: Workload, device="cpu", name="uniforms") -> torch.Tensor:
     """f32 [B]: the sampler's uniforms in [0, 1)."""
     return torch.rand(wl.B, generator=_gen(wl, name, 0, device), device=device, dtype=torch.float32)
+
+
+def chunk_visible(wl: Workload, t) -> torch.Tensor:
+    """Entries query t of a prefill chunk may see: the chunk is the last T =
+    prefill_rows tokens of a context of 4 N tokens, and entry e (tokens 4e ..
+    4e + 3) is visible once its last token is at or before the query's."""
+    T = wl.prefill_rows
+    p0 = 4 * wl.N - T
+    return (p0 + torch.as_tensor(t) + 1) // 4
+
+
+def chunk_index(wl: Workload, device="cpu") -> torch.Tensor:
+    """int32 [B, T, K]: each chunk query's list, K unique entries uniform over
+    the entries it may see, sorted (all of them, padded with -1, when it sees
+    fewer than K).  Drawn as the first K distinct values of i.i.d. uniform
+    draws, which is a uniform K-subset (a random permutation's first K when
+    the range is at most 4 K)."""
+    T, K = wl.prefill_rows, wl.K
+    out = torch.full((wl.B, T, K), -1, dtype=torch.int32)
+    vis = chunk_visible(wl, torch.arange(T))
+    for b in range(wl.B):
+        g = _gen(wl, "chunk_idx", b, "cpu")
+        D = K + K // 2 + 64
+        draws = (torch.rand(T, D, generator=g, dtype=torch.float64) * vis[:, None]).floor().long()
+        srt, order = torch.sort(draws, dim=1, stable=True)
+        dup_sorted = torch.zeros_like(srt, dtype=torch.bool)
+        dup_sorted[:, 1:] = srt[:, 1:] == srt[:, :-1]
+        dup = torch.zeros_like(dup_sorted).scatter_(1, order, dup_sorted)   # later repeats, in draw order
+        rank = torch.cumsum((~dup).long(), dim=1)
+        keep = (~dup) & (rank <= K)
+        for t in range(T):
+            v = int(vis[t])
+            if v <= K:
+                out[b, t, :v] = torch.arange(v, dtype=torch.int32)
+                continue
+            if v <= 4 * K:        # a small range: the draws may hold fewer than K distinct values
+                out[b, t] = torch.sort(torch.randperm(v, generator=g)[:K]).values.to(torch.int32)
+                continue
+            sel = draws[t][keep[t]]
+            assert sel.numel() == K, "too few distinct draws"
+            out[b, t] = torch.sort(sel).values.to(torch.int32)
+    return out.to(device)

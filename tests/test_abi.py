@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
 
@@ -204,3 +204,24 @@ def test_sample_validation(lib):
     assert s(A, 2, 129280, 2048, 1.0, 1.0, A, A, N, N, N, need, N) == WS
     assert s(A, 2, 129280, 2048, 1.0, 1.0, A, A, N, N, A, need - 1, N) == WS
     assert s(A, 2, 129280, 2048, 1.0, 1.0, A, A, N, N, U, need, N) == ALIGN
+
+
+
+def test_prefill_attn_validation(lib):
+    f = lib.csa2_prefill_sparse_attn_fp4
+
+    def call(q=A, S=2, T=8, K=512, H=64, d_c=512, d_r=64, Ncap=100, out=A, ws=A, wsb=1 << 30):
+        return f(q, A, 512, A, 512, A, 512, A, K, S, T, H, d_c, d_r, Ncap, ctypes.c_float(0.04), out, N, ws, wsb, N)
+    assert call(S=0) == OK
+    assert call(T=0) == OK
+    assert call(S=-1) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert call(S=4096, T=4097) == RANGE           # more than 2^24 queries
+    assert call(K=0) == SHAPE
+    assert call(d_c=256) == UNSUP
+    assert call(q=N) == NULL
+    assert call(out=U) == ALIGN
+    need = lib.csa2_sparse_attn_workspace_bytes(2 * 8, 64, 512, 512)
+    assert need > 0
+    assert call(ws=N) == WS
+    assert call(wsb=need - 4) == WS
