@@ -203,6 +203,11 @@ def csa2_topk(scores, K, ids=None, n_valid=None, out_idx=None, out_score=None, w
               want_score=True):
     """Top-K (score desc, id asc): returns (idx i32 [B, K], score f32 [B, K] or None)."""
     lib = load()
+    _need(scores, torch.float32, "scores")
+    if ids is not None:
+        _need(ids, torch.int32, "ids")
+    if n_valid is not None:
+        _need(n_valid, torch.int32, "n_valid")
     B, M = scores.shape
     dev = scores.device
     if out_idx is None:
@@ -226,6 +231,9 @@ def csa2_sample_draw(cand_idx, cand_score, temperature, top_p, u, token=None, pr
     """Draw over Top-K candidates: cand_idx i32 [B, K], cand_score f32 [B, K],
     u f32 [B] -> (token i32 [B], prob f32 [B], n_kept i32 [B])."""
     lib = load()
+    _need(cand_idx, torch.int32, "cand_idx")
+    _need(cand_score, torch.float32, "cand_score")
+    _need(u, torch.float32, "u")
     B, K = cand_idx.shape
     dev = cand_idx.device
     token = torch.empty(B, dtype=torch.int32, device=dev) if token is None else token
@@ -244,6 +252,8 @@ def csa2_sample_workspace_bytes(B, V, K):
 def csa2_sample(logits, K, temperature, top_p, u, token=None, prob=None, n_kept=None, workspace=None):
     """Top-K over logits f32 [B, V], then the draw: (token, prob, n_kept)."""
     lib = load()
+    _need(logits, torch.float32, "logits")
+    _need(u, torch.float32, "u")
     B, V = logits.shape
     dev = logits.device
     token = torch.empty(B, dtype=torch.int32, device=dev) if token is None else token
@@ -290,6 +300,7 @@ def csa2_swa_attn_fp8(q, codes, sigma, rope, sm_scale=None, n_win=None, merge_ou
     [B, W_cap], merged with (merge_out, merge_lse) when given: returns
     (out f32 [B, H, d_c], lse f32 [B, H])."""
     lib = load()
+    _need(q, torch.bfloat16, "q")
     B, H, D = q.shape
     W_cap, d_c = codes.shape[1], codes.shape[2]
     d_r = D - d_c
@@ -344,10 +355,12 @@ def csa2_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, l
     scales, rope: [B, N_cap, *] views as from alloc_cache): returns
     (out f32 [B, H, d_c], lse f32 [B, H])."""
     lib = load()
+    _need(q, torch.bfloat16, "q")
     B, H, D = q.shape
     N_cap = codes.shape[1]
     d_c = codes.shape[2] * 2
     d_r = D - d_c
+    _need(idx, torch.int32, "idx")
     K = idx.shape[1]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
@@ -376,6 +389,8 @@ def csa2_prefill_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out
     cache per sequence (codes, scales, rope: [S, N_cap, *] views as from
     alloc_cache): returns (out f32 [S, T, H, d_c], lse f32 [S, T, H])."""
     lib = load()
+    _need(q, torch.bfloat16, "q")
+    _need(idx, torch.int32, "idx")
     S, T, H, D = q.shape
     N_cap = codes.shape[1]
     d_c = codes.shape[2] * 2

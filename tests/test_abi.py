@@ -225,3 +225,29 @@ def test_prefill_attn_validation(lib):
     assert need > 0
     assert call(ws=N) == WS
     assert call(wsb=need - 4) == WS
+
+
+def test_binding_rejects_wrong_tensors(lib):
+    """The binding checks dtype and contiguity before it calls the library
+    (CPU tensors: nothing is launched)."""
+    import torch
+    f32 = torch.zeros(4, 8, dtype=torch.float32)
+    i32 = torch.zeros(4, 8, dtype=torch.int32)
+    u = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        csa2.csa2_topk(f32.double(), 2)
+    with pytest.raises(ValueError):
+        csa2.csa2_topk(f32.t(), 2)                       # not contiguous
+    with pytest.raises(ValueError):
+        csa2.csa2_sample(f32.half(), 2, 1.0, 1.0, u)
+    with pytest.raises(ValueError):
+        csa2.csa2_sample(f32, 2, 1.0, 1.0, u.double())
+    with pytest.raises(ValueError):
+        csa2.csa2_sample_draw(i32.long(), f32, 1.0, 1.0, u)
+    q = torch.zeros(2, 4, 576, dtype=torch.float32)
+    codes = torch.zeros(2, 16, 256, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        csa2.csa2_sparse_attn_fp4(q, codes, codes[..., :32], codes[..., :128], i32[:2])
+    with pytest.raises(ValueError):
+        csa2.csa2_prefill_sparse_attn_fp4(q.to(torch.bfloat16)[None], codes, codes[..., :32], codes[..., :128],
+                                          i32[:2].long()[None])
