@@ -362,6 +362,10 @@ def csa2_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, l
     d_r = D - d_c
     _need(idx, torch.int32, "idx")
     K = idx.shape[1]
+    if idx.dim() != 2 or idx.shape[0] != B:
+        raise ValueError(f"idx must be [B={B}, K], got {tuple(idx.shape)}")
+    if codes.shape[0] < B or scales.shape[0] < B or (d_r > 0 and rope.shape[0] < B):
+        raise ValueError(f"the cache holds {codes.shape[0]} sequences, {B} queries need one each")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     dev = q.device
@@ -396,6 +400,10 @@ def csa2_prefill_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out
     d_c = codes.shape[2] * 2
     d_r = D - d_c
     K = idx.shape[2]
+    if tuple(idx.shape[:2]) != (S, T):
+        raise ValueError(f"idx must be [S={S}, T={T}, K], got {tuple(idx.shape)}")
+    if codes.shape[0] < S or scales.shape[0] < S or (d_r > 0 and rope.shape[0] < S):
+        raise ValueError(f"the cache holds {codes.shape[0]} sequences, the chunk needs {S}")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     dev = q.device

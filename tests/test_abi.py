@@ -251,3 +251,22 @@ def test_binding_rejects_wrong_tensors(lib):
     with pytest.raises(ValueError):
         csa2.csa2_prefill_sparse_attn_fp4(q.to(torch.bfloat16)[None], codes, codes[..., :32], codes[..., :128],
                                           i32[:2].long()[None])
+
+
+def test_binding_rejects_caches_too_small_for_the_queries(lib):
+    """Each decode query reads its own sequence of the cache, a prefill chunk
+    one sequence per S: a cache with fewer sequences is refused before any
+    call (CPU tensors: nothing is launched)."""
+    import torch
+    from sparse_attention_decode_csa2_amd import csa2 as c
+    codes, scales, rope = c.alloc_cache(2, 16, 512, 64, "cpu")
+    q = torch.zeros(4, 8, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="sequences"):
+        c.csa2_sparse_attn_fp4(q, codes, scales, rope, torch.zeros(4, 8, dtype=torch.int32))
+    with pytest.raises(ValueError, match="idx"):
+        c.csa2_sparse_attn_fp4(q[:2], codes, scales, rope, torch.zeros(3, 8, dtype=torch.int32))
+    qp = torch.zeros(3, 5, 8, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="sequences"):
+        c.csa2_prefill_sparse_attn_fp4(qp, codes, scales, rope, torch.zeros(3, 5, 8, dtype=torch.int32))
+    with pytest.raises(ValueError, match="idx"):
+        c.csa2_prefill_sparse_attn_fp4(qp[:2], codes, scales, rope, torch.zeros(2, 4, 8, dtype=torch.int32))

@@ -126,3 +126,39 @@ def test_prefill_full_workload_sampled_rows():
     ro, rl = _oracle_rows(wl, q, (codes, scales, rope), idx.numpy(), rows)
     ts = [t for _, t in rows]
     attn_close(out[0, ts].cpu().numpy(), lse[0, ts].cpu().numpy(), ro, rl, 2e-3)
+
+
+def test_prefill_in_a_hip_graph_matches_eager():
+    """csa2_prefill_sparse_attn_fp4 captured into a HIP graph and replayed
+    three times, with eager work in between, reproduces the eager result bit
+    for bit."""
+    wl = W.WORKLOADS[1]
+    S, T, N, K = 2, 64, 2048, 512
+    note(f"prefill attn: HIP graph capture + 3 replays vs eager S={S} T={T}")
+    codes, scales, rope = _raw_caches(wl, S, N)
+    q = W.attn_query(wl.scaled(B=S * T), DEV).view(S, T, wl.H, wl.D)
+    idx = torch.from_numpy(_causal_idx(wl, S, T, N, K)).to(DEV)
+    out = torch.empty(S, T, wl.H, wl.d_c, dtype=torch.float32, device=DEV)
+    lse = torch.empty(S, T, wl.H, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(csa2.csa2_sparse_attn_workspace_bytes(S * T, wl.H, wl.d_c, K), 16), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        csa2.csa2_prefill_sparse_attn_fp4(q, codes, scales, rope, idx, wl.sm_scale, out=out, lse=lse, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    ref = [out.clone(), lse.clone()]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), rep
+        # eager work between replays: two decode queries, one per sequence of the cache
+        csa2.csa2_sparse_attn_fp4(q[0, :S], codes, scales, rope, idx[0, :S], wl.sm_scale)
+        torch.cuda.synchronize()

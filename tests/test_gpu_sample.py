@@ -157,3 +157,38 @@ def test_sample_full_workload():
     torch.cuda.synchronize()
     _compare(x.cpu().numpy(), wl.K, wl.temperature, wl.top_p, u.cpu().numpy(), tok.cpu().numpy(),
              prob.cpu().numpy(), n.cpu().numpy(), max_near=2)
+
+
+def test_sample_in_a_hip_graph_matches_eager():
+    """csa2_sample captured into a HIP graph (outputs and workspace passed in)
+    and replayed three times, with eager work in between, reproduces the
+    eager result bit for bit."""
+    B, V, K = 16, 40000, 1024
+    note(f"csa2_sample: HIP graph capture + 3 replays vs eager B={B} V={V} K={K}")
+    rng = np.random.default_rng(9)
+    x = torch.from_numpy(_logits(rng, B, V, "cont")).to(DEV)
+    u = torch.from_numpy(rng.random(B).astype(np.float32)).to(DEV)
+    tok = torch.empty(B, dtype=torch.int32, device=DEV)
+    prob = torch.empty(B, dtype=torch.float32, device=DEV)
+    nk = torch.empty(B, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(csa2.csa2_sample_workspace_bytes(B, V, K), 16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        csa2.csa2_sample(x, K, 0.9, 0.8, u, token=tok, prob=prob, n_kept=nk, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (tok, prob, nk)]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(3):
+        for t in (tok, prob, nk):
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((tok, prob, nk), ref):
+            assert torch.equal(a, b), rep
+        csa2.csa2_topk(x, 64)                       # eager work between replays
+        torch.cuda.synchronize()
