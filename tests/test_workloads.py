@@ -49,3 +49,35 @@ def test_rmsnorm_rows_stay_in_normal_scale_range():
     x = W.prefill_chunk(W.WORKLOADS[4].scaled(prefill_rows=2048))
     _, s = oracle.quantize_fp4(W.bf16_bits(x))
     assert np.all(s >= 0x08) and np.all(s < 0x7E)
+
+
+def test_chunk_lists_are_causal_unique_sorted_and_uniform():
+    """Prefill chunk lists: K distinct entries each query may see, sorted;
+    every query sees its visible entries in full when it sees fewer than K;
+    the lists are deterministic and cover the visible range evenly."""
+    wl = W.BY_NAME["prefill-reuse-1m"].scaled(B=2, N=3000, prefill_rows=400, K=256)
+    idx = W.chunk_index(wl)
+    assert idx.shape == (2, 400, 256) and torch.equal(idx, W.chunk_index(wl))
+    vis = W.chunk_visible(wl, torch.arange(400))
+    assert int(vis[-1]) == wl.N and torch.all(torch.diff(vis) >= 0)
+    for s in range(2):
+        for t in range(400):
+            row = idx[s, t]
+            v = row[row >= 0]
+            assert v.numel() == min(256, int(vis[t]))
+            assert torch.all(v < vis[t]) and torch.all(torch.diff(v) > 0)
+    # uniform over the visible range: each quarter of it holds about a quarter of the picks
+    picks = idx[0].float() / vis[:, None].float()
+    frac = torch.histc(picks[idx[0] >= 0], bins=4, min=0, max=1) / (idx[0] >= 0).sum()
+    assert torch.all((frac - 0.25).abs() < 0.02), frac
+    small = W.chunk_index(wl.scaled(N=40, prefill_rows=100, K=16))
+    assert small[0, 0].tolist() == list(range(15)) + [-1]      # sees 15 entries: all of them, then -1
+
+
+def test_sampler_inputs():
+    wl = W.BY_NAME["sample-129k"].scaled(B=3, N=5000)
+    x = W.vocab_logits(wl)
+    u = W.sampler_uniforms(wl)
+    assert x.dtype == torch.float32 and x.shape == (3, 5000) and torch.equal(x, W.vocab_logits(wl))
+    assert abs(float(x.std()) - 4.0) < 0.2
+    assert u.shape == (3,) and torch.all((u >= 0) & (u < 1))
