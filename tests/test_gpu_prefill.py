@@ -162,3 +162,21 @@ def test_prefill_in_a_hip_graph_matches_eager():
         # eager work between replays: two decode queries, one per sequence of the cache
         csa2.csa2_sparse_attn_fp4(q[0, :S], codes, scales, rope, idx[0, :S], wl.sm_scale)
         torch.cuda.synchronize()
+
+
+
+@pytest.mark.parametrize("H,dc,dr,S,T", [(40, 512, 64, 1, 300), (64, 512, 0, 2, 150), (17, 512, 64, 3, 100),
+                                         (8, 128, 64, 2, 70)])
+def test_prefill_head_counts_and_dims(H, dc, dr, S, T):
+    """Partial 32-head groups and the variant without a RoPE part on the
+    32-head kernel (S * T * ceil(H / 32) >= 256), and small head counts and
+    the 128-channel latent on the 16-head kernel."""
+    wl = W.WORKLOADS[1].scaled(H=H, d_c=dc, d_r=dr)
+    N, K = 2048, 512
+    note(f"prefill attn: H={H} d_c={dc} d_r={dr} S={S} T={T}")
+    q, cache, idx, out, lse = _run(wl, S, T, N, K)
+    codes, scales, rope = cache
+    ro, rl = oracle.prefill_sparse_attn(np_bits(q), codes.cpu().numpy(), scales.cpu().numpy(),
+                                        np_bits(rope.contiguous()), idx, wl.sm_scale)
+    attn_close(out.cpu().numpy().reshape(S * T, H, -1), lse.cpu().numpy().reshape(S * T, H),
+               ro.reshape(S * T, H, -1), rl.reshape(S * T, H), 2e-3)
