@@ -470,6 +470,8 @@ def main():
     line = {
         "metric": ("decode sampler rows/s + achieved HBM GB/s (% of peak), Top-K + top-p draw"
                    if wl.mode == "sample" else
+                   "prefill chunk queries/s + achieved TFLOP/s (% of MFMA peak), CSA2 FP4 sparse attn"
+                   if wl.mode == "prefill_reuse" else
                    "decode queries/s + achieved HBM GB/s (% of peak), CSA2 FP4 sparse attn"),
         "value": qps,
         "unit": "rows/s" if wl.mode == "sample" else "queries/s",
