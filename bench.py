@@ -1,11 +1,18 @@
 """Benchmark of the CSA2 FP4 sparse-attention decode step on one MI355X.
 
-Default workload: Full-mode decode, batch 1, 64 query heads over a 64K-token
-context (16384 FP4 entries of 512 latent + 64 RoPE channels), indexer 8 heads
-x 128, Top-512.  One step = csa2_index_full -> csa2_topk ->
-csa2_sparse_attn_fp4, all on the GPU through the C ABI, with every input
-resident in HBM.  Inputs rotate over enough distinct sets (>= 1 GiB per
-rotation) that no step finds its data in the 256 MB Infinity Cache.
+Default workload: prefill-full-1m, the largest configuration that fits one
+GPU: an 8192-row post-RoPE bf16 chunk is quantised to FP4 and appended to
+sequence 0, then a batch of 8 Full-mode decode queries (64 heads, indexer
+8 heads x 128) scores 262144 entries per sequence (1M tokens at 4:1), takes
+the Top-512 and runs the sparse attention over them.  One step =
+csa2_quantize_fp4 -> csa2_index_full -> csa2_topk -> csa2_sparse_attn_fp4, all
+on the GPU through the C ABI, with every input resident in HBM.  The other
+workloads (--workload) give the supplementary lines.
+
+Inputs rotate over R distinct sets, R sized from the bytes one step actually
+reads so that a rotation touches >= 1 GiB (4x the 256 MB Infinity Cache); the
+timed steps start after the sets the warm-up used, and the line records how
+many distinct sets and bytes the timed steps touched.
 
 Prints ONE JSON line (rank 0).  `roofline` describes the dominant kernel:
 algorithmic bytes per launch over its average duration (HIP events on the
@@ -32,6 +39,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATION_BYTES = 1 << 30
+MAX_SETS = 512
+DEFAULT_WORKLOAD = "prefill-full-1m"
 
 
 def parse():
@@ -39,10 +48,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="full-64k",
-                    help="full-64k (default, the reported line); others for supplementary runs: "
-                         "tiny-full, reindex-1m, reuse-128k, prefill-full-1m, pool-build-1m, reuse-swa-128k, "
-                         "sample-129k, prefill-reuse-1m")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="prefill-full-1m (default, the reported line: the largest configuration); others for "
+                         "supplementary runs: tiny-full, full-64k, reindex-1m, reuse-128k, pool-build-1m, "
+                         "reuse-swa-128k, sample-129k, prefill-reuse-1m")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -99,21 +108,15 @@ class Step:
         if self.mode == "sample":
             self._init_sample(wl, dev)
             return
+        self.touched = self.step_read_bytes()
+        self.R = min(MAX_SETS, max(2, math.ceil(rotation_bytes / self.touched)))
         if self.mode == "full":
-            per_set = B * N * (wl.D_I * 2 + _entry_bytes(wl))
-            self.R = max(2, math.ceil(rotation_bytes / per_set))
             self.sets = [self._full_set(wl.scaled(seed=wl.seed * 1000 + r)) for r in range(self.R)]
         else:
             if self.mode != "pool_build":
                 self.cache = self._cache(wl)
             if self.mode in ("reindex", "prefill_full", "pool_build"):
                 self.keys = torch.stack([W.index_keys(wl, b, dev) for b in range(B)])
-            touched = {"prefill_reuse": wl.prefill_rows * (wl.K * _entry_bytes(wl) + wl.H * wl.D * 2),
-                       "reindex": B * (wl.n_blocks * wl.block * wl.D_I * 2 + wl.K * _entry_bytes(wl)),
-                       "reuse": B * wl.K * _entry_bytes(wl),
-                       "reuse_swa": B * (wl.K * _entry_bytes(wl) + wl.window * _window_bytes(wl)),
-                       "prefill_full": B * N * wl.D_I * 2, "pool_build": B * N * wl.D_I * 2}[self.mode]
-            self.R = max(2, math.ceil(rotation_bytes / touched))
             self.sets = []
             for r in range(self.R):
                 ws = wl.scaled(seed=wl.seed * 1000 + r)
@@ -177,7 +180,8 @@ class Step:
         import torch
         csa2, W = self.csa2, self.W
         B, V, K = wl.B, wl.N, wl.K
-        self.R = max(2, math.ceil(ROTATION_BYTES / (B * V * 4)))
+        self.touched = self.step_read_bytes()
+        self.R = min(MAX_SETS, max(2, math.ceil(ROTATION_BYTES / self.touched)))
         self.sets = []
         for r in range(self.R):
             ws = wl.scaled(seed=wl.seed * 1000 + r)
@@ -192,6 +196,24 @@ class Step:
         self.prob = torch.empty(B, dtype=torch.float32, device=dev)
         self.n_kept = torch.empty(B, dtype=torch.int32, device=dev)
         self.stages = ["topk", "draw"]
+
+    def step_read_bytes(self):
+        """Bytes one step reads from HBM (the inputs of all its stages, read
+        once): the figure the rotation is sized from."""
+        wl = self.wl
+        B, N, K = wl.B, wl.N, wl.K
+        if self.mode == "sample":
+            return B * N * 4
+        ent = _entry_bytes(wl)
+        q = wl.H * wl.D * 2
+        qi = wl.H_I * wl.D_I * 2
+        return {"full": B * (N * wl.D_I * 2 + qi + K * ent + q),
+                "prefill_reuse": wl.prefill_rows * (K * ent + q + K * 4),
+                "reindex": B * (wl.n_blocks * wl.block * wl.D_I * 2 + qi + K * ent + q),
+                "reuse": B * (K * ent + q + K * 4),
+                "reuse_swa": B * (K * ent + wl.window * _window_bytes(wl) + q + K * 4),
+                "prefill_full": B * (N * wl.D_I * 2 + qi + K * ent + q) + wl.prefill_rows * wl.D * 2,
+                "pool_build": B * (N * wl.D_I * 2 + qi)}[self.mode]
 
     def draw(self, r):
         wl = self.wl
@@ -325,33 +347,116 @@ class Step:
 
 
 def cpu_baseline(wl, budget_s):
-    """The oracle, as it stands, on a bounded sample: one oracle-quantised
-    cache (prepared outside the timed region) and as many Full-mode decode
-    queries as fit in the budget."""
+    """The oracle, as it stands, on a bounded sample of the workload.
+
+    Inputs for one sequence are prepared outside the timed region; then the
+    oracle runs the workload's step for as many queries (sampler rows, chunk
+    queries) as fit in the budget, one at a time, timed by wall clock.  The
+    rate is the measured count over the measured time; in prefill-full the
+    chunk write is timed once and the step rate is B / (write + B x the mean
+    query time)."""
     import numpy as np
     import oracle
     from sparse_attention_decode_csa2_amd import workloads as W
     from threadpoolctl import threadpool_info
-    ws = wl.scaled(B=1, seed=wl.seed * 1000)
-    lat = W.bf16_bits(W.latent_rows(ws, 0, wl.N))
-    codes, scales = oracle.quantize_fp4(lat)
-    rope = W.bf16_bits(W.rope_rows(ws, 0, wl.N))[None] if wl.d_r else np.zeros((1, wl.N, 0), np.uint16)
-    keys = W.bf16_bits(W.index_keys(ws, 0))[None]
-    qs = [(W.bf16_bits(W.index_query(wl.scaled(B=1, seed=1000 + i))),
-           W.bf16_bits(W.attn_query(wl.scaled(B=1, seed=1000 + i)))) for i in range(16)]
+    bits = W.bf16_bits
+    mode = wl.mode
+    one = wl.scaled(B=1, seed=wl.seed * 1000)
+    prep = []
+
+    def cache(n):
+        if mode == "full":
+            codes, scales = oracle.quantize_fp4(bits(W.latent_rows(one, 0, n)))
+            prep.append(f"one oracle-quantised cache of {n} entries")
+        else:
+            c, sc = W.random_codes(one, 0, n)
+            codes, scales = c.numpy(), sc.numpy()
+            prep.append(f"one cache of {n} entries (seeded random FP4 codes and E4M3 scales)")
+        rope = bits(W.rope_rows(one, 0, n))[None] if wl.d_r else np.zeros((1, n, 0), np.uint16)
+        return codes[None], scales[None], rope
+
+    def queries(i):
+        w1 = wl.scaled(B=1, seed=1000 + i)
+        return bits(W.index_query(w1)) if wl.H_I else None, bits(W.attn_query(w1)) if wl.H else None
+
+    n_q = 16
+    qs = [queries(i) for i in range(n_q)] if mode != "sample" else []
+    fixed_s = 0.0
+    if mode in ("full", "prefill_full", "reindex", "pool_build"):
+        keys = bits(W.index_keys(one, 0))[None]
+    if mode in ("full", "prefill_full", "reindex", "reuse", "reuse_swa", "prefill_reuse"):
+        codes, scales, rope = cache(wl.N)
+    if mode == "prefill_full":
+        chunk = bits(W.prefill_chunk(one))
+        t0 = time.perf_counter()
+        oracle.quantize_fp4(chunk)
+        fixed_s = time.perf_counter() - t0
+        prep.append(f"the {wl.prefill_rows}-row chunk write timed once ({fixed_s:.2f} s)")
+    if mode == "reindex":
+        pools = [W.pool_blocks(wl.scaled(B=1, seed=1000 + i)) for i in range(n_q)]
+        pools = [(p.numpy(), nb.numpy()) for p, nb in pools]
+    if mode in ("reuse", "reuse_swa"):
+        lists = W.reuse_index(wl.scaled(B=n_q, seed=wl.seed * 1000)).numpy()
+    if mode == "prefill_reuse":
+        # the last chunk of the context sees all but its last few entries: lists
+        # uniform over the visible range stand in for the chunk's own lists
+        vis = int(W.chunk_visible(wl, 0))
+        lists = W.reuse_index(wl.scaled(B=n_q, N=vis, seed=wl.seed * 1000)).numpy()
+    if mode == "reuse_swa":
+        wcodes, wsig = oracle.quantize_fp8(bits(W.latent_rows(one, 0, wl.window, name="window")))
+        wrope = bits(W.rope_rows(one.scaled(seed=one.seed + 7919), 0, wl.window))[None]
+        wcodes, wsig = wcodes[None], wsig[None]
+    if mode == "sample":
+        rows = [W.vocab_logits(wl.scaled(B=1, seed=1000 + i)).numpy() for i in range(n_q)]
+        us = [W.sampler_uniforms(wl.scaled(B=1, seed=1000 + i)).numpy() for i in range(n_q)]
+
+    def run(i):
+        j = i % n_q
+        if mode == "sample":
+            oracle.sample(rows[j], wl.K, wl.temperature, wl.top_p, us[j])
+            return
+        qi, q = qs[j]
+        if mode in ("full", "prefill_full"):
+            oracle.decode_full(qi, None, keys, None, q, codes, scales, rope, wl.K, wl.sm_scale)
+        elif mode == "reindex":
+            oracle.decode_reindex(qi, None, keys, None, pools[j][0], pools[j][1], wl.block, q, codes, scales,
+                                  rope, wl.K, wl.sm_scale)
+        elif mode == "pool_build":
+            oracle.build_pool(oracle.index_full(qi, None, keys, None), None, wl.block, wl.P_max)
+        elif mode == "reuse":
+            oracle.decode_reuse(lists[j:j + 1], q, codes, scales, rope, wl.sm_scale)
+        elif mode == "reuse_swa":
+            o, l = oracle.decode_reuse(lists[j:j + 1], q, codes, scales, rope, wl.sm_scale)
+            ow, lw = oracle.swa_attn(q, wcodes, wsig, wrope, None, wl.sm_scale)
+            oracle.merge_branches(o, l, ow, lw)
+        elif mode == "prefill_reuse":
+            oracle.prefill_sparse_attn(q[:, None], codes, scales, rope, lists[j:j + 1][:, None], wl.sm_scale)
+        else:
+            raise ValueError(mode)
+
     n = 0
     t0 = time.perf_counter()
     while True:
-        qi, q = qs[n % len(qs)]
-        oracle.decode_full(qi, None, keys, None, q, codes[None], scales[None], rope, wl.K, wl.sm_scale)
+        run(n)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s and n >= 3:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} Full-mode decode queries (batch 1, {wl.N} entries, Top-{wl.K}) over one "
-                      f"oracle-quantised cache, {el:.1f} s; NumPy float64, BLAS threads={threads}"}
+    what = {"full": "Full-mode decode queries", "prefill_full": "Full-mode decode queries",
+            "reindex": "Reindex-mode decode queries", "reuse": "Reuse-mode decode queries",
+            "reuse_swa": "Reuse-mode decode queries with the window branch merged",
+            "pool_build": "pool constructions (Full scores + pool)", "sample": "sampler rows",
+            "prefill_reuse": "prefill chunk queries"}[mode]
+    if mode == "prefill_full":
+        value = wl.B / (fixed_s + wl.B * el / n)
+    else:
+        value = n / el
+    unit = "rows/s" if mode == "sample" else "queries/s"
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{n} {what} (batch 1, {wl.N} {'vocabulary logits' if mode == 'sample' else 'entries'}"
+                      f"{'' if mode == 'sample' else f', pool of {wl.P_max} blocks' if mode == 'pool_build' else f', Top-{wl.K}'}) in {el:.1f} s"
+                      f"{'; ' + '; '.join(prep) if prep else ''}; NumPy float64, BLAS threads={threads}"}
 
 
 def main():
@@ -378,22 +483,25 @@ def main():
     # sets), and per stage one graph of K launches of that stage alone.
     stream = torch.cuda.Stream()
 
-    def capture(fn, n):
+    def capture(fn, n, start):
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=stream):
             for i in range(n):
-                fn(i % R)
+                fn((start + i) % R)
         torch.cuda.synchronize()
         return g
 
     for i in range(min(args.warmup, R)):   # eager pass: sets up every buffer once
         step.step(i)
     torch.cuda.synchronize()
-    g_warm = capture(step.step, max(args.warmup, 1))
-    g_timed = capture(step.step, args.steps)
+    # the warm-up takes sets 0 .. W-1, the timed steps the next K sets (mod R),
+    # the per-stage graphs the K after those
+    W0 = max(args.warmup, 1)
+    g_warm = capture(step.step, W0, 0)
+    g_timed = capture(step.step, args.steps, W0)
     stages = step.stages
-    g_stage = {s: capture(getattr(step, s), args.steps) for s in stages}
+    g_stage = {s: capture(getattr(step, s), args.steps, W0 + args.steps) for s in stages}
 
     def timed(g):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -418,19 +526,19 @@ def main():
     # equal scores is unspecified), K launches on the stage's own score rows
     torch_topk_us = torch_sampler_us = None
     if wl.mode == "sample" and wl.top_p >= 1.0:
-        g_ts = capture(step.torch_sampler, args.steps)
+        g_ts = capture(step.torch_sampler, args.steps, W0 + args.steps)
         g_ts.replay()
         torch_sampler_us = 1000.0 * timed(g_ts) / args.steps
         del g_ts
     if "topk" in stages:
-        g_tt = capture(lambda r: torch.topk(step.scores, wl.K, dim=1), args.steps)
+        g_tt = capture(lambda r: torch.topk(step.scores, wl.K, dim=1), args.steps, 0)
         g_tt.replay()
         torch_topk_us = 1000.0 * timed(g_tt) / args.steps
         del g_tt
     # one step on its own with cold caches (what an isolated decode step
     # waits for, beside the steady-state rate above): a 512 MiB write evicts
     # the L2s and the Infinity Cache before each run; median of five
-    g_one = capture(step.step, 1)
+    g_one = capture(step.step, 1, 0)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = []
     for _ in range(5):
@@ -496,13 +604,15 @@ def main():
         "step_hbm_gbs": alg["step"] / (ms_per_step * 1e-3) / 1e9,
         "single_step_us_cold": round(single_step_us, 2),
         "step_alg_bytes": alg["step"],
+        "step_read_bytes": step.touched,
+        "timed_distinct_sets": min(args.steps, R),
         "stage_us": {s: round(v, 3) for s, v in stage_us.items()},
         "stage_gbs": {s: round(alg[s] / (stage_us[s] * 1e-6) / 1e9, 1) for s in stages},
         "torch_topk_us": None if torch_topk_us is None else round(torch_topk_us, 3),
         "torch_sampler_us": None if torch_sampler_us is None else round(torch_sampler_us, 3),
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline and wl.mode == "full":
+    if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
