@@ -35,6 +35,12 @@
  *    state; calls on different streams may run concurrently.  Where a kernel
  *    needs scratch space the caller passes a workspace whose size comes from
  *    the matching *_workspace_bytes() query.
+ *  - Each kernel launch holds fewer than 2^32 work-items (workgroups x
+ *    threads).  A call whose sizes would need a larger launch (e.g. an index
+ *    call with B * N_cap >= 2^30, a Top-K with B * ceil(M / 16384) >= 2^22
+ *    rows x chunks, an attention call with about 2^22 queries at 64 heads, or
+ *    a K so large that its slices alone pass the limit) returns
+ *    CSA2_ERR_RANGE before anything is enqueued.
  */
 #ifndef CSA2_H
 #define CSA2_H

@@ -91,9 +91,24 @@ def _check(fn, st):
         raise Csa2Error(fn, st)
 
 
-def _need(t, dtype, name):
+def _need(t, dtype, name, shape=None):
+    """Input check: a contiguous tensor of `dtype` (and of `shape` when given;
+    None in `shape` accepts any size in that dimension)."""
     if t.dtype != dtype or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dtype} tensor")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(w is not None and d != w for d, w in zip(t.shape, shape))):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _out(t, shape, dtype, device, name):
+    """An output buffer: allocated when None, else checked to be exactly the
+    contiguous `shape` / `dtype` the kernels write (the C ABI sees only a
+    pointer, so this is the only guard on its size)."""
+    if t is None:
+        return torch.empty(*shape, dtype=dtype, device=device)
+    _need(t, dtype, name, shape)
+    return t
 
 
 # ------------------------------------------------------------------ the FP4 cache
@@ -108,6 +123,27 @@ def _row_stride(t, elem_bytes, name):
     if t.dim() == 3 and t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) != t.shape[1] * rs:
         raise ValueError(f"{name}: sequences must be evenly spaced rows")
     return rs * elem_bytes
+
+
+def _cache_views(codes, scales, rope, d_r, dims):
+    """The three views of an FP4 cache: codes u8 [..., d_c/2], scales u8
+    [..., d_c/16], rope bf16 [..., d_r] with the same leading (sequence, row)
+    shape, so that every row the kernels address exists in all three."""
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError("codes and scales must be uint8 views")
+    if dims == 2 and codes.dim() == 3 and codes.shape[0] == 1:
+        dims = 3   # one sequence's cache, as [1, cap, *] views
+    if codes.dim() != dims or scales.dim() != dims:
+        raise ValueError(f"codes and scales must have {dims} dimensions")
+    if tuple(scales.shape[:-1]) != tuple(codes.shape[:-1]) or scales.shape[-1] * 8 != codes.shape[-1]:
+        raise ValueError(f"scales {tuple(scales.shape)} do not match codes {tuple(codes.shape)} "
+                         f"(one scale byte per 16 channels, the same rows)")
+    if d_r > 0:
+        if rope is None or rope.dtype != torch.bfloat16 or rope.dim() != dims:
+            raise ValueError(f"rope must be a bf16 view with {dims} dimensions")
+        if tuple(rope.shape[:-1]) != tuple(codes.shape[:-1]) or rope.shape[-1] != d_r:
+            raise ValueError(f"rope {tuple(rope.shape)} does not match codes {tuple(codes.shape)} with "
+                             f"{d_r} RoPE channels")
 
 
 def alloc_cache(B, N, d_c, d_r, device="cuda", layout="record"):
@@ -145,8 +181,15 @@ def csa2_quantize_fp4(x, codes, scales, dst_row0=0, rope_src=None, rope_dst=None
     copies the RoPE part rope_src [R, d_r] when given."""
     lib = load()
     _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError(f"x must be [R, d_c], got {tuple(x.shape)}")
     R, d_c = x.shape
-    d_r = 0 if rope_src is None else rope_src.shape[1]
+    d_r = 0 if rope_src is None else rope_src.shape[-1]
+    if rope_src is not None:
+        _need(rope_src, torch.bfloat16, "rope_src", (R, None))
+    _cache_views(codes, scales, rope_dst, d_r, 2)
+    if codes.shape[1] * 2 != d_c:
+        raise ValueError(f"codes rows hold {codes.shape[1] * 2} channels, x has {d_c}")
     cs = _row_stride(codes, 1, "codes")
     ss = _row_stride(scales, 1, "scales")
     rs = _row_stride(rope_dst, 2, "rope_dst") if d_r else 0
@@ -160,13 +203,26 @@ def csa2_quantize_fp4(x, codes, scales, dst_row0=0, rope_src=None, rope_dst=None
 # ------------------------------------------------------------------ a1 / a2
 
 
+def _index_inputs(q_idx, k_idx, w, n_valid):
+    _need(q_idx, torch.bfloat16, "q_idx")
+    if q_idx.dim() != 3:
+        raise ValueError(f"q_idx must be [B, H_I, D_I], got {tuple(q_idx.shape)}")
+    B, H_I, D_I = q_idx.shape
+    _need(k_idx, torch.bfloat16, "k_idx")
+    if k_idx.dim() != 3 or k_idx.shape[0] < B or k_idx.shape[2] != D_I:
+        raise ValueError(f"k_idx must be [>= {B}, N_cap, {D_I}], got {tuple(k_idx.shape)}")
+    if w is not None:
+        _need(w, torch.float32, "w", (B, H_I))
+    if n_valid is not None:
+        _need(n_valid, torch.int32, "n_valid", (B,))
+    return B, H_I, D_I, k_idx.shape[1]
+
+
 def csa2_index_full(q_idx, k_idx, scores=None, w=None, n_valid=None):
     """Full-mode indexer scores [B, N_cap] (f32)."""
     lib = load()
-    B, H_I, D_I = q_idx.shape
-    N_cap = k_idx.shape[1]
-    if scores is None:
-        scores = torch.empty(B, N_cap, dtype=torch.float32, device=k_idx.device)
+    B, H_I, D_I, N_cap = _index_inputs(q_idx, k_idx, w, n_valid)
+    scores = _out(scores, (B, N_cap), torch.float32, k_idx.device, "scores")
     st = lib.csa2_index_full(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(n_valid), B, H_I, D_I, N_cap,
                              _ptr(scores), _stream())
     _check("csa2_index_full", st)
@@ -177,14 +233,13 @@ def csa2_index_pool(q_idx, k_idx, pool_blocks, n_blocks, block=8, scores=None, p
                     n_valid=None):
     """Reindex-mode pool scores and global positions, both [B, P_max*block]."""
     lib = load()
-    B, H_I, D_I = q_idx.shape
-    N_cap = k_idx.shape[1]
+    B, H_I, D_I, N_cap = _index_inputs(q_idx, k_idx, w, n_valid)
+    _need(pool_blocks, torch.int32, "pool_blocks", (B, None))
+    _need(n_blocks, torch.int32, "n_blocks", (B,))
     P_max = pool_blocks.shape[1]
     M = P_max * block
-    if scores is None:
-        scores = torch.empty(B, M, dtype=torch.float32, device=k_idx.device)
-    if positions is None:
-        positions = torch.empty(B, M, dtype=torch.int32, device=k_idx.device)
+    scores = _out(scores, (B, M), torch.float32, k_idx.device, "scores")
+    positions = _out(positions, (B, M), torch.int32, k_idx.device, "positions")
     st = lib.csa2_index_pool(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(n_valid), _ptr(pool_blocks),
                              _ptr(n_blocks), B, H_I, D_I, N_cap, P_max, block, _ptr(scores),
                              _ptr(positions), _stream())
@@ -204,16 +259,17 @@ def csa2_topk(scores, K, ids=None, n_valid=None, out_idx=None, out_score=None, w
     """Top-K (score desc, id asc): returns (idx i32 [B, K], score f32 [B, K] or None)."""
     lib = load()
     _need(scores, torch.float32, "scores")
-    if ids is not None:
-        _need(ids, torch.int32, "ids")
-    if n_valid is not None:
-        _need(n_valid, torch.int32, "n_valid")
+    if scores.dim() != 2:
+        raise ValueError(f"scores must be [B, M], got {tuple(scores.shape)}")
     B, M = scores.shape
+    if ids is not None:
+        _need(ids, torch.int32, "ids", (B, M))
+    if n_valid is not None:
+        _need(n_valid, torch.int32, "n_valid", (B,))
     dev = scores.device
-    if out_idx is None:
-        out_idx = torch.empty(B, K, dtype=torch.int32, device=dev)
-    if out_score is None and want_score:
-        out_score = torch.empty(B, K, dtype=torch.float32, device=dev)
+    out_idx = _out(out_idx, (B, K), torch.int32, dev, "out_idx")
+    if out_score is not None or want_score:
+        out_score = _out(out_score, (B, K), torch.float32, dev, "out_score")
     need = csa2_topk_workspace_bytes(B, M, K)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -232,13 +288,15 @@ def csa2_sample_draw(cand_idx, cand_score, temperature, top_p, u, token=None, pr
     u f32 [B] -> (token i32 [B], prob f32 [B], n_kept i32 [B])."""
     lib = load()
     _need(cand_idx, torch.int32, "cand_idx")
-    _need(cand_score, torch.float32, "cand_score")
-    _need(u, torch.float32, "u")
+    if cand_idx.dim() != 2:
+        raise ValueError(f"cand_idx must be [B, K], got {tuple(cand_idx.shape)}")
     B, K = cand_idx.shape
+    _need(cand_score, torch.float32, "cand_score", (B, K))
+    _need(u, torch.float32, "u", (B,))
     dev = cand_idx.device
-    token = torch.empty(B, dtype=torch.int32, device=dev) if token is None else token
-    prob = torch.empty(B, dtype=torch.float32, device=dev) if prob is None else prob
-    n_kept = torch.empty(B, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    token = _out(token, (B,), torch.int32, dev, "token")
+    prob = _out(prob, (B,), torch.float32, dev, "prob")
+    n_kept = _out(n_kept, (B,), torch.int32, dev, "n_kept")
     st = lib.csa2_sample_draw(_ptr(cand_idx), _ptr(cand_score), B, K, float(temperature), float(top_p), _ptr(u),
                               _ptr(token), _ptr(prob), _ptr(n_kept), _stream())
     _check("csa2_sample_draw", st)
@@ -253,12 +311,14 @@ def csa2_sample(logits, K, temperature, top_p, u, token=None, prob=None, n_kept=
     """Top-K over logits f32 [B, V], then the draw: (token, prob, n_kept)."""
     lib = load()
     _need(logits, torch.float32, "logits")
-    _need(u, torch.float32, "u")
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [B, V], got {tuple(logits.shape)}")
     B, V = logits.shape
+    _need(u, torch.float32, "u", (B,))
     dev = logits.device
-    token = torch.empty(B, dtype=torch.int32, device=dev) if token is None else token
-    prob = torch.empty(B, dtype=torch.float32, device=dev) if prob is None else prob
-    n_kept = torch.empty(B, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    token = _out(token, (B,), torch.int32, dev, "token")
+    prob = _out(prob, (B,), torch.float32, dev, "prob")
+    n_kept = _out(n_kept, (B,), torch.int32, dev, "n_kept")
     if workspace is None:
         workspace = torch.empty(max(csa2_sample_workspace_bytes(B, V, K), 16), dtype=torch.uint8, device=dev)
     st = lib.csa2_sample(_ptr(logits), B, V, K, float(temperature), float(top_p), _ptr(u), _ptr(token),
@@ -284,9 +344,18 @@ def csa2_quantize_fp8(x, codes, sigma, dst_row0=0, rope_src=None, rope_dst=None)
     of codes u8 [cap, d_c] / sigma f32 [cap] (and the RoPE part, copied)."""
     lib = load()
     _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError(f"x must be [R, d_c], got {tuple(x.shape)}")
     R, d_c = x.shape
-    d_r = 0 if rope_src is None else rope_src.shape[1]
+    d_r = 0 if rope_src is None else rope_src.shape[-1]
+    if rope_src is not None:
+        _need(rope_src, torch.bfloat16, "rope_src", (R, None))
+    if codes.dtype != torch.uint8 or codes.dim() != 2 or codes.shape[1] != d_c:
+        raise ValueError(f"codes must be a uint8 [cap, {d_c}] view, got {tuple(codes.shape)}")
     cap = codes.shape[0]
+    _need(sigma, torch.float32, "sigma", (cap,))
+    if d_r > 0 and (rope_dst is None or rope_dst.dtype != torch.bfloat16 or tuple(rope_dst.shape) != (cap, d_r)):
+        raise ValueError(f"rope_dst must be a bf16 [{cap}, {d_r}] view")
     cs = _row_stride(codes, 1, "codes")
     rs = _row_stride(rope_dst, 2, "rope_dst") if d_r > 0 else 0
     st = lib.csa2_quantize_fp8(_ptr(x), R, d_c, _ptr(rope_src), d_r, _ptr(codes), cs, _ptr(sigma),
@@ -301,16 +370,27 @@ def csa2_swa_attn_fp8(q, codes, sigma, rope, sm_scale=None, n_win=None, merge_ou
     (out f32 [B, H, d_c], lse f32 [B, H])."""
     lib = load()
     _need(q, torch.bfloat16, "q")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, H, D], got {tuple(q.shape)}")
     B, H, D = q.shape
+    if codes.dtype != torch.uint8 or codes.dim() != 3 or codes.shape[0] != B:
+        raise ValueError(f"codes must be a uint8 [{B}, W_cap, d_c] view, got {tuple(codes.shape)}")
     W_cap, d_c = codes.shape[1], codes.shape[2]
     d_r = D - d_c
+    _need(sigma, torch.float32, "sigma", (B, W_cap))
+    if d_r > 0 and (rope is None or rope.dtype != torch.bfloat16 or tuple(rope.shape) != (B, W_cap, d_r)):
+        raise ValueError(f"rope must be a bf16 [{B}, {W_cap}, {d_r}] view")
+    if n_win is not None:
+        _need(n_win, torch.int32, "n_win", (B,))
+    if merge_out is not None:
+        _need(merge_out, torch.float32, "merge_out", (B, H, d_c))
+    if merge_lse is not None:
+        _need(merge_lse, torch.float32, "merge_lse", (B, H))
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     dev = q.device
-    if out is None:
-        out = torch.empty(B, H, d_c, dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    out = _out(out, (B, H, d_c), torch.float32, dev, "out")
+    lse = _out(lse, (B, H), torch.float32, dev, "lse")
     cs = _row_stride(codes, 1, "codes")
     rs = _row_stride(rope, 2, "rope") if d_r > 0 else 0
     st = lib.csa2_swa_attn_fp8(_ptr(q), _ptr(codes), cs, _ptr(sigma), _ptr(rope if d_r > 0 else None), rs,
@@ -328,13 +408,15 @@ def csa2_build_pool(scores, P_max, block=8, n_valid=None, pool_blocks=None, n_bl
     """Block-level candidate pool from a Full layer's scores f32 [B, M]:
     returns (pool_blocks i32 [B, P_max], n_blocks i32 [B])."""
     lib = load()
+    _need(scores, torch.float32, "scores")
+    if scores.dim() != 2:
+        raise ValueError(f"scores must be [B, M], got {tuple(scores.shape)}")
     B, M = scores.shape
     dev = scores.device
-    _need(scores, torch.float32, "scores")
-    if pool_blocks is None:
-        pool_blocks = torch.empty(B, P_max, dtype=torch.int32, device=dev)
-    if n_blocks is None:
-        n_blocks = torch.empty(B, dtype=torch.int32, device=dev)
+    if n_valid is not None:
+        _need(n_valid, torch.int32, "n_valid", (B,))
+    pool_blocks = _out(pool_blocks, (B, P_max), torch.int32, dev, "pool_blocks")
+    n_blocks = _out(n_blocks, (B,), torch.int32, dev, "n_blocks")
     need = csa2_build_pool_workspace_bytes(B, M, block, P_max)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
@@ -356,23 +438,25 @@ def csa2_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, l
     (out f32 [B, H, d_c], lse f32 [B, H])."""
     lib = load()
     _need(q, torch.bfloat16, "q")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, H, D], got {tuple(q.shape)}")
     B, H, D = q.shape
     N_cap = codes.shape[1]
     d_c = codes.shape[2] * 2
     d_r = D - d_c
+    _cache_views(codes, scales, rope, d_r, 3)
     _need(idx, torch.int32, "idx")
-    K = idx.shape[1]
     if idx.dim() != 2 or idx.shape[0] != B:
         raise ValueError(f"idx must be [B={B}, K], got {tuple(idx.shape)}")
-    if codes.shape[0] < B or scales.shape[0] < B or (d_r > 0 and rope.shape[0] < B):
+    K = idx.shape[1]
+    if codes.shape[0] < B:
         raise ValueError(f"the cache holds {codes.shape[0]} sequences, {B} queries need one each")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     dev = q.device
-    if out is None:
-        out = torch.empty(B, H, d_c, dtype=torch.float32, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    out = _out(out, (B, H, d_c), torch.float32, dev, "out")
+    if lse is not None or want_lse:
+        lse = _out(lse, (B, H), torch.float32, dev, "lse")
     need = csa2_sparse_attn_workspace_bytes(B, H, d_c, K)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -395,22 +479,24 @@ def csa2_prefill_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out
     lib = load()
     _need(q, torch.bfloat16, "q")
     _need(idx, torch.int32, "idx")
+    if q.dim() != 4:
+        raise ValueError(f"q must be [S, T, H, D], got {tuple(q.shape)}")
     S, T, H, D = q.shape
     N_cap = codes.shape[1]
     d_c = codes.shape[2] * 2
     d_r = D - d_c
-    K = idx.shape[2]
-    if tuple(idx.shape[:2]) != (S, T):
+    _cache_views(codes, scales, rope, d_r, 3)
+    if idx.dim() != 3 or tuple(idx.shape[:2]) != (S, T):
         raise ValueError(f"idx must be [S={S}, T={T}, K], got {tuple(idx.shape)}")
-    if codes.shape[0] < S or scales.shape[0] < S or (d_r > 0 and rope.shape[0] < S):
+    K = idx.shape[2]
+    if codes.shape[0] < S:
         raise ValueError(f"the cache holds {codes.shape[0]} sequences, the chunk needs {S}")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     dev = q.device
-    if out is None:
-        out = torch.empty(S, T, H, d_c, dtype=torch.float32, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty(S, T, H, dtype=torch.float32, device=dev)
+    out = _out(out, (S, T, H, d_c), torch.float32, dev, "out")
+    if lse is not None or want_lse:
+        lse = _out(lse, (S, T, H), torch.float32, dev, "lse")
     need = csa2_sparse_attn_workspace_bytes(S * T, H, d_c, K)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

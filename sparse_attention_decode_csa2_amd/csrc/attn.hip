@@ -845,11 +845,11 @@ static int attn_heads_per_wg(int B, int H, int d_c) {
 static void attn_plan(int B, int H, int K, int d_c, int* n_split, int* per_split) {
   const int hpw = attn_heads_per_wg(B, H, d_c);
   const int n_hg = (H + hpw - 1) / hpw;
-  const int tiles = (K + AT_TILE - 1) / AT_TILE;
-  const int base = B * n_hg;
+  const int tiles = (int)(((int64_t)K + AT_TILE - 1) / AT_TILE);
+  const int64_t base = (int64_t)B * n_hg;
   // about one workgroup per CU: measured, splitting further (two per CU)
   // costs more in partials and contention than it gains in parallelism
-  int s = base >= 256 ? 1 : (256 + base - 1) / max(base, 1);
+  int s = base >= 256 ? 1 : (int)((256 + base - 1) / (base > 1 ? base : 1));
   s = max(s, (tiles + AT_IDS / AT_TILE - 1) / (AT_IDS / AT_TILE));  // <= 8 tiles per split
   s = max(1, min(s, tiles));
   const int tps = (tiles + s - 1) / s;
@@ -857,6 +857,22 @@ static void attn_plan(int B, int H, int K, int d_c, int* n_split, int* per_split
   *n_split = s;
   *per_split = tps * AT_TILE;
 }
+
+// The attention grid (and the combine's, when the query is split).
+int64_t attn_launch_items(int B, int H, int d_c, int K) {
+  if (B <= 0) return 0;
+  int s, ps;
+  attn_plan(B, H, K, d_c, &s, &ps);
+  const int hpw = attn_heads_per_wg(B, H, d_c);
+  const int n_hg = (H + hpw - 1) / hpw;
+  const bool spread = B < 8;
+  const int64_t groups = spread ? ((int64_t)B * s + 7) / 8 : ((int64_t)B + 7) / 8 * s;
+  const int64_t items = groups * 8 * n_hg * (hpw == 32 ? 512 : 256);
+  const int64_t comb = s > 1 ? (spread ? (int64_t)B * H : ((int64_t)B + 7) / 8 * 8 * H) * 128 : 0;
+  return items > comb ? items : comb;
+}
+
+int64_t swa_launch_items(int B, int H) { return ((int64_t)B + 7) / 8 * 8 * ((H + 15) / 16) * 256; }
 
 // Workspace: partial outputs f32 [B, H, s, d_c], then (max, sum) f32 [B, H, s, 2].
 size_t attn_workspace_bytes(int B, int H, int d_c, int K) {

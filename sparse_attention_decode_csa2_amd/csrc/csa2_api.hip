@@ -9,6 +9,7 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool opt_aligned16(const void* p) { return p == nullptr || aligned16(p); }
 inline int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 inline hipStream_t as_stream(csa2_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool too_large(int64_t items) { return items > csa2::kMaxLaunchItems; }
 
 }  // namespace
 
@@ -57,6 +58,7 @@ int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint
   if (!aligned16(x) || !opt_aligned16(rope_src)) return CSA2_ERR_ALIGN;
   const int st = check_cache(d_c, d_r, codes, codes_stride, scales, scales_stride, rope_dst, rope_stride);
   if (st != CSA2_OK) return st;
+  if (too_large(csa2::quantize_fp4_launch_items(n_rows, d_c, d_r))) return CSA2_ERR_RANGE;
   const csa2::CacheRef c{codes, codes_stride, scales, scales_stride, d_r > 0 ? rope_dst : nullptr, rope_stride};
   return hip_status(csa2::launch_quantize_fp4(x, n_rows, d_c, d_r > 0 ? rope_src : nullptr, d_r, c,
                                               dst_row0, as_stream(stream)));
@@ -79,6 +81,7 @@ int csa2_quantize_fp8(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint
       codes_stride % 8 != 0 || (reinterpret_cast<uintptr_t>(sigma) & 3u) != 0 ||
       (d_r > 0 && (!aligned16(rope_dst) || rope_stride % 16 != 0)))
     return CSA2_ERR_ALIGN;
+  if (too_large(csa2::quantize_fp8_launch_items(n_rows))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_quantize_fp8(x, n_rows, d_c, d_r > 0 ? rope_src : nullptr, d_r, codes,
                                               codes_stride, sigma, d_r > 0 ? rope_dst : nullptr, rope_stride,
                                               dst_row0, as_stream(stream)));
@@ -106,6 +109,7 @@ int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
   }
   const int st = check_index_common(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, scores);
   if (st != CSA2_OK) return st;
+  if (too_large(csa2::index_launch_items(B, N_cap, false))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_index(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, nullptr,
                                        nullptr, 0, 1, scores, nullptr, as_stream(stream)));
 }
@@ -121,6 +125,7 @@ int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
   if (st != CSA2_OK) return st;
   if (!pool_blocks || !n_blocks || !positions) return CSA2_ERR_NULL;
   if (!aligned16(pool_blocks) || !aligned16(n_blocks) || !aligned16(positions)) return CSA2_ERR_ALIGN;
+  if (too_large(csa2::index_launch_items(B, (int64_t)P_max * block, true))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_index(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, pool_blocks,
                                        n_blocks, P_max, block, scores, positions,
                                        as_stream(stream)));
@@ -144,6 +149,7 @@ int csa2_swa_attn_fp8(const uint16_t* q, const uint8_t* codes, int64_t codes_str
       codes_stride % 16 != 0 || (reinterpret_cast<uintptr_t>(sigma) & 3u) != 0 ||
       (d_r > 0 && (!aligned16(rope) || rope_stride % 16 != 0)))))
     return CSA2_ERR_ALIGN;
+  if (too_large(csa2::swa_launch_items(B, H))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_swa_attn(q, codes, codes_stride, sigma, d_r > 0 ? rope : nullptr, rope_stride,
                                           n_win, B, H, d_r, W_cap, sm_scale, merge_out, merge_lse, out, lse,
                                           as_stream(stream)));
@@ -165,6 +171,7 @@ int csa2_build_pool(const float* scores, const int32_t* n_valid, int32_t B, int6
       !aligned16(workspace))
     return CSA2_ERR_ALIGN;
   if (workspace_bytes < csa2::pool_workspace_bytes(B, M, block, P_max)) return CSA2_ERR_WORKSPACE;
+  if (too_large(csa2::pool_launch_items(B, M, block, P_max))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_build_pool(scores, n_valid, B, M, block, P_max, pool_blocks, n_blocks,
                                             workspace, as_stream(stream)));
 }
@@ -187,6 +194,7 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, i
   const size_t need = csa2::topk_workspace_bytes(B, M, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;
+  if (too_large(csa2::topk_launch_items(B, M, K))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_topk(scores, ids, n_valid, B, M, K, out_idx, out_score, workspace,
                                       as_stream(stream)));
 }
@@ -206,6 +214,7 @@ int csa2_sample_draw(const int32_t* cand_idx, const float* cand_score, int32_t B
   if (!aligned16(cand_idx) || !aligned16(cand_score) || !aligned16(u) || !aligned16(token) ||
       !opt_aligned16(prob) || !opt_aligned16(n_kept))
     return CSA2_ERR_ALIGN;
+  if (too_large(csa2::sample_draw_launch_items(B))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_sample_draw(cand_idx, cand_score, B, K, temperature, top_p, u, token, prob,
                                              n_kept, as_stream(stream)));
 }
@@ -227,6 +236,8 @@ int csa2_sample(const float* logits, int32_t B, int64_t V, int32_t K, float temp
       !opt_aligned16(n_kept) || !aligned16(workspace))
     return CSA2_ERR_ALIGN;
   if (workspace_bytes < csa2::sample_workspace_bytes(B, V, K)) return CSA2_ERR_WORKSPACE;
+  if (too_large(csa2::topk_launch_items(B, V, K)) || too_large(csa2::sample_draw_launch_items(B)))
+    return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_sample(logits, B, V, K, temperature, top_p, u, token, prob, n_kept, workspace,
                                         as_stream(stream)));
 }
@@ -256,6 +267,7 @@ static int sparse_attn_checked(const uint16_t* q, const uint8_t* codes, int64_t 
   if (N_cap > 0 && (N_cap > lim / codes_stride || N_cap > lim / scales_stride ||
                     (d_r > 0 && N_cap > lim / rope_stride)))
     return CSA2_ERR_RANGE;
+  if (too_large(csa2::attn_launch_items(B, H, d_c, K))) return CSA2_ERR_RANGE;
   const size_t need = csa2::attn_workspace_bytes(B, H, d_c, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;

@@ -8,6 +8,20 @@
 
 namespace csa2 {
 
+// Work-items (workgroups x threads) of the largest single launch a call makes,
+// computed by the same grid rules the launches use: one launch holds fewer
+// than 2^32, so the entry points refuse larger calls (CSA2_ERR_RANGE) before
+// anything is enqueued.
+constexpr int64_t kMaxLaunchItems = ((int64_t)1 << 32) - 1;
+int64_t quantize_fp4_launch_items(int64_t n_rows, int d_c, int d_r);
+int64_t quantize_fp8_launch_items(int64_t n_rows);
+int64_t index_launch_items(int B, int64_t M, bool pool);
+int64_t topk_launch_items(int B, int64_t M, int K);
+int64_t pool_launch_items(int B, int64_t M, int block, int P_max);
+int64_t attn_launch_items(int B, int H, int d_c, int K);
+int64_t swa_launch_items(int B, int H);
+int64_t sample_draw_launch_items(int B);
+
 // Row strides are in bytes and already resolved (non-zero).
 struct CacheRef {
   uint8_t* codes;

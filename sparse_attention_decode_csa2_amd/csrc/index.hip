@@ -161,19 +161,33 @@ __global__ __launch_bounds__(256) void index_kernel(
   }
 }
 
+// Grid of the indexer: 16-key tiles, four waves per workgroup, `tpw` tiles per
+// wave.  Tiles per wave, measured: Full mode is fastest with one (its
+// contiguous loads keep enough in flight; prefill-full-1m 80.6 us against
+// 86.7 with four); pool mode, whose loads wait for block lookups, with two once
+// the grid fills the GPU (reindex-1m 28.7 us against 30.4 with four).
+static void index_grid(int B, int64_t M, bool pool, int* tpw, int64_t* wg_per_row) {
+  const int64_t tiles_per_row = (M + 15) / 16;
+  const int64_t total_tiles = tiles_per_row * B;
+  *tpw = (pool && total_tiles >= 2 * 4 * 2048) ? 2 : 1;
+  *wg_per_row = (tiles_per_row + 4 * *tpw - 1) / (4 * *tpw);
+}
+
+int64_t index_launch_items(int B, int64_t M, bool pool) {
+  int tpw;
+  int64_t wpr;
+  index_grid(B, M, pool, &tpw, &wpr);
+  return wpr * B * 256;
+}
+
 template <int KS, bool POOL>
 static hipError_t launch_index_ks(const uint16_t* q, const float* w, const uint16_t* k,
                                   const int32_t* n_valid, int B, int H_I, int64_t N_cap,
                                   const int32_t* pool, const int32_t* n_blocks, int P_max, int block,
                                   int64_t M, float* scores, int32_t* positions, hipStream_t stream) {
-  const int64_t tiles_per_row = (M + 15) / 16;
-  const int64_t total_tiles = tiles_per_row * B;
-  // Tiles per wave, measured: Full mode is fastest with one (its contiguous
-  // loads keep enough in flight; prefill-full-1m 80.6 us against 86.7 with
-  // four); pool mode, whose loads wait for block lookups, with two once the
-  // grid fills the GPU (reindex-1m 28.7 us against 30.4 with four).
-  const int tpw = (POOL && total_tiles >= 2 * 4 * 2048) ? 2 : 1;
-  const int64_t wg_per_row = (tiles_per_row + 4 * tpw - 1) / (4 * tpw);
+  int tpw;
+  int64_t wg_per_row;
+  index_grid(B, M, POOL, &tpw, &wg_per_row);
   const dim3 grid((unsigned)(wg_per_row * B)), blk(256);
 #define CSA2_IDX_LAUNCH(T)                                                                          \
   hipLaunchKernelGGL((index_kernel<KS, T, POOL>), grid, blk, 0, stream, q, w, k, n_valid, H_I, N_cap, \

@@ -62,6 +62,12 @@ size_t pool_workspace_bytes(int B, int64_t M, int block, int P_max) {
          topk_workspace_bytes(B, NB, P_max);
 }
 
+int64_t pool_launch_items(int B, int64_t M, int block, int P_max) {
+  const int64_t NB = (M + block - 1) / block;
+  const int64_t reduce = (int64_t)B * ((NB + 255) / 256) * 256;
+  return reduce > topk_launch_items(B, NB, P_max) ? reduce : topk_launch_items(B, NB, P_max);
+}
+
 hipError_t launch_build_pool(const float* scores, const int32_t* n_valid, int B, int64_t M, int block,
                              int P_max, int32_t* pool_blocks, int32_t* n_blocks, void* workspace,
                              hipStream_t stream) {

@@ -58,13 +58,19 @@ __global__ __launch_bounds__(256) void quantize_fp4_kernel(
   }
 }
 
+// One thread per 16-channel group and per 8 RoPE channels, 256 per workgroup.
+int64_t quantize_fp4_launch_items(int64_t n_rows, int d_c, int d_r) {
+  const int64_t total = n_rows * (d_c / 16) + (d_r > 0 ? n_rows * (d_r / 8) : 0);
+  return (total + 255) / 256 * 256;
+}
+
 hipError_t launch_quantize_fp4(const uint16_t* x, int64_t n_rows, int d_c, const uint16_t* rope_src,
                                int d_r, CacheRef cache, int64_t dst_row0, hipStream_t stream) {
   const int64_t n_groups = n_rows * (d_c / 16);
   const int64_t n_rope = d_r > 0 ? n_rows * (d_r / 8) : 0;
   const int64_t total = n_groups + n_rope;
   if (total == 0) return hipSuccess;
-  const int64_t blocks = (total + 255) / 256;
+  const int64_t blocks = quantize_fp4_launch_items(n_rows, d_c, d_r) / 256;
   hipLaunchKernelGGL(quantize_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n_rows,
                      d_c, rope_src, d_r, cache, dst_row0, n_groups, n_rope);
   return hipGetLastError();
@@ -149,6 +155,9 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(
       *reinterpret_cast<u32x4*>(rd + 2 * c0) = *reinterpret_cast<const u32x4*>(rope_src + r * d_r + c0);
   }
 }
+
+// One wave per row, four rows per workgroup.
+int64_t quantize_fp8_launch_items(int64_t n_rows) { return (n_rows + 3) / 4 * 256; }
 
 hipError_t launch_quantize_fp8(const uint16_t* x, int64_t n_rows, int d_c, const uint16_t* rope_src, int d_r,
                                uint8_t* codes, int64_t codes_stride, float* sigma, uint16_t* rope_dst,

@@ -222,6 +222,8 @@ size_t sample_workspace_bytes(int B, int64_t V, int K) {
   return 2 * align256((size_t)B * K * 4) + topk_workspace_bytes(B, V, K);
 }
 
+int64_t sample_draw_launch_items(int B) { return (int64_t)B * SMP_T; }
+
 hipError_t launch_sample_draw(const int32_t* cand_idx, const float* cand_score, int B, int K, float temperature,
                               float top_p, const float* u, int32_t* token, float* prob, int32_t* n_kept,
                               hipStream_t stream) {

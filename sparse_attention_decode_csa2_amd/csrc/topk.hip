@@ -923,6 +923,13 @@ static int topk_levels(int64_t M, int K, int64_t* chunks_per_level, int max_leve
   return n;
 }
 
+// The first level has the most workgroups: one per 16384-candidate chunk.
+int64_t topk_launch_items(int B, int64_t M, int K) {
+  int64_t ch[16];
+  topk_levels(M, K, ch, 16);
+  return (int64_t)B * ch[0] * TK_T;
+}
+
 size_t topk_workspace_bytes(int B, int64_t M, int K) {
   int64_t ch[16];
   const int n = topk_levels(M, K, ch, 16);

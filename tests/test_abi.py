@@ -270,3 +270,101 @@ def test_binding_rejects_caches_too_small_for_the_queries(lib):
         c.csa2_prefill_sparse_attn_fp4(qp, codes, scales, rope, torch.zeros(3, 5, 8, dtype=torch.int32))
     with pytest.raises(ValueError, match="idx"):
         c.csa2_prefill_sparse_attn_fp4(qp[:2], codes, scales, rope, torch.zeros(2, 4, 8, dtype=torch.int32))
+
+
+def test_launches_past_2_32_work_items_are_refused(lib):
+    """Sizes whose launch would hold 2^32 work-items or more return
+    CSA2_ERR_RANGE from host validation (nothing is launched)."""
+    # index: 16-key tiles, 4 waves of 64 threads per 64 keys -> 4 threads per key
+    assert lib.csa2_index_full(A, N, A, N, 1 << 12, 8, 128, 1 << 18, A, N) == RANGE
+    assert lib.csa2_index_full(A, N, A, N, 8, 8, 128, 1 << 18, A, N) != RANGE
+    # Top-K: one 1024-thread workgroup per 16384 candidates in the first level
+    M = 1 << 30
+    assert lib.csa2_topk(A, N, N, 1 << 10, M, 512, A, N, A, 1 << 62, N) == RANGE
+    # attention: 2^22 queries x 2 head groups x 512 threads = 2^32
+    f = lib.csa2_sparse_attn_fp4
+    sm = ctypes.c_float(0.04)
+    assert f(A, A, 512, A, 512, A, 512, A, 512, 1 << 22, 64, 512, 64, 100, sm, A, N, A, 1 << 62, N) == RANGE
+    # a K whose slices alone pass the limit: 2^25 tiles of 64 entries, 8 tiles a slice
+    assert f(A, A, 512, A, 512, A, 512, A, (1 << 31) - 1, 1, 64, 512, 64, 100, sm, A, N, A, 1 << 62, N) == RANGE
+    p = lib.csa2_prefill_sparse_attn_fp4
+    assert p(A, A, 512, A, 512, A, 512, A, 512, 1 << 11, 1 << 11, 64, 512, 64, 100, sm, A, N, A, 1 << 62,
+             N) == RANGE
+    # sampler draw: one 256-thread workgroup per row
+    assert lib.csa2_sample_draw(A, A, (1 << 31) - 1, 8, 1.0, 1.0, A, A, N, N, N) == RANGE
+
+
+def test_binding_checks_index_inputs_and_output_shapes(lib):
+    """The binding is the only guard on buffer sizes (the C ABI sees
+    pointers): wrong dtypes, too few key sequences and output tensors of the
+    wrong shape are refused before any call (CPU tensors: nothing launches)."""
+    import torch
+    bf = torch.bfloat16
+    qi = torch.zeros(2, 8, 128, dtype=bf)
+    k = torch.zeros(2, 64, 128, dtype=bf)
+    with pytest.raises(ValueError):
+        csa2.csa2_index_full(qi.float(), k)
+    with pytest.raises(ValueError):
+        csa2.csa2_index_full(qi, k.transpose(1, 2).contiguous().transpose(1, 2))   # not contiguous
+    with pytest.raises(ValueError, match="k_idx"):
+        csa2.csa2_index_full(qi, k[:1])                                           # fewer sequences
+    with pytest.raises(ValueError, match="k_idx"):
+        csa2.csa2_index_full(qi, k[..., :64].contiguous())                        # other D_I
+    with pytest.raises(ValueError, match="w"):
+        csa2.csa2_index_full(qi, k, w=torch.ones(2, 8, dtype=torch.float64))
+    with pytest.raises(ValueError, match="n_valid"):
+        csa2.csa2_index_full(qi, k, n_valid=torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError, match="scores"):
+        csa2.csa2_index_full(qi, k, scores=torch.empty(2, 63))
+    pool = torch.zeros(2, 16, dtype=torch.int32)
+    nb = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="pool_blocks"):
+        csa2.csa2_index_pool(qi, k, pool.long(), nb)
+    with pytest.raises(ValueError, match="n_blocks"):
+        csa2.csa2_index_pool(qi, k, pool, nb[:1])
+    with pytest.raises(ValueError, match="positions"):
+        csa2.csa2_index_pool(qi, k, pool, nb, positions=torch.empty(2, 16 * 8 - 1, dtype=torch.int32))
+    sc = torch.zeros(2, 100)
+    with pytest.raises(ValueError, match="ids"):
+        csa2.csa2_topk(sc, 8, ids=torch.zeros(2, 99, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out_idx"):
+        csa2.csa2_topk(sc, 8, out_idx=torch.empty(2, 7, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out_score"):
+        csa2.csa2_topk(sc, 8, out_score=torch.empty(2, 8, dtype=torch.float64))
+    with pytest.raises(ValueError, match="pool_blocks"):
+        csa2.csa2_build_pool(sc, 4, pool_blocks=torch.empty(2, 5, dtype=torch.int32))
+    u = torch.zeros(2)
+    with pytest.raises(ValueError, match="token"):
+        csa2.csa2_sample(sc, 8, 1.0, 1.0, u, token=torch.empty(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="u"):
+        csa2.csa2_sample_draw(torch.zeros(2, 8, dtype=torch.int32), torch.zeros(2, 8), 1.0, 1.0, u[:1])
+
+
+def test_binding_checks_cache_views_and_attention_outputs(lib):
+    import torch
+    codes, scales, rope = csa2.alloc_cache(2, 16, 512, 64, "cpu")
+    q = torch.zeros(2, 8, 576, dtype=torch.bfloat16)
+    idx = torch.zeros(2, 8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="scales"):
+        csa2.csa2_sparse_attn_fp4(q, codes, scales[:, :8], rope, idx)              # fewer scale rows
+    with pytest.raises(ValueError, match="rope"):
+        csa2.csa2_sparse_attn_fp4(q, codes, scales, rope[:, :15], idx)            # fewer RoPE rows
+    with pytest.raises(ValueError, match="out"):
+        csa2.csa2_sparse_attn_fp4(q, codes, scales, rope, idx, out=torch.empty(2, 8, 511))
+    with pytest.raises(ValueError, match="lse"):
+        csa2.csa2_sparse_attn_fp4(q, codes, scales, rope, idx, lse=torch.empty(2, 7))
+    with pytest.raises(ValueError, match="out"):
+        csa2.csa2_prefill_sparse_attn_fp4(q[None], codes[:1], scales[:1], rope[:1], idx[None],
+                                          out=torch.empty(1, 2, 8, 512, dtype=torch.float64))
+    x = torch.zeros(4, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="scales"):
+        csa2.csa2_quantize_fp4(x, codes[0], scales[0, :8])
+    with pytest.raises(ValueError, match="channels"):
+        csa2.csa2_quantize_fp4(x[:, :256].contiguous(), codes[0], scales[0])
+    wc, ws, wr = csa2.alloc_window(2, 16, 512, 64, "cpu")
+    with pytest.raises(ValueError, match="sigma"):
+        csa2.csa2_swa_attn_fp8(q, wc, ws[:, :8], wr)
+    with pytest.raises(ValueError, match="merge_lse"):
+        csa2.csa2_swa_attn_fp8(q, wc, ws, wr, merge_out=torch.zeros(2, 8, 512), merge_lse=torch.zeros(2, 9))
+    with pytest.raises(ValueError, match="sigma"):
+        csa2.csa2_quantize_fp8(x, wc[0], ws[0, :3], 0)

@@ -1,0 +1,250 @@
+"""CPU model of every global address the sparse-attention launches form.
+
+The model restates, in NumPy, the index arithmetic of the launch plan (heads
+per workgroup, slices per query, the XCD-ordered grid), of both attention
+kernels (16 heads per workgroup; 32 heads with score and value waves) and of
+the split combine, and checks each offset against the extent of the buffer it
+addresses: the queries, the index lists, the cache rows (codes, scales, RoPE
+part; 32-bit row offsets inside one sequence), the outputs, the LSE and the
+workspace.  It also checks that every (query, slice, head group) unit is owned
+by exactly one workgroup and every output element written exactly once.
+
+The model's slice count is pinned to the library's own plan through
+csa2_sparse_attn_workspace_bytes (which is B * H * slices * (d_c + 2) * 4
+bytes when a query is split), so the plan the model enumerates is the one the
+library launches.  Pure host code: nothing is launched.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from sparse_attention_decode_csa2_amd import csa2
+
+TILE, IDS, IDS_PAD = 64, 512, 640
+
+
+def heads_per_wg(B, H, d_c):
+    return 32 if (d_c == 512 and H > 16 and B * ((H + 31) // 32) >= 256) else 16
+
+
+def plan(B, H, K, d_c):
+    hpw = heads_per_wg(B, H, d_c)
+    n_hg = -(-H // hpw)
+    tiles = -(-K // TILE)
+    base = B * n_hg
+    s = 1 if base >= 256 else -(-256 // base)
+    s = max(s, -(-tiles // (IDS // TILE)))
+    s = max(1, min(s, tiles))
+    tps = -(-tiles // s)
+    s = -(-tiles // tps)
+    return hpw, n_hg, s, tps * TILE
+
+
+def grid_units(B, H, K, d_c):
+    """Workgroup -> (active, b, split, head group) for the attention grid."""
+    hpw, n_hg, s, ps = plan(B, H, K, d_c)
+    spread = B < 8
+    groups = (B * s + 7) // 8 if spread else (B + 7) // 8 * s
+    bx = np.arange(groups * 8 * n_hg, dtype=np.int64)
+    xcd, slot = bx & 7, bx >> 3
+    if spread:
+        unit = (slot // n_hg) * 8 + xcd
+        active = unit < B * s
+        b, split = unit // s, unit % s
+    else:
+        per_q = s * n_hg
+        b = (slot // per_q) * 8 + xcd
+        active = b < B
+        split = (slot % per_q) // n_hg
+    hg = slot % n_hg
+    return hpw, n_hg, s, ps, active, b[active], split[active], hg[active]
+
+
+def combine_rows(B, H):
+    """Combine block -> output row (b * H + h) for a split query."""
+    spread = B < 8
+    if spread:
+        return np.arange(B * H, dtype=np.int64)
+    bx = np.arange((B + 7) // 8 * 8 * H, dtype=np.int64)
+    xcd, slot = bx & 7, bx >> 3
+    b = (slot // H) * 8 + xcd
+    ok = b < B
+    return (b * H + slot % H)[ok]
+
+
+def pv_chunk(dc, w, m):
+    return 8 * (w >> 1) + (w & 1) + 2 * m if dc >= 512 else w
+
+
+def epilogue_channels_16(dc):
+    """Channels the 16-head kernel's epilogue writes per (head slot): wave w,
+    d-block d, lane column n."""
+    ndb = dc // 4 // 16
+    return sorted(32 * pv_chunk(dc, w, d >> 1) + 16 * (d & 1) + n
+                  for w in range(4) for d in range(ndb) for n in range(16))
+
+
+def epilogue_heads_16():
+    """Head slots (4 g + i) of the 16-head epilogue: lane group g, element i."""
+    return sorted(4 * g + i for g in range(4) for i in range(4))
+
+
+def epilogue_role():
+    """(head slot, channel) pairs the value waves of the 32-head kernel write:
+    value wave r, lane (hl, kh), accumulator k, element i."""
+    out = []
+    for r in range(4):
+        for lane in range(64):
+            hl, kh = lane & 31, lane >> 5
+            for i in range(16):
+                hh = 8 * (i >> 2) + 4 * kh + (i & 3)
+                for k in range(4):
+                    out.append((hh, 128 * r + 32 * k + hl))
+    return out
+
+
+def max_gather_tile_16(n_tiles):
+    """Largest tile the 16-head kernel's look-ahead gathers read ids for:
+    tiles 0 and 1 first, then t + 2 and t + 3 for t = 0, 2, ... while
+    t + 2 <= n_tiles."""
+    if n_tiles == 0:
+        return -1
+    m = 1
+    t = 0
+    while t + 2 <= n_tiles:
+        m = max(m, t + 3)
+        t += 2
+    return m
+
+
+def check(B, H, K, d_c, d_r, qps=1, N_cap=1000):
+    """Every check for one launch configuration; returns the plan."""
+    D = d_c + d_r
+    hpw, n_hg, s, ps, active, b, split, hg = grid_units(B, H, K, d_c)
+    # ---- each (b, split, hg) unit exactly once
+    key = (b * s + split) * n_hg + hg
+    assert np.array_equal(np.sort(key), np.arange(B * s * n_hg)), "units not covered exactly once"
+    assert (b >= 0).all() and (b < B).all()
+    e_begin = split * ps
+    e_end = np.minimum(K, e_begin + ps)
+    assert (e_end > e_begin).all(), "an empty slice"
+    assert (e_end - e_begin <= IDS).all(), "a slice holds more ids than the staging array"
+    n_tiles = -(-(e_end - e_begin) // TILE)
+    # ---- index list reads: idx[b * K + clamp(e)] with e the staged positions
+    if hpw == 16:
+        e = e_begin[:, None] + np.arange(IDS)[None, :]
+    else:
+        e = e_begin[:, None] + np.arange(512)[None, :]
+    j = np.minimum(e, np.maximum(e_end[:, None] - 1, 0))
+    off = b[:, None] * K + j
+    assert off.min() >= 0 and off.max() < B * K, "idx read out of bounds"
+    assert (j >= e_begin[:, None]).all() and (j < e_end[:, None]).all(), "id read outside the slice"
+    # ---- staged-id reads of the gathers
+    if hpw == 16:
+        mt = max(max_gather_tile_16(int(t)) for t in np.unique(n_tiles))
+        assert mt * TILE + 63 < IDS_PAD, "look-ahead gather past the staged ids"
+    # (the 32-head kernel clamps its gather tile to IDS_PAD / TILE - 1)
+    # ---- query reads: rows b * H + h (h < H) of D bf16 values, 16-byte pieces
+    h0 = hg * hpw
+    heads = h0[:, None] + np.arange(hpw)[None, :]
+    rows = np.where(heads < H, b[:, None] * H + heads, b[:, None] * H)
+    assert rows.min() >= 0 and rows.max() < B * H, "query row out of bounds"
+    if hpw == 16:
+        qoffs = [128 * (t >> 2) + 32 * g + 8 * (t & 3) for t in range(d_c // 32) for g in range(4)]
+        qoffs += [d_c + 16 * g + 8 * t for t in range(d_r // 32) for g in range(4)]
+    else:
+        KSL, KS = d_c // 32, (d_c + d_r) // 32
+        qoffs = []
+        for sub in range(8):
+            for m in range(KS * 4 // 8):
+                p = sub + 8 * m
+                t, gg = p >> 2, p & 3
+                qoffs.append(128 * (t >> 2) + 32 * gg + 8 * (t & 3) if t < KSL else d_c + 16 * gg + 8 * (t - KSL))
+    assert min(qoffs) >= 0 and max(qoffs) + 8 <= D, "query piece outside its row"
+    # ---- cache rows: sequence b // qps; row id < N_cap (ids are clamped), and
+    # the in-row offsets of one lane stay inside the row widths
+    seq = b // qps
+    assert seq.max() < B // qps, "query reads a sequence past the cache"
+    ncw = d_c // 128
+    if hpw == 16:
+        code_end = max(16 * g + 64 * i + 16 for g in range(4) for i in range(ncw))
+        scale_end = max(2 * g + 8 * i + 2 for g in range(4) for i in range(ncw))
+        rope_end = max(32 * g + 16 * t + 16 for g in range(4) for t in range(d_r // 32)) if d_r else 0
+    else:
+        code_end = max(16 * g + 64 * i + 16 for g in range(4) for i in range(4))
+        scale_end = max(2 * g + 8 * i + 2 for g in range(4) for i in range(4))
+        rope_end = max(32 * g + 16 * t + 16 for g in range(4) for t in range(d_r // 32)) if d_r else 0
+    assert code_end <= d_c // 2 and scale_end <= d_c // 16 and rope_end <= 2 * d_r, "gather past the row"
+    # 32-bit row offsets: the host refuses N_cap * stride > 2^32, so the last
+    # row's last byte stays below 2^32
+    for stride, end in ((d_c // 2, code_end), (d_c // 16, scale_end), (2 * d_r, rope_end)):
+        if stride:
+            ncap_max = (1 << 32) // stride
+            assert (ncap_max - 1) * stride + end <= (1 << 32)
+    # ---- outputs
+    if hpw == 16:
+        ch = epilogue_channels_16(d_c)
+        assert ch == list(range(d_c)), "16-head epilogue channels not a permutation"
+        hs = epilogue_heads_16()
+        assert hs == list(range(16))
+        written = heads[:, hs][heads[:, hs] < H]
+    else:
+        pairs = epilogue_role()
+        assert len(pairs) == len(set(pairs)) == 32 * 512, "32-head epilogue writes a cell twice"
+        written = heads[heads < H]
+    if s == 1:
+        out_rows = (b[:, None] * H + (heads * (heads < H)))[heads < H]
+        assert np.array_equal(np.sort(out_rows), np.arange(B * H)), "an output row written twice or never"
+        ws_bytes = 0
+    else:
+        slot_o = ((b[:, None] * H + heads) * s + split[:, None])[heads < H]
+        assert np.array_equal(np.sort(slot_o), np.arange(B * H * s)), "a partial written twice or never"
+        assert slot_o.max() * d_c + d_c <= B * H * s * d_c
+        assert 2 * slot_o.max() + 2 <= B * H * s * 2
+        ws_bytes = B * H * s * (d_c + 2) * 4
+        crow = combine_rows(B, H)
+        assert np.array_equal(np.sort(crow), np.arange(B * H)), "combine rows not covered exactly once"
+        assert (crow * s * d_c + (s - 1) * d_c + 4 * (d_c // 4) <= B * H * s * d_c).all()
+        assert (crow * s * 2 + 2 * (s - 1) + 2 <= B * H * s * 2).all()
+    assert written.max() < H
+    return hpw, n_hg, s, ps, ws_bytes
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return csa2.load()
+
+
+def _pin_plan(lib, B, H, K, d_c, ws_bytes):
+    assert lib.csa2_sparse_attn_workspace_bytes(B, H, d_c, K) == ws_bytes, (B, H, K, d_c)
+
+
+def test_every_batch_at_the_decode_shape(lib):
+    """B = 1 .. 256 at 64 heads, K = 512, both latent sizes: the shapes of the
+    decode workloads, including 8 <= B < 64 (split slices, one query per
+    XCD)."""
+    for B in range(1, 257):
+        for d_c, d_r in ((512, 64), (128, 0)):
+            _, _, _, _, ws = check(B, 64, 512, d_c, d_r)
+            _pin_plan(lib, B, 64, 512, d_c, ws)
+
+
+@pytest.mark.parametrize("d_c,d_r", [(512, 64), (512, 0), (128, 0), (128, 64)])
+def test_heads_and_list_lengths(lib, d_c, d_r):
+    Bs = list(range(1, 17)) + [31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256]
+    Hs = [1, 8, 15, 16, 17, 31, 32, 33, 64, 100, 128]
+    Ks = [1, 63, 64, 65, 511, 512, 513, 1000, 2048]
+    for B, H, K in itertools.product(Bs, Hs, Ks):
+        _, _, _, _, ws = check(B, H, K, d_c, d_r)
+        _pin_plan(lib, B, H, K, d_c, ws)
+
+
+def test_prefill_queries_per_sequence(lib):
+    """A prefill chunk: S sequences x T queries, query b reading sequence
+    b // T."""
+    for S, T in ((1, 8192), (2, 8), (3, 5), (1, 1), (4, 64)):
+        for K in (1, 512, 700):
+            _, _, _, _, ws = check(S * T, 64, K, 512, 64, qps=T)
+            _pin_plan(lib, S * T, 64, K, 512, ws)
