@@ -181,6 +181,23 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
               void* workspace, size_t workspace_bytes, csa2_stream_t stream);
 
 /*
+ * csa2_topk without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments (less the workspace), same results, bit
+ * for bit, as csa2_topk.  The chunk winners go to one static device array of
+ * the library (32 MiB, held by each GPU the library runs on until the process
+ * ends; its device address is looked up once per device).  This call
+ * allocates nothing.  Calls on one GPU share that array: calls that overlap
+ * on one GPU (two streams, two host threads) race, and must be ordered by the
+ * caller.  Requires csa2_topk_workspace_bytes(B, M, K) <= 32 MiB (e.g. up to
+ * 2048 rows x chunks of 16384 candidates at K = 512); CSA2_ERR_RANGE beyond.
+ * CSA2_ERR_HIP when the array's device address cannot be looked up.
+ */
+int csa2_topk_noalloc(const float* scores, const int32_t* ids, const int32_t* n_valid,
+                      int32_t B, int64_t M, int32_t K, int32_t* out_idx, float* out_score,
+                      csa2_stream_t stream);
+
+/*
  * The decode sampler on the Top-K selection.  One Top-K implementation serves
  * the sparse attention and the sampler ([P3] DeepSelect paragraph); sampling
  * is set by a temperature and a top_p ([P1] interface paragraph).  The order

@@ -46,6 +46,7 @@ def load():
         "csa2_index_pool": (ctypes.c_int, [P, P, P, P, P, P, I32, I32, I32, I64, I32, I32, P, P, P]),
         "csa2_topk_workspace_bytes": (SZ, [I32, I64, I32]),
         "csa2_topk": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P, SZ, P]),
+        "csa2_topk_noalloc": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P]),
         "csa2_quantize_fp8": (ctypes.c_int, [P, I64, I32, P, I32, P, I64, P, P, I64, I64, I64, P]),
         "csa2_swa_attn_fp8": (ctypes.c_int, [P, P, I64, P, P, I64, P, I32, I32, I32, I32, I32, F, P, P, P, P, P]),
         "csa2_build_pool_workspace_bytes": (SZ, [I32, I64, I32, I32]),
@@ -277,6 +278,29 @@ def csa2_topk(scores, K, ids=None, n_valid=None, out_idx=None, out_score=None, w
     st = lib.csa2_topk(_ptr(scores), _ptr(ids), _ptr(n_valid), B, M, K, _ptr(out_idx), _ptr(out_score),
                        _ptr(workspace), ws_bytes, _stream())
     _check("csa2_topk", st)
+    return out_idx, out_score
+
+
+def csa2_topk_noalloc(scores, K, ids=None, n_valid=None, out_idx=None, out_score=None, want_score=True):
+    """csa2_topk with its scratch in the library's static device array (no
+    workspace; the library allocates nothing).  Pass out_idx / out_score to
+    allocate nothing here either.  Calls that overlap on one GPU race."""
+    lib = load()
+    _need(scores, torch.float32, "scores")
+    if scores.dim() != 2:
+        raise ValueError(f"scores must be [B, M], got {tuple(scores.shape)}")
+    B, M = scores.shape
+    if ids is not None:
+        _need(ids, torch.int32, "ids", (B, M))
+    if n_valid is not None:
+        _need(n_valid, torch.int32, "n_valid", (B,))
+    dev = scores.device
+    out_idx = _out(out_idx, (B, K), torch.int32, dev, "out_idx")
+    if out_score is not None or want_score:
+        out_score = _out(out_score, (B, K), torch.float32, dev, "out_score")
+    st = lib.csa2_topk_noalloc(_ptr(scores), _ptr(ids), _ptr(n_valid), B, M, K, _ptr(out_idx), _ptr(out_score),
+                               _stream())
+    _check("csa2_topk_noalloc", st)
     return out_idx, out_score
 
 

@@ -199,6 +199,23 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, i
                                       as_stream(stream)));
 }
 
+int csa2_topk_noalloc(const float* scores, const int32_t* ids, const int32_t* n_valid, int32_t B, int64_t M,
+                      int32_t K, int32_t* out_idx, float* out_score, csa2_stream_t stream) {
+  if (B < 0 || M < 1 || M > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
+  if (K < 1 || K > 2048) return CSA2_ERR_RANGE;
+  if (B == 0) return CSA2_OK;
+  if (!scores || !out_idx) return CSA2_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(out_idx) || !opt_aligned16(ids) || !opt_aligned16(n_valid) ||
+      !opt_aligned16(out_score))
+    return CSA2_ERR_ALIGN;
+  const size_t need = csa2::topk_workspace_bytes(B, M, K);
+  if (need > csa2::kStaticScratchBytes) return CSA2_ERR_RANGE;
+  if (too_large(csa2::topk_launch_items(B, M, K))) return CSA2_ERR_RANGE;
+  void* ws = nullptr;
+  if (need > 0 && csa2::static_scratch(&ws) != hipSuccess) return CSA2_ERR_HIP;
+  return hip_status(csa2::launch_topk(scores, ids, n_valid, B, M, K, out_idx, out_score, ws, as_stream(stream)));
+}
+
 static bool sampler_params_ok(float temperature, float top_p) {
   // 1/T must stay a finite float; top_p > 0 (NaN fails both tests)
   return temperature >= 1e-30f && temperature <= 1e30f && top_p > 0.0f && top_p <= 1e30f;

@@ -40,6 +40,11 @@ hipError_t launch_index(const uint16_t* q, const float* w, const uint16_t* k, co
                         const int32_t* n_blocks, int P_max, int block, float* scores,
                         int32_t* positions, hipStream_t stream);
 
+// Size of the static device scratch array (scratch.hip) and the lookup of its
+// device address on the current device (once per device; thread-safe).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void** ptr);
+
 size_t topk_workspace_bytes(int B, int64_t M, int K);
 hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, int B,
                        int64_t M, int K, int32_t* out_idx, float* out_score, void* workspace,

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
 
@@ -368,3 +368,18 @@ def test_binding_checks_cache_views_and_attention_outputs(lib):
         csa2.csa2_swa_attn_fp8(q, wc, ws, wr, merge_out=torch.zeros(2, 8, 512), merge_lse=torch.zeros(2, 9))
     with pytest.raises(ValueError, match="sigma"):
         csa2.csa2_quantize_fp8(x, wc[0], ws[0, :3], 0)
+
+
+def test_topk_noalloc_validation(lib):
+    """The no-allocation Top-K validates like csa2_topk and refuses, before
+    touching the device, a call whose chunk winners exceed its 32 MiB array."""
+    f = lib.csa2_topk_noalloc
+    assert f(A, N, N, 0, 100, 8, A, A, N) == OK
+    assert f(A, N, N, -1, 100, 8, A, A, N) == SHAPE
+    assert f(A, N, N, 1, 0, 8, A, A, N) == SHAPE
+    assert f(A, N, N, 1, 100, 2049, A, A, N) == RANGE
+    assert f(N, N, N, 1, 100, 8, A, A, N) == NULL
+    assert f(U, N, N, 1, 100, 8, A, A, N) == ALIGN
+    # 4096 rows x 16 chunks x 512 winners x 8 bytes = 256 MiB > 32 MiB
+    assert lib.csa2_topk_workspace_bytes(4096, 262144, 512) > 32 << 20
+    assert f(A, N, N, 4096, 262144, 512, A, A, N) == RANGE
