@@ -40,6 +40,9 @@ Parity status per function (the pins live in ``tests/test_oracle_*.py``):
 * sample: pinned (hand-derived draws, the token frequencies over a grid of
   uniforms against scipy's softmax, the nucleus' minimality, greedy and
   single-candidate limits).
+* sample_full: pinned (hand-derived draws, token frequencies against scipy's
+  softmax over the whole vocabulary, the inverse-CDF boundary checked with
+  exactly rounded sums, the vanishing-temperature limit).
 """
 
 from .codec import (  # noqa: F401
@@ -67,6 +70,7 @@ from .method import (  # noqa: F401
     swa_attn,
     merge_branches,
     sample,
+    sample_full,
     decode_full,
     decode_reindex,
     decode_reuse,

@@ -486,3 +486,41 @@ def sample(logits, K, temperature, top_p, u):
         token[b] = idx[b, p]
         prob[b] = w[b, p] / nucleus
     return token, prob, n_kept, pos, idx, w
+
+
+def sample_full(logits, temperature, u):
+    """One token per row drawn from the softmax of logits / T over the whole
+    vocabulary, untruncated: the recommended decode settings, temperature
+    1.0 and top_p 1.0 [P1 interface paragraph], taken literally (top_p 1.0
+    keeps every token, so no Top-K cap applies).
+
+    The pages give only the two settings.  Reading taken:
+    1. weight w_i = exp((l_i - l_max) / T) for every token i of the row (a
+       -inf logit weighs 0), l_max the row's largest logit;
+    2. the draw takes the uniform u in [0, 1) as an input and returns the
+       first token, in token-id order, whose running weight exceeds
+       u * sum(w) (if rounding leaves none, the last token of nonzero
+       weight); prob = w_token / sum(w);
+    3. a row whose largest logit is -inf draws token 0 with probability 1.
+    Token-id order makes the draw a plain inverse CDF over the vocabulary;
+    the distribution is the softmax whatever the order.
+
+    logits float [B, V]; u float [B].  Returns (token int32 [B], prob float64 [B]).
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    B, V = logits.shape
+    u = np.asarray(u, dtype=np.float64).reshape(B)
+    token = np.zeros(B, dtype=np.int32)
+    prob = np.ones(B)
+    for b in range(B):
+        l_max = logits[b].max()
+        if l_max == -np.inf:
+            continue
+        w = np.where(logits[b] == -np.inf, 0.0, np.exp((logits[b] - l_max) / temperature))
+        run = np.cumsum(w)
+        total = run[-1]
+        hit = np.nonzero(run > u[b] * total)[0]
+        t = int(hit[0]) if hit.size else int(np.nonzero(w > 0)[0][-1])
+        token[b] = t
+        prob[b] = w[t] / total
+    return token, prob

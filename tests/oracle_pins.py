@@ -695,6 +695,79 @@ def check_sample_limits():
         assert np.array_equal(t0, want) and np.all(p0 == 1.0)
 
 
+def _sample_full_records():
+    out = []
+    for rec in _records("sampler_full_rows.txt"):
+        a = rec.index("|")
+        b = rec.index("|", a + 1)
+        T, u = float(rec[0]), float(rec[1])
+        logits = np.array([float(v) for v in rec[a + 1:b]])
+        out.append((T, u, logits, int(rec[b + 1]), float(rec[b + 2])))
+    return out
+
+
+def check_sample_full_golden():
+    """Hand-derived untruncated draws (tests/golden/sampler_full_rows.txt)."""
+    for T, u, logits, tok, prob in _sample_full_records():
+        t, p = oracle.sample_full(logits[None], T, [u])
+        assert int(t[0]) == tok, (T, u, logits, t)
+        assert abs(float(p[0]) - prob) <= 1e-15, (T, u, logits, p, prob)
+
+
+def check_sample_full_frequencies_vs_softmax():
+    """Over a uniform grid of u the untruncated draw gives every token of the
+    vocabulary the share scipy's softmax of logits / T gives it (within one
+    grid step), tokens coming in id order along u."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(71)
+    V, T, G = 40, 1.3, 20000
+    logits = rng.standard_normal(V) * 2.0
+    logits[[3, 17]] = -np.inf
+    u = (np.arange(G) + 0.5) / G
+    tok, prob = oracle.sample_full(np.tile(logits, (G, 1)), T, u)
+    want = softmax(logits / T)
+    freq = np.bincount(tok, minlength=V) / G
+    assert np.all(np.abs(freq - want) <= 1.0 / G + 1e-12), np.abs(freq - want).max()
+    assert np.all(np.diff(tok) >= 0)                        # along u: token ids ascending
+    assert freq[3] == 0 and freq[17] == 0
+    assert np.allclose(prob, want[tok], rtol=1e-12, atol=0)
+
+
+def check_sample_full_boundary_exact_sums():
+    """The drawn token t of every row satisfies C(t - 1) <= u * W < C(t), with
+    C the running weights and W their total summed exactly (math.fsum), over
+    random rows of a large vocabulary, temperatures and uniforms."""
+    import math
+    rng = np.random.default_rng(72)
+    B, V = 12, 3000
+    logits = rng.standard_normal((B, V)) * 4.0
+    T = rng.uniform(0.3, 2.0, size=B)
+    u = rng.random(B)
+    for b in range(B):
+        t, p = oracle.sample_full(logits[b][None], float(T[b]), u[b:b + 1])
+        t = int(t[0])
+        w = np.exp((logits[b] - logits[b].max()) / T[b])
+        W = math.fsum(w)
+        before, through = math.fsum(w[:t]), math.fsum(w[:t + 1])
+        target = u[b] * W
+        assert before <= target * (1 + 1e-12) and through > target * (1 - 1e-12), (b, t, before, target, through)
+        assert abs(float(p[0]) - w[t] / W) <= 1e-12
+
+
+def check_sample_full_limits():
+    """A vanishing temperature draws the unique largest logit whatever u is,
+    and a one-token vocabulary always draws token 0 with probability 1."""
+    rng = np.random.default_rng(73)
+    logits = np.round(rng.standard_normal((16, 50)) * 3)
+    want = np.argmax(logits, axis=1)
+    logits[np.arange(16), want] += 0.5                       # unique maxima, gap >= 0.5
+    for uu in (0.0, 0.5, 0.999999):
+        t, p = oracle.sample_full(logits, 1e-3, np.full(16, uu))
+        assert np.array_equal(t, want) and np.all(p == 1.0)
+    t, p = oracle.sample_full(np.array([[-2.5]]), 0.7, [0.99])
+    assert int(t[0]) == 0 and float(p[0]) == 1.0
+
+
 ALL_PINS = [
     check_e2m1_value_set, check_e4m3_decode, check_e4m3_encode_vs_torch, check_scale_code_vs_torch,
     check_e2m1_encode_vs_numpy_round, check_bf16_decode, check_quantize_golden,
@@ -707,4 +780,6 @@ ALL_PINS = [
     check_fp8_golden, check_fp8_vs_torch_cast, check_swa_vs_sdpa, check_merge_is_one_softmax_over_the_union,
     check_sample_golden, check_sample_frequencies_vs_softmax, check_sample_nucleus_is_minimal,
     check_sample_limits,
+    check_sample_full_golden, check_sample_full_frequencies_vs_softmax, check_sample_full_boundary_exact_sums,
+    check_sample_full_limits,
 ]

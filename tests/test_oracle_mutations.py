@@ -199,6 +199,51 @@ def _sample_unmutated(*a):
     return _sample_generic(*a, _W, _REACH, _EXCEEDS)
 
 
+_orig_sample_full = method.sample_full
+
+
+def _sample_full_generic(logits, temperature, u, weight, order, exceeds):
+    """The untruncated draw written with one step replaceable (for the plants below)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    B = logits.shape[0]
+    u = np.asarray(u, dtype=np.float64).reshape(B)
+    tok = np.zeros(B, dtype=np.int32)
+    prob = np.ones(B)
+    for b in range(B):
+        lm = logits[b].max()
+        if lm == -np.inf:
+            continue
+        w = np.where(logits[b] == -np.inf, 0.0, weight(logits[b], lm, temperature))
+        ids = order(logits[b])
+        run = np.cumsum(w[ids])
+        hit = [i for i in range(len(ids)) if exceeds(run, i, u[b] * run[-1])]
+        t = int(ids[hit[0]]) if hit else int(np.nonzero(w > 0)[0][-1])
+        tok[b], prob[b] = t, w[t] / run[-1]
+    return tok, prob
+
+
+_IDS = lambda l: np.arange(len(l))                   # noqa: E731
+
+
+def _sample_full_temperature_multiplies(*a):
+    # plant: logits multiplied by the temperature instead of divided
+    return _sample_full_generic(*a, lambda l, lm, T: np.exp((l - lm) * T), _IDS, _EXCEEDS)
+
+
+def _sample_full_logit_order(*a):
+    # plant: the inverse CDF walks the tokens by logit (descending), not by id
+    return _sample_full_generic(*a, _W, lambda l: np.argsort(-l, kind="stable"), _EXCEEDS)
+
+
+def _sample_full_boundary_inclusive(*a):
+    # plant: a running weight equal to the target already selects the token
+    return _sample_full_generic(*a, _W, _IDS, lambda run, i, t: run[i] >= t)
+
+
+def _sample_full_unmutated(*a):
+    return _sample_full_generic(*a, _W, _IDS, _EXCEEDS)
+
+
 def _prefill_first_cache(q_bits, codes, scales, rope_bits, idx, sm_scale):
     # plant: every sequence of the chunk reads the first sequence's cache
     rep = lambda a: np.broadcast_to(a[:1], a.shape)   # noqa: E731
@@ -238,6 +283,12 @@ MUTATIONS = {
     "sample_draw_exclusive": [(method, "sample", _sample_draw_exclusive), (oracle, "sample", _sample_draw_exclusive)],
     "sample_probs_over_vocab": [(method, "sample", _sample_probs_over_vocab),
                                 (oracle, "sample", _sample_probs_over_vocab)],
+    "sample_full_temperature_multiplies": [(method, "sample_full", _sample_full_temperature_multiplies),
+                                           (oracle, "sample_full", _sample_full_temperature_multiplies)],
+    "sample_full_logit_order": [(method, "sample_full", _sample_full_logit_order),
+                                (oracle, "sample_full", _sample_full_logit_order)],
+    "sample_full_boundary_inclusive": [(method, "sample_full", _sample_full_boundary_inclusive),
+                                       (oracle, "sample_full", _sample_full_boundary_inclusive)],
 }
 
 
@@ -259,6 +310,8 @@ def test_sampler_plant_harness_is_faithful(monkeypatch):
     plant is caught for its planted step, not for the harness)."""
     monkeypatch.setattr(method, "sample", _sample_unmutated)
     monkeypatch.setattr(oracle, "sample", _sample_unmutated)
+    monkeypatch.setattr(method, "sample_full", _sample_full_unmutated)
+    monkeypatch.setattr(oracle, "sample_full", _sample_full_unmutated)
     for pin in P.ALL_PINS:
         if "sample" in pin.__name__:
             pin()
