@@ -105,7 +105,7 @@ class Step:
         self.wl, self.csa2, self.W, self.dev = wl, csa2, W, dev
         B, N = wl.B, wl.N
         self.mode = wl.mode
-        if self.mode == "sample":
+        if self.mode in ("sample", "sample_full"):
             self._init_sample(wl, dev)
             return
         self.touched = self.step_read_bytes()
@@ -190,11 +190,14 @@ class Step:
         self.scores = self.sets[0]["logits"]
         self.idx = torch.empty(B, K, dtype=torch.int32, device=dev)
         self.top = torch.empty(B, K, dtype=torch.float32, device=dev)
-        tk = csa2.csa2_topk_workspace_bytes(B, V, K)
-        self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
         self.token = torch.empty(B, dtype=torch.int32, device=dev)
         self.prob = torch.empty(B, dtype=torch.float32, device=dev)
         self.n_kept = torch.empty(B, dtype=torch.int32, device=dev)
+        if self.mode == "sample_full":
+            self.stages = ["draw_full"]
+            return
+        tk = csa2.csa2_topk_workspace_bytes(B, V, K)
+        self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
         self.stages = ["topk", "draw"]
 
     def step_read_bytes(self):
@@ -202,7 +205,7 @@ class Step:
         once): the figure the rotation is sized from."""
         wl = self.wl
         B, N, K = wl.B, wl.N, wl.K
-        if self.mode == "sample":
+        if self.mode in ("sample", "sample_full"):
             return B * N * 4
         ent = _entry_bytes(wl)
         q = wl.H * wl.D * 2
@@ -215,6 +218,10 @@ class Step:
                 "prefill_full": B * (N * wl.D_I * 2 + qi + K * ent + q) + wl.prefill_rows * wl.D * 2,
                 "pool_build": B * (N * wl.D_I * 2 + qi)}[self.mode]
 
+    def draw_full(self, r):
+        self.csa2.csa2_sample_full(self.sets[r]["logits"], self.wl.temperature, self.sets[r]["u"], token=self.token,
+                                   prob=self.prob)
+
     def draw(self, r):
         wl = self.wl
         self.csa2.csa2_sample_draw(self.idx, self.top, wl.temperature, wl.top_p, self.sets[r]["u"],
@@ -224,6 +231,9 @@ class Step:
         """The same draw in eager torch ops (speed reference; top_p = 1 only)."""
         import torch
         wl = self.wl
+        if self.mode == "sample_full":
+            c = torch.cumsum(torch.softmax(self.sets[r]["logits"] / wl.temperature, dim=1), dim=1)
+            return torch.searchsorted(c, self.sets[r]["u"][:, None] * c[:, -1:], right=True)
         vals, ids = torch.topk(self.sets[r]["logits"], wl.K, dim=1)
         c = torch.cumsum(torch.softmax(vals / wl.temperature, dim=1), dim=1)
         pos = torch.searchsorted(c, self.sets[r]["u"][:, None] * c[:, -1:], right=True)
@@ -312,6 +322,9 @@ class Step:
         if self.mode == "sample":
             # logits read once; uniform in, token + prob + n_kept out; candidates (ids + logits) between stages
             return {"topk": B * (N * 4 + K * 8), "draw": B * (K * 8 + 4 + 12), "step": B * (N * 4 + 4 + 12)}
+        if self.mode == "sample_full":
+            # logits read once, uniform in, token + prob out (the drawn tile's second read is not counted)
+            return {"draw_full": B * (N * 4 + 4 + 8), "step": B * (N * 4 + 4 + 8)}
         ent = _entry_bytes(wl)
         qi = wl.H_I * wl.D_I * 2
         if self.mode == "prefill_reuse":
@@ -380,7 +393,7 @@ def cpu_baseline(wl, budget_s):
         return bits(W.index_query(w1)) if wl.H_I else None, bits(W.attn_query(w1)) if wl.H else None
 
     n_q = 16
-    qs = [queries(i) for i in range(n_q)] if mode != "sample" else []
+    qs = [queries(i) for i in range(n_q)] if mode not in ("sample", "sample_full") else []
     fixed_s = 0.0
     if mode in ("full", "prefill_full", "reindex", "pool_build"):
         keys = bits(W.index_keys(one, 0))[None]
@@ -406,7 +419,7 @@ def cpu_baseline(wl, budget_s):
         wcodes, wsig = oracle.quantize_fp8(bits(W.latent_rows(one, 0, wl.window, name="window")))
         wrope = bits(W.rope_rows(one.scaled(seed=one.seed + 7919), 0, wl.window))[None]
         wcodes, wsig = wcodes[None], wsig[None]
-    if mode == "sample":
+    if mode in ("sample", "sample_full"):
         rows = [W.vocab_logits(wl.scaled(B=1, seed=1000 + i)).numpy() for i in range(n_q)]
         us = [W.sampler_uniforms(wl.scaled(B=1, seed=1000 + i)).numpy() for i in range(n_q)]
 
@@ -414,6 +427,9 @@ def cpu_baseline(wl, budget_s):
         j = i % n_q
         if mode == "sample":
             oracle.sample(rows[j], wl.K, wl.temperature, wl.top_p, us[j])
+            return
+        if mode == "sample_full":
+            oracle.sample_full(rows[j], wl.temperature, us[j])
             return
         qi, q = qs[j]
         if mode in ("full", "prefill_full"):
@@ -447,15 +463,16 @@ def cpu_baseline(wl, budget_s):
             "reindex": "Reindex-mode decode queries", "reuse": "Reuse-mode decode queries",
             "reuse_swa": "Reuse-mode decode queries with the window branch merged",
             "pool_build": "pool constructions (Full scores + pool)", "sample": "sampler rows",
+            "sample_full": "untruncated sampler rows",
             "prefill_reuse": "prefill chunk queries"}[mode]
     if mode == "prefill_full":
         value = wl.B / (fixed_s + wl.B * el / n)
     else:
         value = n / el
-    unit = "rows/s" if mode == "sample" else "queries/s"
+    unit = "rows/s" if mode in ("sample", "sample_full") else "queries/s"
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{n} {what} (batch 1, {wl.N} {'vocabulary logits' if mode == 'sample' else 'entries'}"
-                      f"{'' if mode == 'sample' else f', pool of {wl.P_max} blocks' if mode == 'pool_build' else f', Top-{wl.K}'}) in {el:.1f} s"
+            "sample": f"{n} {what} (batch 1, {wl.N} {'vocabulary logits' if mode in ('sample', 'sample_full') else 'entries'}"
+                      f"{'' if mode in ('sample', 'sample_full') else f', pool of {wl.P_max} blocks' if mode == 'pool_build' else f', Top-{wl.K}'}) in {el:.1f} s"
                       f"{'; ' + '; '.join(prep) if prep else ''}; NumPy float64, BLAS threads={threads}"}
 
 
@@ -525,7 +542,7 @@ def main():
     # the same selection by torch.topk (speed reference only: its order among
     # equal scores is unspecified), K launches on the stage's own score rows
     torch_topk_us = torch_sampler_us = None
-    if wl.mode == "sample" and wl.top_p >= 1.0:
+    if wl.mode in ("sample", "sample_full") and wl.top_p >= 1.0:
         g_ts = capture(step.torch_sampler, args.steps, W0 + args.steps)
         g_ts.replay()
         torch_sampler_us = 1000.0 * timed(g_ts) / args.steps
@@ -549,7 +566,8 @@ def main():
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
     kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
-                   "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip"}[dom]
+                   "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip",
+                   "draw_full": "sample.hip"}[dom]
     achieved = alg[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = committed_traffic(kernel_file, wl.name)
 
@@ -578,11 +596,13 @@ def main():
     line = {
         "metric": ("decode sampler rows/s + achieved HBM GB/s (% of peak), Top-K + top-p draw"
                    if wl.mode == "sample" else
+                   "decode sampler rows/s + achieved HBM GB/s (% of peak), untruncated draw over the vocabulary"
+                   if wl.mode == "sample_full" else
                    "prefill chunk queries/s + achieved TFLOP/s (% of MFMA peak), CSA2 FP4 sparse attn"
                    if wl.mode == "prefill_reuse" else
                    "decode queries/s + achieved HBM GB/s (% of peak), CSA2 FP4 sparse attn"),
         "value": qps,
-        "unit": "rows/s" if wl.mode == "sample" else "queries/s",
+        "unit": "rows/s" if wl.mode in ("sample", "sample_full") else "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -590,13 +610,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("f32 logits, f32 weights" if wl.mode == "sample" else
+        "dtype": ("f32 logits, f32 weights" if wl.mode in ("sample", "sample_full") else
                   "fp4(e2m1)+e4m3 cache, bf16/fp16 mfma, fp32 softmax"),
-        "data": ("synthetic (seeded; N(0,1) x 4 logits, uniform draws)" if wl.mode == "sample" else
+        "data": ("synthetic (seeded; N(0,1) x 4 logits, uniform draws)" if wl.mode in ("sample", "sample_full") else
                  "synthetic (seeded; integer indexer, RMS-normalised N(0,1) latents)"),
         "config": ({"workload": wl.name, "mode": wl.mode, "batch": wl.B, "vocab": wl.N, "top_k": wl.K,
                     "temperature": wl.temperature, "top_p": wl.top_p, "rotation_sets": R}
-                   if wl.mode == "sample" else
+                   if wl.mode in ("sample", "sample_full") else
                    {"workload": wl.name, "mode": wl.mode, "batch": wl.B, "entries": wl.N,
                     "context_tokens": wl.N * 4, "latent": wl.d_c, "rope": wl.d_r, "heads": wl.H,
                     "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "rotation_sets": R,

@@ -247,6 +247,30 @@ int csa2_sample(const float* logits, int32_t B, int64_t V, int32_t K, float temp
                 size_t workspace_bytes, csa2_stream_t stream);
 
 /*
+ * The untruncated draw: the recommended sampling settings, temperature 1.0 and
+ * top_p 1.0 ([P1] interface paragraph), taken literally: top_p 1.0 keeps
+ * every token of the vocabulary, so no Top-K cap applies and the draw is over
+ * the whole softmax of logits / T.  The order is this build's reading:
+ *   w_i   = exp((l_i - l_max) / T) for every token i of the row (0 for -inf);
+ *   token = the first token, in token-id order, whose running weight exceeds
+ *           u * sum(w) (the last token of nonzero weight if rounding leaves
+ *           none);  prob = w_token / sum(w).
+ * A row whose largest logit is -inf draws token 0 with probability 1.  The
+ * weights and running sums are float32 (tile totals and the running weights
+ * inside a tile are summed in different orders), so a token decided by a
+ * running weight within float32 rounding of u * sum(w) may differ from an
+ * exact evaluation by one token; the token always has nonzero weight.  A +inf
+ * or NaN logit gives an unspecified token of the row.
+ *
+ * logits f32 [B, V] (row b at logits + b * V), u f32 [B] in [0, 1), token
+ * i32 [B] out, prob f32 [B] out (nullable).  One pass over the logits and one
+ * 16384-token tile read again per row; no workspace.  Requires 1 <= V <= 2^20
+ * (CSA2_ERR_RANGE beyond), 1e-30 <= T <= 1e30, 16-byte aligned arrays.
+ */
+int csa2_sample_full(const float* logits, int32_t B, int64_t V, float temperature, const float* u,
+                     int32_t* token, float* prob, csa2_stream_t stream);
+
+/*
  * Sliding-window branch, write: FP8 rows of the window KV.  The window branch
  * keeps its KV in FP8 ([P4] CSA2 paragraph; [P1] 效率组件四件, item 4); the
  * pages give no scale granularity, this build uses one power-of-two scale per

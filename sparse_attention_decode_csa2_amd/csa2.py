@@ -54,6 +54,7 @@ def load():
         "csa2_sample_draw": (ctypes.c_int, [P, P, I32, I32, F, F, P, P, P, P, P]),
         "csa2_sample_workspace_bytes": (SZ, [I32, I64, I32]),
         "csa2_sample": (ctypes.c_int, [P, I32, I64, I32, F, F, P, P, P, P, P, SZ, P]),
+        "csa2_sample_full": (ctypes.c_int, [P, I32, I64, F, P, P, P, P]),
         "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "csa2_sparse_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I64,
                                                 F, P, P, P, SZ, P]),
@@ -349,6 +350,23 @@ def csa2_sample(logits, K, temperature, top_p, u, token=None, prob=None, n_kept=
                          _ptr(prob), _ptr(n_kept), _ptr(workspace), workspace.numel(), _stream())
     _check("csa2_sample", st)
     return token, prob, n_kept
+
+
+def csa2_sample_full(logits, temperature, u, token=None, prob=None):
+    """The untruncated draw (top_p 1.0 over the whole vocabulary): logits f32
+    [B, V], u f32 [B] -> (token i32 [B], prob f32 [B])."""
+    lib = load()
+    _need(logits, torch.float32, "logits")
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [B, V], got {tuple(logits.shape)}")
+    B, V = logits.shape
+    _need(u, torch.float32, "u", (B,))
+    dev = logits.device
+    token = _out(token, (B,), torch.int32, dev, "token")
+    prob = _out(prob, (B,), torch.float32, dev, "prob")
+    st = lib.csa2_sample_full(_ptr(logits), B, V, float(temperature), _ptr(u), _ptr(token), _ptr(prob), _stream())
+    _check("csa2_sample_full", st)
+    return token, prob
 
 
 # ------------------------------------------------------------------ a4 / a5

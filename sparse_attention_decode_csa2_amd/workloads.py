@@ -37,6 +37,9 @@ compressed entry per 4 tokens):
                   129280-token vocabulary (N(0,1) x 4), Top-2048, temperature
                   1 and top_p 1 (the recommended sampling settings), one
                   uniform per row
+9. sample-full-129k  the same rows and uniforms (same seed), drawn without a
+                  Top-K cap: temperature 1 and top_p 1 over the whole
+                  vocabulary
 """
 
 from dataclasses import dataclass
@@ -50,7 +53,7 @@ import torch
 class Workload:
     name: str
     mode: str            # "full" | "reindex" | "reuse" | "prefill_full" | "pool_build" | "reuse_swa" | "sample"
-                         # | "prefill_reuse"
+                         # | "prefill_reuse" | "sample_full"
     B: int               # decode queries (sequences) per step
     N: int               # compressed entries per sequence (cache capacity)
     d_c: int             # FP4 latent channels
@@ -98,6 +101,7 @@ WORKLOADS = [
     Workload("sample-129k", "sample", B=128, N=129280, d_c=0, d_r=0, H=0, H_I=0, D_I=0, K=2048, seed=7),
     Workload("prefill-reuse-1m", "prefill_reuse", B=1, N=262144, d_c=512, d_r=64, H=64, H_I=8, D_I=128, K=512,
              seed=8, prefill_rows=8192),
+    Workload("sample-full-129k", "sample_full", B=128, N=129280, d_c=0, d_r=0, H=0, H_I=0, D_I=0, K=0, seed=7),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
 
@@ -383,3 +383,17 @@ def test_topk_noalloc_validation(lib):
     # 4096 rows x 16 chunks x 512 winners x 8 bytes = 256 MiB > 32 MiB
     assert lib.csa2_topk_workspace_bytes(4096, 262144, 512) > 32 << 20
     assert f(A, N, N, 4096, 262144, 512, A, A, N) == RANGE
+
+
+def test_sample_full_validation(lib):
+    f = lib.csa2_sample_full
+    assert f(A, 0, 129280, 1.0, A, A, N, N) == OK
+    assert f(A, -1, 129280, 1.0, A, A, N, N) == SHAPE
+    assert f(A, 2, 0, 1.0, A, A, N, N) == SHAPE
+    assert f(A, 2, (1 << 20) + 1, 1.0, A, A, N, N) == RANGE
+    assert f(A, 2, 129280, 0.0, A, A, N, N) == RANGE
+    assert f(A, 2, 129280, float("nan"), A, A, N, N) == RANGE
+    assert f(N, 2, 129280, 1.0, A, A, N, N) == NULL
+    assert f(A, 2, 129280, 1.0, A, N, N, N) == NULL
+    assert f(U, 2, 129280, 1.0, A, A, N, N) == ALIGN
+    assert f(A, 2, 129280, 1.0, A, A, U, N) == ALIGN
