@@ -17,7 +17,10 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+# CSA2_LIBRARY names another build of the same library (e.g. the host-ASan
+# build the CPU tests make of the validation layer); the default is the
+# in-tree libcsa2.so
+LIB_PATH = os.environ.get("CSA2_LIBRARY") or os.path.join(_HERE, "libcsa2.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "csa2.h")
 
 _lib = None

@@ -5,27 +5,33 @@
 // "larger key" is exactly "higher score, then lower id" and an empty candidate
 // is key 0.  One workgroup of 1024 threads owns up to 16384 candidates, thread
 // t the 16 consecutive columns [16t, 16t + 16) of its chunk, held in registers
-// as 32-bit score keys (thread order is column order):
+// as fp32 scores and ids (thread order is column order):
 //
 //  1. a block reduction gives the number of valid candidates and the highest
-//     and lowest score keys; the bits they share are skipped;
-//  2. one radix pass over the chunk (11 bits, 2048 LDS bins, one suffix scan)
-//     finds the bin holding the K-th largest score key;
-//  3. the keys above that bin go straight to the output buffer and the keys
-//     of the bin (at most 2048, else the passes continue over the chunk) to a
-//     candidate buffer, both in column order;
-//  4. the rest of the selection runs on the candidates, 2 per thread: radix
-//     passes until the wanted part of a bin is the whole bin or one exact
-//     score, then a tie on one score is cut by id (in column order by one
-//     block scan when the ids are the columns, else by radix select on ~id);
-//  5. a bitonic network (DPP / permlane exchanges below stride 64, LDS for
-//     strides 64 and 128, in-register above) sorts the K keys descending.
+//     and lowest score;
+//  2. linear score buckets (the first path): when both ends are finite and
+//     distinct, bucket (s - lo) * 2048 / (hi - lo) is monotone in the score;
+//     one LDS histogram and one suffix scan give the bucket holding the K-th
+//     largest key and where every bucket's keys start in the output order;
+//  3. the keys of the buckets above it (and of it, when it holds at most 2048)
+//     are staged wave by wave into LDS and placed bucket by bucket; a key's
+//     output slot is its bucket's start plus its rank among the keys of its
+//     bucket, and one wave orders the boundary bucket (counting ranks up to
+//     24 keys, a bitonic network up to 64) and keeps its first r keys;
+//  4. exact fallbacks: a selected bucket longer than 32 keys -> bitonic sort
+//     of the K keys; a boundary bucket of 65-2048 keys -> radix select on its
+//     keys (ties by radix select on ~id); more than 2048 keys in one bucket,
+//     non-finite ends or NaN-only rows -> radix selection on the 32-bit score
+//     keys of the whole chunk (11-bit digits, suffix scans; a tie on one score
+//     cut by id) and a bitonic network (DPP / permlane exchanges below stride
+//     64, LDS above) that sorts the K keys descending.
 //
 // Rows longer than 16384 are cut into 16384-key chunks; each chunk keeps its
 // own top K keys, unsorted (the union of chunk winners contains the row's
 // winners, the key order being total) and the winners are reduced again
-// until one chunk remains.  Bit-exact by construction: only integer compares
-// and counts.
+// until one chunk remains.  The bucket index is an fp32 computation that only
+// routes keys; every order decision is an integer compare of the 64-bit keys,
+// so the result is bit-exact.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
