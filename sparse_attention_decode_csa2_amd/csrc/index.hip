@@ -23,7 +23,9 @@
 
 namespace csa2 {
 
-template <int KS, int TPW, bool POOL>
+// BLK: positions per pool block known at compile time (the 8-position blocks of
+// the candidate pool: the block lookups become shifts), 0 = the runtime `block`.
+template <int KS, int TPW, bool POOL, int BLK>
 __global__ __launch_bounds__(256) void index_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     const int32_t* __restrict__ n_valid, int H_I, int64_t N_cap, const int32_t* __restrict__ pool,
@@ -31,6 +33,7 @@ __global__ __launch_bounds__(256) void index_kernel(
     float* __restrict__ scores, int32_t* __restrict__ positions) {
   constexpr int D_I = 32 * KS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t bsz = BLK > 0 ? (uint64_t)BLK : (uint64_t)block;  // columns are non-negative
   const int n = lane & 15, g = lane >> 4;
   const int64_t b = blockIdx.x / wg_per_row;
   const int64_t wg = blockIdx.x - b * wg_per_row;
@@ -64,10 +67,10 @@ __global__ __launch_bounds__(256) void index_kernel(
     int64_t p = col;
     bool valid;
     if (POOL) {
-      const int64_t i = col / block;
-      const int j = (int)(col - i * block);
+      const int64_t i = (int64_t)((uint64_t)col / bsz);
+      const int j = (int)(col - i * (int64_t)bsz);
       const int64_t blk = (col < M && i < nb) ? (int64_t)pool[b * P_max + i] : -1;
-      p = blk * block + j;
+      p = blk * (int64_t)bsz + j;
       valid = blk >= 0 && p < nv;
     } else {
       valid = col < nv;
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256) void index_kernel(
   // contiguous loads in pool mode when every load's keys sit in one block
   // (8-position blocks and 128-dimension keys: 4 keys per load): then a
   // load needs one block id, the same for the whole wave
-  const bool contig = !POOL || block % KPL == 0;
+  const bool contig = !POOL || bsz % KPL == 0;
   __shared__ u32x4 kbuf[4][16 * (KW + 1)];
   u32x4* kb = kbuf[wave];
   const int64_t tile0 = (int64_t)(wg * 4 + __builtin_amdgcn_readfirstlane(wave)) * TPW;
@@ -113,9 +116,9 @@ __global__ __launch_bounds__(256) void index_kernel(
       } else if (POOL) {
         // block of keys 16 t' + KPL s .. (wave-uniform), then the lane's key in it
         const int64_t c0 = (tile0 + t) * 16 + KPL * s;
-        const int64_t i = c0 / block;
+        const int64_t i = (int64_t)((uint64_t)c0 / bsz);
         const int64_t blk = (c0 < M && i < nb) ? (int64_t)pool[b * P_max + i] : -1;
-        const int64_t p = blk * block + (c0 - i * block) + lane / KW;
+        const int64_t p = blk * (int64_t)bsz + (c0 - i * (int64_t)bsz) + lane / KW;
         valid = blk >= 0 && p < nv;
         kp = k + (b * N_cap + (valid ? p : 0)) * D_I + 8 * (w % KW);
       } else {
@@ -189,11 +192,16 @@ static hipError_t launch_index_ks(const uint16_t* q, const float* w, const uint1
   int64_t wg_per_row;
   index_grid(B, M, POOL, &tpw, &wg_per_row);
   const dim3 grid((unsigned)(wg_per_row * B)), blk(256);
-#define CSA2_IDX_LAUNCH(T)                                                                          \
-  hipLaunchKernelGGL((index_kernel<KS, T, POOL>), grid, blk, 0, stream, q, w, k, n_valid, H_I, N_cap, \
+#define CSA2_IDX_LAUNCH(T, BL)                                                                          \
+  hipLaunchKernelGGL((index_kernel<KS, T, POOL, BL>), grid, blk, 0, stream, q, w, k, n_valid, H_I, N_cap, \
                      pool, n_blocks, P_max, block, M, wg_per_row, scores, positions)
-  if (tpw == 2) CSA2_IDX_LAUNCH(2);
-  else CSA2_IDX_LAUNCH(1);
+  if (POOL && block == 8) {
+    if (tpw == 2) CSA2_IDX_LAUNCH(2, 8);
+    else CSA2_IDX_LAUNCH(1, 8);
+  } else {
+    if (tpw == 2) CSA2_IDX_LAUNCH(2, 0);
+    else CSA2_IDX_LAUNCH(1, 0);
+  }
 #undef CSA2_IDX_LAUNCH
   return hipGetLastError();
 }
