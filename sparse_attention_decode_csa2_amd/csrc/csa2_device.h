@@ -64,6 +64,36 @@ __device__ __forceinline__ uint32_t e4m3_scale_code(float amax) {
   return lo;
 }
 
+// The same scale code from an estimate and one exact correction: the E4M3
+// code nearest to the float32 product amax * (1/6) (relative error below
+// 2^-24, so its nearest code is within one of the exact one: subnormal codes
+// m * 2^-9 by rounding t * 512, normal codes by rounding t's mantissa to
+// three bits), then one step up or down decided by the exact thresholds T(c)
+// of e4m3_scale_code (the code is the number of c with amax > T(c), or
+// amax == T(c) and c odd, and that count is monotone in c).
+__device__ __forceinline__ bool e4m3_scale_above(float amax, uint32_t c) {
+  const float T = 3.0f * (e4m3_value(c) + e4m3_value(c + 1));
+  return (amax > T) || (amax == T && (c & 1u));
+}
+__device__ __forceinline__ uint32_t e4m3_scale_code_fast(float amax) {
+  const float t = amax * (1.0f / 6.0f);
+  uint32_t c;
+  if (!(t < 448.0f)) {
+    c = 126u;                                   // saturated (also +inf / NaN: unspecified codes)
+  } else if (t < 0x1p-6f) {
+    c = (uint32_t)__builtin_rintf(t * 512.0f);  // subnormal codes 0..7 (8: the smallest normal)
+  } else {
+    const uint32_t u = __float_as_uint(t);
+    const uint32_t e = (u >> 23) - 120u;        // E4M3 exponent field: binary exponent + 7
+    c = (e << 3) | ((u >> 20) & 7u);
+    c += (u & 0xFFFFFu) >= 0x80000u ? 1u : 0u;  // nearest (a carry moves to the next binade)
+    c = c < 126u ? c : 126u;
+  }
+  if (c < 126u && e4m3_scale_above(amax, c)) return c + 1u;
+  if (c > 0u && !e4m3_scale_above(amax, c - 1u)) return c - 1u;
+  return c;
+}
+
 // E2M1 magnitude code (0..7) of |x| for block scale sigma > 0: nearest of
 // {0, .5, 1, 1.5, 2, 3, 4, 6} * sigma, ties to the even code, saturating.
 // Midpoints mu = {.25, .75, 1.25, 1.75, 2.5, 3.5, 5}; mu * sigma is exact in

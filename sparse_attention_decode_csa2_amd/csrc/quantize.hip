@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void quantize_fp4_kernel(
       mbits = max(mbits, w[i] & 0x7FFFu);
       mbits = max(mbits, (w[i] >> 16) & 0x7FFFu);
     }
-    const uint32_t S = e4m3_scale_code(bf16_bits_to_f32(mbits));
+    const uint32_t S = e4m3_scale_code_fast(bf16_bits_to_f32(mbits));
     const float sigma = e4m3_value(S);
     uint64_t packed = 0;
 #pragma unroll
