@@ -5,8 +5,9 @@ GPU: an 8192-row post-RoPE bf16 chunk is quantised to FP4 and appended to
 sequence 0, then a batch of 8 Full-mode decode queries (64 heads, indexer
 8 heads x 128) scores 262144 entries per sequence (1M tokens at 4:1), takes
 the Top-512 and runs the sparse attention over them.  One step =
-csa2_quantize_fp4 -> csa2_index_full -> csa2_topk -> csa2_sparse_attn_fp4, all
-on the GPU through the C ABI, with every input resident in HBM.  The other
+csa2_quantize_fp4 -> csa2_index_topk_full (the indexer scores and their
+Top-512 in one call) -> csa2_sparse_attn_fp4, all on the GPU through the C
+ABI, with every input resident in HBM.  The other
 workloads (--workload) give the supplementary lines.
 
 Inputs rotate over R distinct sets, R sized from the bytes one step actually
@@ -14,9 +15,12 @@ reads so that a rotation touches >= 1 GiB (4x the 256 MB Infinity Cache); the
 timed steps start after the sets the warm-up used, and the line records how
 many distinct sets and bytes the timed steps touched.
 
-Prints ONE JSON line (rank 0).  `roofline` describes the dominant kernel:
-algorithmic bytes per launch over its average duration (HIP events on the
-stream the kernels run on), against the 8 TB/s HBM peak.  `traffic` comes from
+Prints ONE JSON line (rank 0).  `roofline` describes the dominant stage:
+algorithmic bytes per call over its average duration (HIP events on the
+stream the kernels run on), against the 8 TB/s HBM peak.  The dominant stage
+of the Full workloads, `select` (csa2_index_topk_full), is two launches at
+1M entries: the fused indexer + chunk Top-K kernel, then the final Top-K
+level; its duration covers both.  `traffic` comes from
 the committed rocprofv3 FETCH_SIZE / WRITE_SIZE measurement of that kernel
 (profiles/), and is null when the kernel source changed since it was taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
@@ -87,10 +91,10 @@ def _entry_bytes(wl):
 class Step:
     """One decode step of a workload over R rotating input sets.
 
-    Full (tiny-full, full-64k): index -> topk -> attn, each set its own caches.
+    Full (tiny-full, full-64k): select (indexer scores + Top-K) -> attn, each set its own caches.
     Reindex (reindex-1m): pool -> topk -> attn over one cache; sets = pools + queries.
     Reuse (reuse-128k): attn over one cache; sets = index lists + queries.
-    Prefill + Full (prefill-full-1m): quantize (append 8192 rows) -> index -> topk -> attn.
+    Prefill + Full (prefill-full-1m): quantize (append 8192 rows) -> select -> attn.
     Pool construction (pool-build-1m): index (Full scores) -> build (the Reindex pool).
     Reuse + window (reuse-swa-128k): attn -> swa (the FP8 window branch merged in).
     Sampler (sample-129k): topk (over the vocabulary logits) -> draw; sets = logits + uniforms.
@@ -105,6 +109,7 @@ class Step:
         self.wl, self.csa2, self.W, self.dev = wl, csa2, W, dev
         B, N = wl.B, wl.N
         self.mode = wl.mode
+        self.fused_select = False
         if self.mode in ("sample", "sample_full"):
             self._init_sample(wl, dev)
             return
@@ -148,12 +153,16 @@ class Step:
         self.out = torch.empty(B, wl.H, wl.d_c, dtype=torch.float32, device=dev)
         self.lse = torch.empty(B, wl.H, dtype=torch.float32, device=dev)
         tk = csa2.csa2_topk_workspace_bytes(B, M, wl.K) if M else 0
+        # the fused chunk kernel runs when the rows hold a workgroup per CU
+        self.fused_select = self.mode in ("full", "prefill_full") and wl.D_I <= 128 and B * -(-N // 8192) >= 256
+        if self.mode in ("full", "prefill_full"):
+            tk = csa2.csa2_index_topk_full_workspace_bytes(B, wl.D_I, N, wl.K)
         nq = wl.prefill_rows if self.mode == "prefill_reuse" else B
         at = csa2.csa2_sparse_attn_workspace_bytes(nq, wl.H, wl.d_c, wl.K)
         self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
         self.ws_attn = torch.empty(max(at, 16), dtype=torch.uint8, device=dev) if at else None
-        self.stages = {"full": ["index", "topk", "attn"], "reindex": ["pool", "topk", "attn"],
-                       "reuse": ["attn"], "prefill_full": ["quantize", "index", "topk", "attn"],
+        self.stages = {"full": ["select", "attn"], "reindex": ["pool", "topk", "attn"],
+                       "reuse": ["attn"], "prefill_full": ["quantize", "select", "attn"],
                        "pool_build": ["index", "build"], "reuse_swa": ["attn", "swa"],
                        "prefill_reuse": ["attn"]}[self.mode]
         if self.mode == "prefill_reuse":
@@ -275,6 +284,10 @@ class Step:
     def index(self, r):
         self.csa2.csa2_index_full(self.sets[r]["qi"], self._keys(r), scores=self.scores)
 
+    def select(self, r):
+        self.csa2.csa2_index_topk_full(self.sets[r]["qi"], self._keys(r), self.wl.K, out_idx=self.idx,
+                                       out_score=self.top, workspace=self.ws_topk)
+
     def pool(self, r):
         st = self.sets[r]
         self.csa2.csa2_index_pool(st["qi"], self.keys, st["pool"], st["nb"], block=self.wl.block,
@@ -343,8 +356,9 @@ class Step:
             d["step"] = B * (N * wl.D_I * 2 + qi + wl.P_max * 4 + 4)
             return d
         if self.mode in ("full", "prefill_full"):
-            d["index"] = B * (N * wl.D_I * 2 + qi + N * 4)
-            d["topk"] = B * (N * 4 + K * 8)
+            # keys and queries read, the K (id, score) pairs written: the
+            # scores themselves are not algorithmic bytes
+            d["select"] = B * (N * wl.D_I * 2 + qi + K * 8)
             step += B * (N * wl.D_I * 2 + qi)
         if self.mode == "reindex":
             Mp = wl.P_max * wl.block
@@ -547,7 +561,10 @@ def main():
         g_ts.replay()
         torch_sampler_us = 1000.0 * timed(g_ts) / args.steps
         del g_ts
-    if "topk" in stages:
+    if "topk" in stages or "select" in stages:
+        if "select" in stages:      # score rows for the reference, outside the timed region
+            step.index(0)
+            torch.cuda.synchronize()
         g_tt = capture(lambda r: torch.topk(step.scores, wl.K, dim=1), args.steps, 0)
         g_tt.replay()
         torch_topk_us = 1000.0 * timed(g_tt) / args.steps
@@ -566,6 +583,7 @@ def main():
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
     kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
+                   "select": "index_topk.hip",
                    "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip",
                    "draw_full": "sample.hip"}[dom]
     achieved = alg[dom] / (stage_us[dom] * 1e-6) / 1e9
@@ -581,7 +599,10 @@ def main():
 
     n_queries = wl.prefill_rows if wl.mode == "prefill_reuse" else wl.B
     qps = n_queries / (ms_per_step * 1e-3)
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+    launches = {"select": "index_topk_kernel + topk_kernel (final level)" if step.fused_select else
+                "index_kernel + topk_kernel"}
+    roofline = {"bound": "hbm", "kernel": dom, "launches": launches.get(dom, dom), "achieved": achieved,
+                "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "alg_bytes_per_launch": alg[dom]}
     if wl.mode == "prefill_reuse":

@@ -181,6 +181,30 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
               void* workspace, size_t workspace_bytes, csa2_stream_t stream);
 
 /*
+ * a1 + a3 in one call, Full mode: the indexer scores of every entry and their
+ * Top-K ([P1] 架构三件套, CSA2: a Full layer scores every entry and keeps the
+ * Top-512; Hierarchical Sparse Indexer).  Bit for bit the result of
+ * csa2_index_full followed by csa2_topk(scores, NULL, n_valid, B, N_cap, K,
+ * ...) with the same n_valid: out_idx i32 [B, K] and out_score f32 [B, K]
+ * (nullable) as csa2_topk, ids being entry positions; entries n >= n_valid[b]
+ * are not candidates and their keys are not read.
+ * When the rows hold at least 256 chunks of 8192 entries (B * ceil(N_cap /
+ * 8192) >= 256) and D_I <= 128, one kernel scores each chunk on chip and
+ * keeps its K best, so the scores never reach device memory; otherwise the
+ * kernels of csa2_index_full and csa2_topk run, the scores in the workspace.
+ * The workspace (at least csa2_index_topk_full_workspace_bytes(B, D_I, N_cap,
+ * K) bytes, 16-byte aligned, caller-owned, contents not preserved) holds the
+ * chunk winners or the scores, and the Top-K's level buffers.
+ * Other arguments as csa2_index_full.  Requires 1 <= N_cap < 2^31,
+ * 1 <= K <= 2048, B >= 0.
+ */
+size_t csa2_index_topk_full_workspace_bytes(int32_t B, int32_t D_I, int64_t N_cap, int32_t K);
+int csa2_index_topk_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                         const int32_t* n_valid, int32_t B, int32_t H_I, int32_t D_I,
+                         int64_t N_cap, int32_t K, int32_t* out_idx, float* out_score,
+                         void* workspace, size_t workspace_bytes, csa2_stream_t stream);
+
+/*
  * csa2_topk without a workspace, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments (less the workspace), same results, bit

@@ -50,6 +50,8 @@ def load():
         "csa2_topk_workspace_bytes": (SZ, [I32, I64, I32]),
         "csa2_topk": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P, SZ, P]),
         "csa2_topk_noalloc": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P]),
+        "csa2_index_topk_full_workspace_bytes": (SZ, [I32, I32, I64, I32]),
+        "csa2_index_topk_full": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I64, I32, P, P, P, SZ, P]),
         "csa2_quantize_fp8": (ctypes.c_int, [P, I64, I32, P, I32, P, I64, P, P, I64, I64, I64, P]),
         "csa2_swa_attn_fp8": (ctypes.c_int, [P, P, I64, P, P, I64, P, I32, I32, I32, I32, I32, F, P, P, P, P, P]),
         "csa2_build_pool_workspace_bytes": (SZ, [I32, I64, I32, I32]),
@@ -250,6 +252,30 @@ def csa2_index_pool(q_idx, k_idx, pool_blocks, n_blocks, block=8, scores=None, p
                              _ptr(positions), _stream())
     _check("csa2_index_pool", st)
     return scores, positions
+
+
+def csa2_index_topk_full_workspace_bytes(B, D_I, N_cap, K):
+    return int(load().csa2_index_topk_full_workspace_bytes(B, D_I, N_cap, K))
+
+
+def csa2_index_topk_full(q_idx, k_idx, K, w=None, n_valid=None, out_idx=None, out_score=None, workspace=None,
+                         want_score=True):
+    """Full-mode indexer scores and their Top-K in one call: (idx i32 [B, K],
+    score f32 [B, K] or None), as csa2_topk(csa2_index_full(...), K, n_valid)."""
+    lib = load()
+    B, H_I, D_I, N_cap = _index_inputs(q_idx, k_idx, w, n_valid)
+    dev = k_idx.device
+    out_idx = _out(out_idx, (B, K), torch.int32, dev, "out_idx")
+    if out_score is not None or want_score:
+        out_score = _out(out_score, (B, K), torch.float32, dev, "out_score")
+    need = csa2_index_topk_full_workspace_bytes(B, D_I, N_cap, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.csa2_index_topk_full(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(n_valid), B, H_I, D_I, N_cap, K,
+                                  _ptr(out_idx), _ptr(out_score), _ptr(workspace), ws_bytes, _stream())
+    _check("csa2_index_topk_full", st)
+    return out_idx, out_score
 
 
 # ------------------------------------------------------------------ a3

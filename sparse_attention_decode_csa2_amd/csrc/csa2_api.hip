@@ -199,6 +199,31 @@ int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, i
                                       as_stream(stream)));
 }
 
+size_t csa2_index_topk_full_workspace_bytes(int32_t B, int32_t D_I, int64_t N_cap, int32_t K) {
+  if (B <= 0 || N_cap < 1 || N_cap > 0x7FFFFFFFll || K < 1 || K > 2048) return 0;
+  if (D_I != 32 && D_I != 64 && D_I != 128 && D_I != 256) return 0;
+  return csa2::index_topk_workspace_bytes(B, D_I, N_cap, K);
+}
+
+int csa2_index_topk_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int32_t* n_valid,
+                         int32_t B, int32_t H_I, int32_t D_I, int64_t N_cap, int32_t K, int32_t* out_idx,
+                         float* out_score, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+  if (B < 0 || N_cap < 1 || N_cap > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
+  if (K < 1 || K > 2048) return CSA2_ERR_RANGE;
+  if (H_I < 1 || H_I > 16 || (D_I != 32 && D_I != 64 && D_I != 128 && D_I != 256)) return CSA2_ERR_UNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  if (!q_idx || !k_idx || !out_idx) return CSA2_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(out_idx) || !opt_aligned16(w) ||
+      !opt_aligned16(n_valid) || !opt_aligned16(out_score))
+    return CSA2_ERR_ALIGN;
+  const size_t need = csa2::index_topk_workspace_bytes(B, D_I, N_cap, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;
+  if (too_large(csa2::index_topk_launch_items(B, D_I, N_cap, K))) return CSA2_ERR_RANGE;
+  return hip_status(csa2::launch_index_topk(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, K, out_idx, out_score,
+                                            workspace, as_stream(stream)));
+}
+
 int csa2_topk_noalloc(const float* scores, const int32_t* ids, const int32_t* n_valid, int32_t B, int64_t M,
                       int32_t K, int32_t* out_idx, float* out_score, csa2_stream_t stream) {
   if (B < 0 || M < 1 || M > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;

@@ -49,6 +49,18 @@ size_t topk_workspace_bytes(int B, int64_t M, int K);
 hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, int B,
                        int64_t M, int K, int32_t* out_idx, float* out_score, void* workspace,
                        hipStream_t stream);
+// The Top-K levels after the first, on B rows of m chunk-winner keys.
+size_t topk_keys_workspace_bytes(int B, int64_t m, int K);
+hipError_t launch_topk_from_keys(const uint64_t* keys, int B, int64_t m, int K, int32_t* out_idx,
+                                 float* out_score, void* workspace, hipStream_t stream);
+
+// Full-mode indexer scores and their Top-K in one call (fused chunk kernel when
+// the rows give a workgroup per CU, else the two kernels).
+int64_t index_topk_launch_items(int B, int D_I, int64_t N_cap, int K);
+size_t index_topk_workspace_bytes(int B, int D_I, int64_t N_cap, int K);
+hipError_t launch_index_topk(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* n_valid, int B,
+                             int H_I, int D_I, int64_t N_cap, int K, int32_t* out_idx, float* out_score,
+                             void* workspace, hipStream_t stream);
 
 size_t pool_workspace_bytes(int B, int64_t M, int block, int P_max);
 hipError_t launch_build_pool(const float* scores, const int32_t* n_valid, int B, int64_t M, int block,

@@ -5,21 +5,17 @@
 // ([P1] 架构三件套 - CSA2 and Hierarchical Sparse Indexer; [P4] CSA2 paragraph;
 // the ReLU-gated multi-head form is the reading documented in the header).
 //
-// The multi-head q . K contraction runs on the matrix cores: one
-// v_mfma_f32_16x16x32_bf16 per 32 key dimensions computes a 16 (heads, padded
-// with zero rows) x 16 (keys) tile.  For k-step s, lane (key l % 16, group
-// l / 16) supplies dimensions 32s + 8 (l / 16) .. +7 of its key; a wave's KS
-// steps cover 16 whole keys (contiguous in Full mode, two 8-entry runs per
-// tile in pool mode).  Full mode loads the 16 keys contiguously and reorders
-// them through LDS (see below); pool mode loads each lane's operand directly.
-// The query is laid out the same way, which is the MFMA's own k order.  The
-// epilogue applies ReLU and the head weights and reduces the four head
-// quarters across lane groups.
+// The multi-head q . K contraction of a 16-key tile runs on the matrix cores
+// (index_tile.h).  A wave's tiles hold 16 whole keys (contiguous in Full
+// mode, two 8-entry runs per tile in pool mode).  Full mode loads the 16 keys
+// contiguously and reorders them through LDS (see below); pool mode loads
+// each lane's operand directly unless its blocks allow the contiguous loads.
 //
 // HBM-bound: 2*D_I bytes of key per scored entry against 4*H_I*D_I flops
 // (8 flop/byte at H_I = 8): the matrix cores only have to keep up with HBM.
 #include "csa2_device.h"
 #include "csa2_internal.h"
+#include "index_tile.h"
 
 namespace csa2 {
 
@@ -38,24 +34,9 @@ __global__ __launch_bounds__(256) void index_kernel(
   const int64_t b = blockIdx.x / wg_per_row;
   const int64_t wg = blockIdx.x - b * wg_per_row;
 
-  // A operand: indexer query head n (rows >= H_I are zero), dims of quarter g
   bf16x8 A[KS];
-  {
-    const uint16_t* qrow = q + (b * H_I + n) * D_I + 8 * g;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (n < H_I) v = *reinterpret_cast<const u32x4*>(qrow + 32 * s);
-      A[s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  // weights of the four heads whose dot products this lane receives
   float wv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * g + i;
-    wv[i] = h < H_I ? (w ? w[b * H_I + h] : 1.0f) : 0.0f;
-  }
+  index_query<KS>(q, w, b, H_I, lane, A, wv);
   int64_t nv = N_cap;
   if (n_valid) nv = min<int64_t>(max<int64_t>(n_valid[b], 0), N_cap);
   int nb = 0;
@@ -138,24 +119,9 @@ __global__ __launch_bounds__(256) void index_kernel(
 #pragma unroll
       for (int s = 0; s < KS; ++s) Bt[s] = Bv[t][s];
     } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int w = 64 * s + lane;
-        kb[(w / KW) * (KW + 1) + w % KW] = Bv[t][s];
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) Bt[s] = kb[n * (KW + 1) + 4 * s + g];
+      index_reorder<KS>(Bv[t], kb, lane, Bt);
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mfma16x16x32_bf16(A[s], __builtin_bit_cast(bf16x8, Bt[s]), acc);
-    // acc[i] = dot(head 4g + i, key n of this tile)
-    float part = wv[0] * fmaxf(acc[0], 0.f);
-    part += wv[1] * fmaxf(acc[1], 0.f);
-    part += wv[2] * fmaxf(acc[2], 0.f);
-    part += wv[3] * fmaxf(acc[3], 0.f);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
+    const float part = index_tile_score<KS>(A, wv, Bt);
     const int64_t col = (tile0 + t) * 16 + n;
     if (g == 0 && col < M) {
       scores[b * M + col] = ok[t] ? part : -INFINITY;

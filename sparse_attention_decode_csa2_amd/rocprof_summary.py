@@ -39,11 +39,28 @@ import sys
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
+def _local_sources(name):
+    """The source file and every header of csrc/ it includes, directly or
+    through another (in the order first met)."""
+    seen, todo = [], [name]
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        seen.append(f)
+        with open(os.path.join(CSRC, f)) as fh:
+            todo += re.findall(r'^#include "([^"]+)"', fh.read(), flags=re.M)
+    return seen
+
+
 def kernel_source_hash(name):
-    """Hash of one kernel source file plus the shared device header."""
+    """Hash of one kernel source file plus the local headers it includes (less
+    csa2_internal.h, which only declares the host-side launch functions)."""
     h = hashlib.sha256()
-    for f in (os.path.join(CSRC, name), os.path.join(CSRC, "csa2_device.h")):
-        with open(f, "rb") as fh:
+    for f in _local_sources(name):
+        if f == "csa2_internal.h":
+            continue
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

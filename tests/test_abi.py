@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
 
@@ -89,6 +89,34 @@ def test_topk_validation(lib):
     assert lib.csa2_topk_workspace_bytes(2, 16384, 512) == 0
     assert f(A, N, N, 2, 40000, 512, A, N, N, 0, N) == WS
     assert f(A, N, N, 2, 40000, 512, A, N, A, need - 1, N) == WS
+
+
+def test_index_topk_validation(lib):
+    f = lib.csa2_index_topk_full
+    wsb = lib.csa2_index_topk_full_workspace_bytes
+    # fused (8 x 32 chunks of 8192): the chunk winners, one later level
+    assert wsb(8, 128, 262144, 512) == 8 * 32 * 512 * 8
+    # fused, one row of 256 chunks: winners + the middle level's 8 chunks
+    assert wsb(1, 128, 1 << 21, 512) == 256 * 512 * 8 + 8 * 512 * 8
+    # too few chunks (or D_I 256): the scores, then the Top-K's workspace
+    assert wsb(1, 128, 16384, 512) == 16384 * 4
+    assert wsb(8, 256, 262144, 512) == 8 * 262144 * 4 + 8 * 16 * 512 * 8
+    assert wsb(1, 128, 5, 4) == 32                   # scores rounded up to 16 bytes
+    assert wsb(0, 128, 100, 8) == 0 and wsb(1, 96, 100, 8) == 0 and wsb(1, 128, 100, 0) == 0
+    need = wsb(1, 128, 100, 8)
+
+    def call(q=A, k=A, B=1, H_I=8, D_I=128, N_cap=100, K=8, out=A, score=N, ws=A, wsn=need, w=N, nv=N):
+        return f(q, w, k, nv, B, H_I, D_I, N_cap, K, out, score, ws, wsn, N)
+    assert call(B=0) == OK
+    assert call(B=-1) == SHAPE
+    assert call(N_cap=0) == SHAPE
+    assert call(N_cap=1 << 31) == SHAPE
+    assert call(K=0) == RANGE and call(K=2049) == RANGE
+    assert call(H_I=17) == UNSUP and call(D_I=96) == UNSUP
+    assert call(q=N) == NULL and call(k=N) == NULL and call(out=N) == NULL
+    assert call(out=U) == ALIGN and call(w=U) == ALIGN and call(nv=U) == ALIGN and call(score=U) == ALIGN
+    assert call(ws=N) == WS and call(wsn=need - 1) == WS
+    assert call(ws=U) == ALIGN
 
 
 def test_build_pool_validation(lib):

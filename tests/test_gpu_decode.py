@@ -16,9 +16,12 @@ def _keys(wl, B):
     return torch.stack([W.index_keys(wl, b, DEV) for b in range(B)])
 
 
-def _check_full(wl, cache, k, qi, q, check_b, n_valid=None):
-    sc = csa2.csa2_index_full(qi, k, n_valid=n_valid)
-    idx, top = csa2.csa2_topk(sc, wl.K, n_valid=n_valid)
+def _check_full(wl, cache, k, qi, q, check_b, n_valid=None, fused=False):
+    if fused:
+        idx, top = csa2.csa2_index_topk_full(qi, k, wl.K, n_valid=n_valid)
+    else:
+        sc = csa2.csa2_index_full(qi, k, n_valid=n_valid)
+        idx, top = csa2.csa2_topk(sc, wl.K, n_valid=n_valid)
     out, lse = csa2.csa2_sparse_attn_fp4(q, cache.codes, cache.scales, cache.rope, idx, wl.sm_scale)
     torch.cuda.synchronize()
     for b in check_b:
@@ -116,7 +119,9 @@ def test_prefill_write_then_full_decode_1m():
             full[r0:] = np_bits(crope)
         return full if rows is None else full[np.asarray(rows)]
     cache.latents_host, cache.rope_host = lat0, rope0
-    _check_full(wl, cache, _keys(wl, wl.B), W.index_query(wl, DEV), W.attn_query(wl, DEV), range(wl.B))
+    # scores and Top-K in the one call the step makes (the fused chunk kernel here)
+    _check_full(wl, cache, _keys(wl, wl.B), W.index_query(wl, DEV), W.attn_query(wl, DEV), range(wl.B),
+                fused=True)
 
 
 def test_full_step_in_a_hip_graph_matches_eager():
