@@ -109,7 +109,7 @@ int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
   }
   const int st = check_index_common(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, scores);
   if (st != CSA2_OK) return st;
-  if (too_large(csa2::index_launch_items(B, N_cap, false))) return CSA2_ERR_RANGE;
+  if (too_large(csa2::index_launch_items(B, N_cap, false, 1, D_I))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_index(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, nullptr,
                                        nullptr, 0, 1, scores, nullptr, as_stream(stream)));
 }
@@ -125,7 +125,7 @@ int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
   if (st != CSA2_OK) return st;
   if (!pool_blocks || !n_blocks || !positions) return CSA2_ERR_NULL;
   if (!aligned16(pool_blocks) || !aligned16(n_blocks) || !aligned16(positions)) return CSA2_ERR_ALIGN;
-  if (too_large(csa2::index_launch_items(B, (int64_t)P_max * block, true))) return CSA2_ERR_RANGE;
+  if (too_large(csa2::index_launch_items(B, (int64_t)P_max * block, true, block, D_I))) return CSA2_ERR_RANGE;
   return hip_status(csa2::launch_index(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, pool_blocks,
                                        n_blocks, P_max, block, scores, positions,
                                        as_stream(stream)));

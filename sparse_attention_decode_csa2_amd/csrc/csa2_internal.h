@@ -15,7 +15,7 @@ namespace csa2 {
 constexpr int64_t kMaxLaunchItems = ((int64_t)1 << 32) - 1;
 int64_t quantize_fp4_launch_items(int64_t n_rows, int d_c, int d_r);
 int64_t quantize_fp8_launch_items(int64_t n_rows);
-int64_t index_launch_items(int B, int64_t M, bool pool);
+int64_t index_launch_items(int B, int64_t M, bool pool, int block, int D_I);
 int64_t topk_launch_items(int B, int64_t M, int K);
 int64_t pool_launch_items(int B, int64_t M, int block, int P_max);
 int64_t attn_launch_items(int B, int H, int d_c, int K);

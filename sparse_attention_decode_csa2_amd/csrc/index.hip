@@ -8,8 +8,11 @@
 // The multi-head q . K contraction of a 16-key tile runs on the matrix cores
 // (index_tile.h).  A wave's tiles hold 16 whole keys (contiguous in Full
 // mode, two 8-entry runs per tile in pool mode).  Full mode loads the 16 keys
-// contiguously and reorders them through LDS (see below); pool mode loads
-// each lane's operand directly unless its blocks allow the contiguous loads.
+// contiguously and reorders them through LDS (see below); pool mode with the
+// pool's 8-position blocks runs index_pool8_kernel (eight tiles per wave,
+// the block ids in one vector load, the next tile's keys in flight); other
+// block sizes load contiguously when their blocks allow it, else each lane's
+// operand directly.
 //
 // HBM-bound: 2*D_I bytes of key per scored entry against 4*H_I*D_I flops
 // (8 flop/byte at H_I = 8): the matrix cores only have to keep up with HBM.
@@ -130,11 +133,92 @@ __global__ __launch_bounds__(256) void index_kernel(
   }
 }
 
-// Grid of the indexer: 16-key tiles, four waves per workgroup, `tpw` tiles per
-// wave.  Tiles per wave, measured: Full mode is fastest with one (its
+// Pool mode with the candidate pool's 8-position blocks (a 16-key tile is two
+// whole blocks) and keys of 64 dimensions or more: one wave scores POOL_TW
+// consecutive tiles.  It loads the block ids of all its tiles with one vector
+// load (block 2 t + l of its tiles in lane l) and takes each with a lane read,
+// loads its query operand once, and keeps the next tile's key loads in flight
+// while it scores a tile.  The loads and the LDS reorder are the contiguous
+// ones of index_kernel (KPL keys of one block per wave-wide load).
+// Measured on the 32 x 2048-block pool over 262144 entries: 27.0 us against
+// 28.5 with 4 tiles per wave, 29.9 with 16, 28.9 for the 4-wave grid of
+// index_kernel (two tiles per wave), and 31.4 with two tiles in flight.
+constexpr int POOL_TW = 8;
+static_assert(2 * POOL_TW <= 64, "a wave's block ids fit one vector register");
+
+template <int KS>
+__global__ __launch_bounds__(256) void index_pool8_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
+    const int32_t* __restrict__ n_valid, int H_I, int64_t N_cap, const int32_t* __restrict__ pool,
+    const int32_t* __restrict__ n_blocks, int P_max, int64_t M, int64_t wg_per_row, float* __restrict__ scores,
+    int32_t* __restrict__ positions) {
+  constexpr int D_I = 32 * KS;
+  constexpr int KW = D_I / 8;   // 16-byte words per key
+  constexpr int KPL = 64 / KW;  // keys per wave-wide load
+  static_assert(8 % KPL == 0, "a wave-wide load stays in one 8-position block");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t b = blockIdx.x / wg_per_row;
+  const int64_t wg = blockIdx.x - b * wg_per_row;
+  bf16x8 A[KS];
+  float wv[4];
+  index_query<KS>(q, w, b, H_I, lane, A, wv);
+  int64_t nv = N_cap;
+  if (n_valid) nv = min<int64_t>(max<int64_t>(n_valid[b], 0), N_cap);
+  const int64_t nb = min(max(n_blocks[b], 0), P_max);
+  const int64_t tile0 = (wg * 4 + wave) * POOL_TW;
+  int blk_l = -1;  // block id of pool slot 2 tile0 + lane (-1: empty slot)
+  if (lane < 2 * POOL_TW && 2 * tile0 + lane < nb) blk_l = pool[b * P_max + 2 * tile0 + lane];
+  __shared__ u32x4 kbuf[4][16 * (KW + 1)];
+  u32x4* kb = kbuf[wave];
+  const uint16_t* krow = k + b * N_cap * D_I;
+  // load s of the wave's tile t: keys KPL s .. of the tile, in block 2 t + KPL s / 8
+  auto load = [&](int t, u32x4 (&Bv)[KS]) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = KPL * s;
+      const int64_t blk = __builtin_amdgcn_readlane(blk_l, 2 * t + c / 8);
+      const int64_t p = blk * 8 + c % 8 + lane / KW;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (blk >= 0 && p < nv)
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + p * D_I + 8 * (lane % KW)));
+      Bv[s] = v;
+    }
+  };
+  u32x4 cur[KS];
+  load(0, cur);
+  for (int t = 0; t < POOL_TW; ++t) {
+    const int64_t tile = tile0 + t;
+    if (tile * 16 >= M) break;
+    const bool more = t + 1 < POOL_TW && (tile + 1) * 16 < M;
+    u32x4 nxt[KS];
+    if (more) load(t + 1, nxt);
+    u32x4 Bt[KS];
+    index_reorder<KS>(cur, kb, lane, Bt);
+    const float part = index_tile_score<KS>(A, wv, Bt);
+    const int64_t col = tile * 16 + n;
+    if (g == 0 && col < M) {
+      const int blk_a = __builtin_amdgcn_readlane(blk_l, 2 * t), blk_b = __builtin_amdgcn_readlane(blk_l, 2 * t + 1);
+      const int64_t blk = n < 8 ? blk_a : blk_b;
+      const int64_t p = blk * 8 + (n & 7);
+      const bool ok = blk >= 0 && p < nv;
+      scores[b * M + col] = ok ? part : -INFINITY;
+      positions[b * M + col] = ok ? (int32_t)p : -1;
+    }
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) cur[s] = nxt[s];
+    }
+  }
+}
+
+// Grid of index_kernel: 16-key tiles, four waves per workgroup, `tpw` tiles
+// per wave.  Tiles per wave, measured: Full mode is fastest with one (its
 // contiguous loads keep enough in flight; prefill-full-1m 80.6 us against
-// 86.7 with four); pool mode, whose loads wait for block lookups, with two once
-// the grid fills the GPU (reindex-1m 28.7 us against 30.4 with four).
+// 86.7 with four); pool mode (blocks other than 8 positions, or 32-dimension
+// keys), whose loads wait for block lookups, with two once the grid fills the
+// GPU (the 2048 x 8 pool: 28.7 us against 30.4 with four).
 static void index_grid(int B, int64_t M, bool pool, int* tpw, int64_t* wg_per_row) {
   const int64_t tiles_per_row = (M + 15) / 16;
   const int64_t total_tiles = tiles_per_row * B;
@@ -142,7 +226,11 @@ static void index_grid(int B, int64_t M, bool pool, int* tpw, int64_t* wg_per_ro
   *wg_per_row = (tiles_per_row + 4 * *tpw - 1) / (4 * *tpw);
 }
 
-int64_t index_launch_items(int B, int64_t M, bool pool) {
+int64_t index_launch_items(int B, int64_t M, bool pool, int block, int D_I) {
+  if (pool && block == 8 && D_I >= 64) {
+    const int64_t tiles = (M + 15) / 16;
+    return (tiles + 4 * POOL_TW - 1) / (4 * POOL_TW) * B * 256;
+  }
   int tpw;
   int64_t wpr;
   index_grid(B, M, pool, &tpw, &wpr);
@@ -161,6 +249,14 @@ static hipError_t launch_index_ks(const uint16_t* q, const float* w, const uint1
 #define CSA2_IDX_LAUNCH(T, BL)                                                                          \
   hipLaunchKernelGGL((index_kernel<KS, T, POOL, BL>), grid, blk, 0, stream, q, w, k, n_valid, H_I, N_cap, \
                      pool, n_blocks, P_max, block, M, wg_per_row, scores, positions)
+  if constexpr (POOL && KS >= 2) {
+    if (block == 8) {
+      const int64_t tiles = (M + 15) / 16, wpr = (tiles + 4 * POOL_TW - 1) / (4 * POOL_TW);
+      hipLaunchKernelGGL((index_pool8_kernel<KS>), dim3((unsigned)(wpr * B)), blk, 0, stream, q, w, k, n_valid,
+                         H_I, N_cap, pool, n_blocks, P_max, M, wpr, scores, positions);
+      return hipGetLastError();
+    }
+  }
   if (POOL && block == 8) {
     if (tpw == 2) CSA2_IDX_LAUNCH(2, 8);
     else CSA2_IDX_LAUNCH(1, 8);

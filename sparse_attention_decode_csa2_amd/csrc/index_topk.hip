@@ -129,7 +129,7 @@ static bool it_fused(int B, int D_I, int64_t N_cap) {
 
 int64_t index_topk_launch_items(int B, int D_I, int64_t N_cap, int K) {
   if (!it_fused(B, D_I, N_cap)) {
-    const int64_t a = index_launch_items(B, N_cap, false), t = topk_launch_items(B, N_cap, K);
+    const int64_t a = index_launch_items(B, N_cap, false, 1, D_I), t = topk_launch_items(B, N_cap, K);
     return a > t ? a : t;
   }
   return (int64_t)B * it_chunks(N_cap) * TK_T;

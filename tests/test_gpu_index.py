@@ -101,3 +101,24 @@ def test_pool_mode_edges(D_I, blocks):
         rs, rp = oracle.index_pool(np_bits(q), None, np_bits(k), nv, blk, nb, block)
         assert np.array_equal(pos.cpu().numpy(), rp), block
         assert np.array_equal(sc.cpu().numpy().astype(np.float64), rs), block
+
+
+@pytest.mark.parametrize("D_I,P_max", [(256, 41), (128, 33), (64, 7), (128, 2048)])
+def test_pool_mode_8_position_blocks(D_I, P_max):
+    """The pool's 8-position blocks (the streaming pool kernel, eight tiles per
+    wave): an odd P_max leaves the last tile half empty, and waves whose tiles
+    run past it; empty slots, negative ids and ids past n_valid."""
+    N = 8 * 3000
+    note(f"index_pool: 8-position blocks D_I={D_I} P_max={P_max}")
+    wl = W.WORKLOADS[1].scaled(B=3, N=N, H_I=8, D_I=D_I)
+    k = _keys(wl, 3)
+    q = W.index_query(wl, DEV)
+    rng = np.random.default_rng(P_max + D_I)
+    blk = rng.integers(-2, N // 8 + 5, size=(3, P_max)).astype(np.int32)
+    nb = np.array([P_max, P_max // 2 + 1, 0], dtype=np.int32)
+    nv = np.array([N, 12345, N], dtype=np.int32)
+    bt, nbt, nvt = (torch.from_numpy(a).to(DEV) for a in (blk, nb, nv))
+    sc, pos = csa2.csa2_index_pool(q, k, bt, nbt, block=8, n_valid=nvt)
+    rs, rp = oracle.index_pool(np_bits(q), None, np_bits(k), nv, blk, nb, 8)
+    assert np.array_equal(pos.cpu().numpy(), rp)
+    assert np.array_equal(sc.cpu().numpy().astype(np.float64), rs)

@@ -54,8 +54,11 @@ def _check(s, K, ids=None, nv=None):
     assert np.array_equal(gs, rs, equal_nan=True)
 
 
+# rows of one chunk, of two levels (3, 5 and 19 chunks of 16384; 8 chunks at
+# K = 2048, whose winners fill the final chunk) and ragged tails
 CASES = [(1, 1, 1), (2, 7, 4), (3, 1000, 64), (1, 16384, 512), (2, 16385, 512), (2, 40000, 512),
-         (1, 5000, 2048), (4, 16384, 2048), (2, 100, 512), (1, 300000, 100)]
+         (1, 5000, 2048), (4, 16384, 2048), (2, 100, 512), (1, 300000, 100), (2, 81920, 512),
+         (1, 131072, 2048)]
 
 
 @pytest.mark.parametrize("B,M,K", CASES)
