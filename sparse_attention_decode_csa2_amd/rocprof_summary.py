@@ -54,10 +54,15 @@ def _local_sources(name):
 
 
 def kernel_source_hash(name):
-    """Hash of one kernel source file plus the local headers it includes (less
-    csa2_internal.h, which only declares the host-side launch functions)."""
+    """Hash of a kernel source file plus the local headers it includes (less
+    csa2_internal.h, which only declares the host-side launch functions).
+    `name` may join several files with '+' (a stage whose launches come from
+    more than one file)."""
     h = hashlib.sha256()
-    for f in _local_sources(name):
+    files = []
+    for part in name.split("+"):
+        files += [f for f in _local_sources(part) if f not in files]
+    for f in files:
         if f == "csa2_internal.h":
             continue
         with open(os.path.join(CSRC, f), "rb") as fh:
