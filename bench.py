@@ -96,7 +96,7 @@ class Step:
     Reuse (reuse-128k): attn over one cache; sets = index lists + queries.
     Prefill + Full (prefill-full-1m): quantize (append 8192 rows) -> select -> attn.
     Pool construction (pool-build-1m): index (Full scores) -> build (the Reindex pool).
-    Reuse + window (reuse-swa-128k): attn -> swa (the FP8 window branch merged in).
+    Reuse + window (reuse-swa-128k): attn_swa (the selected entries and the FP8 window in one softmax).
     Sampler (sample-129k): topk (over the vocabulary logits) -> draw; sets = logits + uniforms.
     Prefill, Reuse layer (prefill-reuse-1m): attn over one cache for the 8192 queries of a chunk,
     each with its own causal list; sets = queries + lists.
@@ -163,12 +163,14 @@ class Step:
         self.ws_attn = torch.empty(max(at, 16), dtype=torch.uint8, device=dev) if at else None
         self.stages = {"full": ["select", "attn"], "reindex": ["pool", "topk", "attn"],
                        "reuse": ["attn"], "prefill_full": ["quantize", "select", "attn"],
-                       "pool_build": ["index", "build"], "reuse_swa": ["attn", "swa"],
+                       "pool_build": ["index", "build"], "reuse_swa": ["attn_swa"],
                        "prefill_reuse": ["attn"]}[self.mode]
         if self.mode == "prefill_reuse":
             self.out = torch.empty(1, wl.prefill_rows, wl.H, wl.d_c, dtype=torch.float32, device=dev)
             self.lse = torch.empty(1, wl.prefill_rows, wl.H, dtype=torch.float32, device=dev)
         if self.mode == "reuse_swa":
+            sw = csa2.csa2_sparse_swa_attn_workspace_bytes(B, wl.H, wl.d_c, wl.K)
+            self.ws_swa = torch.empty(max(sw, 16), dtype=torch.uint8, device=dev)
             Wn = wl.window
             self.win = csa2.alloc_window(B, Wn, wl.d_c, wl.d_r, dev)
             for b in range(B):
@@ -306,6 +308,12 @@ class Step:
         self.csa2.csa2_topk(self.scores, self.wl.K, ids=ids, out_idx=self.idx, out_score=self.top,
                             workspace=self.ws_topk)
 
+    def attn_swa(self, r):
+        kv, st = self.cache, self.sets[r]
+        c, sg, rp = self.win
+        self.csa2.csa2_sparse_swa_attn_fp4(st["q"], kv["codes"], kv["scales"], kv["rope"], st["idx"], c, sg, rp,
+                                           self.wl.sm_scale, out=self.out, lse=self.lse, workspace=self.ws_swa)
+
     def swa(self, r):
         c, sg, rp = self.win
         self.csa2.csa2_swa_attn_fp8(self.sets[r]["q"], c, sg, rp, self.wl.sm_scale, merge_out=self.out,
@@ -347,7 +355,7 @@ class Step:
         step = attn
         if self.mode == "reuse_swa":
             win = B * wl.window * _window_bytes(wl)
-            d["swa"] = win + B * (H * wl.D * 2 + 2 * (H * wl.d_c * 4 + H * 4))
+            d["attn_swa"] = attn + win
             d["step"] = attn + win
             return d
         if self.mode == "pool_build":
@@ -584,6 +592,7 @@ def main():
     dom = max(stages, key=lambda s: stage_us[s])
     kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
                    "select": "index_topk.hip+topk.hip" if step.fused_select else "index_topk.hip+index.hip+topk.hip",
+                   "attn_swa": "attn.hip",
                    "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip",
                    "draw_full": "sample.hip"}[dom]
     achieved = alg[dom] / (stage_us[dom] * 1e-6) / 1e9

@@ -319,6 +319,38 @@ int csa2_quantize_fp8(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint
                       csa2_stream_t stream);
 
 /*
+ * The sparse attention and the sliding window in one call: one softmax over
+ * the union of the selected entries and the query's window rows ([P4] CSA2
+ * paragraph: the SWA branch, its KV in FP8, beside the sparse one), i.e. the
+ * result csa2_sparse_attn_fp4 followed by csa2_swa_attn_fp8 merging into it
+ * gives, up to rounding.  Arguments as csa2_sparse_attn_fp4 (the selected
+ * entries) and csa2_swa_attn_fp8 (w_codes / w_sigma / w_rope / n_win / W_cap,
+ * the window rows of query b); W_cap = 0 (window pointers may then be NULL)
+ * is the sparse attention alone.  out f32 [B, H, 512], lse f32 [B, H]
+ * (nullable).
+ * When the batch fills the GPU with 32-head workgroups (B * ceil(H / 32) >=
+ * 256) one kernel attends to the window rows as its first tiles: exact E4M3
+ * values in fp16, the row scale applied to the fp32 latent scores and, as
+ * sigma_j / max sigma, to the probabilities of the value products, the
+ * accumulator taking max sigma before the first selected entry.  Other
+ * batches run the sparse kernels, then the window kernel merging into their
+ * result.  The error is < 2e-3 of max|out| per (b, h) row.
+ * Requires d_c == 512, d_r in {0, 64}, 1 <= H <= 128, K >= 1, 0 <= W_cap <=
+ * 256, the alignment rules of both calls, and a workspace of at least
+ * csa2_sparse_swa_attn_workspace_bytes(B, H, d_c, K) bytes (16-byte aligned,
+ * caller-owned, contents not preserved).
+ */
+size_t csa2_sparse_swa_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t K);
+int csa2_sparse_swa_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
+                             const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
+                             int64_t rope_stride, const int32_t* idx, int32_t K, int32_t B, int32_t H,
+                             int32_t d_c, int32_t d_r, int64_t N_cap, const uint8_t* w_codes,
+                             int64_t w_codes_stride, const float* w_sigma, const uint16_t* w_rope,
+                             int64_t w_rope_stride, const int32_t* n_win, int32_t W_cap, float sm_scale,
+                             float* out, float* lse, void* workspace, size_t workspace_bytes,
+                             csa2_stream_t stream);
+
+/*
  * Sliding-window branch, attention, and its merge with the sparse branch.  A
  * layer's sparse branch and its SWA branch ([P4] CSA2 paragraph) are read as
  * one softmax over the union of their keys: the window rows attend like the

@@ -61,6 +61,9 @@ def load():
         "csa2_sample": (ctypes.c_int, [P, I32, I64, I32, F, F, P, P, P, P, P, SZ, P]),
         "csa2_sample_full": (ctypes.c_int, [P, I32, I64, F, P, P, P, P]),
         "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "csa2_sparse_swa_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "csa2_sparse_swa_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I64,
+                                                    P, I64, P, P, I64, P, I32, F, P, P, P, SZ, P]),
         "csa2_sparse_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I64,
                                                 F, P, P, P, SZ, P]),
         "csa2_prefill_sparse_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I32,
@@ -539,6 +542,62 @@ def csa2_sparse_attn_fp4(q, codes, scales, rope, idx, sm_scale=None, out=None, l
                                   _ptr(rope if d_r > 0 else None), rs, _ptr(idx), K, B, H, d_c, d_r, N_cap,
                                   float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream())
     _check("csa2_sparse_attn_fp4", st)
+    return out, lse
+
+
+def csa2_sparse_swa_attn_workspace_bytes(B, H, d_c, K):
+    return int(load().csa2_sparse_swa_attn_workspace_bytes(B, H, d_c, K))
+
+
+def csa2_sparse_swa_attn_fp4(q, codes, scales, rope, idx, w_codes, w_sigma, w_rope, sm_scale=None, n_win=None,
+                             out=None, lse=None, workspace=None, want_lse=True):
+    """Sparse attention over the selected FP4 entries and the FP8 window rows
+    (w_codes [B, W_cap, d_c] E4M3, w_sigma [B, W_cap], w_rope [B, W_cap, d_r]
+    as from alloc_window) in one softmax: returns (out f32 [B, H, d_c],
+    lse f32 [B, H])."""
+    lib = load()
+    _need(q, torch.bfloat16, "q")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, H, D], got {tuple(q.shape)}")
+    B, H, D = q.shape
+    N_cap = codes.shape[1]
+    d_c = codes.shape[2] * 2
+    d_r = D - d_c
+    _cache_views(codes, scales, rope, d_r, 3)
+    _need(idx, torch.int32, "idx")
+    if idx.dim() != 2 or idx.shape[0] != B:
+        raise ValueError(f"idx must be [B={B}, K], got {tuple(idx.shape)}")
+    K = idx.shape[1]
+    if codes.shape[0] < B:
+        raise ValueError(f"the cache holds {codes.shape[0]} sequences, {B} queries need one each")
+    if w_codes.dtype != torch.uint8 or w_codes.dim() != 3 or w_codes.shape[0] != B or w_codes.shape[2] != d_c:
+        raise ValueError(f"w_codes must be a uint8 [{B}, W_cap, {d_c}] view, got {tuple(w_codes.shape)}")
+    W_cap = w_codes.shape[1]
+    _need(w_sigma, torch.float32, "w_sigma", (B, W_cap))
+    if d_r > 0 and (w_rope is None or w_rope.dtype != torch.bfloat16 or tuple(w_rope.shape) != (B, W_cap, d_r)):
+        raise ValueError(f"w_rope must be a bf16 [{B}, {W_cap}, {d_r}] view")
+    if n_win is not None:
+        _need(n_win, torch.int32, "n_win", (B,))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    out = _out(out, (B, H, d_c), torch.float32, dev, "out")
+    if lse is not None or want_lse:
+        lse = _out(lse, (B, H), torch.float32, dev, "lse")
+    need = csa2_sparse_swa_attn_workspace_bytes(B, H, d_c, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cs = _row_stride(codes, 1, "codes")
+    ss = _row_stride(scales, 1, "scales")
+    rs = _row_stride(rope, 2, "rope") if d_r > 0 else 0
+    wcs = _row_stride(w_codes, 1, "w_codes")
+    wrs = _row_stride(w_rope, 2, "w_rope") if d_r > 0 else 0
+    st = lib.csa2_sparse_swa_attn_fp4(_ptr(q), _ptr(codes), cs, _ptr(scales), ss, _ptr(rope if d_r > 0 else None),
+                                      rs, _ptr(idx), K, B, H, d_c, d_r, N_cap, _ptr(w_codes), wcs, _ptr(w_sigma),
+                                      _ptr(w_rope if d_r > 0 else None), wrs, _ptr(n_win), W_cap, float(sm_scale),
+                                      _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream())
+    _check("csa2_sparse_swa_attn_fp4", st)
     return out, lse
 
 

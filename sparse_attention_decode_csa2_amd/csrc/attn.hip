@@ -437,7 +437,7 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
     const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, int qps, float sm_scale_log2e, int n_hp,
     int n_split, int per_split, int spread, float* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, const WinRef win) {
   constexpr int DC = 512;
   constexpr int KSL = DC / 32;           // latent k-steps of the scores
   constexpr int KSR = DR / 32;           // RoPE k-steps
@@ -452,6 +452,8 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   __shared__ __attribute__((aligned(16))) float sHd[4][2][32];     // value wave: per-head broadcast
   __shared__ float sFs[32];                                        // per head: MFMA result -> base-2 logit
   __shared__ int32_t sIdx[AT_IDS_PAD];
+  __shared__ float sFw[2][AT_TILE];                                // window tile: sigma_j / max sigma
+  __shared__ float sWm[8];                                         // per wave: largest window row scale
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -475,6 +477,23 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   const int e_end = min(K, e_begin + per_split);
   const int32_t* idx_row = idx + b * K;
   const int n_tiles = N_cap > 0 ? (e_end - e_begin + AT_TILE - 1) / AT_TILE : 0;
+  // the query's sliding window (slice 0 only): its rows j < nw are n_wt more
+  // tiles after the selected entries', in a second loop (one tile gathered at
+  // a time: the window's 128-byte rows per lane have no room for look-ahead
+  // buffers beside the entry pipeline's).  Window values are exact E4M3
+  // values in fp16; the row scale sigma_j multiplies the latent score in fp32
+  // and enters the value products as P * sigma_j / sigma_max, the
+  // accumulator being divided by sigma_max before the first window tile and
+  // multiplied by it in the epilogue (powers of two: exact)
+  const int nw = (win.codes && split == 0) ? (win.n_win ? min(max(win.n_win[b], 0), win.W_cap) : win.W_cap) : 0;
+  const int n_wt = (nw + AT_TILE - 1) / AT_TILE;
+  {
+    float sg = 0.f;
+    if (tid < nw) sg = win.sigma[b * win.W_cap + tid];  // nw <= 256 < 512 threads
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) sg = fmaxf(sg, __shfl_xor(sg, o));
+    if (lane == 0) sWm[wave] = sg;
+  }
   // wave-uniform sequence bases (query b reads sequence b / qps); rows are
   // addressed by 32-bit offsets from them
   const int64_t sq = b / qps;
@@ -511,6 +530,11 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   // iterations: in iteration i the score waves handle tile i (buffer i % 2)
   // and the value waves tile i - 1; an even count, one barrier each
   const int n_iter = n_tiles > 0 ? (n_tiles + 2) & ~1 : 0;
+  const int n_iter_w = n_wt > 0 ? (n_wt + 2) & ~1 : 0;
+  float sig_max = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sig_max = fmaxf(sig_max, sWm[i]);
+  const float inv_sig_max = sig_max > 0.f ? 1.0f / sig_max : 0.f;
   // converted query: 16-byte piece (k, t, lane) = head group k, k-step t of
   // score-wave lane (n, g), in the second value buffer (first written by tile 1)
   const u32x4* qcv = reinterpret_cast<const u32x4*>(&sV[1][0][0]);
@@ -585,13 +609,91 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
       }
     };
 
+    // ---- window rows: row 64 tile + 16 w + n, the lane's channels 128 i +
+    // 32 g .. + 31 (i < 4) as two 16-byte words of E4M3 values each, 16
+    // channels of the RoPE part and the row scale
+    struct WinRegs {
+      u32x4 cw[8];
+      u32x4 rw[RW];
+      float sig;
+      bool valid;
+    };
+    auto wgather = [&](WinRegs& wr, int tile) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int row = tile * AT_TILE + 16 * w + n;
+      wr.valid = row < nw;
+      const int64_t rr = b * win.W_cap + (wr.valid ? row : 0);
+      const uint8_t* crow = win.codes + rr * win.codes_stride + 32 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wr.cw[2 * i] = *reinterpret_cast<const u32x4*>(crow + 128 * i);
+        wr.cw[2 * i + 1] = *reinterpret_cast<const u32x4*>(crow + 128 * i + 16);
+      }
+      if constexpr (DR > 0) {
+        const uint8_t* rrow = reinterpret_cast<const uint8_t*>(win.rope) + rr * win.rope_stride + 32 * g;
+#pragma unroll
+        for (int t = 0; t < RW; ++t) wr.rw[t] = *reinterpret_cast<const u32x4*>(rrow + 16 * t);
+      }
+      wr.sig = win.sigma[rr];
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // exact E4M3 -> fp16 into the value tile and the score products (latent
+    // and RoPE in separate accumulators: the row scale multiplies the latent
+    // part only); the value waves get sigma_j / max sigma for the entry
+    auto wprocess = [&](WinRegs& wr, int buf) {
+      __builtin_amdgcn_sched_barrier(0);
+      _Float16 (*tk)[LDK] = sV[buf];
+      const int e = 16 * w + n;
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+      f32x4 r0 = {0.f, 0.f, 0.f, 0.f}, r1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 src = wr.cw[2 * i + (j >> 1)];
+          const uint32_t lo = src[2 * (j & 1)], hi = src[2 * (j & 1) + 1];
+          const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+          const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+          const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+          const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+          f16x8 a = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          if (!wr.valid) a = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          *reinterpret_cast<f16x8*>(&tk[e][tile_col(e, 4 * i + g, j)]) = a;
+          c0 = mfma16x16x32_f16(a, Bq[0][4 * i + j], c0);
+          c1 = mfma16x16x32_f16(a, Bq[1][4 * i + j], c1);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < KSR; ++t) {
+        const bf16x8 rv = __builtin_bit_cast(bf16x8, wr.rw[t]);
+        r0 = mfma16x16x32_bf16(rv, Br[0][t], r0);
+        r1 = mfma16x16x32_bf16(rv, Br[1][t], r1);
+      }
+      // c_k[i], r_k[i]: entry 16 w + 4 g + i, head hq0 + 16 k + n; its row
+      // scale is held by lane 4 g + i
+      float sg[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sg[i] = __shfl(wr.sig, 4 * g + i);
+      const uint64_t vb = __ballot(g == 0 && wr.valid);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const f32x4 c = k ? c1 : c0, rp = k ? r1 : r0;
+        f32x4 sv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sv[i] = ((vb >> (4 * g + i)) & 1u) ? (c[i] * sg[i] + rp[i]) * fscale[k] : -INFINITY;
+        *reinterpret_cast<f32x4*>(&sS[buf][16 * k + n][16 * w + 4 * g]) = sv;
+      }
+      if (g == 0) sFw[buf][e] = wr.sig * inv_sig_max;
+    };
+
     GR ga, gb;
     if (n_iter > 0) {
       gather(ga, 0);
       gather(gb, 1);
     }
     __syncthreads();  // the value waves have written the converted query
-    if (n_iter > 0) {
+    if (n_iter + n_iter_w > 0) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
 #pragma unroll
@@ -600,6 +702,8 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
         for (int t = 0; t < KSR; ++t) Br[k][t] = __builtin_bit_cast(bf16x8, qcv[(k * KS + KSL + t) * 64 + lane]);
         fscale[k] = sFs[16 * k + n];
       }
+    }
+    if (n_iter > 0) {
       // every gather is unconditional (past the last tile they load row 0
       // again), so each process step waits for exactly the loads it needs
       for (int i = 0; i < n_iter; i += 2) {
@@ -614,6 +718,20 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
       // waits for them, so that no load returns into its registers after it
       // has ended and they have been handed to another wave
       __builtin_amdgcn_s_waitcnt(0);
+    }
+    // window tiles: gathered and scored one at a time
+    for (int i = 0; i < n_iter_w; i += 2) {
+      WinRegs wr;
+      if (i < n_wt) {
+        wgather(wr, i);
+        wprocess(wr, 0);
+      }
+      __syncthreads();
+      if (i + 1 < n_wt) {
+        wgather(wr, i + 1);
+        wprocess(wr, 1);
+      }
+      __syncthreads();
     }
     return;
   }
@@ -677,7 +795,9 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   // points at 4 channels of one entry row
   const int G = lane >> 4, tr_r = (lane & 15) >> 2, tr_c = lane & 3;
 
-  auto pv = [&](int buf) {
+  // wtile: a window tile, whose P enters the value products as P * sigma_j /
+  // max sigma; the first one divides the accumulator by max sigma
+  auto pv = [&](int buf, bool wtile, bool first_w) {
     _Float16 (*tk)[LDK] = sV[buf];
     // ---- softmax of head hl over the tile: this lane holds entries 16 u +
     // 8 kh + 0..7 (u < 4), its partner lane hl + 32 the other half
@@ -696,13 +816,27 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
     f16x8 a[4];
     float ps = 0.f;
+    if (wtile) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sFw[buf][16 * u + 8 * kh]);
+        const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sFw[buf][16 * u + 8 * kh + 4]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(sv[2 * u + (j >> 2)][j & 3] - m_ref);
-        ps += p;
-        a[u][j] = (_Float16)p;
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(sv[2 * u + (j >> 2)][j & 3] - m_ref);
+          ps += p;
+          a[u][j] = (_Float16)(p * (j < 4 ? f0[j & 3] : f1[j & 3]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(sv[2 * u + (j >> 2)][j & 3] - m_ref);
+          ps += p;
+          a[u][j] = (_Float16)p;
+        }
       }
     }
     ps += xor32f(ps);
@@ -713,6 +847,10 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     f32x4 al[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) al[qq] = *reinterpret_cast<const f32x4*>(&sHd[r][0][8 * qq + 4 * kh]);
+    if (first_w && sig_max > 0.f) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) al[qq] *= inv_sig_max;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -732,11 +870,18 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   };
 
   for (int i = 0; i < n_iter; i += 2) {
-    if (i >= 1 && i - 1 < n_tiles) pv(1);
+    if (i >= 1 && i - 1 < n_tiles) pv(1, false, false);
     __syncthreads();
-    if (i < n_tiles) pv(0);
+    if (i < n_tiles) pv(0, false, false);
     __syncthreads();
   }
+  for (int i = 0; i < n_iter_w; i += 2) {
+    if (i >= 1 && i - 1 < n_wt) pv(1, true, false);
+    __syncthreads();
+    if (i < n_wt) pv(0, true, i == 0);
+    __syncthreads();
+  }
+  const float tail = (n_wt > 0 && sig_max > 0.f) ? sig_max : 1.f;
 
   // ---- epilogue: element i of acc[k] is head 8 (i / 4) + 4 kh + i % 4,
   // channel 32 (4 r + k) + hl
@@ -754,14 +899,14 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     if (h >= H) continue;
     const float l = lv[i >> 2][i & 3];
     if (n_split == 1) {
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      const float inv = l > 0.f ? tail / l : 0.f;
       float* orow = out + (b * H + h) * DC + 128 * r + hl;
 #pragma unroll
       for (int k = 0; k < 4; ++k) orow[32 * k] = acc[k][i] * inv;
     } else {
       float* orow = ws_o + ((b * H + h) * n_split + split) * DC + 128 * r + hl;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) orow[32 * k] = acc[k][i];
+      for (int k = 0; k < 4; ++k) orow[32 * k] = acc[k][i] * tail;
     }
   }
   if (r == 0 && kh == 0 && hq0 + hl < H) {
@@ -900,13 +1045,14 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
 #define CSA2_ATTN(KERNEL, THREADS, DCV, DRV)                                                          \
   hipLaunchKernelGGL((KERNEL<DCV, DRV>), grid, dim3(THREADS), 0, stream, q, cache, idx, K, B, H, N_cap, qps, sl, \
                      n_hg, s, ps, spread, out, lse, ws_o, ws_ml)
+  const WinRef no_win{nullptr, 0, nullptr, nullptr, 0, nullptr, 0};
   if (hpw == 32) {
     if (d_r == 64)
       hipLaunchKernelGGL((sparse_attn_role_kernel<64>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, qps,
-                         sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml);
+                         sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, no_win);
     else if (d_r == 0)
       hipLaunchKernelGGL((sparse_attn_role_kernel<0>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, qps,
-                         sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml);
+                         sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, no_win);
     else return hipErrorInvalidValue;
   } else if (d_c == 512 && d_r == 64) CSA2_ATTN(sparse_attn_kernel, 256, 512, 64);
   else if (d_c == 512 && d_r == 0) CSA2_ATTN(sparse_attn_kernel, 256, 512, 0);
@@ -919,6 +1065,55 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
   const int64_t cblocks = spread ? (int64_t)B * H : ((int64_t)B + 7) / 8 * 8 * H;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)cblocks), dim3(128), 0, stream, ws_o, ws_ml, B, H,
                      s, d_c, spread, out, lse);
+  return hipGetLastError();
+}
+
+// The sparse attention and the query's sliding window as one softmax over the
+// union of their keys ([P4] CSA2 paragraph: the SWA branch beside the sparse
+// one).  The 32-head kernel takes the window rows as its first tiles; batches
+// it does not serve run the sparse kernels and then the window kernel, which
+// merges into their (out, lse).
+bool sparse_swa_fused(int B, int H, int d_c) { return attn_heads_per_wg(B, H, d_c) == 32; }
+
+size_t sparse_swa_workspace_bytes(int B, int H, int d_c, int K) {
+  const size_t a = (attn_workspace_bytes(B, H, d_c, K) + 15) & ~(size_t)15;
+  return sparse_swa_fused(B, H, d_c) ? a : a + (size_t)B * H * sizeof(float);
+}
+
+hipError_t launch_sparse_swa_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
+                                  int d_r, int64_t N_cap, WinRef win, float sm_scale, float* out, float* lse,
+                                  void* workspace, hipStream_t stream) {
+  constexpr int d_c = 512;
+  if (B == 0) return hipSuccess;
+  if (!sparse_swa_fused(B, H, d_c)) {
+    const size_t a = (attn_workspace_bytes(B, H, d_c, K) + 15) & ~(size_t)15;
+    float* l = lse ? lse : reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + a);
+    hipError_t e = launch_sparse_attn(q, cache, idx, K, B, H, d_c, d_r, N_cap, 1, sm_scale, out, l, workspace, stream);
+    if (e != hipSuccess) return e;
+    return launch_swa_attn(q, win.codes, win.codes_stride, win.sigma, win.rope, win.rope_stride, win.n_win, B, H,
+                           d_r, win.W_cap, sm_scale, out, l, out, lse, stream);
+  }
+  int s, ps;
+  attn_plan(B, H, K, d_c, &s, &ps);
+  const int n_hg = (H + 31) / 32;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = s > 1 ? ws_o + (size_t)B * H * s * d_c : nullptr;
+  const int spread = B < 8 ? 1 : 0;
+  const int64_t groups = spread ? ((int64_t)B * s + 7) / 8 : ((int64_t)B + 7) / 8 * s;
+  const dim3 grid((unsigned)(groups * 8 * n_hg));
+  const float sl = sm_scale * LOG2E;
+  if (d_r == 64)
+    hipLaunchKernelGGL((sparse_attn_role_kernel<64>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, 1,
+                       sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, win);
+  else if (d_r == 0)
+    hipLaunchKernelGGL((sparse_attn_role_kernel<0>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, 1,
+                       sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, win);
+  else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || s == 1) return e;
+  const int64_t cblocks = spread ? (int64_t)B * H : ((int64_t)B + 7) / 8 * 8 * H;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)cblocks), dim3(128), 0, stream, ws_o, ws_ml, B, H, s, d_c,
+                     spread, out, lse);
   return hipGetLastError();
 }
 

@@ -339,6 +339,55 @@ int csa2_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_
                              d_c, d_r, N_cap, sm_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+size_t csa2_sparse_swa_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t K) {
+  if (B <= 0 || H < 1 || H > 128 || d_c != 512 || K < 1) return 0;
+  return csa2::sparse_swa_workspace_bytes(B, H, d_c, K);
+}
+
+int csa2_sparse_swa_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride, const uint8_t* scales,
+                             int64_t scales_stride, const uint16_t* rope, int64_t rope_stride, const int32_t* idx,
+                             int32_t K, int32_t B, int32_t H, int32_t d_c, int32_t d_r, int64_t N_cap,
+                             const uint8_t* w_codes, int64_t w_codes_stride, const float* w_sigma,
+                             const uint16_t* w_rope, int64_t w_rope_stride, const int32_t* n_win, int32_t W_cap,
+                             float sm_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                             csa2_stream_t stream) {
+  if (B < 0 || K < 1 || N_cap < 0 || codes_stride < 0 || scales_stride < 0 || rope_stride < 0 || W_cap < 0 ||
+      w_codes_stride < 0 || w_rope_stride < 0)
+    return CSA2_ERR_SHAPE;
+  if (d_c != 512 || !(d_r == 0 || d_r == 64) || H < 1 || H > 128) return CSA2_ERR_UNSUPPORTED;
+  if (W_cap > 256) return CSA2_ERR_RANGE;
+  if (B == 0) return CSA2_OK;
+  if (!q || !codes || !scales || !idx || !out || (d_r > 0 && !rope) ||
+      (W_cap > 0 && (!w_codes || !w_sigma || (d_r > 0 && !w_rope))))
+    return CSA2_ERR_NULL;
+  if (w_codes_stride == 0) w_codes_stride = d_c;
+  if (w_rope_stride == 0) w_rope_stride = 2 * (int64_t)d_r;
+  if (w_codes_stride < d_c || (d_r > 0 && w_rope_stride < 2 * (int64_t)d_r)) return CSA2_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(idx) || !aligned16(out) || !opt_aligned16(lse) || !opt_aligned16(n_win) ||
+      (W_cap > 0 && (!aligned16(w_codes) || w_codes_stride % 16 != 0 ||
+                     (reinterpret_cast<uintptr_t>(w_sigma) & 3u) != 0 ||
+                     (d_r > 0 && (!aligned16(w_rope) || w_rope_stride % 16 != 0)))))
+    return CSA2_ERR_ALIGN;
+  const int st = check_cache(d_c, d_r, codes, codes_stride, scales, scales_stride, rope, rope_stride);
+  if (st != CSA2_OK) return st;
+  // the kernels address a row inside its sequence with 32-bit offsets
+  const int64_t lim = (int64_t)1 << 32;
+  if (N_cap > 0 && (N_cap > lim / codes_stride || N_cap > lim / scales_stride ||
+                    (d_r > 0 && N_cap > lim / rope_stride)))
+    return CSA2_ERR_RANGE;
+  if (too_large(csa2::attn_launch_items(B, H, d_c, K)) || too_large(csa2::swa_launch_items(B, H)))
+    return CSA2_ERR_RANGE;
+  const size_t need = csa2::sparse_swa_workspace_bytes(B, H, d_c, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;
+  const csa2::CacheRef c{const_cast<uint8_t*>(codes), codes_stride, const_cast<uint8_t*>(scales), scales_stride,
+                         d_r > 0 ? const_cast<uint16_t*>(rope) : nullptr, rope_stride};
+  const csa2::WinRef wr{W_cap > 0 ? w_codes : nullptr, w_codes_stride, w_sigma, d_r > 0 ? w_rope : nullptr,
+                        w_rope_stride, n_win, W_cap};
+  return hip_status(csa2::launch_sparse_swa_attn(q, c, idx, K, B, H, d_r, N_cap, wr, sm_scale, out, lse, workspace,
+                                                 as_stream(stream)));
+}
+
 int csa2_prefill_sparse_attn_fp4(const uint16_t* q, const uint8_t* codes, int64_t codes_stride,
                                  const uint8_t* scales, int64_t scales_stride, const uint16_t* rope,
                                  int64_t rope_stride, const int32_t* idx, int32_t K, int32_t S, int32_t T,

@@ -32,6 +32,20 @@ struct CacheRef {
   int64_t rope_stride;
 };
 
+// The FP8 sliding window of each query for the attention kernels (codes null:
+// no window): rows j < n_win[b] (clamped to [0, W_cap]; n_win null = W_cap)
+// of query b are rows b * W_cap + j of codes / sigma / rope, as written by
+// csa2_quantize_fp8.
+struct WinRef {
+  const uint8_t* codes;
+  int64_t codes_stride;
+  const float* sigma;
+  const uint16_t* rope;
+  int64_t rope_stride;
+  const int32_t* n_win;
+  int W_cap;
+};
+
 hipError_t launch_quantize_fp4(const uint16_t* x, int64_t n_rows, int d_c, const uint16_t* rope_src,
                                int d_r, CacheRef cache, int64_t dst_row0, hipStream_t stream);
 
@@ -92,5 +106,15 @@ size_t attn_workspace_bytes(int B, int H, int d_c, int K);
 hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
                               int d_c, int d_r, int64_t N_cap, int qps, float sm_scale, float* out, float* lse,
                               void* workspace, hipStream_t stream);
+// The sparse attention and the sliding window of each query in one softmax:
+// inside the 32-head kernel when it serves the batch (window tiles first),
+// else the sparse kernels, then the window kernel merging into their result
+// (lse_tmp: B x H floats for that merge when lse is null).  Decode only (one
+// query per sequence), d_c = 512.
+bool sparse_swa_fused(int B, int H, int d_c);
+size_t sparse_swa_workspace_bytes(int B, int H, int d_c, int K);
+hipError_t launch_sparse_swa_attn(const uint16_t* q, CacheRef cache, const int32_t* idx, int K, int B, int H,
+                                  int d_r, int64_t N_cap, WinRef win, float sm_scale, float* out, float* lse,
+                                  void* workspace, hipStream_t stream);
 
 }  // namespace csa2

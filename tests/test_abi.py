@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
 
@@ -117,6 +117,33 @@ def test_index_topk_validation(lib):
     assert call(out=U) == ALIGN and call(w=U) == ALIGN and call(nv=U) == ALIGN and call(score=U) == ALIGN
     assert call(ws=N) == WS and call(wsn=need - 1) == WS
     assert call(ws=U) == ALIGN
+
+
+def test_sparse_swa_validation(lib):
+    f = lib.csa2_sparse_swa_attn_fp4
+    wsb = lib.csa2_sparse_swa_attn_workspace_bytes
+    # 32-head kernel (B * ceil(H / 32) >= 256): only its split workspace; smaller
+    # batches: the sparse kernels' workspace, then B x H floats of lse for the merge
+    assert wsb(128, 64, 512, 512) == lib.csa2_sparse_attn_workspace_bytes(128, 64, 512, 512) == 0
+    s8 = lib.csa2_sparse_attn_workspace_bytes(8, 64, 512, 512)
+    assert wsb(8, 64, 512, 512) == ((s8 + 15) // 16) * 16 + 8 * 64 * 4
+    assert wsb(8, 64, 128, 512) == 0 and wsb(0, 64, 512, 512) == 0
+    need = wsb(8, 64, 512, 512)
+
+    def call(q=A, codes=A, cst=0, scales=A, sst=0, rope=A, rst=0, idx=A, K=512, B=8, H=64, d_c=512, d_r=64,
+             N=1000, wc=A, wcs=0, ws=A, wr=A, wrs=0, nw=N, W=128, out=A, lse=N, wsp=A, wsn=need):
+        return f(q, codes, cst, scales, sst, rope, rst, idx, K, B, H, d_c, d_r, N, wc, wcs, ws, wr, wrs, nw, W,
+                 0.05, out, lse, wsp, wsn, N)
+    assert call(B=0) == OK
+    assert call(B=-1) == SHAPE and call(K=0) == SHAPE and call(W=-1) == SHAPE and call(wcs=-16) == SHAPE
+    assert call(d_c=128) == UNSUP and call(d_r=32) == UNSUP and call(H=129) == UNSUP
+    assert call(W=257) == RANGE
+    assert call(q=N) == NULL and call(wc=N) == NULL and call(ws=N) == NULL and call(wr=N) == NULL
+    assert call(W=0, wc=N, ws=N, wr=N, K=0) == SHAPE          # no window: its buffers may be NULL
+    assert call(wcs=256) == SHAPE                             # window stride narrower than a row
+    assert call(wc=U) == ALIGN and call(wcs=520) == ALIGN and call(ws=ctypes.c_void_p(0x1002)) == ALIGN
+    assert call(wr=U) == ALIGN and call(nw=U) == ALIGN and call(lse=U) == ALIGN
+    assert call(wsp=N) == WS and call(wsn=need - 1) == WS
 
 
 def test_build_pool_validation(lib):
