@@ -432,7 +432,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 // tile t - 1 is multiplied, from two buffers, so one barrier per tile
 // separates the roles and the two kinds of work of a SIMD (one wave of each
 // role) overlap.
-template <int DR>
+// WIN: the query's sliding window is attended as well (its own
+// instantiation, so that the registers of the window tiles do not weigh on
+// the selected-entry pipeline of the plain kernel).
+template <int DR, bool WIN>
 __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
     const int32_t* __restrict__ idx, int K, int B, int H, int64_t N_cap, int qps, float sm_scale_log2e, int n_hp,
@@ -485,9 +488,9 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   // and enters the value products as P * sigma_j / sigma_max, the
   // accumulator being divided by sigma_max before the first window tile and
   // multiplied by it in the epilogue (powers of two: exact)
-  const int nw = (win.codes && split == 0) ? (win.n_win ? min(max(win.n_win[b], 0), win.W_cap) : win.W_cap) : 0;
+  const int nw = (WIN && win.codes && split == 0) ? (win.n_win ? min(max(win.n_win[b], 0), win.W_cap) : win.W_cap) : 0;
   const int n_wt = (nw + AT_TILE - 1) / AT_TILE;
-  {
+  if constexpr (WIN) {
     float sg = 0.f;
     if (tid < nw) sg = win.sigma[b * win.W_cap + tid];  // nw <= 256 < 512 threads
 #pragma unroll
@@ -532,8 +535,10 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   const int n_iter = n_tiles > 0 ? (n_tiles + 2) & ~1 : 0;
   const int n_iter_w = n_wt > 0 ? (n_wt + 2) & ~1 : 0;
   float sig_max = 0.f;
+  if constexpr (WIN) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) sig_max = fmaxf(sig_max, sWm[i]);
+    for (int i = 0; i < 8; ++i) sig_max = fmaxf(sig_max, sWm[i]);
+  }
   const float inv_sig_max = sig_max > 0.f ? 1.0f / sig_max : 0.f;
   // converted query: 16-byte piece (k, t, lane) = head group k, k-step t of
   // score-wave lane (n, g), in the second value buffer (first written by tile 1)
@@ -1048,11 +1053,11 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
   const WinRef no_win{nullptr, 0, nullptr, nullptr, 0, nullptr, 0};
   if (hpw == 32) {
     if (d_r == 64)
-      hipLaunchKernelGGL((sparse_attn_role_kernel<64>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, qps,
-                         sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, no_win);
+      hipLaunchKernelGGL((sparse_attn_role_kernel<64, false>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,
+                         qps, sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, no_win);
     else if (d_r == 0)
-      hipLaunchKernelGGL((sparse_attn_role_kernel<0>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, qps,
-                         sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, no_win);
+      hipLaunchKernelGGL((sparse_attn_role_kernel<0, false>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,
+                         qps, sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, no_win);
     else return hipErrorInvalidValue;
   } else if (d_c == 512 && d_r == 64) CSA2_ATTN(sparse_attn_kernel, 256, 512, 64);
   else if (d_c == 512 && d_r == 0) CSA2_ATTN(sparse_attn_kernel, 256, 512, 0);
@@ -1103,11 +1108,11 @@ hipError_t launch_sparse_swa_attn(const uint16_t* q, CacheRef cache, const int32
   const dim3 grid((unsigned)(groups * 8 * n_hg));
   const float sl = sm_scale * LOG2E;
   if (d_r == 64)
-    hipLaunchKernelGGL((sparse_attn_role_kernel<64>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, 1,
-                       sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, win);
+    hipLaunchKernelGGL((sparse_attn_role_kernel<64, true>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,
+                       1, sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, win);
   else if (d_r == 0)
-    hipLaunchKernelGGL((sparse_attn_role_kernel<0>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap, 1,
-                       sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, win);
+    hipLaunchKernelGGL((sparse_attn_role_kernel<0, true>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,
+                       1, sl, n_hg, s, ps, spread, out, lse, ws_o, ws_ml, win);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
