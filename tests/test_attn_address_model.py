@@ -6,7 +6,8 @@ kernels (16 heads per workgroup; 32 heads with score and value waves) and of
 the split combine, and checks each offset against the extent of the buffer it
 addresses: the queries, the index lists, the cache rows (codes, scales, RoPE
 part; 32-bit row offsets inside one sequence), the outputs, the LSE and the
-workspace.  It also checks that every (query, slice, head group) unit is owned
+workspace, and the window rows and row scales of the 32-head kernel's window
+variant.  It also checks that every (query, slice, head group) unit is owned
 by exactly one workgroup and every output element written exactly once.
 
 The model's slice count is pinned to the library's own plan through
@@ -248,3 +249,50 @@ def test_prefill_queries_per_sequence(lib):
         for K in (1, 512, 700):
             _, _, _, _, ws = check(S * T, 64, K, 512, 64, qps=T)
             _pin_plan(lib, S * T, 64, K, 512, ws)
+
+
+def check_window(B, H, K, W_cap, d_r, n_win):
+    """The window reads of the 32-head kernel's window variant: only slice 0
+    of a query reads them; row scales sigma[b * W_cap + j] for j < nw; tile t,
+    wave w, lane (n, g) reads row 64 t + 16 w + n (row 0 when that is past
+    nw) at bytes 32 g + 128 i + {0, 16} (16 each, i < 4) of its 512-byte code
+    row, and bytes 32 g + 16 t' (t' < d_r / 32) of its RoPE row, and its scale."""
+    hpw, n_hg, s, ps, active, b, split, hg = grid_units(B, H, K, 512)
+    assert hpw == 32
+    code_end = max(32 * g + 128 * i + o + 16 for g in range(4) for i in range(4) for o in (0, 16))
+    rope_end = max(32 * g + 16 * t + 16 for g in range(4) for t in range(d_r // 32)) if d_r else 0
+    assert code_end <= 512 and rope_end <= 2 * d_r, "window lane reads past its row"
+    nw = np.where(split == 0, np.minimum(np.maximum(n_win[b], 0), W_cap), 0)
+    assert (nw <= W_cap).all()
+    # row scales read by threads tid < nw (512 threads per workgroup)
+    assert (nw <= 512).all()
+    last_sig = b * W_cap + nw - 1
+    assert (last_sig[nw > 0] < B * W_cap).all(), "row scale past the window"
+    n_wt = -(-nw // TILE)
+    rows = np.arange(4 * TILE).reshape(4, TILE)          # tile t: rows 64 t .. 64 t + 63
+    for u in np.nonzero(n_wt > 0)[0]:
+        r = rows[:n_wt[u]].ravel()
+        rr = b[u] * W_cap + np.where(r < nw[u], r, 0)
+        assert rr.min() >= 0 and rr.max() < B * W_cap, "window row out of bounds"
+    return n_wt
+
+
+@pytest.mark.parametrize("d_r", [64, 0])
+def test_window_variant_reads(lib, d_r):
+    """Every batch the 32-head kernel serves at 64 heads (and a partial head
+    group), windows of 0 .. 256 rows and n_win past W_cap or negative; the
+    workspace of the one-call entry is pinned to the library's."""
+    rng = np.random.default_rng(d_r)
+    for B, H in ((128, 64), (129, 64), (256, 64), (200, 40), (300, 128)):
+        for K in (1, 512, 1000):
+            for W_cap in (1, 64, 65, 128, 256):
+                n_win = rng.integers(-3, W_cap + 4, size=B)
+                n_win[0] = W_cap
+                check_window(B, H, K, W_cap, d_r, n_win)
+                _, _, _, _, ws = check(B, H, K, 512, d_r)
+                assert lib.csa2_sparse_swa_attn_workspace_bytes(B, H, 512, K) == ws
+    # batches the 32-head kernel does not serve: the sparse kernels' workspace,
+    # then B x H floats of LSE for the merge
+    for B, H in ((1, 64), (8, 64), (127, 64), (200, 16)):
+        _, _, _, _, ws = check(B, H, 512, 512, d_r)
+        assert lib.csa2_sparse_swa_attn_workspace_bytes(B, H, 512, 512) == -(-ws // 16) * 16 + B * H * 4
