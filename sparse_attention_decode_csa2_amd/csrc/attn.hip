@@ -644,11 +644,20 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     };
     // exact E4M3 -> fp16 into the value tile and the score products (latent
     // and RoPE in separate accumulators: the row scale multiplies the latent
-    // part only); the value waves get sigma_j / max sigma for the entry
-    auto wprocess = [&](WinRegs& wr, int buf) {
+    // part only); the value waves get sigma_j / max sigma for the entry.  Each
+    // register of wr is refilled with the same piece of window tile `next`
+    // (none when next < 0) right after its last use, so the next tile's rows
+    // are in flight while this one is scored, with no second buffer.
+    auto wprocess = [&](WinRegs& wr, int buf, int next) {
       __builtin_amdgcn_sched_barrier(0);
       _Float16 (*tk)[LDK] = sV[buf];
       const int e = 16 * w + n;
+      const bool valid = wr.valid;
+      const float sig = wr.sig;
+      const int nrow = next * AT_TILE + 16 * w + n;
+      const bool nvalid = next >= 0 && nrow < nw;
+      const int64_t nrr = b * win.W_cap + (nvalid ? nrow : 0);
+      const uint8_t* ncrow = win.codes + nrr * win.codes_stride + 32 * g;
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
       f32x4 r0 = {0.f, 0.f, 0.f, 0.f}, r1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -662,10 +671,12 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
           const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
           const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
           f16x8 a = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-          if (!wr.valid) a = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          if (!valid) a = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
           *reinterpret_cast<f16x8*>(&tk[e][tile_col(e, 4 * i + g, j)]) = a;
           c0 = mfma16x16x32_f16(a, Bq[0][4 * i + j], c0);
           c1 = mfma16x16x32_f16(a, Bq[1][4 * i + j], c1);
+          if ((j & 1) && next >= 0)
+            wr.cw[2 * i + (j >> 1)] = *reinterpret_cast<const u32x4*>(ncrow + 128 * i + 16 * (j >> 1));
         }
       }
 #pragma unroll
@@ -673,13 +684,16 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
         const bf16x8 rv = __builtin_bit_cast(bf16x8, wr.rw[t]);
         r0 = mfma16x16x32_bf16(rv, Br[0][t], r0);
         r1 = mfma16x16x32_bf16(rv, Br[1][t], r1);
+        if (next >= 0)
+          wr.rw[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(win.rope) +
+                                                     nrr * win.rope_stride + 32 * g + 16 * t);
       }
       // c_k[i], r_k[i]: entry 16 w + 4 g + i, head hq0 + 16 k + n; its row
       // scale is held by lane 4 g + i
       float sg[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sg[i] = __shfl(wr.sig, 4 * g + i);
-      const uint64_t vb = __ballot(g == 0 && wr.valid);
+      for (int i = 0; i < 4; ++i) sg[i] = __shfl(sig, 4 * g + i);
+      const uint64_t vb = __ballot(g == 0 && valid);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const f32x4 c = k ? c1 : c0, rp = k ? r1 : r0;
@@ -689,7 +703,11 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
           sv[i] = ((vb >> (4 * g + i)) & 1u) ? (c[i] * sg[i] + rp[i]) * fscale[k] : -INFINITY;
         *reinterpret_cast<f32x4*>(&sS[buf][16 * k + n][16 * w + 4 * g]) = sv;
       }
-      if (g == 0) sFw[buf][e] = wr.sig * inv_sig_max;
+      if (g == 0) sFw[buf][e] = sig * inv_sig_max;
+      if (next >= 0) {
+        wr.sig = win.sigma[nrr];
+        wr.valid = nvalid;
+      }
     };
 
     GR ga, gb;
@@ -724,19 +742,17 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
       // has ended and they have been handed to another wave
       __builtin_amdgcn_s_waitcnt(0);
     }
-    // window tiles: gathered and scored one at a time
-    for (int i = 0; i < n_iter_w; i += 2) {
+    // window tiles: the first gathered here, each later one while the tile
+    // before it is scored
+    if (n_wt > 0) {
       WinRegs wr;
-      if (i < n_wt) {
-        wgather(wr, i);
-        wprocess(wr, 0);
+      wgather(wr, 0);
+      for (int i = 0; i < n_iter_w; i += 2) {
+        if (i < n_wt) wprocess(wr, 0, i + 1 < n_wt ? i + 1 : -1);
+        __syncthreads();
+        if (i + 1 < n_wt) wprocess(wr, 1, i + 2 < n_wt ? i + 2 : -1);
+        __syncthreads();
       }
-      __syncthreads();
-      if (i + 1 < n_wt) {
-        wgather(wr, i + 1);
-        wprocess(wr, 1);
-      }
-      __syncthreads();
     }
     return;
   }
