@@ -329,12 +329,13 @@ int csa2_quantize_fp8(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint
  * is the sparse attention alone.  out f32 [B, H, 512], lse f32 [B, H]
  * (nullable).
  * When the batch fills the GPU with 32-head workgroups (B * ceil(H / 32) >=
- * 256) one kernel attends to the window rows as its first tiles: exact E4M3
- * values in fp16, the row scale applied to the fp32 latent scores and, as
- * sigma_j / max sigma, to the probabilities of the value products, the
- * accumulator taking max sigma before the first selected entry.  Other
- * batches run the sparse kernels, then the window kernel merging into their
- * result.  The error is < 2e-3 of max|out| per (b, h) row.
+ * 256) one kernel attends to the window rows as more tiles after the
+ * selected entries': exact E4M3 values in fp16, the row scale applied to the
+ * fp32 latent scores and, as sigma_j / max sigma, to the probabilities of
+ * the value products (the accumulator divided by max sigma before the first
+ * window tile and multiplied by it at the end).  Other batches run the
+ * sparse kernels, then the window kernel merging into their result.  The
+ * error is < 2e-3 of max|out| per (b, h) row.
  * Requires d_c == 512, d_r in {0, 64}, 1 <= H <= 128, K >= 1, 0 <= W_cap <=
  * 256, the alignment rules of both calls, and a workspace of at least
  * csa2_sparse_swa_attn_workspace_bytes(B, H, d_c, K) bytes (16-byte aligned,

@@ -432,9 +432,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 // tile t - 1 is multiplied, from two buffers, so one barrier per tile
 // separates the roles and the two kinds of work of a SIMD (one wave of each
 // role) overlap.
-// WIN: the query's sliding window is attended as well (its own
+// WIN: the query's sliding window is attended as well, as more tiles of the
+// same online softmax after the selected entries' tiles ([P4] CSA2
+// paragraph: the SWA branch beside the sparse one, its KV in FP8); its own
 // instantiation, so that the registers of the window tiles do not weigh on
-// the selected-entry pipeline of the plain kernel).
+// the selected-entry pipeline of the plain kernel.
 template <int DR, bool WIN>
 __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     const uint16_t* __restrict__ q, const CacheRef cache,
