@@ -172,8 +172,23 @@ int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
  * -0.0 ranks equal to +0.0 and is reported as +0.0; NaN ranks below every
  * other score and is reported as a quiet NaN.  Ids must be >= 0 (other than
  * -1); equal (score, id) pairs are interchangeable.  Bit-exact.
+ * Rows of up to 16384 columns are selected by one workgroup each.  Longer
+ * rows take one of two routes with the same result:
+ *   chunked reduction: each 16384-column chunk keeps its K best keys, and the
+ *     winners are reduced again until one chunk remains (the workspace holds
+ *     the levels' winners: B * ch_l * K * 8 bytes for each level l but the
+ *     last, ch_0 = ceil(M / 16384), ch_l+1 = ceil(ch_l * K / 16384));
+ *   threshold filter, for K >= 1024 on rows of at most 2^20 columns whose
+ *     first level would take more than 768 chunks in all (B * ch_0 > 768) or
+ *     whose reduction takes more than two levels: a 16384-column sample of each
+ *     row gives a score threshold, one pass keeps the candidates at or above
+ *     it, and one workgroup per row selects among them (the workspace holds
+ *     128 bytes and 16384 keys of 8 bytes per row).  A row whose kept
+ *     candidates cannot hold its Top-K (too many, or fewer than K above a
+ *     non-zero threshold) is reduced by its workgroup over the whole row.
  * Requires 1 <= K <= 2048, 1 <= M < 2^31, B >= 0, and a workspace of at
- * least csa2_topk_workspace_bytes(B, M, K) bytes (may be 0 / NULL then).
+ * least csa2_topk_workspace_bytes(B, M, K) bytes (may be 0 / NULL then),
+ * 16-byte aligned, caller-owned, contents not preserved.
  */
 size_t csa2_topk_workspace_bytes(int32_t B, int64_t M, int32_t K);
 int csa2_topk(const float* scores, const int32_t* ids, const int32_t* n_valid,
@@ -208,13 +223,14 @@ int csa2_index_topk_full(const uint16_t* q_idx, const float* w, const uint16_t* 
  * csa2_topk without a workspace, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments (less the workspace), same results, bit
- * for bit, as csa2_topk.  The chunk winners go to one static device array of
- * the library (32 MiB, held by each GPU the library runs on until the process
- * ends; its device address is looked up once per device).  This call
- * allocates nothing.  Calls on one GPU share that array: calls that overlap
- * on one GPU (two streams, two host threads) race, and must be ordered by the
- * caller.  Requires csa2_topk_workspace_bytes(B, M, K) <= 32 MiB (e.g. up to
- * 2048 rows x chunks of 16384 candidates at K = 512); CSA2_ERR_RANGE beyond.
+ * for bit, as csa2_topk.  It always takes csa2_topk's chunked reduction,
+ * whose level winners go to one static device array of the library (32 MiB,
+ * held by each GPU the library runs on until the process ends; its device
+ * address is looked up once per device).  This call allocates nothing.  Calls
+ * on one GPU share that array: calls that overlap on one GPU (two streams,
+ * two host threads) race, and must be ordered by the caller.  Requires the
+ * chunked reduction's level buffers (see csa2_topk) to fit in 32 MiB (e.g.
+ * 8192 chunks of 16384 candidates in all at K = 512); CSA2_ERR_RANGE beyond.
  * CSA2_ERR_HIP when the array's device address cannot be looked up.
  */
 int csa2_topk_noalloc(const float* scores, const int32_t* ids, const int32_t* n_valid,

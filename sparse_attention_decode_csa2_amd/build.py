@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
 SOURCES = ["csa2_api.hip", "quantize.hip", "index.hip", "topk.hip", "pool.hip", "sample.hip", "attn.hip",
-           "scratch.hip", "index_topk.hip"]
+           "scratch.hip", "index_topk.hip", "topk_filter.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -233,12 +233,13 @@ int csa2_topk_noalloc(const float* scores, const int32_t* ids, const int32_t* n_
   if (!aligned16(scores) || !aligned16(out_idx) || !opt_aligned16(ids) || !opt_aligned16(n_valid) ||
       !opt_aligned16(out_score))
     return CSA2_ERR_ALIGN;
-  const size_t need = csa2::topk_workspace_bytes(B, M, K);
+  const size_t need = csa2::topk_chunk_workspace_bytes(B, M, K);
   if (need > csa2::kStaticScratchBytes) return CSA2_ERR_RANGE;
-  if (too_large(csa2::topk_launch_items(B, M, K))) return CSA2_ERR_RANGE;
+  if (too_large(csa2::topk_chunk_launch_items(B, M, K))) return CSA2_ERR_RANGE;
   void* ws = nullptr;
   if (need > 0 && csa2::static_scratch(&ws) != hipSuccess) return CSA2_ERR_HIP;
-  return hip_status(csa2::launch_topk(scores, ids, n_valid, B, M, K, out_idx, out_score, ws, as_stream(stream)));
+  return hip_status(
+      csa2::launch_topk_chunked(scores, ids, n_valid, B, M, K, out_idx, out_score, ws, as_stream(stream)));
 }
 
 static bool sampler_params_ok(float temperature, float top_p) {

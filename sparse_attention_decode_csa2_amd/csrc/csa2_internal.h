@@ -59,10 +59,25 @@ hipError_t launch_index(const uint16_t* q, const float* w, const uint16_t* k, co
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 hipError_t static_scratch(void** ptr);
 
+// Top-K of B rows of M scores: the threshold filter for long rows (more than
+// one round of chunk workgroups or more than two chunk levels), else the
+// chunked reduction.  topk_chunk_* always take the chunked reduction.
 size_t topk_workspace_bytes(int B, int64_t M, int K);
 hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, int B,
                        int64_t M, int K, int32_t* out_idx, float* out_score, void* workspace,
                        hipStream_t stream);
+int64_t topk_chunk_launch_items(int B, int64_t M, int K);
+size_t topk_chunk_workspace_bytes(int B, int64_t M, int K);
+hipError_t launch_topk_chunked(const float* scores, const int32_t* ids, const int32_t* n_valid, int B,
+                               int64_t M, int K, int32_t* out_idx, float* out_score, void* workspace,
+                               hipStream_t stream);
+// The threshold filter's limits (rows of 16384 < M <= 2^20, K <= 2048), sizes
+// and launches.
+bool topk_filter_fits(int B, int64_t M, int K);
+int64_t topk_filter_launch_items(int B, int64_t M);
+size_t topk_filter_workspace_bytes(int B);
+hipError_t launch_topk_filtered(const float* scores, const int32_t* ids, const int32_t* n_valid, int B, int64_t M,
+                                int K, int32_t* out_idx, float* out_score, void* workspace, hipStream_t stream);
 // The Top-K levels after the first, on B rows of m chunk-winner keys.
 size_t topk_keys_workspace_bytes(int B, int64_t m, int K);
 hipError_t launch_topk_from_keys(const uint64_t* keys, int B, int64_t m, int K, int32_t* out_idx,

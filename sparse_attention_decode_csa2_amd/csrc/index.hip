@@ -86,8 +86,10 @@ __global__ __launch_bounds__(256) void index_kernel(
   u32x4 Bv[TPW][KS];
   int64_t pos[TPW];
   bool ok[TPW];
+  uint32_t vmask[TPW];  // bit s: load s of tile t holds a key
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
+    vmask[t] = 0u;
     ok[t] = locate((tile0 + t) * 16 + n, &pos[t]);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -110,13 +112,17 @@ __global__ __launch_bounds__(256) void index_kernel(
         valid = locate((tile0 + t) * 16 + w / KW, &p);
         kp = k + (b * N_cap + (valid ? p : 0)) * D_I + 8 * (w % KW);
       }
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
-      Bv[t][s] = v;
+      // unconditional (an empty slot reads key 0 of the row, zeroed where
+      // it is used), so that every load is in flight before the first is used
+      Bv[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
+      vmask[t] |= (uint32_t)valid << s;
     }
   }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      if (!((vmask[t] >> s) & 1u)) Bv[t][s] = u32x4{0u, 0u, 0u, 0u};
     u32x4 Bt[KS];
     if (POOL && !contig) {
 #pragma unroll
@@ -173,27 +179,35 @@ __global__ __launch_bounds__(256) void index_pool8_kernel(
   __shared__ u32x4 kbuf[4][16 * (KW + 1)];
   u32x4* kb = kbuf[wave];
   const uint16_t* krow = k + b * N_cap * D_I;
-  // load s of the wave's tile t: keys KPL s .. of the tile, in block 2 t + KPL s / 8
-  auto load = [&](int t, u32x4 (&Bv)[KS]) {
+  // load s of the wave's tile t: keys KPL s .. of the tile, in block 2 t + KPL
+  // s / 8.  Unconditional (an empty slot reads key 0 of the row; bit s of vm
+  // clear, zeroed where it is used), so that the next tile's loads stay in
+  // flight while a tile is scored.
+  auto load = [&](int t, u32x4 (&Bv)[KS], uint32_t& vm) {
+    vm = 0u;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int c = KPL * s;
       const int64_t blk = __builtin_amdgcn_readlane(blk_l, 2 * t + c / 8);
       const int64_t p = blk * 8 + c % 8 + lane / KW;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (blk >= 0 && p < nv)
-        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + p * D_I + 8 * (lane % KW)));
-      Bv[s] = v;
+      const bool valid = blk >= 0 && p < nv;
+      Bv[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + (valid ? p : 0) * D_I + 8 * (lane % KW)));
+      vm |= (uint32_t)valid << s;
     }
   };
   u32x4 cur[KS];
-  load(0, cur);
+  uint32_t cur_m;
+  load(0, cur, cur_m);
   for (int t = 0; t < POOL_TW; ++t) {
     const int64_t tile = tile0 + t;
     if (tile * 16 >= M) break;
     const bool more = t + 1 < POOL_TW && (tile + 1) * 16 < M;
     u32x4 nxt[KS];
-    if (more) load(t + 1, nxt);
+    uint32_t nxt_m = 0u;
+    if (more) load(t + 1, nxt, nxt_m);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      if (!((cur_m >> s) & 1u)) cur[s] = u32x4{0u, 0u, 0u, 0u};
     u32x4 Bt[KS];
     index_reorder<KS>(cur, kb, lane, Bt);
     const float part = index_tile_score<KS>(A, wv, Bt);
@@ -209,6 +223,7 @@ __global__ __launch_bounds__(256) void index_pool8_kernel(
     if (more) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) cur[s] = nxt[s];
+      cur_m = nxt_m;
     }
   }
 }

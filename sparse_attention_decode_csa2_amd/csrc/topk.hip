@@ -33,43 +33,44 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
     ids_are_columns = ids == nullptr;
     const float* srow = scores + b * M;
     const int32_t* irow = ids ? ids + b * M : nullptr;
+    // every load is issued before any result is used: a load under a
+    // per-element branch would wait for the one before it
+    float x[TK_E];
+    uint32_t ii[TK_E];
     if (col0 + TK_E <= limit && (M & 3) == 0) {
       // a whole run of columns: 16-byte loads (rows stay 16-byte aligned)
+      f32x4 v4[TK_E / 4];
+      u32x4 i4[TK_E / 4];
 #pragma unroll
-      for (int q4 = 0; q4 < TK_E / 4; ++q4) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>(srow + col0 + 4 * q4);
-        u32x4 i4;
-        if (irow) i4 = *reinterpret_cast<const u32x4*>(irow + col0 + 4 * q4);
+      for (int q = 0; q < TK_E / 4; ++q) v4[q] = *reinterpret_cast<const f32x4*>(srow + col0 + 4 * q);
+      if (irow) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * q4 + j;
-          if (irow) {
-            const bool ok = i4[j] != 0xFFFFFFFFu;
-            idv[e] = i4[j];
-            v[e] = ok ? v4[j] : qnan;
-            valid |= (lanemask)ok << e;
-          } else {
-            idv[e] = (uint32_t)(col0 + e);
-            v[e] = v4[j];
-          }
-        }
+        for (int q = 0; q < TK_E / 4; ++q) i4[q] = *reinterpret_cast<const u32x4*>(irow + col0 + 4 * q);
       }
-      if (!irow) valid = (lanemask(1) << TK_E) - 1u;
-    } else {
 #pragma unroll
       for (int e = 0; e < TK_E; ++e) {
-        const int64_t col = col0 + e;
-        uint32_t i = 0xFFFFFFFFu;
-        float x = qnan;
-        if (col < limit) {
-          i = irow ? (uint32_t)irow[col] : (uint32_t)col;
-          if (i != 0xFFFFFFFFu) x = srow[col];
-        }
-        const bool ok = i != 0xFFFFFFFFu;
-        idv[e] = i;
-        v[e] = ok ? x : qnan;
-        valid |= (lanemask)ok << e;
+        x[e] = v4[e / 4][e % 4];
+        ii[e] = irow ? i4[e / 4][e % 4] : (uint32_t)(col0 + e);
       }
+    } else {
+      // columns past the end read the last column in range (column 0 of an
+      // empty row) and are then dropped
+      const int64_t last = limit > 0 ? limit - 1 : 0;
+#pragma unroll
+      for (int e = 0; e < TK_E; ++e) {
+        const int64_t cc = min<int64_t>(col0 + e, last);
+        x[e] = srow[cc];
+        ii[e] = irow ? (uint32_t)irow[cc] : (uint32_t)(col0 + e);
+      }
+#pragma unroll
+      for (int e = 0; e < TK_E; ++e) ii[e] = col0 + e < limit ? ii[e] : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int e = 0; e < TK_E; ++e) {
+      const bool ok = ii[e] != 0xFFFFFFFFu;
+      idv[e] = ii[e];
+      v[e] = ok ? x[e] : qnan;
+      valid |= (lanemask)ok << e;
     }
   } else {
     ids_are_columns = false;
@@ -84,8 +85,12 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
         k[2 * q + 1] = ((uint64_t)w[3] << 32) | w[2];
       }
     } else {
+      // keys past the end read the last key in range and are then dropped
+      const int64_t last = limit > 0 ? limit - 1 : 0;
 #pragma unroll
-      for (int e = 0; e < TK_E; ++e) k[e] = col0 + e < limit ? krow[col0 + e] : 0ull;
+      for (int e = 0; e < TK_E; ++e) k[e] = krow[min<int64_t>(col0 + e, last)];
+#pragma unroll
+      for (int e = 0; e < TK_E; ++e) k[e] = col0 + e < limit ? k[e] : 0ull;
     }
 #pragma unroll
     for (int e = 0; e < TK_E; ++e) {
@@ -136,19 +141,41 @@ static int topk_levels(int64_t M, int K, int64_t* chunks_per_level, int max_leve
   return n;
 }
 
-// The first level has the most workgroups: one per 16384-candidate chunk.
-int64_t topk_launch_items(int B, int64_t M, int K) {
+// The chunked reduction's first level has the most workgroups: one per
+// 16384-candidate chunk.
+int64_t topk_chunk_launch_items(int B, int64_t M, int K) {
   int64_t ch[16];
   topk_levels(M, K, ch, 16);
   return (int64_t)B * ch[0] * TK_T;
 }
 
-size_t topk_workspace_bytes(int B, int64_t M, int K) {
+size_t topk_chunk_workspace_bytes(int B, int64_t M, int K) {
   int64_t ch[16];
   const int n = topk_levels(M, K, ch, 16);
   size_t bytes = 0;
   for (int l = 0; l + 1 < n; ++l) bytes += (size_t)B * ch[l] * K * sizeof(uint64_t);
   return bytes;
+}
+
+// The threshold filter (topk_filter.hip) serves K >= 1024 on rows whose
+// chunked reduction takes more than three rounds of workgroups at its first
+// level (more than three chunks per CU) or more than two levels: there its
+// three launches (a sample, one streaming pass, one selection per row) beat
+// the levels, whose per-chunk selection costs grow with K.  Elsewhere the
+// levels are as fast or faster (measured on MI355X).
+static bool use_filter(int B, int64_t M, int K) {
+  if (!topk_filter_fits(B, M, K) || K < 1024) return false;
+  int64_t ch[16];
+  const int n = topk_levels(M, K, ch, 16);
+  return (int64_t)B * ch[0] > 768 || n > 2;
+}
+
+int64_t topk_launch_items(int B, int64_t M, int K) {
+  return use_filter(B, M, K) ? topk_filter_launch_items(B, M) : topk_chunk_launch_items(B, M, K);
+}
+
+size_t topk_workspace_bytes(int B, int64_t M, int K) {
+  return use_filter(B, M, K) ? topk_filter_workspace_bytes(B) : topk_chunk_workspace_bytes(B, M, K);
 }
 
 // The levels that reduce chunk winners: keys holds B rows of m keys (the
@@ -188,7 +215,7 @@ hipError_t launch_topk_from_keys(const uint64_t* keys, int B, int64_t m, int K, 
 
 // Level 0 reads the scores; the chunk winners (when the row has more than one
 // chunk) go to the workspace, followed by the later levels' buffers.
-hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, int B,
+hipError_t launch_topk_chunked(const float* scores, const int32_t* ids, const int32_t* n_valid, int B,
                        int64_t M, int K, int32_t* out_idx, float* out_score, void* workspace,
                        hipStream_t stream) {
   if (B == 0) return hipSuccess;
@@ -207,6 +234,15 @@ hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_from_keys(ws, B, ch[0] * K, K, out_idx, out_score, ws + (size_t)B * ch[0] * K, stream);
+}
+
+hipError_t launch_topk(const float* scores, const int32_t* ids, const int32_t* n_valid, int B,
+                       int64_t M, int K, int32_t* out_idx, float* out_score, void* workspace,
+                       hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  if (use_filter(B, M, K))
+    return launch_topk_filtered(scores, ids, n_valid, B, M, K, out_idx, out_score, workspace, stream);
+  return launch_topk_chunked(scores, ids, n_valid, B, M, K, out_idx, out_score, workspace, stream);
 }
 
 }  // namespace csa2

@@ -87,6 +87,15 @@ def test_topk_validation(lib):
     need = lib.csa2_topk_workspace_bytes(2, 40000, 512)
     assert need == 2 * 3 * 512 * 8
     assert lib.csa2_topk_workspace_bytes(2, 16384, 512) == 0
+    # the threshold filter (128 bytes + 16384 keys per row): K >= 1024 and
+    # more than 768 first-level chunks, or more than two levels, in rows of at
+    # most 2^20
+    assert lib.csa2_topk_workspace_bytes(128, 129280, 512) == 128 * 8 * 512 * 8
+    assert lib.csa2_topk_workspace_bytes(128, 129280, 2048) == 128 * (128 + 16384 * 8)
+    assert lib.csa2_topk_workspace_bytes(1, 300000, 2048) == 128 + 16384 * 8
+    assert lib.csa2_topk_workspace_bytes(1, 300000, 512) == 19 * 512 * 8
+    assert lib.csa2_topk_workspace_bytes(32, 32768, 2048) == 32 * 2 * 2048 * 8
+    assert lib.csa2_topk_workspace_bytes(1, 2 ** 20 + 1, 8) == 65 * 8 * 8
     assert f(A, N, N, 2, 40000, 512, A, N, N, 0, N) == WS
     assert f(A, N, N, 2, 40000, 512, A, N, A, need - 1, N) == WS
 
@@ -435,8 +444,8 @@ def test_topk_noalloc_validation(lib):
     assert f(A, N, N, 1, 100, 2049, A, A, N) == RANGE
     assert f(N, N, N, 1, 100, 8, A, A, N) == NULL
     assert f(U, N, N, 1, 100, 8, A, A, N) == ALIGN
-    # 4096 rows x 16 chunks x 512 winners x 8 bytes = 256 MiB > 32 MiB
-    assert lib.csa2_topk_workspace_bytes(4096, 262144, 512) > 32 << 20
+    # the chunked reduction: 4096 rows x 16 chunks x 512 winners x 8 bytes =
+    # 256 MiB > 32 MiB
     assert f(A, N, N, 4096, 262144, 512, A, A, N) == RANGE
 
 
