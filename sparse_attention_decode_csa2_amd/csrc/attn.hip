@@ -44,6 +44,9 @@ namespace csa2 {
 constexpr int AT_TILE = 64;
 constexpr int AT_IDS = 512;  // entry ids one workgroup handles (8 tiles)
 constexpr int AT_IDS_PAD = AT_IDS + 2 * AT_TILE;  // + two tiles of -1 for the look-ahead loads
+// Base-2 logits a running softmax reference may lag behind the maximum (the
+// 32-head kernel): exponentials stay below 2^8 in fp16, far from its range.
+constexpr float RESCALE_SLACK = 8.0f;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // D = A(32x16) * B(16x32) + C, fp32 accumulate.  Lane l supplies row (l % 32)
@@ -834,9 +837,14 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) mt = fmaxf(mt, fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])));
     mt = fmaxf(mt, xor32f(mt));
-    const float m_new = fmaxf(m_run, mt);
+    // the reference moves only when the tile's maximum passes it by more
+    // than RESCALE_SLACK (the first finite logit always moves it), so the
+    // exponentials stay below 2^RESCALE_SLACK and most tiles leave the
+    // accumulator unscaled; softmax is unchanged by the choice of reference
+    const bool move = mt > m_run + RESCALE_SLACK;
+    const float m_new = move ? mt : m_run;
     const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // nothing valid yet: O = l = 0
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.f;
     f16x8 a[4];
     float ps = 0.f;
     if (wtile) {
@@ -866,18 +874,21 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
     l_run = l_run * alpha + ps;
     m_run = m_new;
     // alpha of the heads whose output rows this lane holds: 8 q + 4 kh + 0..3
-    if (kh == 0) sHd[r][0][hl] = alpha;
-    f32x4 al[4];
+    // (skipped, wave-uniformly, when no head of the wave moved its reference)
+    if (__any(move) || (first_w && sig_max > 0.f)) {
+      if (kh == 0) sHd[r][0][hl] = alpha;
+      f32x4 al[4];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) al[qq] = *reinterpret_cast<const f32x4*>(&sHd[r][0][8 * qq + 4 * kh]);
-    if (first_w && sig_max > 0.f) {
+      for (int qq = 0; qq < 4; ++qq) al[qq] = *reinterpret_cast<const f32x4*>(&sHd[r][0][8 * qq + 4 * kh]);
+      if (first_w && sig_max > 0.f) {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) al[qq] *= inv_sig_max;
+        for (int qq = 0; qq < 4; ++qq) al[qq] *= inv_sig_max;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[k][i] *= al[i >> 2][i & 3];
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[k][i] *= al[i >> 2][i & 3];
 #pragma unroll
     for (int u = 0; u < AT_TILE / 16; ++u) {
       const int r0 = 16 * u + 8 * (G >> 1) + tr_r, r1 = r0 + 4;
