@@ -208,6 +208,8 @@ class Step:
             self.stages = ["draw_full"]
             return
         tk = csa2.csa2_topk_workspace_bytes(B, V, K)
+        # the threshold filter's workspace: a 128-byte record and 16384 keys per row
+        self.filtered_topk = V > 16384 and tk == B * (128 + 16384 * 8)
         self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
         self.stages = ["topk", "draw"]
 
@@ -590,7 +592,7 @@ def main():
     single_step_us = sorted(cold)[len(cold) // 2]
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
-    kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip", "attn": "attn.hip",
+    kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip+topk_filter.hip", "attn": "attn.hip",
                    "select": "index_topk.hip+topk.hip" if step.fused_select else "index_topk.hip+index.hip+topk.hip",
                    "attn_swa": "attn.hip",
                    "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip",
@@ -609,7 +611,9 @@ def main():
     n_queries = wl.prefill_rows if wl.mode == "prefill_reuse" else wl.B
     qps = n_queries / (ms_per_step * 1e-3)
     launches = {"select": "index_topk_kernel + topk_kernel (final level)" if step.fused_select else
-                "index_kernel + topk_kernel"}
+                "index_kernel + topk_kernel",
+                "topk": "topk_estimate_kernel + topk_filter_kernel + topk_select_kernel"
+                if getattr(step, "filtered_topk", False) else "topk_kernel (chunk levels)"}
     roofline = {"bound": "hbm", "kernel": dom, "launches": launches.get(dom, dom), "achieved": achieved,
                 "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

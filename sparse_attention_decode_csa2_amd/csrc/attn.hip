@@ -406,7 +406,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       float* orow = out + (b * H + h) * DC;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) orow[32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + n] = acc[d][i] * inv;
+      for (int d = 0; d < NDB; ++d)
+        __builtin_nontemporal_store(acc[d][i] * inv, &orow[32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + n]);
       if (lse && wave == 0 && n == 0) lse[b * H + h] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
     } else {
       const int64_t slot_o = (b * H + h) * n_split + split;
@@ -936,7 +937,12 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
       const float inv = l > 0.f ? tail / l : 0.f;
       float* orow = out + (b * H + h) * DC + 128 * r + hl;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) orow[32 * k] = acc[k][i] * inv;
+      // final outputs are streamed past the caches (non-temporal stores):
+      // nothing here reads them again, and L2 lines left dirty would have to
+      // be written back before the kernel counts as finished (measured:
+      // reuse-128k attention 23.8 -> 23.1 us); the split partials, which the
+      // merge kernel reads on the same XCD, keep ordinary stores
+      for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(acc[k][i] * inv, &orow[32 * k]);
     } else {
       float* orow = ws_o + ((b * H + h) * n_split + split) * DC + 128 * r + hl;
 #pragma unroll
@@ -1007,7 +1013,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
     m = mn;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  if (has) *reinterpret_cast<f32x4*>(out + row * DC + c) = o * inv;
+  if (has) __builtin_nontemporal_store(o * inv, reinterpret_cast<f32x4*>(out + row * DC + c));
   if (lse && threadIdx.x == 0) lse[row] = L > 0.f ? (m + __log2f(L)) * LN2 : -INFINITY;
 }
 
@@ -1446,7 +1452,7 @@ __global__ __launch_bounds__(256) void swa_attn_kernel(
     for (int d = 0; d < NDB; ++d) {
       const int64_t c = orow + 32 * pv_chunk<DC>(wave, d >> 1) + 16 * (d & 1) + n;
       const float v = acc[d][i] * ow;
-      out[c] = in_lse ? (wa * mi[d] + wb * v) * inv_den : v;
+      __builtin_nontemporal_store(in_lse ? (wa * mi[d] + wb * v) * inv_den : v, &out[c]);
     }
     if (lse && wave == 0 && n == 0) lse[b * H + h] = lo;
   }
