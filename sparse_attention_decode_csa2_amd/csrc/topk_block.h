@@ -702,7 +702,7 @@ __device__ uint32_t bucket_select(const float (&v)[TK_E], const uint32_t (&idv)[
 // to sm.buf[0 .. count), count = min(K, #valid), or the output row itself
 // (returns TK_WRITTEN).
 template <bool FINAL>
-__device__ uint32_t block_select(const float (&v)[TK_E], const uint32_t (&idv)[TK_E], lanemask valid,
+__device__ __forceinline__ uint32_t block_select(const float (&v)[TK_E], const uint32_t (&idv)[TK_E], lanemask valid,
                                  bool ids_are_columns, int K, const TkDst& dst, TkSmem& sm) {
   int par = 0;
   // count, highest and lowest score of the valid elements (NaN scores and
