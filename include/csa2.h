@@ -344,8 +344,9 @@ int csa2_quantize_fp8(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint
  * the window rows of query b); W_cap = 0 (window pointers may then be NULL)
  * is the sparse attention alone.  out f32 [B, H, 512], lse f32 [B, H]
  * (nullable).
- * When the batch fills the GPU with 32-head workgroups (B * ceil(H / 32) >=
- * 256) one kernel attends to the window rows as more tiles after the
+ * When the batch gives at least 64 units of 32 heads (B * ceil(H / 32) >=
+ * 64; each query then in at most four slices, the window in the first) one
+ * kernel attends to the window rows as more tiles after the
  * selected entries': exact E4M3 values in fp16, the row scale applied to the
  * fp32 latent scores and, as sigma_j / max sigma, to the probabilities of
  * the value products (the accumulator divided by max sigma before the first

@@ -1018,12 +1018,14 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 }
 
 // Heads per workgroup: 32 (score waves and value waves) for the 512-channel
-// latent when the batch alone gives a workgroup per CU that way, else 16.
-// Measured: the 32-head kernel is faster unsplit (batch 128: 25.6 vs 34.7 us)
-// but slower where slices are needed (batch 1: 12.1 vs 10.8 us), where the
-// per-workgroup latency path rather than the CU's throughput sets the time.
+// latent when the batch gives at least 64 (query, head group) units, i.e. at
+// most four slices per query, else 16.  Measured: the 32-head kernel is
+// faster unsplit (batch 128: 25.6 vs 34.7 us) and with four slices (batch
+// 32: 16.9 vs 19.1 us) but slower with eight or more (batch 8: 12.4 vs 11.8
+// us; batch 1: 12.1 vs 10.8 us), where the per-workgroup latency path rather
+// than the CU's throughput sets the time.
 static int attn_heads_per_wg(int B, int H, int d_c) {
-  return (d_c == 512 && H > 16 && (int64_t)B * ((H + 31) / 32) >= 256) ? 32 : 16;
+  return (d_c == 512 && H > 16 && (int64_t)B * ((H + 31) / 32) >= 64) ? 32 : 16;
 }
 
 // Slices per query: enough workgroups for 256 CUs, whole 64-entry tiles.

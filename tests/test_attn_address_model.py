@@ -27,7 +27,7 @@ TILE, IDS, IDS_PAD = 64, 512, 640
 
 
 def heads_per_wg(B, H, d_c):
-    return 32 if (d_c == 512 and H > 16 and B * ((H + 31) // 32) >= 256) else 16
+    return 32 if (d_c == 512 and H > 16 and B * ((H + 31) // 32) >= 64) else 16
 
 
 def plan(B, H, K, d_c):
@@ -283,7 +283,7 @@ def test_window_variant_reads(lib, d_r):
     group), windows of 0 .. 256 rows and n_win past W_cap or negative; the
     workspace of the one-call entry is pinned to the library's."""
     rng = np.random.default_rng(d_r)
-    for B, H in ((128, 64), (129, 64), (256, 64), (200, 40), (300, 128)):
+    for B, H in ((32, 64), (33, 64), (63, 64), (128, 64), (129, 64), (256, 64), (200, 40), (300, 128)):
         for K in (1, 512, 1000):
             for W_cap in (1, 64, 65, 128, 256):
                 n_win = rng.integers(-3, W_cap + 4, size=B)
@@ -293,6 +293,6 @@ def test_window_variant_reads(lib, d_r):
                 assert lib.csa2_sparse_swa_attn_workspace_bytes(B, H, 512, K) == ws
     # batches the 32-head kernel does not serve: the sparse kernels' workspace,
     # then B x H floats of LSE for the merge
-    for B, H in ((1, 64), (8, 64), (127, 64), (200, 16)):
+    for B, H in ((1, 64), (8, 64), (31, 64), (200, 16)):
         _, _, _, _, ws = check(B, H, 512, 512, d_r)
         assert lib.csa2_sparse_swa_attn_workspace_bytes(B, H, 512, 512) == -(-ws // 16) * 16 + B * H * 4

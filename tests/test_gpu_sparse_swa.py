@@ -1,7 +1,7 @@
 """The sparse branch and the sliding window in one call (csa2_sparse_swa_attn_fp4)
 on the GPU against the oracle: sparse_attn and swa_attn merged by
 merge_branches, one softmax over the union of both key sets, within 2e-3.
-Batches of 128+ queries at 64 heads run the window tiles inside the 32-head
+Batches of 32+ queries at 64 heads run the window tiles inside the 32-head
 kernel; smaller batches run the two kernels and merge; both are checked, over
 ragged windows, empty windows, empty index lists, extreme row scales and
 split queries (K > 512)."""
@@ -101,7 +101,14 @@ def test_fused_window_extreme_row_scales(lo, hi, sm_mult):
               sm_mult=sm_mult)
 
 
-@pytest.mark.parametrize("B,H", [(8, 64), (3, 40), (130, 40)])
+def test_fused_window_four_slices_per_query():
+    """32 queries x 64 heads: the 32-head kernel with each query in four
+    slices, the window tiles in the first, merged by the split combine."""
+    note("sparse+swa fused: B=32 H=64 K=512 W_cap=128 (four slices)")
+    _run_case(32, 64, 64, 2048, 512, 128, 17, check_rows=[0, 1, 2, 3, 4, 5, 17, 31])
+
+
+@pytest.mark.parametrize("B,H", [(8, 64), (3, 40), (20, 40)])
 def test_small_batches_run_the_two_kernels(B, H):
     """Batches the 32-head kernel does not serve (and a partial head group):
     sparse kernels, then the window kernel merging into their result."""
