@@ -1034,9 +1034,10 @@ static void attn_plan(int B, int H, int K, int d_c, int* n_split, int* per_split
   const int n_hg = (H + hpw - 1) / hpw;
   const int tiles = (int)(((int64_t)K + AT_TILE - 1) / AT_TILE);
   const int64_t base = (int64_t)B * n_hg;
-  // about one workgroup per CU: measured, splitting further (two per CU)
-  // costs more in partials and contention than it gains in parallelism
-  int s = base >= 256 ? 1 : (int)((256 + base - 1) / (base > 1 ? base : 1));
+  // at most one workgroup per CU: measured, splitting further (two per CU)
+  // costs more in partials and contention than it gains in parallelism, and
+  // a second, partial round of workgroups costs a whole workgroup lifetime
+  int s = base >= 256 ? 1 : (int)(256 / (base > 1 ? base : 1));
   s = max(s, (tiles + AT_IDS / AT_TILE - 1) / (AT_IDS / AT_TILE));  // <= 8 tiles per split
   s = max(1, min(s, tiles));
   const int tps = (tiles + s - 1) / s;

@@ -35,7 +35,7 @@ def plan(B, H, K, d_c):
     n_hg = -(-H // hpw)
     tiles = -(-K // TILE)
     base = B * n_hg
-    s = 1 if base >= 256 else -(-256 // base)
+    s = 1 if base >= 256 else 256 // base
     s = max(s, -(-tiles // (IDS // TILE)))
     s = max(1, min(s, tiles))
     tps = -(-tiles // s)
