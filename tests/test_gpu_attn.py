@@ -45,6 +45,21 @@ def test_attention_workload_shapes(wi, B, N):
     _check(wl, B, N, _rand_idx(rng, B, wl.K, N))
 
 
+@pytest.mark.parametrize("B", [5, 9, 24, 32, 48, 96])
+def test_attention_batch_sizes_and_slices(B):
+    """64 heads, K = 512 at batch sizes that take different plans: the 16-head
+    kernel with its slices spread over the XCDs (5), four and two slices per
+    query (9, 24), the 32-head kernel with four and two slices merged by the
+    combine (32, 48), and unsplit on fewer workgroups than CUs (96)."""
+    wl = W.WORKLOADS[3]
+    note(f"attn: B={B} H={wl.H} K={wl.K} slices per the plan")
+    rng = np.random.default_rng(500 + B)
+    N = 2048
+    idx = _rand_idx(rng, B, wl.K, N)
+    idx[0, ::9] = -1
+    _check(wl, B, N, idx)
+
+
 @pytest.mark.parametrize("K", [1, 5, 63, 64, 65, 200, 1000])
 def test_attention_ragged_k(K):
     wl = W.WORKLOADS[1]
