@@ -5,10 +5,11 @@
 // total order.
 //
 //  A. estimate (one 1024-thread workgroup per row): sixteen runs of 1024
-//     columns spread evenly over the row form a sample of 16384 scores; a
-//     radix selection on their order-preserving score keys finds the k'-th
-//     largest sample key, theta, with k' the sample's expected share of the
-//     row's K winners raised by a quarter, four standard deviations and 8.
+//     columns spread evenly over the row form a sample of 16384 scores; two
+//     radix passes over their order-preserving score keys place the k'-th
+//     largest sample key in a narrow range whose floor is theta, with k' the
+//     sample's expected share of the row's K winners raised by a quarter,
+//     four standard deviations and 8.
 //     Rows of at most 16384 columns, and samples of at most k' valid
 //     columns, take theta = 0 (every candidate).
 //  B. filter (about two 1024-thread workgroups per CU, each a contiguous
@@ -144,14 +145,12 @@ __global__ __launch_bounds__(TK_T) void topk_estimate_kernel(const float* __rest
   // a sample with at most k' valid keys keeps every candidate (theta 0): the
   // row then holds few of them, about as many as the list has room for
   if (kp < n) {  // uniform
-    const TkRegion g = radix_select<TK_E>(key, act, kp, kmax, kmin, n, 99, sm, par);
-    // the k'-th largest sample key is the lowest one in the region or above
-    uint32_t lo = 0xFFFFFFFFu, d1 = 0u, d2 = 0u;
-#pragma unroll
-    for (int e = 0; e < TK_E; ++e)
-      if (((act >> e) & 1u) && key[e] >= g.prefix) lo = min(lo, key[e]);
-    block_reduce3<OpMin, OpAdd, OpAdd>(lo, d1, d2, 0xFFFFFFFFu, 0u, 0u, sm, par);
-    theta = lo;
+    // two radix passes (22 bits below the keys' common prefix) place the
+    // k'-th largest sample key in a region; its floor, at or below every key
+    // of the region, is the threshold (a third pass and the exact key cost a
+    // further ~1.8 us for a few more kept keys)
+    const TkRegion g = radix_select<TK_E>(key, act, kp, kmax, kmin, n, 2, sm, par);
+    theta = g.prefix;
   }
   if (tid == 0) {
     rows[b].theta = theta;
