@@ -960,6 +960,403 @@ __global__ __launch_bounds__(512) void sparse_attn_role_kernel(
   }
 }
 
+// The 32-head kernel as a persistent loop, for launches with more (query,
+// 32-head) units than CUs and one slice per query (prefill chunks): workgroup
+// x takes units x, x + G, x + 2G, ... (G workgroups, a multiple of eight, so
+// every unit keeps the XCD of the one-unit-per-workgroup grid) and walks their
+// tiles as one stream.  The score and value waves and the per-tile work are
+// those of sparse_attn_role_kernel; what changes is the hand-over between
+// units, which that kernel pays as a workgroup's start-up (ids, then the
+// gathers; the query fetched and converted) and drain:
+//  * one boundary step per unit: the value waves multiply the last tile of
+//    the unit before and convert this unit's query, whose rows they fetched
+//    one unit earlier, into the value buffer that no tile occupies at that
+//    moment; the score waves take their operands from there after the step's
+//    barrier, and score the unit's first tile while the value waves write
+//    the outputs of the unit before;
+//  * the score waves' look-ahead gathers run on across the boundary (the
+//    first two tiles of a unit load during the last two of the unit before);
+//  * the entry ids are double-buffered in LDS: the value waves fetch a unit's
+//    ids two units ahead and store them during the boundary step before it.
+// Tile j of unit u (T tiles per unit) uses value buffer X_u ^ (j & 1), with
+// X_u = (T odd) ? 0 : u & 1, so the buffer the value waves read in a boundary
+// step (the unit before's last tile) is X_u and the converted query goes to
+// X_u ^ 1, which the unit's tile 1 overwrites only after every score wave has
+// read it.  Needs T >= 2 (the look-ahead reaches one unit ahead only).
+template <int DR>
+__global__ __launch_bounds__(512) void sparse_attn_role_stream_kernel(
+    const uint16_t* __restrict__ q, const CacheRef cache, const int32_t* __restrict__ idx, int K, int B, int H,
+    int64_t N_cap, int qps, float sm_scale_log2e, int n_hp, int64_t n_units, float* __restrict__ out,
+    float* __restrict__ lse) {
+  constexpr int DC = 512;
+  constexpr int KSL = DC / 32;
+  constexpr int KSR = DR / 32;
+  constexpr int KS = KSL + KSR;
+  constexpr int LDK = DC + 16;
+  constexpr int SP = AT_TILE + 4;
+  using GR = GatherRegs<DC, DR>;
+  constexpr int NCW = GR::NCW, RW = GR::RW;
+  static_assert(4 * NCW == KSL && (DR == 0 || RW == KSR), "gather layout = MFMA k-steps");
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2][AT_TILE][LDK];
+  __shared__ __attribute__((aligned(16))) float sS[2][32][SP];
+  __shared__ __attribute__((aligned(16))) float sHd[4][2][32];
+  __shared__ float sFs[32];
+  __shared__ int32_t sIdx[2][AT_IDS];
+  static_assert(2 * KS * 64 * 16 <= (int)sizeof(sV[1]), "converted query fits one value buffer");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int T = (K + AT_TILE - 1) / AT_TILE;  // 2 .. 8 (checked by the host)
+  // this workgroup's units: v = blockIdx.x + k G for k < n_my; unit v is query
+  // b = (v / 8 / n_hp) * 8 + v % 8, heads 32 ((v / 8) % n_hp) ..; units with
+  // b >= B (the padding of the batch to eight) come last in every sequence
+  // (n_units < 2^31, checked by the host: unit numbers are 32-bit)
+  const uint32_t G = gridDim.x, nhp = (uint32_t)n_hp;
+  auto unit_b = [&](int k) -> int64_t {
+    const uint32_t v = blockIdx.x + (uint32_t)k * G;
+    return (int64_t)(((v >> 3) / nhp) * 8 + (v & 7));
+  };
+  auto unit_h0 = [&](int k) -> int {
+    const uint32_t v = blockIdx.x + (uint32_t)k * G;
+    return (int)((v >> 3) % nhp) * 32;
+  };
+  int n_my = 0;
+  {
+    const int cnt = n_units > (int64_t)blockIdx.x ? (int)((n_units - 1 - blockIdx.x) / G) + 1 : 0;
+    int lo = 0, hi = cnt;  // the first k whose query is padding
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (unit_b(mid) < B) lo = mid + 1;
+      else hi = mid;
+    }
+    n_my = lo;
+  }
+  if (n_my == 0) return;
+  const uint32_t cs32 = (uint32_t)cache.codes_stride, ss32 = (uint32_t)cache.scales_stride;
+  const uint32_t rs32 = (uint32_t)cache.rope_stride, ncap32 = (uint32_t)min<int64_t>(N_cap, INT32_MAX);
+
+  // ---- unit 0's entry ids to LDS (one per thread, -1 past K)
+  {
+    const int64_t b0 = unit_b(0);
+    const int32_t id = idx[b0 * K + min(tid, K - 1)];
+    sIdx[0][tid] = tid < K ? id : -1;
+  }
+  constexpr int NPC = KS * 4 / 8;
+  const int hh = 8 * (wave & 3) + (lane >> 3), sub = lane & 7;
+
+  if (wave < 4) {
+    // ================= score waves
+    const int w = wave;
+    // gather tile j of unit k (k >= n_my: a masked load of row 0)
+    auto gather = [&](GR& gr, int k, int j) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bool uok = k < n_my;
+      const int64_t sq = unit_b(uok ? k : n_my - 1) / qps;
+      const uint8_t* seq_codes = cache.codes + sq * N_cap * cache.codes_stride;
+      const uint8_t* seq_scales = cache.scales + sq * N_cap * cache.scales_stride;
+      const uint8_t* seq_rope = reinterpret_cast<const uint8_t*>(cache.rope) + sq * N_cap * cache.rope_stride;
+      const uint32_t id = uok ? (uint32_t)sIdx[k & 1][j * AT_TILE + 16 * w + n] : 0xFFFFFFFFu;
+      gr.valid = id < ncap32;
+      const uint32_t r = gr.valid ? id : 0u;
+      const uint32_t oc = r * cs32 + 16 * g, os = r * ss32 + 2 * g, orp = r * rs32 + 32 * g;
+#pragma unroll
+      for (int i = 0; i < NCW; ++i) {
+        gr.cw[i] = *reinterpret_cast<const u32x4*>(seq_codes + (oc + 64 * i));
+        gr.sb[i] = *reinterpret_cast<const uint16_t*>(seq_scales + (os + 8 * i));
+      }
+      if constexpr (DR > 0) {
+#pragma unroll
+        for (int t = 0; t < RW; ++t) gr.rw[t] = *reinterpret_cast<const u32x4*>(seq_rope + (orp + 16 * t));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    f16x8 Bq[2][KSL];
+    bf16x8 Br[2][KSR > 0 ? KSR : 1];
+    float fscale[2];
+    auto process = [&](GR& gr, int buf) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NCW; ++i) asm volatile("" : "+v"(gr.sb[i]));
+      _Float16 (*tk)[LDK] = sV[buf];
+      const int e = 16 * w + n;
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NCW; ++i) {
+        const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gr.valid ? (uint32_t)gr.sb[i] : 0u, 1.0f, false);
+        const f16x2 s_lo = {sc[0], sc[0]}, s_hi = {sc[1], sc[1]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t word = gr.cw[i][j];
+          const f16x2 sv = j < 2 ? s_lo : s_hi;
+          const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sv;
+          const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sv;
+          const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sv;
+          const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sv;
+          const f16x8 a = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          *reinterpret_cast<f16x8*>(&tk[e][tile_col(e, 4 * i + g, j)]) = a;
+          c0 = mfma16x16x32_f16(a, Bq[0][4 * i + j], c0);
+          c1 = mfma16x16x32_f16(a, Bq[1][4 * i + j], c1);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < KSR; ++t) {
+        const bf16x8 rv = __builtin_bit_cast(bf16x8, gr.rw[t]);
+        c0 = mfma16x16x32_bf16(rv, Br[0][t], c0);
+        c1 = mfma16x16x32_bf16(rv, Br[1][t], c1);
+      }
+      const uint64_t vb = __ballot(g == 0 && gr.valid);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const f32x4 c = k ? c1 : c0;
+        f32x4 sv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = ((vb >> (4 * g + i)) & 1u) ? c[i] * fscale[k] : -INFINITY;
+        *reinterpret_cast<f32x4*>(&sS[buf][16 * k + n][16 * w + 4 * g]) = sv;
+      }
+    };
+
+    __syncthreads();  // unit 0's ids are in place
+    GR ga, gb;
+    gather(ga, 0, 0);
+    gather(gb, 0, 1);
+    // one step per tile: (k, j) is the tile processed, (nk, nj) the one two
+    // tiles later whose gather follows; gathers alternate between ga and gb
+    // along the stream (tile s of the stream in ga when s is even)
+    int k = 0, j = 0;
+    const int total = n_my * T;
+    auto step = [&](GR& gr) {
+      const int X = (T & 1) ? 0 : (k & 1);
+      if (j == 0) {
+        __syncthreads();  // boundary step: the value waves convert unit k's query into buffer X ^ 1
+        const u32x4* qcv = reinterpret_cast<const u32x4*>(&sV[X ^ 1][0][0]);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int t = 0; t < KSL; ++t) Bq[kk][t] = __builtin_bit_cast(f16x8, qcv[(kk * KS + t) * 64 + lane]);
+#pragma unroll
+          for (int t = 0; t < KSR; ++t) Br[kk][t] = __builtin_bit_cast(bf16x8, qcv[(kk * KS + KSL + t) * 64 + lane]);
+          fscale[kk] = sFs[16 * kk + n];
+        }
+      }
+      process(gr, X ^ (j & 1));
+      int nj = j + 2, nk = k;
+      if (nj >= T) {
+        nj -= T;
+        ++nk;
+      }
+      gather(gr, nk, nj);
+      __syncthreads();
+      if (++j == T) {
+        j = 0;
+        ++k;
+      }
+    };
+    int s = 0;
+    for (; s + 2 <= total; s += 2) {
+      step(ga);
+      step(gb);
+    }
+    if (s < total) step(ga);
+    // the look-ahead gathers past the last tile are never used: wait for them
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  // ================= value waves: channels 128 r .. + 127 of all 32 heads
+  const int r = wave - 4;
+  // the query rows of unit k (8 heads per wave, 8 lanes per head; pieces in
+  // the order the gather lays out the latent) and the ids of unit k (two per
+  // lane), fetched one and two units ahead of their use
+  u32x4 raw[NPC];
+  auto fetch_query = [&](int k) {
+    const int h = unit_h0(k) + hh;
+    const bool hok = h < H;
+    const uint16_t* qrow = q + (unit_b(k) * H + (hok ? h : 0)) * (DC + DR);
+#pragma unroll
+    for (int m = 0; m < NPC; ++m) {
+      const int p = sub + 8 * m, t = p >> 2, gg = p & 3;
+      const int off = t < KSL ? 128 * (t >> 2) + 32 * gg + 8 * (t & 3) : DC + 16 * gg + 8 * (t - KSL);
+      raw[m] = hok ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  const int tv = tid - 256;  // 0 .. 255
+  int32_t nid[2];
+  auto fetch_ids = [&](int k) {
+    const int64_t bk = unit_b(k < n_my ? k : 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) nid[i] = idx[bk * K + min(tv + 256 * i, K - 1)];
+  };
+  auto store_ids = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sIdx[k & 1][tv + 256 * i] = tv + 256 * i < K ? nid[i] : -1;
+  };
+  // converts raw into the score waves' operands in value buffer `buf`
+  auto convert_query = [&](int buf) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int m = 0; m < NPC; ++m)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) mx = max(mx, max(raw[m][jj] & 0x7FFFu, (raw[m][jj] >> 16) & 0x7FFFu));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4));
+    // 2^sh brings the largest |q| of the head into [2^14, 2^15), where fp16
+    // keeps every bit of a bf16 value; bf16 subnormals count as exponent -126
+    int ex = (int)((mx >> 7) & 0xFF) - 127;
+    if (ex < -126) ex = -126;
+    const int sh = mx == 0 ? 0 : min(120, max(-120, 14 - ex));
+    const float up = __builtin_amdgcn_ldexpf(1.0f, sh);
+    u32x4* qc = reinterpret_cast<u32x4*>(&sV[buf][0][0]);
+    const int kq = hh >> 4, nn = hh & 15;
+#pragma unroll
+    for (int m = 0; m < NPC; ++m) {
+      const int p = sub + 8 * m, t = p >> 2, gg = p & 3;
+      u32x4 o;
+      if (t < KSL) {
+        f16x8 h;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          h[2 * jj] = (_Float16)(bf16_bits_to_f32(raw[m][jj] & 0xFFFFu) * up);
+          h[2 * jj + 1] = (_Float16)(bf16_bits_to_f32(raw[m][jj] >> 16) * up);
+        }
+        o = __builtin_bit_cast(u32x4, h);
+      } else {
+        bf16x8 h;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          h[2 * jj] = (__bf16)(bf16_bits_to_f32(raw[m][jj] & 0xFFFFu) * up);
+          h[2 * jj + 1] = (__bf16)(bf16_bits_to_f32(raw[m][jj] >> 16) * up);
+        }
+        o = __builtin_bit_cast(u32x4, h);
+      }
+      qc[(kq * KS + t) * 64 + 16 * gg + nn] = o;
+    }
+    if (sub == 0) sFs[hh] = sm_scale_log2e * __builtin_amdgcn_ldexpf(1.0f, -sh);
+  };
+
+  const int hl = lane & 31, kh = lane >> 5;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[kk][i] = 0.f;
+  const int G4 = lane >> 4, tr_r = (lane & 15) >> 2, tr_c = lane & 3;
+
+  auto pv = [&](int buf) {
+    _Float16 (*tk)[LDK] = sV[buf];
+    f32x4 sv[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sv[2 * u] = *reinterpret_cast<const f32x4*>(&sS[buf][hl][16 * u + 8 * kh]);
+      sv[2 * u + 1] = *reinterpret_cast<const f32x4*>(&sS[buf][hl][16 * u + 8 * kh + 4]);
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) mt = fmaxf(mt, fmaxf(fmaxf(sv[jj][0], sv[jj][1]), fmaxf(sv[jj][2], sv[jj][3])));
+    mt = fmaxf(mt, xor32f(mt));
+    const bool move = mt > m_run + RESCALE_SLACK;
+    const float m_new = move ? mt : m_run;
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.f;
+    f16x8 a[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float p = __builtin_amdgcn_exp2f(sv[2 * u + (jj >> 2)][jj & 3] - m_ref);
+        ps += p;
+        a[u][jj] = (_Float16)p;
+      }
+    }
+    ps += xor32f(ps);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (__any(move)) {
+      if (kh == 0) sHd[r][0][hl] = alpha;
+      f32x4 al[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) al[qq] = *reinterpret_cast<const f32x4*>(&sHd[r][0][8 * qq + 4 * kh]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[kk][i] *= al[i >> 2][i & 3];
+    }
+#pragma unroll
+    for (int u = 0; u < AT_TILE / 16; ++u) {
+      const int r0 = 16 * u + 8 * (G4 >> 1) + tr_r, r1 = r0 + 4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ch = 32 * (4 * r + kk) + 16 * (G4 & 1) + 4 * tr_c;
+        const f16x4 v0 = tr16_read(&tk[r0][tile_col(r0, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+        const f16x4 v1 = tr16_read(&tk[r1][tile_col(r1, ch >> 5, (ch >> 3) & 3) + (ch & 7)]);
+        const f16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[kk] = mfma32x32x16_f16(a[u], bv, acc[kk]);
+      }
+    }
+  };
+  // outputs of unit k: element i of acc[kk] is head 8 (i / 4) + 4 kh + i % 4,
+  // channel 32 (4 r + kk) + hl; the state is reset for the next unit
+  auto epilogue = [&](int k) {
+    const int64_t bk = unit_b(k);
+    const int h0 = unit_h0(k);
+    if (kh == 0) sHd[r][1][hl] = l_run;
+    f32x4 lv[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) lv[qq] = *reinterpret_cast<const f32x4*>(&sHd[r][1][8 * qq + 4 * kh]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = h0 + 8 * (i >> 2) + 4 * kh + (i & 3);
+      if (h >= H) continue;
+      const float l = lv[i >> 2][i & 3];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      float* orow = out + (bk * H + h) * DC + 128 * r + hl;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) __builtin_nontemporal_store(acc[kk][i] * inv, &orow[32 * kk]);
+    }
+    if (r == 0 && kh == 0 && h0 + hl < H && lse)
+      lse[bk * H + h0 + hl] = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[kk][i] = 0.f;
+  };
+
+  fetch_query(0);
+  fetch_ids(1);
+  __syncthreads();  // unit 0's ids are in place
+  for (int k = 0; k < n_my; ++k) {
+    // boundary step of unit k (the score waves wait at its barrier): the
+    // last tile of unit k - 1, whose buffer tile 0 of unit k overwrites next,
+    // and unit k's query
+    const int X = (T & 1) ? 0 : (k & 1);
+    if (k > 0) pv(X);
+    convert_query(X ^ 1);
+    if (k + 1 < n_my) store_ids(k + 1);
+    __syncthreads();
+    // while tile 0 of unit k is scored: the outputs of unit k - 1, then the
+    // fetches for the next units (after the stores, so that the query rows
+    // are not held in registers beside the accumulators)
+    if (k > 0) epilogue(k - 1);
+    if (k + 1 < n_my) fetch_query(k + 1);
+    if (k + 2 < n_my) fetch_ids(k + 2);
+    __syncthreads();
+    for (int jt = 1; jt < T; ++jt) {
+      pv(X ^ ((jt - 1) & 1));
+      __syncthreads();
+    }
+  }
+  {
+    const int X = (T & 1) ? 0 : (n_my & 1);  // the last tile's buffer
+    pv(X);
+    epilogue(n_my - 1);
+  }
+}
+
 // Merge the per-slice partial results of one (b, h) row by log-sum-exp; each
 // of the 128 threads owns 4 consecutive channels (d_c <= 512).  The slices are
 // taken 8 at a time with every load of a round issued together (one memory
@@ -1046,6 +1443,15 @@ static void attn_plan(int B, int H, int K, int d_c, int* n_split, int* per_split
   *per_split = tps * AT_TILE;
 }
 
+// The persistent 32-head kernel: one workgroup per CU walking several units
+// each, when the query is unsplit, has 2 to 8 tiles, and the units outnumber
+// the workgroups.
+constexpr int AT_STREAM_WG = 256;
+static bool attn_streamed(int hpw, int n_split, int K, int64_t n_units) {
+  return hpw == 32 && n_split == 1 && K > AT_TILE && K <= AT_IDS && n_units > AT_STREAM_WG &&
+         n_units < ((int64_t)1 << 31);
+}
+
 // The attention grid (and the combine's, when the query is split).
 int64_t attn_launch_items(int B, int H, int d_c, int K) {
   if (B <= 0) return 0;
@@ -1089,6 +1495,18 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
   hipLaunchKernelGGL((KERNEL<DCV, DRV>), grid, dim3(THREADS), 0, stream, q, cache, idx, K, B, H, N_cap, qps, sl, \
                      n_hg, s, ps, spread, out, lse, ws_o, ws_ml)
   const WinRef no_win{nullptr, 0, nullptr, nullptr, 0, nullptr, 0};
+  const int64_t n_units = groups * 8 * n_hg;
+  if (attn_streamed(hpw, s, K, n_units)) {
+    const dim3 sgrid((unsigned)AT_STREAM_WG);
+    if (d_r == 64)
+      hipLaunchKernelGGL((sparse_attn_role_stream_kernel<64>), sgrid, dim3(512), 0, stream, q, cache, idx, K, B, H,
+                         N_cap, qps, sl, n_hg, n_units, out, lse);
+    else if (d_r == 0)
+      hipLaunchKernelGGL((sparse_attn_role_stream_kernel<0>), sgrid, dim3(512), 0, stream, q, cache, idx, K, B, H,
+                         N_cap, qps, sl, n_hg, n_units, out, lse);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (hpw == 32) {
     if (d_r == 64)
       hipLaunchKernelGGL((sparse_attn_role_kernel<64, false>), grid, dim3(512), 0, stream, q, cache, idx, K, B, H, N_cap,

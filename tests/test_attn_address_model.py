@@ -296,3 +296,134 @@ def test_window_variant_reads(lib, d_r):
     for B, H in ((1, 64), (8, 64), (31, 64), (200, 16)):
         _, _, _, _, ws = check(B, H, 512, 512, d_r)
         assert lib.csa2_sparse_swa_attn_workspace_bytes(B, H, 512, 512) == -(-ws // 16) * 16 + B * H * 4
+
+
+# ---------------------------------------------------------------- persistent kernel
+STREAM_WG = 256
+
+
+def streamed(B, H, K, d_c):
+    """The persistent 32-head kernel serves unsplit queries of 2..8 tiles
+    when the (query, 32-head) units outnumber its 256 workgroups."""
+    hpw, n_hg, s, _ = plan(B, H, K, d_c)
+    n_units = (B + 7) // 8 * 8 * n_hg
+    return hpw == 32 and s == 1 and TILE < K <= IDS and n_units > STREAM_WG, n_hg, n_units
+
+
+def stream_units(B, n_hp, n_units, G=STREAM_WG):
+    """Workgroup x -> its units (b, head group) in order: v = x + k G while
+    the query of v is a real one (the padding of the batch to eight comes
+    last in every workgroup's sequence; found by the same bisection)."""
+    owned = []
+    for x in range(G):
+        def ub(k):
+            v = x + k * G
+            return ((v >> 3) // n_hp) * 8 + (v & 7)
+        cnt = (n_units - 1 - x) // G + 1 if n_units > x else 0
+        lo, hi = 0, cnt
+        while lo < hi:
+            mid = (lo + hi) // 2
+            if ub(mid) < B:
+                lo = mid + 1
+            else:
+                hi = mid
+        bs = [ub(k) for k in range(cnt)]
+        assert all(b < B for b in bs[:lo]) and all(b >= B for b in bs[lo:]), "padding units not last"
+        assert all(bs[k] <= bs[k + 1] for k in range(cnt - 1))
+        units = []
+        for k in range(lo):
+            v = x + k * G
+            assert v & 7 == x & 7, "a unit left its XCD"
+            units.append((ub(k), (v >> 3) % n_hp))
+        owned.append(units)
+    return owned
+
+
+def stream_protocol(n_my, T):
+    """Replays the barrier intervals of one persistent workgroup with n_my
+    units of T tiles, both roles, and checks every LDS access of the value
+    buffers (tiles, score rows, the converted query), the head scales and the
+    double-buffered ids against what it must find: a read sees the last write
+    of an earlier interval with the expected contents, and no interval has a
+    write that another role (or the other half of a role) also touches."""
+    X = lambda k: 0 if T & 1 else k & 1
+    ev = {}            # interval -> list of (role, op, resource, tag)
+
+    def put(i, role, op, res, tag):
+        ev.setdefault(i, []).append((role, op, res, tag))
+
+    # every thread stages unit 0's ids before the first barrier
+    put(0, "all", "w", "idx0", ("ids", 0))
+    # score waves
+    i = 1
+    for kk in range(min(2, T)):
+        put(i, "S", "r", "idx0", ("ids", 0))
+    for s in range(n_my * T):
+        k, j = divmod(s, T)
+        if j == 0:
+            i += 1
+            put(i, "S", "r", f"v{X(k) ^ 1}", ("query", k))
+            put(i, "S", "r", "fs", ("query", k))
+        put(i, "S", "w", f"v{X(k) ^ (j & 1)}", ("tile", k, j))
+        nk, nj = (k, j + 2) if j + 2 < T else (k + 1, j + 2 - T)
+        if nk < n_my:
+            put(i, "S", "r", f"idx{nk & 1}", ("ids", nk))
+        i += 1
+    s_barriers = i
+    # value waves
+    i = 1
+    for k in range(n_my):
+        if k > 0:
+            put(i, "V", "r", f"v{X(k)}", ("tile", k - 1, T - 1))
+        put(i, "V", "w", f"v{X(k) ^ 1}", ("query", k))
+        put(i, "V", "w", "fs", ("query", k))
+        if k + 1 < n_my:
+            put(i, "V", "w", f"idx{(k + 1) & 1}", ("ids", k + 1))
+        i += 1
+        for jt in range(T):
+            if jt > 0:
+                put(i, "V", "r", f"v{X(k) ^ ((jt - 1) & 1)}", ("tile", k, jt - 1))
+            i += 1
+    assert i == s_barriers, "the two roles pass different numbers of barriers"
+    put(i, "V", "r", f"v{X(n_my)}", ("tile", n_my - 1, T - 1))
+    state = {}
+    for it in sorted(ev):
+        acc = ev[it]
+        for role, op, res, tag in acc:
+            if op == "r":
+                assert state.get(res) == tag, (n_my, T, it, role, res, tag, state.get(res))
+        for role, op, res, tag in acc:
+            if op == "w":
+                others = [a for a in acc if a[2] == res and a[0] != role]
+                assert not others, ("race", n_my, T, it, res, acc)
+        for role, op, res, tag in acc:
+            if op == "w":
+                state[res] = tag
+
+
+def test_stream_kernel_units_and_lds_protocol(lib):
+    """The persistent 32-head kernel: every (query, head group) unit owned by
+    exactly one workgroup, on the XCD of the one-unit-per-workgroup grid;
+    the LDS hand-over between units for every unit count and tile count it
+    can meet; and its reads are those of the 32-head kernel (checked above
+    through `check`) for the shapes it serves."""
+    for n_my in range(1, 9):
+        for T in range(2, 9):
+            stream_protocol(n_my, T)
+    stream_protocol(64, 8)
+    stream_protocol(33, 3)
+    cases = [(8192, 64, 512), (8192, 64, 100), (257, 64, 512), (300, 40, 512), (129, 64, 128),
+             (2048, 128, 512), (1000, 100, 65), (4096, 64, 700), (128, 64, 512), (64, 64, 512)]
+    n_streamed = 0
+    for B, H, K in cases:
+        ok, n_hp, n_units = streamed(B, H, K, 512)
+        _, _, _, _, ws = check(B, H, K, 512, 64, qps=B if B > 256 else 1)
+        _pin_plan(lib, B, H, K, 512, ws)
+        if not ok:
+            continue
+        n_streamed += 1
+        owned = stream_units(B, n_hp, n_units)
+        flat = [u for us in owned for u in us]
+        assert len(flat) == len(set(flat)) == B * n_hp, (B, H, K)
+        assert all(0 <= b < B and 0 <= hg < n_hp for b, hg in flat)
+    assert n_streamed >= 6

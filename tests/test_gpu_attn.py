@@ -45,6 +45,24 @@ def test_attention_workload_shapes(wi, B, N):
     _check(wl, B, N, _rand_idx(rng, B, wl.K, N))
 
 
+@pytest.mark.parametrize("B,K", [(300, 512), (300, 130), (260, 65), (520, 200)])
+def test_attention_persistent_many_units(B, K):
+    """More (query, 32-head) units than CUs with unsplit queries: the
+    persistent 32-head kernel, each workgroup walking two or three units of
+    8, 3, 2 or 4 tiles, each query over its own sequence; batches padded to
+    a multiple of eight (300, 260); masked, repeated and empty lists."""
+    wl = W.WORKLOADS[3]
+    note(f"attn: persistent B={B} K={K} H={wl.H}")
+    rng = np.random.default_rng(700 + B + K)
+    N = 1024
+    idx = _rand_idx(rng, B, K, N)
+    idx[0, ::5] = -1
+    idx[1, :] = idx[1, 0]
+    idx[2, :] = -1
+    idx[B - 1, K // 2:] = N + 7
+    _check(wl, B, N, idx)
+
+
 @pytest.mark.parametrize("B", [5, 9, 24, 32, 48, 96])
 def test_attention_batch_sizes_and_slices(B):
     """64 heads, K = 512 at batch sizes that take different plans: the 16-head

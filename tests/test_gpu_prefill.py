@@ -128,12 +128,14 @@ def test_prefill_full_workload_sampled_rows():
     attn_close(out[0, ts].cpu().numpy(), lse[0, ts].cpu().numpy(), ro, rl, 2e-3)
 
 
-def test_prefill_in_a_hip_graph_matches_eager():
+@pytest.mark.parametrize("T", [64, 150])
+def test_prefill_in_a_hip_graph_matches_eager(T):
     """csa2_prefill_sparse_attn_fp4 captured into a HIP graph and replayed
     three times, with eager work in between, reproduces the eager result bit
-    for bit."""
+    for bit (128 queries: one unit per workgroup; 300: the persistent
+    kernel)."""
     wl = W.WORKLOADS[1]
-    S, T, N, K = 2, 64, 2048, 512
+    S, N, K = 2, 2048, 512
     note(f"prefill attn: HIP graph capture + 3 replays vs eager S={S} T={T}")
     codes, scales, rope = _raw_caches(wl, S, N)
     q = W.attn_query(wl.scaled(B=S * T), DEV).view(S, T, wl.H, wl.D)
