@@ -5,9 +5,10 @@ GPU: an 8192-row post-RoPE bf16 chunk is quantised to FP4 and appended to
 sequence 0, then a batch of 8 Full-mode decode queries (64 heads, indexer
 8 heads x 128) scores 262144 entries per sequence (1M tokens at 4:1), takes
 the Top-512 and runs the sparse attention over them.  One step =
-csa2_quantize_fp4 -> csa2_index_topk_full (the indexer scores and their
-Top-512 in one call) -> csa2_sparse_attn_fp4, all on the GPU through the C
-ABI, with every input resident in HBM.  The other
+csa2_index_topk_full_append (the chunk write, the indexer scores and their
+Top-512 in one call; the chunk is written by the Top-K's last launch on the
+CUs its selection leaves idle) -> csa2_sparse_attn_fp4, all on the GPU
+through the C ABI, with every input resident in HBM.  The other
 workloads (--workload) give the supplementary lines.
 
 Inputs rotate over R distinct sets, R sized from the bytes one step actually
@@ -18,9 +19,9 @@ many distinct sets and bytes the timed steps touched.
 Prints ONE JSON line (rank 0).  `roofline` describes the dominant stage:
 algorithmic bytes per call over its average duration (HIP events on the
 stream the kernels run on), against the 8 TB/s HBM peak.  The dominant stage
-of the Full workloads, `select` (csa2_index_topk_full), is two launches at
-1M entries: the fused indexer + chunk Top-K kernel, then the final Top-K
-level; its duration covers both.  `traffic` comes from
+of the Full workloads, `select` (csa2_index_topk_full, with the chunk write
+at prefill-full-1m), is two launches at 1M entries: the fused indexer +
+chunk Top-K kernel, then the final Top-K level; its duration covers both.  `traffic` comes from
 the committed rocprofv3 FETCH_SIZE / WRITE_SIZE measurement of that kernel
 (profiles/), and is null when the kernel source changed since it was taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
@@ -94,7 +95,7 @@ class Step:
     Full (tiny-full, full-64k): select (indexer scores + Top-K) -> attn, each set its own caches.
     Reindex (reindex-1m): pool -> topk -> attn over one cache; sets = pools + queries.
     Reuse (reuse-128k): attn over one cache; sets = index lists + queries.
-    Prefill + Full (prefill-full-1m): quantize (append 8192 rows) -> select -> attn.
+    Prefill + Full (prefill-full-1m): select (append 8192 rows + indexer scores + Top-K) -> attn.
     Pool construction (pool-build-1m): index (Full scores) -> build (the Reindex pool).
     Reuse + window (reuse-swa-128k): attn_swa (the selected entries and the FP8 window in one softmax).
     Sampler (sample-129k): topk (over the vocabulary logits) -> draw; sets = logits + uniforms.
@@ -162,7 +163,7 @@ class Step:
         self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
         self.ws_attn = torch.empty(max(at, 16), dtype=torch.uint8, device=dev) if at else None
         self.stages = {"full": ["select", "attn"], "reindex": ["pool", "topk", "attn"],
-                       "reuse": ["attn"], "prefill_full": ["quantize", "select", "attn"],
+                       "reuse": ["attn"], "prefill_full": ["select", "attn"],
                        "pool_build": ["index", "build"], "reuse_swa": ["attn_swa"],
                        "prefill_reuse": ["attn"]}[self.mode]
         if self.mode == "prefill_reuse":
@@ -289,6 +290,15 @@ class Step:
         self.csa2.csa2_index_full(self.sets[r]["qi"], self._keys(r), scores=self.scores)
 
     def select(self, r):
+        if self.mode == "prefill_full":
+            # the chunk write rides in the scoring call (the Top-K's last
+            # level runs it on the CUs its selection leaves idle)
+            c, wl = self.cache, self.wl
+            self.csa2.csa2_index_topk_full_append(self.sets[r]["qi"], self._keys(r), wl.K, self.chunk,
+                                                  c["codes"][0], c["scales"][0], wl.prefill_row0,
+                                                  self.chunk_rope, c["rope"][0], out_idx=self.idx,
+                                                  out_score=self.top, workspace=self.ws_topk)
+            return
         self.csa2.csa2_index_topk_full(self.sets[r]["qi"], self._keys(r), self.wl.K, out_idx=self.idx,
                                        out_score=self.top, workspace=self.ws_topk)
 
@@ -376,9 +386,11 @@ class Step:
             d["topk"] = B * (Mp * 8 + K * 8)
             step += B * (wl.n_blocks * wl.block * wl.D_I * 2 + qi + wl.n_blocks * 4)
         if self.mode == "prefill_full":
+            # the chunk write (bf16 rows read, FP4 records written) is part of the select call
             R = wl.prefill_rows
-            d["quantize"] = R * (wl.d_c * 2 + wl.d_r * 2) + R * (wl.d_c // 2 + wl.d_c // 16 + wl.d_r * 2)
-            step += d["quantize"]
+            chunk = R * (wl.d_c * 2 + wl.d_r * 2) + R * (wl.d_c // 2 + wl.d_c // 16 + wl.d_r * 2)
+            d["select"] += chunk
+            step += chunk
         d["step"] = step
         return d
 
@@ -610,8 +622,9 @@ def main():
 
     n_queries = wl.prefill_rows if wl.mode == "prefill_reuse" else wl.B
     qps = n_queries / (ms_per_step * 1e-3)
-    launches = {"select": "index_topk_kernel + topk_kernel (final level)" if step.fused_select else
-                "index_kernel + topk_kernel",
+    launches = {"select": ("index_topk_kernel + topk_final_append_kernel (final level + chunk write)"
+                           if wl.mode == "prefill_full" else "index_topk_kernel + topk_kernel (final level)")
+                if step.fused_select else "index_kernel + topk_kernel",
                 "topk": "topk_estimate_kernel + topk_filter_kernel + topk_select_kernel"
                 if getattr(step, "filtered_topk", False) else "topk_kernel (chunk levels)"}
     roofline = {"bound": "hbm", "kernel": dom, "launches": launches.get(dom, dom), "achieved": achieved,

@@ -220,6 +220,30 @@ int csa2_index_topk_full(const uint16_t* q_idx, const float* w, const uint16_t* 
                          void* workspace, size_t workspace_bytes, csa2_stream_t stream);
 
 /*
+ * a0 + a1 + a3 in one call: csa2_index_topk_full and an independent
+ * csa2_quantize_fp4 (a prefill chunk's rows appended to the main cache while
+ * the indexer scores the same step's queries: [P1] 效率组件四件, item 4, and
+ * 架构三件套, Hierarchical Sparse Indexer).  The results are bit for bit
+ * those of the two calls, in either order.  When the scoring takes the fused
+ * chunk kernel, the append runs in the launch of the Top-K's last level, on
+ * the CUs its B selection workgroups leave idle, so it adds no launch and
+ * almost no time to the step; otherwise the append's own kernel runs first.
+ * The append must not write memory the scoring reads (k_idx, q_idx, w,
+ * n_valid) or the outputs and workspace (results undefined otherwise).
+ * Arguments: those of csa2_index_topk_full, then those of csa2_quantize_fp4
+ * (x .. capacity), each validated as in its own call (n_rows = 0: the
+ * scoring alone; B = 0: the append alone).
+ */
+int csa2_index_topk_full_append(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                                const int32_t* n_valid, int32_t B, int32_t H_I, int32_t D_I,
+                                int64_t N_cap, int32_t K, int32_t* out_idx, float* out_score,
+                                void* workspace, size_t workspace_bytes, const uint16_t* x,
+                                int64_t n_rows, int32_t d_c, const uint16_t* rope_src, int32_t d_r,
+                                uint8_t* codes, int64_t codes_stride, uint8_t* scales,
+                                int64_t scales_stride, uint16_t* rope_dst, int64_t rope_stride,
+                                int64_t dst_row0, int64_t capacity, csa2_stream_t stream);
+
+/*
  * csa2_topk without a workspace, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments (less the workspace), same results, bit

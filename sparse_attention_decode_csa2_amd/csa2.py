@@ -52,6 +52,8 @@ def load():
         "csa2_topk_noalloc": (ctypes.c_int, [P, P, P, I32, I64, I32, P, P, P]),
         "csa2_index_topk_full_workspace_bytes": (SZ, [I32, I32, I64, I32]),
         "csa2_index_topk_full": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I64, I32, P, P, P, SZ, P]),
+        "csa2_index_topk_full_append": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I64, I32, P, P, P, SZ,
+                                                       P, I64, I32, P, I32, P, I64, P, I64, P, I64, I64, I64, P]),
         "csa2_quantize_fp8": (ctypes.c_int, [P, I64, I32, P, I32, P, I64, P, P, I64, I64, I64, P]),
         "csa2_swa_attn_fp8": (ctypes.c_int, [P, P, I64, P, P, I64, P, I32, I32, I32, I32, I32, F, P, P, P, P, P]),
         "csa2_build_pool_workspace_bytes": (SZ, [I32, I64, I32, I32]),
@@ -278,6 +280,44 @@ def csa2_index_topk_full(q_idx, k_idx, K, w=None, n_valid=None, out_idx=None, ou
     st = lib.csa2_index_topk_full(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(n_valid), B, H_I, D_I, N_cap, K,
                                   _ptr(out_idx), _ptr(out_score), _ptr(workspace), ws_bytes, _stream())
     _check("csa2_index_topk_full", st)
+    return out_idx, out_score
+
+
+def csa2_index_topk_full_append(q_idx, k_idx, K, x, codes, scales, dst_row0=0, rope_src=None, rope_dst=None,
+                                w=None, n_valid=None, out_idx=None, out_score=None, workspace=None,
+                                want_score=True):
+    """csa2_index_topk_full and csa2_quantize_fp4 (x rows into rows dst_row0..
+    of one sequence's cache views, as csa2_quantize_fp4 takes them) in one
+    call: returns (idx, score) of the scoring; the cache views are written."""
+    lib = load()
+    B, H_I, D_I, N_cap = _index_inputs(q_idx, k_idx, w, n_valid)
+    dev = k_idx.device
+    out_idx = _out(out_idx, (B, K), torch.int32, dev, "out_idx")
+    if out_score is not None or want_score:
+        out_score = _out(out_score, (B, K), torch.float32, dev, "out_score")
+    need = csa2_index_topk_full_workspace_bytes(B, D_I, N_cap, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError(f"x must be [R, d_c], got {tuple(x.shape)}")
+    R, d_c = x.shape
+    d_r = 0 if rope_src is None else rope_src.shape[-1]
+    if rope_src is not None:
+        _need(rope_src, torch.bfloat16, "rope_src", (R, None))
+    _cache_views(codes, scales, rope_dst, d_r, 2)
+    if codes.shape[1] * 2 != d_c:
+        raise ValueError(f"codes rows hold {codes.shape[1] * 2} channels, x has {d_c}")
+    cs = _row_stride(codes, 1, "codes")
+    ss = _row_stride(scales, 1, "scales")
+    rs = _row_stride(rope_dst, 2, "rope_dst") if d_r else 0
+    st = lib.csa2_index_topk_full_append(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(n_valid), B, H_I, D_I, N_cap, K,
+                                         _ptr(out_idx), _ptr(out_score), _ptr(workspace), ws_bytes,
+                                         _ptr(x), R, d_c, _ptr(rope_src), d_r, _ptr(codes), cs, _ptr(scales), ss,
+                                         _ptr(rope_dst if d_r else None), rs, int(dst_row0), codes.shape[-2],
+                                         _stream())
+    _check("csa2_index_topk_full_append", st)
     return out_idx, out_score
 
 

@@ -45,10 +45,13 @@ static int check_cache(int32_t d_c, int32_t d_r, const void* codes, int64_t& cod
   return CSA2_OK;
 }
 
-int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
-                      int32_t d_r, uint8_t* codes, int64_t codes_stride, uint8_t* scales,
-                      int64_t scales_stride, uint16_t* rope_dst, int64_t rope_stride,
-                      int64_t dst_row0, int64_t capacity, csa2_stream_t stream) {
+// Validates csa2_quantize_fp4's operands and fills *a (n_rows == 0: CSA2_OK
+// with a->n_rows = 0 and nothing else looked at).
+static int check_fp4_append(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
+                            int32_t d_r, uint8_t* codes, int64_t codes_stride, uint8_t* scales,
+                            int64_t scales_stride, uint16_t* rope_dst, int64_t rope_stride, int64_t dst_row0,
+                            int64_t capacity, csa2::Fp4Append* a) {
+  a->n_rows = 0;
   if (n_rows < 0 || capacity < 0 || d_c < 32 || d_c > 4096 || d_c % 32 != 0 || d_r < 0 ||
       d_r > 1024 || d_r % 8 != 0 || codes_stride < 0 || scales_stride < 0 || rope_stride < 0)
     return CSA2_ERR_SHAPE;
@@ -60,8 +63,20 @@ int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint
   if (st != CSA2_OK) return st;
   if (too_large(csa2::quantize_fp4_launch_items(n_rows, d_c, d_r))) return CSA2_ERR_RANGE;
   const csa2::CacheRef c{codes, codes_stride, scales, scales_stride, d_r > 0 ? rope_dst : nullptr, rope_stride};
-  return hip_status(csa2::launch_quantize_fp4(x, n_rows, d_c, d_r > 0 ? rope_src : nullptr, d_r, c,
-                                              dst_row0, as_stream(stream)));
+  *a = csa2::Fp4Append{x, n_rows, d_c, d_r > 0 ? rope_src : nullptr, d_r, c, dst_row0};
+  return CSA2_OK;
+}
+
+int csa2_quantize_fp4(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
+                      int32_t d_r, uint8_t* codes, int64_t codes_stride, uint8_t* scales,
+                      int64_t scales_stride, uint16_t* rope_dst, int64_t rope_stride,
+                      int64_t dst_row0, int64_t capacity, csa2_stream_t stream) {
+  csa2::Fp4Append a;
+  const int st = check_fp4_append(x, n_rows, d_c, rope_src, d_r, codes, codes_stride, scales, scales_stride,
+                                  rope_dst, rope_stride, dst_row0, capacity, &a);
+  if (st != CSA2_OK || a.n_rows == 0) return st;
+  return hip_status(csa2::launch_quantize_fp4(a.x, a.n_rows, a.d_c, a.rope_src, a.d_r, a.cache, a.dst_row0,
+                                              as_stream(stream)));
 }
 
 int csa2_quantize_fp8(const uint16_t* x, int64_t n_rows, int32_t d_c, const uint16_t* rope_src,
@@ -205,9 +220,10 @@ size_t csa2_index_topk_full_workspace_bytes(int32_t B, int32_t D_I, int64_t N_ca
   return csa2::index_topk_workspace_bytes(B, D_I, N_cap, K);
 }
 
-int csa2_index_topk_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int32_t* n_valid,
-                         int32_t B, int32_t H_I, int32_t D_I, int64_t N_cap, int32_t K, int32_t* out_idx,
-                         float* out_score, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+static int check_index_topk_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                                 const int32_t* n_valid, int32_t B, int32_t H_I, int32_t D_I, int64_t N_cap,
+                                 int32_t K, int32_t* out_idx, float* out_score, void* workspace,
+                                 size_t workspace_bytes) {
   if (B < 0 || N_cap < 1 || N_cap > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
   if (K < 1 || K > 2048) return CSA2_ERR_RANGE;
   if (H_I < 1 || H_I > 16 || (D_I != 32 && D_I != 64 && D_I != 128 && D_I != 256)) return CSA2_ERR_UNSUPPORTED;
@@ -220,8 +236,37 @@ int csa2_index_topk_full(const uint16_t* q_idx, const float* w, const uint16_t* 
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return CSA2_ERR_ALIGN;
   if (too_large(csa2::index_topk_launch_items(B, D_I, N_cap, K))) return CSA2_ERR_RANGE;
+  return CSA2_OK;
+}
+
+int csa2_index_topk_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int32_t* n_valid,
+                         int32_t B, int32_t H_I, int32_t D_I, int64_t N_cap, int32_t K, int32_t* out_idx,
+                         float* out_score, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+  const int st = check_index_topk_full(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, K, out_idx, out_score,
+                                       workspace, workspace_bytes);
+  if (st != CSA2_OK || B == 0) return st;
   return hip_status(csa2::launch_index_topk(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, K, out_idx, out_score,
                                             workspace, as_stream(stream)));
+}
+
+int csa2_index_topk_full_append(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                                const int32_t* n_valid, int32_t B, int32_t H_I, int32_t D_I, int64_t N_cap,
+                                int32_t K, int32_t* out_idx, float* out_score, void* workspace,
+                                size_t workspace_bytes, const uint16_t* x, int64_t n_rows, int32_t d_c,
+                                const uint16_t* rope_src, int32_t d_r, uint8_t* codes, int64_t codes_stride,
+                                uint8_t* scales, int64_t scales_stride, uint16_t* rope_dst, int64_t rope_stride,
+                                int64_t dst_row0, int64_t capacity, csa2_stream_t stream) {
+  int st = check_index_topk_full(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, K, out_idx, out_score, workspace,
+                                 workspace_bytes);
+  if (st != CSA2_OK) return st;
+  csa2::Fp4Append a;
+  st = check_fp4_append(x, n_rows, d_c, rope_src, d_r, codes, codes_stride, scales, scales_stride, rope_dst,
+                        rope_stride, dst_row0, capacity, &a);
+  if (st != CSA2_OK) return st;
+  if (a.n_rows > 0 && too_large(csa2::topk_final_append_launch_items(B, a))) return CSA2_ERR_RANGE;
+  if (B == 0 && a.n_rows == 0) return CSA2_OK;
+  return hip_status(csa2::launch_index_topk(q_idx, w, k_idx, n_valid, B, H_I, D_I, N_cap, K, out_idx, out_score,
+                                            workspace, as_stream(stream), a.n_rows > 0 ? &a : nullptr));
 }
 
 int csa2_topk_noalloc(const float* scores, const int32_t* ids, const int32_t* n_valid, int32_t B, int64_t M,

@@ -32,6 +32,19 @@ struct CacheRef {
   int64_t rope_stride;
 };
 
+// An FP4 append (csa2_quantize_fp4's operands, validated): rows [0, n_rows)
+// of x (bf16, d_c each) and rope_src (bf16, d_r each; null when d_r == 0)
+// into cache rows dst_row0 + r.
+struct Fp4Append {
+  const uint16_t* x;
+  int64_t n_rows;
+  int d_c;
+  const uint16_t* rope_src;
+  int d_r;
+  CacheRef cache;
+  int64_t dst_row0;
+};
+
 // The FP8 sliding window of each query for the attention kernels (codes null:
 // no window): rows j < n_win[b] (clamped to [0, W_cap]; n_win null = W_cap)
 // of query b are rows b * W_cap + j of codes / sigma / rope, as written by
@@ -80,16 +93,22 @@ hipError_t launch_topk_filtered(const float* scores, const int32_t* ids, const i
                                 int K, int32_t* out_idx, float* out_score, void* workspace, hipStream_t stream);
 // The Top-K levels after the first, on B rows of m chunk-winner keys.
 size_t topk_keys_workspace_bytes(int B, int64_t m, int K);
+// `app` (nullable): an independent FP4 append run by extra workgroups of the
+// final level's launch, on the CUs its B selection workgroups leave idle.
 hipError_t launch_topk_from_keys(const uint64_t* keys, int B, int64_t m, int K, int32_t* out_idx,
-                                 float* out_score, void* workspace, hipStream_t stream);
+                                 float* out_score, void* workspace, hipStream_t stream,
+                                 const Fp4Append* app = nullptr);
 
 // Full-mode indexer scores and their Top-K in one call (fused chunk kernel when
 // the rows give a workgroup per CU, else the two kernels).
 int64_t index_topk_launch_items(int B, int D_I, int64_t N_cap, int K);
 size_t index_topk_workspace_bytes(int B, int D_I, int64_t N_cap, int K);
+// `app` (nullable): an FP4 append to run in the same call, independent of the
+// scoring (in the final Top-K level's launch on the fused path, else first).
 hipError_t launch_index_topk(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* n_valid, int B,
                              int H_I, int D_I, int64_t N_cap, int K, int32_t* out_idx, float* out_score,
-                             void* workspace, hipStream_t stream);
+                             void* workspace, hipStream_t stream, const Fp4Append* app = nullptr);
+int64_t topk_final_append_launch_items(int B, const Fp4Append& app);
 
 size_t pool_workspace_bytes(int B, int64_t M, int block, int P_max);
 hipError_t launch_build_pool(const float* scores, const int32_t* n_valid, int B, int64_t M, int block,

@@ -149,9 +149,17 @@ size_t index_topk_workspace_bytes(int B, int D_I, int64_t N_cap, int K) {
 
 hipError_t launch_index_topk(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* n_valid, int B,
                              int H_I, int D_I, int64_t N_cap, int K, int32_t* out_idx, float* out_score,
-                             void* workspace, hipStream_t stream) {
-  if (B == 0) return hipSuccess;
+                             void* workspace, hipStream_t stream, const Fp4Append* app) {
+  if (B == 0) return app ? launch_quantize_fp4(app->x, app->n_rows, app->d_c, app->rope_src, app->d_r, app->cache,
+                                               app->dst_row0, stream)
+                         : hipSuccess;
   if (!it_fused(B, D_I, N_cap)) {
+    // the two-kernel path has no idle final level: the append goes first
+    if (app) {
+      const hipError_t e = launch_quantize_fp4(app->x, app->n_rows, app->d_c, app->rope_src, app->d_r, app->cache,
+                                               app->dst_row0, stream);
+      if (e != hipSuccess) return e;
+    }
     float* scores = static_cast<float*>(workspace);
     const size_t s = ((size_t)B * N_cap * sizeof(float) + 15) & ~(size_t)15;
     hipError_t e = launch_index(q, w, k, n_valid, B, H_I, D_I, N_cap, nullptr, nullptr, 0, 1, scores, nullptr,
@@ -172,7 +180,7 @@ hipError_t launch_index_topk(const uint16_t* q, const float* w, const uint16_t* 
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_from_keys(keys, B, m, K, out_idx, out_score, keys + (size_t)B * m, stream);
+  return launch_topk_from_keys(keys, B, m, K, out_idx, out_score, keys + (size_t)B * m, stream, app);
 }
 
 }  // namespace csa2

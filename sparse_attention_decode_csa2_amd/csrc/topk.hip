@@ -2,23 +2,22 @@
 // the kernels of the chunked reduction over the block-level selection of
 // topk_block.h.
 #include "csa2_internal.h"
+#include "quantize_task.h"
 #include "topk_block.h"
 
 namespace csa2 {
 
+// One workgroup's selection: chunk `blk` of the level (row blk / chunks).
 template <bool FROM_SCORES, bool FINAL>
-__global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ scores,
-                                                    const int32_t* __restrict__ ids,
-                                                    const int32_t* __restrict__ n_valid,
-                                                    const uint64_t* __restrict__ keys_in, int64_t M,
-                                                    int K, int chunks, uint64_t* __restrict__ keys_out,
-                                                    int32_t* __restrict__ out_idx,
-                                                    float* __restrict__ out_score) {
-  __shared__ TkSmem sm;
+__device__ __forceinline__ void topk_body(TkSmem& sm, int64_t blk, const float* __restrict__ scores,
+                                          const int32_t* __restrict__ ids, const int32_t* __restrict__ n_valid,
+                                          const uint64_t* __restrict__ keys_in, int64_t M, int K, int chunks,
+                                          uint64_t* __restrict__ keys_out, int32_t* __restrict__ out_idx,
+                                          float* __restrict__ out_score) {
   const int tid = threadIdx.x;
   tk_init(sm);
-  const int64_t b = blockIdx.x / chunks;
-  const int c = (int)(blockIdx.x - b * chunks);
+  const int64_t b = blk / chunks;
+  const int c = (int)(blk - b * chunks);
   const int64_t base = (int64_t)c * TK_CHUNK;
   int64_t limit = min<int64_t>(M, base + TK_CHUNK);
   const int64_t col0 = base + (int64_t)TK_E * tid;  // this thread's first column
@@ -126,6 +125,51 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   }
 }
 
+template <bool FROM_SCORES, bool FINAL>
+__global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ scores,
+                                                    const int32_t* __restrict__ ids,
+                                                    const int32_t* __restrict__ n_valid,
+                                                    const uint64_t* __restrict__ keys_in, int64_t M,
+                                                    int K, int chunks, uint64_t* __restrict__ keys_out,
+                                                    int32_t* __restrict__ out_idx,
+                                                    float* __restrict__ out_score) {
+  __shared__ TkSmem sm;
+  topk_body<FROM_SCORES, FINAL>(sm, blockIdx.x, scores, ids, n_valid, keys_in, M, K, chunks, keys_out, out_idx,
+                                out_score);
+}
+
+// The final level over B rows of keys (workgroups 0 .. B - 1, as
+// topk_kernel<false, true>) and, in the workgroups after them, an
+// independent FP4 append walked item by item: the selection occupies B CUs,
+// the append the others, so the append costs no time of its own.
+__global__ __launch_bounds__(TK_T) void topk_final_append_kernel(const uint64_t* __restrict__ keys_in, int64_t M,
+                                                                 int K, int B, int32_t* __restrict__ out_idx,
+                                                                 float* __restrict__ out_score, const Fp4Append app,
+                                                                 int64_t n_groups, int64_t n_rope) {
+  __shared__ TkSmem sm;
+  if ((int)blockIdx.x < B) {
+    topk_body<false, true>(sm, blockIdx.x, nullptr, nullptr, nullptr, keys_in, M, K, 1, nullptr, out_idx,
+                           out_score);
+    return;
+  }
+  const int64_t stride = (int64_t)(gridDim.x - B) * TK_T;
+  for (int64_t i = (int64_t)(blockIdx.x - B) * TK_T + threadIdx.x; i < n_groups + n_rope; i += stride)
+    fp4_append_item(i, app, n_groups, n_rope);
+}
+
+// Append workgroups of the fused final level: enough for about one item per
+// thread, at most the CUs beyond the selection's (256 in all on MI355X).
+static int64_t append_wgs(int B, int64_t items) {
+  const int64_t want = (items + TK_T - 1) / TK_T;
+  const int64_t room = B < 248 ? 256 - B : 8;
+  return want < room ? (want > 0 ? want : 1) : room;
+}
+
+int64_t topk_final_append_launch_items(int B, const Fp4Append& app) {
+  const int64_t items = app.n_rows * (app.d_c / 16) + (app.d_r > 0 ? app.n_rows * (app.d_r / 8) : 0);
+  return ((int64_t)B + append_wgs(B, items)) * TK_T;
+}
+
 // Levels of the chunked reduction: level 0 reads the scores (M columns); level
 // L > 0 reads the chunk winners of level L-1.
 static int topk_levels(int64_t M, int K, int64_t* chunks_per_level, int max_levels) {
@@ -189,7 +233,7 @@ size_t topk_keys_workspace_bytes(int B, int64_t m, int K) {
 }
 
 hipError_t launch_topk_from_keys(const uint64_t* keys, int B, int64_t m, int K, int32_t* out_idx,
-                                 float* out_score, void* workspace, hipStream_t stream) {
+                                 float* out_score, void* workspace, hipStream_t stream, const Fp4Append* app) {
   int64_t ch[16];
   const int n = topk_levels(m, K, ch, 16);
   if (n > 16) return hipErrorInvalidValue;
@@ -198,8 +242,16 @@ hipError_t launch_topk_from_keys(const uint64_t* keys, int B, int64_t m, int K, 
   for (int l = 0; l < n; ++l) {
     const dim3 grid((unsigned)(B * ch[l]));
     if (l + 1 == n) {
-      hipLaunchKernelGGL((topk_kernel<false, true>), grid, dim3(TK_T), 0, stream, nullptr, nullptr,
-                         nullptr, prev, m, K, 1, nullptr, out_idx, out_score);
+      if (app && app->n_rows > 0) {
+        const int64_t n_groups = app->n_rows * (app->d_c / 16);
+        const int64_t n_rope = app->d_r > 0 ? app->n_rows * (app->d_r / 8) : 0;
+        const dim3 agrid((unsigned)(B + append_wgs(B, n_groups + n_rope)));
+        hipLaunchKernelGGL(topk_final_append_kernel, agrid, dim3(TK_T), 0, stream, prev, m, K, B, out_idx,
+                           out_score, *app, n_groups, n_rope);
+      } else {
+        hipLaunchKernelGGL((topk_kernel<false, true>), grid, dim3(TK_T), 0, stream, nullptr, nullptr,
+                           nullptr, prev, m, K, 1, nullptr, out_idx, out_score);
+      }
       return hipGetLastError();
     }
     hipLaunchKernelGGL((topk_kernel<false, false>), grid, dim3(TK_T), 0, stream, nullptr, nullptr,

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
 
@@ -126,6 +126,30 @@ def test_index_topk_validation(lib):
     assert call(out=U) == ALIGN and call(w=U) == ALIGN and call(nv=U) == ALIGN and call(score=U) == ALIGN
     assert call(ws=N) == WS and call(wsn=need - 1) == WS
     assert call(ws=U) == ALIGN
+
+
+def test_index_topk_full_append_validation(lib):
+    """The fused call validates the scoring's operands as csa2_index_topk_full
+    and the append's as csa2_quantize_fp4; an empty side is skipped."""
+    f = lib.csa2_index_topk_full_append
+    need = lib.csa2_index_topk_full_workspace_bytes(1, 128, 100, 8)
+
+    def call(q=A, k=A, B=1, N_cap=100, K=8, out=A, ws=A, wsn=need, x=A, n=4, d_c=512, rs=N, d_r=0, codes=A,
+             cst=0, scales=A, sst=0, rd=N, rst=0, r0=0, cap=10):
+        return f(q, N, k, N, B, 8, 128, N_cap, K, out, N, ws, wsn, x, n, d_c, rs, d_r, codes, cst, scales, sst,
+                 rd, rst, r0, cap, N)
+    # the scoring's checks
+    assert call(B=-1) == SHAPE and call(K=0) == RANGE and call(q=N) == NULL
+    assert call(out=U) == ALIGN and call(ws=N) == WS and call(wsn=need - 1) == WS
+    # the append's checks
+    assert call(n=-1) == SHAPE and call(d_c=500) == SHAPE and call(r0=8) == RANGE
+    assert call(x=N) == NULL and call(codes=N) == NULL and call(x=U) == ALIGN
+    assert call(d_r=64, rs=A, rd=N) == NULL
+    # either side empty: only the other is checked; both empty: nothing to do
+    assert call(B=0, q=N, out=N, ws=N, x=N, n=0, r0=10) == OK
+    assert call(B=0, q=N, out=N, ws=N, x=U) == ALIGN
+    assert call(n=0, r0=10, x=N, codes=N, scales=N, q=N) == NULL
+
 
 
 def test_sparse_swa_validation(lib):

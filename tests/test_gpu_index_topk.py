@@ -128,3 +128,95 @@ def test_fused_call_in_a_hip_graph_matches_eager():
         assert torch.equal(idx, ref[0]) and torch.equal(top, ref[1]), rep
         csa2.csa2_index_topk_full(q[:1], k[:1], 64)      # eager work between replays
         torch.cuda.synchronize()
+
+
+def _rand_cache(wl, cap, seed):
+    """Two identical FP4 caches of one sequence, filled with random bytes (so
+    that rows an append must not touch are checked too)."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    ca = csa2.alloc_cache(1, cap, wl.d_c, wl.d_r, DEV)
+    cb = csa2.alloc_cache(1, cap, wl.d_c, wl.d_r, DEV)
+    for ta, tb in zip(ca, cb):
+        if ta.numel() == 0:
+            continue
+        if ta.dtype == torch.uint8:
+            ta.copy_(torch.randint(0, 256, ta.shape, generator=g, device=DEV, dtype=torch.uint8))
+        else:
+            ta.copy_(torch.randn(ta.shape, generator=g, device=DEV).to(ta.dtype))
+        tb.copy_(ta)
+    return ca, cb
+
+
+def _append_vs_separate(wl, q, k, K, rows, cap, row0, seed=0):
+    x = W.latent_rows(wl, 0, rows, DEV)
+    rs = W.rope_rows(wl, 0, rows, DEV) if wl.d_r else None
+    ca, cb = _rand_cache(wl, cap, seed)
+    fi, fs = csa2.csa2_index_topk_full_append(q, k, K, x, ca[0][0], ca[1][0], row0, rs, ca[2][0] if wl.d_r else None)
+    si, ss = csa2.csa2_index_topk_full(q, k, K)
+    csa2.csa2_quantize_fp4(x, cb[0][0], cb[1][0], row0, rs, cb[2][0] if wl.d_r else None)
+    torch.cuda.synchronize()
+    assert torch.equal(fi, si)
+    assert torch.equal(fs.view(torch.int32), ss.view(torch.int32))
+    for ta, tb in zip(ca, cb):
+        if ta.numel():
+            assert torch.equal(ta.contiguous().view(torch.uint8), tb.contiguous().view(torch.uint8))
+    return fi
+
+
+def test_scoring_and_append_in_one_call():
+    """csa2_index_topk_full_append = csa2_index_topk_full + csa2_quantize_fp4,
+    bit for bit, on the benchmarked step (8 x 262144 entries, the 8192-row
+    chunk appended by the Top-K's last level) and with ragged and tiny
+    appends, no RoPE part, the separate-kernel path (one row of 16384
+    entries), an empty scoring (B = 0) and an empty append."""
+    wl = W.BY_NAME["prefill-full-1m"]
+    note(f"index_topk + append: {wl.name} B={wl.B} N={wl.N} chunk {wl.prefill_rows} rows")
+    q, k = W.index_query(wl, DEV), _keys(wl, wl.B)
+    fi = _append_vs_separate(wl, q, k, wl.K, wl.prefill_rows, wl.N, wl.prefill_row0, seed=1)
+    ri, _ = _oracle_row(q, k, wl.K, None, None, 3)
+    assert np.array_equal(fi[3].cpu().numpy(), ri[0])
+    _append_vs_separate(wl, q, k, wl.K, 1000, 4096, 5, seed=2)
+    _append_vs_separate(wl, q, k, wl.K, 1, 16, 15, seed=3)
+    _append_vs_separate(wl.scaled(d_r=0), q, k, wl.K, 777, 1000, 200, seed=4)
+    _append_vs_separate(wl, q, k, wl.K, 0, 16, 16, seed=5)
+    w64 = W.BY_NAME["full-64k"]
+    note("index_topk + append: separate-kernel path, B = 0")
+    _append_vs_separate(w64, W.index_query(w64, DEV), _keys(w64, 1), w64.K, 3000, 8192, 100, seed=6)
+    _append_vs_separate(wl, q[:0], k[:0], wl.K, 500, 600, 50, seed=7)
+
+
+def test_scoring_and_append_in_a_hip_graph():
+    """The one-call step captured into a HIP graph and replayed three times
+    (outputs and the appended rows cleared in between, eager work between the
+    replays) reproduces the eager result bit for bit."""
+    wl = W.BY_NAME["prefill-full-1m"]
+    note("index_topk + append: HIP graph capture + 3 replays vs eager")
+    q, k = W.index_query(wl, DEV), _keys(wl, wl.B)
+    x = W.latent_rows(wl, 0, wl.prefill_rows, DEV)
+    rs = W.rope_rows(wl, 0, wl.prefill_rows, DEV)
+    codes, scales, rope = csa2.alloc_cache(1, wl.prefill_rows, wl.d_c, wl.d_r, DEV)
+    idx = torch.empty(wl.B, wl.K, dtype=torch.int32, device=DEV)
+    top = torch.empty(wl.B, wl.K, dtype=torch.float32, device=DEV)
+    ws = torch.empty(csa2.csa2_index_topk_full_workspace_bytes(wl.B, wl.D_I, wl.N, wl.K), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        csa2.csa2_index_topk_full_append(q, k, wl.K, x, codes[0], scales[0], 0, rs, rope[0], out_idx=idx,
+                                         out_score=top, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (idx, top, codes, scales, rope)]
+    s = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        step()
+    for rep in range(3):
+        for t in (idx, top, codes, scales, rope):
+            t.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((idx, top, codes, scales, rope), ref):
+            assert torch.equal(t, r), rep
+        csa2.csa2_index_topk_full(q[:1], k[:1], 64)      # eager work between replays
+        torch.cuda.synchronize()
