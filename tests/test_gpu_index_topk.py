@@ -183,6 +183,11 @@ def test_scoring_and_append_in_one_call():
     note("index_topk + append: separate-kernel path, B = 0")
     _append_vs_separate(w64, W.index_query(w64, DEV), _keys(w64, 1), w64.K, 3000, 8192, 100, seed=6)
     _append_vs_separate(wl, q[:0], k[:0], wl.K, 500, 600, 50, seed=7)
+    # 256 rows of one chunk each: the last level has 256 selection
+    # workgroups and the append its minimum of eight
+    wb = wl.scaled(B=256, N=8192)
+    note("index_topk + append: B = 256 rows of 8192 entries")
+    _append_vs_separate(wb, W.index_query(wb, DEV), _keys(wb, 256), wb.K, 3000, 4096, 1000, seed=8)
 
 
 def test_scoring_and_append_in_a_hip_graph():
