@@ -20,20 +20,22 @@ __device__ __forceinline__ void topk_body(TkSmem& sm, int64_t blk, const float* 
   const int c = (int)(blk - b * chunks);
   const int64_t base = (int64_t)c * TK_CHUNK;
   int64_t limit = min<int64_t>(M, base + TK_CHUNK);
-  const int64_t col0 = base + (int64_t)TK_E * tid;  // this thread's first column
+  const int64_t col0 = base + (int64_t)TK_E * tid;  // this thread's first score column
   // element e: score v[e] (NaN when empty), id idv[e], valid bit e
   float v[TK_E];
   uint32_t idv[TK_E];
   lanemask valid = 0;
   const float qnan = __uint_as_float(F_NAN);
   bool ids_are_columns;
+  // every load is issued before any result is used: a load under a
+  // per-element branch would wait for the one before it
   if (FROM_SCORES) {
+    // thread t holds the TK_E consecutive columns from col0 (thread order is
+    // column order)
     if (n_valid) limit = min<int64_t>(limit, max<int64_t>(n_valid[b], 0));
     ids_are_columns = ids == nullptr;
     const float* srow = scores + b * M;
     const int32_t* irow = ids ? ids + b * M : nullptr;
-    // every load is issued before any result is used: a load under a
-    // per-element branch would wait for the one before it
     float x[TK_E];
     uint32_t ii[TK_E];
     if (col0 + TK_E <= limit && (M & 3) == 0) {
@@ -72,14 +74,21 @@ __device__ __forceinline__ void topk_body(TkSmem& sm, int64_t blk, const float* 
       valid |= (lanemask)ok << e;
     }
   } else {
+    // keys are held lane-contiguously: element e of thread t is key base +
+    // 2 (TK_T (e / 2) + t) + e % 2, so that each 16-byte load instruction
+    // reads 1 KiB of consecutive keys (8 cache lines, not 64).  Which thread
+    // holds a key does not matter: keys are unique up to identical (score,
+    // id) pairs, and ties between those are invisible in the output
     ids_are_columns = false;
     const uint64_t* krow = keys_in + b * M;
+    auto pos = [&](int e) { return base + 2 * ((int64_t)TK_T * (e >> 1) + tid) + (e & 1); };
     uint64_t k[TK_E];
-    if (col0 + TK_E <= limit && (M & 1) == 0) {
-      // a whole run: 16-byte loads (rows stay 16-byte aligned)
+    if ((M & 1) == 0) {
+      // 16-byte loads (rows stay 16-byte aligned), clamped to the row's last
+      // word: the keys of a clamped word all lie past the row, hence past limit
 #pragma unroll
       for (int q = 0; q < TK_E / 2; ++q) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(krow + col0 + 2 * q);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(krow + min<int64_t>(pos(2 * q), M - 2));
         k[2 * q] = ((uint64_t)w[1] << 32) | w[0];
         k[2 * q + 1] = ((uint64_t)w[3] << 32) | w[2];
       }
@@ -87,10 +96,10 @@ __device__ __forceinline__ void topk_body(TkSmem& sm, int64_t blk, const float* 
       // keys past the end read the last key in range and are then dropped
       const int64_t last = limit > 0 ? limit - 1 : 0;
 #pragma unroll
-      for (int e = 0; e < TK_E; ++e) k[e] = krow[min<int64_t>(col0 + e, last)];
-#pragma unroll
-      for (int e = 0; e < TK_E; ++e) k[e] = col0 + e < limit ? k[e] : 0ull;
+      for (int e = 0; e < TK_E; ++e) k[e] = krow[min<int64_t>(pos(e), last)];
     }
+#pragma unroll
+    for (int e = 0; e < TK_E; ++e) k[e] = pos(e) < limit ? k[e] : 0ull;
 #pragma unroll
     for (int e = 0; e < TK_E; ++e) {
       const uint32_t hk = (uint32_t)(k[e] >> 32);
