@@ -207,6 +207,7 @@ class Step:
         self.n_kept = torch.empty(B, dtype=torch.int32, device=dev)
         if self.mode == "sample_full":
             self.stages = ["draw_full"]
+            self.ws_full = torch.empty(csa2.csa2_sample_full_workspace_bytes(B, V), dtype=torch.uint8, device=dev)
             return
         tk = csa2.csa2_topk_workspace_bytes(B, V, K)
         # the threshold filter's workspace: a 128-byte record and 16384 keys per row
@@ -234,7 +235,7 @@ class Step:
 
     def draw_full(self, r):
         self.csa2.csa2_sample_full(self.sets[r]["logits"], self.wl.temperature, self.sets[r]["u"], token=self.token,
-                                   prob=self.prob)
+                                   prob=self.prob, workspace=self.ws_full)
 
     def draw(self, r):
         wl = self.wl

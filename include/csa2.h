@@ -327,12 +327,18 @@ int csa2_sample(const float* logits, int32_t B, int64_t V, int32_t K, float temp
  * or NaN logit gives an unspecified token of the row.
  *
  * logits f32 [B, V] (row b at logits + b * V), u f32 [B] in [0, 1), token
- * i32 [B] out, prob f32 [B] out (nullable).  One pass over the logits and one
- * 16384-token tile read again per row; no workspace.  Requires 1 <= V <= 2^20
+ * i32 [B] out, prob f32 [B] out (nullable).  One pass over the logits, spread
+ * over several workgroups per row, then one 16384-token tile read again per
+ * row.  The workspace (at least csa2_sample_full_workspace_bytes(B, V) =
+ * B * ceil(V / 16384) * 128 bytes, 16-byte aligned, caller-owned, contents
+ * not preserved) holds per 16384-token tile the 16 (largest scaled logit,
+ * weight sum) pairs of the first pass.  Requires 1 <= V <= 2^20
  * (CSA2_ERR_RANGE beyond), 1e-30 <= T <= 1e30, 16-byte aligned arrays.
  */
+size_t csa2_sample_full_workspace_bytes(int32_t B, int64_t V);
 int csa2_sample_full(const float* logits, int32_t B, int64_t V, float temperature, const float* u,
-                     int32_t* token, float* prob, csa2_stream_t stream);
+                     int32_t* token, float* prob, void* workspace, size_t workspace_bytes,
+                     csa2_stream_t stream);
 
 /*
  * Sliding-window branch, write: FP8 rows of the window KV.  The window branch

@@ -61,7 +61,8 @@ def load():
         "csa2_sample_draw": (ctypes.c_int, [P, P, I32, I32, F, F, P, P, P, P, P]),
         "csa2_sample_workspace_bytes": (SZ, [I32, I64, I32]),
         "csa2_sample": (ctypes.c_int, [P, I32, I64, I32, F, F, P, P, P, P, P, SZ, P]),
-        "csa2_sample_full": (ctypes.c_int, [P, I32, I64, F, P, P, P, P]),
+        "csa2_sample_full_workspace_bytes": (SZ, [I32, I64]),
+        "csa2_sample_full": (ctypes.c_int, [P, I32, I64, F, P, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "csa2_sparse_swa_attn_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "csa2_sparse_swa_attn_fp4": (ctypes.c_int, [P, P, I64, P, I64, P, I64, P, I32, I32, I32, I32, I32, I64,
@@ -424,7 +425,11 @@ def csa2_sample(logits, K, temperature, top_p, u, token=None, prob=None, n_kept=
     return token, prob, n_kept
 
 
-def csa2_sample_full(logits, temperature, u, token=None, prob=None):
+def csa2_sample_full_workspace_bytes(B, V):
+    return int(load().csa2_sample_full_workspace_bytes(B, V))
+
+
+def csa2_sample_full(logits, temperature, u, token=None, prob=None, workspace=None):
     """The untruncated draw (top_p 1.0 over the whole vocabulary): logits f32
     [B, V], u f32 [B] -> (token i32 [B], prob f32 [B])."""
     lib = load()
@@ -436,7 +441,12 @@ def csa2_sample_full(logits, temperature, u, token=None, prob=None):
     dev = logits.device
     token = _out(token, (B,), torch.int32, dev, "token")
     prob = _out(prob, (B,), torch.float32, dev, "prob")
-    st = lib.csa2_sample_full(_ptr(logits), B, V, float(temperature), _ptr(u), _ptr(token), _ptr(prob), _stream())
+    need = csa2_sample_full_workspace_bytes(B, V)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.csa2_sample_full(_ptr(logits), B, V, float(temperature), _ptr(u), _ptr(token), _ptr(prob),
+                              _ptr(workspace), ws_bytes, _stream())
     _check("csa2_sample_full", st)
     return token, prob
 

@@ -330,15 +330,23 @@ int csa2_sample(const float* logits, int32_t B, int64_t V, int32_t K, float temp
                                         as_stream(stream)));
 }
 
+size_t csa2_sample_full_workspace_bytes(int32_t B, int64_t V) {
+  if (B <= 0 || V < 1 || V > csa2::kSampleFullMaxVocab) return 0;
+  return csa2::sample_full_workspace_bytes(B, V);
+}
+
 int csa2_sample_full(const float* logits, int32_t B, int64_t V, float temperature, const float* u, int32_t* token,
-                     float* prob, csa2_stream_t stream) {
+                     float* prob, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
   if (B < 0 || V < 1) return CSA2_ERR_SHAPE;
   if (V > csa2::kSampleFullMaxVocab || !sampler_params_ok(temperature, 1.0f)) return CSA2_ERR_RANGE;
   if (B == 0) return CSA2_OK;
   if (!logits || !u || !token) return CSA2_ERR_NULL;
   if (!aligned16(logits) || !aligned16(u) || !aligned16(token) || !opt_aligned16(prob)) return CSA2_ERR_ALIGN;
-  if (too_large(csa2::sample_full_launch_items(B))) return CSA2_ERR_RANGE;
-  return hip_status(csa2::launch_sample_full(logits, B, V, temperature, u, token, prob, as_stream(stream)));
+  if (!workspace || workspace_bytes < csa2::sample_full_workspace_bytes(B, V)) return CSA2_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CSA2_ERR_ALIGN;
+  if (too_large(csa2::sample_full_launch_items(B, V))) return CSA2_ERR_RANGE;
+  return hip_status(csa2::launch_sample_full(logits, B, V, temperature, u, token, prob, workspace,
+                                             as_stream(stream)));
 }
 
 size_t csa2_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t K) {

@@ -127,10 +127,11 @@ size_t sample_workspace_bytes(int B, int64_t V, int K);
 hipError_t launch_sample_draw(const int32_t* cand_idx, const float* cand_score, int B, int K, float temperature,
                               float top_p, const float* u, int32_t* token, float* prob, int32_t* n_kept,
                               hipStream_t stream);
-int64_t sample_full_launch_items(int B);
+int64_t sample_full_launch_items(int B, int64_t V);
 constexpr int64_t kSampleFullMaxVocab = (int64_t)1 << 20;
+size_t sample_full_workspace_bytes(int B, int64_t V);
 hipError_t launch_sample_full(const float* logits, int B, int64_t V, float temperature, const float* u,
-                              int32_t* token, float* prob, hipStream_t stream);
+                              int32_t* token, float* prob, void* workspace, hipStream_t stream);
 hipError_t launch_sample(const float* logits, int B, int64_t V, int K, float temperature, float top_p,
                          const float* u, int32_t* token, float* prob, int32_t* n_kept, void* workspace,
                          hipStream_t stream);

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = csa2.declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
 
@@ -475,13 +475,23 @@ def test_topk_noalloc_validation(lib):
 
 def test_sample_full_validation(lib):
     f = lib.csa2_sample_full
-    assert f(A, 0, 129280, 1.0, A, A, N, N) == OK
-    assert f(A, -1, 129280, 1.0, A, A, N, N) == SHAPE
-    assert f(A, 2, 0, 1.0, A, A, N, N) == SHAPE
-    assert f(A, 2, (1 << 20) + 1, 1.0, A, A, N, N) == RANGE
-    assert f(A, 2, 129280, 0.0, A, A, N, N) == RANGE
-    assert f(A, 2, 129280, float("nan"), A, A, N, N) == RANGE
-    assert f(N, 2, 129280, 1.0, A, A, N, N) == NULL
-    assert f(A, 2, 129280, 1.0, A, N, N, N) == NULL
-    assert f(U, 2, 129280, 1.0, A, A, N, N) == ALIGN
-    assert f(A, 2, 129280, 1.0, A, A, U, N) == ALIGN
+    wsb = lib.csa2_sample_full_workspace_bytes
+    # 16 (max, sum) pairs of 8 bytes per 16384-token tile and row
+    assert wsb(128, 129280) == 128 * 8 * 16 * 8 and wsb(1, 1) == 128 and wsb(0, 10) == 0
+    assert wsb(2, (1 << 20) + 1) == 0
+    need = wsb(2, 129280)
+
+    def call(lg=A, B=2, V=129280, T=1.0, u=A, tok=A, prob=N, ws=A, wsn=need):
+        return f(lg, B, V, T, u, tok, prob, ws, wsn, N)
+    assert call(B=0, lg=N, ws=N) == OK
+    assert call(B=-1) == SHAPE
+    assert call(V=0) == SHAPE
+    assert call(V=(1 << 20) + 1) == RANGE
+    assert call(T=0.0) == RANGE
+    assert call(T=float("nan")) == RANGE
+    assert call(lg=N) == NULL
+    assert call(tok=N) == NULL
+    assert call(lg=U) == ALIGN
+    assert call(prob=U) == ALIGN
+    assert call(ws=N) == WS and call(wsn=need - 1) == WS
+    assert call(ws=U) == ALIGN
