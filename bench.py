@@ -627,7 +627,8 @@ def main():
                            if wl.mode == "prefill_full" else "index_topk_kernel + topk_kernel (final level)")
                 if step.fused_select else "index_kernel + topk_kernel",
                 "topk": "topk_estimate_kernel + topk_filter_kernel + topk_select_kernel"
-                if getattr(step, "filtered_topk", False) else "topk_kernel (chunk levels)"}
+                if getattr(step, "filtered_topk", False) else "topk_kernel (chunk levels)",
+                "draw_full": "sample_full_stats_kernel + sample_full_kernel"}
     roofline = {"bound": "hbm", "kernel": dom, "launches": launches.get(dom, dom), "achieved": achieved,
                 "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
