@@ -98,7 +98,7 @@ class Step:
     Prefill + Full (prefill-full-1m): select (append 8192 rows + indexer scores + Top-K) -> attn.
     Pool construction (pool-build-1m): index (Full scores) -> build (the Reindex pool).
     Reuse + window (reuse-swa-128k): attn_swa (the selected entries and the FP8 window in one softmax).
-    Sampler (sample-129k): topk (over the vocabulary logits) -> draw; sets = logits + uniforms.
+    Sampler (sample-129k): sample (csa2_sample: Top-K over the vocabulary logits + the draw); sets = logits + uniforms.
     Prefill, Reuse layer (prefill-reuse-1m): attn over one cache for the 8192 queries of a chunk,
     each with its own causal list; sets = queries + lists.
     """
@@ -213,7 +213,11 @@ class Step:
         # the threshold filter's workspace: a 128-byte record and 16384 keys per row
         self.filtered_topk = V > 16384 and tk == B * (128 + 16384 * 8)
         self.ws_topk = torch.empty(max(tk, 16), dtype=torch.uint8, device=dev) if tk else None
-        self.stages = ["topk", "draw"]
+        self.ws_sample = torch.empty(max(csa2.csa2_sample_workspace_bytes(B, V, K), 16), dtype=torch.uint8,
+                                     device=dev)
+        # one call, csa2_sample (Top-K + draw; with the threshold filter its
+        # last kernel draws from the rows it writes)
+        self.stages = ["sample"]
 
     def step_read_bytes(self):
         """Bytes one step reads from HBM (the inputs of all its stages, read
@@ -236,6 +240,11 @@ class Step:
     def draw_full(self, r):
         self.csa2.csa2_sample_full(self.sets[r]["logits"], self.wl.temperature, self.sets[r]["u"], token=self.token,
                                    prob=self.prob, workspace=self.ws_full)
+
+    def sample(self, r):
+        wl = self.wl
+        self.csa2.csa2_sample(self.sets[r]["logits"], wl.K, wl.temperature, wl.top_p, self.sets[r]["u"],
+                              token=self.token, prob=self.prob, n_kept=self.n_kept, workspace=self.ws_sample)
 
     def draw(self, r):
         wl = self.wl
@@ -355,7 +364,8 @@ class Step:
         B, N, K, H = wl.B, wl.N, wl.K, wl.H
         if self.mode == "sample":
             # logits read once; uniform in, token + prob + n_kept out; candidates (ids + logits) between stages
-            return {"topk": B * (N * 4 + K * 8), "draw": B * (K * 8 + 4 + 12), "step": B * (N * 4 + 4 + 12)}
+            return {"sample": B * (N * 4 + 4 + 12), "topk": B * (N * 4 + K * 8), "draw": B * (K * 8 + 4 + 12),
+                    "step": B * (N * 4 + 4 + 12)}
         if self.mode == "sample_full":
             # logits read once, uniform in, token + prob out (the drawn tile's second read is not counted)
             return {"draw_full": B * (N * 4 + 4 + 8), "step": B * (N * 4 + 4 + 8)}
@@ -606,6 +616,7 @@ def main():
     alg = step.alg_bytes()
     dom = max(stages, key=lambda s: stage_us[s])
     kernel_file = {"index": "index.hip", "pool": "index.hip", "topk": "topk.hip+topk_filter.hip", "attn": "attn.hip",
+                   "sample": "topk.hip+topk_filter.hip+sample.hip",
                    "select": "index_topk.hip+topk.hip" if step.fused_select else "index_topk.hip+index.hip+topk.hip",
                    "attn_swa": "attn.hip",
                    "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip",
@@ -628,7 +639,9 @@ def main():
                 if step.fused_select else "index_kernel + topk_kernel",
                 "topk": "topk_estimate_kernel + topk_filter_kernel + topk_select_kernel"
                 if getattr(step, "filtered_topk", False) else "topk_kernel (chunk levels)",
-                "draw_full": "sample_full_stats_kernel + sample_full_kernel"}
+                "draw_full": "sample_full_stats_kernel + sample_full_kernel",
+                "sample": "topk_estimate_kernel + topk_filter_kernel + topk_select_draw_kernel"
+                if getattr(step, "filtered_topk", False) else "topk_kernel (chunk levels) + sample_draw_kernel"}
     roofline = {"bound": "hbm", "kernel": dom, "launches": launches.get(dom, dom), "achieved": achieved,
                 "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

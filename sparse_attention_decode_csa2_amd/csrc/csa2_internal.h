@@ -89,8 +89,22 @@ hipError_t launch_topk_chunked(const float* scores, const int32_t* ids, const in
 bool topk_filter_fits(int B, int64_t M, int K);
 int64_t topk_filter_launch_items(int B, int64_t M);
 size_t topk_filter_workspace_bytes(int B);
+// The sampler's draw settings, for a Top-K whose last kernel also draws
+// (csa2_sample): the draw of sample_draw_kernel over the candidate rows.
+struct SampleDraw {
+  float log2e_over_t;
+  float top_p;
+  const float* u;
+  int32_t* token;
+  float* prob;
+  int32_t* n_kept;
+};
+// `draw` (nullable, scores without ids only): the last kernel draws too.
 hipError_t launch_topk_filtered(const float* scores, const int32_t* ids, const int32_t* n_valid, int B, int64_t M,
-                                int K, int32_t* out_idx, float* out_score, void* workspace, hipStream_t stream);
+                                int K, int32_t* out_idx, float* out_score, void* workspace, hipStream_t stream,
+                                const SampleDraw* draw = nullptr);
+// Whether csa2_topk's dispatch takes the threshold filter for these rows.
+bool topk_uses_filter(int B, int64_t M, int K);
 // The Top-K levels after the first, on B rows of m chunk-winner keys.
 size_t topk_keys_workspace_bytes(int B, int64_t m, int K);
 // `app` (nullable): an independent FP4 append run by extra workgroups of the

@@ -223,6 +223,8 @@ static bool use_filter(int B, int64_t M, int K) {
   return (int64_t)B * ch[0] > 768 || n > 2;
 }
 
+bool topk_uses_filter(int B, int64_t M, int K) { return use_filter(B, M, K); }
+
 int64_t topk_launch_items(int B, int64_t M, int K) {
   return use_filter(B, M, K) ? topk_filter_launch_items(B, M) : topk_chunk_launch_items(B, M, K);
 }

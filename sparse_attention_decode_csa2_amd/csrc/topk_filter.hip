@@ -31,6 +31,7 @@
 // Every load of a thread is issued before the first result is used; a load
 // under a per-element branch would wait for the one before it.
 #include "csa2_internal.h"
+#include "sample_draw.h"
 #include "topk_block.h"
 
 namespace csa2 {
@@ -301,17 +302,13 @@ __device__ __forceinline__ void tf_from_key(uint64_t k, int e, float (&v)[TK_E],
   valid |= (lanemask)(hk != 0) << e;
 }
 
-__global__ __launch_bounds__(TK_T) void topk_select_kernel(const float* __restrict__ scores,
-                                                           const int32_t* __restrict__ ids,
-                                                           const int32_t* __restrict__ n_valid, int64_t M, int K,
-                                                           const TfRow* __restrict__ rows,
-                                                           const uint64_t* __restrict__ cand,
-                                                           int32_t* __restrict__ out_idx,
-                                                           float* __restrict__ out_score) {
-  __shared__ TkSmem sm;
-  __shared__ uint64_t run_keys[TK_KMAX];  // fallback: the running Top-K
+// Row b's final selection (run_keys: the fallback's running Top-K).
+__device__ __forceinline__ void tf_select_row(int64_t b, const float* __restrict__ scores,
+                                              const int32_t* __restrict__ ids, const int32_t* __restrict__ n_valid,
+                                              int64_t M, int K, const TfRow* __restrict__ rows,
+                                              const uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx,
+                                              float* __restrict__ out_score, TkSmem& sm, uint64_t* run_keys) {
   const int tid = threadIdx.x;
-  const int64_t b = blockIdx.x;
   const uint32_t theta = rows[b].theta, n = rows[b].count;
   const int64_t limit = tf_limit(n_valid, b, M);
   float v[TK_E];
@@ -392,6 +389,37 @@ __global__ __launch_bounds__(TK_T) void topk_select_kernel(const float* __restri
   tf_final(v, idv, valid, cols, K, out_idx + b * K, out_score ? out_score + b * K : nullptr, sm);
 }
 
+__global__ __launch_bounds__(TK_T) void topk_select_kernel(const float* __restrict__ scores,
+                                                           const int32_t* __restrict__ ids,
+                                                           const int32_t* __restrict__ n_valid, int64_t M, int K,
+                                                           const TfRow* __restrict__ rows,
+                                                           const uint64_t* __restrict__ cand,
+                                                           int32_t* __restrict__ out_idx,
+                                                           float* __restrict__ out_score) {
+  __shared__ TkSmem sm;
+  __shared__ uint64_t run_keys[TK_KMAX];
+  tf_select_row(blockIdx.x, scores, ids, n_valid, M, K, rows, cand, out_idx, out_score, sm, run_keys);
+}
+
+// The selection, then the sampler's draw over the row just written (the
+// candidates of csa2_sample): one launch fewer than the draw kernel after
+// the Top-K, the same draw (sample_draw_row).
+__global__ __launch_bounds__(TK_T) void topk_select_draw_kernel(const float* __restrict__ scores,
+                                                                const int32_t* __restrict__ n_valid, int64_t M,
+                                                                int K, const TfRow* __restrict__ rows,
+                                                                const uint64_t* __restrict__ cand,
+                                                                int32_t* __restrict__ out_idx,
+                                                                float* __restrict__ out_score, const SampleDraw d) {
+  __shared__ TkSmem sm;
+  __shared__ uint64_t run_keys[TK_KMAX];
+  __shared__ SmpSmem dsm;
+  const int64_t b = blockIdx.x;
+  tf_select_row(b, scores, nullptr, n_valid, M, K, rows, cand, out_idx, out_score, sm, run_keys);
+  __syncthreads();  // the row's candidates are written (and visible to the workgroup)
+  sample_draw_row(b, out_idx + b * K, out_score + b * K, K, d.log2e_over_t, d.top_p, d.u, d.token, d.prob,
+                  d.n_kept, dsm);
+}
+
 // ---------------------------------------------------------------- host
 bool topk_filter_fits(int B, int64_t M, int K) { return B > 0 && M > TK_CHUNK && M <= TF_MAX_M && K <= TK_KMAX; }
 
@@ -405,7 +433,8 @@ int64_t topk_filter_launch_items(int B, int64_t M) {
 }
 
 hipError_t launch_topk_filtered(const float* scores, const int32_t* ids, const int32_t* n_valid, int B, int64_t M,
-                                int K, int32_t* out_idx, float* out_score, void* workspace, hipStream_t stream) {
+                                int K, int32_t* out_idx, float* out_score, void* workspace, hipStream_t stream,
+                                const SampleDraw* draw) {
   TfRow* rows = static_cast<TfRow*>(workspace);
   uint64_t* cand = reinterpret_cast<uint64_t*>(rows + B);
   hipLaunchKernelGGL(topk_estimate_kernel, dim3((unsigned)B), dim3(TK_T), 0, stream, scores, ids, n_valid, M, K,
@@ -426,8 +455,12 @@ hipError_t launch_topk_filtered(const float* scores, const int32_t* ids, const i
                        ids, n_valid, M, (int)wpr, (int)tpw, rows, cand);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)B), dim3(TK_T), 0, stream, scores, ids, n_valid, M, K, rows,
-                     cand, out_idx, out_score);
+  if (draw && !ids && out_score)
+    hipLaunchKernelGGL(topk_select_draw_kernel, dim3((unsigned)B), dim3(TK_T), 0, stream, scores, n_valid, M, K,
+                       rows, cand, out_idx, out_score, *draw);
+  else
+    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)B), dim3(TK_T), 0, stream, scores, ids, n_valid, M, K,
+                       rows, cand, out_idx, out_score);
   return hipGetLastError();
 }
 

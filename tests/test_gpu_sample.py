@@ -125,14 +125,22 @@ def test_sample_golden_rows():
             assert abs(float(p[0]) - prob) <= 1e-6, (via, p, prob)
 
 
-def test_draw_on_topk_output_equals_sample():
-    B, V, K = 8, 50000, 1000
-    note(f"csa2_sample vs csa2_topk + csa2_sample_draw B={B} V={V} K={K}")
-    rng = np.random.default_rng(5)
+@pytest.mark.parametrize("B,V,K,T,top_p", [(8, 50000, 1000, 0.8, 0.95), (64, 200000, 1024, 0.8, 0.95),
+                                            (128, 129280, 2048, 1.0, 1.0), (100, 129280, 2048, 0.7, 0.5)])
+def test_draw_on_topk_output_equals_sample(B, V, K, T, top_p):
+    """csa2_sample = csa2_topk + csa2_sample_draw, bit for bit: below the
+    threshold filter's shapes the draw is its own kernel; on them (the last
+    three) the filter's last kernel draws from the rows it has written."""
+    note(f"csa2_sample vs csa2_topk + csa2_sample_draw B={B} V={V} K={K} T={T} top_p={top_p}")
+    rng = np.random.default_rng(5 + B)
     x = _logits(rng, B, V, "cont")
+    x[0, :] = -np.inf                      # a row with no finite logit
+    x[1, : V // 2] = -np.inf               # half the row masked
     u = rng.random(B).astype(np.float32)
-    a = _run(x, K, 0.8, 0.95, u, "sample")
-    b = _run(x, K, 0.8, 0.95, u, "draw")
+    u[2] = 0.0
+    u[3] = np.float32(1.0) - np.float32(2 ** -24)
+    a = _run(x, K, T, top_p, u, "sample")
+    b = _run(x, K, T, top_p, u, "draw")
     for ga, gb in zip(a, b):
         assert np.array_equal(ga, gb)
 
