@@ -26,7 +26,8 @@ the committed rocprofv3 FETCH_SIZE / WRITE_SIZE measurement of that kernel
 (profiles/), and is null when the kernel source changed since it was taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 `torch_topk_us` times torch.topk on the same score rows (K launches in one
-graph), the reference the pages quote for their Top-K kernel's speed-up.
+graph), the reference the pages quote for their Top-K kernel's speed-up;
+the sampler line adds `csa2_topk_us`, its Top-K alone on the same rows.
 `single_step_us_cold` is one step run on its own after a 512 MiB write has
 evicted the caches (median of five): the latency of an isolated decode step,
 beside `value`, the steady-state rate of back-to-back steps.
@@ -594,7 +595,8 @@ def main():
         g_ts.replay()
         torch_sampler_us = 1000.0 * timed(g_ts) / args.steps
         del g_ts
-    if "topk" in stages or "select" in stages:
+    csa2_topk_us = None
+    if "topk" in stages or "select" in stages or wl.mode == "sample":
         if "select" in stages:      # score rows for the reference, outside the timed region
             step.index(0)
             torch.cuda.synchronize()
@@ -602,6 +604,12 @@ def main():
         g_tt.replay()
         torch_topk_us = 1000.0 * timed(g_tt) / args.steps
         del g_tt
+    if wl.mode == "sample":
+        # the sampler's Top-K alone (csa2_topk over the same rows), beside torch.topk
+        g_ck = capture(step.topk, args.steps, W0 + args.steps)
+        g_ck.replay()
+        csa2_topk_us = 1000.0 * timed(g_ck) / args.steps
+        del g_ck
     # one step on its own with cold caches (what an isolated decode step
     # waits for, beside the steady-state rate above): a 512 MiB write evicts
     # the L2s and the Infinity Cache before each run; median of five
@@ -691,6 +699,7 @@ def main():
         "stage_us": {s: round(v, 3) for s, v in stage_us.items()},
         "stage_gbs": {s: round(alg[s] / (stage_us[s] * 1e-6) / 1e9, 1) for s in stages},
         "torch_topk_us": None if torch_topk_us is None else round(torch_topk_us, 3),
+        **({"csa2_topk_us": round(csa2_topk_us, 3)} if csa2_topk_us is not None else {}),
         "torch_sampler_us": None if torch_sampler_us is None else round(torch_sampler_us, 3),
         "roofline": roofline,
     }
