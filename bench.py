@@ -292,11 +292,6 @@ class Step:
         return self.sets[r]["keys"] if self.mode == "full" else self.keys
 
     # ---- stages
-    def quantize(self, r):
-        c, wl = self.cache, self.wl
-        self.csa2.csa2_quantize_fp4(self.chunk, c["codes"][0], c["scales"][0], wl.prefill_row0,
-                                    self.chunk_rope, c["rope"][0])
-
     def index(self, r):
         self.csa2.csa2_index_full(self.sets[r]["qi"], self._keys(r), scores=self.scores)
 
@@ -627,7 +622,7 @@ def main():
                    "sample": "topk.hip+topk_filter.hip+sample.hip",
                    "select": "index_topk.hip+topk.hip" if step.fused_select else "index_topk.hip+index.hip+topk.hip",
                    "attn_swa": "attn.hip",
-                   "quantize": "quantize.hip", "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip",
+                   "build": "pool.hip", "swa": "attn.hip", "draw": "sample.hip",
                    "draw_full": "sample.hip"}[dom]
     achieved = alg[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = committed_traffic(kernel_file, wl.name)
