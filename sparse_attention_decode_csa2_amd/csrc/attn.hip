@@ -1531,9 +1531,10 @@ hipError_t launch_sparse_attn(const uint16_t* q, CacheRef cache, const int32_t* 
 
 // The sparse attention and the query's sliding window as one softmax over the
 // union of their keys ([P4] CSA2 paragraph: the SWA branch beside the sparse
-// one).  The 32-head kernel takes the window rows as its first tiles; batches
-// it does not serve run the sparse kernels and then the window kernel, which
-// merges into their (out, lse).
+// one).  The 32-head kernel attends to the window rows as more tiles after the
+// selected entries' (in the query's first slice); batches it does not serve
+// run the sparse kernels and then the window kernel, which merges into their
+// (out, lse).
 bool sparse_swa_fused(int B, int H, int d_c) { return attn_heads_per_wg(B, H, d_c) == 32; }
 
 size_t sparse_swa_workspace_bytes(int B, int H, int d_c, int K) {
