@@ -167,11 +167,12 @@ def test_sample_full_workload():
              prob.cpu().numpy(), n.cpu().numpy(), max_near=2)
 
 
-def test_sample_in_a_hip_graph_matches_eager():
+@pytest.mark.parametrize("B,V,K", [(16, 40000, 1024), (64, 200000, 1024)])
+def test_sample_in_a_hip_graph_matches_eager(B, V, K):
     """csa2_sample captured into a HIP graph (outputs and workspace passed in)
     and replayed three times, with eager work in between, reproduces the
-    eager result bit for bit."""
-    B, V, K = 16, 40000, 1024
+    eager result bit for bit (the chunk levels and the draw kernel; the
+    threshold filter with the draw in its last kernel)."""
     note(f"csa2_sample: HIP graph capture + 3 replays vs eager B={B} V={V} K={K}")
     rng = np.random.default_rng(9)
     x = torch.from_numpy(_logits(rng, B, V, "cont")).to(DEV)

@@ -143,3 +143,37 @@ def test_sample_full_frequencies_match_softmax():
     want = softmax(row.astype(np.float64))
     assert np.all(np.abs(freq - want) <= 2.0 / G + 1e-9), np.abs(freq - want).max()
     assert np.all(np.diff(tok) >= 0)
+
+
+def test_sample_full_in_a_hip_graph_matches_eager():
+    """The two launches captured into a HIP graph (outputs and workspace
+    passed in) and replayed three times, with eager work in between,
+    reproduce the eager result bit for bit."""
+    B, V = 64, 129280
+    note(f"csa2_sample_full: HIP graph capture + 3 replays vs eager B={B} V={V}")
+    rng = np.random.default_rng(17)
+    x = torch.from_numpy((rng.standard_normal((B, V)) * 4).astype(np.float32)).to(DEV)
+    u = torch.from_numpy(rng.random(B).astype(np.float32)).to(DEV)
+    tok = torch.empty(B, dtype=torch.int32, device=DEV)
+    prob = torch.empty(B, dtype=torch.float32, device=DEV)
+    ws = torch.empty(csa2.csa2_sample_full_workspace_bytes(B, V), dtype=torch.uint8, device=DEV)
+
+    def step():
+        csa2.csa2_sample_full(x, 1.0, u, token=tok, prob=prob, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (tok, prob)]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(3):
+        tok.fill_(0)
+        prob.fill_(0)
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tok, ref[0]) and torch.equal(prob, ref[1]), rep
+        csa2.csa2_sample_full(x[:2], 0.5, u[:2])            # eager work between replays
+        torch.cuda.synchronize()
