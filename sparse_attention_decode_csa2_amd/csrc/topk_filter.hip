@@ -4,8 +4,8 @@
 // bit for bit that of the chunked reduction: the same 64-bit keys, the same
 // total order.
 //
-//  A. estimate (one 1024-thread workgroup per row): sixteen runs of 1024
-//     columns spread evenly over the row form a sample of 16384 scores; two
+//  A. estimate (one 1024-thread workgroup per row): sixteen runs of 256
+//     columns spread evenly over the row form a sample of 4096 scores; two
 //     radix passes over their order-preserving score keys place the k'-th
 //     largest sample key in a narrow range whose floor is theta, with k' the
 //     sample's expected share of the row's K winners raised by a quarter,
@@ -37,8 +37,9 @@
 namespace csa2 {
 
 constexpr int TF_CAP = TK_CHUNK;          // candidate slots per row: one block selection
-constexpr int TF_RUN = 1024;              // sample run length (columns)
-constexpr int TF_RUNS = TK_CHUNK / TF_RUN;
+constexpr int TF_SE = 4;                  // sample elements per thread
+constexpr int TF_RUN = 64 * TF_SE;        // sample run length (columns): one wave
+constexpr int TF_RUNS = TK_WAVES;
 constexpr int TF_FT = 1024;               // filter threads per workgroup
 constexpr int TF_FCOLS = TF_FT * TK_E;    // columns of a filter tile
 constexpr int TF_LCAP = 8192;             // keys a filter workgroup gathers in LDS
@@ -115,32 +116,34 @@ __global__ __launch_bounds__(TK_T) void topk_estimate_kernel(const float* __rest
   tk_init(sm);
   const float* srow = scores + b * M;
   const int32_t* irow = ids ? ids + b * M : nullptr;
-  // wave r reads run r, which starts at column r (limit - 1024) / 15 (the
+  // wave r reads run r, which starts at column r (limit - 256) / 15 (the
   // runs are evenly spaced and cover both ends of the row); element e of lane
   // l is column 64 e + l of the run, so each load is one contiguous 256-byte
-  // piece
-  static_assert(TF_RUN == WAVE * TK_E && TF_RUNS == TK_WAVES, "one run per wave");
+  // piece.  A sample of 4096 measured faster than one of 16384 (sample-129k
+  // Top-K + draw 43.1 -> 39.8 us): the estimate's loads and radix passes
+  // shrink, and the threshold keeps a few hundred more candidates
+  static_assert(TF_RUN == WAVE * TF_SE && TF_RUNS == TK_WAVES, "one run per wave");
   const int64_t c0 = (int64_t)wave_id() * (limit - TF_RUN) / (TF_RUNS - 1) + lane_id();
-  int64_t col[TK_E];
-  float s[TK_E];
-  uint32_t id[TK_E], key[TK_E];
+  int64_t col[TF_SE];
+  float s[TF_SE];
+  uint32_t id[TF_SE], key[TF_SE];
 #pragma unroll
-  for (int e = 0; e < TK_E; ++e) col[e] = c0 + WAVE * e;
-  tf_load_cols<TK_E>(srow, irow, col, limit, s, id);
+  for (int e = 0; e < TF_SE; ++e) col[e] = c0 + WAVE * e;
+  tf_load_cols<TF_SE>(srow, irow, col, limit, s, id);
   lanemask act = 0;
 #pragma unroll
-  for (int e = 0; e < TK_E; ++e) {
+  for (int e = 0; e < TF_SE; ++e) {
     const bool ok = id[e] != 0xFFFFFFFFu;
     key[e] = ok ? score_key(s[e]) : 0u;
     act |= (lanemask)ok << e;
   }
   int par = 0;
   uint32_t n, kmax, kmin;
-  active_stats<TK_E>(key, act, sm, par, &n, &kmax, &kmin);
+  active_stats<TF_SE>(key, act, sm, par, &n, &kmax, &kmin);
   // the sample's expected share of the row's K winners, raised so that theta
   // lies below the row's K-th key unless the sample misleads (the selection
   // detects that and reduces the row itself)
-  const float expct = (float)K * (float)TF_CAP / (float)limit;
+  const float expct = (float)K * (float)(TF_RUN * TF_RUNS) / (float)limit;
   uint32_t kp = (uint32_t)ceilf(1.25f * expct + 4.0f * sqrtf(expct) + 8.0f);
   uint32_t theta = 0u;
   // a sample with at most k' valid keys keeps every candidate (theta 0): the
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(TK_T) void topk_estimate_kernel(const float* __rest
     // k'-th largest sample key in a region; its floor, at or below every key
     // of the region, is the threshold (a third pass and the exact key cost a
     // further ~1.8 us for a few more kept keys)
-    const TkRegion g = radix_select<TK_E>(key, act, kp, kmax, kmin, n, 2, sm, par);
+    const TkRegion g = radix_select<TF_SE>(key, act, kp, kmax, kmin, n, 2, sm, par);
     theta = g.prefix;
   }
   if (tid == 0) {
