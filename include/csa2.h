@@ -178,7 +178,7 @@ int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
  *     winners are reduced again until one chunk remains (the workspace holds
  *     the levels' winners: B * ch_l * K * 8 bytes for each level l but the
  *     last, ch_0 = ceil(M / 16384), ch_l+1 = ceil(ch_l * K / 16384));
- *   threshold filter, for K >= 1024 on rows of at most 2^20 columns whose
+ *   threshold filter, for K >= 64 on rows of at most 2^20 columns whose
  *     first level would take more than 768 chunks in all (B * ch_0 > 768) or
  *     whose reduction takes more than two levels: a 16384-column sample of each
  *     row gives a score threshold, one pass keeps the candidates at or above

@@ -210,14 +210,15 @@ size_t topk_chunk_workspace_bytes(int B, int64_t M, int K) {
   return bytes;
 }
 
-// The threshold filter (topk_filter.hip) serves K >= 1024 on rows whose
+// The threshold filter (topk_filter.hip) serves K >= 64 on rows whose
 // chunked reduction takes more than three rounds of workgroups at its first
 // level (more than three chunks per CU) or more than two levels: there its
 // three launches (a sample, one streaming pass, one selection per row) beat
-// the levels, whose per-chunk selection costs grow with K.  Elsewhere the
-// levels are as fast or faster (measured on MI355X).
+// the levels, whose per-chunk selection costs grow with K (by 7-25% from
+// K = 64 to 2048).  Elsewhere, and for K below 64, where a chunk's selection
+// is cheap, the levels are as fast or faster (measured on MI355X).
 static bool use_filter(int B, int64_t M, int K) {
-  if (!topk_filter_fits(B, M, K) || K < 1024) return false;
+  if (!topk_filter_fits(B, M, K) || K < 64) return false;
   int64_t ch[16];
   const int n = topk_levels(M, K, ch, 16);
   return (int64_t)B * ch[0] > 768 || n > 2;

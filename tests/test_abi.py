@@ -87,10 +87,14 @@ def test_topk_validation(lib):
     need = lib.csa2_topk_workspace_bytes(2, 40000, 512)
     assert need == 2 * 3 * 512 * 8
     assert lib.csa2_topk_workspace_bytes(2, 16384, 512) == 0
-    # the threshold filter (128 bytes + 16384 keys per row): K >= 1024 and
+    # the threshold filter (128 bytes + 16384 keys per row): K >= 64 and
     # more than 768 first-level chunks, or more than two levels, in rows of at
     # most 2^20
-    assert lib.csa2_topk_workspace_bytes(128, 129280, 512) == 128 * 8 * 512 * 8
+    assert lib.csa2_topk_workspace_bytes(128, 129280, 512) == 128 * (128 + 16384 * 8)
+    assert lib.csa2_topk_workspace_bytes(128, 129280, 64) == 128 * (128 + 16384 * 8)
+    assert lib.csa2_topk_workspace_bytes(128, 129280, 32) == 128 * 8 * 32 * 8
+    assert lib.csa2_topk_workspace_bytes(1, 2 ** 20, 512) == 128 + 16384 * 8
+    assert lib.csa2_topk_workspace_bytes(1, 2 ** 20, 256) == 64 * 256 * 8
     assert lib.csa2_topk_workspace_bytes(128, 129280, 2048) == 128 * (128 + 16384 * 8)
     assert lib.csa2_topk_workspace_bytes(1, 300000, 2048) == 128 + 16384 * 8
     assert lib.csa2_topk_workspace_bytes(1, 300000, 512) == 19 * 512 * 8

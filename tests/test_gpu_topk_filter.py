@@ -1,4 +1,4 @@
-"""a3 csa2_topk on rows that take the threshold filter (K >= 1024 and more
+"""a3 csa2_topk on rows that take the threshold filter (K >= 64 and more
 than 768 first-level chunks in all, or more than two chunk levels, in rows of
 at most 2^20 columns) against the oracle: bit-exact ids and scores, and equal bit for
 bit to the chunked reduction (csa2_topk_noalloc always takes it).
@@ -78,8 +78,9 @@ def _family(rng, B, M, kind):
 
 # (B, M, K): more than 768 first-level chunks (B * ceil(M / 16384) > 768), or
 # three levels (19 and 64 chunks), ragged tails (an odd row length takes the
-# 4-byte loads), the longest row
-SHAPES = [(400, 20000, 1024), (20, 300001, 1024), (1, 300000, 2048), (1, 1 << 20, 2048), (100, 129280, 2048)]
+# 4-byte loads), the longest row; K from 64 to 2048
+SHAPES = [(400, 20000, 1024), (20, 300001, 1024), (1, 300000, 2048), (1, 1 << 20, 2048), (100, 129280, 2048),
+          (128, 129280, 512), (1, 1 << 20, 512), (300, 40000, 64), (200, 65537, 200)]
 
 
 @pytest.mark.parametrize("B,M,K", SHAPES)
