@@ -79,7 +79,7 @@ def _run(logits, K, T, top_p, u, via="sample"):
 
 
 CASES = [(1, 1, 1), (3, 10, 16), (4, 1000, 64), (3, 300, 65), (5, 5000, 2047), (2, 20000, 512),
-         (64, 4096, 100), (2, 129280, 2048)]
+         (64, 4096, 100), (2, 129280, 2048), (400, 20000, 64)]
 
 
 @pytest.mark.parametrize("B,V,K", CASES)
@@ -126,11 +126,12 @@ def test_sample_golden_rows():
 
 
 @pytest.mark.parametrize("B,V,K,T,top_p", [(8, 50000, 1000, 0.8, 0.95), (64, 200000, 1024, 0.8, 0.95),
-                                            (128, 129280, 2048, 1.0, 1.0), (100, 129280, 2048, 0.7, 0.5)])
+                                            (128, 129280, 2048, 1.0, 1.0), (100, 129280, 2048, 0.7, 0.5),
+                                            (128, 129280, 64, 1.0, 1.0), (100, 129280, 200, 0.8, 0.9)])
 def test_draw_on_topk_output_equals_sample(B, V, K, T, top_p):
     """csa2_sample = csa2_topk + csa2_sample_draw, bit for bit: below the
     threshold filter's shapes the draw is its own kernel; on them (the last
-    three) the filter's last kernel draws from the rows it has written."""
+    five) the filter's last kernel draws from the rows it has written."""
     note(f"csa2_sample vs csa2_topk + csa2_sample_draw B={B} V={V} K={K} T={T} top_p={top_p}")
     rng = np.random.default_rng(5 + B)
     x = _logits(rng, B, V, "cont")
