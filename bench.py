@@ -522,8 +522,8 @@ def cpu_baseline(wl, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
-              f"multi-GPU path; see DESIGN.md for how the step would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the step has no "
+              f"multi-GPU path (each GPU would run it on its own shard of the batch).", file=sys.stderr)
         sys.exit(2)
     import torch
     from sparse_attention_decode_csa2_amd import workloads as W

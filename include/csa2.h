@@ -159,7 +159,7 @@ int csa2_index_pool(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
 /*
  * a3. Top-K selection with the lower id winning ties.
  * Top-512 per [P1] 架构三件套, CSA2; the tie rule (lower index wins) is a
- * fixed parameter of this build; ids are global entry positions.
+ * fixed parameter of this library; ids are global entry positions.
  *
  * scores    f32 [B, M]
  * ids       i32 [B, M]  candidate ids, or NULL for the column index; id -1
@@ -265,7 +265,7 @@ int csa2_topk_noalloc(const float* scores, const int32_t* ids, const int32_t* n_
  * The decode sampler on the Top-K selection.  One Top-K implementation serves
  * the sparse attention and the sampler ([P3] DeepSelect paragraph); sampling
  * is set by a temperature and a top_p ([P1] interface paragraph).  The order
- * of the steps is this build's reading, the usual one:
+ * of the steps is this library's reading, the usual one:
  *   candidates = the row's K largest logits, in csa2_topk order (logit
  *                descending, token id ascending);
  *   w_i        = exp((l_i - l_0) / T) for the i-th candidate (0 for -inf);
@@ -314,7 +314,7 @@ int csa2_sample(const float* logits, int32_t B, int64_t V, int32_t K, float temp
  * The untruncated draw: the recommended sampling settings, temperature 1.0 and
  * top_p 1.0 ([P1] interface paragraph), taken literally: top_p 1.0 keeps
  * every token of the vocabulary, so no Top-K cap applies and the draw is over
- * the whole softmax of logits / T.  The order is this build's reading:
+ * the whole softmax of logits / T.  The order is this library's reading:
  *   w_i   = exp((l_i - l_max) / T) for every token i of the row (0 for -inf);
  *   token = the first token, in token-id order, whose running weight exceeds
  *           u * sum(w) (the last token of nonzero weight if rounding leaves
@@ -343,7 +343,7 @@ int csa2_sample_full(const float* logits, int32_t B, int64_t V, float temperatur
 /*
  * Sliding-window branch, write: FP8 rows of the window KV.  The window branch
  * keeps its KV in FP8 ([P4] CSA2 paragraph; [P1] 效率组件四件, item 4); the
- * pages give no scale granularity, this build uses one power-of-two scale per
+ * pages give no scale granularity, this library uses one power-of-two scale per
  * row: sigma = 2^e, e the smallest integer with max|x| <= 448 * 2^e (1 for an
  * all-zero row, e clamped to [-126, 127]), codes = E4M3 (OCP E4M3FN) nearest
  * to |x| / sigma, ties to the even code, sign bit copied (-0 -> 0x80).
@@ -437,7 +437,7 @@ int csa2_swa_attn_fp8(const uint16_t* q, const uint8_t* codes, int64_t codes_str
  * Candidate-pool construction for Reindex mode: the block-level pool that the
  * decoder's first Full layer keeps (at most 2048 blocks x 8 positions) so that
  * later layers score only inside it ([P1] 架构三件套, Hierarchical Sparse
- * Indexer; [P4] CSA2 paragraph).  The pages give no block score; this build
+ * Indexer; [P4] CSA2 paragraph).  The pages give no block score; this library
  * reads it as the largest score of the block's valid positions.
  *
  * scores      f32 [B, M]  a Full layer's indexer scores (csa2_index_full)

@@ -2,7 +2,7 @@
 
 What the step computes, stage by stage (citations use the page keys of the
 package docstring; the pages give no formulas, so where they are silent the
-reading taken is stated at the function and listed in the design doc):
+reading taken is stated at the function):
 
 1. a0  ``quantize_fp4``  - the FP4 main-KV write: E2M1 values, one E4M3
        scale per 16 channels, no global scale, applied to post-RoPE values
