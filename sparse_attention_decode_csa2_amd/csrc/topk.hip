@@ -214,9 +214,10 @@ size_t topk_chunk_workspace_bytes(int B, int64_t M, int K) {
 // chunked reduction takes more than three rounds of workgroups at its first
 // level (more than three chunks per CU) or more than two levels: there its
 // three launches (a sample, one streaming pass, one selection per row) beat
-// the levels, whose per-chunk selection costs grow with K (by 7-25% from
-// K = 64 to 2048).  Elsewhere, and for K below 64, where a chunk's selection
-// is cheap, the levels are as fast or faster (measured on MI355X).
+// the levels, whose per-chunk selection costs grow with K (128 rows of
+// 129280 columns: 37.7 us at K = 64, 51.3 us at K = 2048, against 30.8 and
+// 36.1 us filtered).  Elsewhere, and for K below 64, where a chunk's
+// selection is cheap, the levels are as fast or faster (measured on MI355X).
 static bool use_filter(int B, int64_t M, int K) {
   if (!topk_filter_fits(B, M, K) || K < 64) return false;
   int64_t ch[16];
